@@ -1,0 +1,139 @@
+/*
+ * msda.h -- C ABI of the MI355X (gfx950) multi-scale deformable attention
+ * (MSDeformAttn) sampling core.
+ *
+ * The operation.  For every batch b, query q and head m the core returns
+ *
+ *     out[b, q, m*D + d] = sum_l sum_k A[b,q,m,l,k] * S_l(value[b, :, m, d], loc[b,q,m,l,k])
+ *
+ * the attention-weighted sum over levels l and points k of bilinear samples of
+ * the flattened multi-level value ("Deformable attention: multi-scale sparse
+ * sampling and detection practice", section 2.2, the multi-scale formula with
+ * the value and output projections left outside; "Deformable DETR" tutorial,
+ * section 3.3).  A sample S_l at normalized location (u, v) of level l, whose
+ * rows in the level table are (H_l, W_l) and whose pixels start at flattened
+ * index start_l, takes the pixel coordinates x = u*W_l - 0.5, y = v*H_l - 0.5
+ * (the grid_sample convention with align_corners=False, first page, sections
+ * 2.3 and 3.2) and sums the four integer neighbours (x0,y0), (x0+1,y0),
+ * (x0,y0+1), (x0+1,y0+1) with bilinear weights; neighbours outside the map
+ * contribute zero (first page, section 2.3).  The pixel coordinate is
+ * computed as one fp32 fused multiply-add and floored in fp32.  Locations
+ * whose coordinates are not finite contribute zero.
+ *
+ * Layouts.  Every tensor is dense and row-major with no strides:
+ *   value              [B, Nv, M, D]          fp32, or bf16 when value_dtype == MSDA_BF16
+ *   spatial_shapes     [L, 2]  int64, rows (H_l, W_l)
+ *   level_start_index  [L]     int64, start_l = sum of H*W of the levels before l
+ *   sampling_loc       [B, Nq, M, L, K, 2]    fp32, last axis (x, y) = (u, v), normalized
+ *   attn_weight        [B, Nq, M, L, K]       fp32
+ *   out, grad_out      [B, Nq, M*D]           fp32, head-major (channel m*D + d)
+ *   grad_value         [B, Nv, M, D]          fp32 for either value dtype
+ *   grad_sampling_loc  [B, Nq, M, L, K, 2]    fp32
+ *   grad_attn_weight   [B, Nq, M, L, K]       fp32
+ * with Nv = sum_l H_l*W_l.
+ *
+ * Memory and ownership.  Every tensor pointer, spatial_shapes and
+ * level_start_index included, is a DEVICE pointer on the current HIP device;
+ * the caller allocates and owns all of them.  The library allocates nothing,
+ * frees nothing and keeps no state between calls.  Outputs must not alias
+ * inputs.
+ *
+ * Streams and errors.  `stream` is a hipStream_t (NULL = the null stream).
+ * Work is enqueued on it and the call returns without synchronizing; a
+ * kernel fault therefore surfaces at the caller's next synchronization.
+ * Every function returns an msda_status; nothing is thrown across the ABI.
+ * The launch-time checks cover null pointers, negative sizes, 1 <= L <= 16,
+ * the supported head widths and dtypes, and the 32-bit addressing limit.
+ * The level table is on the device and is not read by the host:
+ * msda_validate_host checks a host copy of it.  The kernels address value and
+ * grad_value through range-checked buffer descriptors, so an inconsistent
+ * level table cannot make them touch memory outside those tensors: a level
+ * that does not fit inside value contributes zero.
+ *
+ * Limits.  D in {4, 8, 16, 32, 64, 128, 256}; 1 <= L <= 16; K >= 1;
+ * Nv*M*D*4 < 2^31 bytes (one batch slice of grad_value); Nq*M*L*K*2 < 2^31.
+ * B, Nq may be 0 (nothing is launched, except the grad_value fill).
+ */
+#ifndef MSDA_H
+#define MSDA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum msda_status {
+    MSDA_OK = 0,
+    MSDA_ERR_NULL = -1,        /* a required pointer is NULL                          */
+    MSDA_ERR_SHAPE = -2,       /* sizes are negative or inconsistent                  */
+    MSDA_ERR_DTYPE = -3,       /* value_dtype is not an msda_dtype                    */
+    MSDA_ERR_UNSUPPORTED = -4, /* valid but outside the limits above (D, L, size)     */
+    MSDA_ERR_HIP = -5          /* the HIP runtime refused a launch (see msda_last_hip_error) */
+} msda_status;
+
+typedef enum msda_dtype {
+    MSDA_F32 = 0,
+    MSDA_BF16 = 1              /* bfloat16 value only; all else fp32                  */
+} msda_dtype;
+
+/* Flags of msda_backward. */
+#define MSDA_BWD_ACCUMULATE 1u /* add into grad_value instead of overwriting it      */
+
+/*
+ * Forward: out = MSDeformAttn core(value, level table, sampling_loc, attn_weight).
+ * out is overwritten.  value_dtype is an msda_dtype.
+ */
+msda_status msda_forward(const void *value, int value_dtype,
+                         const int64_t *spatial_shapes, const int64_t *level_start_index,
+                         const float *sampling_loc, const float *attn_weight, float *out,
+                         int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
+                         int64_t L, int64_t K, void *stream);
+
+/*
+ * Backward of msda_forward for the upstream gradient grad_out.  The pages give
+ * no formulas (first page, section 2.3 says the interpolation is differentiable
+ * so the gradient reaches the offsets); these are the exact derivatives of the
+ * forward above.  With the four neighbours' bilinear weights w_c, values v_c
+ * (zero outside the map) and fractional parts fx, fy of the pixel coordinate:
+ *   grad_attn_weight = sum_d g_d * sum_c w_c v_c,d
+ *   grad_loc.x = A * W_l * sum_d g_d * ((1-fy)(v_TR - v_TL) + fy (v_BR - v_BL))_d
+ *   grad_loc.y = A * H_l * sum_d g_d * ((1-fx)(v_BL - v_TL) + fx (v_BR - v_TR))_d
+ *   grad_value[neighbour c] += A * w_c * g            (scatter-add, fp32 atomics)
+ * At an integer pixel coordinate the derivative is the one of the cell
+ * [x0, x0+1) chosen by the floor.
+ * grad_value is overwritten (zero-filled first, on `stream`) unless flags has
+ * MSDA_BWD_ACCUMULATE.  Its summation order is not fixed, so repeated calls
+ * may differ in the last bits.  grad_sampling_loc and grad_attn_weight are
+ * overwritten and deterministic.
+ */
+msda_status msda_backward(const void *value, int value_dtype,
+                          const int64_t *spatial_shapes, const int64_t *level_start_index,
+                          const float *sampling_loc, const float *attn_weight,
+                          const float *grad_out, float *grad_value,
+                          float *grad_sampling_loc, float *grad_attn_weight,
+                          int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
+                          int64_t L, int64_t K, uint32_t flags, void *stream);
+
+/*
+ * Pure host check of the sizes and of a HOST copy of the level table:
+ * H_l, W_l >= 1, level_start_host[l] = sum of H*W of levels before l,
+ * Nv = sum H*W, plus every limit msda_forward/msda_backward check.
+ * Needs no GPU.
+ */
+msda_status msda_validate_host(const int64_t *spatial_shapes_host,
+                               const int64_t *level_start_host,
+                               int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
+                               int64_t L, int64_t K);
+
+/* Static English text for a status code (never NULL). */
+const char *msda_status_string(int status);
+
+/* hipError_t of the last MSDA_ERR_HIP returned on this thread (0 if none). */
+int msda_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSDA_H */

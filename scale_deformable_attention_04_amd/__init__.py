@@ -1,0 +1,41 @@
+"""MI355X-native multi-scale deformable attention (MSDeformAttn) sampling core.
+
+``forward`` / ``backward`` call the C ABI of libmsda.so (include/msda.h): hand
+written gfx950 HIP kernels.  ``ms_deform_attn`` wraps them as a
+torch.autograd.Function.  torch is used for device memory and the stream only.
+"""
+from __future__ import annotations
+
+import torch
+
+from ._binding import (EXPORTED, LIB_PATH, MSDA_BF16, MSDA_BWD_ACCUMULATE, MSDA_ERR_DTYPE,
+                       MSDA_ERR_HIP, MSDA_ERR_NULL, MSDA_ERR_SHAPE, MSDA_ERR_UNSUPPORTED,
+                       MSDA_F32, MSDA_OK, MSDAError, backward, forward, load, status_string,
+                       validate_host)
+
+__all__ = ["forward", "backward", "validate_host", "status_string", "load", "MSDAError",
+           "ms_deform_attn", "MSDeformAttnFunction", "LIB_PATH", "EXPORTED"]
+
+
+class MSDeformAttnFunction(torch.autograd.Function):
+    """out = core(value, level table, sampling_loc, attn_weight) with the
+    library's backward.  grad_value comes back in fp32; autograd casts it to
+    value's dtype."""
+
+    @staticmethod
+    def forward(ctx, value, spatial_shapes, level_start_index, sampling_loc, attn_weight):
+        out = forward(value, spatial_shapes, level_start_index, sampling_loc, attn_weight)
+        ctx.save_for_backward(value, spatial_shapes, level_start_index, sampling_loc,
+                              attn_weight)
+        return out
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        value, ss, st, loc, attn = ctx.saved_tensors
+        gv, gl, ga = backward(value, ss, st, loc, attn, grad_out.contiguous(), validate=False)
+        return gv, None, None, gl, ga
+
+
+def ms_deform_attn(value, spatial_shapes, level_start_index, sampling_loc, attn_weight):
+    return MSDeformAttnFunction.apply(value, spatial_shapes, level_start_index, sampling_loc,
+                                      attn_weight)

@@ -1,0 +1,291 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Metric (per output tensor): max_i |x_i - r_i| / max_i |r_i|.  Bars: fp32
+forward 1e-5; fp32 backward 1e-4 (grad_value is summed with atomics in no
+fixed order); bf16 value 2e-2 against the oracle on the unrounded fp32 values,
+and the fp32 bars against the oracle on the bf16-rounded values.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from oracle_pins import max_rel
+
+pytestmark = pytest.mark.gpu
+
+FWD_TOL = 1e-5
+BWD_TOL = 1e-4
+BF16_TOL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def msda():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the gpu tests must run on an MI355X")
+    import scale_deformable_attention_04_amd as m
+    m.load()
+    return m
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def dev_inputs(w: workloads.Workload, bf16: bool = False):
+    d = torch.device("cuda:0")
+    if bf16:
+        bits = torch.from_numpy(w.value_bf16.view(np.int16).copy())
+        value = bits.view(torch.bfloat16).to(d)
+    else:
+        value = torch.from_numpy(w.value).to(d)
+    t = lambda a, dt=None: torch.from_numpy(np.ascontiguousarray(a)).to(d)
+    return dict(value=value, spatial_shapes=t(w.spatial_shapes),
+                level_start_index=t(w.level_start_index), sampling_loc=t(w.sampling_loc),
+                attn_weight=t(w.attn_weight))
+
+
+def gpu_forward(m, w, bf16=False):
+    x = dev_inputs(w, bf16)
+    out = m.forward(**x)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def gpu_backward(m, w, bf16=False, **kw):
+    x = dev_inputs(w, bf16)
+    g = torch.from_numpy(w.grad_out).cuda()
+    gv, gl, ga = m.backward(**x, grad_out=g, **kw)
+    torch.cuda.synchronize()
+    return gv.cpu().numpy(), gl.cpu().numpy(), ga.cpu().numpy()
+
+
+def oracle_fwd(w, value=None):
+    return oracle.forward(w.value if value is None else value, w.spatial_shapes,
+                          w.level_start_index, w.sampling_loc, w.attn_weight)
+
+
+def oracle_bwd(w, value=None):
+    return oracle.backward(w.value if value is None else value, w.spatial_shapes,
+                           w.level_start_index, w.sampling_loc, w.attn_weight, w.grad_out)
+
+
+def check_fwd(m, w, tol=FWD_TOL, bf16=False):
+    got = gpu_forward(m, w, bf16)
+    ref = oracle_fwd(w).reshape(got.shape)
+    e = max_rel(got, ref)
+    assert e <= tol, f"{w.name}: forward max rel {e:.3e} > {tol}"
+    return got, e
+
+
+def check_bwd(m, w, tol=BWD_TOL, bf16=False):
+    gv, gl, ga = gpu_backward(m, w, bf16)
+    rv, rl, ra = oracle_bwd(w)
+    errs = (max_rel(gv, rv), max_rel(gl, rl), max_rel(ga, ra))
+    for name, e in zip(("grad_value", "grad_sampling_loc", "grad_attn_weight"), errs):
+        assert e <= tol, f"{w.name}: {name} max rel {e:.3e} > {tol}"
+    return errs
+
+
+# ---------------------------------------------------------------------------
+# the five configurations at full size
+# ---------------------------------------------------------------------------
+def test_tiny_fwd_bwd(msda):
+    _say("tiny fwd+bwd")
+    w = workloads.make(0)
+    check_fwd(msda, w)
+    check_bwd(msda, w)
+
+
+def test_encoder_fwd(msda):
+    _say("encoder fwd B=2 Nq=Nv=22223 M=8 D=32 L=4 K=4")
+    check_fwd(msda, workloads.make(1))
+
+
+def test_decoder_fwd(msda):
+    _say("decoder fwd B=2 Nq=300")
+    check_fwd(msda, workloads.make(2))
+
+
+def test_encoder_bwd(msda):
+    _say("encoder bwd B=2 Nq=Nv=22223")
+    check_bwd(msda, workloads.make(3))
+
+
+def test_train_bf16_fwd_bwd(msda):
+    _say("train bf16 B=4 K=8 fwd+bwd")
+    w = workloads.make(4)
+    # strict: against the oracle on the bf16-rounded values (w.value)
+    got = gpu_forward(msda, w, bf16=True)
+    assert max_rel(got, oracle_fwd(w).reshape(got.shape)) <= FWD_TOL
+    gv, gl, ga = gpu_backward(msda, w, bf16=True)
+    rv, rl, ra = oracle_bwd(w)
+    for x, r in ((gv, rv), (gl, rl), (ga, ra)):
+        assert max_rel(x, r) <= BWD_TOL
+    # pass/fail bar: against the oracle on the unrounded fp32 values
+    assert max_rel(got, oracle_fwd(w, w.value_unrounded).reshape(got.shape)) <= BF16_TOL
+    rv, rl, ra = oracle_bwd(w, w.value_unrounded)
+    for x, r in ((gv, rv), (gl, rl), (ga, ra)):
+        assert max_rel(x, r) <= BF16_TOL
+
+
+# ---------------------------------------------------------------------------
+# every head width, both value dtypes, ragged tails, several tiles
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("D", [4, 8, 16, 32, 64, 128, 256])
+@pytest.mark.parametrize("bf16", [False, True])
+def test_random_shapes(msda, D, bf16):
+    shapes = ((13, 21), (7, 11), (4, 6))
+    Nq = 301 if D <= 32 else 97      # several workgroups and a partial last one
+    w = workloads.random_case(100 + D, 3, shapes, Nq, 3, D, 3, bf16=bf16)
+    _say(f"random D={D} bf16={bf16} Nq={Nq}")
+    check_fwd(msda, w, bf16=bf16)
+    check_bwd(msda, w, bf16=bf16)
+
+
+@pytest.mark.parametrize("L,K", [(1, 1), (1, 7), (3, 5), (4, 16), (2, 40)])
+def test_point_counts(msda, L, K):
+    """L*K up to 80: the point tables are walked in several chunks."""
+    shapes = ((9, 10), (5, 5), (3, 2), (2, 2))[:L]
+    w = workloads.random_case(200 + 10 * L + K, 2, shapes, 67, 4, 32, K)
+    _say(f"points L={L} K={K}")
+    check_fwd(msda, w)
+    check_bwd(msda, w)
+
+
+def test_sixteen_levels_and_thin_maps(msda):
+    shapes = tuple((1 + (i % 4), 1 + (7 * i) % 9) for i in range(16))
+    w = workloads.random_case(300, 2, shapes, 45, 2, 16, 2, -0.3, 1.3)
+    _say("16 levels")
+    check_fwd(msda, w)
+    check_bwd(msda, w)
+
+
+def test_pixel_centres_are_exact(msda):
+    """A point at a pixel centre with weight 1 returns the stored row exactly."""
+    shapes = ((8, 16), (4, 8))
+    w = workloads.random_case(400, 2, shapes, 40, 4, 32, 2)
+    rng = np.random.Generator(np.random.PCG64(1))
+    loc = w.sampling_loc.copy()
+    attn = np.zeros_like(w.attn_weight)
+    expect = np.zeros((2, 40, 4, 32), np.float32)
+    for b in range(2):
+        for q in range(40):
+            for m in range(4):
+                l = int(rng.integers(2))
+                H, W = shapes[l]
+                i, j = int(rng.integers(H)), int(rng.integers(W))
+                loc[b, q, m, l, 0] = ((j + 0.5) / W, (i + 0.5) / H)
+                attn[b, q, m, l, 0] = 1.0
+                expect[b, q, m] = w.value[b, w.level_start_index[l] + i * W + j, m]
+    w.sampling_loc, w.attn_weight = loc, attn
+    _say("pixel centres")
+    got = gpu_forward(msda, w).reshape(expect.shape)
+    assert np.array_equal(got, expect)
+
+
+def test_out_of_map_and_nonfinite(msda):
+    w = workloads.random_case(500, 2, ((6, 5), (3, 3)), 33, 2, 8, 3)
+    loc = w.sampling_loc.copy()
+    loc[:, ::2, :, :, :, 0] = -0.5                  # fully left of every map
+    loc[:, 1::4, :, :, :, 1] = 1.7                  # fully below
+    loc[:, 3, 0, 0, 0, 0] = np.nan
+    loc[:, 5, 1, 1, 2, 1] = np.inf
+    loc[:, 7, 0, 1, 1, 0] = -np.inf
+    w.sampling_loc = loc
+    _say("out of map / non-finite")
+    got, _ = check_fwd(msda, w)
+    assert np.all(np.isfinite(got))
+    assert np.all(got.reshape(2, 33, -1)[:, ::2] == 0.0)
+    gv, gl, ga = gpu_backward(msda, w)
+    rv, rl, ra = oracle_bwd(w)
+    assert np.all(np.isfinite(gl)) and np.all(np.isfinite(ga))
+    assert np.all(gl[:, ::2] == 0.0) and np.all(ga[:, ::2] == 0.0)
+    for x, r in ((gv, rv), (gl, rl), (ga, ra)):
+        assert max_rel(x, r) <= BWD_TOL
+
+
+def test_empty_inputs(msda):
+    d = torch.device("cuda:0")
+    _say("empty")
+    ss = torch.tensor([[4, 4]], device=d)
+    st = torch.tensor([0], device=d)
+    # no queries
+    v = torch.randn(2, 16, 2, 8, device=d)
+    loc = torch.zeros(2, 0, 2, 1, 3, 2, device=d)
+    a = torch.zeros(2, 0, 2, 1, 3, device=d)
+    out = msda.forward(v, ss, st, loc, a)
+    assert out.shape == (2, 0, 16)
+    gv, gl, ga = msda.backward(v, ss, st, loc, a, torch.zeros(2, 0, 16, device=d))
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(gv).item() == 0          # overwritten with zeros
+    # no batch
+    v = torch.randn(0, 16, 2, 8, device=d)
+    out = msda.forward(v, ss, st, torch.zeros(0, 5, 2, 1, 3, 2, device=d),
+                       torch.zeros(0, 5, 2, 1, 3, device=d))
+    assert out.shape == (0, 5, 16)
+
+
+def test_accumulate_adds_into_grad_value(msda):
+    w = workloads.random_case(600, 2, ((7, 9), (3, 4)), 50, 2, 32, 4)
+    x = dev_inputs(w)
+    g = torch.from_numpy(w.grad_out).cuda()
+    base = torch.randn(x["value"].shape, device="cuda")
+    gv = base.clone()
+    _say("accumulate")
+    msda.backward(**x, grad_out=g, grad_value=gv, accumulate=True)
+    torch.cuda.synchronize()
+    rv, _, _ = oracle_bwd(w)
+    assert max_rel(gv.cpu().numpy() - base.cpu().numpy(), rv) <= BWD_TOL
+
+
+def test_runs_on_the_callers_stream(msda):
+    w = workloads.random_case(700, 2, ((9, 9), (4, 4)), 90, 4, 32, 4)
+    x = dev_inputs(w)
+    s = torch.cuda.Stream()
+    _say("side stream")
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        out = msda.forward(**x, validate=False)
+        gv, gl, ga = msda.backward(**x, grad_out=torch.from_numpy(w.grad_out).cuda(),
+                                   validate=False)
+    s.synchronize()
+    assert max_rel(out.cpu().numpy(), oracle_fwd(w)) <= FWD_TOL
+    rv, rl, ra = oracle_bwd(w)
+    assert max_rel(gl.cpu().numpy(), rl) <= BWD_TOL
+
+
+def test_autograd_function(msda):
+    w = workloads.random_case(800, 1, ((6, 7), (3, 3)), 20, 2, 16, 2)
+    x = dev_inputs(w)
+    v = x["value"].clone().requires_grad_(True)
+    loc = x["sampling_loc"].clone().requires_grad_(True)
+    a = x["attn_weight"].clone().requires_grad_(True)
+    _say("autograd")
+    out = msda.ms_deform_attn(v, x["spatial_shapes"], x["level_start_index"], loc, a)
+    out.backward(torch.from_numpy(w.grad_out).cuda())
+    rv, rl, ra = oracle_bwd(w)
+    assert max_rel(out.detach().cpu().numpy(), oracle_fwd(w)) <= FWD_TOL
+    assert max_rel(v.grad.cpu().numpy(), rv) <= BWD_TOL
+    assert max_rel(loc.grad.cpu().numpy(), rl) <= BWD_TOL
+    assert max_rel(a.grad.cpu().numpy(), ra) <= BWD_TOL
+
+
+def test_backward_repeatability(msda):
+    """grad_value is summed with atomics in no fixed order: report the spread
+    over repeated runs; grad_loc and grad_attn are deterministic."""
+    w = workloads.make(3)
+    x = dev_inputs(w)
+    g = torch.from_numpy(w.grad_out).cuda()
+    _say("repeatability x5 encoder bwd")
+    runs = [tuple(t.clone() for t in msda.backward(**x, grad_out=g, validate=False))
+            for _ in range(5)]
+    torch.cuda.synchronize()
+    ref = runs[0]
+    scale = ref[0].abs().max().item()
+    spread = max((r[0] - ref[0]).abs().max().item() for r in runs[1:]) / scale
+    print(f"grad_value spread over 5 runs: {spread:.3e} (relative to max)", flush=True)
+    assert spread <= 1e-5
+    for r in runs[1:]:
+        assert torch.equal(r[1], ref[1]) and torch.equal(r[2], ref[2])
