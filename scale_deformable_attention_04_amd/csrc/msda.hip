@@ -270,13 +270,24 @@ msda_bwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
     const size_t pt0 = ((size_t)b * NqM + item0) * LK;
 
     const int it = threadIdx.x / G, c = threadIdx.x % G;
-    float4 g4 = make_float4(0.f, 0.f, 0.f, 0.f);  // channels 4c..4c+3, for the dot products
-    float gs[4] = {0.f, 0.f, 0.f, 0.f};           // channels c, c+G, c+2G, c+3G, for the scatter
+    // The lane's grad_out row in two arrangements: channels 4c..4c+3 for the dot
+    // products and channels c, c+G, c+2G, c+3G for the scatter.  Both are read
+    // through buffer loads: with plain pointer loads the load/store vectorizer
+    // of the ROCm 7.2 compiler merged the float4's last element into the strided
+    // loads' address chain (reading channel c+3 instead of 4c+3 for G = 2).
+    float4 g4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    float gs[4] = {0.f, 0.f, 0.f, 0.f};
     if (it < nitems) {
-        const float *gp = grad_out + ((size_t)b * NqM + item0 + it) * D;
-        g4 = reinterpret_cast<const float4 *>(gp)[c];
+        const rsrc_t go = make_rsrc(grad_out + ((size_t)b * NqM + item0) * D,
+                                    (uint32_t)(nitems * D * 4));
+        const uint32_t row = (uint32_t)(it * D) * 4u;
+        auto u = __builtin_amdgcn_raw_buffer_load_b128(go, (int)(row + 16u * c), 0, 0);
+        g4 = make_float4(__uint_as_float(u[0]), __uint_as_float(u[1]), __uint_as_float(u[2]),
+                         __uint_as_float(u[3]));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) gs[i] = gp[c + i * G];
+        for (int i = 0; i < 4; ++i)
+            gs[i] = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(go, (int)(row + 4u * (c + i * G)), 0, 0));
     }
 
     for (int j0 = 0; j0 < LK; j0 += dm.PC) {
