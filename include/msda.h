@@ -34,9 +34,9 @@
  *
  * Memory and ownership.  Every tensor pointer, spatial_shapes and
  * level_start_index included, is a DEVICE pointer on the current HIP device;
- * the caller allocates and owns all of them.  The library allocates nothing,
- * frees nothing and keeps no state between calls.  Outputs must not alias
- * inputs.
+ * the caller allocates and owns all of them, and the backward's scratch
+ * workspace too.  The library allocates nothing, frees nothing and keeps no
+ * state between calls.  Outputs must not alias inputs.
  *
  * Streams and errors.  `stream` is a hipStream_t (NULL = the null stream).
  * Work is enqueued on it and the call returns without synchronizing; a
@@ -57,6 +57,7 @@
 #ifndef MSDA_H
 #define MSDA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -69,7 +70,8 @@ typedef enum msda_status {
     MSDA_ERR_SHAPE = -2,       /* sizes are negative or inconsistent                  */
     MSDA_ERR_DTYPE = -3,       /* value_dtype is not an msda_dtype                    */
     MSDA_ERR_UNSUPPORTED = -4, /* valid but outside the limits above (D, L, size)     */
-    MSDA_ERR_HIP = -5          /* the HIP runtime refused a launch (see msda_last_hip_error) */
+    MSDA_ERR_HIP = -5,         /* the HIP runtime refused a launch (see msda_last_hip_error) */
+    MSDA_ERR_WORKSPACE = -6    /* workspace too small or not 256-byte aligned             */
 } msda_status;
 
 typedef enum msda_dtype {
@@ -91,6 +93,15 @@ msda_status msda_forward(const void *value, int value_dtype,
                          int64_t L, int64_t K, void *stream);
 
 /*
+ * Bytes of device workspace msda_backward needs for these sizes (0 when
+ * nothing is launched or the sizes are invalid).  It depends on the sizes
+ * only, not on the level table, and is at most about 16 bytes per sampling
+ * point plus 12 bytes per 8x8 value tile and head.
+ */
+size_t msda_backward_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
+                                    int64_t L, int64_t K);
+
+/*
  * Backward of msda_forward for the upstream gradient grad_out.  The pages give
  * no formulas (first page, section 2.3 says the interpolation is differentiable
  * so the gradient reaches the offsets); these are the exact derivatives of the
@@ -99,13 +110,20 @@ msda_status msda_forward(const void *value, int value_dtype,
  *   grad_attn_weight = sum_d g_d * sum_c w_c v_c,d
  *   grad_loc.x = A * W_l * sum_d g_d * ((1-fy)(v_TR - v_TL) + fy (v_BR - v_BL))_d
  *   grad_loc.y = A * H_l * sum_d g_d * ((1-fx)(v_BL - v_TL) + fx (v_BR - v_TR))_d
- *   grad_value[neighbour c] += A * w_c * g            (scatter-add, fp32 atomics)
+ *   grad_value[neighbour c] += A * w_c * g             (summed over all points)
  * At an integer pixel coordinate the derivative is the one of the cell
  * [x0, x0+1) chosen by the floor.
+ *
+ * workspace: a DEVICE buffer of at least msda_backward_workspace_size(...)
+ * bytes, 256-byte aligned, owned by the caller; its contents on entry do not
+ * matter and are clobbered.  Calls that overlap in time (other streams) need
+ * separate workspaces.
+ *
  * grad_value is overwritten (zero-filled first, on `stream`) unless flags has
- * MSDA_BWD_ACCUMULATE.  Its summation order is not fixed, so repeated calls
- * may differ in the last bits.  grad_sampling_loc and grad_attn_weight are
- * overwritten and deterministic.
+ * MSDA_BWD_ACCUMULATE, in which case the gradient is added to it.  Its
+ * summation order is not fixed, so repeated calls may differ in the last
+ * bits.  grad_sampling_loc and grad_attn_weight are overwritten and
+ * deterministic.
  */
 msda_status msda_backward(const void *value, int value_dtype,
                           const int64_t *spatial_shapes, const int64_t *level_start_index,
@@ -113,7 +131,8 @@ msda_status msda_backward(const void *value, int value_dtype,
                           const float *grad_out, float *grad_value,
                           float *grad_sampling_loc, float *grad_attn_weight,
                           int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
-                          int64_t L, int64_t K, uint32_t flags, void *stream);
+                          int64_t L, int64_t K, void *workspace, size_t workspace_bytes,
+                          uint32_t flags, void *stream);
 
 /*
  * Pure host check of the sizes and of a HOST copy of the level table:

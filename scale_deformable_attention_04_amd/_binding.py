@@ -22,12 +22,13 @@ MSDA_ERR_SHAPE = -2
 MSDA_ERR_DTYPE = -3
 MSDA_ERR_UNSUPPORTED = -4
 MSDA_ERR_HIP = -5
+MSDA_ERR_WORKSPACE = -6
 MSDA_F32 = 0
 MSDA_BF16 = 1
 MSDA_BWD_ACCUMULATE = 1
 
-EXPORTED = ("msda_forward", "msda_backward", "msda_validate_host", "msda_status_string",
-            "msda_last_hip_error")
+EXPORTED = ("msda_forward", "msda_backward_workspace_size", "msda_backward",
+            "msda_validate_host", "msda_status_string", "msda_last_hip_error")
 
 _lib = None
 
@@ -53,8 +54,11 @@ def load():
     p, i64, ci, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32
     lib.msda_forward.argtypes = [p, ci, p, p, p, p, p] + [i64] * 7 + [p]
     lib.msda_forward.restype = ci
-    lib.msda_backward.argtypes = [p, ci, p, p, p, p, p, p, p, p] + [i64] * 7 + [u32, p]
+    lib.msda_backward.argtypes = ([p, ci, p, p, p, p, p, p, p, p] + [i64] * 7 +
+                                  [p, ctypes.c_size_t, u32, p])
     lib.msda_backward.restype = ci
+    lib.msda_backward_workspace_size.argtypes = [i64] * 7
+    lib.msda_backward_workspace_size.restype = ctypes.c_size_t
     lib.msda_validate_host.argtypes = [p, p] + [i64] * 7
     lib.msda_validate_host.restype = ci
     lib.msda_status_string.argtypes = [ci]
@@ -114,6 +118,26 @@ def validate_host(spatial_shapes, level_start_index, B, Nv, Nq, M, D, L, K) -> i
     return int(load().msda_validate_host(_ptr(ss), _ptr(st), B, Nv, Nq, M, D, L, K))
 
 
+_workspaces = {}
+
+
+def workspace_size(B, Nv, Nq, M, D, L, K) -> int:
+    """msda_backward_workspace_size: bytes of scratch the backward needs."""
+    return int(load().msda_backward_workspace_size(B, Nv, Nq, M, D, L, K))
+
+
+def _workspace(dev: torch.device, nbytes: int) -> Optional[torch.Tensor]:
+    """A cached device buffer of at least nbytes (256-byte aligned, torch-owned)."""
+    if nbytes == 0:
+        return None
+    key = (dev.type, dev.index)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        _workspaces[key] = ws
+    return ws
+
+
 def _check_inputs(value, spatial_shapes, level_start_index, sampling_loc, attn_weight, validate):
     dev = value.device
     if dev.type != "cuda":
@@ -161,11 +185,15 @@ def backward(value: torch.Tensor, spatial_shapes: torch.Tensor, level_start_inde
              grad_value: Optional[torch.Tensor] = None,
              grad_sampling_loc: Optional[torch.Tensor] = None,
              grad_attn_weight: Optional[torch.Tensor] = None,
-             accumulate: bool = False, validate: bool = True
+             accumulate: bool = False, validate: bool = True,
+             workspace: Optional[torch.Tensor] = None
              ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """msda_backward: (grad_value fp32 [B,Nv,M,D], grad_sampling_loc, grad_attn_weight).
 
-    accumulate=True adds into the given grad_value instead of overwriting it."""
+    accumulate=True adds into the given grad_value instead of overwriting it.
+    workspace: a uint8 device tensor of at least workspace_size(...) bytes; by
+    default a per-device buffer cached by this module is used (calls on
+    different streams that overlap in time must pass their own)."""
     lib = load()
     dev, (B, Nv, Nq, M, D, L, K) = _check_inputs(value, spatial_shapes, level_start_index,
                                                 sampling_loc, attn_weight, validate)
@@ -185,13 +213,19 @@ def backward(value: torch.Tensor, spatial_shapes: torch.Tensor, level_start_inde
     else:
         _need(grad_attn_weight, "grad_attn_weight", torch.float32, dev, attn_weight.shape)
     flags = MSDA_BWD_ACCUMULATE if accumulate else 0
+    need = workspace_size(B, Nv, Nq, M, D, L, K)
+    if workspace is None:
+        workspace = _workspace(dev, need)
+    elif workspace.device != dev or workspace.dtype != torch.uint8 or workspace.numel() < need:
+        raise ValueError(f"workspace must be a uint8 tensor on {dev} of >= {need} bytes")
+    ws_bytes = workspace.numel() if workspace is not None else 0
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         rc = lib.msda_backward(_ptr(value), _dtype_code(value), _ptr(spatial_shapes),
                                _ptr(level_start_index), _ptr(sampling_loc), _ptr(attn_weight),
                                _ptr(grad_out), _ptr(grad_value), _ptr(grad_sampling_loc),
-                               _ptr(grad_attn_weight), B, Nv, Nq, M, D, L, K, flags,
-                               ctypes.c_void_p(stream))
+                               _ptr(grad_attn_weight), B, Nv, Nq, M, D, L, K,
+                               _ptr(workspace), ws_bytes, flags, ctypes.c_void_p(stream))
     if rc != MSDA_OK:
         raise MSDAError(rc, "msda_backward")
     return grad_value, grad_sampling_loc, grad_attn_weight

@@ -2,29 +2,42 @@
 // deformable attention (MSDeformAttn) sampling core.  The operation, layouts
 // and error behaviour are specified in include/msda.h.
 //
-// Work decomposition (both passes).  An "item" is one (batch, query, head);
-// it owns L*K sampling points and D output channels.  A group of G = D/4
-// lanes serves one item, lane c holding channels 4c..4c+3, so every
-// neighbour fetch of a point is one coalesced read of the head's row of D
-// values (16 bytes per lane for fp32, 8 for bf16).  A 256-thread workgroup
-// serves IPB = 256/G consecutive items of one batch and walks their points in
-// chunks:
-//   phase 1  one thread per point: pixel coordinate, floor, the four
-//            neighbours' row offsets and bilinear weights, into LDS;
-//   phase 2  one lane group per item: fetch the four rows of every point and
-//            accumulate (forward), or form the four <grad_out, row> dot
-//            products, reduce them across the group with DPP, and scatter
-//            A*w*grad_out into grad_value with fp32 atomics (backward);
-//   phase 3  (backward) one thread per point: grad_attn_weight and
-//            grad_sampling_loc from the reduced dot products.
-// so the per-point coordinate work is done once per point rather than once
-// per lane.
+// Vocabulary.  An "item" is one (batch b, query q, head m); it owns L*K
+// sampling points and D channels.  A group of G = D/4 lanes serves one item,
+// lane c holding channels 4c..4c+3, so each neighbour fetch of a point is one
+// coalesced read of the head's row of D values (16 bytes per lane for fp32,
+// 8 for bf16).  Per-point coordinate work (pixel coordinate, floor, the four
+// neighbours' offsets and weights) is done once per point, by one thread,
+// into LDS, and the lane groups read it from there.
+//
+// Forward (msda_fwd_kernel): per item, sum over its points of A * bilinear
+// sample, accumulated in registers, one store per item.
+//
+// Backward (msda_backward) runs as a pipeline on the caller's stream:
+//   1. bwd_dots_kernel: per point the four <grad_out, neighbour row> dot
+//      products, reduced across the lane group with DPP, give
+//      grad_attn_weight and grad_sampling_loc.  The same pass counts, per
+//      8x8-pixel tile of grad_value ("bin"), how many points have a
+//      neighbour in it (LDS histogram, one global add per bin per workgroup).
+//   2. bin_scan_kernel: exclusive scan of the counts -> bin offsets, and a
+//      work list of (bin, chunk of at most kChunk points).
+//   3. bin_scatter_kernel: every point's index is written into each bin it
+//      touches (LDS ranks, one global reservation per bin per workgroup).
+//   4. grad_value_tile_kernel: per work item, the points of the chunk push
+//      A * w * grad_out into private LDS copies of the 8x8xD tile -- each
+//      half-wave (or wave) owns one copy, so plain read-modify-writes never
+//      race -- then the copies are summed and every pixel is written once.
+//      Only bins split over several chunks add into grad_value atomically.
+// fp32 atomics on this chip run at a few hundred G lane-ops/s whether they
+// target LDS or memory, so scattering the 4*D contributions of every point
+// with atomics would cost milliseconds at the encoder shape; the binned
+// pipeline replaces them with integer LDS atomics and plain LDS traffic.
 //
 // value and grad_value are addressed through raw buffer descriptors whose
 // size is the batch slice.  A neighbour outside the map gets the offset
-// kOOB, beyond every slice, so its fetch returns zeros and its atomic is
-// dropped by the hardware range check instead of needing a branch.  The same
-// check keeps an inconsistent level table from touching other memory.
+// kOOB, beyond every slice, so its fetch returns zeros without a branch; the
+// same range check keeps an inconsistent level table from touching other
+// memory.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -38,6 +51,14 @@ constexpr int kMaxLevels = 16;
 constexpr uint32_t kOOB = 0x80000000u;     // byte offset past every slice (slices < 2^31 B)
 constexpr int kRsrcWord3 = 0x00020000;     // gfx9 buffer descriptor word 3 (raw, 32-bit data)
 constexpr int kSetupLdsBytes = 36 * 1024;  // per-workgroup budget for the point tables
+constexpr int kTileShift = 3;              // grad_value tiles of 8x8 pixels
+constexpr int kTile = 1 << kTileShift;
+constexpr int kTilePx = kTile * kTile;
+constexpr int kChunk = 2048;               // points per grad_value work item, at most
+constexpr int kHistLds = 4096;             // bins of one (batch, head) kept in an LDS histogram
+constexpr int kScatterQueries = 64;        // queries per scatter workgroup
+constexpr int kScanThreads = 1024;
+constexpr int kTileGrid = 1024;            // persistent workgroups of the tile kernel
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
@@ -67,10 +88,6 @@ template <> struct Row4<uint16_t> {
     }
 };
 
-__device__ __forceinline__ void atomic_add(rsrc_t r, uint32_t off, float v) {
-    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, (int)off, 0, 0);
-}
-
 template <int CTRL> __device__ __forceinline__ float dpp(float v) {
     return __builtin_bit_cast(
         float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
@@ -88,18 +105,43 @@ template <int G> __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
-// Level table entry staged in LDS: (H, W, start, 0).  A level whose pixels do
-// not fit inside value becomes (0, 0, 0, 0), which puts every neighbour
-// outside the map.
-__device__ __forceinline__ void stage_levels(int4 *s_lvl, const int64_t *shapes,
-                                             const int64_t *starts, int L, int Nv) {
+// Level table staged in LDS.  lvl[l] = (H, W, start, first bin of the level);
+// a level whose pixels do not fit inside value, or whose tiles would not fit
+// the bin stride, becomes (0, 0, 0, first bin) and has no pixel and no bin.
+struct LevelLds {
+    int4 lvl[kMaxLevels];
+    int tw[kMaxLevels];  // tiles along W
+    int nbins;           // bins of one (batch, head)
+};
+
+__device__ __forceinline__ void stage_levels(LevelLds *s, const int64_t *shapes,
+                                             const int64_t *starts, int L, int Nv, int nb_max) {
     const int t = threadIdx.x;
     if (t < L) {
         const int64_t H = shapes[2 * t], W = shapes[2 * t + 1], S = starts[t];
         const bool ok = H >= 1 && W >= 1 && H <= Nv && W <= Nv && S >= 0 && S <= Nv &&
                         H * W <= (int64_t)Nv - S;
-        s_lvl[t] = ok ? make_int4((int)H, (int)W, (int)S, 0) : make_int4(0, 0, 0, 0);
+        s->lvl[t] = ok ? make_int4((int)H, (int)W, (int)S, 0) : make_int4(0, 0, 0, 0);
     }
+    __syncthreads();
+    if (t == 0) {
+        int tb = 0;
+        for (int l = 0; l < L; ++l) {
+            int4 v = s->lvl[l];
+            const int tw = (v.y + kTile - 1) >> kTileShift, th = (v.x + kTile - 1) >> kTileShift;
+            int n = tw * th;
+            if (n > nb_max - tb) {  // keep every bin inside the caller's workspace
+                v = make_int4(0, 0, 0, 0);
+                n = 0;
+            }
+            v.w = tb;
+            s->lvl[l] = v;
+            s->tw[l] = n ? tw : 0;
+            tb += n;
+        }
+        s->nbins = tb;
+    }
+    __syncthreads();
 }
 
 // Neighbours of one sampling point, in the order TL (x0,y0), TR (x0+1,y0),
@@ -108,6 +150,7 @@ struct Neighbours {
     uint4 off;       // fp32-unit byte offsets of the rows in the batch slice, or kOOB
     float4 w;        // bilinear weights, 0 outside the map
     float fx, fy;    // fractional parts of the pixel coordinate
+    int xi, yi;      // x0, y0 clamped to [-1, W] x [-1, H]
     uint32_t valid;  // bit c: neighbour c inside the map
 };
 
@@ -127,9 +170,9 @@ __device__ __forceinline__ Neighbours neighbours(float u, float v, int4 lvl, uin
     const bool vy0 = y0 >= 0.f && y0 <= (float)(H - 1);
     const bool vy1 = y0 >= -1.f && y0 <= (float)(H - 2);
     // clamp first so the conversion is defined for every input
-    const int xi = (int)fminf(fmaxf(x0, -1.f), (float)W);
-    const int yi = (int)fminf(fmaxf(y0, -1.f), (float)H);
-    const int pTL = S + yi * W + xi;
+    n.xi = (int)fminf(fmaxf(x0, -1.f), (float)W);
+    n.yi = (int)fminf(fmaxf(y0, -1.f), (float)H);
+    const int pTL = S + n.yi * W + n.xi;
     const uint32_t oTL = (uint32_t)pTL * row_stride + head_off;
     const bool vTL = vx0 && vy0, vTR = vx1 && vy0, vBL = vx0 && vy1, vBR = vx1 && vy1;
     n.off.x = vTL ? oTL : kOOB;
@@ -145,6 +188,23 @@ __device__ __forceinline__ Neighbours neighbours(float u, float v, int4 lvl, uin
     return n;
 }
 
+// The distinct grad_value tiles (bins, relative to the (batch, head)) that
+// hold at least one of the point's neighbours inside the map.
+__device__ __forceinline__ int point_bins(const Neighbours &n, int4 lvl, int tw, int bins[4]) {
+    if (!n.valid) return 0;
+    const int tx0 = n.xi >> kTileShift, tx1 = (n.xi + 1) >> kTileShift;
+    const int ty0 = n.yi >> kTileShift, ty1 = (n.yi + 1) >> kTileShift;
+    const bool sx = tx1 != tx0, sy = ty1 != ty0;
+    const bool vTL = n.valid & 1u, vTR = n.valid & 2u, vBL = n.valid & 4u, vBR = n.valid & 8u;
+    int k = 0;
+    if (vTL || (!sx && vTR) || (!sy && vBL) || (!sx && !sy && vBR))
+        bins[k++] = lvl.w + ty0 * tw + tx0;
+    if (sx && (vTR || (!sy && vBR))) bins[k++] = lvl.w + ty0 * tw + tx1;
+    if (sy && (vBL || (!sx && vBR))) bins[k++] = lvl.w + ty1 * tw + tx0;
+    if (sx && sy && vBR) bins[k++] = lvl.w + ty1 * tw + tx1;
+    return k;
+}
+
 __device__ __forceinline__ void fma4(float4 &acc, float w, const float4 &v) {
     acc.x = __builtin_fmaf(w, v.x, acc.x);
     acc.y = __builtin_fmaf(w, v.y, acc.y);
@@ -156,11 +216,27 @@ __device__ __forceinline__ float dot4(const float4 &a, const float4 &b) {
     return __builtin_fmaf(a.w, b.w, __builtin_fmaf(a.z, b.z, __builtin_fmaf(a.y, b.y, a.x * b.x)));
 }
 
+__device__ __forceinline__ float pick(const float4 &v, int c) {
+    return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
+}
+
 struct Dims {
     int Nv, Nq, M, L, K;
-    int PC;   // points per chunk
-    int PS;   // LDS stride per item (PC rounded to an odd count, for bank spread)
-    int b0;   // first batch of this launch
+    int PC;      // points per chunk (point-table kernels)
+    int PS;      // LDS stride per item (PC rounded to an odd count, for bank spread)
+    int b0;      // first batch of this launch
+    int nb_max;  // bin stride per (batch, head) in the workspace
+    int accumulate;  // grad_value already holds a gradient to add to
+};
+
+// Workspace of the backward pipeline (all 32-bit words).
+struct Work {
+    uint32_t *counts;      // [B*M*nb_max] points per bin
+    uint32_t *start;       // [B*M*nb_max] first entry of each bin in `sorted`
+    uint32_t *cursor;      // [B*M*nb_max] next free entry while scattering
+    uint2 *items;          // [work_max] (bin, chunk)
+    uint32_t *work_total;  // [1]
+    uint32_t *sorted;      // [4 * points] point indices grouped by bin
 };
 
 // ---------------------------------------------------------------------------
@@ -173,9 +249,9 @@ msda_fwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
                 const float *__restrict__ attn, float *__restrict__ out, Dims dm) {
     constexpr int G = D / 4;
     constexpr int IPB = kThreads / G;
+    __shared__ LevelLds s_lv;
     extern __shared__ __align__(16) unsigned char smem[];
-    int4 *s_lvl = reinterpret_cast<int4 *>(smem);
-    uint4 *s_off = reinterpret_cast<uint4 *>(smem + kMaxLevels * sizeof(int4));
+    uint4 *s_off = reinterpret_cast<uint4 *>(smem);
     float4 *s_w = reinterpret_cast<float4 *>(s_off + IPB * dm.PS);
 
     const int M = dm.M, K = dm.K, LK = dm.L * dm.K;
@@ -185,7 +261,7 @@ msda_fwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
     const int nitems = min(IPB, NqM - item0);
     const uint32_t row_stride = (uint32_t)M * D * 4u;
 
-    stage_levels(s_lvl, shapes, starts, dm.L, dm.Nv);
+    stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, 0x7fffffff);
 
     const size_t slice = (size_t)dm.Nv * M * D;
     const rsrc_t vr = make_rsrc(value + (size_t)b * slice, (uint32_t)(slice * sizeof(VT)));
@@ -196,14 +272,15 @@ msda_fwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
 
     for (int j0 = 0; j0 < LK; j0 += dm.PC) {
         const int pc = min(dm.PC, LK - j0);
-        __syncthreads();  // level table staged / previous chunk consumed
+        if (j0) __syncthreads();  // previous chunk consumed
         for (int idx = threadIdx.x; idx < nitems * pc; idx += kThreads) {
             const int i1 = idx / pc, jj = idx - i1 * pc, j = j0 + jj;
             const size_t p = pt0 + (size_t)i1 * LK + j;
             const float2 uv = reinterpret_cast<const float2 *>(loc)[p];
             const float A = attn[p];
             const int m = (item0 + i1) % M;
-            Neighbours n = neighbours(uv.x, uv.y, s_lvl[j / K], row_stride, (uint32_t)m * D * 4u);
+            Neighbours n = neighbours(uv.x, uv.y, s_lv.lvl[j / K], row_stride,
+                                      (uint32_t)m * D * 4u);
             s_off[i1 * dm.PS + jj] = n.off;
             // skip outside neighbours outright, so a non-finite A cannot leak through them
             s_w[i1 * dm.PS + jj] = make_float4((n.valid & 1u) ? A * n.w.x : 0.f,
@@ -237,72 +314,82 @@ msda_fwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
 }
 
 // ---------------------------------------------------------------------------
-// backward
+// backward 1: grad_attn_weight, grad_sampling_loc, bin counts
+// Workgroup = (batch b, head m, IPB consecutive queries).
 // ---------------------------------------------------------------------------
 template <int D, typename VT>
 __global__ void __launch_bounds__(kThreads)
-msda_bwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes,
+bwd_dots_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes,
                 const int64_t *__restrict__ starts, const float *__restrict__ loc,
                 const float *__restrict__ attn, const float *__restrict__ grad_out,
-                float *__restrict__ grad_value, float *__restrict__ grad_loc,
-                float *__restrict__ grad_attn, Dims dm) {
+                float *__restrict__ grad_loc, float *__restrict__ grad_attn,
+                uint32_t *__restrict__ counts, int hist_cap, Dims dm) {
     constexpr int G = D / 4;
     constexpr int IPB = kThreads / G;
+    __shared__ LevelLds s_lv;
     extern __shared__ __align__(16) unsigned char smem[];
-    int4 *s_lvl = reinterpret_cast<int4 *>(smem);
-    uint4 *s_off = reinterpret_cast<uint4 *>(smem + kMaxLevels * sizeof(int4));
+    uint4 *s_off = reinterpret_cast<uint4 *>(smem);
     float4 *s_w = reinterpret_cast<float4 *>(s_off + IPB * dm.PS);
-    float4 *s_aux = s_w + IPB * dm.PS;   // (fx, fy, A, valid bits)
+    float4 *s_aux = s_w + IPB * dm.PS;    // (fx, fy, A, valid bits)
     float4 *s_dot = s_aux + IPB * dm.PS;  // <g, row> of the four neighbours
+    uint32_t *s_hist = reinterpret_cast<uint32_t *>(s_dot + IPB * dm.PS);
 
-    const int M = dm.M, K = dm.K, LK = dm.L * dm.K;
-    const int NqM = dm.Nq * M;
-    const int b = blockIdx.y + dm.b0;
-    const int item0 = blockIdx.x * IPB;
-    const int nitems = min(IPB, NqM - item0);
+    const int M = dm.M, K = dm.K, LK = dm.L * dm.K, Nq = dm.Nq;
+    const int m = blockIdx.y;
+    const int b = blockIdx.z + dm.b0;
+    const int q0 = blockIdx.x * IPB;
+    const int nitems = min(IPB, Nq - q0);
     const uint32_t row_stride = (uint32_t)M * D * 4u;
+    const uint32_t head_off = (uint32_t)m * D * 4u;
 
-    stage_levels(s_lvl, shapes, starts, dm.L, dm.Nv);
+    stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
+    const int nbins = s_lv.nbins;
+    const bool lds_hist = nbins <= hist_cap;
+    uint32_t *gcount = counts + (size_t)(b * M + m) * dm.nb_max;
+    if (lds_hist)
+        for (int i = threadIdx.x; i < nbins; i += kThreads) s_hist[i] = 0u;
 
     const size_t slice = (size_t)dm.Nv * M * D;
     const rsrc_t vr = make_rsrc(value + (size_t)b * slice, (uint32_t)(slice * sizeof(VT)));
-    const rsrc_t gr = make_rsrc(grad_value + (size_t)b * slice, (uint32_t)(slice * 4u));
-    const size_t pt0 = ((size_t)b * NqM + item0) * LK;
+    const size_t row0 = ((size_t)b * Nq + q0) * M + m;  // item row of query q0
+    const size_t pt0 = row0 * LK;
 
     const int it = threadIdx.x / G, c = threadIdx.x % G;
-    // The lane's grad_out row in two arrangements: channels 4c..4c+3 for the dot
-    // products and channels c, c+G, c+2G, c+3G for the scatter.  Both are read
-    // through buffer loads: with plain pointer loads the load/store vectorizer
-    // of the ROCm 7.2 compiler merged the float4's last element into the strided
-    // loads' address chain (reading channel c+3 instead of 4c+3 for G = 2).
+    // The lane's grad_out row is read through a buffer load: with plain pointer
+    // loads the load/store vectorizer of the ROCm 7.2 compiler merged a float4
+    // element into a neighbouring scalar load's address chain (wrong channel).
     float4 g4 = make_float4(0.f, 0.f, 0.f, 0.f);
-    float gs[4] = {0.f, 0.f, 0.f, 0.f};
     if (it < nitems) {
-        const rsrc_t go = make_rsrc(grad_out + ((size_t)b * NqM + item0) * D,
-                                    (uint32_t)(nitems * D * 4));
-        const uint32_t row = (uint32_t)(it * D) * 4u;
-        auto u = __builtin_amdgcn_raw_buffer_load_b128(go, (int)(row + 16u * c), 0, 0);
+        const rsrc_t go = make_rsrc(grad_out + row0 * D,
+                                    (uint32_t)(((size_t)(nitems - 1) * M + 1) * D * 4));
+        auto u = __builtin_amdgcn_raw_buffer_load_b128(
+            go, (int)((uint32_t)it * M * D * 4u + 16u * c), 0, 0);
         g4 = make_float4(__uint_as_float(u[0]), __uint_as_float(u[1]), __uint_as_float(u[2]),
                          __uint_as_float(u[3]));
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            gs[i] = __uint_as_float(
-                __builtin_amdgcn_raw_buffer_load_b32(go, (int)(row + 4u * (c + i * G)), 0, 0));
     }
 
     for (int j0 = 0; j0 < LK; j0 += dm.PC) {
         const int pc = min(dm.PC, LK - j0);
-        __syncthreads();
+        __syncthreads();  // histogram zeroed / previous chunk consumed
         for (int idx = threadIdx.x; idx < nitems * pc; idx += kThreads) {
             const int i1 = idx / pc, jj = idx - i1 * pc, j = j0 + jj;
-            const size_t p = pt0 + (size_t)i1 * LK + j;
+            const size_t p = pt0 + (size_t)i1 * M * LK + j;
             const float2 uv = reinterpret_cast<const float2 *>(loc)[p];
             const float A = attn[p];
-            const int m = (item0 + i1) % M;
-            Neighbours n = neighbours(uv.x, uv.y, s_lvl[j / K], row_stride, (uint32_t)m * D * 4u);
+            const int l = j / K;
+            const int4 lvl = s_lv.lvl[l];
+            Neighbours n = neighbours(uv.x, uv.y, lvl, row_stride, head_off);
             s_off[i1 * dm.PS + jj] = n.off;
             s_w[i1 * dm.PS + jj] = n.w;
             s_aux[i1 * dm.PS + jj] = make_float4(n.fx, n.fy, A, __uint_as_float(n.valid));
+            int bins[4];
+            const int nb = point_bins(n, lvl, s_lv.tw[l], bins);
+            for (int k = 0; k < nb; ++k) {
+                if (lds_hist)
+                    atomicAdd(&s_hist[bins[k]], 1u);
+                else
+                    atomicAdd(&gcount[bins[k]], 1u);
+            }
         }
         __syncthreads();
         if (it < nitems) {
@@ -310,8 +397,6 @@ msda_bwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
 #pragma unroll 2
             for (int jj = 0; jj < pc; ++jj) {
                 const uint4 o = s_off[base + jj];
-                const float4 w = s_w[base + jj];
-                const float A = s_aux[base + jj].z;
                 const float4 v0 = Row4<VT>::load(vr, o.x, 4 * c);
                 const float4 v1 = Row4<VT>::load(vr, o.y, 4 * c);
                 const float4 v2 = Row4<VT>::load(vr, o.z, 4 * c);
@@ -321,25 +406,16 @@ msda_bwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
                 const float d2 = group_sum<G>(dot4(g4, v2));
                 const float d3 = group_sum<G>(dot4(g4, v3));
                 if (c == 0) s_dot[base + jj] = make_float4(d0, d1, d2, d3);
-                const float a0 = A * w.x, a1 = A * w.y, a2 = A * w.z, a3 = A * w.w;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t ch = 4u * (uint32_t)(c + i * G);
-                    atomic_add(gr, o.x + ch, a0 * gs[i]);
-                    atomic_add(gr, o.y + ch, a1 * gs[i]);
-                    atomic_add(gr, o.z + ch, a2 * gs[i]);
-                    atomic_add(gr, o.w + ch, a3 * gs[i]);
-                }
             }
         }
         __syncthreads();
         for (int idx = threadIdx.x; idx < nitems * pc; idx += kThreads) {
             const int i1 = idx / pc, jj = idx - i1 * pc, j = j0 + jj;
-            const size_t p = pt0 + (size_t)i1 * LK + j;
+            const size_t p = pt0 + (size_t)i1 * M * LK + j;
             const float4 d = s_dot[i1 * dm.PS + jj];
             const float4 w = s_w[i1 * dm.PS + jj];
             const float4 ax = s_aux[i1 * dm.PS + jj];
-            const int4 lvl = s_lvl[j / K];
+            const int4 lvl = s_lv.lvl[j / K];
             float ga = 0.f, gx = 0.f, gy = 0.f;
             if (__float_as_uint(ax.w) != 0u) {
                 const float fx = ax.x, fy = ax.y, A = ax.z;
@@ -350,6 +426,292 @@ msda_bwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
             grad_attn[p] = ga;
             reinterpret_cast<float2 *>(grad_loc)[p] = make_float2(gx, gy);
         }
+    }
+    if (lds_hist) {
+        __syncthreads();
+        for (int i = threadIdx.x; i < nbins; i += kThreads) {
+            const uint32_t v = s_hist[i];
+            if (v) atomicAdd(&gcount[i], v);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// backward 2: scan of the bin counts, work list of (bin, chunk)
+// One workgroup of kScanThreads; bins are visited in (batch, head, bin) order.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void block_exclusive_scan2(uint32_t &a, uint32_t &b, uint32_t *s_a,
+                                                      uint32_t *s_b, uint32_t &tot_a,
+                                                      uint32_t &tot_b) {
+    const int t = threadIdx.x;
+    s_a[t] = a;
+    s_b[t] = b;
+    __syncthreads();
+    for (int off = 1; off < kScanThreads; off <<= 1) {
+        const uint32_t xa = t >= off ? s_a[t - off] : 0u;
+        const uint32_t xb = t >= off ? s_b[t - off] : 0u;
+        __syncthreads();
+        s_a[t] += xa;
+        s_b[t] += xb;
+        __syncthreads();
+    }
+    tot_a = s_a[kScanThreads - 1];
+    tot_b = s_b[kScanThreads - 1];
+    a = s_a[t] - a;  // exclusive
+    b = s_b[t] - b;
+    __syncthreads();
+}
+
+__global__ void __launch_bounds__(kScanThreads)
+bin_scan_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ starts,
+                const uint32_t *__restrict__ counts, uint32_t *__restrict__ start,
+                uint32_t *__restrict__ cursor, uint2 *__restrict__ items,
+                uint32_t *__restrict__ work_total, int BM, Dims dm) {
+    constexpr int kPer = 8;
+    __shared__ LevelLds s_lv;
+    __shared__ uint32_t s_a[kScanThreads], s_b[kScanThreads];
+    stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
+    const int nbins = s_lv.nbins;
+    const int64_t n = (int64_t)BM * nbins;
+    uint32_t carry_e = 0, carry_c = 0;
+    for (int64_t base = 0; base < n; base += (int64_t)kScanThreads * kPer) {
+        uint32_t cnt[kPer], e = 0, ch = 0;
+        const int64_t g0 = base + (int64_t)threadIdx.x * kPer;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int64_t g = g0 + i;
+            cnt[i] = 0;
+            if (g < n) {
+                const int64_t bin = (g / nbins) * dm.nb_max + g % nbins;
+                cnt[i] = counts[bin];
+            }
+            e += cnt[i];
+            ch += (cnt[i] + kChunk - 1) / kChunk;
+        }
+        uint32_t tot_e, tot_c;
+        block_exclusive_scan2(e, ch, s_a, s_b, tot_e, tot_c);
+        e += carry_e;
+        ch += carry_c;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int64_t g = g0 + i;
+            if (g < n) {
+                const uint32_t bin = (uint32_t)((g / nbins) * dm.nb_max + g % nbins);
+                start[bin] = e;
+                cursor[bin] = e;
+                const uint32_t nch = (cnt[i] + kChunk - 1) / kChunk;
+                for (uint32_t k = 0; k < nch; ++k) items[ch + k] = make_uint2(bin, k);
+                e += cnt[i];
+                ch += nch;
+            }
+        }
+        carry_e += tot_e;
+        carry_c += tot_c;
+    }
+    if (threadIdx.x == 0) *work_total = carry_c;
+}
+
+// ---------------------------------------------------------------------------
+// backward 3: scatter point indices into their bins
+// Workgroup = (batch b, head m, kScatterQueries consecutive queries).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kThreads)
+bin_scatter_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ starts,
+                   const float *__restrict__ loc, uint32_t *__restrict__ cursor,
+                   uint32_t *__restrict__ sorted, int hist_cap, Dims dm) {
+    __shared__ LevelLds s_lv;
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint32_t *s_cnt = reinterpret_cast<uint32_t *>(smem);  // [hist_cap] counts, then ranks
+    uint32_t *s_base = s_cnt + hist_cap;                    // [hist_cap] reserved offsets
+
+    const int M = dm.M, K = dm.K, LK = dm.L * dm.K, Nq = dm.Nq;
+    const int m = blockIdx.y;
+    const int b = blockIdx.z + dm.b0;
+    const int q0 = blockIdx.x * kScatterQueries;
+    const int nq = min(kScatterQueries, Nq - q0);
+    const size_t row0 = ((size_t)b * Nq + q0) * M + m;
+    const int npts = nq * LK;
+
+    stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
+    const int nbins = s_lv.nbins;
+    uint32_t *gcur = cursor + (size_t)(b * M + m) * dm.nb_max;
+    if (nbins > hist_cap) {  // too many bins for LDS: reserve one slot at a time
+        for (int idx = threadIdx.x; idx < npts; idx += kThreads) {
+            const int i1 = idx / LK, j = idx - i1 * LK;
+            const size_t p = (row0 + (size_t)i1 * M) * LK + j;
+            const float2 uv = reinterpret_cast<const float2 *>(loc)[p];
+            const int l = j / K;
+            Neighbours n = neighbours(uv.x, uv.y, s_lv.lvl[l], 0u, 0u);
+            int bins[4];
+            const int nb = point_bins(n, s_lv.lvl[l], s_lv.tw[l], bins);
+            for (int k = 0; k < nb; ++k) sorted[atomicAdd(&gcur[bins[k]], 1u)] = (uint32_t)p;
+        }
+        return;
+    }
+    for (int i = threadIdx.x; i < nbins; i += kThreads) s_cnt[i] = 0u;
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < npts; idx += kThreads) {
+        const int i1 = idx / LK, j = idx - i1 * LK;
+        const size_t p = (row0 + (size_t)i1 * M) * LK + j;
+        const float2 uv = reinterpret_cast<const float2 *>(loc)[p];
+        const int l = j / K;
+        Neighbours n = neighbours(uv.x, uv.y, s_lv.lvl[l], 0u, 0u);
+        int bins[4];
+        const int nb = point_bins(n, s_lv.lvl[l], s_lv.tw[l], bins);
+        for (int k = 0; k < nb; ++k) atomicAdd(&s_cnt[bins[k]], 1u);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nbins; i += kThreads) {
+        const uint32_t v = s_cnt[i];
+        s_base[i] = v ? atomicAdd(&gcur[i], v) : 0u;
+        s_cnt[i] = 0u;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < npts; idx += kThreads) {
+        const int i1 = idx / LK, j = idx - i1 * LK;
+        const size_t p = (row0 + (size_t)i1 * M) * LK + j;
+        const float2 uv = reinterpret_cast<const float2 *>(loc)[p];
+        const int l = j / K;
+        Neighbours n = neighbours(uv.x, uv.y, s_lv.lvl[l], 0u, 0u);
+        int bins[4];
+        const int nb = point_bins(n, s_lv.lvl[l], s_lv.tw[l], bins);
+        for (int k = 0; k < nb; ++k)
+            sorted[s_base[bins[k]] + atomicAdd(&s_cnt[bins[k]], 1u)] = (uint32_t)p;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// backward 4: grad_value, one 8x8 tile (and chunk of its points) per work item
+//
+// The chunk's points are counting-sorted in LDS by the cell of their top-left
+// neighbour (a 9x9 grid: the tile plus one column and row before it).  Pixel
+// (x, y) of the tile receives from the points of four cells, in four roles:
+// top-left from cell (x, y), top-right from (x-1, y), bottom-left from
+// (x, y-1), bottom-right from (x-1, y-1).  A lane owns one (pixel, 4-channel
+// quad) and sums A * w * grad_out over those lists in registers, so no two
+// lanes ever add into the same value and the loop iterations are independent.
+// ---------------------------------------------------------------------------
+constexpr int kTileThreads = 512;
+constexpr int kCellsW = kTile + 1;
+constexpr int kCells = kCellsW * kCellsW;
+
+template <int D>
+__global__ void __launch_bounds__(kTileThreads)
+grad_value_tile_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ starts,
+                       const float *__restrict__ loc, const float *__restrict__ attn,
+                       const float *__restrict__ grad_out, const uint32_t *__restrict__ counts,
+                       const uint32_t *__restrict__ start, const uint2 *__restrict__ items,
+                       const uint32_t *__restrict__ work_total,
+                       const uint32_t *__restrict__ sorted, float *__restrict__ grad_value,
+                       Dims dm) {
+    constexpr int kQuads = D / 4;
+    constexpr int kPxPerPass = kTileThreads / kQuads < kTilePx ? kTileThreads / kQuads : kTilePx;
+    __shared__ LevelLds s_lv;
+    __shared__ float4 s_w[kChunk];       // A * bilinear weight of each neighbour
+    __shared__ uint32_t s_item[kChunk];  // (b, q, m) row of the point
+    __shared__ uint16_t s_cell[kChunk];  // cell of the point's top-left neighbour
+    __shared__ uint16_t s_ent[kChunk];   // points ordered by cell
+    __shared__ uint32_t s_cnt[kCells + 1];
+    __shared__ uint32_t s_cur[kCells];
+
+    const int M = dm.M, LK = dm.L * dm.K;
+    stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
+    const uint32_t total = *work_total;
+    const int tid = threadIdx.x;
+
+    for (uint32_t w = blockIdx.x; w < total; w += gridDim.x) {
+        const uint2 wk = items[w];
+        const uint32_t bin = wk.x;
+        const int bm = (int)(bin / (uint32_t)dm.nb_max);
+        const int lb = (int)(bin - (uint32_t)bm * dm.nb_max);
+        const int b = bm / M, m = bm - b * M;
+        int l = 0;
+        while (l + 1 < dm.L && s_lv.lvl[l + 1].w <= lb) ++l;
+        const int4 lvl = s_lv.lvl[l];
+        const int tw = s_lv.tw[l];
+        const int ty = (lb - lvl.w) / tw, tx = (lb - lvl.w) - ty * tw;
+        const int x0t = tx * kTile, y0t = ty * kTile;
+        const uint32_t cnt = counts[bin];
+        const uint32_t s0 = start[bin] + wk.y * kChunk;
+        const int n = (int)min((uint32_t)kChunk, cnt - wk.y * kChunk);
+        const bool whole = cnt <= (uint32_t)kChunk;
+
+        for (int i = tid; i < kCells; i += kTileThreads) s_cnt[i] = 0u;
+        __syncthreads();
+        for (int i = tid; i < n; i += kTileThreads) {
+            const uint32_t p = sorted[s0 + i];
+            const float2 uv = reinterpret_cast<const float2 *>(loc)[p];
+            const float A = attn[p];
+            const Neighbours nb = neighbours(uv.x, uv.y, lvl, 0u, 0u);
+            // a point of this bin has a neighbour inside the tile, so its
+            // top-left neighbour lies in the 9x9 cell grid
+            const int cx = nb.xi - x0t + 1, cy = nb.yi - y0t + 1;
+            const bool inside = cx >= 0 && cx < kCellsW && cy >= 0 && cy < kCellsW;
+            const int cell = inside ? cx + cy * kCellsW : 0;
+            s_cell[i] = (uint16_t)cell;
+            s_w[i] = inside ? make_float4(A * nb.w.x, A * nb.w.y, A * nb.w.z, A * nb.w.w)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+            s_item[i] = p / (uint32_t)LK;
+            atomicAdd(&s_cnt[cell], 1u);
+        }
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t acc = 0;
+            for (int c = 0; c < kCells; ++c) {
+                const uint32_t v = s_cnt[c];
+                s_cnt[c] = acc;
+                s_cur[c] = acc;
+                acc += v;
+            }
+            s_cnt[kCells] = acc;
+        }
+        __syncthreads();
+        for (int i = tid; i < n; i += kTileThreads)
+            s_ent[atomicAdd(&s_cur[s_cell[i]], 1u)] = (uint16_t)i;
+        __syncthreads();
+
+        const size_t slice = (size_t)dm.Nv * M * D;
+        float *gv = grad_value + (size_t)b * slice + (size_t)m * D;
+        for (int px0 = 0; px0 < kTilePx; px0 += kPxPerPass) {
+            const int px = px0 + tid / kQuads, q = tid % kQuads;
+            if (tid >= kPxPerPass * kQuads) continue;
+            const int x = px & (kTile - 1), y = px >> kTileShift;
+            const int gx = x0t + x, gy = y0t + y;
+            if (gy >= lvl.x || gx >= lvl.y) continue;
+            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int role = 0; role < 4; ++role) {
+                const int cell = (x - (role & 1) + 1) + (y - (role >> 1) + 1) * kCellsW;
+                const int e0 = (int)s_cnt[cell], e1 = (int)s_cnt[cell + 1];
+#pragma unroll 4
+                for (int e = e0; e < e1; ++e) {
+                    const int pt = s_ent[e];
+                    const float wgt = pick(s_w[pt], role);
+                    const float4 g =
+                        reinterpret_cast<const float4 *>(grad_out + (size_t)s_item[pt] * D)[q];
+                    fma4(acc, wgt, g);
+                }
+            }
+            float *dst = gv + (size_t)(lvl.z + gy * lvl.y + gx) * M * D + 4 * q;
+            if (whole) {
+                // this work item alone owns the pixel: plain read-add-write
+                float4 *d4 = reinterpret_cast<float4 *>(dst);
+                if (dm.accumulate) {
+                    const float4 o = *d4;
+                    acc.x += o.x;
+                    acc.y += o.y;
+                    acc.z += o.z;
+                    acc.w += o.w;
+                }
+                *d4 = acc;
+            } else {
+                atomicAdd(dst + 0, acc.x);
+                atomicAdd(dst + 1, acc.y);
+                atomicAdd(dst + 2, acc.z);
+                atomicAdd(dst + 3, acc.w);
+            }
+        }
+        __syncthreads();  // the tables are reused by the next work item
     }
 }
 
@@ -373,15 +735,53 @@ msda_status check_sizes(int value_dtype, int64_t B, int64_t Nv, int64_t Nq, int6
     if (value_dtype != MSDA_F32 && value_dtype != MSDA_BF16) return MSDA_ERR_DTYPE;
     if (B < 0 || Nv < 0 || Nq < 0 || M < 1 || D < 1 || L < 1 || K < 1) return MSDA_ERR_SHAPE;
     if (L > kMaxLevels || !supported_d(D)) return MSDA_ERR_UNSUPPORTED;
-    // one batch slice of grad_value (fp32) and of the point arrays must be 31-bit addressable
     const int64_t lim = (int64_t)1 << 31;
+    // the rows of one workgroup's queries stay 31-bit addressable
+    if (M > ((int64_t)1 << 20) / D) return MSDA_ERR_UNSUPPORTED;
+    // one batch slice of grad_value (fp32) and of the point arrays must be 31-bit addressable
     if (Nv > lim / (M * D * 4) || Nv * M * D * 4 >= lim) return MSDA_ERR_UNSUPPORTED;
     if (K > lim / L || Nq > lim / (M * L * K * 2) || Nq * M * L * K * 2 >= lim)
         return MSDA_ERR_UNSUPPORTED;
-    if (B > lim) return MSDA_ERR_UNSUPPORTED;
+    // the backward stores point indices of the whole problem, four per point, in 32 bits
+    if (B > 0 && Nq > 0 && B > (((int64_t)1 << 32) - 1) / (Nq * M * L * K * 4))
+        return MSDA_ERR_UNSUPPORTED;
     // one launch covers Nq*M items with D/4 lanes each: keep the grid under 2^31 threads
     if (Nq * M > lim / (D / 4)) return MSDA_ERR_UNSUPPORTED;
     return MSDA_OK;
+}
+
+// Upper bound of the number of 8x8 tiles over all levels, from Nv and L only:
+// sum ceil(H/8)*ceil(W/8) <= sum (HW + 7(H+W) + 49)/64 <= (15 Nv + 49 L)/64.
+int64_t bins_bound(int64_t Nv, int64_t L) { return (15 * Nv + 49 * L) / 64 + 1; }
+
+struct WorkLayout {
+    int64_t nb_max, bm_bins, work_max, sorted_max;
+    size_t off_counts, off_start, off_cursor, off_items, off_total, off_sorted, bytes;
+};
+
+WorkLayout work_layout(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t L, int64_t K) {
+    WorkLayout w;
+    w.nb_max = bins_bound(Nv, L);
+    w.bm_bins = B * M * w.nb_max;
+    const int64_t pts = B * Nq * M * L * K;
+    w.sorted_max = 4 * pts;
+    w.work_max = w.bm_bins + (w.sorted_max + kChunk - 1) / kChunk;
+    auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    size_t o = 0;
+    w.off_counts = o;
+    o = align(o + 4 * (size_t)w.bm_bins);
+    w.off_start = o;
+    o = align(o + 4 * (size_t)w.bm_bins);
+    w.off_cursor = o;
+    o = align(o + 4 * (size_t)w.bm_bins);
+    w.off_items = o;
+    o = align(o + 8 * (size_t)w.work_max);
+    w.off_total = o;
+    o = align(o + 4);
+    w.off_sorted = o;
+    o = align(o + 4 * (size_t)w.sorted_max);
+    w.bytes = o;
+    return w;
 }
 
 struct Launch {
@@ -397,7 +797,7 @@ Launch plan(int64_t D, int64_t L, int64_t K, int bytes_per_point) {
     pc = pc < 1 ? 1 : pc;
     p.pc = pc < lk ? pc : lk;
     p.ps = p.pc + ((p.pc % 2 == 0) ? 1 : 2);
-    p.lds = kMaxLevels * sizeof(int4) + (size_t)p.ipb * p.ps * bytes_per_point;
+    p.lds = (size_t)p.ipb * p.ps * bytes_per_point;
     return p;
 }
 
@@ -416,7 +816,7 @@ msda_status launch_fwd(const void *value, const int64_t *shapes, const int64_t *
     const unsigned gx = (unsigned)((items + p.ipb - 1) / p.ipb);
     for (int64_t b0 = 0; b0 < B; b0 += 65535) {
         const unsigned gy = (unsigned)((B - b0) < 65535 ? (B - b0) : 65535);
-        Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, p.pc, p.ps, (int)b0};
+        Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, p.pc, p.ps, (int)b0, 0, 0};
         hipLaunchKernelGGL((msda_fwd_kernel<D, VT>), dim3(gx, gy), dim3(kThreads), p.lds, s,
                            static_cast<const VT *>(value), shapes, starts, loc, attn, out, dm);
         msda_status st = hip_status(hipGetLastError());
@@ -425,24 +825,66 @@ msda_status launch_fwd(const void *value, const int64_t *shapes, const int64_t *
     return MSDA_OK;
 }
 
+// Zero n4 float4s (16-byte units) at p.
+msda_status fill_zero(void *p, size_t n4, hipStream_t s) {
+    if (n4 == 0) return MSDA_OK;
+    size_t blocks = (n4 + kThreads - 1) / kThreads;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s,
+                       reinterpret_cast<float4 *>(p), n4);
+    return hip_status(hipGetLastError());
+}
+
 template <int D, typename VT>
 msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *starts,
                        const float *loc, const float *attn, const float *gout, float *gval,
                        float *gloc, float *gattn, int64_t B, int64_t Nv, int64_t Nq, int64_t M,
-                       int64_t L, int64_t K, hipStream_t s) {
+                       int64_t L, int64_t K, const WorkLayout &wl, unsigned char *ws,
+                       bool accumulate, hipStream_t s) {
+    Work w;
+    w.counts = reinterpret_cast<uint32_t *>(ws + wl.off_counts);
+    w.start = reinterpret_cast<uint32_t *>(ws + wl.off_start);
+    w.cursor = reinterpret_cast<uint32_t *>(ws + wl.off_cursor);
+    w.items = reinterpret_cast<uint2 *>(ws + wl.off_items);
+    w.work_total = reinterpret_cast<uint32_t *>(ws + wl.off_total);
+    w.sorted = reinterpret_cast<uint32_t *>(ws + wl.off_sorted);
+    // the counts region is padded to 256 bytes, so whole float4s can be cleared
+    msda_status st = fill_zero(w.counts, (wl.off_start - wl.off_counts) / 16, s);
+    if (st != MSDA_OK) return st;
+
+    const int hist_cap = (int)(wl.nb_max < kHistLds ? wl.nb_max : kHistLds);
     const Launch p = plan(D, L, K, 64);
-    const int64_t items = Nq * M;
-    const unsigned gx = (unsigned)((items + p.ipb - 1) / p.ipb);
+    const unsigned gq = (unsigned)((Nq + p.ipb - 1) / p.ipb);
+    const unsigned gs = (unsigned)((Nq + kScatterQueries - 1) / kScatterQueries);
     for (int64_t b0 = 0; b0 < B; b0 += 65535) {
-        const unsigned gy = (unsigned)((B - b0) < 65535 ? (B - b0) : 65535);
-        Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, p.pc, p.ps, (int)b0};
-        hipLaunchKernelGGL((msda_bwd_kernel<D, VT>), dim3(gx, gy), dim3(kThreads), p.lds, s,
-                           static_cast<const VT *>(value), shapes, starts, loc, attn, gout, gval,
-                           gloc, gattn, dm);
-        msda_status st = hip_status(hipGetLastError());
+        const unsigned gb = (unsigned)((B - b0) < 65535 ? (B - b0) : 65535);
+        Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, p.pc, p.ps, (int)b0, (int)wl.nb_max, 0};
+        hipLaunchKernelGGL((bwd_dots_kernel<D, VT>), dim3(gq, (unsigned)M, gb), dim3(kThreads),
+                           p.lds + 4 * (size_t)hist_cap, s, static_cast<const VT *>(value),
+                           shapes, starts, loc, attn, gout, gloc, gattn, w.counts, hist_cap, dm);
+        st = hip_status(hipGetLastError());
         if (st != MSDA_OK) return st;
     }
-    return MSDA_OK;
+    Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, 0, 0, 0, (int)wl.nb_max, accumulate ? 1 : 0};
+    hipLaunchKernelGGL(bin_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, shapes, starts,
+                       w.counts, w.start, w.cursor, w.items, w.work_total, (int)(B * M), dm);
+    st = hip_status(hipGetLastError());
+    if (st != MSDA_OK) return st;
+    for (int64_t b0 = 0; b0 < B; b0 += 65535) {
+        const unsigned gb = (unsigned)((B - b0) < 65535 ? (B - b0) : 65535);
+        Dims d2 = dm;
+        d2.b0 = (int)b0;
+        hipLaunchKernelGGL(bin_scatter_kernel, dim3(gs, (unsigned)M, gb), dim3(kThreads),
+                           8 * (size_t)hist_cap, s, shapes, starts, loc, w.cursor, w.sorted,
+                           hist_cap, d2);
+        st = hip_status(hipGetLastError());
+        if (st != MSDA_OK) return st;
+    }
+    const int64_t grid = wl.work_max < kTileGrid ? wl.work_max : kTileGrid;
+    hipLaunchKernelGGL((grad_value_tile_kernel<D>), dim3((unsigned)grid), dim3(kTileThreads), 0, s,
+                       shapes, starts, loc, attn, gout, w.counts, w.start, w.items,
+                       w.work_total, w.sorted, gval, dm);
+    return hip_status(hipGetLastError());
 }
 
 template <typename VT>
@@ -450,27 +892,32 @@ msda_status dispatch_fwd(int64_t D, const void *value, const int64_t *shapes,
                          const int64_t *starts, const float *loc, const float *attn, float *out,
                          int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t L, int64_t K,
                          hipStream_t s) {
+#define MSDA_FWD_CASE(DD)                                                                     \
+    case DD:                                                                                  \
+        return launch_fwd<DD, VT>(value, shapes, starts, loc, attn, out, B, Nv, Nq, M, L, K, s);
     switch (D) {
-    case 4: return launch_fwd<4, VT>(value, shapes, starts, loc, attn, out, B, Nv, Nq, M, L, K, s);
-    case 8: return launch_fwd<8, VT>(value, shapes, starts, loc, attn, out, B, Nv, Nq, M, L, K, s);
-    case 16: return launch_fwd<16, VT>(value, shapes, starts, loc, attn, out, B, Nv, Nq, M, L, K, s);
-    case 32: return launch_fwd<32, VT>(value, shapes, starts, loc, attn, out, B, Nv, Nq, M, L, K, s);
-    case 64: return launch_fwd<64, VT>(value, shapes, starts, loc, attn, out, B, Nv, Nq, M, L, K, s);
-    case 128: return launch_fwd<128, VT>(value, shapes, starts, loc, attn, out, B, Nv, Nq, M, L, K, s);
-    case 256: return launch_fwd<256, VT>(value, shapes, starts, loc, attn, out, B, Nv, Nq, M, L, K, s);
+        MSDA_FWD_CASE(4)
+        MSDA_FWD_CASE(8)
+        MSDA_FWD_CASE(16)
+        MSDA_FWD_CASE(32)
+        MSDA_FWD_CASE(64)
+        MSDA_FWD_CASE(128)
+        MSDA_FWD_CASE(256)
     default: return MSDA_ERR_UNSUPPORTED;
     }
+#undef MSDA_FWD_CASE
 }
 
 template <typename VT>
 msda_status dispatch_bwd(int64_t D, const void *value, const int64_t *shapes,
                          const int64_t *starts, const float *loc, const float *attn,
                          const float *gout, float *gval, float *gloc, float *gattn, int64_t B,
-                         int64_t Nv, int64_t Nq, int64_t M, int64_t L, int64_t K, hipStream_t s) {
+                         int64_t Nv, int64_t Nq, int64_t M, int64_t L, int64_t K,
+                         const WorkLayout &wl, unsigned char *ws, bool acc, hipStream_t s) {
 #define MSDA_BWD_CASE(DD)                                                                      \
     case DD:                                                                                   \
         return launch_bwd<DD, VT>(value, shapes, starts, loc, attn, gout, gval, gloc, gattn, B, \
-                                  Nv, Nq, M, L, K, s);
+                                  Nv, Nq, M, L, K, wl, ws, acc, s);
     switch (D) {
         MSDA_BWD_CASE(4)
         MSDA_BWD_CASE(8)
@@ -482,16 +929,6 @@ msda_status dispatch_bwd(int64_t D, const void *value, const int64_t *shapes,
     default: return MSDA_ERR_UNSUPPORTED;
     }
 #undef MSDA_BWD_CASE
-}
-
-msda_status fill_zero(float *p, int64_t n, hipStream_t s) {
-    if (n <= 0) return MSDA_OK;
-    const size_t n4 = (size_t)n / 4;  // n is a multiple of D, itself a multiple of 4
-    size_t blocks = (n4 + kThreads - 1) / kThreads;
-    if (blocks > 8192) blocks = 8192;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s,
-                       reinterpret_cast<float4 *>(p), n4);
-    return hip_status(hipGetLastError());
 }
 
 }  // namespace
@@ -516,36 +953,52 @@ msda_status msda_forward(const void *value, int value_dtype, const int64_t *spat
                                   attn_weight, out, B, Nv, Nq, M, L, K, s);
 }
 
+size_t msda_backward_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
+                                    int64_t L, int64_t K) {
+    if (check_sizes(MSDA_F32, B, Nv, Nq, M, D, L, K) != MSDA_OK) return 0;
+    if (B == 0 || Nq == 0) return 0;
+    return work_layout(B, Nv, Nq, M, L, K).bytes;
+}
+
 msda_status msda_backward(const void *value, int value_dtype, const int64_t *spatial_shapes,
                           const int64_t *level_start_index, const float *sampling_loc,
                           const float *attn_weight, const float *grad_out, float *grad_value,
                           float *grad_sampling_loc, float *grad_attn_weight, int64_t B,
                           int64_t Nv, int64_t Nq, int64_t M, int64_t D, int64_t L, int64_t K,
-                          uint32_t flags, void *stream) {
+                          void *workspace, size_t workspace_bytes, uint32_t flags,
+                          void *stream) {
     msda_status st = check_sizes(value_dtype, B, Nv, Nq, M, D, L, K);
     if (st != MSDA_OK) return st;
     if (flags & ~MSDA_BWD_ACCUMULATE) return MSDA_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t nval = B * Nv * M * D;
     if (nval > 0 && !grad_value) return MSDA_ERR_NULL;
-    if (B > 0 && Nq > 0) {
+    const bool work = B > 0 && Nq > 0;
+    WorkLayout wl{};
+    if (work) {
         if (Nv < 1) return MSDA_ERR_SHAPE;
         if (!value || !spatial_shapes || !level_start_index || !sampling_loc || !attn_weight ||
             !grad_out || !grad_sampling_loc || !grad_attn_weight)
             return MSDA_ERR_NULL;
+        wl = work_layout(B, Nv, Nq, M, L, K);
+        if (!workspace) return MSDA_ERR_NULL;
+        if (workspace_bytes < wl.bytes) return MSDA_ERR_WORKSPACE;
+        if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return MSDA_ERR_WORKSPACE;
     }
     if (!(flags & MSDA_BWD_ACCUMULATE)) {
-        st = fill_zero(grad_value, nval, s);
+        st = fill_zero(grad_value, (size_t)nval / 4, s);  // D is a multiple of 4
         if (st != MSDA_OK) return st;
     }
-    if (B == 0 || Nq == 0) return MSDA_OK;
+    if (!work) return MSDA_OK;
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    const bool acc = (flags & MSDA_BWD_ACCUMULATE) != 0;
     if (value_dtype == MSDA_F32)
         return dispatch_bwd<float>(D, value, spatial_shapes, level_start_index, sampling_loc,
                                    attn_weight, grad_out, grad_value, grad_sampling_loc,
-                                   grad_attn_weight, B, Nv, Nq, M, L, K, s);
+                                   grad_attn_weight, B, Nv, Nq, M, L, K, wl, ws, acc, s);
     return dispatch_bwd<uint16_t>(D, value, spatial_shapes, level_start_index, sampling_loc,
                                   attn_weight, grad_out, grad_value, grad_sampling_loc,
-                                  grad_attn_weight, B, Nv, Nq, M, L, K, s);
+                                  grad_attn_weight, B, Nv, Nq, M, L, K, wl, ws, acc, s);
 }
 
 msda_status msda_validate_host(const int64_t *spatial_shapes_host, const int64_t *level_start_host,
@@ -578,6 +1031,8 @@ const char *msda_status_string(int status) {
     case MSDA_ERR_UNSUPPORTED:
         return "outside the supported limits (D in {4,8,...,256}, 1 <= L <= 16, 31-bit slices)";
     case MSDA_ERR_HIP: return "the HIP runtime refused a launch";
+    case MSDA_ERR_WORKSPACE:
+        return "workspace smaller than msda_backward_workspace_size or not 256-byte aligned";
     default: return "unknown msda status";
     }
 }

@@ -95,7 +95,7 @@ def test_backward_rejects_before_launch():
     lib = msda.load()
     z = ctypes.c_void_p(0)
     bwd = lambda dt, flags, *dims: lib.msda_backward(z, dt, z, z, z, z, z, z, z, z, *dims,
-                                                      flags, z)
+                                                      z, 0, flags, z)
     assert bwd(2, 0, 1, 80, 16, 2, 8, 2, 2) == B_.MSDA_ERR_DTYPE
     assert bwd(0, 4, 1, 80, 16, 2, 8, 2, 2) == B_.MSDA_ERR_UNSUPPORTED  # unknown flag
     assert bwd(0, 0, 1, 80, 16, 2, 8, 2, 2) == B_.MSDA_ERR_NULL
@@ -104,8 +104,28 @@ def test_backward_rejects_before_launch():
     assert bwd(0, B_.MSDA_BWD_ACCUMULATE, 1, 80, 0, 2, 8, 2, 2) == B_.MSDA_ERR_NULL  # grad_value needed
 
 
+def test_backward_workspace_checks():
+    """Workspace size: 0 for nothing to do, positive otherwise, and the call
+    rejects a missing, short or misaligned workspace before any launch."""
+    lib = msda.load()
+    assert lib.msda_backward_workspace_size(0, 80, 16, 2, 8, 2, 2) == 0
+    assert lib.msda_backward_workspace_size(1, 80, 16, 2, 12, 2, 2) == 0   # invalid D
+    n = lib.msda_backward_workspace_size(2, 22223, 22223, 8, 32, 4, 4)
+    pts = 2 * 22223 * 8 * 16
+    assert 16 * pts <= n <= 16 * pts + 4 << 20
+    z = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(1 << 20)   # never dereferenced: the checks fail first
+    bwd = lambda ws, nbytes: lib.msda_backward(fake, 0, fake, fake, fake, fake, fake, fake,
+                                               fake, fake, 1, 80, 16, 2, 8, 2, 2, ws, nbytes,
+                                               0, z)
+    need = lib.msda_backward_workspace_size(1, 80, 16, 2, 8, 2, 2)
+    assert bwd(z, need) == B_.MSDA_ERR_NULL
+    assert bwd(fake, need - 1) == B_.MSDA_ERR_WORKSPACE
+    assert bwd(ctypes.c_void_p((1 << 20) + 4), need) == B_.MSDA_ERR_WORKSPACE
+
+
 def test_status_strings():
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         s = msda.status_string(code)
         assert isinstance(s, str) and s and s != msda.status_string(42)
     assert msda.status_string(42) == "unknown msda status"

@@ -29,6 +29,11 @@ def msda():
     return m
 
 
+def close(x, r, tol, what=""):
+    e = max_rel(x, r)
+    assert e <= tol, f"{what}: max rel error {e:.3e} > {tol}"
+
+
 def _say(msg):
     print(f"[case] {msg}", flush=True)
 
@@ -118,16 +123,16 @@ def test_train_bf16_fwd_bwd(msda):
     w = workloads.make(4)
     # strict: against the oracle on the bf16-rounded values (w.value)
     got = gpu_forward(msda, w, bf16=True)
-    assert max_rel(got, oracle_fwd(w).reshape(got.shape)) <= FWD_TOL
+    close(got, oracle_fwd(w).reshape(got.shape), FWD_TOL)
     gv, gl, ga = gpu_backward(msda, w, bf16=True)
     rv, rl, ra = oracle_bwd(w)
     for x, r in ((gv, rv), (gl, rl), (ga, ra)):
-        assert max_rel(x, r) <= BWD_TOL
+        close(x, r, BWD_TOL)
     # pass/fail bar: against the oracle on the unrounded fp32 values
-    assert max_rel(got, oracle_fwd(w, w.value_unrounded).reshape(got.shape)) <= BF16_TOL
+    close(got, oracle_fwd(w, w.value_unrounded).reshape(got.shape), BF16_TOL)
     rv, rl, ra = oracle_bwd(w, w.value_unrounded)
     for x, r in ((gv, rv), (gl, rl), (ga, ra)):
-        assert max_rel(x, r) <= BF16_TOL
+        close(x, r, BF16_TOL)
 
 
 # ---------------------------------------------------------------------------
@@ -203,7 +208,7 @@ def test_out_of_map_and_nonfinite(msda):
     assert np.all(np.isfinite(gl)) and np.all(np.isfinite(ga))
     assert np.all(gl[:, ::2] == 0.0) and np.all(ga[:, ::2] == 0.0)
     for x, r in ((gv, rv), (gl, rl), (ga, ra)):
-        assert max_rel(x, r) <= BWD_TOL
+        close(x, r, BWD_TOL)
 
 
 def test_empty_inputs(msda):
@@ -237,7 +242,7 @@ def test_accumulate_adds_into_grad_value(msda):
     msda.backward(**x, grad_out=g, grad_value=gv, accumulate=True)
     torch.cuda.synchronize()
     rv, _, _ = oracle_bwd(w)
-    assert max_rel(gv.cpu().numpy() - base.cpu().numpy(), rv) <= BWD_TOL
+    close(gv.cpu().numpy() - base.cpu().numpy(), rv, BWD_TOL)
 
 
 def test_runs_on_the_callers_stream(msda):
@@ -251,9 +256,9 @@ def test_runs_on_the_callers_stream(msda):
         gv, gl, ga = msda.backward(**x, grad_out=torch.from_numpy(w.grad_out).cuda(),
                                    validate=False)
     s.synchronize()
-    assert max_rel(out.cpu().numpy(), oracle_fwd(w)) <= FWD_TOL
+    close(out.cpu().numpy(), oracle_fwd(w), FWD_TOL)
     rv, rl, ra = oracle_bwd(w)
-    assert max_rel(gl.cpu().numpy(), rl) <= BWD_TOL
+    close(gl.cpu().numpy(), rl, BWD_TOL)
 
 
 def test_autograd_function(msda):
@@ -266,10 +271,10 @@ def test_autograd_function(msda):
     out = msda.ms_deform_attn(v, x["spatial_shapes"], x["level_start_index"], loc, a)
     out.backward(torch.from_numpy(w.grad_out).cuda())
     rv, rl, ra = oracle_bwd(w)
-    assert max_rel(out.detach().cpu().numpy(), oracle_fwd(w)) <= FWD_TOL
-    assert max_rel(v.grad.cpu().numpy(), rv) <= BWD_TOL
-    assert max_rel(loc.grad.cpu().numpy(), rl) <= BWD_TOL
-    assert max_rel(a.grad.cpu().numpy(), ra) <= BWD_TOL
+    close(out.detach().cpu().numpy(), oracle_fwd(w), FWD_TOL)
+    close(v.grad.cpu().numpy(), rv, BWD_TOL)
+    close(loc.grad.cpu().numpy(), rl, BWD_TOL)
+    close(a.grad.cpu().numpy(), ra, BWD_TOL)
 
 
 def test_backward_repeatability(msda):
