@@ -58,7 +58,7 @@ constexpr int kChunk = 2048;               // points per grad_value work item, a
 constexpr int kHistLds = 4096;             // bins of one (batch, head) kept in an LDS histogram
 constexpr int kScatterQueries = 64;        // queries per scatter workgroup
 constexpr int kScanThreads = 1024;
-constexpr int kTileGrid = 1024;            // persistent workgroups of the tile kernel
+constexpr int kTileGrid = 2048;            // persistent workgroups of the tile kernel
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
@@ -220,20 +220,34 @@ __device__ __forceinline__ float pick(const float4 &v, int c) {
     return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
 }
 
+// Workgroup ids are dispatched round-robin over the 8 XCDs (workgroup k runs
+// on XCD k % 8), and each XCD has its own L2.  Mapping id k to the logical
+// index below gives every XCD one contiguous range of the work, so the value
+// rows, grad_out rows and points one XCD touches stay together in its L2.
+// The mapping is a permutation of [0, total): results never depend on it.
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ int xcd_contiguous(int k, int total) {
+    const int per = total / kXcds, rem = total % kXcds;
+    const int x = k % kXcds, j = k / kXcds;
+    return x * per + min(x, rem) + j;
+}
+
 struct Dims {
     int Nv, Nq, M, L, K;
     int PC;      // points per chunk (point-table kernels)
     int PS;      // LDS stride per item (PC rounded to an odd count, for bank spread)
     int b0;      // first batch of this launch
-    int nb_max;  // bin stride per (batch, head) in the workspace
+    int nblk;    // workgroups per batch (forward) or per (batch, head) (backward)
+    int nb_max;      // bin stride per (batch, head) in the workspace
     int accumulate;  // grad_value already holds a gradient to add to
 };
 
 // Workspace of the backward pipeline (all 32-bit words).
 struct Work {
-    uint32_t *counts;      // [B*M*nb_max] points per bin
-    uint32_t *start;       // [B*M*nb_max] first entry of each bin in `sorted`
-    uint32_t *cursor;      // [B*M*nb_max] next free entry while scattering
+    uint32_t *counts;      // [B][nb_max][M] points per bin
+    uint32_t *start;       // [B][nb_max][M] first entry of each bin in `sorted`
+    uint32_t *cursor;      // [B][nb_max][M] next free entry while scattering
     uint2 *items;          // [work_max] (bin, chunk)
     uint32_t *work_total;  // [1]
     uint32_t *sorted;      // [4 * points] point indices grouped by bin
@@ -256,8 +270,9 @@ msda_fwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
 
     const int M = dm.M, K = dm.K, LK = dm.L * dm.K;
     const int NqM = dm.Nq * M;
-    const int b = blockIdx.y + dm.b0;
-    const int item0 = blockIdx.x * IPB;
+    const int wg = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int b = wg / dm.nblk + dm.b0;
+    const int item0 = (wg % dm.nblk) * IPB;
     const int nitems = min(IPB, NqM - item0);
     const uint32_t row_stride = (uint32_t)M * D * 4u;
 
@@ -335,9 +350,10 @@ bwd_dots_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
     uint32_t *s_hist = reinterpret_cast<uint32_t *>(s_dot + IPB * dm.PS);
 
     const int M = dm.M, K = dm.K, LK = dm.L * dm.K, Nq = dm.Nq;
-    const int m = blockIdx.y;
-    const int b = blockIdx.z + dm.b0;
-    const int q0 = blockIdx.x * IPB;
+    const int wg = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int bm = wg / dm.nblk + dm.b0 * M;
+    const int m = bm % M, b = bm / M;
+    const int q0 = (wg % dm.nblk) * IPB;
     const int nitems = min(IPB, Nq - q0);
     const uint32_t row_stride = (uint32_t)M * D * 4u;
     const uint32_t head_off = (uint32_t)m * D * 4u;
@@ -345,7 +361,8 @@ bwd_dots_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
     stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
     const int nbins = s_lv.nbins;
     const bool lds_hist = nbins <= hist_cap;
-    uint32_t *gcount = counts + (size_t)(b * M + m) * dm.nb_max;
+    // bins are laid out (batch, tile, head): tile i of this (b, m) is gcount[i * M]
+    uint32_t *gcount = counts + (size_t)b * dm.nb_max * M + m;
     if (lds_hist)
         for (int i = threadIdx.x; i < nbins; i += kThreads) s_hist[i] = 0u;
 
@@ -388,7 +405,7 @@ bwd_dots_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
                 if (lds_hist)
                     atomicAdd(&s_hist[bins[k]], 1u);
                 else
-                    atomicAdd(&gcount[bins[k]], 1u);
+                    atomicAdd(&gcount[(size_t)bins[k] * M], 1u);
             }
         }
         __syncthreads();
@@ -431,7 +448,7 @@ bwd_dots_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
         __syncthreads();
         for (int i = threadIdx.x; i < nbins; i += kThreads) {
             const uint32_t v = s_hist[i];
-            if (v) atomicAdd(&gcount[i], v);
+            if (v) atomicAdd(&gcount[(size_t)i * M], v);
         }
     }
 }
@@ -466,13 +483,15 @@ __global__ void __launch_bounds__(kScanThreads)
 bin_scan_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ starts,
                 const uint32_t *__restrict__ counts, uint32_t *__restrict__ start,
                 uint32_t *__restrict__ cursor, uint2 *__restrict__ items,
-                uint32_t *__restrict__ work_total, int BM, Dims dm) {
+                uint32_t *__restrict__ work_total, int B, Dims dm) {
     constexpr int kPer = 8;
     __shared__ LevelLds s_lv;
     __shared__ uint32_t s_a[kScanThreads], s_b[kScanThreads];
     stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
     const int nbins = s_lv.nbins;
-    const int64_t n = (int64_t)BM * nbins;
+    // bins in (batch, tile, head) order; entry g maps to bin (b*nb_max + tile)*M + m
+    const int64_t per_b = (int64_t)nbins * dm.M;
+    const int64_t n = (int64_t)B * per_b;
     uint32_t carry_e = 0, carry_c = 0;
     for (int64_t base = 0; base < n; base += (int64_t)kScanThreads * kPer) {
         uint32_t cnt[kPer], e = 0, ch = 0;
@@ -481,10 +500,7 @@ bin_scan_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ 
         for (int i = 0; i < kPer; ++i) {
             const int64_t g = g0 + i;
             cnt[i] = 0;
-            if (g < n) {
-                const int64_t bin = (g / nbins) * dm.nb_max + g % nbins;
-                cnt[i] = counts[bin];
-            }
+            if (g < n) cnt[i] = counts[(g / per_b) * dm.nb_max * dm.M + g % per_b];
             e += cnt[i];
             ch += (cnt[i] + kChunk - 1) / kChunk;
         }
@@ -496,7 +512,7 @@ bin_scan_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ 
         for (int i = 0; i < kPer; ++i) {
             const int64_t g = g0 + i;
             if (g < n) {
-                const uint32_t bin = (uint32_t)((g / nbins) * dm.nb_max + g % nbins);
+                const uint32_t bin = (uint32_t)((g / per_b) * dm.nb_max * dm.M + g % per_b);
                 start[bin] = e;
                 cursor[bin] = e;
                 const uint32_t nch = (cnt[i] + kChunk - 1) / kChunk;
@@ -525,16 +541,17 @@ bin_scatter_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict
     uint32_t *s_base = s_cnt + hist_cap;                    // [hist_cap] reserved offsets
 
     const int M = dm.M, K = dm.K, LK = dm.L * dm.K, Nq = dm.Nq;
-    const int m = blockIdx.y;
-    const int b = blockIdx.z + dm.b0;
-    const int q0 = blockIdx.x * kScatterQueries;
+    const int wg = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int bm = wg / dm.nblk + dm.b0 * M;
+    const int m = bm % M, b = bm / M;
+    const int q0 = (wg % dm.nblk) * kScatterQueries;
     const int nq = min(kScatterQueries, Nq - q0);
     const size_t row0 = ((size_t)b * Nq + q0) * M + m;
     const int npts = nq * LK;
 
     stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
     const int nbins = s_lv.nbins;
-    uint32_t *gcur = cursor + (size_t)(b * M + m) * dm.nb_max;
+    uint32_t *gcur = cursor + (size_t)b * dm.nb_max * M + m;  // tile i at gcur[i * M]
     if (nbins > hist_cap) {  // too many bins for LDS: reserve one slot at a time
         for (int idx = threadIdx.x; idx < npts; idx += kThreads) {
             const int i1 = idx / LK, j = idx - i1 * LK;
@@ -544,7 +561,8 @@ bin_scatter_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict
             Neighbours n = neighbours(uv.x, uv.y, s_lv.lvl[l], 0u, 0u);
             int bins[4];
             const int nb = point_bins(n, s_lv.lvl[l], s_lv.tw[l], bins);
-            for (int k = 0; k < nb; ++k) sorted[atomicAdd(&gcur[bins[k]], 1u)] = (uint32_t)p;
+            for (int k = 0; k < nb; ++k)
+                sorted[atomicAdd(&gcur[(size_t)bins[k] * M], 1u)] = (uint32_t)p;
         }
         return;
     }
@@ -563,7 +581,7 @@ bin_scatter_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict
     __syncthreads();
     for (int i = threadIdx.x; i < nbins; i += kThreads) {
         const uint32_t v = s_cnt[i];
-        s_base[i] = v ? atomicAdd(&gcur[i], v) : 0u;
+        s_base[i] = v ? atomicAdd(&gcur[(size_t)i * M], v) : 0u;
         s_cnt[i] = 0u;
     }
     __syncthreads();
@@ -583,17 +601,21 @@ bin_scatter_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict
 // ---------------------------------------------------------------------------
 // backward 4: grad_value, one 8x8 tile (and chunk of its points) per work item
 //
-// The chunk's points are counting-sorted in LDS by the cell of their top-left
-// neighbour (a 9x9 grid: the tile plus one column and row before it).  Pixel
-// (x, y) of the tile receives from the points of four cells, in four roles:
-// top-left from cell (x, y), top-right from (x-1, y), bottom-left from
-// (x, y-1), bottom-right from (x-1, y-1).  A lane owns one (pixel, 4-channel
-// quad) and sums A * w * grad_out over those lists in registers, so no two
-// lanes ever add into the same value and the loop iterations are independent.
+// The chunk is walked in sub-chunks of kSubRows(D) points.  For each, the
+// points' grad_out rows are staged in LDS (one read of each row), and the
+// points are counting-sorted in LDS by the cell of their top-left neighbour
+// (a 9x9 grid: the tile plus one column and row before it).  Pixel (x, y) of
+// the tile receives from the points of four cells, in four roles: top-left
+// from cell (x, y), top-right from (x-1, y), bottom-left from (x, y-1),
+// bottom-right from (x-1, y-1).  A lane owns (pixel, 4-channel quad) pairs
+// and sums A * w * grad_out over those lists in registers across all
+// sub-chunks, so no two lanes ever add into the same value and the loop
+// iterations are independent.  Each pixel is written once per work item.
 // ---------------------------------------------------------------------------
 constexpr int kTileThreads = 512;
 constexpr int kCellsW = kTile + 1;
 constexpr int kCells = kCellsW * kCellsW;
+constexpr int kStageBytes = 32 * 1024;  // grad_out rows staged per sub-chunk
 
 template <int D>
 __global__ void __launch_bounds__(kTileThreads)
@@ -605,12 +627,14 @@ grad_value_tile_kernel(const int64_t *__restrict__ shapes, const int64_t *__rest
                        const uint32_t *__restrict__ sorted, float *__restrict__ grad_value,
                        Dims dm) {
     constexpr int kQuads = D / 4;
-    constexpr int kPxPerPass = kTileThreads / kQuads < kTilePx ? kTileThreads / kQuads : kTilePx;
+    constexpr int kSub = kStageBytes / (D * 4) < 512 ? kStageBytes / (D * 4) : 512;  // points per sub-chunk
+    constexpr int kOwn = (kTilePx * kQuads + kTileThreads - 1) / kTileThreads;  // pairs per lane
     __shared__ LevelLds s_lv;
-    __shared__ float4 s_w[kChunk];       // A * bilinear weight of each neighbour
-    __shared__ uint32_t s_item[kChunk];  // (b, q, m) row of the point
-    __shared__ uint16_t s_cell[kChunk];  // cell of the point's top-left neighbour
-    __shared__ uint16_t s_ent[kChunk];   // points ordered by cell
+    __shared__ float4 s_g[kSub * kQuads];  // staged grad_out rows
+    __shared__ float4 s_w[kSub];           // A * bilinear weight of each neighbour
+    __shared__ uint32_t s_item[kSub];      // (b, q, m) row of the point
+    __shared__ uint16_t s_cell[kSub];      // cell of the point's top-left neighbour
+    __shared__ uint16_t s_ent[kSub];       // points ordered by cell
     __shared__ uint32_t s_cnt[kCells + 1];
     __shared__ uint32_t s_cur[kCells];
 
@@ -618,13 +642,17 @@ grad_value_tile_kernel(const int64_t *__restrict__ shapes, const int64_t *__rest
     stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
     const uint32_t total = *work_total;
     const int tid = threadIdx.x;
-
+    // The work list is in (batch, level, tile, head) order and workgroup k
+    // (dispatched to XCD k % 8) takes items k, k + grid, ...  With 8 heads the
+    // XCDs therefore split the work by head: every XCD gets the same mix of
+    // tiles, and the grad_out rows it gathers are those of one head.
     for (uint32_t w = blockIdx.x; w < total; w += gridDim.x) {
         const uint2 wk = items[w];
-        const uint32_t bin = wk.x;
-        const int bm = (int)(bin / (uint32_t)dm.nb_max);
-        const int lb = (int)(bin - (uint32_t)bm * dm.nb_max);
-        const int b = bm / M, m = bm - b * M;
+        const uint32_t bin = wk.x;  // (b * nb_max + tile) * M + m
+        const int m = (int)(bin % (uint32_t)M);
+        const uint32_t bt = bin / (uint32_t)M;
+        const int b = (int)(bt / (uint32_t)dm.nb_max);
+        const int lb = (int)(bt - (uint32_t)b * dm.nb_max);
         int l = 0;
         while (l + 1 < dm.L && s_lv.lvl[l + 1].w <= lb) ++l;
         const int4 lvl = s_lv.lvl[l];
@@ -636,82 +664,109 @@ grad_value_tile_kernel(const int64_t *__restrict__ shapes, const int64_t *__rest
         const int n = (int)min((uint32_t)kChunk, cnt - wk.y * kChunk);
         const bool whole = cnt <= (uint32_t)kChunk;
 
-        for (int i = tid; i < kCells; i += kTileThreads) s_cnt[i] = 0u;
-        __syncthreads();
-        for (int i = tid; i < n; i += kTileThreads) {
-            const uint32_t p = sorted[s0 + i];
-            const float2 uv = reinterpret_cast<const float2 *>(loc)[p];
-            const float A = attn[p];
-            const Neighbours nb = neighbours(uv.x, uv.y, lvl, 0u, 0u);
-            // a point of this bin has a neighbour inside the tile, so its
-            // top-left neighbour lies in the 9x9 cell grid
-            const int cx = nb.xi - x0t + 1, cy = nb.yi - y0t + 1;
-            const bool inside = cx >= 0 && cx < kCellsW && cy >= 0 && cy < kCellsW;
-            const int cell = inside ? cx + cy * kCellsW : 0;
-            s_cell[i] = (uint16_t)cell;
-            s_w[i] = inside ? make_float4(A * nb.w.x, A * nb.w.y, A * nb.w.z, A * nb.w.w)
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
-            s_item[i] = p / (uint32_t)LK;
-            atomicAdd(&s_cnt[cell], 1u);
-        }
-        __syncthreads();
-        if (tid == 0) {
-            uint32_t acc = 0;
-            for (int c = 0; c < kCells; ++c) {
-                const uint32_t v = s_cnt[c];
-                s_cnt[c] = acc;
-                s_cur[c] = acc;
-                acc += v;
+        float4 acc[kOwn];
+#pragma unroll
+        for (int o = 0; o < kOwn; ++o) acc[o] = make_float4(0.f, 0.f, 0.f, 0.f);
+
+        for (int sub = 0; sub < n; sub += kSub) {
+            const int ns = min(kSub, n - sub);
+            for (int i = tid; i < kCells; i += kTileThreads) s_cnt[i] = 0u;
+            __syncthreads();
+            for (int i = tid; i < ns; i += kTileThreads) {
+                const uint32_t p = sorted[s0 + sub + i];
+                const float2 uv = reinterpret_cast<const float2 *>(loc)[p];
+                const float A = attn[p];
+                const Neighbours nb = neighbours(uv.x, uv.y, lvl, 0u, 0u);
+                // a point of this bin has a neighbour inside the tile, so its
+                // top-left neighbour lies in the 9x9 cell grid
+                const int cx = nb.xi - x0t + 1, cy = nb.yi - y0t + 1;
+                const bool inside = cx >= 0 && cx < kCellsW && cy >= 0 && cy < kCellsW;
+                const int cell = inside ? cx + cy * kCellsW : 0;
+                s_cell[i] = (uint16_t)cell;
+                s_w[i] = inside ? make_float4(A * nb.w.x, A * nb.w.y, A * nb.w.z, A * nb.w.w)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+                s_item[i] = p / (uint32_t)LK;
+                atomicAdd(&s_cnt[cell], 1u);
             }
-            s_cnt[kCells] = acc;
+            __syncthreads();
+            for (int i = tid; i < ns * kQuads; i += kTileThreads) {
+                const int pt = i / kQuads, q = i - pt * kQuads;
+                s_g[i] = reinterpret_cast<const float4 *>(grad_out + (size_t)s_item[pt] * D)[q];
+            }
+            if (tid < 64) {  // exclusive scan of the 81 cell counts by one wave, 2 cells a lane
+                const int c0 = 2 * tid, c1 = 2 * tid + 1;
+                const uint32_t v0 = c0 < kCells ? s_cnt[c0] : 0u;
+                const uint32_t v1 = c1 < kCells ? s_cnt[c1] : 0u;
+                uint32_t incl = v0 + v1;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const uint32_t t = __shfl_up(incl, off, 64);
+                    if (tid >= off) incl += t;
+                }
+                const uint32_t ex = incl - v0 - v1;
+                if (c0 < kCells) {
+                    s_cnt[c0] = ex;
+                    s_cur[c0] = ex;
+                }
+                if (c1 < kCells) {
+                    s_cnt[c1] = ex + v0;
+                    s_cur[c1] = ex + v0;
+                }
+                if (tid == 63) s_cnt[kCells] = incl;
+            }
+            __syncthreads();
+            for (int i = tid; i < ns; i += kTileThreads)
+                s_ent[atomicAdd(&s_cur[s_cell[i]], 1u)] = (uint16_t)i;
+            __syncthreads();
+#pragma unroll
+            for (int o = 0; o < kOwn; ++o) {
+                const int pair = tid + o * kTileThreads;
+                if (pair >= kTilePx * kQuads) break;
+                const int px = pair / kQuads, q = pair - px * kQuads;
+                const int x = px & (kTile - 1), y = px >> kTileShift;
+#pragma unroll
+                for (int role = 0; role < 4; ++role) {
+                    const int cell = (x - (role & 1) + 1) + (y - (role >> 1) + 1) * kCellsW;
+                    const int e0 = (int)s_cnt[cell], e1 = (int)s_cnt[cell + 1];
+#pragma unroll 4
+                    for (int e = e0; e < e1; ++e) {
+                        const int pt = s_ent[e];
+                        fma4(acc[o], pick(s_w[pt], role), s_g[pt * kQuads + q]);
+                    }
+                }
+            }
+            __syncthreads();  // the tables are rebuilt for the next sub-chunk
         }
-        __syncthreads();
-        for (int i = tid; i < n; i += kTileThreads)
-            s_ent[atomicAdd(&s_cur[s_cell[i]], 1u)] = (uint16_t)i;
-        __syncthreads();
 
         const size_t slice = (size_t)dm.Nv * M * D;
         float *gv = grad_value + (size_t)b * slice + (size_t)m * D;
-        for (int px0 = 0; px0 < kTilePx; px0 += kPxPerPass) {
-            const int px = px0 + tid / kQuads, q = tid % kQuads;
-            if (tid >= kPxPerPass * kQuads) continue;
-            const int x = px & (kTile - 1), y = px >> kTileShift;
-            const int gx = x0t + x, gy = y0t + y;
-            if (gy >= lvl.x || gx >= lvl.y) continue;
-            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-            for (int role = 0; role < 4; ++role) {
-                const int cell = (x - (role & 1) + 1) + (y - (role >> 1) + 1) * kCellsW;
-                const int e0 = (int)s_cnt[cell], e1 = (int)s_cnt[cell + 1];
-#pragma unroll 4
-                for (int e = e0; e < e1; ++e) {
-                    const int pt = s_ent[e];
-                    const float wgt = pick(s_w[pt], role);
-                    const float4 g =
-                        reinterpret_cast<const float4 *>(grad_out + (size_t)s_item[pt] * D)[q];
-                    fma4(acc, wgt, g);
-                }
-            }
+        for (int o = 0; o < kOwn; ++o) {
+            const int pair = tid + o * kTileThreads;
+            if (pair >= kTilePx * kQuads) break;
+            const int px = pair / kQuads, q = pair - px * kQuads;
+            const int gx = x0t + (px & (kTile - 1)), gy = y0t + (px >> kTileShift);
+            if (gy >= lvl.x || gx >= lvl.y) continue;
             float *dst = gv + (size_t)(lvl.z + gy * lvl.y + gx) * M * D + 4 * q;
+            float4 a = acc[o];
             if (whole) {
                 // this work item alone owns the pixel: plain read-add-write
                 float4 *d4 = reinterpret_cast<float4 *>(dst);
                 if (dm.accumulate) {
-                    const float4 o = *d4;
-                    acc.x += o.x;
-                    acc.y += o.y;
-                    acc.z += o.z;
-                    acc.w += o.w;
+                    const float4 v = *d4;
+                    a.x += v.x;
+                    a.y += v.y;
+                    a.z += v.z;
+                    a.w += v.w;
                 }
-                *d4 = acc;
+                *d4 = a;
             } else {
-                atomicAdd(dst + 0, acc.x);
-                atomicAdd(dst + 1, acc.y);
-                atomicAdd(dst + 2, acc.z);
-                atomicAdd(dst + 3, acc.w);
+                atomicAdd(dst + 0, a.x);
+                atomicAdd(dst + 1, a.y);
+                atomicAdd(dst + 2, a.z);
+                atomicAdd(dst + 3, a.w);
             }
         }
-        __syncthreads();  // the tables are reused by the next work item
     }
 }
 
@@ -807,18 +862,28 @@ msda_status hip_status(hipError_t e) {
     return MSDA_ERR_HIP;
 }
 
+// Batches per launch so that a 1-D grid of per_batch workgroups per batch
+// stays below 2^23 workgroups (2^31 threads).
+int64_t batch_chunk(int64_t per_batch, int64_t B) {
+    int64_t c = ((int64_t)1 << 23) / (per_batch > 0 ? per_batch : 1);
+    c = c < 1 ? 1 : c;
+    return c < B ? c : B;
+}
+
 template <int D, typename VT>
 msda_status launch_fwd(const void *value, const int64_t *shapes, const int64_t *starts,
                        const float *loc, const float *attn, float *out, int64_t B, int64_t Nv,
                        int64_t Nq, int64_t M, int64_t L, int64_t K, hipStream_t s) {
     const Launch p = plan(D, L, K, 32);
     const int64_t items = Nq * M;
-    const unsigned gx = (unsigned)((items + p.ipb - 1) / p.ipb);
-    for (int64_t b0 = 0; b0 < B; b0 += 65535) {
-        const unsigned gy = (unsigned)((B - b0) < 65535 ? (B - b0) : 65535);
-        Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, p.pc, p.ps, (int)b0, 0, 0};
-        hipLaunchKernelGGL((msda_fwd_kernel<D, VT>), dim3(gx, gy), dim3(kThreads), p.lds, s,
-                           static_cast<const VT *>(value), shapes, starts, loc, attn, out, dm);
+    const int64_t gx = (items + p.ipb - 1) / p.ipb;
+    const int64_t bchunk = batch_chunk(gx, B);
+    for (int64_t b0 = 0; b0 < B; b0 += bchunk) {
+        const int64_t nb = (B - b0) < bchunk ? (B - b0) : bchunk;
+        Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, p.pc, p.ps, (int)b0, (int)gx, 0, 0};
+        hipLaunchKernelGGL((msda_fwd_kernel<D, VT>), dim3((unsigned)(gx * nb)), dim3(kThreads),
+                           p.lds, s, static_cast<const VT *>(value), shapes, starts, loc, attn,
+                           out, dm);
         msda_status st = hip_status(hipGetLastError());
         if (st != MSDA_OK) return st;
     }
@@ -854,27 +919,33 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
 
     const int hist_cap = (int)(wl.nb_max < kHistLds ? wl.nb_max : kHistLds);
     const Launch p = plan(D, L, K, 64);
-    const unsigned gq = (unsigned)((Nq + p.ipb - 1) / p.ipb);
-    const unsigned gs = (unsigned)((Nq + kScatterQueries - 1) / kScatterQueries);
-    for (int64_t b0 = 0; b0 < B; b0 += 65535) {
-        const unsigned gb = (unsigned)((B - b0) < 65535 ? (B - b0) : 65535);
-        Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, p.pc, p.ps, (int)b0, (int)wl.nb_max, 0};
-        hipLaunchKernelGGL((bwd_dots_kernel<D, VT>), dim3(gq, (unsigned)M, gb), dim3(kThreads),
-                           p.lds + 4 * (size_t)hist_cap, s, static_cast<const VT *>(value),
-                           shapes, starts, loc, attn, gout, gloc, gattn, w.counts, hist_cap, dm);
+    const int64_t gq = (Nq + p.ipb - 1) / p.ipb;
+    const int64_t gs = (Nq + kScatterQueries - 1) / kScatterQueries;
+    int64_t bchunk = batch_chunk(gq * M, B);
+    for (int64_t b0 = 0; b0 < B; b0 += bchunk) {
+        const int64_t nb = (B - b0) < bchunk ? (B - b0) : bchunk;
+        Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, p.pc, p.ps, (int)b0, (int)gq,
+                (int)wl.nb_max, 0};
+        hipLaunchKernelGGL((bwd_dots_kernel<D, VT>), dim3((unsigned)(gq * M * nb)),
+                           dim3(kThreads), p.lds + 4 * (size_t)hist_cap, s,
+                           static_cast<const VT *>(value), shapes, starts, loc, attn, gout, gloc,
+                           gattn, w.counts, hist_cap, dm);
         st = hip_status(hipGetLastError());
         if (st != MSDA_OK) return st;
     }
-    Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, 0, 0, 0, (int)wl.nb_max, accumulate ? 1 : 0};
+    Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, 0, 0, 0, 0, (int)wl.nb_max,
+            accumulate ? 1 : 0};
     hipLaunchKernelGGL(bin_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, shapes, starts,
-                       w.counts, w.start, w.cursor, w.items, w.work_total, (int)(B * M), dm);
+                       w.counts, w.start, w.cursor, w.items, w.work_total, (int)B, dm);
     st = hip_status(hipGetLastError());
     if (st != MSDA_OK) return st;
-    for (int64_t b0 = 0; b0 < B; b0 += 65535) {
-        const unsigned gb = (unsigned)((B - b0) < 65535 ? (B - b0) : 65535);
+    bchunk = batch_chunk(gs * M, B);
+    for (int64_t b0 = 0; b0 < B; b0 += bchunk) {
+        const int64_t nb = (B - b0) < bchunk ? (B - b0) : bchunk;
         Dims d2 = dm;
         d2.b0 = (int)b0;
-        hipLaunchKernelGGL(bin_scatter_kernel, dim3(gs, (unsigned)M, gb), dim3(kThreads),
+        d2.nblk = (int)gs;
+        hipLaunchKernelGGL(bin_scatter_kernel, dim3((unsigned)(gs * M * nb)), dim3(kThreads),
                            8 * (size_t)hist_cap, s, shapes, starts, loc, w.cursor, w.sorted,
                            hist_cap, d2);
         st = hip_status(hipGetLastError());
