@@ -2,22 +2,26 @@
 """Throughput of the MSDeformAttn sampling core on one MI355X.
 
 A step is one pass of the whole hot path over one batch: the forward
-(msda_forward) and the backward (msda_backward: grad_value fill + gradient
-kernel) at the Deformable-DETR encoder shape -- B=2, four levels 100x167,
+(msda_forward) and the backward (msda_backward: grad_value fill, gradient
+pipeline) at the Deformable-DETR encoder shape -- B=2, four levels 100x167,
 50x84, 25x42, 13x21 (Nv = 22,223), every pixel a query (Nq = Nv), M=8 heads,
 D=32, K=4, fp32.  Inputs are seeded synthetic data (workloads.make) resident
 in HBM before the timed region.
 
 Printed: one JSON line.  value = sampled points (B*Nq*M*L*K) per second of
-fwd+bwd steps.  "roofline" describes the dominant kernel: algorithmic bytes
-(each input read once, each output written once) over its average duration,
+fwd+bwd steps, timed with HIP events over `--steps` back-to-back steps.
+"roofline" describes the dominant kernel of a step: its algorithmic bytes
+(each tensor it must touch read or written once) over its average duration,
 timed with HIP events on the launch stream with the 256 MB last-level cache
-flushed before every launch, against the 8 TB/s HBM peak.  "cpu_baseline"
-times the CPU oracle on the same workload on this host's cores.
+flushed before every launch, against the 8 TB/s HBM peak; "traffic" is the
+HBM byte count rocprofv3 measured for that kernel (profiles/traffic.json),
+when it was taken on the current kernel source.  "cpu_baseline" times the CPU
+oracle on the same workload on this host's cores.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import statistics
@@ -30,24 +34,44 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 FLUSH_BYTES = 512 << 20   # > the 256 MB Infinity Cache
+KERNEL_SOURCE = os.path.join(ROOT, "scale_deformable_attention_04_amd", "csrc", "msda.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+# kernel names as rocprofv3 reports them, per stage of a step
+KERNELS = {
+    "forward": "msda_fwd_kernel<32, float>",
+    "fill_grad_value": "fill_zero_kernel",
+    "clear_bins": "fill_zero_kernel",
+    "dots": "bwd_dots_kernel<32, float>",
+    "scan": "bin_scan_kernel",
+    "scatter": "bin_scatter_kernel",
+    "tiles": "grad_value_tile_kernel<32>",
+}
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def source_sha() -> str:
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
 def byte_model(B, Nv, Nq, M, D, L, K, value_bytes=4):
-    """Algorithmic bytes: every input read once, every output written once."""
+    """Algorithmic bytes per kernel: every tensor it needs read or written once."""
     pts = B * Nq * M * L * K
     value = B * Nv * M * D * value_bytes
     loc, attn = pts * 2 * 4, pts * 4
-    out = B * Nq * M * D * 4
-    grad_value = B * Nv * M * D * 4
+    rows = B * Nq * M * D * 4           # out or grad_out
+    gvalue = B * Nv * M * D * 4
     return {
         "points": pts,
-        "fwd": value + loc + attn + out,
-        "bwd": value + loc + attn + out + grad_value + loc + attn,  # grad_out read; 3 grads written
-        "fill": grad_value,
+        "forward": value + loc + attn + rows,
+        "backward": value + loc + attn + rows + gvalue + loc + attn + gvalue,  # + fill
+        "fill_grad_value": gvalue,
+        "dots": value + loc + attn + rows + loc + attn,    # grad_loc, grad_attn written
+        "scatter": loc,
+        "tiles": loc + attn + rows + gvalue,
     }
 
 
@@ -66,8 +90,7 @@ def to_device(w, torch, bf16=False):
     return x, g
 
 
-def kernel_times(torch, fn, reps, flush=None):
-    """Average duration (s) of fn() over reps launches, HIP events on the current stream."""
+def time_forward(torch, fn, reps, flush):
     s = torch.cuda.current_stream()
     times = []
     for _ in range(reps):
@@ -79,8 +102,20 @@ def kernel_times(torch, fn, reps, flush=None):
         fn()
         e1.record(s)
         e1.synchronize()
-        times.append(e0.elapsed_time(e1) * 1e-3)
-    return statistics.mean(times), statistics.median(times)
+        times.append(e0.elapsed_time(e1) * 1e3)
+    return statistics.mean(times)
+
+
+def time_backward_stages(torch, msda, x, g, bufs, reps, flush):
+    """Mean per-stage us of msda_backward_timed (events between its launches)."""
+    acc = None
+    for _ in range(reps):
+        if flush is not None:
+            flush.fill_(1)
+        st = []
+        msda.backward(**x, grad_out=g, **bufs, validate=False, stage_us=st)
+        acc = st if acc is None else [a + b for a, b in zip(acc, st)]
+    return {k: v / reps for k, v in zip(msda.BWD_STAGES, acc)}
 
 
 def measure_config(torch, msda, w, bf16, reps, flush, label):
@@ -93,33 +128,25 @@ def measure_config(torch, msda, w, bf16, reps, flush, label):
     fwd = lambda: msda.forward(**x, out=out, validate=False)
     for _ in range(3):
         fwd()
-    mean_c, med_c = kernel_times(torch, fwd, reps, flush)
-    mean_w, _ = kernel_times(torch, fwd, reps, None)
-    res["fwd"] = {"us_cold": mean_c * 1e6, "us_warm": mean_w * 1e6,
-                  "points_per_s": bm["points"] / mean_c,
-                  "algorithmic_GBps": bm["fwd"] / mean_c / 1e9,
-                  "algorithmic_bytes": bm["fwd"]}
+    cold = time_forward(torch, fwd, reps, flush)
+    warm = time_forward(torch, fwd, reps, None)
+    res["forward"] = {"us_cold": cold, "us_warm": warm, "points_per_s": bm["points"] / cold * 1e6,
+                      "algorithmic_GBps": bm["forward"] / cold / 1e3,
+                      "algorithmic_bytes": bm["forward"]}
     if g is not None:
-        gv = torch.zeros(x["value"].shape, dtype=torch.float32, device="cuda")
-        gl = torch.empty_like(x["sampling_loc"])
-        ga = torch.empty_like(x["attn_weight"])
-        main = lambda: msda.backward(**x, grad_out=g, grad_value=gv, grad_sampling_loc=gl,
-                                     grad_attn_weight=ga, accumulate=True, validate=False)
-        full = lambda: msda.backward(**x, grad_out=g, grad_value=gv, grad_sampling_loc=gl,
-                                     grad_attn_weight=ga, validate=False)
+        bufs = dict(grad_value=torch.empty(x["value"].shape, dtype=torch.float32, device="cuda"),
+                    grad_sampling_loc=torch.empty_like(x["sampling_loc"]),
+                    grad_attn_weight=torch.empty_like(x["attn_weight"]))
         for _ in range(3):
-            full()
-        mean_c, _ = kernel_times(torch, main, reps, flush)
-        mean_w, _ = kernel_times(torch, main, reps, None)
-        mean_f, _ = kernel_times(torch, full, reps, flush)
-        res["bwd"] = {"us_cold": mean_c * 1e6, "us_warm": mean_w * 1e6,
-                      "us_cold_with_fill": mean_f * 1e6,
-                      "points_per_s": bm["points"] / mean_c,
-                      "algorithmic_GBps": bm["bwd"] / mean_c / 1e9,
-                      "algorithmic_bytes": bm["bwd"],
-                      "fill_bytes": bm["fill"]}
+            msda.backward(**x, grad_out=g, **bufs, validate=False)
+        stages = time_backward_stages(torch, msda, x, g, bufs, reps, flush)
+        total = sum(stages.values())
+        res["backward"] = {"us_cold": total, "stages_us": stages,
+                           "points_per_s": bm["points"] / total * 1e6,
+                           "algorithmic_GBps": bm["backward"] / total / 1e3,
+                           "algorithmic_bytes": bm["backward"]}
     log(f"{label}: {json.dumps(res)}")
-    return res, x, g
+    return res, x, g, bm
 
 
 def cpu_baseline(w, min_seconds=10.0):
@@ -137,7 +164,21 @@ def cpu_baseline(w, min_seconds=10.0):
     return {"value": pts / med, "unit": "points/s", "cores": oracle.max_threads(),
             "kind": "oracle",
             "sample": f"the whole encoder workload ({pts} points), forward + backward, "
-                      f"{len(times)} runs, median {med:.2f} s, fp64 accumulation"}
+                      f"{len(times)} runs, median {med:.2f} s per step, fp64 accumulation"}
+
+
+def traffic_for(kernel_name: str):
+    """HBM bytes per launch measured by rocprofv3 for this kernel on this source."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha") != source_sha():
+        return None
+    k = t.get("kernels", {}).get(kernel_name)
+    if not k:
+        return None
+    return int(k["fetch_bytes"] + k["write_bytes"])
 
 
 def main():
@@ -145,7 +186,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--reps", type=int, default=50, help="launches per kernel timing")
+    ap.add_argument("--reps", type=int, default=30, help="launches per kernel timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the decoder and bf16 configs")
     args = ap.parse_args()
@@ -168,10 +209,8 @@ def main():
 
     w = workloads.make(3)   # encoder shapes with grad_out
     dims = w.dims
-    bm = byte_model(**{k: dims[k] for k in ("B", "Nv", "Nq", "M", "D", "L", "K")})
     flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
-
-    enc, x, g = measure_config(torch, msda, w, False, args.reps, flush, "encoder")
+    enc, x, g, bm = measure_config(torch, msda, w, False, args.reps, flush, "encoder")
 
     # ---- timed region: K whole steps (fwd + bwd) -------------------------------------
     out = torch.empty(dims["B"], dims["Nq"], dims["M"] * dims["D"], device="cuda")
@@ -200,23 +239,24 @@ def main():
     step_s = e0.elapsed_time(e1) * 1e-3 / args.steps
     log(f"timed {args.steps} steps: {step_s * 1e6:.1f} us/step (events), wall {wall:.3f} s")
 
-    # dominant kernel: the longer of the forward and the backward gradient kernel
-    dom = "bwd" if enc["bwd"]["us_cold"] >= enc["fwd"]["us_cold"] else "fwd"
-    kern = {"fwd": "msda_fwd_kernel<32, float>", "bwd": "msda_bwd_kernel<32, float>"}[dom]
-    achieved = enc[dom]["algorithmic_GBps"]
+    # dominant kernel of a step
+    per_kernel = {"forward": enc["forward"]["us_cold"]}
+    per_kernel.update({k: v for k, v in enc["backward"]["stages_us"].items()})
+    dom = max((k for k in per_kernel if k in bm), key=lambda k: per_kernel[k])
+    us = per_kernel[dom]
+    achieved = bm[dom] / us / 1e3
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": kern,
-                "algorithmic_bytes_per_launch": enc[dom]["algorithmic_bytes"],
-                "avg_launch_us": round(enc[dom]["us_cold"], 2)}
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic_for(KERNELS[dom]), "kernel": KERNELS[dom],
+                "algorithmic_bytes_per_launch": bm[dom], "avg_launch_us": round(us, 2)}
 
     extra = {}
     if not args.no_extra:
-        dec, _, _ = measure_config(torch, msda, workloads.make(2), False, args.reps, flush,
-                                   "decoder")
-        extra["decoder_fwd"] = dec["fwd"]
-        trn, _, _ = measure_config(torch, msda, workloads.make(4), True, args.reps // 2, flush,
-                                   "train_bf16")
+        dec, _, _, _ = measure_config(torch, msda, workloads.make(2), False, args.reps, flush,
+                                      "decoder")
+        extra["decoder"] = dec
+        trn, _, _, _ = measure_config(torch, msda, workloads.make(4), True, max(5, args.reps // 3),
+                                      flush, "train_bf16")
         extra["train_bf16"] = trn
 
     result = {
@@ -238,8 +278,8 @@ def main():
                    "L": dims["L"], "K": dims["K"], "value_dtype": "fp32",
                    "points_per_step": bm["points"]},
         "roofline": roofline,
-        "fwd": enc["fwd"],
-        "bwd": enc["bwd"],
+        "encoder": enc,
+        "kernel_source_sha": source_sha(),
         **extra,
     }
     if not args.no_cpu_baseline:

@@ -135,6 +135,26 @@ msda_status msda_backward(const void *value, int value_dtype,
                           uint32_t flags, void *stream);
 
 /*
+ * Measurement entry point: msda_backward with the same arguments, followed by
+ * a synchronization of `stream`; stage_us[0..MSDA_BWD_STAGES) receives the
+ * duration in microseconds of each stage, timed with HIP events recorded on
+ * `stream` between the launches:
+ *   0 grad_value zero-fill (0 with MSDA_BWD_ACCUMULATE)   1 workspace clear
+ *   2 grad_attn_weight / grad_sampling_loc and tile counts   3 count scan
+ *   4 point scatter into tiles   5 grad_value tiles
+ * Not for production loops: it blocks the calling thread.
+ */
+#define MSDA_BWD_STAGES 6
+msda_status msda_backward_timed(const void *value, int value_dtype,
+                                const int64_t *spatial_shapes, const int64_t *level_start_index,
+                                const float *sampling_loc, const float *attn_weight,
+                                const float *grad_out, float *grad_value,
+                                float *grad_sampling_loc, float *grad_attn_weight,
+                                int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
+                                int64_t L, int64_t K, void *workspace, size_t workspace_bytes,
+                                uint32_t flags, void *stream, float *stage_us);
+
+/*
  * Pure host check of the sizes and of a HOST copy of the level table:
  * H_l, W_l >= 1, level_start_host[l] = sum of H*W of levels before l,
  * Nv = sum H*W, plus every limit msda_forward/msda_backward check.

@@ -28,7 +28,9 @@ MSDA_BF16 = 1
 MSDA_BWD_ACCUMULATE = 1
 
 EXPORTED = ("msda_forward", "msda_backward_workspace_size", "msda_backward",
-            "msda_validate_host", "msda_status_string", "msda_last_hip_error")
+            "msda_backward_timed", "msda_validate_host", "msda_status_string",
+            "msda_last_hip_error")
+BWD_STAGES = ("fill_grad_value", "clear_bins", "dots", "scan", "scatter", "tiles")
 
 _lib = None
 
@@ -57,6 +59,9 @@ def load():
     lib.msda_backward.argtypes = ([p, ci, p, p, p, p, p, p, p, p] + [i64] * 7 +
                                   [p, ctypes.c_size_t, u32, p])
     lib.msda_backward.restype = ci
+    lib.msda_backward_timed.argtypes = ([p, ci, p, p, p, p, p, p, p, p] + [i64] * 7 +
+                                        [p, ctypes.c_size_t, u32, p, p])
+    lib.msda_backward_timed.restype = ci
     lib.msda_backward_workspace_size.argtypes = [i64] * 7
     lib.msda_backward_workspace_size.restype = ctypes.c_size_t
     lib.msda_validate_host.argtypes = [p, p] + [i64] * 7
@@ -186,14 +191,17 @@ def backward(value: torch.Tensor, spatial_shapes: torch.Tensor, level_start_inde
              grad_sampling_loc: Optional[torch.Tensor] = None,
              grad_attn_weight: Optional[torch.Tensor] = None,
              accumulate: bool = False, validate: bool = True,
-             workspace: Optional[torch.Tensor] = None
+             workspace: Optional[torch.Tensor] = None, stage_us: Optional[list] = None
              ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """msda_backward: (grad_value fp32 [B,Nv,M,D], grad_sampling_loc, grad_attn_weight).
 
     accumulate=True adds into the given grad_value instead of overwriting it.
     workspace: a uint8 device tensor of at least workspace_size(...) bytes; by
     default a per-device buffer cached by this module is used (calls on
-    different streams that overlap in time must pass their own)."""
+    different streams that overlap in time must pass their own).
+    stage_us: if a list is given, msda_backward_timed is called instead (it
+    synchronizes) and the list receives the per-stage durations in us, in the
+    order of BWD_STAGES."""
     lib = load()
     dev, (B, Nv, Nq, M, D, L, K) = _check_inputs(value, spatial_shapes, level_start_index,
                                                 sampling_loc, attn_weight, validate)
@@ -219,13 +227,20 @@ def backward(value: torch.Tensor, spatial_shapes: torch.Tensor, level_start_inde
     elif workspace.device != dev or workspace.dtype != torch.uint8 or workspace.numel() < need:
         raise ValueError(f"workspace must be a uint8 tensor on {dev} of >= {need} bytes")
     ws_bytes = workspace.numel() if workspace is not None else 0
+    args = [_ptr(value), _dtype_code(value), _ptr(spatial_shapes), _ptr(level_start_index),
+            _ptr(sampling_loc), _ptr(attn_weight), _ptr(grad_out), _ptr(grad_value),
+            _ptr(grad_sampling_loc), _ptr(grad_attn_weight), B, Nv, Nq, M, D, L, K,
+            _ptr(workspace), ws_bytes, flags]
     with torch.cuda.device(dev):
-        stream = torch.cuda.current_stream(dev).cuda_stream
-        rc = lib.msda_backward(_ptr(value), _dtype_code(value), _ptr(spatial_shapes),
-                               _ptr(level_start_index), _ptr(sampling_loc), _ptr(attn_weight),
-                               _ptr(grad_out), _ptr(grad_value), _ptr(grad_sampling_loc),
-                               _ptr(grad_attn_weight), B, Nv, Nq, M, D, L, K,
-                               _ptr(workspace), ws_bytes, flags, ctypes.c_void_p(stream))
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        if stage_us is None:
+            rc = lib.msda_backward(*args, stream)
+            where = "msda_backward"
+        else:
+            times = (ctypes.c_float * len(BWD_STAGES))()
+            rc = lib.msda_backward_timed(*args, stream, times)
+            where = "msda_backward_timed"
+            stage_us[:] = list(times)
     if rc != MSDA_OK:
-        raise MSDAError(rc, "msda_backward")
+        raise MSDAError(rc, where)
     return grad_value, grad_sampling_loc, grad_attn_weight

@@ -905,7 +905,11 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
                        const float *loc, const float *attn, const float *gout, float *gval,
                        float *gloc, float *gattn, int64_t B, int64_t Nv, int64_t Nq, int64_t M,
                        int64_t L, int64_t K, const WorkLayout &wl, unsigned char *ws,
-                       bool accumulate, hipStream_t s) {
+                       bool accumulate, hipStream_t s, hipEvent_t *ev) {
+    // ev (optional): events recorded before each stage, for msda_backward_timed
+    auto mark = [&](int i) {
+        if (ev) (void)hipEventRecord(ev[i], s);
+    };
     Work w;
     w.counts = reinterpret_cast<uint32_t *>(ws + wl.off_counts);
     w.start = reinterpret_cast<uint32_t *>(ws + wl.off_start);
@@ -914,6 +918,7 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
     w.work_total = reinterpret_cast<uint32_t *>(ws + wl.off_total);
     w.sorted = reinterpret_cast<uint32_t *>(ws + wl.off_sorted);
     // the counts region is padded to 256 bytes, so whole float4s can be cleared
+    mark(1);
     msda_status st = fill_zero(w.counts, (wl.off_start - wl.off_counts) / 16, s);
     if (st != MSDA_OK) return st;
 
@@ -922,6 +927,7 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
     const int64_t gq = (Nq + p.ipb - 1) / p.ipb;
     const int64_t gs = (Nq + kScatterQueries - 1) / kScatterQueries;
     int64_t bchunk = batch_chunk(gq * M, B);
+    mark(2);
     for (int64_t b0 = 0; b0 < B; b0 += bchunk) {
         const int64_t nb = (B - b0) < bchunk ? (B - b0) : bchunk;
         Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, p.pc, p.ps, (int)b0, (int)gq,
@@ -935,11 +941,13 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
     }
     Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, 0, 0, 0, 0, (int)wl.nb_max,
             accumulate ? 1 : 0};
+    mark(3);
     hipLaunchKernelGGL(bin_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, shapes, starts,
                        w.counts, w.start, w.cursor, w.items, w.work_total, (int)B, dm);
     st = hip_status(hipGetLastError());
     if (st != MSDA_OK) return st;
     bchunk = batch_chunk(gs * M, B);
+    mark(4);
     for (int64_t b0 = 0; b0 < B; b0 += bchunk) {
         const int64_t nb = (B - b0) < bchunk ? (B - b0) : bchunk;
         Dims d2 = dm;
@@ -952,10 +960,13 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
         if (st != MSDA_OK) return st;
     }
     const int64_t grid = wl.work_max < kTileGrid ? wl.work_max : kTileGrid;
+    mark(5);
     hipLaunchKernelGGL((grad_value_tile_kernel<D>), dim3((unsigned)grid), dim3(kTileThreads), 0, s,
                        shapes, starts, loc, attn, gout, w.counts, w.start, w.items,
                        w.work_total, w.sorted, gval, dm);
-    return hip_status(hipGetLastError());
+    st = hip_status(hipGetLastError());
+    mark(6);
+    return st;
 }
 
 template <typename VT>
@@ -984,11 +995,12 @@ msda_status dispatch_bwd(int64_t D, const void *value, const int64_t *shapes,
                          const int64_t *starts, const float *loc, const float *attn,
                          const float *gout, float *gval, float *gloc, float *gattn, int64_t B,
                          int64_t Nv, int64_t Nq, int64_t M, int64_t L, int64_t K,
-                         const WorkLayout &wl, unsigned char *ws, bool acc, hipStream_t s) {
+                         const WorkLayout &wl, unsigned char *ws, bool acc, hipStream_t s,
+                         hipEvent_t *ev) {
 #define MSDA_BWD_CASE(DD)                                                                      \
     case DD:                                                                                   \
         return launch_bwd<DD, VT>(value, shapes, starts, loc, attn, gout, gval, gloc, gattn, B, \
-                                  Nv, Nq, M, L, K, wl, ws, acc, s);
+                                  Nv, Nq, M, L, K, wl, ws, acc, s, ev);
     switch (D) {
         MSDA_BWD_CASE(4)
         MSDA_BWD_CASE(8)
@@ -1031,17 +1043,20 @@ size_t msda_backward_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int64_t M
     return work_layout(B, Nv, Nq, M, L, K).bytes;
 }
 
-msda_status msda_backward(const void *value, int value_dtype, const int64_t *spatial_shapes,
+}  // extern "C"
+
+namespace {
+
+msda_status backward_impl(const void *value, int value_dtype, const int64_t *spatial_shapes,
                           const int64_t *level_start_index, const float *sampling_loc,
                           const float *attn_weight, const float *grad_out, float *grad_value,
                           float *grad_sampling_loc, float *grad_attn_weight, int64_t B,
                           int64_t Nv, int64_t Nq, int64_t M, int64_t D, int64_t L, int64_t K,
                           void *workspace, size_t workspace_bytes, uint32_t flags,
-                          void *stream) {
+                          hipStream_t s, hipEvent_t *ev) {
     msda_status st = check_sizes(value_dtype, B, Nv, Nq, M, D, L, K);
     if (st != MSDA_OK) return st;
     if (flags & ~MSDA_BWD_ACCUMULATE) return MSDA_ERR_UNSUPPORTED;
-    hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t nval = B * Nv * M * D;
     if (nval > 0 && !grad_value) return MSDA_ERR_NULL;
     const bool work = B > 0 && Nq > 0;
@@ -1056,20 +1071,75 @@ msda_status msda_backward(const void *value, int value_dtype, const int64_t *spa
         if (workspace_bytes < wl.bytes) return MSDA_ERR_WORKSPACE;
         if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return MSDA_ERR_WORKSPACE;
     }
+    if (ev) (void)hipEventRecord(ev[0], s);
     if (!(flags & MSDA_BWD_ACCUMULATE)) {
         st = fill_zero(grad_value, (size_t)nval / 4, s);  // D is a multiple of 4
         if (st != MSDA_OK) return st;
     }
-    if (!work) return MSDA_OK;
+    if (!work) {
+        if (ev)
+            for (int i = 1; i < 7; ++i) (void)hipEventRecord(ev[i], s);
+        return MSDA_OK;
+    }
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     const bool acc = (flags & MSDA_BWD_ACCUMULATE) != 0;
     if (value_dtype == MSDA_F32)
         return dispatch_bwd<float>(D, value, spatial_shapes, level_start_index, sampling_loc,
                                    attn_weight, grad_out, grad_value, grad_sampling_loc,
-                                   grad_attn_weight, B, Nv, Nq, M, L, K, wl, ws, acc, s);
+                                   grad_attn_weight, B, Nv, Nq, M, L, K, wl, ws, acc, s, ev);
     return dispatch_bwd<uint16_t>(D, value, spatial_shapes, level_start_index, sampling_loc,
                                   attn_weight, grad_out, grad_value, grad_sampling_loc,
-                                  grad_attn_weight, B, Nv, Nq, M, L, K, wl, ws, acc, s);
+                                  grad_attn_weight, B, Nv, Nq, M, L, K, wl, ws, acc, s, ev);
+}
+
+}  // namespace
+
+extern "C" {
+
+msda_status msda_backward(const void *value, int value_dtype, const int64_t *spatial_shapes,
+                          const int64_t *level_start_index, const float *sampling_loc,
+                          const float *attn_weight, const float *grad_out, float *grad_value,
+                          float *grad_sampling_loc, float *grad_attn_weight, int64_t B,
+                          int64_t Nv, int64_t Nq, int64_t M, int64_t D, int64_t L, int64_t K,
+                          void *workspace, size_t workspace_bytes, uint32_t flags,
+                          void *stream) {
+    return backward_impl(value, value_dtype, spatial_shapes, level_start_index, sampling_loc,
+                         attn_weight, grad_out, grad_value, grad_sampling_loc, grad_attn_weight,
+                         B, Nv, Nq, M, D, L, K, workspace, workspace_bytes, flags,
+                         static_cast<hipStream_t>(stream), nullptr);
+}
+
+msda_status msda_backward_timed(const void *value, int value_dtype,
+                                const int64_t *spatial_shapes, const int64_t *level_start_index,
+                                const float *sampling_loc, const float *attn_weight,
+                                const float *grad_out, float *grad_value,
+                                float *grad_sampling_loc, float *grad_attn_weight, int64_t B,
+                                int64_t Nv, int64_t Nq, int64_t M, int64_t D, int64_t L,
+                                int64_t K, void *workspace, size_t workspace_bytes,
+                                uint32_t flags, void *stream, float *stage_us) {
+    if (!stage_us) return MSDA_ERR_NULL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipEvent_t ev[7];
+    int made = 0;
+    msda_status st = MSDA_OK;
+    for (; made < 7; ++made) {
+        st = hip_status(hipEventCreate(&ev[made]));
+        if (st != MSDA_OK) break;
+    }
+    if (st == MSDA_OK) {
+        st = backward_impl(value, value_dtype, spatial_shapes, level_start_index, sampling_loc,
+                           attn_weight, grad_out, grad_value, grad_sampling_loc,
+                           grad_attn_weight, B, Nv, Nq, M, D, L, K, workspace, workspace_bytes,
+                           flags, s, ev);
+        if (st == MSDA_OK) st = hip_status(hipEventSynchronize(ev[6]));
+        for (int i = 0; i < MSDA_BWD_STAGES && st == MSDA_OK; ++i) {
+            float ms = 0.f;
+            st = hip_status(hipEventElapsedTime(&ms, ev[i], ev[i + 1]));
+            stage_us[i] = 1000.f * ms;
+        }
+    }
+    for (int i = 0; i < made; ++i) (void)hipEventDestroy(ev[i]);
+    return st;
 }
 
 msda_status msda_validate_host(const int64_t *spatial_shapes_host, const int64_t *level_start_host,

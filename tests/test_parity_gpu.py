@@ -294,3 +294,18 @@ def test_backward_repeatability(msda):
     assert spread <= 1e-5
     for r in runs[1:]:
         assert torch.equal(r[1], ref[1]) and torch.equal(r[2], ref[2])
+
+
+def test_timed_backward_matches_and_reports_stages(msda):
+    """msda_backward_timed gives the same gradients and a duration per stage."""
+    w = workloads.random_case(900, 2, ((9, 13), (5, 7)), 70, 4, 32, 4)
+    x = dev_inputs(w)
+    g = torch.from_numpy(w.grad_out).cuda()
+    _say("timed backward")
+    st = []
+    gv, gl, ga = msda.backward(**x, grad_out=g, stage_us=st)
+    assert len(st) == len(msda.BWD_STAGES) and all(t >= 0.0 for t in st) and sum(st) > 0.0
+    rv, rl, ra = oracle_bwd(w)
+    close(gv.cpu().numpy(), rv, BWD_TOL)
+    close(gl.cpu().numpy(), rl, BWD_TOL)
+    close(ga.cpu().numpy(), ra, BWD_TOL)
