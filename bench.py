@@ -42,6 +42,7 @@ KERNELS = {
     "forward": "msda_fwd_kernel<32, float>",
     "fill_grad_value": "fill_zero_kernel",
     "clear_bins": "fill_zero_kernel",
+    "count": "bin_count_kernel",
     "dots": "bwd_dots_kernel<32, float>",
     "scan": "bin_scan_kernel",
     "scatter": "bin_scatter_kernel",
@@ -69,9 +70,10 @@ def byte_model(B, Nv, Nq, M, D, L, K, value_bytes=4):
         "forward": value + loc + attn + rows,
         "backward": value + loc + attn + rows + gvalue + loc + attn + gvalue,  # + fill
         "fill_grad_value": gvalue,
+        "count": loc,
         "dots": value + loc + attn + rows + loc + attn,    # grad_loc, grad_attn written
-        "scatter": loc,
-        "tiles": loc + attn + rows + gvalue,
+        "scatter": loc + attn,
+        "tiles": rows + gvalue,
     }
 
 

@@ -51,7 +51,8 @@
  * that does not fit inside value contributes zero.
  *
  * Limits.  D in {4, 8, 16, 32, 64, 128, 256}; 1 <= L <= 16; K >= 1;
- * Nv*M*D*4 < 2^31 bytes (one batch slice of grad_value); Nq*M*L*K*2 < 2^31.
+ * Nv*M*D*4 < 2^31 bytes (one batch slice of grad_value); Nq*M*L*K*2 < 2^31;
+ * B*Nq*M*L*K*4 < 2^32.  msda_backward also needs Nq <= 2^25.
  * B, Nq may be 0 (nothing is launched, except the grad_value fill).
  */
 #ifndef MSDA_H
@@ -95,8 +96,9 @@ msda_status msda_forward(const void *value, int value_dtype,
 /*
  * Bytes of device workspace msda_backward needs for these sizes (0 when
  * nothing is launched or the sizes are invalid).  It depends on the sizes
- * only, not on the level table, and is at most about 16 bytes per sampling
- * point plus 12 bytes per 8x8 value tile and head.
+ * only, not on the level table: 64 bytes per sampling point (room for one
+ * 16-byte record per 8x8 value tile the point's neighbours touch, at most
+ * four) plus about 16 bytes per tile bound and head.
  */
 size_t msda_backward_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
                                     int64_t L, int64_t K);
@@ -140,11 +142,11 @@ msda_status msda_backward(const void *value, int value_dtype,
  * duration in microseconds of each stage, timed with HIP events recorded on
  * `stream` between the launches:
  *   0 grad_value zero-fill (0 with MSDA_BWD_ACCUMULATE)   1 workspace clear
- *   2 grad_attn_weight / grad_sampling_loc and tile counts   3 count scan
- *   4 point scatter into tiles   5 grad_value tiles
+ *   2 points per value tile   3 grad_attn_weight / grad_sampling_loc
+ *   4 count scan   5 record scatter into tiles   6 grad_value tiles
  * Not for production loops: it blocks the calling thread.
  */
-#define MSDA_BWD_STAGES 6
+#define MSDA_BWD_STAGES 7
 msda_status msda_backward_timed(const void *value, int value_dtype,
                                 const int64_t *spatial_shapes, const int64_t *level_start_index,
                                 const float *sampling_loc, const float *attn_weight,

@@ -40,6 +40,7 @@
 // memory.
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 #include "msda.h"
@@ -56,7 +57,6 @@ constexpr int kTile = 1 << kTileShift;
 constexpr int kTilePx = kTile * kTile;
 constexpr int kChunk = 2048;               // points per grad_value work item, at most
 constexpr int kHistLds = 4096;             // bins of one (batch, head) kept in an LDS histogram
-constexpr int kScatterQueries = 64;        // queries per scatter workgroup
 constexpr int kScanThreads = 1024;
 constexpr int kTileGrid = 2048;            // persistent workgroups of the tile kernel
 
@@ -154,6 +154,14 @@ struct Neighbours {
     uint32_t valid;  // bit c: neighbour c inside the map
 };
 
+// Bilinear weights of the four neighbours from the fractional parts; 0 for a
+// neighbour outside the map (bit c of `valid` clear).
+__device__ __forceinline__ float4 tent_weights(float fx, float fy, uint32_t valid) {
+    const float gx = 1.f - fx, gy = 1.f - fy;
+    return make_float4((valid & 1u) ? gx * gy : 0.f, (valid & 2u) ? fx * gy : 0.f,
+                       (valid & 4u) ? gx * fy : 0.f, (valid & 8u) ? fx * fy : 0.f);
+}
+
 __device__ __forceinline__ Neighbours neighbours(float u, float v, int4 lvl, uint32_t row_stride,
                                                  uint32_t head_off) {
     const int H = lvl.x, W = lvl.y, S = lvl.z;
@@ -179,12 +187,8 @@ __device__ __forceinline__ Neighbours neighbours(float u, float v, int4 lvl, uin
     n.off.y = vTR ? oTL + row_stride : kOOB;
     n.off.z = vBL ? oTL + (uint32_t)W * row_stride : kOOB;
     n.off.w = vBR ? oTL + (uint32_t)(W + 1) * row_stride : kOOB;
-    const float gx = 1.f - n.fx, gy = 1.f - n.fy;
-    n.w.x = vTL ? gx * gy : 0.f;
-    n.w.y = vTR ? n.fx * gy : 0.f;
-    n.w.z = vBL ? gx * n.fy : 0.f;
-    n.w.w = vBR ? n.fx * n.fy : 0.f;
     n.valid = (vTL ? 1u : 0u) | (vTR ? 2u : 0u) | (vBL ? 4u : 0u) | (vBR ? 8u : 0u);
+    n.w = tent_weights(n.fx, n.fy, n.valid);
     return n;
 }
 
@@ -205,6 +209,23 @@ __device__ __forceinline__ int point_bins(const Neighbours &n, int4 lvl, int tw,
     return k;
 }
 
+// The same tiles as point_bins, as tile coordinates packed (ty << 16) | tx.
+__device__ __forceinline__ int point_tiles(const Neighbours &n, uint32_t tiles[4]) {
+    if (!n.valid) return 0;
+    // x0 = -1 gives tile -1, which only ever holds outside neighbours
+    const int tx0 = n.xi >> kTileShift, tx1 = (n.xi + 1) >> kTileShift;
+    const int ty0 = n.yi >> kTileShift, ty1 = (n.yi + 1) >> kTileShift;
+    const bool sx = tx1 != tx0, sy = ty1 != ty0;
+    const bool vTL = n.valid & 1u, vTR = n.valid & 2u, vBL = n.valid & 4u, vBR = n.valid & 8u;
+    auto pack = [](int tx, int ty) { return ((uint32_t)ty << 16) | (uint32_t)tx; };
+    int k = 0;
+    if (vTL || (!sx && vTR) || (!sy && vBL) || (!sx && !sy && vBR)) tiles[k++] = pack(tx0, ty0);
+    if (sx && (vTR || (!sy && vBR))) tiles[k++] = pack(tx1, ty0);
+    if (sy && (vBL || (!sx && vBR))) tiles[k++] = pack(tx0, ty1);
+    if (sx && sy && vBR) tiles[k++] = pack(tx1, ty1);
+    return k;
+}
+
 __device__ __forceinline__ void fma4(float4 &acc, float w, const float4 &v) {
     acc.x = __builtin_fmaf(w, v.x, acc.x);
     acc.y = __builtin_fmaf(w, v.y, acc.y);
@@ -214,10 +235,6 @@ __device__ __forceinline__ void fma4(float4 &acc, float w, const float4 &v) {
 
 __device__ __forceinline__ float dot4(const float4 &a, const float4 &b) {
     return __builtin_fmaf(a.w, b.w, __builtin_fmaf(a.z, b.z, __builtin_fmaf(a.y, b.y, a.x * b.x)));
-}
-
-__device__ __forceinline__ float pick(const float4 &v, int c) {
-    return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
 }
 
 // Workgroup ids are dispatched round-robin over the 8 XCDs (workgroup k runs
@@ -248,9 +265,9 @@ struct Work {
     uint32_t *counts;      // [B][nb_max][M] points per bin
     uint32_t *start;       // [B][nb_max][M] first entry of each bin in `sorted`
     uint32_t *cursor;      // [B][nb_max][M] next free entry while scattering
-    uint2 *items;          // [work_max] (bin, chunk)
+    uint4 *items;          // [work_max] (bin, first record, records, whole bin)
     uint32_t *work_total;  // [1]
-    uint32_t *sorted;      // [4 * points] point indices grouped by bin
+    uint4 *recs;           // [4 * points] records grouped by bin
 };
 
 // ---------------------------------------------------------------------------
@@ -329,25 +346,23 @@ msda_fwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
 }
 
 // ---------------------------------------------------------------------------
-// backward 1: grad_attn_weight, grad_sampling_loc, bin counts
-// Workgroup = (batch b, head m, IPB consecutive queries).
+// backward: grad_attn_weight and grad_sampling_loc
+// Workgroup = (batch b, head m, IPB consecutive queries).  Per point the
+// table holds the four row offsets (later overwritten by the four dot
+// products <grad_out row, value row>) and (fx, fy, A, valid bits).
 // ---------------------------------------------------------------------------
 template <int D, typename VT>
 __global__ void __launch_bounds__(kThreads)
 bwd_dots_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes,
                 const int64_t *__restrict__ starts, const float *__restrict__ loc,
                 const float *__restrict__ attn, const float *__restrict__ grad_out,
-                float *__restrict__ grad_loc, float *__restrict__ grad_attn,
-                uint32_t *__restrict__ counts, int hist_cap, Dims dm) {
+                float *__restrict__ grad_loc, float *__restrict__ grad_attn, Dims dm) {
     constexpr int G = D / 4;
     constexpr int IPB = kThreads / G;
     __shared__ LevelLds s_lv;
     extern __shared__ __align__(16) unsigned char smem[];
-    uint4 *s_off = reinterpret_cast<uint4 *>(smem);
-    float4 *s_w = reinterpret_cast<float4 *>(s_off + IPB * dm.PS);
-    float4 *s_aux = s_w + IPB * dm.PS;    // (fx, fy, A, valid bits)
-    float4 *s_dot = s_aux + IPB * dm.PS;  // <g, row> of the four neighbours
-    uint32_t *s_hist = reinterpret_cast<uint32_t *>(s_dot + IPB * dm.PS);
+    uint4 *s_off = reinterpret_cast<uint4 *>(smem);  // row offsets, then the dots
+    float4 *s_aux = reinterpret_cast<float4 *>(s_off + IPB * dm.PS);
 
     const int M = dm.M, K = dm.K, LK = dm.L * dm.K, Nq = dm.Nq;
     const int wg = xcd_contiguous(blockIdx.x, gridDim.x);
@@ -358,13 +373,7 @@ bwd_dots_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
     const uint32_t row_stride = (uint32_t)M * D * 4u;
     const uint32_t head_off = (uint32_t)m * D * 4u;
 
-    stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
-    const int nbins = s_lv.nbins;
-    const bool lds_hist = nbins <= hist_cap;
-    // bins are laid out (batch, tile, head): tile i of this (b, m) is gcount[i * M]
-    uint32_t *gcount = counts + (size_t)b * dm.nb_max * M + m;
-    if (lds_hist)
-        for (int i = threadIdx.x; i < nbins; i += kThreads) s_hist[i] = 0u;
+    stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, 0x7fffffff);
 
     const size_t slice = (size_t)dm.Nv * M * D;
     const rsrc_t vr = make_rsrc(value + (size_t)b * slice, (uint32_t)(slice * sizeof(VT)));
@@ -387,31 +396,19 @@ bwd_dots_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
 
     for (int j0 = 0; j0 < LK; j0 += dm.PC) {
         const int pc = min(dm.PC, LK - j0);
-        __syncthreads();  // histogram zeroed / previous chunk consumed
+        if (j0) __syncthreads();  // previous chunk consumed
         for (int idx = threadIdx.x; idx < nitems * pc; idx += kThreads) {
             const int i1 = idx / pc, jj = idx - i1 * pc, j = j0 + jj;
             const size_t p = pt0 + (size_t)i1 * M * LK + j;
             const float2 uv = reinterpret_cast<const float2 *>(loc)[p];
             const float A = attn[p];
-            const int l = j / K;
-            const int4 lvl = s_lv.lvl[l];
-            Neighbours n = neighbours(uv.x, uv.y, lvl, row_stride, head_off);
+            const Neighbours n = neighbours(uv.x, uv.y, s_lv.lvl[j / K], row_stride, head_off);
             s_off[i1 * dm.PS + jj] = n.off;
-            s_w[i1 * dm.PS + jj] = n.w;
             s_aux[i1 * dm.PS + jj] = make_float4(n.fx, n.fy, A, __uint_as_float(n.valid));
-            int bins[4];
-            const int nb = point_bins(n, lvl, s_lv.tw[l], bins);
-            for (int k = 0; k < nb; ++k) {
-                if (lds_hist)
-                    atomicAdd(&s_hist[bins[k]], 1u);
-                else
-                    atomicAdd(&gcount[(size_t)bins[k] * M], 1u);
-            }
         }
         __syncthreads();
         if (it < nitems) {
             const int base = it * dm.PS;
-#pragma unroll 2
             for (int jj = 0; jj < pc; ++jj) {
                 const uint4 o = s_off[base + jj];
                 const float4 v0 = Row4<VT>::load(vr, o.x, 4 * c);
@@ -422,32 +419,91 @@ bwd_dots_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
                 const float d1 = group_sum<G>(dot4(g4, v1));
                 const float d2 = group_sum<G>(dot4(g4, v2));
                 const float d3 = group_sum<G>(dot4(g4, v3));
-                if (c == 0) s_dot[base + jj] = make_float4(d0, d1, d2, d3);
+                // the group's lanes are one wave: every lane has read the
+                // offsets before lane 0 overwrites them
+                if (c == 0)
+                    s_off[base + jj] = make_uint4(__float_as_uint(d0), __float_as_uint(d1),
+                                                  __float_as_uint(d2), __float_as_uint(d3));
             }
         }
         __syncthreads();
         for (int idx = threadIdx.x; idx < nitems * pc; idx += kThreads) {
             const int i1 = idx / pc, jj = idx - i1 * pc, j = j0 + jj;
             const size_t p = pt0 + (size_t)i1 * M * LK + j;
-            const float4 d = s_dot[i1 * dm.PS + jj];
-            const float4 w = s_w[i1 * dm.PS + jj];
+            const uint4 du = s_off[i1 * dm.PS + jj];
             const float4 ax = s_aux[i1 * dm.PS + jj];
             const int4 lvl = s_lv.lvl[j / K];
             float ga = 0.f, gx = 0.f, gy = 0.f;
-            if (__float_as_uint(ax.w) != 0u) {
+            const uint32_t valid = __float_as_uint(ax.w);
+            if (valid != 0u) {
+                const float d0 = __uint_as_float(du.x), d1 = __uint_as_float(du.y);
+                const float d2 = __uint_as_float(du.z), d3 = __uint_as_float(du.w);
                 const float fx = ax.x, fy = ax.y, A = ax.z;
-                ga = w.x * d.x + w.y * d.y + w.z * d.z + w.w * d.w;
-                gx = A * (float)lvl.y * ((1.f - fy) * (d.y - d.x) + fy * (d.w - d.z));
-                gy = A * (float)lvl.x * ((1.f - fx) * (d.z - d.x) + fx * (d.w - d.y));
+                const float4 w = tent_weights(fx, fy, valid);
+                ga = w.x * d0 + w.y * d1 + w.z * d2 + w.w * d3;
+                gx = A * (float)lvl.y * ((1.f - fy) * (d1 - d0) + fy * (d3 - d2));
+                gy = A * (float)lvl.x * ((1.f - fx) * (d2 - d0) + fx * (d3 - d1));
             }
             grad_attn[p] = ga;
             reinterpret_cast<float2 *>(grad_loc)[p] = make_float2(gx, gy);
         }
     }
-    if (lds_hist) {
+}
+
+// ---------------------------------------------------------------------------
+// backward: points per bin
+// Workgroup = (batch b, head m, kBinPoints consecutive points of the
+// (b, m) list in (query, level, point) order), kBinPPT points per thread.
+// ---------------------------------------------------------------------------
+constexpr int kBinPoints = 1024;
+constexpr int kBinPPT = kBinPoints / kThreads;
+
+__global__ void __launch_bounds__(kThreads)
+bin_count_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ starts,
+                 const float *__restrict__ loc, uint32_t *__restrict__ counts, int hist_cap,
+                 Dims dm) {
+    __shared__ LevelLds s_lv;
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint32_t *s_cnt = reinterpret_cast<uint32_t *>(smem);  // [hist_cap]
+
+    const int M = dm.M, K = dm.K, LK = dm.L * dm.K, Nq = dm.Nq;
+    const int wg = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int bm = wg / dm.nblk + dm.b0 * M;
+    const int m = bm % M, b = bm / M;
+    const int f0 = (wg % dm.nblk) * kBinPoints;
+    const int nf = Nq * LK;
+
+    stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
+    const int nbins = s_lv.nbins;
+    const bool lds = nbins <= hist_cap;
+    uint32_t *gcount = counts + (size_t)b * dm.nb_max * M + m;  // tile i at gcount[i * M]
+    if (lds) {
+        for (int i = threadIdx.x; i < nbins; i += kThreads) s_cnt[i] = 0u;
+        __syncthreads();
+    }
+#pragma unroll
+    for (int r = 0; r < kBinPPT; ++r) {
+        const int f = f0 + threadIdx.x + r * kThreads;
+        if (f < nf) {
+            const int q = f / LK, j = f - q * LK;
+            const size_t p = (((size_t)b * Nq + q) * M + m) * LK + j;
+            const float2 uv = reinterpret_cast<const float2 *>(loc)[p];
+            const int l = j / K;
+            const Neighbours n = neighbours(uv.x, uv.y, s_lv.lvl[l], 0u, 0u);
+            int bins[4];
+            const int nb = point_bins(n, s_lv.lvl[l], s_lv.tw[l], bins);
+            for (int k = 0; k < nb; ++k) {
+                if (lds)
+                    atomicAdd(&s_cnt[bins[k]], 1u);
+                else
+                    atomicAdd(&gcount[(size_t)bins[k] * M], 1u);
+            }
+        }
+    }
+    if (lds) {
         __syncthreads();
         for (int i = threadIdx.x; i < nbins; i += kThreads) {
-            const uint32_t v = s_hist[i];
+            const uint32_t v = s_cnt[i];
             if (v) atomicAdd(&gcount[(size_t)i * M], v);
         }
     }
@@ -482,7 +538,7 @@ __device__ __forceinline__ void block_exclusive_scan2(uint32_t &a, uint32_t &b, 
 __global__ void __launch_bounds__(kScanThreads)
 bin_scan_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ starts,
                 const uint32_t *__restrict__ counts, uint32_t *__restrict__ start,
-                uint32_t *__restrict__ cursor, uint2 *__restrict__ items,
+                uint32_t *__restrict__ cursor, uint4 *__restrict__ items,
                 uint32_t *__restrict__ work_total, int B, Dims dm) {
     constexpr int kPer = 8;
     __shared__ LevelLds s_lv;
@@ -516,7 +572,10 @@ bin_scan_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ 
                 start[bin] = e;
                 cursor[bin] = e;
                 const uint32_t nch = (cnt[i] + kChunk - 1) / kChunk;
-                for (uint32_t k = 0; k < nch; ++k) items[ch + k] = make_uint2(bin, k);
+                for (uint32_t k = 0; k < nch; ++k)
+                    items[ch + k] = make_uint4(bin, e + k * kChunk,
+                                               min((uint32_t)kChunk, cnt[i] - k * kChunk),
+                                               nch == 1 ? 1u : 0u);
                 e += cnt[i];
                 ch += nch;
             }
@@ -528,13 +587,21 @@ bin_scan_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// backward 3: scatter point indices into their bins
-// Workgroup = (batch b, head m, kScatterQueries consecutive queries).
+// backward: one record per (point, bin), scattered into the bins
+// Same workgroups as bin_count_kernel.  A record holds what the tile kernel
+// needs of the point: (q << 7 | cell, A * (1 - fx), A * fx, fy), where cell =
+// (x0 - tile x + 1) + 9 * (y0 - tile y + 1) places the point's top-left
+// neighbour in the 9x9 grid made of the tile and the column and row before it.
 // ---------------------------------------------------------------------------
+constexpr int kCellsW = kTile + 1;
+constexpr int kCells = kCellsW * kCellsW;
+constexpr int kRecQueryShift = 7;  // cells < 128
+
 __global__ void __launch_bounds__(kThreads)
 bin_scatter_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ starts,
-                   const float *__restrict__ loc, uint32_t *__restrict__ cursor,
-                   uint32_t *__restrict__ sorted, int hist_cap, Dims dm) {
+                   const float *__restrict__ loc, const float *__restrict__ attn,
+                   uint32_t *__restrict__ cursor, uint4 *__restrict__ recs, int hist_cap,
+                   Dims dm) {
     __shared__ LevelLds s_lv;
     extern __shared__ __align__(16) unsigned char smem[];
     uint32_t *s_cnt = reinterpret_cast<uint32_t *>(smem);  // [hist_cap] counts, then ranks
@@ -544,229 +611,338 @@ bin_scatter_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict
     const int wg = xcd_contiguous(blockIdx.x, gridDim.x);
     const int bm = wg / dm.nblk + dm.b0 * M;
     const int m = bm % M, b = bm / M;
-    const int q0 = (wg % dm.nblk) * kScatterQueries;
-    const int nq = min(kScatterQueries, Nq - q0);
-    const size_t row0 = ((size_t)b * Nq + q0) * M + m;
-    const int npts = nq * LK;
+    const int f0 = (wg % dm.nblk) * kBinPoints;
+    const int nf = Nq * LK;
 
     stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
     const int nbins = s_lv.nbins;
+    const bool lds = nbins <= hist_cap;
     uint32_t *gcur = cursor + (size_t)b * dm.nb_max * M + m;  // tile i at gcur[i * M]
-    if (nbins > hist_cap) {  // too many bins for LDS: reserve one slot at a time
-        for (int idx = threadIdx.x; idx < npts; idx += kThreads) {
-            const int i1 = idx / LK, j = idx - i1 * LK;
-            const size_t p = (row0 + (size_t)i1 * M) * LK + j;
+    if (lds) {
+        for (int i = threadIdx.x; i < nbins; i += kThreads) s_cnt[i] = 0u;
+        __syncthreads();
+    }
+
+    // the thread's points, kept for the second pass
+    Neighbours nb[kBinPPT];
+    float a0[kBinPPT], a1[kBinPPT];
+    int qq[kBinPPT], ll[kBinPPT];
+#pragma unroll
+    for (int r = 0; r < kBinPPT; ++r) {
+        const int f = f0 + threadIdx.x + r * kThreads;
+        nb[r].valid = 0u;
+        qq[r] = 0;
+        ll[r] = 0;
+        a0[r] = a1[r] = 0.f;
+        if (f < nf) {
+            const int q = f / LK, j = f - q * LK;
+            const size_t p = (((size_t)b * Nq + q) * M + m) * LK + j;
             const float2 uv = reinterpret_cast<const float2 *>(loc)[p];
+            const float A = attn[p];
             const int l = j / K;
-            Neighbours n = neighbours(uv.x, uv.y, s_lv.lvl[l], 0u, 0u);
-            int bins[4];
-            const int nb = point_bins(n, s_lv.lvl[l], s_lv.tw[l], bins);
-            for (int k = 0; k < nb; ++k)
-                sorted[atomicAdd(&gcur[(size_t)bins[k] * M], 1u)] = (uint32_t)p;
+            nb[r] = neighbours(uv.x, uv.y, s_lv.lvl[l], 0u, 0u);
+            qq[r] = q;
+            ll[r] = l;
+            a0[r] = A * (1.f - nb[r].fx);
+            a1[r] = A * nb[r].fx;
+            if (lds) {
+                uint32_t t[4];
+                const int nt = point_tiles(nb[r], t);
+                for (int k = 0; k < nt; ++k)
+                    atomicAdd(&s_cnt[s_lv.lvl[l].w + (int)(t[k] >> 16) * s_lv.tw[l] +
+                                     (int)(t[k] & 0xffffu)],
+                              1u);
+            }
         }
-        return;
     }
-    for (int i = threadIdx.x; i < nbins; i += kThreads) s_cnt[i] = 0u;
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < npts; idx += kThreads) {
-        const int i1 = idx / LK, j = idx - i1 * LK;
-        const size_t p = (row0 + (size_t)i1 * M) * LK + j;
-        const float2 uv = reinterpret_cast<const float2 *>(loc)[p];
-        const int l = j / K;
-        Neighbours n = neighbours(uv.x, uv.y, s_lv.lvl[l], 0u, 0u);
-        int bins[4];
-        const int nb = point_bins(n, s_lv.lvl[l], s_lv.tw[l], bins);
-        for (int k = 0; k < nb; ++k) atomicAdd(&s_cnt[bins[k]], 1u);
+    if (lds) {
+        __syncthreads();
+        for (int i = threadIdx.x; i < nbins; i += kThreads) {
+            const uint32_t v = s_cnt[i];
+            s_base[i] = v ? atomicAdd(&gcur[(size_t)i * M], v) : 0u;
+            s_cnt[i] = 0u;
+        }
+        __syncthreads();
     }
-    __syncthreads();
-    for (int i = threadIdx.x; i < nbins; i += kThreads) {
-        const uint32_t v = s_cnt[i];
-        s_base[i] = v ? atomicAdd(&gcur[(size_t)i * M], v) : 0u;
-        s_cnt[i] = 0u;
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < npts; idx += kThreads) {
-        const int i1 = idx / LK, j = idx - i1 * LK;
-        const size_t p = (row0 + (size_t)i1 * M) * LK + j;
-        const float2 uv = reinterpret_cast<const float2 *>(loc)[p];
-        const int l = j / K;
-        Neighbours n = neighbours(uv.x, uv.y, s_lv.lvl[l], 0u, 0u);
-        int bins[4];
-        const int nb = point_bins(n, s_lv.lvl[l], s_lv.tw[l], bins);
-        for (int k = 0; k < nb; ++k)
-            sorted[s_base[bins[k]] + atomicAdd(&s_cnt[bins[k]], 1u)] = (uint32_t)p;
+#pragma unroll
+    for (int r = 0; r < kBinPPT; ++r) {
+        uint32_t t[4];
+        const int nt = point_tiles(nb[r], t);
+        const int l = ll[r];
+        for (int k = 0; k < nt; ++k) {
+            const int tx = (int)(t[k] & 0xffffu), ty = (int)(t[k] >> 16);
+            const int bin = s_lv.lvl[l].w + ty * s_lv.tw[l] + tx;
+            const uint32_t slot = lds ? s_base[bin] + atomicAdd(&s_cnt[bin], 1u)
+                                      : atomicAdd(&gcur[(size_t)bin * M], 1u);
+            const int cell = (nb[r].xi - tx * kTile + 1) + kCellsW * (nb[r].yi - ty * kTile + 1);
+            recs[slot] = make_uint4(((uint32_t)qq[r] << kRecQueryShift) | (uint32_t)cell,
+                                    __float_as_uint(a0[r]), __float_as_uint(a1[r]),
+                                    __float_as_uint(nb[r].fy));
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
-// backward 4: grad_value, one 8x8 tile (and chunk of its points) per work item
+// backward: grad_value, one 8x8 tile (and chunk of its records) per work item
 //
-// The chunk is walked in sub-chunks of kSubRows(D) points.  For each, the
-// points' grad_out rows are staged in LDS (one read of each row), and the
-// points are counting-sorted in LDS by the cell of their top-left neighbour
-// (a 9x9 grid: the tile plus one column and row before it).  Pixel (x, y) of
-// the tile receives from the points of four cells, in four roles: top-left
-// from cell (x, y), top-right from (x-1, y), bottom-left from (x, y-1),
-// bottom-right from (x-1, y-1).  A lane owns (pixel, 4-channel quad) pairs
-// and sums A * w * grad_out over those lists in registers across all
-// sub-chunks, so no two lanes ever add into the same value and the loop
-// iterations are independent.  Each pixel is written once per work item.
+// A workgroup walks its work items in sub-chunks of kSub records as a
+// two-stage pipeline over two LDS buffers: while it sums sub-chunk k out of
+// one buffer, it counting-sorts sub-chunk k+1 by cell, loads that
+// sub-chunk's grad_out rows straight into the other buffer in sorted order
+// (global_load_lds, no registers held), and loads the records of sub-chunk
+// k+2 into registers.
+//
+// Pixel (x, y) of the tile receives from the points of four cells, in four
+// roles: top-right from cell (x, y+1), top-left from (x+1, y+1), bottom-right
+// from (x, y), bottom-left from (x+1, y).  After the sort, cells (x, y+1) and
+// (x+1, y+1) are one contiguous range of the buffer, and so are (x, y) and
+// (x+1, y).  A lane owns (pixel, 4-channel quad) pairs and sums
+// A * w * grad_out over those two ranges in registers across all sub-chunks
+// of the item, so no two lanes ever add into the same value.  Each pixel is
+// written once per work item.
 // ---------------------------------------------------------------------------
 constexpr int kTileThreads = 512;
-constexpr int kCellsW = kTile + 1;
-constexpr int kCells = kCellsW * kCellsW;
-constexpr int kStageBytes = 32 * 1024;  // grad_out rows staged per sub-chunk
+constexpr int kStageBytes = 16 * 1024;  // grad_out rows per LDS buffer
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void global_void_t;
+
+// A sub-chunk: records [it.y + off, it.y + off + kSub) of work item w.
+struct SubChunk {
+    uint32_t w, off;
+    uint4 it;  // the work item: (bin, first record, records, whole bin)
+    bool valid;
+};
+
+// acc += w[4e + role] * g[e * kQuads] over e in [e0, e2), role r0 below e1 and
+// r1 from e1 on; four entries per round, all eight LDS reads issued first.
+template <int kQuads>
+__device__ __forceinline__ void pull_range(float4 &acc, const float *__restrict__ w,
+                                           const float4 *__restrict__ g, int e0, int e1, int e2,
+                                           int r0, int r1) {
+    int e = e0;
+    for (; e + 4 <= e2; e += 4) {
+        const float w0 = w[4 * e + (e < e1 ? r0 : r1)];
+        const float w1 = w[4 * e + 4 + (e + 1 < e1 ? r0 : r1)];
+        const float w2 = w[4 * e + 8 + (e + 2 < e1 ? r0 : r1)];
+        const float w3 = w[4 * e + 12 + (e + 3 < e1 ? r0 : r1)];
+        const float4 g0 = g[e * kQuads];
+        const float4 g1 = g[(e + 1) * kQuads];
+        const float4 g2 = g[(e + 2) * kQuads];
+        const float4 g3 = g[(e + 3) * kQuads];
+        fma4(acc, w0, g0);
+        fma4(acc, w1, g1);
+        fma4(acc, w2, g2);
+        fma4(acc, w3, g3);
+    }
+    for (; e < e2; ++e) fma4(acc, w[4 * e + (e < e1 ? r0 : r1)], g[e * kQuads]);
+}
 
 template <int D>
 __global__ void __launch_bounds__(kTileThreads)
 grad_value_tile_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ starts,
-                       const float *__restrict__ loc, const float *__restrict__ attn,
-                       const float *__restrict__ grad_out, const uint32_t *__restrict__ counts,
-                       const uint32_t *__restrict__ start, const uint2 *__restrict__ items,
-                       const uint32_t *__restrict__ work_total,
-                       const uint32_t *__restrict__ sorted, float *__restrict__ grad_value,
-                       Dims dm) {
+                       const float *__restrict__ grad_out, const uint4 *__restrict__ items,
+                       const uint32_t *__restrict__ work_total, const uint4 *__restrict__ recs,
+                       float *__restrict__ grad_value, Dims dm) {
     constexpr int kQuads = D / 4;
-    constexpr int kSub = kStageBytes / (D * 4) < 512 ? kStageBytes / (D * 4) : 512;  // points per sub-chunk
+    constexpr int kSub = kStageBytes / (D * 4) < kTileThreads ? kStageBytes / (D * 4)
+                                                              : kTileThreads;
     constexpr int kOwn = (kTilePx * kQuads + kTileThreads - 1) / kTileThreads;  // pairs per lane
     __shared__ LevelLds s_lv;
-    __shared__ float4 s_g[kSub * kQuads];  // staged grad_out rows
-    __shared__ float4 s_w[kSub];           // A * bilinear weight of each neighbour
-    __shared__ uint32_t s_item[kSub];      // (b, q, m) row of the point
-    __shared__ uint16_t s_cell[kSub];      // cell of the point's top-left neighbour
-    __shared__ uint16_t s_ent[kSub];       // points ordered by cell
-    __shared__ uint32_t s_cnt[kCells + 1];
-    __shared__ uint32_t s_cur[kCells];
+    __shared__ float4 s_g0[kSub * kQuads];  // grad_out rows in sorted order, buffer 0
+    __shared__ float4 s_g1[kSub * kQuads];  // buffer 1
+    __shared__ float4 s_w0[kSub];           // A * bilinear weights (TL, TR, BL, BR), sorted
+    __shared__ float4 s_w1[kSub];
+    __shared__ uint32_t s_st0[kCells + 1];  // first sorted slot of each cell, and the total
+    __shared__ uint32_t s_st1[kCells + 1];
+    __shared__ uint32_t s_tmp[kCells];      // cell counts, then placement cursors
+    __shared__ uint32_t s_q[kSub];          // query of the record in each sorted slot
 
-    const int M = dm.M, LK = dm.L * dm.K;
-    stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
-    const uint32_t total = *work_total;
+    const int M = dm.M, Nq = dm.Nq;
     const int tid = threadIdx.x;
-    // The work list is in (batch, level, tile, head) order and workgroup k
-    // (dispatched to XCD k % 8) takes items k, k + grid, ...  With 8 heads the
-    // XCDs therefore split the work by head: every XCD gets the same mix of
-    // tiles, and the grad_out rows it gathers are those of one head.
-    for (uint32_t w = blockIdx.x; w < total; w += gridDim.x) {
-        const uint2 wk = items[w];
-        const uint32_t bin = wk.x;  // (b * nb_max + tile) * M + m
-        const int m = (int)(bin % (uint32_t)M);
-        const uint32_t bt = bin / (uint32_t)M;
-        const int b = (int)(bt / (uint32_t)dm.nb_max);
-        const int lb = (int)(bt - (uint32_t)b * dm.nb_max);
-        int l = 0;
-        while (l + 1 < dm.L && s_lv.lvl[l + 1].w <= lb) ++l;
-        const int4 lvl = s_lv.lvl[l];
-        const int tw = s_lv.tw[l];
-        const int ty = (lb - lvl.w) / tw, tx = (lb - lvl.w) - ty * tw;
-        const int x0t = tx * kTile, y0t = ty * kTile;
-        const uint32_t cnt = counts[bin];
-        const uint32_t s0 = start[bin] + wk.y * kChunk;
-        const int n = (int)min((uint32_t)kChunk, cnt - wk.y * kChunk);
-        const bool whole = cnt <= (uint32_t)kChunk;
+    stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
+    if (tid < kCells) s_tmp[tid] = 0u;
+    const uint32_t total = *work_total;
+    const uint32_t grid = gridDim.x;
 
-        float4 acc[kOwn];
-#pragma unroll
-        for (int o = 0; o < kOwn; ++o) acc[o] = make_float4(0.f, 0.f, 0.f, 0.f);
+    // Sub-chunk k (summed), k+1 (sorted, rows loading), k+2 (records loading),
+    // and the work item after the one of k+2.  The work list is in (batch,
+    // level, tile, head) order and workgroup g (dispatched to XCD g % 8) takes
+    // items g, g + grid, ...  With 8 heads the XCDs therefore split the work
+    // by head: every XCD gets the same mix of tiles, and the grad_out rows it
+    // gathers are those of one head.
+    SubChunk A{0, 0, make_uint4(0, 0, 0, 0), false};
+    SubChunk Bn{0, 0, make_uint4(0, 0, 0, 0), false};
+    SubChunk C{blockIdx.x, 0, make_uint4(0, 0, 0, 0), blockIdx.x < total};
+    uint4 next_item = make_uint4(0, 0, 0, 0);
+    if (C.valid) C.it = items[C.w];
+    if (C.w + grid < total) next_item = items[C.w + grid];
+    auto advance = [&](SubChunk &c) {
+        if (!c.valid) return;
+        if (c.off + kSub < c.it.z) {
+            c.off += kSub;
+            return;
+        }
+        c.w += grid;
+        c.off = 0;
+        c.valid = c.w < total;
+        c.it = next_item;
+        if (c.valid && c.w + grid < total) next_item = items[c.w + grid];
+    };
+    auto count_of = [&](const SubChunk &c) {
+        return c.valid ? (int)min((uint32_t)kSub, c.it.z - c.off) : 0;
+    };
 
-        for (int sub = 0; sub < n; sub += kSub) {
-            const int ns = min(kSub, n - sub);
-            for (int i = tid; i < kCells; i += kTileThreads) s_cnt[i] = 0u;
-            __syncthreads();
-            for (int i = tid; i < ns; i += kTileThreads) {
-                const uint32_t p = sorted[s0 + sub + i];
-                const float2 uv = reinterpret_cast<const float2 *>(loc)[p];
-                const float A = attn[p];
-                const Neighbours nb = neighbours(uv.x, uv.y, lvl, 0u, 0u);
-                // a point of this bin has a neighbour inside the tile, so its
-                // top-left neighbour lies in the 9x9 cell grid
-                const int cx = nb.xi - x0t + 1, cy = nb.yi - y0t + 1;
-                const bool inside = cx >= 0 && cx < kCellsW && cy >= 0 && cy < kCellsW;
-                const int cell = inside ? cx + cy * kCellsW : 0;
-                s_cell[i] = (uint16_t)cell;
-                s_w[i] = inside ? make_float4(A * nb.w.x, A * nb.w.y, A * nb.w.z, A * nb.w.w)
-                                : make_float4(0.f, 0.f, 0.f, 0.f);
-                s_item[i] = p / (uint32_t)LK;
-                atomicAdd(&s_cnt[cell], 1u);
-            }
-            __syncthreads();
-            for (int i = tid; i < ns * kQuads; i += kTileThreads) {
-                const int pt = i / kQuads, q = i - pt * kQuads;
-                s_g[i] = reinterpret_cast<const float4 *>(grad_out + (size_t)s_item[pt] * D)[q];
-            }
-            if (tid < 64) {  // exclusive scan of the 81 cell counts by one wave, 2 cells a lane
-                const int c0 = 2 * tid, c1 = 2 * tid + 1;
-                const uint32_t v0 = c0 < kCells ? s_cnt[c0] : 0u;
-                const uint32_t v1 = c1 < kCells ? s_cnt[c1] : 0u;
-                uint32_t incl = v0 + v1;
+    uint4 rec = make_uint4(0, 0, 0, 0);  // record `tid` of sub-chunk k+1
+    float4 acc[kOwn];
 #pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const uint32_t t = __shfl_up(incl, off, 64);
-                    if (tid >= off) incl += t;
-                }
-                const uint32_t ex = incl - v0 - v1;
-                if (c0 < kCells) {
-                    s_cnt[c0] = ex;
-                    s_cur[c0] = ex;
-                }
-                if (c1 < kCells) {
-                    s_cnt[c1] = ex + v0;
-                    s_cur[c1] = ex + v0;
-                }
-                if (tid == 63) s_cnt[kCells] = incl;
+    for (int o = 0; o < kOwn; ++o) acc[o] = make_float4(0.f, 0.f, 0.f, 0.f);
+
+    // sum sub-chunk A out of buffer P while preparing Bn in buffer P ^ 1
+    auto step = [&](auto pc) {
+        constexpr int P = decltype(pc)::value;
+        float4 *gP = P ? s_g1 : s_g0;
+        float4 *gF = P ? s_g0 : s_g1;
+        const float *wP = reinterpret_cast<const float *>(P ? s_w1 : s_w0);
+        float4 *wF = P ? s_w0 : s_w1;
+        const uint32_t *stP = P ? s_st1 : s_st0;
+        uint32_t *stF = P ? s_st0 : s_st1;
+
+        // 1. count the cells of Bn
+        const int nb = count_of(Bn);
+        const int cell = (int)(rec.x & ((1u << kRecQueryShift) - 1u));
+        if (tid < nb) atomicAdd(&s_tmp[cell], 1u);
+        __syncthreads();
+        // 2. exclusive scan of the 81 counts by one wave, 2 cells a lane
+        if (tid < 64) {
+            const int c0 = 2 * tid, c1 = 2 * tid + 1;
+            const uint32_t v0 = c0 < kCells ? s_tmp[c0] : 0u;
+            const uint32_t v1 = c1 < kCells ? s_tmp[c1] : 0u;
+            uint32_t incl = v0 + v1;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const uint32_t t = __shfl_up(incl, off, 64);
+                if (tid >= off) incl += t;
             }
-            __syncthreads();
-            for (int i = tid; i < ns; i += kTileThreads)
-                s_ent[atomicAdd(&s_cur[s_cell[i]], 1u)] = (uint16_t)i;
-            __syncthreads();
+            const uint32_t ex = incl - v0 - v1;
+            if (c0 < kCells) {
+                stF[c0] = ex;
+                s_tmp[c0] = ex;
+            }
+            if (c1 < kCells) {
+                stF[c1] = ex + v0;
+                s_tmp[c1] = ex + v0;
+            }
+            if (tid == 63) stF[kCells] = incl;
+        }
+        __syncthreads();
+        // 3. place the records of Bn in cell order
+        if (tid < nb) {
+            const uint32_t slot = atomicAdd(&s_tmp[cell], 1u);
+            const float a0 = __uint_as_float(rec.y), a1 = __uint_as_float(rec.z);
+            const float fy = __uint_as_float(rec.w), gy = 1.f - fy;
+            wF[slot] = make_float4(a0 * gy, a1 * gy, a0 * fy, a1 * fy);
+            s_q[slot] = rec.x >> kRecQueryShift;
+        }
+        __syncthreads();
+        // 4. start the loads of Bn's rows (into gF) and of C's records
+        if (tid < kCells) s_tmp[tid] = 0u;
+        if (nb) {
+            const uint32_t bm = Bn.it.x;  // (b * nb_max + tile) * M + m
+            const int m = (int)(bm % (uint32_t)M);
+            const int b = (int)(bm / (uint32_t)M / (uint32_t)dm.nb_max);
+            const float *gob = grad_out + ((size_t)b * Nq * M + m) * D;
+            for (int i = tid; i < nb * kQuads; i += kTileThreads) {
+                const int slot = i / kQuads, qd = i - slot * kQuads;
+                const float *src = gob + (size_t)s_q[slot] * M * D + 4 * qd;
+                // each wave fills 64 consecutive float4 slots: lane l writes slot base + l
+                __builtin_amdgcn_global_load_lds((global_void_t *)src,
+                                                 (lds_void_t *)(gF + (i & ~63)), 16, 0, 0);
+            }
+        }
+        const int ncn = count_of(C);
+        if (tid < ncn) rec = recs[C.it.y + C.off + tid];
+        // 5. sum A out of buffer P
+        if (A.valid) {
 #pragma unroll
             for (int o = 0; o < kOwn; ++o) {
                 const int pair = tid + o * kTileThreads;
                 if (pair >= kTilePx * kQuads) break;
                 const int px = pair / kQuads, q = pair - px * kQuads;
                 const int x = px & (kTile - 1), y = px >> kTileShift;
+                const int cT = (y + 1) * kCellsW + x, cB = y * kCellsW + x;
+                // cells (x, y+1) then (x+1, y+1): top-right, then top-left roles;
+                // cells (x, y) then (x+1, y): bottom-right, then bottom-left roles
+                pull_range<kQuads>(acc[o], wP, gP + q, (int)stP[cT], (int)stP[cT + 1], (int)stP[cT + 2],
+                           1, 0);
+                pull_range<kQuads>(acc[o], wP, gP + q, (int)stP[cB], (int)stP[cB + 1], (int)stP[cB + 2],
+                           3, 2);
+            }
+            // 6. the item ends with A: write its tile
+            if (A.off + kSub >= A.it.z) {
+                const uint32_t bin = A.it.x;
+                const int m = (int)(bin % (uint32_t)M);
+                const uint32_t bt = bin / (uint32_t)M;
+                const int b = (int)(bt / (uint32_t)dm.nb_max);
+                const int lb = (int)(bt - (uint32_t)b * dm.nb_max);
+                int l = 0;
+                while (l + 1 < dm.L && s_lv.lvl[l + 1].w <= lb) ++l;
+                const int4 lvl = s_lv.lvl[l];
+                const int tw = s_lv.tw[l];
+                const int ty = (lb - lvl.w) / tw, tx = (lb - lvl.w) - ty * tw;
+                const size_t slice = (size_t)dm.Nv * M * D;
+                float *gv = grad_value + (size_t)b * slice + (size_t)m * D;
 #pragma unroll
-                for (int role = 0; role < 4; ++role) {
-                    const int cell = (x - (role & 1) + 1) + (y - (role >> 1) + 1) * kCellsW;
-                    const int e0 = (int)s_cnt[cell], e1 = (int)s_cnt[cell + 1];
-#pragma unroll 4
-                    for (int e = e0; e < e1; ++e) {
-                        const int pt = s_ent[e];
-                        fma4(acc[o], pick(s_w[pt], role), s_g[pt * kQuads + q]);
+                for (int o = 0; o < kOwn; ++o) {
+                    const int pair = tid + o * kTileThreads;
+                    if (pair >= kTilePx * kQuads) break;
+                    const int px = pair / kQuads, q = pair - px * kQuads;
+                    const int gx = tx * kTile + (px & (kTile - 1));
+                    const int gy = ty * kTile + (px >> kTileShift);
+                    float4 a = acc[o];
+                    acc[o] = make_float4(0.f, 0.f, 0.f, 0.f);
+                    if (gy >= lvl.x || gx >= lvl.y) continue;
+                    float *dst = gv + (size_t)(lvl.z + gy * lvl.y + gx) * M * D + 4 * q;
+                    if (A.it.w) {
+                        // this work item alone owns the pixel: plain read-add-write
+                        float4 *d4 = reinterpret_cast<float4 *>(dst);
+                        if (dm.accumulate) {
+                            const float4 v = *d4;
+                            a.x += v.x;
+                            a.y += v.y;
+                            a.z += v.z;
+                            a.w += v.w;
+                        }
+                        *d4 = a;
+                    } else {
+                        atomicAdd(dst + 0, a.x);
+                        atomicAdd(dst + 1, a.y);
+                        atomicAdd(dst + 2, a.z);
+                        atomicAdd(dst + 3, a.w);
                     }
                 }
             }
-            __syncthreads();  // the tables are rebuilt for the next sub-chunk
         }
+        // 7. rows of Bn and records of C have landed; buffer P is free
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __syncthreads();
+        A = Bn;
+        Bn = C;
+        advance(C);
+    };
 
-        const size_t slice = (size_t)dm.Nv * M * D;
-        float *gv = grad_value + (size_t)b * slice + (size_t)m * D;
-#pragma unroll
-        for (int o = 0; o < kOwn; ++o) {
-            const int pair = tid + o * kTileThreads;
-            if (pair >= kTilePx * kQuads) break;
-            const int px = pair / kQuads, q = pair - px * kQuads;
-            const int gx = x0t + (px & (kTile - 1)), gy = y0t + (px >> kTileShift);
-            if (gy >= lvl.x || gx >= lvl.y) continue;
-            float *dst = gv + (size_t)(lvl.z + gy * lvl.y + gx) * M * D + 4 * q;
-            float4 a = acc[o];
-            if (whole) {
-                // this work item alone owns the pixel: plain read-add-write
-                float4 *d4 = reinterpret_cast<float4 *>(dst);
-                if (dm.accumulate) {
-                    const float4 v = *d4;
-                    a.x += v.x;
-                    a.y += v.y;
-                    a.z += v.z;
-                    a.w += v.w;
-                }
-                *d4 = a;
-            } else {
-                atomicAdd(dst + 0, a.x);
-                atomicAdd(dst + 1, a.y);
-                atomicAdd(dst + 2, a.z);
-                atomicAdd(dst + 3, a.w);
-            }
-        }
+    // prologue: records of the first sub-chunk
+    {
+        const int n0 = count_of(C);
+        if (tid < n0) rec = recs[C.it.y + C.off + tid];
+        Bn = C;
+        advance(C);
+        __syncthreads();  // s_tmp cleared
+    }
+    while (A.valid || Bn.valid) {
+        step(std::integral_constant<int, 0>());
+        if (!(A.valid || Bn.valid)) break;
+        step(std::integral_constant<int, 1>());
     }
 }
 
@@ -830,11 +1006,11 @@ WorkLayout work_layout(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t L, 
     w.off_cursor = o;
     o = align(o + 4 * (size_t)w.bm_bins);
     w.off_items = o;
-    o = align(o + 8 * (size_t)w.work_max);
+    o = align(o + 16 * (size_t)w.work_max);
     w.off_total = o;
     o = align(o + 4);
     w.off_sorted = o;
-    o = align(o + 4 * (size_t)w.sorted_max);
+    o = align(o + 16 * (size_t)w.sorted_max);
     w.bytes = o;
     return w;
 }
@@ -914,58 +1090,69 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
     w.counts = reinterpret_cast<uint32_t *>(ws + wl.off_counts);
     w.start = reinterpret_cast<uint32_t *>(ws + wl.off_start);
     w.cursor = reinterpret_cast<uint32_t *>(ws + wl.off_cursor);
-    w.items = reinterpret_cast<uint2 *>(ws + wl.off_items);
+    w.items = reinterpret_cast<uint4 *>(ws + wl.off_items);
     w.work_total = reinterpret_cast<uint32_t *>(ws + wl.off_total);
-    w.sorted = reinterpret_cast<uint32_t *>(ws + wl.off_sorted);
+    w.recs = reinterpret_cast<uint4 *>(ws + wl.off_sorted);
     // the counts region is padded to 256 bytes, so whole float4s can be cleared
     mark(1);
     msda_status st = fill_zero(w.counts, (wl.off_start - wl.off_counts) / 16, s);
     if (st != MSDA_OK) return st;
 
     const int hist_cap = (int)(wl.nb_max < kHistLds ? wl.nb_max : kHistLds);
-    const Launch p = plan(D, L, K, 64);
-    const int64_t gq = (Nq + p.ipb - 1) / p.ipb;
-    const int64_t gs = (Nq + kScatterQueries - 1) / kScatterQueries;
-    int64_t bchunk = batch_chunk(gq * M, B);
-    mark(2);
-    for (int64_t b0 = 0; b0 < B; b0 += bchunk) {
-        const int64_t nb = (B - b0) < bchunk ? (B - b0) : bchunk;
-        Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, p.pc, p.ps, (int)b0, (int)gq,
-                (int)wl.nb_max, 0};
-        hipLaunchKernelGGL((bwd_dots_kernel<D, VT>), dim3((unsigned)(gq * M * nb)),
-                           dim3(kThreads), p.lds + 4 * (size_t)hist_cap, s,
-                           static_cast<const VT *>(value), shapes, starts, loc, attn, gout, gloc,
-                           gattn, w.counts, hist_cap, dm);
-        st = hip_status(hipGetLastError());
-        if (st != MSDA_OK) return st;
-    }
-    Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, 0, 0, 0, 0, (int)wl.nb_max,
+    const int64_t gb = (Nq * L * K + kBinPoints - 1) / kBinPoints;  // per (batch, head)
+    Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, 0, 0, 0, (int)gb, (int)wl.nb_max,
             accumulate ? 1 : 0};
+    auto per_batch = [&](int64_t per_b, auto &&launch) -> msda_status {
+        const int64_t bchunk = batch_chunk(per_b, B);
+        for (int64_t b0 = 0; b0 < B; b0 += bchunk) {
+            const int64_t nb = (B - b0) < bchunk ? (B - b0) : bchunk;
+            launch(b0, (unsigned)(per_b * nb));
+            const msda_status e = hip_status(hipGetLastError());
+            if (e != MSDA_OK) return e;
+        }
+        return MSDA_OK;
+    };
+    mark(2);
+    st = per_batch(gb * M, [&](int64_t b0, unsigned grid) {
+        Dims d2 = dm;
+        d2.b0 = (int)b0;
+        hipLaunchKernelGGL(bin_count_kernel, dim3(grid), dim3(kThreads), 4 * (size_t)hist_cap, s,
+                           shapes, starts, loc, w.counts, hist_cap, d2);
+    });
+    if (st != MSDA_OK) return st;
+
+    const Launch p = plan(D, L, K, 32);
+    const int64_t gq = (Nq + p.ipb - 1) / p.ipb;
     mark(3);
+    st = per_batch(gq * M, [&](int64_t b0, unsigned grid) {
+        Dims d2{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, p.pc, p.ps, (int)b0, (int)gq, 0, 0};
+        hipLaunchKernelGGL((bwd_dots_kernel<D, VT>), dim3(grid), dim3(kThreads), p.lds, s,
+                           static_cast<const VT *>(value), shapes, starts, loc, attn, gout, gloc,
+                           gattn, d2);
+    });
+    if (st != MSDA_OK) return st;
+
+    mark(4);
     hipLaunchKernelGGL(bin_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, shapes, starts,
                        w.counts, w.start, w.cursor, w.items, w.work_total, (int)B, dm);
     st = hip_status(hipGetLastError());
     if (st != MSDA_OK) return st;
-    bchunk = batch_chunk(gs * M, B);
-    mark(4);
-    for (int64_t b0 = 0; b0 < B; b0 += bchunk) {
-        const int64_t nb = (B - b0) < bchunk ? (B - b0) : bchunk;
+
+    mark(5);
+    st = per_batch(gb * M, [&](int64_t b0, unsigned grid) {
         Dims d2 = dm;
         d2.b0 = (int)b0;
-        d2.nblk = (int)gs;
-        hipLaunchKernelGGL(bin_scatter_kernel, dim3((unsigned)(gs * M * nb)), dim3(kThreads),
-                           8 * (size_t)hist_cap, s, shapes, starts, loc, w.cursor, w.sorted,
-                           hist_cap, d2);
-        st = hip_status(hipGetLastError());
-        if (st != MSDA_OK) return st;
-    }
+        hipLaunchKernelGGL(bin_scatter_kernel, dim3(grid), dim3(kThreads), 8 * (size_t)hist_cap,
+                           s, shapes, starts, loc, attn, w.cursor, w.recs, hist_cap, d2);
+    });
+    if (st != MSDA_OK) return st;
+
     const int64_t grid = wl.work_max < kTileGrid ? wl.work_max : kTileGrid;
-    mark(5);
-    hipLaunchKernelGGL((grad_value_tile_kernel<D>), dim3((unsigned)grid), dim3(kTileThreads), 0, s,
-                       shapes, starts, loc, attn, gout, w.counts, w.start, w.items,
-                       w.work_total, w.sorted, gval, dm);
-    st = hip_status(hipGetLastError());
     mark(6);
+    hipLaunchKernelGGL((grad_value_tile_kernel<D>), dim3((unsigned)grid), dim3(kTileThreads), 0, s,
+                       shapes, starts, gout, w.items, w.work_total, w.recs, gval, dm);
+    st = hip_status(hipGetLastError());
+    mark(7);
     return st;
 }
 
@@ -1057,6 +1244,8 @@ msda_status backward_impl(const void *value, int value_dtype, const int64_t *spa
     msda_status st = check_sizes(value_dtype, B, Nv, Nq, M, D, L, K);
     if (st != MSDA_OK) return st;
     if (flags & ~MSDA_BWD_ACCUMULATE) return MSDA_ERR_UNSUPPORTED;
+    // a grad_value record stores the query index in 25 bits
+    if (Nq > ((int64_t)1 << (32 - kRecQueryShift))) return MSDA_ERR_UNSUPPORTED;
     const int64_t nval = B * Nv * M * D;
     if (nval > 0 && !grad_value) return MSDA_ERR_NULL;
     const bool work = B > 0 && Nq > 0;
@@ -1078,7 +1267,7 @@ msda_status backward_impl(const void *value, int value_dtype, const int64_t *spa
     }
     if (!work) {
         if (ev)
-            for (int i = 1; i < 7; ++i) (void)hipEventRecord(ev[i], s);
+            for (int i = 1; i <= MSDA_BWD_STAGES; ++i) (void)hipEventRecord(ev[i], s);
         return MSDA_OK;
     }
     unsigned char *ws = static_cast<unsigned char *>(workspace);
@@ -1119,10 +1308,10 @@ msda_status msda_backward_timed(const void *value, int value_dtype,
                                 uint32_t flags, void *stream, float *stage_us) {
     if (!stage_us) return MSDA_ERR_NULL;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipEvent_t ev[7];
+    hipEvent_t ev[MSDA_BWD_STAGES + 1];
     int made = 0;
     msda_status st = MSDA_OK;
-    for (; made < 7; ++made) {
+    for (; made < MSDA_BWD_STAGES + 1; ++made) {
         st = hip_status(hipEventCreate(&ev[made]));
         if (st != MSDA_OK) break;
     }
@@ -1131,7 +1320,7 @@ msda_status msda_backward_timed(const void *value, int value_dtype,
                            attn_weight, grad_out, grad_value, grad_sampling_loc,
                            grad_attn_weight, B, Nv, Nq, M, D, L, K, workspace, workspace_bytes,
                            flags, s, ev);
-        if (st == MSDA_OK) st = hip_status(hipEventSynchronize(ev[6]));
+        if (st == MSDA_OK) st = hip_status(hipEventSynchronize(ev[MSDA_BWD_STAGES]));
         for (int i = 0; i < MSDA_BWD_STAGES && st == MSDA_OK; ++i) {
             float ms = 0.f;
             st = hip_status(hipEventElapsedTime(&ms, ev[i], ev[i + 1]));

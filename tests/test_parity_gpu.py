@@ -167,6 +167,15 @@ def test_sixteen_levels_and_thin_maps(msda):
     check_bwd(msda, w)
 
 
+def test_many_tiles_use_global_bin_counters(msda):
+    """A 520x520 level has 65*65 = 4225 tiles of 8x8, more than the LDS bin
+    histograms hold: counts and record slots then go through global atomics."""
+    w = workloads.random_case(350, 1, ((520, 520), (3, 3)), 64, 2, 8, 3)
+    _say("4225 tiles")
+    check_fwd(msda, w)
+    check_bwd(msda, w)
+
+
 def test_pixel_centres_are_exact(msda):
     """A point at a pixel centre with weight 1 returns the stored row exactly."""
     shapes = ((8, 16), (4, 8))
