@@ -41,6 +41,11 @@
  * Streams and errors.  `stream` is a hipStream_t (NULL = the null stream).
  * Work is enqueued on it and the call returns without synchronizing; a
  * kernel fault therefore surfaces at the caller's next synchronization.
+ * msda_backward also uses one side stream per device, created on its first
+ * call on that device and kept until the process ends: it is forked from
+ * `stream` and joined back into it with events inside the call, so work
+ * enqueued on `stream` afterwards sees every output complete (this also
+ * holds under stream capture).
  * Every function returns an msda_status; nothing is thrown across the ABI.
  * The launch-time checks cover null pointers, negative sizes, 1 <= L <= 16,
  * the supported head widths and dtypes, and the 32-bit addressing limit.
@@ -141,10 +146,13 @@ msda_status msda_backward(const void *value, int value_dtype,
  * a synchronization of `stream`; stage_us[0..MSDA_BWD_STAGES) receives the
  * duration in microseconds of each stage, timed with HIP events recorded on
  * `stream` between the launches:
- *   0 grad_value zero-fill (0 with MSDA_BWD_ACCUMULATE)   1 workspace clear
- *   2 points per value tile   3 grad_attn_weight / grad_sampling_loc
- *   4 count scan   5 record scatter into tiles   6 grad_value tiles
- * Not for production loops: it blocks the calling thread.
+ *   0 grad_value zero-fill (0 with MSDA_BWD_ACCUMULATE)
+ *   1 grad_attn_weight / grad_sampling_loc   2 workspace clear
+ *   3 points per value tile   4 count scan   5 record scatter into tiles
+ *   6 grad_value tiles
+ * Unlike msda_backward, which computes stage 1 on a side stream of its own
+ * concurrently with stages 2-6, every stage here runs on `stream`, one after
+ * the other.  Not for production loops: it blocks the calling thread.
  */
 #define MSDA_BWD_STAGES 7
 msda_status msda_backward_timed(const void *value, int value_dtype,

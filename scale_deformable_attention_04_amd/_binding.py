@@ -30,7 +30,7 @@ MSDA_BWD_ACCUMULATE = 1
 EXPORTED = ("msda_forward", "msda_backward_workspace_size", "msda_backward",
             "msda_backward_timed", "msda_validate_host", "msda_status_string",
             "msda_last_hip_error")
-BWD_STAGES = ("fill_grad_value", "clear_bins", "count", "dots", "scan", "scatter", "tiles")
+BWD_STAGES = ("fill_grad_value", "dots", "clear_bins", "count", "scan", "scatter", "tiles")
 
 _lib = None
 

@@ -40,6 +40,7 @@
 // memory.
 
 #include <hip/hip_runtime.h>
+#include <mutex>
 #include <type_traits>
 #include <stdint.h>
 
@@ -1076,12 +1077,58 @@ msda_status fill_zero(void *p, size_t n4, hipStream_t s) {
     return hip_status(hipGetLastError());
 }
 
+// Where the backward enqueues: the caller's stream, an optional side stream
+// (with its fork / join events) and optional per-stage timing events.
+struct Exec {
+    hipStream_t s;
+    hipStream_t side;
+    hipEvent_t fork, join;
+    hipEvent_t *ev;
+};
+
+// One side stream per device, created on first use (default priority,
+// non-blocking with respect to the null stream).  The mutex is held while a
+// backward enqueues, so the fork / join events are never shared between two
+// calls in flight on the host.
+constexpr int kMaxDevices = 64;
+struct SideStream {
+    bool tried = false;
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+
+// Call with g_side_mu held.  nullptr when no side stream can be had.
+SideStream *side_stream() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    SideStream &ss = g_side[dev];
+    if (!ss.tried) {
+        ss.tried = true;
+        bool ok = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) == hipSuccess;
+        ok = ok && hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess;
+        ok = ok && hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) == hipSuccess;
+        if (!ok) {
+            if (ss.join) (void)hipEventDestroy(ss.join);
+            if (ss.fork) (void)hipEventDestroy(ss.fork);
+            if (ss.s) (void)hipStreamDestroy(ss.s);
+            ss.s = nullptr;
+            ss.fork = ss.join = nullptr;
+            (void)hipGetLastError();
+        }
+    }
+    return ss.s ? &ss : nullptr;
+}
+
 template <int D, typename VT>
 msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *starts,
                        const float *loc, const float *attn, const float *gout, float *gval,
                        float *gloc, float *gattn, int64_t B, int64_t Nv, int64_t Nq, int64_t M,
                        int64_t L, int64_t K, const WorkLayout &wl, unsigned char *ws,
-                       bool accumulate, hipStream_t s, hipEvent_t *ev) {
+                       bool accumulate, const Exec &ex) {
+    const hipStream_t s = ex.s;
+    hipEvent_t *ev = ex.ev;
     // ev (optional): events recorded before each stage, for msda_backward_timed
     auto mark = [&](int i) {
         if (ev) (void)hipEventRecord(ev[i], s);
@@ -1093,15 +1140,13 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
     w.items = reinterpret_cast<uint4 *>(ws + wl.off_items);
     w.work_total = reinterpret_cast<uint32_t *>(ws + wl.off_total);
     w.recs = reinterpret_cast<uint4 *>(ws + wl.off_sorted);
-    // the counts region is padded to 256 bytes, so whole float4s can be cleared
-    mark(1);
-    msda_status st = fill_zero(w.counts, (wl.off_start - wl.off_counts) / 16, s);
-    if (st != MSDA_OK) return st;
-
-    const int hist_cap = (int)(wl.nb_max < kHistLds ? wl.nb_max : kHistLds);
-    const int64_t gb = (Nq * L * K + kBinPoints - 1) / kBinPoints;  // per (batch, head)
-    Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, 0, 0, 0, (int)gb, (int)wl.nb_max,
-            accumulate ? 1 : 0};
+    // grad_attn_weight and grad_sampling_loc do not depend on the bin
+    // pipeline: with a side stream (forked from the caller's stream before
+    // anything else) they are computed there, concurrently, and the caller's
+    // stream waits for them at the end
+    const hipStream_t ds = ex.side ? ex.side : s;
+    const Launch p = plan(D, L, K, 32);
+    const int64_t gq = (Nq + p.ipb - 1) / p.ipb;
     auto per_batch = [&](int64_t per_b, auto &&launch) -> msda_status {
         const int64_t bchunk = batch_chunk(per_b, B);
         for (int64_t b0 = 0; b0 < B; b0 += bchunk) {
@@ -1112,23 +1157,34 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
         }
         return MSDA_OK;
     };
+    mark(1);
+    msda_status st = per_batch(gq * M, [&](int64_t b0, unsigned grid) {
+        Dims d2{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, p.pc, p.ps, (int)b0, (int)gq, 0, 0};
+        hipLaunchKernelGGL((bwd_dots_kernel<D, VT>), dim3(grid), dim3(kThreads), p.lds, ds,
+                           static_cast<const VT *>(value), shapes, starts, loc, attn, gout, gloc,
+                           gattn, d2);
+    });
+    if (st != MSDA_OK) return st;
+    if (ex.side) {
+        st = hip_status(hipEventRecord(ex.join, ex.side));
+        if (st != MSDA_OK) return st;
+    }
+
+    // the counts region is padded to 256 bytes, so whole float4s can be cleared
     mark(2);
+    st = fill_zero(w.counts, (wl.off_start - wl.off_counts) / 16, s);
+    if (st != MSDA_OK) return st;
+
+    const int hist_cap = (int)(wl.nb_max < kHistLds ? wl.nb_max : kHistLds);
+    const int64_t gb = (Nq * L * K + kBinPoints - 1) / kBinPoints;  // per (batch, head)
+    Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, 0, 0, 0, (int)gb, (int)wl.nb_max,
+            accumulate ? 1 : 0};
+    mark(3);
     st = per_batch(gb * M, [&](int64_t b0, unsigned grid) {
         Dims d2 = dm;
         d2.b0 = (int)b0;
         hipLaunchKernelGGL(bin_count_kernel, dim3(grid), dim3(kThreads), 4 * (size_t)hist_cap, s,
                            shapes, starts, loc, w.counts, hist_cap, d2);
-    });
-    if (st != MSDA_OK) return st;
-
-    const Launch p = plan(D, L, K, 32);
-    const int64_t gq = (Nq + p.ipb - 1) / p.ipb;
-    mark(3);
-    st = per_batch(gq * M, [&](int64_t b0, unsigned grid) {
-        Dims d2{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, p.pc, p.ps, (int)b0, (int)gq, 0, 0};
-        hipLaunchKernelGGL((bwd_dots_kernel<D, VT>), dim3(grid), dim3(kThreads), p.lds, s,
-                           static_cast<const VT *>(value), shapes, starts, loc, attn, gout, gloc,
-                           gattn, d2);
     });
     if (st != MSDA_OK) return st;
 
@@ -1152,6 +1208,7 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
     hipLaunchKernelGGL((grad_value_tile_kernel<D>), dim3((unsigned)grid), dim3(kTileThreads), 0, s,
                        shapes, starts, gout, w.items, w.work_total, w.recs, gval, dm);
     st = hip_status(hipGetLastError());
+    if (st == MSDA_OK && ex.side) st = hip_status(hipStreamWaitEvent(s, ex.join, 0));
     mark(7);
     return st;
 }
@@ -1182,12 +1239,11 @@ msda_status dispatch_bwd(int64_t D, const void *value, const int64_t *shapes,
                          const int64_t *starts, const float *loc, const float *attn,
                          const float *gout, float *gval, float *gloc, float *gattn, int64_t B,
                          int64_t Nv, int64_t Nq, int64_t M, int64_t L, int64_t K,
-                         const WorkLayout &wl, unsigned char *ws, bool acc, hipStream_t s,
-                         hipEvent_t *ev) {
+                         const WorkLayout &wl, unsigned char *ws, bool acc, const Exec &ex) {
 #define MSDA_BWD_CASE(DD)                                                                      \
     case DD:                                                                                   \
         return launch_bwd<DD, VT>(value, shapes, starts, loc, attn, gout, gval, gloc, gattn, B, \
-                                  Nv, Nq, M, L, K, wl, ws, acc, s, ev);
+                                  Nv, Nq, M, L, K, wl, ws, acc, ex);
     switch (D) {
         MSDA_BWD_CASE(4)
         MSDA_BWD_CASE(8)
@@ -1260,7 +1316,24 @@ msda_status backward_impl(const void *value, int value_dtype, const int64_t *spa
         if (workspace_bytes < wl.bytes) return MSDA_ERR_WORKSPACE;
         if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return MSDA_ERR_WORKSPACE;
     }
+    // The timed variant stays on the caller's stream, so that its stage
+    // times are those of one kernel each.
+    Exec ex{s, nullptr, nullptr, nullptr, ev};
+    std::unique_lock<std::mutex> lock(g_side_mu, std::defer_lock);
+    if (work && !ev) {
+        lock.lock();
+        if (SideStream *ss = side_stream()) {
+            ex.side = ss->s;
+            ex.fork = ss->fork;
+            ex.join = ss->join;
+        }
+    }
     if (ev) (void)hipEventRecord(ev[0], s);
+    if (ex.side) {
+        st = hip_status(hipEventRecord(ex.fork, s));
+        if (st == MSDA_OK) st = hip_status(hipStreamWaitEvent(ex.side, ex.fork, 0));
+        if (st != MSDA_OK) return st;
+    }
     if (!(flags & MSDA_BWD_ACCUMULATE)) {
         st = fill_zero(grad_value, (size_t)nval / 4, s);  // D is a multiple of 4
         if (st != MSDA_OK) return st;
@@ -1275,10 +1348,10 @@ msda_status backward_impl(const void *value, int value_dtype, const int64_t *spa
     if (value_dtype == MSDA_F32)
         return dispatch_bwd<float>(D, value, spatial_shapes, level_start_index, sampling_loc,
                                    attn_weight, grad_out, grad_value, grad_sampling_loc,
-                                   grad_attn_weight, B, Nv, Nq, M, L, K, wl, ws, acc, s, ev);
+                                   grad_attn_weight, B, Nv, Nq, M, L, K, wl, ws, acc, ex);
     return dispatch_bwd<uint16_t>(D, value, spatial_shapes, level_start_index, sampling_loc,
                                   attn_weight, grad_out, grad_value, grad_sampling_loc,
-                                  grad_attn_weight, B, Nv, Nq, M, L, K, wl, ws, acc, s, ev);
+                                  grad_attn_weight, B, Nv, Nq, M, L, K, wl, ws, acc, ex);
 }
 
 }  // namespace

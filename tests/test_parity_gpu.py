@@ -264,10 +264,16 @@ def test_runs_on_the_callers_stream(msda):
         out = msda.forward(**x, validate=False)
         gv, gl, ga = msda.backward(**x, grad_out=torch.from_numpy(w.grad_out).cuda(),
                                    validate=False)
+        # consumers enqueued on the same stream, with no host synchronization:
+        # they must see every output complete (the backward joins its side
+        # stream back into the caller's stream)
+        gv2, gl2, ga2 = gv.clone(), gl.clone(), ga.clone()
     s.synchronize()
     close(out.cpu().numpy(), oracle_fwd(w), FWD_TOL)
     rv, rl, ra = oracle_bwd(w)
-    close(gl.cpu().numpy(), rl, BWD_TOL)
+    close(gv2.cpu().numpy(), rv, BWD_TOL, "grad_value")
+    close(gl2.cpu().numpy(), rl, BWD_TOL, "grad_sampling_loc")
+    close(ga2.cpu().numpy(), ra, BWD_TOL, "grad_attn_weight")
 
 
 def test_autograd_function(msda):
