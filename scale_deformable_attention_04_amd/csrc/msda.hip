@@ -13,25 +13,27 @@
 // Forward (msda_fwd_kernel): per item, sum over its points of A * bilinear
 // sample, accumulated in registers, one store per item.
 //
-// Backward (msda_backward) runs as a pipeline on the caller's stream:
-//   1. bwd_dots_kernel: per point the four <grad_out, neighbour row> dot
-//      products, reduced across the lane group with DPP, give
-//      grad_attn_weight and grad_sampling_loc.  The same pass counts, per
-//      8x8-pixel tile of grad_value ("bin"), how many points have a
-//      neighbour in it (LDS histogram, one global add per bin per workgroup).
-//   2. bin_scan_kernel: exclusive scan of the counts -> bin offsets, and a
-//      work list of (bin, chunk of at most kChunk points).
-//   3. bin_scatter_kernel: every point's index is written into each bin it
-//      touches (LDS ranks, one global reservation per bin per workgroup).
-//   4. grad_value_tile_kernel: per work item, the points of the chunk push
-//      A * w * grad_out into private LDS copies of the 8x8xD tile -- each
-//      half-wave (or wave) owns one copy, so plain read-modify-writes never
-//      race -- then the copies are summed and every pixel is written once.
-//      Only bins split over several chunks add into grad_value atomically.
-// fp32 atomics on this chip run at a few hundred G lane-ops/s whether they
-// target LDS or memory, so scattering the 4*D contributions of every point
-// with atomics would cost milliseconds at the encoder shape; the binned
-// pipeline replaces them with integer LDS atomics and plain LDS traffic.
+// Backward (msda_backward):
+//   bwd_dots_kernel (on a side stream, concurrently with the rest): per
+//      point the four <grad_out row, neighbour row> dot products, reduced
+//      across the lane group with DPP, give grad_attn_weight and
+//      grad_sampling_loc.
+//   grad_value is a scatter (every point adds A * w * grad_out into four
+//   pixels).  fp32 atomics run at a few hundred G lane-ops/s on this chip,
+//   in LDS as in memory, so it is computed in gather form instead, per 8x8
+//   pixel tile and head ("bin"):
+//   bin_count_kernel: points per bin (LDS histogram, one global add per bin
+//      and workgroup).
+//   bin_scan_kernel: exclusive scan of the counts -> bin offsets, and a work
+//      list of (bin, chunk of at most kChunk records).
+//   bin_scatter_kernel: one 16-byte record per (point, bin) it touches,
+//      written into its bin (LDS ranks, one global reservation per bin and
+//      workgroup).
+//   grad_value_tile_kernel: per work item, the records are counting-sorted
+//      by the cell of their top-left neighbour and their grad_out rows are
+//      staged in LDS in that order; a lane owns (pixel, channel quad) pairs
+//      and sums over the four cells that feed its pixel, in registers.  Only
+//      bins split over several chunks add into grad_value atomically.
 //
 // value and grad_value are addressed through raw buffer descriptors whose
 // size is the batch slice.  A neighbour outside the map gets the offset
@@ -59,7 +61,7 @@ constexpr int kTilePx = kTile * kTile;
 constexpr int kChunk = 2048;               // points per grad_value work item, at most
 constexpr int kHistLds = 4096;             // bins of one (batch, head) kept in an LDS histogram
 constexpr int kScanThreads = 1024;
-constexpr int kTileGrid = 2048;            // persistent workgroups of the tile kernel
+constexpr int kTileGrid = 16384;           // workgroups of the tile kernel, at most
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
@@ -103,6 +105,24 @@ template <int G> __device__ __forceinline__ float group_sum(float v) {
     if constexpr (G >= 16) v += dpp<0x140>(v);  // row_mirror: the other half of 16
     if constexpr (G >= 32) v += __shfl_xor(v, 16, 64);
     if constexpr (G >= 64) v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    // lanes whose source is outside the row (or rows outside ROWS) receive 0
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, true);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts, then
+// row broadcasts of the running totals of rows 0 and 0-1).
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
+    v += dpp_u32<0x111, 0xF>(v);  // row_shr:1
+    v += dpp_u32<0x112, 0xF>(v);  // row_shr:2
+    v += dpp_u32<0x114, 0xF>(v);  // row_shr:4
+    v += dpp_u32<0x118, 0xF>(v);  // row_shr:8
+    v += dpp_u32<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v += dpp_u32<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
     return v;
 }
 
@@ -511,29 +531,35 @@ bin_count_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__
 }
 
 // ---------------------------------------------------------------------------
-// backward 2: scan of the bin counts, work list of (bin, chunk)
-// One workgroup of kScanThreads; bins are visited in (batch, head, bin) order.
+// backward: scan of the bin counts, work list
+// One workgroup of kScanThreads.  Bins are visited in (batch, tile, head)
+// order, which is also their order in memory: the bins of batch b are the
+// nbins * M words from b * nb_max * M on.  Each bin of n > 0 points becomes
+// ceil(n / kChunk) work items (bin, first record, records, whole bin).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void block_exclusive_scan2(uint32_t &a, uint32_t &b, uint32_t *s_a,
-                                                      uint32_t *s_b, uint32_t &tot_a,
-                                                      uint32_t &tot_b) {
-    const int t = threadIdx.x;
-    s_a[t] = a;
-    s_b[t] = b;
+// Exclusive scan of (a, b) pairs over the kScanThreads threads of the block:
+// wave-level scans with lane shuffles, then one scan of the wave totals.
+// The block totals are returned in tot_a, tot_b.
+__device__ __forceinline__ void block_exclusive_scan2(uint32_t &a, uint32_t &b, uint2 *s_wave,
+                                                      uint32_t &tot_a, uint32_t &tot_b) {
+    constexpr int kWaves = kScanThreads / 64;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const uint32_t ia = wave_inclusive_scan(a), ib = wave_inclusive_scan(b);
+    if (lane == 63) s_wave[wave] = make_uint2(ia, ib);
     __syncthreads();
-    for (int off = 1; off < kScanThreads; off <<= 1) {
-        const uint32_t xa = t >= off ? s_a[t - off] : 0u;
-        const uint32_t xb = t >= off ? s_b[t - off] : 0u;
-        __syncthreads();
-        s_a[t] += xa;
-        s_b[t] += xb;
-        __syncthreads();
+    if (wave == 0) {
+        const uint2 v = lane < kWaves ? s_wave[lane] : make_uint2(0u, 0u);
+        const uint32_t sa = wave_inclusive_scan(v.x), sb = wave_inclusive_scan(v.y);
+        if (lane < kWaves) s_wave[lane] = make_uint2(sa - v.x, sb - v.y);  // exclusive
+        if (lane == kWaves - 1) s_wave[kWaves] = make_uint2(sa, sb);
     }
-    tot_a = s_a[kScanThreads - 1];
-    tot_b = s_b[kScanThreads - 1];
-    a = s_a[t] - a;  // exclusive
-    b = s_b[t] - b;
     __syncthreads();
+    const uint2 base = s_wave[wave];
+    tot_a = s_wave[kWaves].x;
+    tot_b = s_wave[kWaves].y;
+    a = base.x + ia - a;
+    b = base.y + ib - b;
+    __syncthreads();  // s_wave is reused by the next call
 }
 
 __global__ void __launch_bounds__(kScanThreads)
@@ -543,46 +569,43 @@ bin_scan_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ 
                 uint32_t *__restrict__ work_total, int B, Dims dm) {
     constexpr int kPer = 8;
     __shared__ LevelLds s_lv;
-    __shared__ uint32_t s_a[kScanThreads], s_b[kScanThreads];
+    __shared__ uint2 s_wave[kScanThreads / 64 + 1];
     stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
-    const int nbins = s_lv.nbins;
-    // bins in (batch, tile, head) order; entry g maps to bin (b*nb_max + tile)*M + m
-    const int64_t per_b = (int64_t)nbins * dm.M;
-    const int64_t n = (int64_t)B * per_b;
+    const uint32_t per_b = (uint32_t)s_lv.nbins * (uint32_t)dm.M;
     uint32_t carry_e = 0, carry_c = 0;
-    for (int64_t base = 0; base < n; base += (int64_t)kScanThreads * kPer) {
-        uint32_t cnt[kPer], e = 0, ch = 0;
-        const int64_t g0 = base + (int64_t)threadIdx.x * kPer;
+    for (int b = 0; b < B; ++b) {
+        const uint32_t off_b = (uint32_t)b * (uint32_t)dm.nb_max * (uint32_t)dm.M;
+        for (uint32_t base = 0; base < per_b; base += kScanThreads * kPer) {
+            const uint32_t g0 = base + threadIdx.x * kPer;
+            uint32_t cnt[kPer], e = 0, ch = 0;
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int64_t g = g0 + i;
-            cnt[i] = 0;
-            if (g < n) cnt[i] = counts[(g / per_b) * dm.nb_max * dm.M + g % per_b];
-            e += cnt[i];
-            ch += (cnt[i] + kChunk - 1) / kChunk;
-        }
-        uint32_t tot_e, tot_c;
-        block_exclusive_scan2(e, ch, s_a, s_b, tot_e, tot_c);
-        e += carry_e;
-        ch += carry_c;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int64_t g = g0 + i;
-            if (g < n) {
-                const uint32_t bin = (uint32_t)((g / per_b) * dm.nb_max * dm.M + g % per_b);
-                start[bin] = e;
-                cursor[bin] = e;
-                const uint32_t nch = (cnt[i] + kChunk - 1) / kChunk;
-                for (uint32_t k = 0; k < nch; ++k)
-                    items[ch + k] = make_uint4(bin, e + k * kChunk,
-                                               min((uint32_t)kChunk, cnt[i] - k * kChunk),
-                                               nch == 1 ? 1u : 0u);
+            for (int i = 0; i < kPer; ++i) {
+                cnt[i] = g0 + i < per_b ? counts[off_b + g0 + i] : 0u;
                 e += cnt[i];
-                ch += nch;
+                ch += (cnt[i] + kChunk - 1) / kChunk;
             }
+            uint32_t tot_e, tot_c;
+            block_exclusive_scan2(e, ch, s_wave, tot_e, tot_c);
+            e += carry_e;
+            ch += carry_c;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                if (g0 + i < per_b) {
+                    const uint32_t bin = off_b + g0 + i;
+                    start[bin] = e;
+                    cursor[bin] = e;
+                    const uint32_t nch = (cnt[i] + kChunk - 1) / kChunk;
+                    for (uint32_t k = 0; k < nch; ++k)
+                        items[ch + k] = make_uint4(bin, e + k * kChunk,
+                                                   min((uint32_t)kChunk, cnt[i] - k * kChunk),
+                                                   nch == 1 ? 1u : 0u);
+                    e += cnt[i];
+                    ch += nch;
+                }
+            }
+            carry_e += tot_e;
+            carry_c += tot_c;
         }
-        carry_e += tot_e;
-        carry_c += tot_c;
     }
     if (threadIdx.x == 0) *work_total = carry_c;
 }
@@ -761,23 +784,26 @@ grad_value_tile_kernel(const int64_t *__restrict__ shapes, const int64_t *__rest
 
     const int M = dm.M, Nq = dm.Nq;
     const int tid = threadIdx.x;
-    stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
-    if (tid < kCells) s_tmp[tid] = 0u;
     const uint32_t total = *work_total;
     const uint32_t grid = gridDim.x;
+    if (blockIdx.x >= total) return;  // the grid is sized for the largest possible list
+    stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
+    if (tid < kCells) s_tmp[tid] = 0u;
 
     // Sub-chunk k (summed), k+1 (sorted, rows loading), k+2 (records loading),
-    // and the work item after the one of k+2.  The work list is in (batch,
-    // level, tile, head) order and workgroup g (dispatched to XCD g % 8) takes
-    // items g, g + grid, ...  With 8 heads the XCDs therefore split the work
-    // by head: every XCD gets the same mix of tiles, and the grad_out rows it
-    // gathers are those of one head.
+    // and the work item after the one of k+2.  Workgroup g takes items g,
+    // g + grid, ... counted from the end of the list: the grid is normally
+    // larger than the list, so each workgroup has one item and the hardware
+    // dispatcher balances the load, starting with the last items (the bins of
+    // the coarse levels, the largest).  The list is in (batch, level, tile,
+    // head) order, so with 8 heads workgroup g (dispatched to XCD g % 8) and
+    // its XCD mostly see one head, whose grad_out rows then stay in that L2.
+    auto item_at = [&](uint32_t w) { return items[total - 1u - w]; };
     SubChunk A{0, 0, make_uint4(0, 0, 0, 0), false};
     SubChunk Bn{0, 0, make_uint4(0, 0, 0, 0), false};
-    SubChunk C{blockIdx.x, 0, make_uint4(0, 0, 0, 0), blockIdx.x < total};
+    SubChunk C{blockIdx.x, 0, item_at(blockIdx.x), true};
     uint4 next_item = make_uint4(0, 0, 0, 0);
-    if (C.valid) C.it = items[C.w];
-    if (C.w + grid < total) next_item = items[C.w + grid];
+    if (C.w + grid < total) next_item = item_at(C.w + grid);
     auto advance = [&](SubChunk &c) {
         if (!c.valid) return;
         if (c.off + kSub < c.it.z) {
@@ -788,7 +814,7 @@ grad_value_tile_kernel(const int64_t *__restrict__ shapes, const int64_t *__rest
         c.off = 0;
         c.valid = c.w < total;
         c.it = next_item;
-        if (c.valid && c.w + grid < total) next_item = items[c.w + grid];
+        if (c.valid && c.w + grid < total) next_item = item_at(c.w + grid);
     };
     auto count_of = [&](const SubChunk &c) {
         return c.valid ? (int)min((uint32_t)kSub, c.it.z - c.off) : 0;
@@ -819,12 +845,7 @@ grad_value_tile_kernel(const int64_t *__restrict__ shapes, const int64_t *__rest
             const int c0 = 2 * tid, c1 = 2 * tid + 1;
             const uint32_t v0 = c0 < kCells ? s_tmp[c0] : 0u;
             const uint32_t v1 = c1 < kCells ? s_tmp[c1] : 0u;
-            uint32_t incl = v0 + v1;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const uint32_t t = __shfl_up(incl, off, 64);
-                if (tid >= off) incl += t;
-            }
+            const uint32_t incl = wave_inclusive_scan(v0 + v1);
             const uint32_t ex = incl - v0 - v1;
             if (c0 < kCells) {
                 stF[c0] = ex;
@@ -839,7 +860,8 @@ grad_value_tile_kernel(const int64_t *__restrict__ shapes, const int64_t *__rest
         __syncthreads();
         // 3. place the records of Bn in cell order
         if (tid < nb) {
-            const uint32_t slot = atomicAdd(&s_tmp[cell], 1u);
+            // the scan makes every slot < nb <= kSub; the clamp keeps LDS safe regardless
+            const uint32_t slot = min(atomicAdd(&s_tmp[cell], 1u), (uint32_t)kSub - 1u);
             const float a0 = __uint_as_float(rec.y), a1 = __uint_as_float(rec.z);
             const float fy = __uint_as_float(rec.w), gy = 1.f - fy;
             wF[slot] = make_float4(a0 * gy, a1 * gy, a0 * fy, a1 * fy);
@@ -855,7 +877,8 @@ grad_value_tile_kernel(const int64_t *__restrict__ shapes, const int64_t *__rest
             const float *gob = grad_out + ((size_t)b * Nq * M + m) * D;
             for (int i = tid; i < nb * kQuads; i += kTileThreads) {
                 const int slot = i / kQuads, qd = i - slot * kQuads;
-                const float *src = gob + (size_t)s_q[slot] * M * D + 4 * qd;
+                const uint32_t qy = min(s_q[slot], (uint32_t)Nq - 1u);  // a query of this batch
+                const float *src = gob + (size_t)qy * M * D + 4 * qd;
                 // each wave fills 64 consecutive float4 slots: lane l writes slot base + l
                 __builtin_amdgcn_global_load_lds((global_void_t *)src,
                                                  (lds_void_t *)(gF + (i & ~63)), 16, 0, 0);
@@ -1312,6 +1335,9 @@ msda_status backward_impl(const void *value, int value_dtype, const int64_t *spa
             !grad_out || !grad_sampling_loc || !grad_attn_weight)
             return MSDA_ERR_NULL;
         wl = work_layout(B, Nv, Nq, M, L, K);
+        // bin counters and work items are indexed with 31-bit integers
+        if (wl.bm_bins >= ((int64_t)1 << 31) || wl.work_max >= ((int64_t)1 << 31))
+            return MSDA_ERR_UNSUPPORTED;
         if (!workspace) return MSDA_ERR_NULL;
         if (workspace_bytes < wl.bytes) return MSDA_ERR_WORKSPACE;
         if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return MSDA_ERR_WORKSPACE;
