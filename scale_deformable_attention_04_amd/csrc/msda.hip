@@ -271,6 +271,19 @@ __device__ __forceinline__ int xcd_contiguous(int k, int total) {
     return x * per + min(x, rem) + j;
 }
 
+// Division by a divisor fixed at launch: n / d = (umulhi(n, mul) + n) >> shift
+// with shift = ceil(log2 d) and mul = floor(2^32 (2^shift - d) / d) + 1
+// (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994).  Exact for every n < 2^31, where the sum cannot
+// overflow 32 bits.
+struct FastDiv {
+    uint32_t mul, shift;
+};
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+    return (__umulhi(n, f.mul) + n) >> f.shift;
+}
+
 struct Dims {
     int Nv, Nq, M, L, K;
     int PC;      // points per chunk (point-table kernels)
@@ -279,6 +292,8 @@ struct Dims {
     int nblk;    // workgroups per batch (forward) or per (batch, head) (backward)
     int nb_max;      // bin stride per (batch, head) in the workspace
     int accumulate;  // grad_value already holds a gradient to add to
+    FastDiv div_lk;  // by L * K (count and scatter kernels)
+    FastDiv div_k;   // by K
 };
 
 // Workspace of the backward pipeline (all 32-bit words).
@@ -474,10 +489,11 @@ bwd_dots_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
 // ---------------------------------------------------------------------------
 // backward: points per bin
 // Workgroup = (batch b, head m, kBinPoints consecutive points of the
-// (b, m) list in (query, level, point) order), kBinPPT points per thread.
+// (b, m) list in (query, level, point) order), kBinPPT points per thread,
+// all of whose coordinates are loaded before any is used.
 // ---------------------------------------------------------------------------
-constexpr int kBinPoints = 1024;
-constexpr int kBinPPT = kBinPoints / kThreads;
+constexpr int kBinPPT = 16;
+constexpr int kBinPoints = kBinPPT * kThreads;
 
 __global__ void __launch_bounds__(kThreads)
 bin_count_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ starts,
@@ -487,13 +503,24 @@ bin_count_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__
     extern __shared__ __align__(16) unsigned char smem[];
     uint32_t *s_cnt = reinterpret_cast<uint32_t *>(smem);  // [hist_cap]
 
-    const int M = dm.M, K = dm.K, LK = dm.L * dm.K, Nq = dm.Nq;
+    const int M = dm.M, LK = dm.L * dm.K, Nq = dm.Nq;
     const int wg = xcd_contiguous(blockIdx.x, gridDim.x);
     const int bm = wg / dm.nblk + dm.b0 * M;
     const int m = bm % M, b = bm / M;
     const int f0 = (wg % dm.nblk) * kBinPoints;
     const int nf = Nq * LK;
+    const size_t row0 = (size_t)b * Nq * M + m;  // item row of query 0
 
+    float2 uv[kBinPPT];
+#pragma unroll
+    for (int r = 0; r < kBinPPT; ++r) {
+        const int f = f0 + threadIdx.x + r * kThreads;
+        uv[r] = make_float2(0.f, 0.f);
+        if (f < nf) {
+            const int q = (int)fdiv((uint32_t)f, dm.div_lk), j = f - q * LK;
+            uv[r] = reinterpret_cast<const float2 *>(loc)[(row0 + (size_t)q * M) * LK + j];
+        }
+    }
     stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
     const int nbins = s_lv.nbins;
     const bool lds = nbins <= hist_cap;
@@ -506,11 +533,9 @@ bin_count_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__
     for (int r = 0; r < kBinPPT; ++r) {
         const int f = f0 + threadIdx.x + r * kThreads;
         if (f < nf) {
-            const int q = f / LK, j = f - q * LK;
-            const size_t p = (((size_t)b * Nq + q) * M + m) * LK + j;
-            const float2 uv = reinterpret_cast<const float2 *>(loc)[p];
-            const int l = j / K;
-            const Neighbours n = neighbours(uv.x, uv.y, s_lv.lvl[l], 0u, 0u);
+            const int q = (int)fdiv((uint32_t)f, dm.div_lk), j = f - q * LK;
+            const int l = (int)fdiv((uint32_t)j, dm.div_k);
+            const Neighbours n = neighbours(uv[r].x, uv[r].y, s_lv.lvl[l], 0u, 0u);
             int bins[4];
             const int nb = point_bins(n, s_lv.lvl[l], s_lv.tw[l], bins);
             for (int k = 0; k < nb; ++k) {
@@ -631,13 +656,29 @@ bin_scatter_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict
     uint32_t *s_cnt = reinterpret_cast<uint32_t *>(smem);  // [hist_cap] counts, then ranks
     uint32_t *s_base = s_cnt + hist_cap;                    // [hist_cap] reserved offsets
 
-    const int M = dm.M, K = dm.K, LK = dm.L * dm.K, Nq = dm.Nq;
+    const int M = dm.M, LK = dm.L * dm.K, Nq = dm.Nq;
     const int wg = xcd_contiguous(blockIdx.x, gridDim.x);
     const int bm = wg / dm.nblk + dm.b0 * M;
     const int m = bm % M, b = bm / M;
     const int f0 = (wg % dm.nblk) * kBinPoints;
     const int nf = Nq * LK;
+    const size_t row0 = (size_t)b * Nq * M + m;  // item row of query 0
 
+    // the thread's points: coordinates and weights, kept for both passes
+    float2 uv[kBinPPT];
+    float aw[kBinPPT];
+#pragma unroll
+    for (int r = 0; r < kBinPPT; ++r) {
+        const int f = f0 + threadIdx.x + r * kThreads;
+        uv[r] = make_float2(0.f, 0.f);
+        aw[r] = 0.f;
+        if (f < nf) {
+            const int q = (int)fdiv((uint32_t)f, dm.div_lk), j = f - q * LK;
+            const size_t p = (row0 + (size_t)q * M) * LK + j;
+            uv[r] = reinterpret_cast<const float2 *>(loc)[p];
+            aw[r] = attn[p];
+        }
+    }
     stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
     const int nbins = s_lv.nbins;
     const bool lds = nbins <= hist_cap;
@@ -645,41 +686,18 @@ bin_scatter_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict
     if (lds) {
         for (int i = threadIdx.x; i < nbins; i += kThreads) s_cnt[i] = 0u;
         __syncthreads();
-    }
-
-    // the thread's points, kept for the second pass
-    Neighbours nb[kBinPPT];
-    float a0[kBinPPT], a1[kBinPPT];
-    int qq[kBinPPT], ll[kBinPPT];
 #pragma unroll
-    for (int r = 0; r < kBinPPT; ++r) {
-        const int f = f0 + threadIdx.x + r * kThreads;
-        nb[r].valid = 0u;
-        qq[r] = 0;
-        ll[r] = 0;
-        a0[r] = a1[r] = 0.f;
-        if (f < nf) {
-            const int q = f / LK, j = f - q * LK;
-            const size_t p = (((size_t)b * Nq + q) * M + m) * LK + j;
-            const float2 uv = reinterpret_cast<const float2 *>(loc)[p];
-            const float A = attn[p];
-            const int l = j / K;
-            nb[r] = neighbours(uv.x, uv.y, s_lv.lvl[l], 0u, 0u);
-            qq[r] = q;
-            ll[r] = l;
-            a0[r] = A * (1.f - nb[r].fx);
-            a1[r] = A * nb[r].fx;
-            if (lds) {
-                uint32_t t[4];
-                const int nt = point_tiles(nb[r], t);
-                for (int k = 0; k < nt; ++k)
-                    atomicAdd(&s_cnt[s_lv.lvl[l].w + (int)(t[k] >> 16) * s_lv.tw[l] +
-                                     (int)(t[k] & 0xffffu)],
-                              1u);
+        for (int r = 0; r < kBinPPT; ++r) {
+            const int f = f0 + threadIdx.x + r * kThreads;
+            if (f < nf) {
+                const int q = (int)fdiv((uint32_t)f, dm.div_lk), j = f - q * LK;
+                const int l = (int)fdiv((uint32_t)j, dm.div_k);
+                const Neighbours n = neighbours(uv[r].x, uv[r].y, s_lv.lvl[l], 0u, 0u);
+                int bins[4];
+                const int nb = point_bins(n, s_lv.lvl[l], s_lv.tw[l], bins);
+                for (int k = 0; k < nb; ++k) atomicAdd(&s_cnt[bins[k]], 1u);
             }
         }
-    }
-    if (lds) {
         __syncthreads();
         for (int i = threadIdx.x; i < nbins; i += kThreads) {
             const uint32_t v = s_cnt[i];
@@ -690,18 +708,24 @@ bin_scatter_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict
     }
 #pragma unroll
     for (int r = 0; r < kBinPPT; ++r) {
-        uint32_t t[4];
-        const int nt = point_tiles(nb[r], t);
-        const int l = ll[r];
-        for (int k = 0; k < nt; ++k) {
-            const int tx = (int)(t[k] & 0xffffu), ty = (int)(t[k] >> 16);
-            const int bin = s_lv.lvl[l].w + ty * s_lv.tw[l] + tx;
-            const uint32_t slot = lds ? s_base[bin] + atomicAdd(&s_cnt[bin], 1u)
-                                      : atomicAdd(&gcur[(size_t)bin * M], 1u);
-            const int cell = (nb[r].xi - tx * kTile + 1) + kCellsW * (nb[r].yi - ty * kTile + 1);
-            recs[slot] = make_uint4(((uint32_t)qq[r] << kRecQueryShift) | (uint32_t)cell,
-                                    __float_as_uint(a0[r]), __float_as_uint(a1[r]),
-                                    __float_as_uint(nb[r].fy));
+        const int f = f0 + threadIdx.x + r * kThreads;
+        if (f < nf) {
+            const int q = (int)fdiv((uint32_t)f, dm.div_lk), j = f - q * LK;
+            const int l = (int)fdiv((uint32_t)j, dm.div_k);
+            const Neighbours n = neighbours(uv[r].x, uv[r].y, s_lv.lvl[l], 0u, 0u);
+            uint32_t t[4];
+            const int nt = point_tiles(n, t);
+            const uint32_t a0 = __float_as_uint(aw[r] * (1.f - n.fx));
+            const uint32_t a1 = __float_as_uint(aw[r] * n.fx);
+            for (int k = 0; k < nt; ++k) {
+                const int tx = (int)(t[k] & 0xffffu), ty = (int)(t[k] >> 16);
+                const int bin = s_lv.lvl[l].w + ty * s_lv.tw[l] + tx;
+                const uint32_t slot = lds ? s_base[bin] + atomicAdd(&s_cnt[bin], 1u)
+                                          : atomicAdd(&gcur[(size_t)bin * M], 1u);
+                const int cell = (n.xi - tx * kTile + 1) + kCellsW * (n.yi - ty * kTile + 1);
+                recs[slot] = make_uint4(((uint32_t)q << kRecQueryShift) | (uint32_t)cell, a0, a1,
+                                        __float_as_uint(n.fy));
+            }
         }
     }
 }
@@ -1056,6 +1080,13 @@ Launch plan(int64_t D, int64_t L, int64_t K, int bytes_per_point) {
     return p;
 }
 
+FastDiv make_fastdiv(uint32_t d) {  // d >= 1
+    uint32_t shift = 0;
+    while (shift < 31 && (1u << shift) < d) ++shift;
+    const uint64_t mul = ((uint64_t)1 << 32) * (((uint64_t)1 << shift) - d) / d + 1;
+    return FastDiv{(uint32_t)mul, shift};
+}
+
 msda_status hip_status(hipError_t e) {
     if (e == hipSuccess) return MSDA_OK;
     g_last_hip_error = (int)e;
@@ -1201,7 +1232,7 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
     const int hist_cap = (int)(wl.nb_max < kHistLds ? wl.nb_max : kHistLds);
     const int64_t gb = (Nq * L * K + kBinPoints - 1) / kBinPoints;  // per (batch, head)
     Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, 0, 0, 0, (int)gb, (int)wl.nb_max,
-            accumulate ? 1 : 0};
+            accumulate ? 1 : 0, make_fastdiv((uint32_t)(L * K)), make_fastdiv((uint32_t)K)};
     mark(3);
     st = per_batch(gb * M, [&](int64_t b0, unsigned grid) {
         Dims d2 = dm;
