@@ -213,38 +213,27 @@ __device__ __forceinline__ Neighbours neighbours(float u, float v, int4 lvl, uin
     return n;
 }
 
-// The distinct grad_value tiles (bins, relative to the (batch, head)) that
-// hold at least one of the point's neighbours inside the map.
-__device__ __forceinline__ int point_bins(const Neighbours &n, int4 lvl, int tw, int bins[4]) {
-    if (!n.valid) return 0;
-    const int tx0 = n.xi >> kTileShift, tx1 = (n.xi + 1) >> kTileShift;
-    const int ty0 = n.yi >> kTileShift, ty1 = (n.yi + 1) >> kTileShift;
-    const bool sx = tx1 != tx0, sy = ty1 != ty0;
-    const bool vTL = n.valid & 1u, vTR = n.valid & 2u, vBL = n.valid & 4u, vBR = n.valid & 8u;
-    int k = 0;
-    if (vTL || (!sx && vTR) || (!sy && vBL) || (!sx && !sy && vBR))
-        bins[k++] = lvl.w + ty0 * tw + tx0;
-    if (sx && (vTR || (!sy && vBR))) bins[k++] = lvl.w + ty0 * tw + tx1;
-    if (sy && (vBL || (!sx && vBR))) bins[k++] = lvl.w + ty1 * tw + tx0;
-    if (sx && sy && vBR) bins[k++] = lvl.w + ty1 * tw + tx1;
-    return k;
-}
+// The distinct grad_value tiles (bins) that hold at least one of the point's
+// neighbours inside the map: tile (tx0 + (c & 1), ty0 + (c >> 1)) iff bit c
+// of `mask` is set.  The neighbours span one or two tiles in each direction
+// (sx, sy); x0 = -1 gives tx0 = -1, whose bits are then never set.
+struct TileMask {
+    int tx0, ty0;
+    uint32_t mask;
+};
 
-// The same tiles as point_bins, as tile coordinates packed (ty << 16) | tx.
-__device__ __forceinline__ int point_tiles(const Neighbours &n, uint32_t tiles[4]) {
-    if (!n.valid) return 0;
-    // x0 = -1 gives tile -1, which only ever holds outside neighbours
-    const int tx0 = n.xi >> kTileShift, tx1 = (n.xi + 1) >> kTileShift;
-    const int ty0 = n.yi >> kTileShift, ty1 = (n.yi + 1) >> kTileShift;
-    const bool sx = tx1 != tx0, sy = ty1 != ty0;
-    const bool vTL = n.valid & 1u, vTR = n.valid & 2u, vBL = n.valid & 4u, vBR = n.valid & 8u;
-    auto pack = [](int tx, int ty) { return ((uint32_t)ty << 16) | (uint32_t)tx; };
-    int k = 0;
-    if (vTL || (!sx && vTR) || (!sy && vBL) || (!sx && !sy && vBR)) tiles[k++] = pack(tx0, ty0);
-    if (sx && (vTR || (!sy && vBR))) tiles[k++] = pack(tx1, ty0);
-    if (sy && (vBL || (!sx && vBR))) tiles[k++] = pack(tx0, ty1);
-    if (sx && sy && vBR) tiles[k++] = pack(tx1, ty1);
-    return k;
+__device__ __forceinline__ TileMask point_tile_mask(const Neighbours &n) {
+    const int tx0 = n.xi >> kTileShift, ty0 = n.yi >> kTileShift;
+    const uint32_t sx = ((n.xi + 1) >> kTileShift) != tx0 ? 1u : 0u;
+    const uint32_t sy = ((n.yi + 1) >> kTileShift) != ty0 ? 1u : 0u;
+    const uint32_t v = n.valid;
+    const uint32_t tl = v & 1u, tr = (v >> 1) & 1u, bl = (v >> 2) & 1u, br = (v >> 3) & 1u;
+    const uint32_t nsx = sx ^ 1u, nsy = sy ^ 1u;
+    const uint32_t m0 = tl | (nsx & tr) | (nsy & bl) | (nsx & nsy & br);
+    const uint32_t m1 = sx & (tr | (nsy & br));
+    const uint32_t m2 = sy & (bl | (nsx & br));
+    const uint32_t m3 = sx & sy & br;
+    return TileMask{tx0, ty0, m0 | (m1 << 1) | (m2 << 2) | (m3 << 3)};
 }
 
 __device__ __forceinline__ void fma4(float4 &acc, float w, const float4 &v) {
@@ -536,13 +525,19 @@ bin_count_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__
             const int q = (int)fdiv((uint32_t)f, dm.div_lk), j = f - q * LK;
             const int l = (int)fdiv((uint32_t)j, dm.div_k);
             const Neighbours n = neighbours(uv[r].x, uv[r].y, s_lv.lvl[l], 0u, 0u);
-            int bins[4];
-            const int nb = point_bins(n, s_lv.lvl[l], s_lv.tw[l], bins);
-            for (int k = 0; k < nb; ++k) {
-                if (lds)
-                    atomicAdd(&s_cnt[bins[k]], 1u);
-                else
-                    atomicAdd(&gcount[(size_t)bins[k] * M], 1u);
+            const TileMask tm = point_tile_mask(n);
+            const int tw = s_lv.tw[l];
+            const int b00 = s_lv.lvl[l].w + tm.ty0 * tw + tm.tx0;
+            if (lds) {
+                if (tm.mask & 1u) atomicAdd(&s_cnt[b00], 1u);
+                if (tm.mask & 2u) atomicAdd(&s_cnt[b00 + 1], 1u);
+                if (tm.mask & 4u) atomicAdd(&s_cnt[b00 + tw], 1u);
+                if (tm.mask & 8u) atomicAdd(&s_cnt[b00 + tw + 1], 1u);
+            } else {
+                if (tm.mask & 1u) atomicAdd(&gcount[(size_t)b00 * M], 1u);
+                if (tm.mask & 2u) atomicAdd(&gcount[(size_t)(b00 + 1) * M], 1u);
+                if (tm.mask & 4u) atomicAdd(&gcount[(size_t)(b00 + tw) * M], 1u);
+                if (tm.mask & 8u) atomicAdd(&gcount[(size_t)(b00 + tw + 1) * M], 1u);
             }
         }
     }
@@ -693,9 +688,13 @@ bin_scatter_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict
                 const int q = (int)fdiv((uint32_t)f, dm.div_lk), j = f - q * LK;
                 const int l = (int)fdiv((uint32_t)j, dm.div_k);
                 const Neighbours n = neighbours(uv[r].x, uv[r].y, s_lv.lvl[l], 0u, 0u);
-                int bins[4];
-                const int nb = point_bins(n, s_lv.lvl[l], s_lv.tw[l], bins);
-                for (int k = 0; k < nb; ++k) atomicAdd(&s_cnt[bins[k]], 1u);
+                const TileMask tm = point_tile_mask(n);
+                const int tw = s_lv.tw[l];
+                const int b00 = s_lv.lvl[l].w + tm.ty0 * tw + tm.tx0;
+                if (tm.mask & 1u) atomicAdd(&s_cnt[b00], 1u);
+                if (tm.mask & 2u) atomicAdd(&s_cnt[b00 + 1], 1u);
+                if (tm.mask & 4u) atomicAdd(&s_cnt[b00 + tw], 1u);
+                if (tm.mask & 8u) atomicAdd(&s_cnt[b00 + tw + 1], 1u);
             }
         }
         __syncthreads();
@@ -713,18 +712,25 @@ bin_scatter_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict
             const int q = (int)fdiv((uint32_t)f, dm.div_lk), j = f - q * LK;
             const int l = (int)fdiv((uint32_t)j, dm.div_k);
             const Neighbours n = neighbours(uv[r].x, uv[r].y, s_lv.lvl[l], 0u, 0u);
-            uint32_t t[4];
-            const int nt = point_tiles(n, t);
+            const TileMask tm = point_tile_mask(n);
+            const int tw = s_lv.tw[l];
+            const int b00 = s_lv.lvl[l].w + tm.ty0 * tw + tm.tx0;
             const uint32_t a0 = __float_as_uint(aw[r] * (1.f - n.fx));
             const uint32_t a1 = __float_as_uint(aw[r] * n.fx);
-            for (int k = 0; k < nt; ++k) {
-                const int tx = (int)(t[k] & 0xffffu), ty = (int)(t[k] >> 16);
-                const int bin = s_lv.lvl[l].w + ty * s_lv.tw[l] + tx;
-                const uint32_t slot = lds ? s_base[bin] + atomicAdd(&s_cnt[bin], 1u)
-                                          : atomicAdd(&gcur[(size_t)bin * M], 1u);
-                const int cell = (n.xi - tx * kTile + 1) + kCellsW * (n.yi - ty * kTile + 1);
-                recs[slot] = make_uint4(((uint32_t)q << kRecQueryShift) | (uint32_t)cell, a0, a1,
-                                        __float_as_uint(n.fy));
+            const uint32_t fy = __float_as_uint(n.fy);
+            // cell of the top-left neighbour relative to tile (tx0, ty0); one
+            // tile to the right is 8 cells left, one tile down is 72 cells up
+            const uint32_t key = ((uint32_t)q << kRecQueryShift);
+            const int c00 = (n.xi - tm.tx0 * kTile + 1) + kCellsW * (n.yi - tm.ty0 * kTile + 1);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                if (tm.mask & (1u << c)) {
+                    const int bin = b00 + (c & 1) + (c >> 1) * tw;
+                    const uint32_t slot = lds ? s_base[bin] + atomicAdd(&s_cnt[bin], 1u)
+                                              : atomicAdd(&gcur[(size_t)bin * M], 1u);
+                    const int cell = c00 - (c & 1) * kTile - (c >> 1) * kTile * kCellsW;
+                    recs[slot] = make_uint4(key | (uint32_t)cell, a0, a1, fy);
+                }
             }
         }
     }
