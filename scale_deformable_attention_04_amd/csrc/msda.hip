@@ -62,6 +62,7 @@ constexpr int kChunk = 2048;               // points per grad_value work item, a
 constexpr int kHistLds = 4096;             // bins of one (batch, head) kept in an LDS histogram
 constexpr int kScanThreads = 1024;
 constexpr int kTileGrid = 16384;           // workgroups of the tile kernel, at most
+constexpr int kDotsGrid = 512;             // workgroups of the dots kernel, at most
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
@@ -283,6 +284,7 @@ struct Dims {
     int accumulate;  // grad_value already holds a gradient to add to
     FastDiv div_lk;  // by L * K (count and scatter kernels)
     FastDiv div_k;   // by K
+    int nblocks;     // query blocks of the launch (dots kernel)
 };
 
 // Workspace of the backward pipeline (all 32-bit words).
@@ -390,15 +392,19 @@ bwd_dots_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
     float4 *s_aux = reinterpret_cast<float4 *>(s_off + IPB * dm.PS);
 
     const int M = dm.M, K = dm.K, LK = dm.L * dm.K, Nq = dm.Nq;
-    const int wg = xcd_contiguous(blockIdx.x, gridDim.x);
+    stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, 0x7fffffff);
+    // blocks of IPB queries of one (batch, head), dm.nblk per (batch, head);
+    // workgroup g takes blocks g, g + grid, ...
+    const int total = dm.nblocks;
+    for (int blk = blockIdx.x; blk < total; blk += gridDim.x) {
+    if (blk != (int)blockIdx.x) __syncthreads();  // the point tables are reused
+    const int wg = xcd_contiguous(blk, total);
     const int bm = wg / dm.nblk + dm.b0 * M;
     const int m = bm % M, b = bm / M;
     const int q0 = (wg % dm.nblk) * IPB;
     const int nitems = min(IPB, Nq - q0);
     const uint32_t row_stride = (uint32_t)M * D * 4u;
     const uint32_t head_off = (uint32_t)m * D * 4u;
-
-    stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, 0x7fffffff);
 
     const size_t slice = (size_t)dm.Nv * M * D;
     const rsrc_t vr = make_rsrc(value + (size_t)b * slice, (uint32_t)(slice * sizeof(VT)));
@@ -472,6 +478,7 @@ bwd_dots_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
             grad_attn[p] = ga;
             reinterpret_cast<float2 *>(grad_loc)[p] = make_float2(gx, gy);
         }
+    }
     }
 }
 
@@ -1142,8 +1149,9 @@ msda_status fill_zero(void *p, size_t n4, hipStream_t s) {
 struct Exec {
     hipStream_t s;
     hipStream_t side;
-    hipEvent_t fork, join;
+    hipEvent_t fork, filled, join;  // fork from s; grad_value zeroed; side work done
     hipEvent_t *ev;
+    bool fill_on_side;              // the grad_value zero-fill was enqueued on `side`
 };
 
 // One side stream per device, created on first use (default priority,
@@ -1154,7 +1162,7 @@ constexpr int kMaxDevices = 64;
 struct SideStream {
     bool tried = false;
     hipStream_t s = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
+    hipEvent_t fork = nullptr, filled = nullptr, join = nullptr;
 };
 std::mutex g_side_mu;
 SideStream g_side[kMaxDevices];
@@ -1168,13 +1176,15 @@ SideStream *side_stream() {
         ss.tried = true;
         bool ok = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) == hipSuccess;
         ok = ok && hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess;
+        ok = ok && hipEventCreateWithFlags(&ss.filled, hipEventDisableTiming) == hipSuccess;
         ok = ok && hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) == hipSuccess;
         if (!ok) {
             if (ss.join) (void)hipEventDestroy(ss.join);
+            if (ss.filled) (void)hipEventDestroy(ss.filled);
             if (ss.fork) (void)hipEventDestroy(ss.fork);
             if (ss.s) (void)hipStreamDestroy(ss.s);
             ss.s = nullptr;
-            ss.fork = ss.join = nullptr;
+            ss.fork = ss.filled = ss.join = nullptr;
             (void)hipGetLastError();
         }
     }
@@ -1220,7 +1230,11 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
     mark(1);
     msda_status st = per_batch(gq * M, [&](int64_t b0, unsigned grid) {
         Dims d2{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, p.pc, p.ps, (int)b0, (int)gq, 0, 0};
-        hipLaunchKernelGGL((bwd_dots_kernel<D, VT>), dim3(grid), dim3(kThreads), p.lds, ds,
+        d2.nblocks = (int)grid;
+        // a few workgroups per CU suffice for this gather-bound kernel, and leave
+        // room for the grad_value kernels running beside it
+        const unsigned g = grid > (unsigned)kDotsGrid ? (unsigned)kDotsGrid : grid;
+        hipLaunchKernelGGL((bwd_dots_kernel<D, VT>), dim3(g), dim3(kThreads), p.lds, ds,
                            static_cast<const VT *>(value), shapes, starts, loc, attn, gout, gloc,
                            gattn, d2);
     });
@@ -1264,6 +1278,10 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
     if (st != MSDA_OK) return st;
 
     const int64_t grid = wl.work_max < kTileGrid ? wl.work_max : kTileGrid;
+    if (ex.fill_on_side) {
+        st = hip_status(hipStreamWaitEvent(s, ex.filled, 0));
+        if (st != MSDA_OK) return st;
+    }
     mark(6);
     hipLaunchKernelGGL((grad_value_tile_kernel<D>), dim3((unsigned)grid), dim3(kTileThreads), 0, s,
                        shapes, starts, gout, w.items, w.work_total, w.recs, gval, dm);
@@ -1381,13 +1399,14 @@ msda_status backward_impl(const void *value, int value_dtype, const int64_t *spa
     }
     // The timed variant stays on the caller's stream, so that its stage
     // times are those of one kernel each.
-    Exec ex{s, nullptr, nullptr, nullptr, ev};
+    Exec ex{s, nullptr, nullptr, nullptr, nullptr, ev, false};
     std::unique_lock<std::mutex> lock(g_side_mu, std::defer_lock);
     if (work && !ev) {
         lock.lock();
         if (SideStream *ss = side_stream()) {
             ex.side = ss->s;
             ex.fork = ss->fork;
+            ex.filled = ss->filled;
             ex.join = ss->join;
         }
     }
@@ -1398,7 +1417,13 @@ msda_status backward_impl(const void *value, int value_dtype, const int64_t *spa
         if (st != MSDA_OK) return st;
     }
     if (!(flags & MSDA_BWD_ACCUMULATE)) {
-        st = fill_zero(grad_value, (size_t)nval / 4, s);  // D is a multiple of 4
+        // with a side stream the fill runs there, ahead of the dots kernel, and
+        // the tile kernel waits for it
+        st = fill_zero(grad_value, (size_t)nval / 4, ex.side ? ex.side : s);  // D % 4 == 0
+        if (st == MSDA_OK && ex.side) {
+            st = hip_status(hipEventRecord(ex.filled, ex.side));
+            ex.fill_on_side = true;
+        }
         if (st != MSDA_OK) return st;
     }
     if (!work) {
