@@ -142,27 +142,33 @@ msda_status msda_backward(const void *value, int value_dtype,
                           uint32_t flags, void *stream);
 
 /*
- * Measurement entry point: msda_backward with the same arguments, followed by
- * a synchronization of `stream`; stage_us[0..MSDA_BWD_STAGES) receives the
- * duration in microseconds of each stage, timed with HIP events recorded on
- * `stream` between the launches:
- *   0 grad_value zero-fill (0 with MSDA_BWD_ACCUMULATE)
+ * Measurement entry point: msda_backward with the same arguments and the same
+ * work on the same streams, which in addition records caller-owned HIP events
+ * around each of its MSDA_BWD_STAGES stages: events[2i] just before the
+ * stage's kernel and events[2i + 1] just after it, on the stream that runs it
+ * (stages 0 and 1 run on the library's side stream when it has one, the
+ * others on `stream`).  Nothing is synchronized; once the caller has waited
+ * for `stream`, hipEventElapsedTime(events[2i], events[2i + 1]) is the
+ * duration of stage i.  Stages:
+ *   0 grad_value zero-fill (empty with MSDA_BWD_ACCUMULATE)
  *   1 grad_attn_weight / grad_sampling_loc   2 workspace clear
  *   3 points per value tile   4 count scan   5 record scatter into tiles
  *   6 grad_value tiles
- * Unlike msda_backward, which computes stage 1 on a side stream of its own
- * concurrently with stages 2-6, every stage here runs on `stream`, one after
- * the other.  Not for production loops: it blocks the calling thread.
+ * events: 2 * MSDA_BWD_STAGES hipEvent_t created by the caller (with timing);
+ * a null entry is skipped (an event record costs the stream a few
+ * microseconds, so a caller timing one stage passes only its two events).
+ * events itself must not be NULL (MSDA_ERR_NULL).  The library keeps no
+ * reference to them.
  */
 #define MSDA_BWD_STAGES 7
-msda_status msda_backward_timed(const void *value, int value_dtype,
-                                const int64_t *spatial_shapes, const int64_t *level_start_index,
-                                const float *sampling_loc, const float *attn_weight,
-                                const float *grad_out, float *grad_value,
-                                float *grad_sampling_loc, float *grad_attn_weight,
-                                int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
-                                int64_t L, int64_t K, void *workspace, size_t workspace_bytes,
-                                uint32_t flags, void *stream, float *stage_us);
+msda_status msda_backward_events(const void *value, int value_dtype,
+                                 const int64_t *spatial_shapes, const int64_t *level_start_index,
+                                 const float *sampling_loc, const float *attn_weight,
+                                 const float *grad_out, float *grad_value,
+                                 float *grad_sampling_loc, float *grad_attn_weight,
+                                 int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
+                                 int64_t L, int64_t K, void *workspace, size_t workspace_bytes,
+                                 uint32_t flags, void *stream, void *const *events);
 
 /*
  * Pure host check of the sizes and of a HOST copy of the level table:

@@ -4,20 +4,20 @@
 Two modes:
 
   python3 profile_kernels.py run
-      The workload rocprofv3 is pointed at: the encoder-shape forward and
-      backward (3 calls each), then an elementwise multiply that reads 256 MiB
-      and writes 256 MiB, used to calibrate the FETCH_SIZE / WRITE_SIZE
-      counters (bytes known / counter reading).
+      The workload the two counter passes are pointed at: the encoder-shape
+      forward and backward (3 calls each), then an elementwise multiply that
+      reads 256 MiB and writes 256 MiB, used to calibrate the FETCH_SIZE /
+      WRITE_SIZE counters (bytes known / counter reading).
 
   python3 profile_kernels.py summarize --stats DIR --fetch DIR --write DIR
-      Reads the CSV output of three rocprofv3 runs of `run` (kernel-trace
-      stats; --pmc FETCH_SIZE; --pmc WRITE_SIZE) and writes
-      profiles/encoder_kernels.txt (per-kernel average durations) and
-      profiles/traffic.json (HBM bytes per launch of each kernel, scaled by the
-      copy calibration, tagged with the kernel source hash).
+      Reads the CSV output of three rocprofv3 runs (kernel-trace stats of the
+      bench command itself; --pmc FETCH_SIZE and --pmc WRITE_SIZE of `run`)
+      and writes profiles/encoder_kernels.txt (per-kernel average durations)
+      and profiles/traffic.json (HBM bytes per launch of each kernel, scaled by
+      the multiply's calibration, tagged with the kernel source hash).
 
 The GPU commands (run from /tmp with TMPDIR=/tmp, outputs under gpurun_out):
-  rocprofv3 --kernel-trace --stats --output-format csv -d OUT/stats -o run -- python3 profile_kernels.py run
+  rocprofv3 --kernel-trace --stats --output-format csv -d OUT/stats -o run -- python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline
   rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/fetch -o run -- python3 profile_kernels.py run
   rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/write -o run -- python3 profile_kernels.py run
 """
@@ -88,8 +88,10 @@ def _counter_means(dirpath, counter):
 
 def summarize(stats_dir, fetch_dir, write_dir, commands):
     stats = _rows(os.path.join(stats_dir, "**", "*kernel_stats.csv"))
-    lines = ["# rocprofv3 --kernel-trace --stats, encoder workload (B=2, Nq=Nv=22223, M=8, D=32,",
-             "# L=4, K=4, fp32), 3 forward + 3 backward calls; kernel source sha " + source_sha(),
+    lines = ["# rocprofv3 --kernel-trace --stats of bench.py: encoder workload (B=2, Nq=Nv=22223,",
+             "# M=8, D=32, L=4, K=4, fp32), forward and backward (its grad_attn/grad_loc kernel on",
+             "# a side stream, concurrent with the grad_value kernels); kernel source sha " +
+             source_sha(),
              "# command: " + commands["stats"], "",
              f"{'kernel':46s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}"]
     for r in stats:

@@ -11,9 +11,10 @@ import torch
 from ._binding import (BWD_STAGES, EXPORTED, LIB_PATH, MSDA_BF16, MSDA_BWD_ACCUMULATE, MSDA_ERR_DTYPE,
                        MSDA_ERR_HIP, MSDA_ERR_NULL, MSDA_ERR_SHAPE, MSDA_ERR_UNSUPPORTED,
                        MSDA_ERR_WORKSPACE, MSDA_F32, MSDA_OK, MSDAError, backward, forward, load,
-                       status_string, validate_host, workspace_size)
+                       make_events, stage_times, status_string, validate_host, workspace_size)
 
-__all__ = ["forward", "backward", "BWD_STAGES", "workspace_size", "validate_host", "status_string", "load",
+__all__ = ["forward", "backward", "BWD_STAGES", "make_events", "stage_times", "workspace_size",
+           "validate_host", "status_string", "load",
            "MSDAError",
            "ms_deform_attn", "MSDeformAttnFunction", "LIB_PATH", "EXPORTED"]
 

@@ -28,7 +28,7 @@ MSDA_BF16 = 1
 MSDA_BWD_ACCUMULATE = 1
 
 EXPORTED = ("msda_forward", "msda_backward_workspace_size", "msda_backward",
-            "msda_backward_timed", "msda_validate_host", "msda_status_string",
+            "msda_backward_events", "msda_validate_host", "msda_status_string",
             "msda_last_hip_error")
 BWD_STAGES = ("fill_grad_value", "dots", "clear_bins", "count", "scan", "scatter", "tiles")
 
@@ -59,9 +59,9 @@ def load():
     lib.msda_backward.argtypes = ([p, ci, p, p, p, p, p, p, p, p] + [i64] * 7 +
                                   [p, ctypes.c_size_t, u32, p])
     lib.msda_backward.restype = ci
-    lib.msda_backward_timed.argtypes = ([p, ci, p, p, p, p, p, p, p, p] + [i64] * 7 +
-                                        [p, ctypes.c_size_t, u32, p, p])
-    lib.msda_backward_timed.restype = ci
+    lib.msda_backward_events.argtypes = ([p, ci, p, p, p, p, p, p, p, p] + [i64] * 7 +
+                                         [p, ctypes.c_size_t, u32, p, p])
+    lib.msda_backward_events.restype = ci
     lib.msda_backward_workspace_size.argtypes = [i64] * 7
     lib.msda_backward_workspace_size.restype = ctypes.c_size_t
     lib.msda_validate_host.argtypes = [p, p] + [i64] * 7
@@ -185,13 +185,28 @@ def forward(value: torch.Tensor, spatial_shapes: torch.Tensor, level_start_index
     return out
 
 
+def stage_times(events: list) -> list:
+    """Durations in us of the backward stages recorded by backward(events=...),
+    in the order of BWD_STAGES; call after the stream has been synchronized."""
+    return [1000.0 * events[2 * i].elapsed_time(events[2 * i + 1])
+            if events[2 * i] is not None else None for i in range(len(BWD_STAGES))]
+
+
+def make_events(stage: Optional[str] = None) -> list:
+    """A fresh set of timing events for backward(events=...): for every stage,
+    or only for the named one (None in the other places)."""
+    return [torch.cuda.Event(enable_timing=True)
+            if stage is None or BWD_STAGES[i // 2] == stage else None
+            for i in range(2 * len(BWD_STAGES))]
+
+
 def backward(value: torch.Tensor, spatial_shapes: torch.Tensor, level_start_index: torch.Tensor,
              sampling_loc: torch.Tensor, attn_weight: torch.Tensor, grad_out: torch.Tensor,
              grad_value: Optional[torch.Tensor] = None,
              grad_sampling_loc: Optional[torch.Tensor] = None,
              grad_attn_weight: Optional[torch.Tensor] = None,
              accumulate: bool = False, validate: bool = True,
-             workspace: Optional[torch.Tensor] = None, stage_us: Optional[list] = None
+             workspace: Optional[torch.Tensor] = None, events: Optional[list] = None
              ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """msda_backward: (grad_value fp32 [B,Nv,M,D], grad_sampling_loc, grad_attn_weight).
 
@@ -199,9 +214,9 @@ def backward(value: torch.Tensor, spatial_shapes: torch.Tensor, level_start_inde
     workspace: a uint8 device tensor of at least workspace_size(...) bytes; by
     default a per-device buffer cached by this module is used (calls on
     different streams that overlap in time must pass their own).
-    stage_us: if a list is given, msda_backward_timed is called instead (it
-    synchronizes) and the list receives the per-stage durations in us, in the
-    order of BWD_STAGES."""
+    events: 2 * len(BWD_STAGES) torch.cuda.Event(enable_timing=True) objects
+    or None; if given, msda_backward_events is called instead, which records
+    events 2i and 2i + 1 around stage i (see stage_times), skipping None."""
     lib = load()
     dev, (B, Nv, Nq, M, D, L, K) = _check_inputs(value, spatial_shapes, level_start_index,
                                                 sampling_loc, attn_weight, validate)
@@ -233,14 +248,19 @@ def backward(value: torch.Tensor, spatial_shapes: torch.Tensor, level_start_inde
             _ptr(workspace), ws_bytes, flags]
     with torch.cuda.device(dev):
         stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-        if stage_us is None:
+        if events is None:
             rc = lib.msda_backward(*args, stream)
             where = "msda_backward"
         else:
-            times = (ctypes.c_float * len(BWD_STAGES))()
-            rc = lib.msda_backward_timed(*args, stream, times)
-            where = "msda_backward_timed"
-            stage_us[:] = list(times)
+            if len(events) != 2 * len(BWD_STAGES):
+                raise ValueError(f"events: {2 * len(BWD_STAGES)} torch.cuda.Event expected")
+            for e in events:
+                if e is not None and not e.cuda_event:  # torch creates it at its first record
+                    e.record()
+            handles = (ctypes.c_void_p * len(events))(
+                *[e.cuda_event if e is not None else None for e in events])
+            rc = lib.msda_backward_events(*args, stream, handles)
+            where = "msda_backward_events"
     if rc != MSDA_OK:
         raise MSDAError(rc, where)
     return grad_value, grad_sampling_loc, grad_attn_weight

@@ -1150,8 +1150,12 @@ struct Exec {
     hipStream_t s;
     hipStream_t side;
     hipEvent_t fork, filled, join;  // fork from s; grad_value zeroed; side work done
-    hipEvent_t *ev;
+    hipEvent_t *ev;                 // optional: 2 * MSDA_BWD_STAGES caller events (start, end)
     bool fill_on_side;              // the grad_value zero-fill was enqueued on `side`
+    // record the start (end = false) or end event of stage i on stream `on`
+    void stamp(int i, bool end, hipStream_t on) const {
+        if (ev && ev[2 * i + (end ? 1 : 0)]) (void)hipEventRecord(ev[2 * i + (end ? 1 : 0)], on);
+    }
 };
 
 // One side stream per device, created on first use (default priority,
@@ -1198,11 +1202,6 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
                        int64_t L, int64_t K, const WorkLayout &wl, unsigned char *ws,
                        bool accumulate, const Exec &ex) {
     const hipStream_t s = ex.s;
-    hipEvent_t *ev = ex.ev;
-    // ev (optional): events recorded before each stage, for msda_backward_timed
-    auto mark = [&](int i) {
-        if (ev) (void)hipEventRecord(ev[i], s);
-    };
     Work w;
     w.counts = reinterpret_cast<uint32_t *>(ws + wl.off_counts);
     w.start = reinterpret_cast<uint32_t *>(ws + wl.off_start);
@@ -1227,7 +1226,7 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
         }
         return MSDA_OK;
     };
-    mark(1);
+    ex.stamp(1, false, ds);
     msda_status st = per_batch(gq * M, [&](int64_t b0, unsigned grid) {
         Dims d2{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, p.pc, p.ps, (int)b0, (int)gq, 0, 0};
         d2.nblocks = (int)grid;
@@ -1239,21 +1238,23 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
                            gattn, d2);
     });
     if (st != MSDA_OK) return st;
+    ex.stamp(1, true, ds);
     if (ex.side) {
         st = hip_status(hipEventRecord(ex.join, ex.side));
         if (st != MSDA_OK) return st;
     }
 
     // the counts region is padded to 256 bytes, so whole float4s can be cleared
-    mark(2);
+    ex.stamp(2, false, s);
     st = fill_zero(w.counts, (wl.off_start - wl.off_counts) / 16, s);
     if (st != MSDA_OK) return st;
+    ex.stamp(2, true, s);
 
     const int hist_cap = (int)(wl.nb_max < kHistLds ? wl.nb_max : kHistLds);
     const int64_t gb = (Nq * L * K + kBinPoints - 1) / kBinPoints;  // per (batch, head)
     Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, 0, 0, 0, (int)gb, (int)wl.nb_max,
             accumulate ? 1 : 0, make_fastdiv((uint32_t)(L * K)), make_fastdiv((uint32_t)K)};
-    mark(3);
+    ex.stamp(3, false, s);
     st = per_batch(gb * M, [&](int64_t b0, unsigned grid) {
         Dims d2 = dm;
         d2.b0 = (int)b0;
@@ -1261,14 +1262,16 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
                            shapes, starts, loc, w.counts, hist_cap, d2);
     });
     if (st != MSDA_OK) return st;
+    ex.stamp(3, true, s);
 
-    mark(4);
+    ex.stamp(4, false, s);
     hipLaunchKernelGGL(bin_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, shapes, starts,
                        w.counts, w.start, w.cursor, w.items, w.work_total, (int)B, dm);
     st = hip_status(hipGetLastError());
     if (st != MSDA_OK) return st;
+    ex.stamp(4, true, s);
 
-    mark(5);
+    ex.stamp(5, false, s);
     st = per_batch(gb * M, [&](int64_t b0, unsigned grid) {
         Dims d2 = dm;
         d2.b0 = (int)b0;
@@ -1276,18 +1279,19 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
                            s, shapes, starts, loc, attn, w.cursor, w.recs, hist_cap, d2);
     });
     if (st != MSDA_OK) return st;
+    ex.stamp(5, true, s);
 
     const int64_t grid = wl.work_max < kTileGrid ? wl.work_max : kTileGrid;
     if (ex.fill_on_side) {
         st = hip_status(hipStreamWaitEvent(s, ex.filled, 0));
         if (st != MSDA_OK) return st;
     }
-    mark(6);
+    ex.stamp(6, false, s);
     hipLaunchKernelGGL((grad_value_tile_kernel<D>), dim3((unsigned)grid), dim3(kTileThreads), 0, s,
                        shapes, starts, gout, w.items, w.work_total, w.recs, gval, dm);
     st = hip_status(hipGetLastError());
+    ex.stamp(6, true, s);
     if (st == MSDA_OK && ex.side) st = hip_status(hipStreamWaitEvent(s, ex.join, 0));
-    mark(7);
     return st;
 }
 
@@ -1397,11 +1401,9 @@ msda_status backward_impl(const void *value, int value_dtype, const int64_t *spa
         if (workspace_bytes < wl.bytes) return MSDA_ERR_WORKSPACE;
         if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return MSDA_ERR_WORKSPACE;
     }
-    // The timed variant stays on the caller's stream, so that its stage
-    // times are those of one kernel each.
     Exec ex{s, nullptr, nullptr, nullptr, nullptr, ev, false};
     std::unique_lock<std::mutex> lock(g_side_mu, std::defer_lock);
-    if (work && !ev) {
+    if (work) {
         lock.lock();
         if (SideStream *ss = side_stream()) {
             ex.side = ss->s;
@@ -1410,7 +1412,6 @@ msda_status backward_impl(const void *value, int value_dtype, const int64_t *spa
             ex.join = ss->join;
         }
     }
-    if (ev) (void)hipEventRecord(ev[0], s);
     if (ex.side) {
         st = hip_status(hipEventRecord(ex.fork, s));
         if (st == MSDA_OK) st = hip_status(hipStreamWaitEvent(ex.side, ex.fork, 0));
@@ -1419,16 +1420,25 @@ msda_status backward_impl(const void *value, int value_dtype, const int64_t *spa
     if (!(flags & MSDA_BWD_ACCUMULATE)) {
         // with a side stream the fill runs there, ahead of the dots kernel, and
         // the tile kernel waits for it
-        st = fill_zero(grad_value, (size_t)nval / 4, ex.side ? ex.side : s);  // D % 4 == 0
+        const hipStream_t fs = ex.side ? ex.side : s;
+        ex.stamp(0, false, fs);
+        st = fill_zero(grad_value, (size_t)nval / 4, fs);  // D % 4 == 0
+        ex.stamp(0, true, fs);
         if (st == MSDA_OK && ex.side) {
             st = hip_status(hipEventRecord(ex.filled, ex.side));
             ex.fill_on_side = true;
         }
         if (st != MSDA_OK) return st;
     }
+    if (flags & MSDA_BWD_ACCUMULATE) {  // no fill: an empty stage
+        ex.stamp(0, false, s);
+        ex.stamp(0, true, s);
+    }
     if (!work) {
-        if (ev)
-            for (int i = 1; i <= MSDA_BWD_STAGES; ++i) (void)hipEventRecord(ev[i], s);
+        for (int i = 1; i < MSDA_BWD_STAGES; ++i) {
+            ex.stamp(i, false, s);
+            ex.stamp(i, true, s);
+        }
         return MSDA_OK;
     }
     unsigned char *ws = static_cast<unsigned char *>(workspace);
@@ -1459,37 +1469,21 @@ msda_status msda_backward(const void *value, int value_dtype, const int64_t *spa
                          static_cast<hipStream_t>(stream), nullptr);
 }
 
-msda_status msda_backward_timed(const void *value, int value_dtype,
-                                const int64_t *spatial_shapes, const int64_t *level_start_index,
-                                const float *sampling_loc, const float *attn_weight,
-                                const float *grad_out, float *grad_value,
-                                float *grad_sampling_loc, float *grad_attn_weight, int64_t B,
-                                int64_t Nv, int64_t Nq, int64_t M, int64_t D, int64_t L,
-                                int64_t K, void *workspace, size_t workspace_bytes,
-                                uint32_t flags, void *stream, float *stage_us) {
-    if (!stage_us) return MSDA_ERR_NULL;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipEvent_t ev[MSDA_BWD_STAGES + 1];
-    int made = 0;
-    msda_status st = MSDA_OK;
-    for (; made < MSDA_BWD_STAGES + 1; ++made) {
-        st = hip_status(hipEventCreate(&ev[made]));
-        if (st != MSDA_OK) break;
-    }
-    if (st == MSDA_OK) {
-        st = backward_impl(value, value_dtype, spatial_shapes, level_start_index, sampling_loc,
-                           attn_weight, grad_out, grad_value, grad_sampling_loc,
-                           grad_attn_weight, B, Nv, Nq, M, D, L, K, workspace, workspace_bytes,
-                           flags, s, ev);
-        if (st == MSDA_OK) st = hip_status(hipEventSynchronize(ev[MSDA_BWD_STAGES]));
-        for (int i = 0; i < MSDA_BWD_STAGES && st == MSDA_OK; ++i) {
-            float ms = 0.f;
-            st = hip_status(hipEventElapsedTime(&ms, ev[i], ev[i + 1]));
-            stage_us[i] = 1000.f * ms;
-        }
-    }
-    for (int i = 0; i < made; ++i) (void)hipEventDestroy(ev[i]);
-    return st;
+msda_status msda_backward_events(const void *value, int value_dtype,
+                                 const int64_t *spatial_shapes, const int64_t *level_start_index,
+                                 const float *sampling_loc, const float *attn_weight,
+                                 const float *grad_out, float *grad_value,
+                                 float *grad_sampling_loc, float *grad_attn_weight, int64_t B,
+                                 int64_t Nv, int64_t Nq, int64_t M, int64_t D, int64_t L,
+                                 int64_t K, void *workspace, size_t workspace_bytes,
+                                 uint32_t flags, void *stream, void *const *events) {
+    if (!events) return MSDA_ERR_NULL;
+    hipEvent_t ev[2 * MSDA_BWD_STAGES];
+    for (int i = 0; i < 2 * MSDA_BWD_STAGES; ++i) ev[i] = static_cast<hipEvent_t>(events[i]);
+    return backward_impl(value, value_dtype, spatial_shapes, level_start_index, sampling_loc,
+                         attn_weight, grad_out, grad_value, grad_sampling_loc, grad_attn_weight,
+                         B, Nv, Nq, M, D, L, K, workspace, workspace_bytes, flags,
+                         static_cast<hipStream_t>(stream), ev);
 }
 
 msda_status msda_validate_host(const int64_t *spatial_shapes_host, const int64_t *level_start_host,

@@ -311,16 +311,23 @@ def test_backward_repeatability(msda):
         assert torch.equal(r[1], ref[1]) and torch.equal(r[2], ref[2])
 
 
-def test_timed_backward_matches_and_reports_stages(msda):
-    """msda_backward_timed gives the same gradients and a duration per stage."""
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_backward_with_stage_events(msda, accumulate):
+    """msda_backward_events gives the same gradients as the oracle and records a
+    start and an end event around every stage (empty fill stage when
+    accumulating)."""
     w = workloads.random_case(900, 2, ((9, 13), (5, 7)), 70, 4, 32, 4)
     x = dev_inputs(w)
     g = torch.from_numpy(w.grad_out).cuda()
-    _say("timed backward")
-    st = []
-    gv, gl, ga = msda.backward(**x, grad_out=g, stage_us=st)
-    assert len(st) == len(msda.BWD_STAGES) and all(t >= 0.0 for t in st) and sum(st) > 0.0
+    _say(f"backward with stage events, accumulate={accumulate}")
+    ev = msda.make_events()
+    gv0 = torch.zeros(x["value"].shape, device="cuda") if accumulate else None
+    gv, gl, ga = msda.backward(**x, grad_out=g, grad_value=gv0, accumulate=accumulate, events=ev)
+    torch.cuda.synchronize()
+    st = msda.stage_times(ev)
+    assert len(st) == len(msda.BWD_STAGES) and all(t >= 0.0 for t in st)
+    assert st[msda.BWD_STAGES.index("tiles")] > 0.0 and st[msda.BWD_STAGES.index("dots")] > 0.0
     rv, rl, ra = oracle_bwd(w)
-    close(gv.cpu().numpy(), rv, BWD_TOL)
-    close(gl.cpu().numpy(), rl, BWD_TOL)
-    close(ga.cpu().numpy(), ra, BWD_TOL)
+    close(gv.cpu().numpy(), rv, BWD_TOL, "grad_value")
+    close(gl.cpu().numpy(), rl, BWD_TOL, "grad_sampling_loc")
+    close(ga.cpu().numpy(), ra, BWD_TOL, "grad_attn_weight")
