@@ -25,6 +25,7 @@ _default = None
 
 SPEC = 0    # fp32 coordinate transform (fmaf + floorf), as the GPU library does
 DOUBLE = 1  # every coordinate step in fp64
+ALIGN = 2   # flag: x = u*(W-1), y = v*(H-1) (align_corners=True); combine with SPEC/DOUBLE
 
 
 def build(verbose: bool = False, src: str = _SRC, out: str = _LIB_PATH) -> str:

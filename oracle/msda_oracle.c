@@ -20,7 +20,8 @@
  *    times the tent weight max(0, 1-|x-xi|) * max(0, 1-|y-yi|); a neighbour
  *    outside the feature map contributes zero.
  *  - same page, sections 2.3 and 3.2 (the grid_sample module with
- *    align_corners=False): a normalized coordinate u in [0,1] maps to the
+ *    align_corners=False, the default convention here): a normalized
+ *    coordinate u in [0,1] maps to the
  *    pixel coordinate u*W - 0.5 along the width (W) and v*H - 0.5 along the
  *    height (H); the last axis of a location is (x, y); each row of the
  *    level table is (H, W); the head outputs are concatenated head-major.
@@ -33,11 +34,18 @@
  * the left neighbour x0 and +1 for the right neighbour x0+1 inside the cell
  * [x0, x0+1), and d x / d u = W, d y / d v = H.
  *
- * Coordinate modes
- *   mode 0 ("spec"):   x = fmaf(u, (float)W, -0.5f), x0 = floorf(x), in fp32 with
- *                      one rounding, as the GPU library does; everything after
- *                      the floor is fp64.
- *   mode 1 ("double"): every coordinate step in fp64 (for finite differences).
+ * Coordinate modes (bit flags)
+ *   bit 0 clear ("spec"): x = fmaf(u, (float)W, -0.5f), x0 = floorf(x), in fp32
+ *                      with one rounding, as the GPU library does; everything
+ *                      after the floor is fp64.
+ *   bit 0 set ("double"): every coordinate step in fp64 (for finite differences).
+ *   bit 1 ("align corners"): the other pixel convention, x = u*(W-1) and
+ *                      y = v*(H-1) (grid_sample with align_corners=True): the
+ *                      first page, section 2.3, advises making align_corners and
+ *                      the coordinate scale a configuration option, and its
+ *                      section 6 notes that some inference engines default to
+ *                      True.  In spec mode the product is one fp32 multiply;
+ *                      d x / d u = W-1 and d y / d v = H-1.
  * Accumulation is always fp64, in the order l, k, neighbour.
  *
  * Non-finite coordinates: every neighbour test fails, so such a point
@@ -70,16 +78,26 @@ typedef struct {
     double dwx, dwy;  /* d wx / d x and d wy / d y                         */
 } neighbour;
 
+#define MODE_DOUBLE 1
+#define MODE_ALIGN 2
+
+/* d x / d u on an axis of n pixels */
+static double pixel_scale(int64_t n, int mode)
+{
+    return (mode & MODE_ALIGN) ? (double)(n - 1) : (double)n;
+}
+
 /* Pixel coordinate of a normalized coordinate u on an axis of n pixels,
  * floored; *px receives the continuous coordinate. */
 static double pixel_coord(float u, int64_t n, int mode, double *px)
 {
-    if (mode == 0) {
-        float p = fmaf(u, (float)n, -0.5f);
+    if (!(mode & MODE_DOUBLE)) {
+        float p = (mode & MODE_ALIGN) ? u * (float)(n - 1) : fmaf(u, (float)n, -0.5f);
         *px = (double)p;
         return (double)floorf(p);
     }
-    double p = (double)u * (double)n - 0.5;
+    double p = (mode & MODE_ALIGN) ? (double)u * (double)(n - 1)
+                                   : (double)u * (double)n - 0.5;
     *px = p;
     return floor(p);
 }
@@ -209,8 +227,8 @@ int oracle_backward(const float *value, const int64_t *shapes, const int64_t *st
                             for (int64_t d = 0; d < D; ++d) gvr[d] += s * (double)g[d];
                         }
                         grad_attn[pt] = gA;
-                        grad_loc[2 * pt] = A * gx * (double)W;
-                        grad_loc[2 * pt + 1] = A * gy * (double)H;
+                        grad_loc[2 * pt] = A * gx * pixel_scale(W, mode);
+                        grad_loc[2 * pt + 1] = A * gy * pixel_scale(H, mode);
                     }
                 }
             }

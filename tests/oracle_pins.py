@@ -50,7 +50,7 @@ def max_rel(x, r) -> float:
 # to: first page, section 3.2 -- grid = 2*loc - 1, bilinear, zero padding,
 # align_corners=False, heads folded into the batch).
 # ----------------------------------------------------------------------------
-def grid_sample_core(value, shapes, start, loc, attn):
+def grid_sample_core(value, shapes, start, loc, attn, align_corners=False):
     """Torch CPU composition; tensors in, out [B, Nq, M*D] (keeps autograd)."""
     B, Nv, M, D = value.shape
     _, Nq, _, L, K, _ = loc.shape
@@ -62,18 +62,18 @@ def grid_sample_core(value, shapes, start, loc, attn):
         v_l = v_l.reshape(B * M, D, H, W)
         grid = (2.0 * loc[:, :, :, l] - 1.0).permute(0, 2, 1, 3, 4).reshape(B * M, Nq, K, 2)
         smp = F.grid_sample(v_l, grid, mode="bilinear", padding_mode="zeros",
-                            align_corners=False)               # [B*M, D, Nq, K]
+                            align_corners=align_corners)       # [B*M, D, Nq, K]
         a = attn[:, :, :, l].permute(0, 2, 1, 3).reshape(B * M, 1, Nq, K)
         out = out + (smp * a).sum(-1)
     return out.reshape(B, M, D, Nq).permute(0, 3, 1, 2).reshape(B, Nq, M * D)
 
 
-def torch_reference(w: workloads.Workload):
+def torch_reference(w: workloads.Workload, align_corners=False):
     """fp64 forward + autograd grads of the grid_sample composition."""
     v = torch.tensor(w.value, dtype=torch.float64, requires_grad=True)
     lc = torch.tensor(w.sampling_loc, dtype=torch.float64, requires_grad=True)
     a = torch.tensor(w.attn_weight, dtype=torch.float64, requires_grad=True)
-    out = grid_sample_core(v, w.spatial_shapes, w.level_start_index, lc, a)
+    out = grid_sample_core(v, w.spatial_shapes, w.level_start_index, lc, a, align_corners)
     g = torch.tensor(w.grad_out, dtype=torch.float64).reshape(out.shape)
     out.backward(g)
     return (out.detach().numpy(), v.grad.numpy(), lc.grad.numpy(), a.grad.numpy())
@@ -384,6 +384,94 @@ def pin_linearity(orc):
     assert max_rel(f3, 2.0 * f1) < 1e-15
 
 
+# ----------------------------------------------------------------------------
+# The other pixel convention, x = u*(W-1) (grid_sample align_corners=True),
+# which the first page, section 2.3, advises offering as a configuration.
+# ----------------------------------------------------------------------------
+def pin_align_corners_grid_sample(orc):
+    """In align-corners mode the forward and all three gradients equal the
+    grid_sample composition with align_corners=True (torch CPU, fp64),
+    including maps one pixel wide or tall and points beyond the border."""
+    cases = [workloads.random_case(61, 2, ((5, 7), (3, 4), (2, 1)), 9, 3, 4, 3),
+             workloads.random_case(62, 1, ((6, 6),), 7, 1, 2, 5, -0.6, 1.6),
+             workloads.random_case(63, 2, ((1, 9), (4, 1)), 5, 2, 3, 2)]
+    mode = oracle.DOUBLE | oracle.ALIGN
+    for w in cases:
+        out, gv, gl, ga = torch_reference(w, align_corners=True)
+        o = _fwd(orc, w, mode=mode)
+        assert max_rel(o, out) < 1e-12, f"align forward vs grid_sample on {w.name}"
+        v, l_, a = _bwd(orc, w, mode=mode)
+        assert max_rel(v, gv) < 1e-12, f"align grad_value vs autograd on {w.name}"
+        assert max_rel(l_, gl) < 1e-9, f"align grad_loc vs autograd on {w.name}"
+        assert max_rel(a, ga) < 1e-12, f"align grad_attn vs autograd on {w.name}"
+
+
+def pin_align_corner_pixels(orc):
+    """In align-corners mode the location (j/(W-1), i/(H-1)) is pixel (i, j)
+    itself: the sample is value[i, j] (exactly in fp64; within 1e-6 in the fp32
+    spec mode, whose product can land just below the integer).  Along an axis
+    of one pixel every location maps to that pixel."""
+    w = workloads.random_case(71, 2, ((5, 7), (3, 2), (1, 4), (6, 1)), 12, 3, 8, 2)
+    B, Nq, M, L, K = w.attn_weight.shape
+    rng = np.random.Generator(np.random.PCG64(6))
+    loc = w.sampling_loc.copy()
+    attn = np.zeros_like(w.attn_weight)
+    expect = np.zeros((B, Nq, M, 8))
+    for b in range(B):
+        for q in range(Nq):
+            for m in range(M):
+                l = int(rng.integers(L))
+                k = int(rng.integers(K))
+                H, W = w.spatial_shapes[l]
+                i, j = int(rng.integers(H)), int(rng.integers(W))
+                u = j / (W - 1) if W > 1 else float(rng.uniform(0, 1))
+                v = i / (H - 1) if H > 1 else float(rng.uniform(0, 1))
+                loc[b, q, m, l, k] = (np.float32(u), np.float32(v))
+                attn[b, q, m, l, k] = 1.0
+                expect[b, q, m] = w.value[b, w.level_start_index[l] + i * W + j, m]
+    for mode, tol in ((oracle.DOUBLE | oracle.ALIGN, 1e-6), (oracle.SPEC | oracle.ALIGN, 1e-6)):
+        got = _fwd(orc, w, mode=mode, sampling_loc=loc, attn_weight=attn).reshape(B, Nq, M, 8)
+        err = float(np.max(np.abs(got - expect)))
+        assert err <= tol, f"align-corners pixel sample off by {err} (mode {mode})"
+
+
+def pin_align_finite_differences(orc):
+    """Central differences of the fp64 align-corners forward match its
+    backward: d x / d u = W - 1 (points near a cell edge skipped)."""
+    w = workloads.random_case(81, 1, ((5, 6), (3, 4)), 6, 2, 4, 2, 0.05, 0.95)
+    mode = oracle.DOUBLE | oracle.ALIGN
+    _, gl, _ = _bwd(orc, w, mode=mode)
+    g = w.grad_out.astype(np.float64)
+
+    def obj(**over):
+        return float(np.sum(_fwd(orc, w, mode=mode, **over) * g))
+
+    B, Nq, M, L, K = w.attn_weight.shape
+    checked = 0
+    rng = np.random.Generator(np.random.PCG64(8))
+    for _ in range(40):
+        b, q, m, l, k = (int(rng.integers(n)) for n in (B, Nq, M, L, K))
+        H, W = w.spatial_shapes[l]
+        for c, n in ((0, W), (1, H)):
+            u = float(w.sampling_loc[b, q, m, l, k, c])
+            p = u * (n - 1)
+            h = 1e-3 / n
+            if abs(p - np.round(p)) < 4e-3:
+                continue
+            lp = w.sampling_loc.copy()
+            lm = w.sampling_loc.copy()
+            lp[b, q, m, l, k, c] = u + h
+            lm[b, q, m, l, k, c] = u - h
+            hh = float(lp[b, q, m, l, k, c]) - float(lm[b, q, m, l, k, c])
+            fd = (obj(sampling_loc=lp) - obj(sampling_loc=lm)) / hh
+            an = gl[b, q, m, l, k, c]
+            assert abs(fd - an) <= 1e-4 * max(1.0, abs(an)), f"align grad_loc fd {fd} vs {an}"
+            checked += 1
+    assert checked >= 20
+
+
 ALL_PINS = [pin_pixel_centres, pin_one_hot_grid_sample, pin_four_point_example,
             pin_zero_offsets, pin_finite_differences, pin_adjoint,
-            pin_partition_of_unity, pin_out_of_map, pin_nonfinite, pin_linearity]
+            pin_partition_of_unity, pin_out_of_map, pin_nonfinite, pin_linearity,
+            pin_align_corners_grid_sample, pin_align_corner_pixels,
+            pin_align_finite_differences]

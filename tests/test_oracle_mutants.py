@@ -19,7 +19,11 @@ MUTANTS = [
     ("dwx_sign", "n->dwx = (c & 1) ? 1.0 : -1.0;", "n->dwx = (c & 1) ? -1.0 : 1.0;", 1),
     ("dwy_sign", "n->dwy = (c >> 1) ? 1.0 : -1.0;", "n->dwy = (c >> 1) ? -1.0 : 1.0;", 1),
     ("pixel_index_transposed", "start + (int64_t)yi * W + (int64_t)xi", "start + (int64_t)xi * H + (int64_t)yi", 1),
-    ("grad_loc_scale_swapped", "grad_loc[2 * pt] = A * gx * (double)W;", "grad_loc[2 * pt] = A * gx * (double)H;", 1),
+    ("grad_loc_scale_swapped", "grad_loc[2 * pt] = A * gx * pixel_scale(W, mode);", "grad_loc[2 * pt] = A * gx * pixel_scale(H, mode);", 1),
+    ("align_scale_keeps_W", "return (mode & MODE_ALIGN) ? (double)(n - 1) : (double)n;", "return (double)n;", 1),
+    ("align_ignored_fp32", "(mode & MODE_ALIGN) ? u * (float)(n - 1) : fmaf", "0 ? u * (float)(n - 1) : fmaf", 1),
+    ("align_ignored_fp64", "double p = (mode & MODE_ALIGN) ? (double)u * (double)(n - 1)", "double p = 0 ? (double)u * (double)(n - 1)", 1),
+    ("align_with_half_pixel", "? u * (float)(n - 1) : fmaf", "? u * (float)(n - 1) - 0.5f : fmaf", 1),
     ("grad_value_without_A", "double s = A * w;", "double s = w;", 1),
     ("grad_attn_without_tent", "gA += w * gv;", "gA += gv;", 1),
     ("border_off_by_one", "(xi <= (double)(W - 1))", "(xi < (double)(W - 1))", 1),

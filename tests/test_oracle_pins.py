@@ -15,16 +15,18 @@ def test_pin(orc, pin):
     pin(orc)
 
 
-def test_spec_and_double_modes_agree(orc):
+@pytest.mark.parametrize("align", [0, oracle.ALIGN], ids=["half_pixel", "align_corners"])
+def test_spec_and_double_modes_agree(orc, align):
     """The fp32 coordinate transform and the fp64 one give the same forward
-    to ~1e-6 on the tiny config (their difference is coordinate rounding)."""
+    to ~1e-6 on the tiny config (their difference is coordinate rounding), in
+    either pixel convention."""
     import workloads
     from oracle_pins import max_rel
     w = workloads.make(0)
     a = orc.forward(w.value, w.spatial_shapes, w.level_start_index, w.sampling_loc,
-                    w.attn_weight, mode=oracle.SPEC)
+                    w.attn_weight, mode=oracle.SPEC | align)
     b = orc.forward(w.value, w.spatial_shapes, w.level_start_index, w.sampling_loc,
-                    w.attn_weight, mode=oracle.DOUBLE)
+                    w.attn_weight, mode=oracle.DOUBLE | align)
     assert max_rel(a, b) < 1e-6
 
 
