@@ -20,6 +20,14 @@
  * computed as one fp32 fused multiply-add and floored in fp32.  Locations
  * whose coordinates are not finite contribute zero.
  *
+ * Pixel convention.  With the flag MSDA_ALIGN_CORNERS (forward and backward
+ * alike) the pixel coordinates are instead x = u*(W_l - 1), y = v*(H_l - 1),
+ * one fp32 rounding of the product: grid_sample's align_corners=True, which
+ * the first page (section 2.3) advises offering as a configuration option
+ * because the two conventions differ by half a pixel, and which its section 6
+ * notes some inference engines use by default.  The location gradients then
+ * carry the factors W_l - 1 and H_l - 1 instead of W_l and H_l.
+ *
  * Layouts.  Every tensor is dense and row-major with no strides:
  *   value              [B, Nv, M, D]          fp32, or bf16 when value_dtype == MSDA_BF16
  *   spatial_shapes     [L, 2]  int64, rows (H_l, W_l)
@@ -35,8 +43,9 @@
  * Memory and ownership.  Every tensor pointer, spatial_shapes and
  * level_start_index included, is a DEVICE pointer on the current HIP device;
  * the caller allocates and owns all of them, and the backward's scratch
- * workspace too.  The library allocates nothing, frees nothing and keeps no
- * state between calls.  Outputs must not alias inputs.
+ * workspace too.  The library allocates no memory; its only state is the
+ * backward's side stream per device (see below).  Outputs must not alias
+ * inputs.
  *
  * Streams and errors.  `stream` is a hipStream_t (NULL = the null stream).
  * Work is enqueued on it and the call returns without synchronizing; a
@@ -85,18 +94,20 @@ typedef enum msda_dtype {
     MSDA_BF16 = 1              /* bfloat16 value only; all else fp32                  */
 } msda_dtype;
 
-/* Flags of msda_backward. */
-#define MSDA_BWD_ACCUMULATE 1u /* add into grad_value instead of overwriting it      */
+/* Flags (unknown bits give MSDA_ERR_UNSUPPORTED). */
+#define MSDA_BWD_ACCUMULATE 1u /* backward: add into grad_value instead of overwriting  */
+#define MSDA_ALIGN_CORNERS 2u  /* both: x = u*(W-1), y = v*(H-1) (align_corners=True)   */
 
 /*
  * Forward: out = MSDeformAttn core(value, level table, sampling_loc, attn_weight).
- * out is overwritten.  value_dtype is an msda_dtype.
+ * out is overwritten.  value_dtype is an msda_dtype; flags is 0 or
+ * MSDA_ALIGN_CORNERS.
  */
 msda_status msda_forward(const void *value, int value_dtype,
                          const int64_t *spatial_shapes, const int64_t *level_start_index,
                          const float *sampling_loc, const float *attn_weight, float *out,
                          int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
-                         int64_t L, int64_t K, void *stream);
+                         int64_t L, int64_t K, uint32_t flags, void *stream);
 
 /*
  * Bytes of device workspace msda_backward needs for these sizes (0 when
@@ -126,7 +137,8 @@ size_t msda_backward_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int64_t M
  * matter and are clobbered.  Calls that overlap in time (other streams) need
  * separate workspaces.
  *
- * grad_value is overwritten (zero-filled first, on `stream`) unless flags has
+ * flags: MSDA_BWD_ACCUMULATE and/or MSDA_ALIGN_CORNERS (the latter as given to
+ * the forward).  grad_value is overwritten (zero-filled first) unless flags has
  * MSDA_BWD_ACCUMULATE, in which case the gradient is added to it.  Its
  * summation order is not fixed, so repeated calls may differ in the last
  * bits.  grad_sampling_loc and grad_attn_weight are overwritten and

@@ -8,7 +8,8 @@ from __future__ import annotations
 
 import torch
 
-from ._binding import (BWD_STAGES, EXPORTED, LIB_PATH, MSDA_BF16, MSDA_BWD_ACCUMULATE, MSDA_ERR_DTYPE,
+from ._binding import (BWD_STAGES, EXPORTED, LIB_PATH, MSDA_ALIGN_CORNERS, MSDA_BF16,
+                       MSDA_BWD_ACCUMULATE, MSDA_ERR_DTYPE,
                        MSDA_ERR_HIP, MSDA_ERR_NULL, MSDA_ERR_SHAPE, MSDA_ERR_UNSUPPORTED,
                        MSDA_ERR_WORKSPACE, MSDA_F32, MSDA_OK, MSDAError, backward, forward, load,
                        make_events, stage_times, status_string, validate_host, workspace_size)
@@ -25,19 +26,24 @@ class MSDeformAttnFunction(torch.autograd.Function):
     value's dtype."""
 
     @staticmethod
-    def forward(ctx, value, spatial_shapes, level_start_index, sampling_loc, attn_weight):
-        out = forward(value, spatial_shapes, level_start_index, sampling_loc, attn_weight)
+    def forward(ctx, value, spatial_shapes, level_start_index, sampling_loc, attn_weight,
+                align_corners=False):
+        out = forward(value, spatial_shapes, level_start_index, sampling_loc, attn_weight,
+                      align_corners=align_corners)
         ctx.save_for_backward(value, spatial_shapes, level_start_index, sampling_loc,
                               attn_weight)
+        ctx.align_corners = align_corners
         return out
 
     @staticmethod
     def backward(ctx, grad_out):
         value, ss, st, loc, attn = ctx.saved_tensors
-        gv, gl, ga = backward(value, ss, st, loc, attn, grad_out.contiguous(), validate=False)
-        return gv, None, None, gl, ga
+        gv, gl, ga = backward(value, ss, st, loc, attn, grad_out.contiguous(), validate=False,
+                              align_corners=ctx.align_corners)
+        return gv, None, None, gl, ga, None
 
 
-def ms_deform_attn(value, spatial_shapes, level_start_index, sampling_loc, attn_weight):
+def ms_deform_attn(value, spatial_shapes, level_start_index, sampling_loc, attn_weight,
+                   align_corners=False):
     return MSDeformAttnFunction.apply(value, spatial_shapes, level_start_index, sampling_loc,
-                                      attn_weight)
+                                      attn_weight, align_corners)

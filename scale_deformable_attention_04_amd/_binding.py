@@ -26,6 +26,7 @@ MSDA_ERR_WORKSPACE = -6
 MSDA_F32 = 0
 MSDA_BF16 = 1
 MSDA_BWD_ACCUMULATE = 1
+MSDA_ALIGN_CORNERS = 2
 
 EXPORTED = ("msda_forward", "msda_backward_workspace_size", "msda_backward",
             "msda_backward_events", "msda_validate_host", "msda_status_string",
@@ -54,7 +55,7 @@ def load():
                            "`python -m scale_deformable_attention_04_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)
     p, i64, ci, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32
-    lib.msda_forward.argtypes = [p, ci, p, p, p, p, p] + [i64] * 7 + [p]
+    lib.msda_forward.argtypes = [p, ci, p, p, p, p, p] + [i64] * 7 + [u32, p]
     lib.msda_forward.restype = ci
     lib.msda_backward.argtypes = ([p, ci, p, p, p, p, p, p, p, p] + [i64] * 7 +
                                   [p, ctypes.c_size_t, u32, p])
@@ -163,11 +164,13 @@ def _check_inputs(value, spatial_shapes, level_start_index, sampling_loc, attn_w
 
 def forward(value: torch.Tensor, spatial_shapes: torch.Tensor, level_start_index: torch.Tensor,
             sampling_loc: torch.Tensor, attn_weight: torch.Tensor,
-            out: Optional[torch.Tensor] = None, validate: bool = True) -> torch.Tensor:
+            out: Optional[torch.Tensor] = None, validate: bool = True,
+            align_corners: bool = False) -> torch.Tensor:
     """msda_forward: out[B, Nq, M*D] (fp32) on torch's current stream.
 
     validate=True copies the level table to the host (one synchronization) and
-    checks it with msda_validate_host; pass False when it is known good."""
+    checks it with msda_validate_host; pass False when it is known good.
+    align_corners=True selects the pixel convention x = u*(W-1), y = v*(H-1)."""
     lib = load()
     dev, (B, Nv, Nq, M, D, L, K) = _check_inputs(value, spatial_shapes, level_start_index,
                                                 sampling_loc, attn_weight, validate)
@@ -179,7 +182,9 @@ def forward(value: torch.Tensor, spatial_shapes: torch.Tensor, level_start_index
         stream = torch.cuda.current_stream(dev).cuda_stream
         rc = lib.msda_forward(_ptr(value), _dtype_code(value), _ptr(spatial_shapes),
                               _ptr(level_start_index), _ptr(sampling_loc), _ptr(attn_weight),
-                              _ptr(out), B, Nv, Nq, M, D, L, K, ctypes.c_void_p(stream))
+                              _ptr(out), B, Nv, Nq, M, D, L, K,
+                              MSDA_ALIGN_CORNERS if align_corners else 0,
+                              ctypes.c_void_p(stream))
     if rc != MSDA_OK:
         raise MSDAError(rc, "msda_forward")
     return out
@@ -206,11 +211,13 @@ def backward(value: torch.Tensor, spatial_shapes: torch.Tensor, level_start_inde
              grad_sampling_loc: Optional[torch.Tensor] = None,
              grad_attn_weight: Optional[torch.Tensor] = None,
              accumulate: bool = False, validate: bool = True,
-             workspace: Optional[torch.Tensor] = None, events: Optional[list] = None
+             workspace: Optional[torch.Tensor] = None, events: Optional[list] = None,
+             align_corners: bool = False
              ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """msda_backward: (grad_value fp32 [B,Nv,M,D], grad_sampling_loc, grad_attn_weight).
 
     accumulate=True adds into the given grad_value instead of overwriting it.
+    align_corners must be the value given to the forward.
     workspace: a uint8 device tensor of at least workspace_size(...) bytes; by
     default a per-device buffer cached by this module is used (calls on
     different streams that overlap in time must pass their own).
@@ -235,7 +242,7 @@ def backward(value: torch.Tensor, spatial_shapes: torch.Tensor, level_start_inde
         grad_attn_weight = torch.empty_like(attn_weight)
     else:
         _need(grad_attn_weight, "grad_attn_weight", torch.float32, dev, attn_weight.shape)
-    flags = MSDA_BWD_ACCUMULATE if accumulate else 0
+    flags = (MSDA_BWD_ACCUMULATE if accumulate else 0) | (MSDA_ALIGN_CORNERS if align_corners else 0)
     need = workspace_size(B, Nv, Nq, M, D, L, K)
     if workspace is None:
         workspace = _workspace(dev, need)

@@ -184,13 +184,21 @@ __device__ __forceinline__ float4 tent_weights(float fx, float fy, uint32_t vali
                        (valid & 4u) ? gx * fy : 0.f, (valid & 8u) ? fx * fy : 0.f);
 }
 
+// Pixel scale d x / d u along an axis of n pixels: n (x = u*n - 0.5, the
+// default convention) or n - 1 (x = u*(n - 1), align_corners).
+__device__ __forceinline__ float pixel_scale(int n, bool align) {
+    return align ? (float)(n - 1) : (float)n;
+}
+
 __device__ __forceinline__ Neighbours neighbours(float u, float v, int4 lvl, uint32_t row_stride,
-                                                 uint32_t head_off) {
+                                                 uint32_t head_off, bool align) {
     const int H = lvl.x, W = lvl.y, S = lvl.z;
     Neighbours n;
-    // one rounding, the same as the CPU check: x = u*W - 0.5, y = v*H - 0.5
-    const float x = __builtin_fmaf(u, (float)W, -0.5f);
-    const float y = __builtin_fmaf(v, (float)H, -0.5f);
+    // one rounding, the same as the CPU check: x = u*W - 0.5, y = v*H - 0.5, or
+    // with align_corners x = u*(W-1), y = v*(H-1) (fma with a zero addend)
+    const float off = align ? 0.f : -0.5f;
+    const float x = __builtin_fmaf(u, pixel_scale(W, align), off);
+    const float y = __builtin_fmaf(v, pixel_scale(H, align), off);
     const float x0 = floorf(x), y0 = floorf(y);
     n.fx = x - x0;
     n.fy = y - y0;
@@ -285,6 +293,7 @@ struct Dims {
     FastDiv div_lk;  // by L * K (count and scatter kernels)
     FastDiv div_k;   // by K
     int nblocks;     // query blocks of the launch (dots kernel)
+    int align;       // pixel convention: x = u*(W-1) instead of u*W - 0.5
 };
 
 // Workspace of the backward pipeline (all 32-bit words).
@@ -339,7 +348,7 @@ msda_fwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
             const float A = attn[p];
             const int m = (item0 + i1) % M;
             Neighbours n = neighbours(uv.x, uv.y, s_lv.lvl[j / K], row_stride,
-                                      (uint32_t)m * D * 4u);
+                                      (uint32_t)m * D * 4u, dm.align);
             s_off[i1 * dm.PS + jj] = n.off;
             // skip outside neighbours outright, so a non-finite A cannot leak through them
             s_w[i1 * dm.PS + jj] = make_float4((n.valid & 1u) ? A * n.w.x : 0.f,
@@ -433,7 +442,8 @@ bwd_dots_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
             const size_t p = pt0 + (size_t)i1 * M * LK + j;
             const float2 uv = reinterpret_cast<const float2 *>(loc)[p];
             const float A = attn[p];
-            const Neighbours n = neighbours(uv.x, uv.y, s_lv.lvl[j / K], row_stride, head_off);
+            const Neighbours n =
+                neighbours(uv.x, uv.y, s_lv.lvl[j / K], row_stride, head_off, dm.align);
             s_off[i1 * dm.PS + jj] = n.off;
             s_aux[i1 * dm.PS + jj] = make_float4(n.fx, n.fy, A, __uint_as_float(n.valid));
         }
@@ -472,8 +482,8 @@ bwd_dots_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
                 const float fx = ax.x, fy = ax.y, A = ax.z;
                 const float4 w = tent_weights(fx, fy, valid);
                 ga = w.x * d0 + w.y * d1 + w.z * d2 + w.w * d3;
-                gx = A * (float)lvl.y * ((1.f - fy) * (d1 - d0) + fy * (d3 - d2));
-                gy = A * (float)lvl.x * ((1.f - fx) * (d2 - d0) + fx * (d3 - d1));
+                gx = A * pixel_scale(lvl.y, dm.align) * ((1.f - fy) * (d1 - d0) + fy * (d3 - d2));
+                gy = A * pixel_scale(lvl.x, dm.align) * ((1.f - fx) * (d2 - d0) + fx * (d3 - d1));
             }
             grad_attn[p] = ga;
             reinterpret_cast<float2 *>(grad_loc)[p] = make_float2(gx, gy);
@@ -531,7 +541,7 @@ bin_count_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__
         if (f < nf) {
             const int q = (int)fdiv((uint32_t)f, dm.div_lk), j = f - q * LK;
             const int l = (int)fdiv((uint32_t)j, dm.div_k);
-            const Neighbours n = neighbours(uv[r].x, uv[r].y, s_lv.lvl[l], 0u, 0u);
+            const Neighbours n = neighbours(uv[r].x, uv[r].y, s_lv.lvl[l], 0u, 0u, dm.align);
             const TileMask tm = point_tile_mask(n);
             const int tw = s_lv.tw[l];
             const int b00 = s_lv.lvl[l].w + tm.ty0 * tw + tm.tx0;
@@ -694,7 +704,7 @@ bin_scatter_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict
             if (f < nf) {
                 const int q = (int)fdiv((uint32_t)f, dm.div_lk), j = f - q * LK;
                 const int l = (int)fdiv((uint32_t)j, dm.div_k);
-                const Neighbours n = neighbours(uv[r].x, uv[r].y, s_lv.lvl[l], 0u, 0u);
+                const Neighbours n = neighbours(uv[r].x, uv[r].y, s_lv.lvl[l], 0u, 0u, dm.align);
                 const TileMask tm = point_tile_mask(n);
                 const int tw = s_lv.tw[l];
                 const int b00 = s_lv.lvl[l].w + tm.ty0 * tw + tm.tx0;
@@ -718,7 +728,7 @@ bin_scatter_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict
         if (f < nf) {
             const int q = (int)fdiv((uint32_t)f, dm.div_lk), j = f - q * LK;
             const int l = (int)fdiv((uint32_t)j, dm.div_k);
-            const Neighbours n = neighbours(uv[r].x, uv[r].y, s_lv.lvl[l], 0u, 0u);
+            const Neighbours n = neighbours(uv[r].x, uv[r].y, s_lv.lvl[l], 0u, 0u, dm.align);
             const TileMask tm = point_tile_mask(n);
             const int tw = s_lv.tw[l];
             const int b00 = s_lv.lvl[l].w + tm.ty0 * tw + tm.tx0;
@@ -1117,7 +1127,7 @@ int64_t batch_chunk(int64_t per_batch, int64_t B) {
 template <int D, typename VT>
 msda_status launch_fwd(const void *value, const int64_t *shapes, const int64_t *starts,
                        const float *loc, const float *attn, float *out, int64_t B, int64_t Nv,
-                       int64_t Nq, int64_t M, int64_t L, int64_t K, hipStream_t s) {
+                       int64_t Nq, int64_t M, int64_t L, int64_t K, bool align, hipStream_t s) {
     const Launch p = plan(D, L, K, 32);
     const int64_t items = Nq * M;
     const int64_t gx = (items + p.ipb - 1) / p.ipb;
@@ -1125,6 +1135,7 @@ msda_status launch_fwd(const void *value, const int64_t *shapes, const int64_t *
     for (int64_t b0 = 0; b0 < B; b0 += bchunk) {
         const int64_t nb = (B - b0) < bchunk ? (B - b0) : bchunk;
         Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, p.pc, p.ps, (int)b0, (int)gx, 0, 0};
+        dm.align = align ? 1 : 0;
         hipLaunchKernelGGL((msda_fwd_kernel<D, VT>), dim3((unsigned)(gx * nb)), dim3(kThreads),
                            p.lds, s, static_cast<const VT *>(value), shapes, starts, loc, attn,
                            out, dm);
@@ -1200,7 +1211,7 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
                        const float *loc, const float *attn, const float *gout, float *gval,
                        float *gloc, float *gattn, int64_t B, int64_t Nv, int64_t Nq, int64_t M,
                        int64_t L, int64_t K, const WorkLayout &wl, unsigned char *ws,
-                       bool accumulate, const Exec &ex) {
+                       bool accumulate, bool align, const Exec &ex) {
     const hipStream_t s = ex.s;
     Work w;
     w.counts = reinterpret_cast<uint32_t *>(ws + wl.off_counts);
@@ -1230,6 +1241,7 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
     msda_status st = per_batch(gq * M, [&](int64_t b0, unsigned grid) {
         Dims d2{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, p.pc, p.ps, (int)b0, (int)gq, 0, 0};
         d2.nblocks = (int)grid;
+        d2.align = align ? 1 : 0;
         // a few workgroups per CU suffice for this gather-bound kernel, and leave
         // room for the grad_value kernels running beside it
         const unsigned g = grid > (unsigned)kDotsGrid ? (unsigned)kDotsGrid : grid;
@@ -1254,6 +1266,7 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
     const int64_t gb = (Nq * L * K + kBinPoints - 1) / kBinPoints;  // per (batch, head)
     Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, 0, 0, 0, (int)gb, (int)wl.nb_max,
             accumulate ? 1 : 0, make_fastdiv((uint32_t)(L * K)), make_fastdiv((uint32_t)K)};
+    dm.align = align ? 1 : 0;
     ex.stamp(3, false, s);
     st = per_batch(gb * M, [&](int64_t b0, unsigned grid) {
         Dims d2 = dm;
@@ -1299,10 +1312,11 @@ template <typename VT>
 msda_status dispatch_fwd(int64_t D, const void *value, const int64_t *shapes,
                          const int64_t *starts, const float *loc, const float *attn, float *out,
                          int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t L, int64_t K,
-                         hipStream_t s) {
+                         bool align, hipStream_t s) {
 #define MSDA_FWD_CASE(DD)                                                                     \
     case DD:                                                                                  \
-        return launch_fwd<DD, VT>(value, shapes, starts, loc, attn, out, B, Nv, Nq, M, L, K, s);
+        return launch_fwd<DD, VT>(value, shapes, starts, loc, attn, out, B, Nv, Nq, M, L, K,   \
+                                  align, s);
     switch (D) {
         MSDA_FWD_CASE(4)
         MSDA_FWD_CASE(8)
@@ -1321,11 +1335,12 @@ msda_status dispatch_bwd(int64_t D, const void *value, const int64_t *shapes,
                          const int64_t *starts, const float *loc, const float *attn,
                          const float *gout, float *gval, float *gloc, float *gattn, int64_t B,
                          int64_t Nv, int64_t Nq, int64_t M, int64_t L, int64_t K,
-                         const WorkLayout &wl, unsigned char *ws, bool acc, const Exec &ex) {
+                         const WorkLayout &wl, unsigned char *ws, bool acc, bool align,
+                         const Exec &ex) {
 #define MSDA_BWD_CASE(DD)                                                                      \
     case DD:                                                                                   \
         return launch_bwd<DD, VT>(value, shapes, starts, loc, attn, gout, gval, gloc, gattn, B, \
-                                  Nv, Nq, M, L, K, wl, ws, acc, ex);
+                                  Nv, Nq, M, L, K, wl, ws, acc, align, ex);
     switch (D) {
         MSDA_BWD_CASE(4)
         MSDA_BWD_CASE(8)
@@ -1346,9 +1361,12 @@ extern "C" {
 msda_status msda_forward(const void *value, int value_dtype, const int64_t *spatial_shapes,
                          const int64_t *level_start_index, const float *sampling_loc,
                          const float *attn_weight, float *out, int64_t B, int64_t Nv,
-                         int64_t Nq, int64_t M, int64_t D, int64_t L, int64_t K, void *stream) {
+                         int64_t Nq, int64_t M, int64_t D, int64_t L, int64_t K, uint32_t flags,
+                         void *stream) {
     msda_status st = check_sizes(value_dtype, B, Nv, Nq, M, D, L, K);
     if (st != MSDA_OK) return st;
+    if (flags & ~MSDA_ALIGN_CORNERS) return MSDA_ERR_UNSUPPORTED;
+    const bool align = (flags & MSDA_ALIGN_CORNERS) != 0;
     if (B == 0 || Nq == 0) return MSDA_OK;
     if (Nv < 1) return MSDA_ERR_SHAPE;
     if (!value || !spatial_shapes || !level_start_index || !sampling_loc || !attn_weight || !out)
@@ -1356,9 +1374,9 @@ msda_status msda_forward(const void *value, int value_dtype, const int64_t *spat
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (value_dtype == MSDA_F32)
         return dispatch_fwd<float>(D, value, spatial_shapes, level_start_index, sampling_loc,
-                                   attn_weight, out, B, Nv, Nq, M, L, K, s);
+                                   attn_weight, out, B, Nv, Nq, M, L, K, align, s);
     return dispatch_fwd<uint16_t>(D, value, spatial_shapes, level_start_index, sampling_loc,
-                                  attn_weight, out, B, Nv, Nq, M, L, K, s);
+                                  attn_weight, out, B, Nv, Nq, M, L, K, align, s);
 }
 
 size_t msda_backward_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
@@ -1381,7 +1399,7 @@ msda_status backward_impl(const void *value, int value_dtype, const int64_t *spa
                           hipStream_t s, hipEvent_t *ev) {
     msda_status st = check_sizes(value_dtype, B, Nv, Nq, M, D, L, K);
     if (st != MSDA_OK) return st;
-    if (flags & ~MSDA_BWD_ACCUMULATE) return MSDA_ERR_UNSUPPORTED;
+    if (flags & ~(MSDA_BWD_ACCUMULATE | MSDA_ALIGN_CORNERS)) return MSDA_ERR_UNSUPPORTED;
     // a grad_value record stores the query index in 25 bits
     if (Nq > ((int64_t)1 << (32 - kRecQueryShift))) return MSDA_ERR_UNSUPPORTED;
     const int64_t nval = B * Nv * M * D;
@@ -1443,13 +1461,14 @@ msda_status backward_impl(const void *value, int value_dtype, const int64_t *spa
     }
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     const bool acc = (flags & MSDA_BWD_ACCUMULATE) != 0;
+    const bool align = (flags & MSDA_ALIGN_CORNERS) != 0;
     if (value_dtype == MSDA_F32)
         return dispatch_bwd<float>(D, value, spatial_shapes, level_start_index, sampling_loc,
                                    attn_weight, grad_out, grad_value, grad_sampling_loc,
-                                   grad_attn_weight, B, Nv, Nq, M, L, K, wl, ws, acc, ex);
+                                   grad_attn_weight, B, Nv, Nq, M, L, K, wl, ws, acc, align, ex);
     return dispatch_bwd<uint16_t>(D, value, spatial_shapes, level_start_index, sampling_loc,
                                   attn_weight, grad_out, grad_value, grad_sampling_loc,
-                                  grad_attn_weight, B, Nv, Nq, M, L, K, wl, ws, acc, ex);
+                                  grad_attn_weight, B, Nv, Nq, M, L, K, wl, ws, acc, align, ex);
 }
 
 }  // namespace

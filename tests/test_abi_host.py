@@ -80,7 +80,7 @@ def test_forward_rejects_before_launch():
     """These return before any HIP call, so they are safe without a GPU."""
     lib = msda.load()
     z = ctypes.c_void_p(0)
-    fwd = lambda dt, *dims: lib.msda_forward(z, dt, z, z, z, z, z, *dims, z)
+    fwd = lambda dt, *dims, flags=0: lib.msda_forward(z, dt, z, z, z, z, z, *dims, flags, z)
     assert fwd(7, 1, 80, 16, 2, 8, 2, 2) == B_.MSDA_ERR_DTYPE
     assert fwd(0, 1, 80, 16, 2, 12, 2, 2) == B_.MSDA_ERR_UNSUPPORTED
     assert fwd(0, 1, 80, 16, 2, 8, 0, 2) == B_.MSDA_ERR_SHAPE
@@ -89,6 +89,9 @@ def test_forward_rejects_before_launch():
     # nothing to do: no launch, no pointer needed
     assert fwd(0, 0, 80, 16, 2, 8, 2, 2) == B_.MSDA_OK
     assert fwd(1, 3, 80, 0, 2, 8, 2, 2) == B_.MSDA_OK
+    # flags: align_corners is a forward flag, accumulate is not
+    assert fwd(0, 0, 80, 16, 2, 8, 2, 2, flags=B_.MSDA_ALIGN_CORNERS) == B_.MSDA_OK
+    assert fwd(0, 1, 80, 16, 2, 8, 2, 2, flags=B_.MSDA_BWD_ACCUMULATE) == B_.MSDA_ERR_UNSUPPORTED
 
 
 def test_backward_rejects_before_launch():

@@ -66,14 +66,15 @@ def gpu_backward(m, w, bf16=False, **kw):
     return gv.cpu().numpy(), gl.cpu().numpy(), ga.cpu().numpy()
 
 
-def oracle_fwd(w, value=None):
+def oracle_fwd(w, value=None, mode=oracle.SPEC):
     return oracle.forward(w.value if value is None else value, w.spatial_shapes,
-                          w.level_start_index, w.sampling_loc, w.attn_weight)
+                          w.level_start_index, w.sampling_loc, w.attn_weight, mode=mode)
 
 
-def oracle_bwd(w, value=None):
+def oracle_bwd(w, value=None, mode=oracle.SPEC):
     return oracle.backward(w.value if value is None else value, w.spatial_shapes,
-                           w.level_start_index, w.sampling_loc, w.attn_weight, w.grad_out)
+                           w.level_start_index, w.sampling_loc, w.attn_weight, w.grad_out,
+                           mode=mode)
 
 
 def check_fwd(m, w, tol=FWD_TOL, bf16=False):
@@ -174,6 +175,46 @@ def test_many_tiles_use_global_bin_counters(msda):
     _say("4225 tiles")
     check_fwd(msda, w)
     check_bwd(msda, w)
+
+
+# ---------------------------------------------------------------------------
+# the align_corners pixel convention (x = u*(W-1), y = v*(H-1))
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("D,bf16", [(8, False), (32, False), (32, True), (64, False)])
+def test_align_corners(msda, D, bf16):
+    shapes = ((9, 13), (5, 7), (1, 6), (4, 1))
+    w = workloads.random_case(360 + D, 2, shapes, 83, 3, D, 3, -0.2, 1.2, bf16=bf16)
+    _say(f"align_corners D={D} bf16={bf16}")
+    x = dev_inputs(w, bf16)
+    out = msda.forward(**x, align_corners=True)
+    g = torch.from_numpy(w.grad_out).cuda()
+    gv, gl, ga = msda.backward(**x, grad_out=g, align_corners=True)
+    torch.cuda.synchronize()
+    mode = oracle.SPEC | oracle.ALIGN
+    close(out.cpu().numpy(), oracle_fwd(w, mode=mode).reshape(out.shape), FWD_TOL, "forward")
+    rv, rl, ra = oracle_bwd(w, mode=mode)
+    close(gv.cpu().numpy(), rv, BWD_TOL, "grad_value")
+    close(gl.cpu().numpy(), rl, BWD_TOL, "grad_sampling_loc")
+    close(ga.cpu().numpy(), ra, BWD_TOL, "grad_attn_weight")
+    # the two conventions really differ on these inputs
+    assert max_rel(out.cpu().numpy(), oracle_fwd(w).reshape(out.shape)) > 1e-3
+
+
+def test_align_corners_encoder(msda):
+    """The encoder shape, forward and backward, in the align_corners convention."""
+    w = workloads.make(3)
+    _say("align_corners encoder")
+    x = dev_inputs(w)
+    out = msda.forward(**x, align_corners=True)
+    gv, gl, ga = msda.backward(**x, grad_out=torch.from_numpy(w.grad_out).cuda(),
+                               align_corners=True)
+    torch.cuda.synchronize()
+    mode = oracle.SPEC | oracle.ALIGN
+    close(out.cpu().numpy(), oracle_fwd(w, mode=mode).reshape(out.shape), FWD_TOL, "forward")
+    rv, rl, ra = oracle_bwd(w, mode=mode)
+    close(gv.cpu().numpy(), rv, BWD_TOL, "grad_value")
+    close(gl.cpu().numpy(), rl, BWD_TOL, "grad_sampling_loc")
+    close(ga.cpu().numpy(), ra, BWD_TOL, "grad_attn_weight")
 
 
 def test_pixel_centres_are_exact(msda):
