@@ -193,3 +193,83 @@ def random_case(seed: int, B: int, shapes, Nq: int, M: int, D: int, K: int,
         return Workload(name, bf16_to_f32(bits).reshape(vals.shape), ss, st, loc, w, g,
                         value_bf16=bits.reshape(vals.shape), value_unrounded=vals)
     return Workload(name, vals, ss, st, loc, w, g)
+
+
+@dataclasses.dataclass
+class FusedWorkload:
+    """Inputs of the fused prologue: raw offsets and logits plus reference points."""
+    name: str
+    value: np.ndarray                 # [B,Nv,M,D] float32 (bf16-rounded when value_bf16 is set)
+    spatial_shapes: np.ndarray        # [L,2] int64 rows (H,W)
+    level_start_index: np.ndarray     # [L] int64
+    reference_points: np.ndarray      # [B,Nq,L,2] float32, normalized (x, y)
+    sampling_offsets: np.ndarray      # [B,Nq,M,L,K,2] float32, pixels of level l
+    attn_logits: np.ndarray           # [B,Nq,M,L*K] float32
+    grad_out: Optional[np.ndarray]    # [B,Nq,M*D] float32
+    value_bf16: Optional[np.ndarray] = None   # [B,Nv,M,D] uint16 bits
+
+    @property
+    def dims(self):
+        B, Nv, M, D = self.value.shape
+        _, Nq, _, L, K, _ = self.sampling_offsets.shape
+        return dict(B=B, Nv=Nv, Nq=Nq, M=M, D=D, L=L, K=K)
+
+    @property
+    def points(self) -> int:
+        d = self.dims
+        return d["B"] * d["Nq"] * d["M"] * d["L"] * d["K"]
+
+
+def fused_case(seed: int, B: int, shapes, Nq: int, M: int, D: int, K: int,
+               ref_low: float = 0.0, ref_high: float = 1.0, sigma_px: float = 2.0,
+               logit_scale: float = 1.0, bf16: bool = False) -> FusedWorkload:
+    """Small random case for the fused prologue: references uniform in
+    [ref_low, ref_high) per level, offsets N(0, sigma_px) pixels, logits
+    N(0, logit_scale)."""
+    ss, st = level_table(shapes)
+    Nv = int(ss.prod(axis=1).sum()) if len(shapes) else 0
+    L = len(shapes)
+    r = _rng(seed)
+    vals = r.standard_normal((B, Nv, M, D)).astype(np.float32)
+    ref = r.uniform(ref_low, ref_high, (B, Nq, L, 2)).astype(np.float32)
+    off = (r.standard_normal((B, Nq, M, L, K, 2)) * sigma_px).astype(np.float32)
+    logits = (r.standard_normal((B, Nq, M, L * K)) * logit_scale).astype(np.float32)
+    g = r.standard_normal((B, Nq, M * D)).astype(np.float32)
+    name = f"fused_random(seed={seed})"
+    if bf16:
+        bits = bf16_bits(vals)
+        return FusedWorkload(name, bf16_to_f32(bits).reshape(vals.shape), ss, st, ref, off,
+                             logits, g, value_bf16=bits.reshape(vals.shape))
+    return FusedWorkload(name, vals, ss, st, ref, off, logits, g)
+
+
+def make_fused(config: int | str = "encoder_bwd", batch: Optional[int] = None) -> FusedWorkload:
+    """The encoder-shape configurations in the fused prologue's input form:
+    every flattened pixel is a query whose reference point is its own pixel
+    centre on every level, offsets N(0, sigma) pixels of each level and
+    logits N(0, 1) (seeds 1000*config + 2 and + 3, as in make())."""
+    idx = CONFIG_NAMES.index(config) if isinstance(config, str) else int(config)
+    if idx not in (1, 3, 4):
+        raise ValueError("fused inputs are defined for the encoder-shape configurations")
+    base = 1000 * idx
+    shapes = DETR_LEVELS
+    ss, st = level_table(shapes)
+    Nv = int(ss.prod(axis=1).sum())
+    L = len(shapes)
+    M, D = 8, 32
+    B, K, sigma = (2, 4, 2.0) if idx in (1, 3) else (4, 8, 3.0)
+    if batch is not None:
+        B = int(batch)
+    Nq = Nv
+    vals = _rng(base + 0).standard_normal((B, Nv, M, D)).astype(np.float32)
+    ref = np.broadcast_to(_encoder_refs(shapes)[None, :, None, :], (B, Nq, L, 2))
+    ref = np.ascontiguousarray(ref, dtype=np.float32)
+    off = (_rng(base + 2).standard_normal((B, Nq, M, L, K, 2)) * sigma).astype(np.float32)
+    logits = _rng(base + 3).standard_normal((B, Nq, M, L * K)).astype(np.float32)
+    g = _rng(base + 4).standard_normal((B, Nq, M * D)).astype(np.float32)
+    name = CONFIG_NAMES[idx] + "_fused"
+    if idx == 4:
+        bits = bf16_bits(vals)
+        return FusedWorkload(name, bf16_to_f32(bits).reshape(vals.shape), ss, st, ref, off,
+                             logits, g, value_bf16=bits.reshape(vals.shape))
+    return FusedWorkload(name, vals, ss, st, ref, off, logits, g)
