@@ -97,6 +97,7 @@ typedef enum msda_dtype {
 /* Flags (unknown bits give MSDA_ERR_UNSUPPORTED). */
 #define MSDA_BWD_ACCUMULATE 1u /* backward: add into grad_value instead of overwriting  */
 #define MSDA_ALIGN_CORNERS 2u  /* both: x = u*(W-1), y = v*(H-1) (align_corners=True)   */
+#define MSDA_SOFTMAX_PER_LEVEL 4u /* fused entry points: softmax over each level's K points */
 
 /*
  * Forward: out = MSDeformAttn core(value, level table, sampling_loc, attn_weight).
@@ -181,6 +182,81 @@ msda_status msda_backward_events(const void *value, int value_dtype,
                                  int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
                                  int64_t L, int64_t K, void *workspace, size_t workspace_bytes,
                                  uint32_t flags, void *stream, void *const *events);
+
+/*
+ * Fused prologue.  The module around the core ("Deformable attention:
+ * multi-scale sparse sampling and detection practice", section 3.2; the
+ * "Deformable DETR" tutorial's pseudocode, section 6) predicts per point a
+ * pixel offset and an attention logit; the location is the query's
+ * reference point on that level plus the offset divided by the level's
+ * (W_l, H_l), and the weights are a softmax of the logits:
+ *
+ *   loc[b,q,m,l,k] = reference_points[b,q,l] + sampling_offsets[b,q,m,l,k] / (W_l, H_l)
+ *   A[b,q,m,l,k]   = softmax of attn_logits[b,q,m,:] over its L*K entries, or
+ *                    (MSDA_SOFTMAX_PER_LEVEL) over the K entries of level l
+ *
+ * The module's code normalizes over all L*K points, the same page's text
+ * over the K points of each level (section 2.2); both are offered.  The
+ * location is computed in fp32 as one correctly rounded division and one
+ * addition per coordinate; the softmax in fp32 with its maximum subtracted.
+ * These entry points evaluate exactly the core above on those locations and
+ * weights, without storing them in the forward.
+ *
+ * Layouts (dense, row-major, device pointers, caller-owned):
+ *   reference_points        [B, Nq, L, 2]        fp32, (x, y) normalized
+ *   sampling_offsets        [B, Nq, M, L, K, 2]  fp32, (x, y) in pixels of level l
+ *   attn_logits             [B, Nq, M, L*K]      fp32 (level-major: index l*K + k)
+ *   grad_sampling_offsets   like sampling_offsets
+ *   grad_attn_logits        like attn_logits
+ *   grad_reference_points   like reference_points
+ * value, the level table, out, grad_out and grad_value as above.
+ *
+ * msda_forward_fused: out is overwritten.  flags: MSDA_ALIGN_CORNERS and/or
+ * MSDA_SOFTMAX_PER_LEVEL.  Errors and limits as msda_forward.
+ */
+msda_status msda_forward_fused(const void *value, int value_dtype,
+                               const int64_t *spatial_shapes, const int64_t *level_start_index,
+                               const float *reference_points, const float *sampling_offsets,
+                               const float *attn_logits, float *out,
+                               int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
+                               int64_t L, int64_t K, uint32_t flags, void *stream);
+
+/*
+ * Workspace bytes of msda_backward_fused: msda_backward_workspace_size plus
+ * 12 bytes per sampling point (the locations and weights, recomputed).
+ */
+size_t msda_backward_fused_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int64_t M,
+                                          int64_t D, int64_t L, int64_t K);
+
+/*
+ * Backward of msda_forward_fused: the chain rule through the prologue on top
+ * of the core's gradients (msda_backward):
+ *   grad_sampling_offsets = grad_loc / (W_l, H_l)
+ *   grad_attn_logits      = A * (grad_A - sum over the softmax group of A * grad_A)
+ *   grad_reference_points[b,q,l] = sum over heads m and points k of grad_loc
+ * grad_value is overwritten, or added to with MSDA_BWD_ACCUMULATE; the other
+ * gradients are overwritten.  grad_reference_points may be NULL (not
+ * computed, e.g. for fixed encoder reference points); every other pointer is
+ * required.  flags: MSDA_BWD_ACCUMULATE, MSDA_ALIGN_CORNERS and
+ * MSDA_SOFTMAX_PER_LEVEL, the last two as given to the forward.
+ * workspace: at least msda_backward_fused_workspace_size(...) bytes, 256-byte
+ * aligned, as for msda_backward.
+ * events: NULL, or 2 * MSDA_BWD_FUSED_STAGES caller-owned HIP events recorded
+ * around the stages as msda_backward_events does (null entries skipped):
+ * stages 0-6 as there, 7 the prologue (locations and weights into the
+ * workspace), 8 the epilogue (logit and reference-point gradients).
+ * The same side stream as msda_backward is used.
+ */
+#define MSDA_BWD_FUSED_STAGES (MSDA_BWD_STAGES + 2)
+msda_status msda_backward_fused(const void *value, int value_dtype,
+                                const int64_t *spatial_shapes, const int64_t *level_start_index,
+                                const float *reference_points, const float *sampling_offsets,
+                                const float *attn_logits, const float *grad_out,
+                                float *grad_value, float *grad_sampling_offsets,
+                                float *grad_attn_logits, float *grad_reference_points,
+                                int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
+                                int64_t L, int64_t K, void *workspace, size_t workspace_bytes,
+                                uint32_t flags, void *stream, void *const *events);
 
 /*
  * Pure host check of the sizes and of a HOST copy of the level table:

@@ -8,16 +8,20 @@ from __future__ import annotations
 
 import torch
 
-from ._binding import (BWD_STAGES, EXPORTED, LIB_PATH, MSDA_ALIGN_CORNERS, MSDA_BF16,
-                       MSDA_BWD_ACCUMULATE, MSDA_ERR_DTYPE,
+from ._binding import (BWD_FUSED_STAGES, BWD_STAGES, EXPORTED, LIB_PATH, MSDA_ALIGN_CORNERS,
+                       MSDA_BF16, MSDA_BWD_ACCUMULATE, MSDA_ERR_DTYPE,
                        MSDA_ERR_HIP, MSDA_ERR_NULL, MSDA_ERR_SHAPE, MSDA_ERR_UNSUPPORTED,
-                       MSDA_ERR_WORKSPACE, MSDA_F32, MSDA_OK, MSDAError, backward, forward, load,
-                       make_events, stage_times, status_string, validate_host, workspace_size)
+                       MSDA_ERR_WORKSPACE, MSDA_F32, MSDA_OK, MSDA_SOFTMAX_PER_LEVEL, MSDAError,
+                       backward, backward_fused, forward, forward_fused, fused_workspace_size,
+                       load, make_events, stage_times, status_string, validate_host,
+                       workspace_size)
 
-__all__ = ["forward", "backward", "BWD_STAGES", "make_events", "stage_times", "workspace_size",
-           "validate_host", "status_string", "load",
+__all__ = ["forward", "backward", "forward_fused", "backward_fused", "BWD_STAGES",
+           "BWD_FUSED_STAGES", "make_events", "stage_times", "workspace_size",
+           "fused_workspace_size", "validate_host", "status_string", "load",
            "MSDAError",
-           "ms_deform_attn", "MSDeformAttnFunction", "LIB_PATH", "EXPORTED"]
+           "ms_deform_attn", "MSDeformAttnFunction", "ms_deform_attn_fused",
+           "MSDeformAttnFusedFunction", "LIB_PATH", "EXPORTED"]
 
 
 class MSDeformAttnFunction(torch.autograd.Function):
@@ -47,3 +51,38 @@ def ms_deform_attn(value, spatial_shapes, level_start_index, sampling_loc, attn_
                    align_corners=False):
     return MSDeformAttnFunction.apply(value, spatial_shapes, level_start_index, sampling_loc,
                                       attn_weight, align_corners)
+
+
+class MSDeformAttnFusedFunction(torch.autograd.Function):
+    """out = core(value, level table, ref + offsets / (W_l, H_l), softmax(logits))
+    computed by the fused entry points; the backward returns the gradients of
+    value, reference_points, sampling_offsets and attn_logits."""
+
+    @staticmethod
+    def forward(ctx, value, spatial_shapes, level_start_index, reference_points,
+                sampling_offsets, attn_logits, per_level=False, align_corners=False):
+        out = forward_fused(value, spatial_shapes, level_start_index, reference_points,
+                            sampling_offsets, attn_logits, per_level=per_level,
+                            align_corners=align_corners)
+        ctx.save_for_backward(value, spatial_shapes, level_start_index, reference_points,
+                              sampling_offsets, attn_logits)
+        ctx.per_level = per_level
+        ctx.align_corners = align_corners
+        return out
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        value, ss, st, ref, off, logits = ctx.saved_tensors
+        gv, goff, gz, gref = backward_fused(value, ss, st, ref, off, logits,
+                                            grad_out.contiguous(), validate=False,
+                                            need_grad_ref=ctx.needs_input_grad[3],
+                                            per_level=ctx.per_level,
+                                            align_corners=ctx.align_corners)
+        return gv, None, None, gref, goff, gz, None, None
+
+
+def ms_deform_attn_fused(value, spatial_shapes, level_start_index, reference_points,
+                         sampling_offsets, attn_logits, per_level=False, align_corners=False):
+    return MSDeformAttnFusedFunction.apply(value, spatial_shapes, level_start_index,
+                                           reference_points, sampling_offsets, attn_logits,
+                                           per_level, align_corners)

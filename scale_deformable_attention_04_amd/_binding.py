@@ -27,11 +27,14 @@ MSDA_F32 = 0
 MSDA_BF16 = 1
 MSDA_BWD_ACCUMULATE = 1
 MSDA_ALIGN_CORNERS = 2
+MSDA_SOFTMAX_PER_LEVEL = 4
 
 EXPORTED = ("msda_forward", "msda_backward_workspace_size", "msda_backward",
-            "msda_backward_events", "msda_validate_host", "msda_status_string",
+            "msda_backward_events", "msda_forward_fused", "msda_backward_fused_workspace_size",
+            "msda_backward_fused", "msda_validate_host", "msda_status_string",
             "msda_last_hip_error")
 BWD_STAGES = ("fill_grad_value", "dots", "clear_bins", "count", "scan", "scatter", "tiles")
+BWD_FUSED_STAGES = BWD_STAGES + ("prologue", "epilogue")
 
 _lib = None
 
@@ -65,6 +68,13 @@ def load():
     lib.msda_backward_events.restype = ci
     lib.msda_backward_workspace_size.argtypes = [i64] * 7
     lib.msda_backward_workspace_size.restype = ctypes.c_size_t
+    lib.msda_forward_fused.argtypes = [p, ci, p, p, p, p, p, p] + [i64] * 7 + [u32, p]
+    lib.msda_forward_fused.restype = ci
+    lib.msda_backward_fused_workspace_size.argtypes = [i64] * 7
+    lib.msda_backward_fused_workspace_size.restype = ctypes.c_size_t
+    lib.msda_backward_fused.argtypes = ([p, ci, p, p, p, p, p, p, p, p, p, p] + [i64] * 7 +
+                                        [p, ctypes.c_size_t, u32, p, p])
+    lib.msda_backward_fused.restype = ci
     lib.msda_validate_host.argtypes = [p, p] + [i64] * 7
     lib.msda_validate_host.restype = ci
     lib.msda_status_string.argtypes = [ci]
@@ -191,18 +201,31 @@ def forward(value: torch.Tensor, spatial_shapes: torch.Tensor, level_start_index
 
 
 def stage_times(events: list) -> list:
-    """Durations in us of the backward stages recorded by backward(events=...),
-    in the order of BWD_STAGES; call after the stream has been synchronized."""
+    """Durations in us of the backward stages recorded by backward(events=...)
+    or backward_fused(events=...), in the order of BWD_STAGES (BWD_FUSED_STAGES);
+    call after the stream has been synchronized."""
     return [1000.0 * events[2 * i].elapsed_time(events[2 * i + 1])
-            if events[2 * i] is not None else None for i in range(len(BWD_STAGES))]
+            if events[2 * i] is not None else None for i in range(len(events) // 2)]
 
 
-def make_events(stage: Optional[str] = None) -> list:
-    """A fresh set of timing events for backward(events=...): for every stage,
-    or only for the named one (None in the other places)."""
+def make_events(stage: Optional[str] = None, fused: bool = False) -> list:
+    """A fresh set of timing events for backward(events=...) (fused=False) or
+    backward_fused(events=...): for every stage, or only for the named one
+    (None in the other places)."""
+    stages = BWD_FUSED_STAGES if fused else BWD_STAGES
     return [torch.cuda.Event(enable_timing=True)
-            if stage is None or BWD_STAGES[i // 2] == stage else None
-            for i in range(2 * len(BWD_STAGES))]
+            if stage is None or stages[i // 2] == stage else None
+            for i in range(2 * len(stages))]
+
+
+def _event_handles(events: list, n: int):
+    if len(events) != 2 * n:
+        raise ValueError(f"events: {2 * n} torch.cuda.Event expected")
+    for e in events:
+        if e is not None and not e.cuda_event:  # torch creates it at its first record
+            e.record()
+    return (ctypes.c_void_p * len(events))(
+        *[e.cuda_event if e is not None else None for e in events])
 
 
 def backward(value: torch.Tensor, spatial_shapes: torch.Tensor, level_start_index: torch.Tensor,
@@ -259,15 +282,116 @@ def backward(value: torch.Tensor, spatial_shapes: torch.Tensor, level_start_inde
             rc = lib.msda_backward(*args, stream)
             where = "msda_backward"
         else:
-            if len(events) != 2 * len(BWD_STAGES):
-                raise ValueError(f"events: {2 * len(BWD_STAGES)} torch.cuda.Event expected")
-            for e in events:
-                if e is not None and not e.cuda_event:  # torch creates it at its first record
-                    e.record()
-            handles = (ctypes.c_void_p * len(events))(
-                *[e.cuda_event if e is not None else None for e in events])
+            handles = _event_handles(events, len(BWD_STAGES))
             rc = lib.msda_backward_events(*args, stream, handles)
             where = "msda_backward_events"
     if rc != MSDA_OK:
         raise MSDAError(rc, where)
     return grad_value, grad_sampling_loc, grad_attn_weight
+
+
+# ---------------------------------------------------------------------------
+# fused prologue: reference points + pixel offsets + attention logits
+# ---------------------------------------------------------------------------
+def _check_fused_inputs(value, spatial_shapes, level_start_index, reference_points,
+                        sampling_offsets, attn_logits, validate):
+    dev = value.device
+    if dev.type != "cuda":
+        raise ValueError(f"value must be a GPU tensor, got device {dev}")
+    _dtype_code(value)
+    B, Nv, Nq, M, D, L, K = _dims(value, spatial_shapes, sampling_offsets)
+    _need(value, "value", value.dtype, dev)
+    _need(spatial_shapes, "spatial_shapes", torch.int64, dev, (L, 2))
+    _need(level_start_index, "level_start_index", torch.int64, dev, (L,))
+    _need(reference_points, "reference_points", torch.float32, dev, (B, Nq, L, 2))
+    _need(sampling_offsets, "sampling_offsets", torch.float32, dev, (B, Nq, M, L, K, 2))
+    _need(attn_logits, "attn_logits", torch.float32, dev, (B, Nq, M, L * K))
+    if validate:
+        rc = validate_host(spatial_shapes, level_start_index, B, Nv, Nq, M, D, L, K)
+        if rc != MSDA_OK:
+            raise MSDAError(rc, "msda_validate_host")
+    return dev, (B, Nv, Nq, M, D, L, K)
+
+
+def _fused_flags(per_level: bool, align_corners: bool) -> int:
+    return ((MSDA_SOFTMAX_PER_LEVEL if per_level else 0) |
+            (MSDA_ALIGN_CORNERS if align_corners else 0))
+
+
+def forward_fused(value: torch.Tensor, spatial_shapes: torch.Tensor,
+                  level_start_index: torch.Tensor, reference_points: torch.Tensor,
+                  sampling_offsets: torch.Tensor, attn_logits: torch.Tensor,
+                  out: Optional[torch.Tensor] = None, validate: bool = True,
+                  per_level: bool = False, align_corners: bool = False) -> torch.Tensor:
+    """msda_forward_fused: out[B, Nq, M*D] (fp32) from reference points
+    [B,Nq,L,2], pixel offsets [B,Nq,M,L,K,2] and logits [B,Nq,M,L*K].
+    per_level=True normalizes the logits over each level's K points instead
+    of all L*K; align_corners as in forward()."""
+    lib = load()
+    dev, (B, Nv, Nq, M, D, L, K) = _check_fused_inputs(
+        value, spatial_shapes, level_start_index, reference_points, sampling_offsets,
+        attn_logits, validate)
+    if out is None:
+        out = torch.empty((B, Nq, M * D), dtype=torch.float32, device=dev)
+    else:
+        _need(out, "out", torch.float32, dev, (B, Nq, M * D))
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = lib.msda_forward_fused(_ptr(value), _dtype_code(value), _ptr(spatial_shapes),
+                                    _ptr(level_start_index), _ptr(reference_points),
+                                    _ptr(sampling_offsets), _ptr(attn_logits), _ptr(out),
+                                    B, Nv, Nq, M, D, L, K, _fused_flags(per_level, align_corners),
+                                    ctypes.c_void_p(stream))
+    if rc != MSDA_OK:
+        raise MSDAError(rc, "msda_forward_fused")
+    return out
+
+
+def fused_workspace_size(B, Nv, Nq, M, D, L, K) -> int:
+    """msda_backward_fused_workspace_size."""
+    return int(load().msda_backward_fused_workspace_size(B, Nv, Nq, M, D, L, K))
+
+
+def backward_fused(value: torch.Tensor, spatial_shapes: torch.Tensor,
+                   level_start_index: torch.Tensor, reference_points: torch.Tensor,
+                   sampling_offsets: torch.Tensor, attn_logits: torch.Tensor,
+                   grad_out: torch.Tensor, grad_value: Optional[torch.Tensor] = None,
+                   accumulate: bool = False, need_grad_ref: bool = True,
+                   validate: bool = True, workspace: Optional[torch.Tensor] = None,
+                   events: Optional[list] = None, per_level: bool = False,
+                   align_corners: bool = False):
+    """msda_backward_fused: (grad_value, grad_sampling_offsets, grad_attn_logits,
+    grad_reference_points or None when need_grad_ref is False).
+    events: 2 * len(BWD_FUSED_STAGES) timing events or None (see stage_times)."""
+    lib = load()
+    dev, (B, Nv, Nq, M, D, L, K) = _check_fused_inputs(
+        value, spatial_shapes, level_start_index, reference_points, sampling_offsets,
+        attn_logits, validate)
+    _need(grad_out, "grad_out", torch.float32, dev, (B, Nq, M * D))
+    if grad_value is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs a grad_value to add into")
+        grad_value = torch.empty((B, Nv, M, D), dtype=torch.float32, device=dev)
+    else:
+        _need(grad_value, "grad_value", torch.float32, dev, (B, Nv, M, D))
+    g_off = torch.empty_like(sampling_offsets)
+    g_logits = torch.empty_like(attn_logits)
+    g_ref = torch.empty_like(reference_points) if need_grad_ref else None
+    flags = _fused_flags(per_level, align_corners) | (MSDA_BWD_ACCUMULATE if accumulate else 0)
+    need = fused_workspace_size(B, Nv, Nq, M, D, L, K)
+    if workspace is None:
+        workspace = _workspace(dev, need)
+    elif workspace.device != dev or workspace.dtype != torch.uint8 or workspace.numel() < need:
+        raise ValueError(f"workspace must be a uint8 tensor on {dev} of >= {need} bytes")
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    with torch.cuda.device(dev):
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        handles = None if events is None else _event_handles(events, len(BWD_FUSED_STAGES))
+        rc = lib.msda_backward_fused(
+            _ptr(value), _dtype_code(value), _ptr(spatial_shapes), _ptr(level_start_index),
+            _ptr(reference_points), _ptr(sampling_offsets), _ptr(attn_logits), _ptr(grad_out),
+            _ptr(grad_value), _ptr(g_off), _ptr(g_logits), _ptr(g_ref), B, Nv, Nq, M, D, L, K,
+            _ptr(workspace), ws_bytes, flags, stream, handles)
+    if rc != MSDA_OK:
+        raise MSDAError(rc, "msda_backward_fused")
+    return grad_value, g_off, g_logits, g_ref

@@ -294,6 +294,7 @@ struct Dims {
     FastDiv div_k;   // by K
     int nblocks;     // query blocks of the launch (dots kernel)
     int align;       // pixel convention: x = u*(W-1) instead of u*W - 0.5
+    int loc_div;     // dots kernel: location gradients divided by (W, H) (offset gradients)
 };
 
 // Workspace of the backward pipeline (all 32-bit words).
@@ -306,20 +307,65 @@ struct Work {
     uint4 *recs;           // [4 * points] records grouped by bin
 };
 
+// Raw inputs of the fused prologue, which computes the sampling location and
+// the attention weight of each point from them:
+//   loc = ref[b, q, l] + off[b, q, m, l, k] / (W_l, H_l)   (fp32: one IEEE
+//         division and one addition per coordinate)
+//   A   = softmax of the logits over the L*K points of (b, q, m), or over the
+//         K points of each level when per_level is set.
+struct Prologue {
+    const float *ref;     // [B, Nq, L, 2]
+    const float *off;     // [B, Nq, M, L, K, 2]
+    const float *logits;  // [B, Nq, M, L * K]
+    int per_level;
+};
+
+// (max, 1 / sum exp(z - max)) over the n logits at z.
+__device__ __forceinline__ float2 softmax_stats(const float *__restrict__ z, int n) {
+    float mx = -INFINITY;
+    for (int j = 0; j < n; ++j) mx = fmaxf(mx, z[j]);
+    float sum = 0.f;
+    for (int j = 0; j < n; ++j) sum += expf(z[j] - mx);
+    return make_float2(mx, 1.f / sum);
+}
+
+// Location of a point from its level's reference point and pixel offset.  A
+// level left out of the table (W = H = 0) gives a non-finite location, which
+// samples nothing.
+__device__ __forceinline__ float2 prologue_location(float2 r, float2 o, int4 lvl) {
+    return make_float2(r.x + o.x / (float)lvl.y, r.y + o.y / (float)lvl.x);
+}
+
+// Softmax statistics of the groups of nitems consecutive items starting at
+// point pt0 into s_st[item * groups + group].
+__device__ __forceinline__ void stage_softmax_stats(float2 *s_st, const Prologue &pr, size_t pt0,
+                                                    int nitems, int L, int K) {
+    const int LK = L * K, ng = pr.per_level ? L : 1, gs = pr.per_level ? K : LK;
+    for (int idx = threadIdx.x; idx < nitems * ng; idx += blockDim.x) {
+        const int i1 = idx / ng, g = idx - i1 * ng;
+        s_st[idx] = softmax_stats(pr.logits + pt0 + (size_t)i1 * LK + (size_t)g * gs, gs);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------
-template <int D, typename VT>
+// With FUSED the locations and weights come from the prologue inputs `pr`
+// (loc and attn are unused): per item the softmax statistics of its logits
+// are staged in LDS first, then each point's location and weight are formed
+// where the plain kernel loads them.
+template <int D, typename VT, bool FUSED>
 __global__ void __launch_bounds__(kThreads)
 msda_fwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes,
                 const int64_t *__restrict__ starts, const float *__restrict__ loc,
-                const float *__restrict__ attn, float *__restrict__ out, Dims dm) {
+                const float *__restrict__ attn, Prologue pr, float *__restrict__ out, Dims dm) {
     constexpr int G = D / 4;
     constexpr int IPB = kThreads / G;
     __shared__ LevelLds s_lv;
     extern __shared__ __align__(16) unsigned char smem[];
     uint4 *s_off = reinterpret_cast<uint4 *>(smem);
     float4 *s_w = reinterpret_cast<float4 *>(s_off + IPB * dm.PS);
+    float2 *s_st = reinterpret_cast<float2 *>(s_w + IPB * dm.PS);  // FUSED: softmax stats
 
     const int M = dm.M, K = dm.K, LK = dm.L * dm.K;
     const int NqM = dm.Nq * M;
@@ -334,6 +380,11 @@ msda_fwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
     const size_t slice = (size_t)dm.Nv * M * D;
     const rsrc_t vr = make_rsrc(value + (size_t)b * slice, (uint32_t)(slice * sizeof(VT)));
     const size_t pt0 = ((size_t)b * NqM + item0) * LK;
+    const int ng = pr.per_level ? dm.L : 1;
+    if constexpr (FUSED) {
+        stage_softmax_stats(s_st, pr, pt0, nitems, dm.L, K);
+        __syncthreads();
+    }
 
     const int it = threadIdx.x / G, c = threadIdx.x % G;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -344,10 +395,23 @@ msda_fwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
         for (int idx = threadIdx.x; idx < nitems * pc; idx += kThreads) {
             const int i1 = idx / pc, jj = idx - i1 * pc, j = j0 + jj;
             const size_t p = pt0 + (size_t)i1 * LK + j;
-            const float2 uv = reinterpret_cast<const float2 *>(loc)[p];
-            const float A = attn[p];
+            const int l = j / K;
+            float2 uv;
+            float A;
+            if constexpr (FUSED) {
+                const int q = (item0 + i1) / M;
+                const float2 r =
+                    reinterpret_cast<const float2 *>(pr.ref)[((size_t)b * dm.Nq + q) * dm.L + l];
+                uv = prologue_location(r, reinterpret_cast<const float2 *>(pr.off)[p],
+                                       s_lv.lvl[l]);
+                const float2 st = s_st[i1 * ng + (pr.per_level ? l : 0)];
+                A = expf(pr.logits[p] - st.x) * st.y;
+            } else {
+                uv = reinterpret_cast<const float2 *>(loc)[p];
+                A = attn[p];
+            }
             const int m = (item0 + i1) % M;
-            Neighbours n = neighbours(uv.x, uv.y, s_lv.lvl[j / K], row_stride,
+            Neighbours n = neighbours(uv.x, uv.y, s_lv.lvl[l], row_stride,
                                       (uint32_t)m * D * 4u, dm.align);
             s_off[i1 * dm.PS + jj] = n.off;
             // skip outside neighbours outright, so a non-finite A cannot leak through them
@@ -482,8 +546,13 @@ bwd_dots_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
                 const float fx = ax.x, fy = ax.y, A = ax.z;
                 const float4 w = tent_weights(fx, fy, valid);
                 ga = w.x * d0 + w.y * d1 + w.z * d2 + w.w * d3;
-                gx = A * pixel_scale(lvl.y, dm.align) * ((1.f - fy) * (d1 - d0) + fy * (d3 - d2));
-                gy = A * pixel_scale(lvl.x, dm.align) * ((1.f - fx) * (d2 - d0) + fx * (d3 - d1));
+                float sx = pixel_scale(lvl.y, dm.align), sy = pixel_scale(lvl.x, dm.align);
+                if (dm.loc_div) {  // d loc / d offset = 1 / (W, H)
+                    sx /= (float)lvl.y;
+                    sy /= (float)lvl.x;
+                }
+                gx = A * sx * ((1.f - fy) * (d1 - d0) + fy * (d3 - d2));
+                gy = A * sy * ((1.f - fx) * (d2 - d0) + fx * (d3 - d1));
             }
             grad_attn[p] = ga;
             reinterpret_cast<float2 *>(grad_loc)[p] = make_float2(gx, gy);
@@ -1024,6 +1093,83 @@ __global__ void __launch_bounds__(kThreads) fill_zero_kernel(float4 *__restrict_
 }
 
 // ---------------------------------------------------------------------------
+// fused prologue, backward side
+// fused_prologue_kernel: the locations and weights of every point, written
+//    to the workspace for the backward pipeline (the same arithmetic as the
+//    fused forward).  Workgroup = kProItems consecutive items (b, q, m).
+// fused_epilogue_kernel: grad_logits = A * (grad_A - sum over the softmax
+//    group of A * grad_A), in place over grad_A; and, when asked for,
+//    grad_ref[b, q, l] = sum over heads and points of the location gradient
+//    (the offset gradient times (W_l, H_l)).
+// ---------------------------------------------------------------------------
+constexpr int kProItems = 64;
+
+__global__ void __launch_bounds__(kThreads)
+fused_prologue_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ starts,
+                      Prologue pr, float *__restrict__ loc, float *__restrict__ attn,
+                      int64_t items, Dims dm) {
+    __shared__ LevelLds s_lv;
+    extern __shared__ __align__(16) unsigned char smem[];
+    float2 *s_st = reinterpret_cast<float2 *>(smem);  // [kProItems * groups]
+    stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, 0x7fffffff);
+    const int M = dm.M, K = dm.K, L = dm.L, LK = L * K;
+    const int ng = pr.per_level ? L : 1;
+    const int64_t blocks = (items + kProItems - 1) / kProItems;
+    for (int64_t blk = blockIdx.x; blk < blocks; blk += gridDim.x) {
+        if (blk != (int64_t)blockIdx.x) __syncthreads();  // s_st is reused
+        const int64_t item0 = blk * kProItems;
+        const int nitems = (int)min((int64_t)kProItems, items - item0);
+        const size_t pt0 = (size_t)item0 * LK;
+        stage_softmax_stats(s_st, pr, pt0, nitems, L, K);
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < nitems * LK; idx += kThreads) {
+            const int i1 = idx / LK, j = idx - i1 * LK, l = j / K;
+            const size_t p = pt0 + idx;
+            const size_t bq = (size_t)(item0 + i1) / M;
+            const float2 r = reinterpret_cast<const float2 *>(pr.ref)[bq * L + l];
+            reinterpret_cast<float2 *>(loc)[p] =
+                prologue_location(r, reinterpret_cast<const float2 *>(pr.off)[p], s_lv.lvl[l]);
+            const float2 st = s_st[i1 * ng + (pr.per_level ? l : 0)];
+            attn[p] = expf(pr.logits[p] - st.x) * st.y;
+        }
+    }
+}
+
+__global__ void __launch_bounds__(kThreads)
+fused_epilogue_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ starts,
+                      const float *__restrict__ attn, float *__restrict__ grad_logits,
+                      const float *__restrict__ grad_off, float *__restrict__ grad_ref,
+                      int per_level, int64_t groups, int64_t refs, Dims dm) {
+    __shared__ LevelLds s_lv;
+    stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, 0x7fffffff);
+    const int M = dm.M, K = dm.K, L = dm.L, LK = L * K;
+    const int gs = per_level ? K : LK;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    const int64_t t0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    for (int64_t u = t0; u < groups; u += stride) {
+        const size_t p0 = (size_t)u * gs;  // the groups tile the points in order
+        float s = 0.f;
+        for (int j = 0; j < gs; ++j) s = __builtin_fmaf(attn[p0 + j], grad_logits[p0 + j], s);
+        for (int j = 0; j < gs; ++j) grad_logits[p0 + j] = attn[p0 + j] * (grad_logits[p0 + j] - s);
+    }
+    if (!grad_ref) return;
+    for (int64_t u = t0; u < refs; u += stride) {
+        const int64_t bq = u / L;
+        const int l = (int)(u - bq * L);
+        const int4 lvl = s_lv.lvl[l];
+        const float2 *g = reinterpret_cast<const float2 *>(grad_off) + ((size_t)bq * M * L + l) * K;
+        float gx = 0.f, gy = 0.f;
+        for (int m = 0; m < M; ++m)
+            for (int k = 0; k < K; ++k) {
+                const float2 v = g[(size_t)m * LK + k];
+                gx += v.x;
+                gy += v.y;
+            }
+        reinterpret_cast<float2 *>(grad_ref)[u] = make_float2(gx * (float)lvl.y, gy * (float)lvl.x);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 thread_local int g_last_hip_error = 0;
@@ -1091,11 +1237,12 @@ struct Launch {
     size_t lds;
 };
 
-Launch plan(int64_t D, int64_t L, int64_t K, int bytes_per_point) {
+// `reserve`: LDS bytes taken from the point-table budget for other uses.
+Launch plan(int64_t D, int64_t L, int64_t K, int bytes_per_point, int reserve = 0) {
     Launch p;
     p.ipb = (int)(kThreads / (D / 4));
     const int lk = (int)(L * K);
-    int pc = kSetupLdsBytes / (p.ipb * bytes_per_point) - 2;
+    int pc = (kSetupLdsBytes - reserve) / (p.ipb * bytes_per_point) - 2;
     pc = pc < 1 ? 1 : pc;
     p.pc = pc < lk ? pc : lk;
     p.ps = p.pc + ((p.pc % 2 == 0) ? 1 : 2);
@@ -1124,11 +1271,19 @@ int64_t batch_chunk(int64_t per_batch, int64_t B) {
     return c < B ? c : B;
 }
 
+// pr == nullptr: locations and weights from loc / attn; otherwise from the
+// prologue inputs (loc and attn unused).
 template <int D, typename VT>
 msda_status launch_fwd(const void *value, const int64_t *shapes, const int64_t *starts,
-                       const float *loc, const float *attn, float *out, int64_t B, int64_t Nv,
-                       int64_t Nq, int64_t M, int64_t L, int64_t K, bool align, hipStream_t s) {
-    const Launch p = plan(D, L, K, 32);
+                       const float *loc, const float *attn, const Prologue *pr, float *out,
+                       int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t L, int64_t K,
+                       bool align, hipStream_t s) {
+    const int ipb = (int)(kThreads / (D / 4));
+    const int ng = pr ? (pr->per_level ? (int)L : 1) : 0;
+    const int st_bytes = ipb * ng * (int)sizeof(float2);  // softmax stats per (item, group)
+    const Launch p = plan(D, L, K, 32, st_bytes);
+    const size_t lds = p.lds + (size_t)st_bytes;
+    const Prologue prv = pr ? *pr : Prologue{nullptr, nullptr, nullptr, 0};
     const int64_t items = Nq * M;
     const int64_t gx = (items + p.ipb - 1) / p.ipb;
     const int64_t bchunk = batch_chunk(gx, B);
@@ -1136,9 +1291,15 @@ msda_status launch_fwd(const void *value, const int64_t *shapes, const int64_t *
         const int64_t nb = (B - b0) < bchunk ? (B - b0) : bchunk;
         Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, p.pc, p.ps, (int)b0, (int)gx, 0, 0};
         dm.align = align ? 1 : 0;
-        hipLaunchKernelGGL((msda_fwd_kernel<D, VT>), dim3((unsigned)(gx * nb)), dim3(kThreads),
-                           p.lds, s, static_cast<const VT *>(value), shapes, starts, loc, attn,
-                           out, dm);
+        const dim3 grid((unsigned)(gx * nb));
+        if (pr)
+            hipLaunchKernelGGL((msda_fwd_kernel<D, VT, true>), grid, dim3(kThreads), lds, s,
+                               static_cast<const VT *>(value), shapes, starts, loc, attn, prv,
+                               out, dm);
+        else
+            hipLaunchKernelGGL((msda_fwd_kernel<D, VT, false>), grid, dim3(kThreads), lds, s,
+                               static_cast<const VT *>(value), shapes, starts, loc, attn, prv,
+                               out, dm);
         msda_status st = hip_status(hipGetLastError());
         if (st != MSDA_OK) return st;
     }
@@ -1211,7 +1372,7 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
                        const float *loc, const float *attn, const float *gout, float *gval,
                        float *gloc, float *gattn, int64_t B, int64_t Nv, int64_t Nq, int64_t M,
                        int64_t L, int64_t K, const WorkLayout &wl, unsigned char *ws,
-                       bool accumulate, bool align, const Exec &ex) {
+                       bool accumulate, bool align, bool loc_div, const Exec &ex) {
     const hipStream_t s = ex.s;
     Work w;
     w.counts = reinterpret_cast<uint32_t *>(ws + wl.off_counts);
@@ -1242,6 +1403,7 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
         Dims d2{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, p.pc, p.ps, (int)b0, (int)gq, 0, 0};
         d2.nblocks = (int)grid;
         d2.align = align ? 1 : 0;
+        d2.loc_div = loc_div ? 1 : 0;
         // a few workgroups per CU suffice for this gather-bound kernel, and leave
         // room for the grad_value kernels running beside it
         const unsigned g = grid > (unsigned)kDotsGrid ? (unsigned)kDotsGrid : grid;
@@ -1310,13 +1472,13 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
 
 template <typename VT>
 msda_status dispatch_fwd(int64_t D, const void *value, const int64_t *shapes,
-                         const int64_t *starts, const float *loc, const float *attn, float *out,
-                         int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t L, int64_t K,
-                         bool align, hipStream_t s) {
+                         const int64_t *starts, const float *loc, const float *attn,
+                         const Prologue *pr, float *out, int64_t B, int64_t Nv, int64_t Nq,
+                         int64_t M, int64_t L, int64_t K, bool align, hipStream_t s) {
 #define MSDA_FWD_CASE(DD)                                                                     \
     case DD:                                                                                  \
-        return launch_fwd<DD, VT>(value, shapes, starts, loc, attn, out, B, Nv, Nq, M, L, K,   \
-                                  align, s);
+        return launch_fwd<DD, VT>(value, shapes, starts, loc, attn, pr, out, B, Nv, Nq, M, L,  \
+                                  K, align, s);
     switch (D) {
         MSDA_FWD_CASE(4)
         MSDA_FWD_CASE(8)
@@ -1336,11 +1498,11 @@ msda_status dispatch_bwd(int64_t D, const void *value, const int64_t *shapes,
                          const float *gout, float *gval, float *gloc, float *gattn, int64_t B,
                          int64_t Nv, int64_t Nq, int64_t M, int64_t L, int64_t K,
                          const WorkLayout &wl, unsigned char *ws, bool acc, bool align,
-                         const Exec &ex) {
+                         bool loc_div, const Exec &ex) {
 #define MSDA_BWD_CASE(DD)                                                                      \
     case DD:                                                                                   \
         return launch_bwd<DD, VT>(value, shapes, starts, loc, attn, gout, gval, gloc, gattn, B, \
-                                  Nv, Nq, M, L, K, wl, ws, acc, align, ex);
+                                  Nv, Nq, M, L, K, wl, ws, acc, align, loc_div, ex);
     switch (D) {
         MSDA_BWD_CASE(4)
         MSDA_BWD_CASE(8)
@@ -1374,9 +1536,34 @@ msda_status msda_forward(const void *value, int value_dtype, const int64_t *spat
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (value_dtype == MSDA_F32)
         return dispatch_fwd<float>(D, value, spatial_shapes, level_start_index, sampling_loc,
-                                   attn_weight, out, B, Nv, Nq, M, L, K, align, s);
+                                   attn_weight, nullptr, out, B, Nv, Nq, M, L, K, align, s);
     return dispatch_fwd<uint16_t>(D, value, spatial_shapes, level_start_index, sampling_loc,
-                                  attn_weight, out, B, Nv, Nq, M, L, K, align, s);
+                                  attn_weight, nullptr, out, B, Nv, Nq, M, L, K, align, s);
+}
+
+msda_status msda_forward_fused(const void *value, int value_dtype,
+                               const int64_t *spatial_shapes, const int64_t *level_start_index,
+                               const float *reference_points, const float *sampling_offsets,
+                               const float *attn_logits, float *out, int64_t B, int64_t Nv,
+                               int64_t Nq, int64_t M, int64_t D, int64_t L, int64_t K,
+                               uint32_t flags, void *stream) {
+    msda_status st = check_sizes(value_dtype, B, Nv, Nq, M, D, L, K);
+    if (st != MSDA_OK) return st;
+    if (flags & ~(MSDA_ALIGN_CORNERS | MSDA_SOFTMAX_PER_LEVEL)) return MSDA_ERR_UNSUPPORTED;
+    const bool align = (flags & MSDA_ALIGN_CORNERS) != 0;
+    if (B == 0 || Nq == 0) return MSDA_OK;
+    if (Nv < 1) return MSDA_ERR_SHAPE;
+    if (!value || !spatial_shapes || !level_start_index || !reference_points ||
+        !sampling_offsets || !attn_logits || !out)
+        return MSDA_ERR_NULL;
+    const Prologue pr{reference_points, sampling_offsets, attn_logits,
+                      (flags & MSDA_SOFTMAX_PER_LEVEL) ? 1 : 0};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (value_dtype == MSDA_F32)
+        return dispatch_fwd<float>(D, value, spatial_shapes, level_start_index, nullptr, nullptr,
+                                   &pr, out, B, Nv, Nq, M, L, K, align, s);
+    return dispatch_fwd<uint16_t>(D, value, spatial_shapes, level_start_index, nullptr, nullptr,
+                                  &pr, out, B, Nv, Nq, M, L, K, align, s);
 }
 
 size_t msda_backward_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
@@ -1396,7 +1583,7 @@ msda_status backward_impl(const void *value, int value_dtype, const int64_t *spa
                           float *grad_sampling_loc, float *grad_attn_weight, int64_t B,
                           int64_t Nv, int64_t Nq, int64_t M, int64_t D, int64_t L, int64_t K,
                           void *workspace, size_t workspace_bytes, uint32_t flags,
-                          hipStream_t s, hipEvent_t *ev) {
+                          bool loc_div, hipStream_t s, hipEvent_t *ev) {
     msda_status st = check_sizes(value_dtype, B, Nv, Nq, M, D, L, K);
     if (st != MSDA_OK) return st;
     if (flags & ~(MSDA_BWD_ACCUMULATE | MSDA_ALIGN_CORNERS)) return MSDA_ERR_UNSUPPORTED;
@@ -1465,10 +1652,104 @@ msda_status backward_impl(const void *value, int value_dtype, const int64_t *spa
     if (value_dtype == MSDA_F32)
         return dispatch_bwd<float>(D, value, spatial_shapes, level_start_index, sampling_loc,
                                    attn_weight, grad_out, grad_value, grad_sampling_loc,
-                                   grad_attn_weight, B, Nv, Nq, M, L, K, wl, ws, acc, align, ex);
+                                   grad_attn_weight, B, Nv, Nq, M, L, K, wl, ws, acc, align,
+                                   loc_div, ex);
     return dispatch_bwd<uint16_t>(D, value, spatial_shapes, level_start_index, sampling_loc,
                                   attn_weight, grad_out, grad_value, grad_sampling_loc,
-                                  grad_attn_weight, B, Nv, Nq, M, L, K, wl, ws, acc, align, ex);
+                                  grad_attn_weight, B, Nv, Nq, M, L, K, wl, ws, acc, align,
+                                  loc_div, ex);
+}
+
+// Workspace of the fused backward: the core's, then the locations [pts][2]
+// and weights [pts] the prologue writes.
+struct FusedLayout {
+    size_t core, off_loc, off_attn, bytes;
+};
+
+FusedLayout fused_layout(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t L, int64_t K) {
+    auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t pts = (size_t)(B * Nq * M * L * K);
+    FusedLayout f;
+    f.core = work_layout(B, Nv, Nq, M, L, K).bytes;
+    f.off_loc = f.core;
+    f.off_attn = align(f.off_loc + 8 * pts);
+    f.bytes = align(f.off_attn + 4 * pts);
+    return f;
+}
+
+msda_status backward_fused_impl(const void *value, int value_dtype, const int64_t *shapes,
+                                const int64_t *starts, const float *ref, const float *off,
+                                const float *logits, const float *grad_out, float *grad_value,
+                                float *grad_off, float *grad_logits, float *grad_ref, int64_t B,
+                                int64_t Nv, int64_t Nq, int64_t M, int64_t D, int64_t L,
+                                int64_t K, void *workspace, size_t workspace_bytes,
+                                uint32_t flags, hipStream_t s, hipEvent_t *ev) {
+    msda_status st = check_sizes(value_dtype, B, Nv, Nq, M, D, L, K);
+    if (st != MSDA_OK) return st;
+    if (flags & ~(MSDA_BWD_ACCUMULATE | MSDA_ALIGN_CORNERS | MSDA_SOFTMAX_PER_LEVEL))
+        return MSDA_ERR_UNSUPPORTED;
+    const bool per_level = (flags & MSDA_SOFTMAX_PER_LEVEL) != 0;
+    const uint32_t core_flags = flags & ~MSDA_SOFTMAX_PER_LEVEL;
+    const bool work = B > 0 && Nq > 0;
+    auto stamp = [&](int i, bool end) {
+        if (ev && ev[2 * i + (end ? 1 : 0)]) (void)hipEventRecord(ev[2 * i + (end ? 1 : 0)], s);
+    };
+    if (!work) {
+        stamp(MSDA_BWD_STAGES, false);
+        stamp(MSDA_BWD_STAGES, true);
+        st = backward_impl(value, value_dtype, shapes, starts, nullptr, nullptr, grad_out,
+                           grad_value, nullptr, nullptr, B, Nv, Nq, M, D, L, K, workspace,
+                           workspace_bytes, core_flags, true, s, ev);
+        stamp(MSDA_BWD_STAGES + 1, false);
+        stamp(MSDA_BWD_STAGES + 1, true);
+        return st;
+    }
+    if (Nv < 1) return MSDA_ERR_SHAPE;
+    if (!value || !shapes || !starts || !ref || !off || !logits || !grad_out || !grad_value ||
+        !grad_off || !grad_logits)
+        return MSDA_ERR_NULL;
+    if (!workspace) return MSDA_ERR_NULL;
+    const FusedLayout fl = fused_layout(B, Nv, Nq, M, L, K);
+    if (workspace_bytes < fl.bytes) return MSDA_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return MSDA_ERR_WORKSPACE;
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    float *loc = reinterpret_cast<float *>(ws + fl.off_loc);
+    float *attn = reinterpret_cast<float *>(ws + fl.off_attn);
+    const Prologue pr{ref, off, logits, per_level ? 1 : 0};
+    Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, 0, 0, 0, 0, 0, 0};
+    const int64_t items = B * Nq * M;
+
+    stamp(MSDA_BWD_STAGES, false);
+    {
+        const int64_t blocks = (items + kProItems - 1) / kProItems;
+        const unsigned grid = (unsigned)(blocks < (1 << 20) ? blocks : (1 << 20));
+        const size_t lds = (size_t)kProItems * (per_level ? L : 1) * sizeof(float2);
+        hipLaunchKernelGGL(fused_prologue_kernel, dim3(grid), dim3(kThreads), lds, s, shapes,
+                           starts, pr, loc, attn, items, dm);
+        st = hip_status(hipGetLastError());
+        if (st != MSDA_OK) return st;
+    }
+    stamp(MSDA_BWD_STAGES, true);
+
+    st = backward_impl(value, value_dtype, shapes, starts, loc, attn, grad_out, grad_value,
+                       grad_off, grad_logits, B, Nv, Nq, M, D, L, K, ws, fl.core, core_flags,
+                       true, s, ev);
+    if (st != MSDA_OK) return st;
+
+    stamp(MSDA_BWD_STAGES + 1, false);
+    {
+        const int64_t groups = items * (per_level ? L : 1);
+        const int64_t refs = grad_ref ? B * Nq * L : 0;
+        const int64_t units = groups > refs ? groups : refs;
+        int64_t blocks = (units + kThreads - 1) / kThreads;
+        blocks = blocks < (1 << 16) ? blocks : (1 << 16);
+        hipLaunchKernelGGL(fused_epilogue_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s,
+                           shapes, starts, attn, grad_logits, grad_off, grad_ref,
+                           per_level ? 1 : 0, groups, refs, dm);
+        st = hip_status(hipGetLastError());
+    }
+    stamp(MSDA_BWD_STAGES + 1, true);
+    return st;
 }
 
 }  // namespace
@@ -1484,7 +1765,7 @@ msda_status msda_backward(const void *value, int value_dtype, const int64_t *spa
                           void *stream) {
     return backward_impl(value, value_dtype, spatial_shapes, level_start_index, sampling_loc,
                          attn_weight, grad_out, grad_value, grad_sampling_loc, grad_attn_weight,
-                         B, Nv, Nq, M, D, L, K, workspace, workspace_bytes, flags,
+                         B, Nv, Nq, M, D, L, K, workspace, workspace_bytes, flags, false,
                          static_cast<hipStream_t>(stream), nullptr);
 }
 
@@ -1501,8 +1782,36 @@ msda_status msda_backward_events(const void *value, int value_dtype,
     for (int i = 0; i < 2 * MSDA_BWD_STAGES; ++i) ev[i] = static_cast<hipEvent_t>(events[i]);
     return backward_impl(value, value_dtype, spatial_shapes, level_start_index, sampling_loc,
                          attn_weight, grad_out, grad_value, grad_sampling_loc, grad_attn_weight,
-                         B, Nv, Nq, M, D, L, K, workspace, workspace_bytes, flags,
+                         B, Nv, Nq, M, D, L, K, workspace, workspace_bytes, flags, false,
                          static_cast<hipStream_t>(stream), ev);
+}
+
+size_t msda_backward_fused_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int64_t M,
+                                          int64_t D, int64_t L, int64_t K) {
+    if (check_sizes(MSDA_F32, B, Nv, Nq, M, D, L, K) != MSDA_OK) return 0;
+    if (B == 0 || Nq == 0) return 0;
+    return fused_layout(B, Nv, Nq, M, L, K).bytes;
+}
+
+msda_status msda_backward_fused(const void *value, int value_dtype,
+                                const int64_t *spatial_shapes, const int64_t *level_start_index,
+                                const float *reference_points, const float *sampling_offsets,
+                                const float *attn_logits, const float *grad_out,
+                                float *grad_value, float *grad_sampling_offsets,
+                                float *grad_attn_logits, float *grad_reference_points, int64_t B,
+                                int64_t Nv, int64_t Nq, int64_t M, int64_t D, int64_t L,
+                                int64_t K, void *workspace, size_t workspace_bytes,
+                                uint32_t flags, void *stream, void *const *events) {
+    hipEvent_t ev[2 * MSDA_BWD_FUSED_STAGES];
+    if (events)
+        for (int i = 0; i < 2 * MSDA_BWD_FUSED_STAGES; ++i)
+            ev[i] = static_cast<hipEvent_t>(events[i]);
+    return backward_fused_impl(value, value_dtype, spatial_shapes, level_start_index,
+                               reference_points, sampling_offsets, attn_logits, grad_out,
+                               grad_value, grad_sampling_offsets, grad_attn_logits,
+                               grad_reference_points, B, Nv, Nq, M, D, L, K, workspace,
+                               workspace_bytes, flags, static_cast<hipStream_t>(stream),
+                               events ? ev : nullptr);
 }
 
 msda_status msda_validate_host(const int64_t *spatial_shapes_host, const int64_t *level_start_host,

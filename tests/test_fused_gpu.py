@@ -1,0 +1,195 @@
+"""GPU parity of the fused prologue entry points (msda_forward_fused,
+msda_backward_fused) against the CPU oracle (oracle/fused.py on top of the
+core oracle).  Same metric and bars as the core: max|x - r| / max|r|, fp32
+forward 1e-5, backward 1e-4; bf16 value compared with the oracle run on the
+bf16-rounded values at the fp32 bars."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.fused as ofused
+import workloads
+from oracle_pins import max_rel
+
+pytestmark = pytest.mark.gpu
+
+FWD_TOL = 1e-5
+BWD_TOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def msda():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the gpu tests must run on an MI355X")
+    import scale_deformable_attention_04_amd as m
+    m.load()
+    return m
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def dev_inputs(w: workloads.FusedWorkload, bf16=False):
+    d = torch.device("cuda:0")
+    if bf16:
+        value = torch.from_numpy(w.value_bf16.view(np.int16).copy()).view(torch.bfloat16).to(d)
+    else:
+        value = torch.from_numpy(w.value).to(d)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(d)
+    return dict(value=value, spatial_shapes=t(w.spatial_shapes),
+                level_start_index=t(w.level_start_index), reference_points=t(w.reference_points),
+                sampling_offsets=t(w.sampling_offsets), attn_logits=t(w.attn_logits))
+
+
+def _mode(align):
+    return oracle.SPEC | (oracle.ALIGN if align else 0)
+
+
+def _oracle_args(w):
+    return (w.value, w.spatial_shapes, w.level_start_index, w.reference_points,
+            w.sampling_offsets, w.attn_logits)
+
+
+def check(m, w, per_level=False, align=False, bf16=False, backward=True, need_grad_ref=True):
+    x = dev_inputs(w, bf16)
+    out = m.forward_fused(**x, per_level=per_level, align_corners=align)
+    torch.cuda.synchronize()
+    r_out = ofused.forward(*_oracle_args(w), per_level=per_level, mode=_mode(align))
+    e = max_rel(out.cpu().numpy(), r_out.reshape(out.shape))
+    assert e <= FWD_TOL, f"{w.name}: fused forward max rel {e:.3e}"
+    if not backward:
+        return
+    g = torch.from_numpy(w.grad_out).cuda()
+    gv, goff, gz, gref = m.backward_fused(**x, grad_out=g, per_level=per_level,
+                                          align_corners=align, need_grad_ref=need_grad_ref)
+    torch.cuda.synchronize()
+    rv, roff, rz, rref = ofused.backward(*_oracle_args(w), w.grad_out, per_level=per_level,
+                                         mode=_mode(align))
+    got = [("grad_value", gv, rv), ("grad_sampling_offsets", goff, roff),
+           ("grad_attn_logits", gz, rz)]
+    if need_grad_ref:
+        got.append(("grad_reference_points", gref, rref))
+    else:
+        assert gref is None
+    for name, a, r in got:
+        e = max_rel(a.cpu().numpy(), r)
+        assert e <= BWD_TOL, f"{w.name}: {name} max rel {e:.3e}"
+
+
+SHAPES = ((13, 17), (7, 9), (3, 4))
+
+
+@pytest.mark.parametrize("D", [4, 8, 16, 32, 64, 256])
+@pytest.mark.parametrize("per_level", [False, True])
+def test_fused_random_shapes(msda, D, per_level):
+    _say(f"fused D={D} per_level={per_level}")
+    w = workloads.fused_case(100 + D, 2, SHAPES, 37, 3, D, 3, ref_low=-0.05, ref_high=1.05)
+    check(msda, w, per_level=per_level)
+
+
+@pytest.mark.parametrize("per_level,align", [(False, True), (True, True)])
+def test_fused_align_corners(msda, per_level, align):
+    _say(f"fused align per_level={per_level}")
+    w = workloads.fused_case(201, 2, SHAPES, 29, 2, 32, 4)
+    check(msda, w, per_level=per_level, align=align)
+
+
+@pytest.mark.parametrize("per_level", [False, True])
+def test_fused_bf16(msda, per_level):
+    _say(f"fused bf16 per_level={per_level}")
+    w = workloads.fused_case(301, 2, SHAPES, 41, 4, 32, 4, bf16=True)
+    check(msda, w, per_level=per_level, bf16=True)
+
+
+def test_fused_large_logits_and_no_ref_grad(msda):
+    # logits N(0, 30): the softmax must subtract its maximum
+    _say("fused large logits, grad_ref not requested")
+    w = workloads.fused_case(401, 1, SHAPES, 23, 2, 16, 5, logit_scale=30.0)
+    check(msda, w, per_level=False, need_grad_ref=False)
+    check(msda, w, per_level=True)
+
+
+def test_fused_sixteen_levels_small_head(msda):
+    # D = 4: 256 items per workgroup, the point tables are processed in chunks
+    # of one point next to the per-level softmax statistics
+    _say("fused L=16 D=4 per_level")
+    shapes = tuple((1 + (l % 5), 2 + (l % 3)) for l in range(16))
+    w = workloads.fused_case(501, 2, shapes, 19, 2, 4, 2)
+    check(msda, w, per_level=True)
+    check(msda, w, per_level=False)
+
+
+def test_fused_accumulate(msda):
+    _say("fused accumulate")
+    w = workloads.fused_case(601, 1, SHAPES, 17, 2, 8, 3)
+    x = dev_inputs(w)
+    g = torch.from_numpy(w.grad_out).cuda()
+    base = torch.randn(tuple(w.value.shape), generator=torch.Generator().manual_seed(3)).cuda()
+    gv = base.clone()
+    msda.backward_fused(**x, grad_out=g, grad_value=gv, accumulate=True)
+    torch.cuda.synchronize()
+    rv, _, _, _ = ofused.backward(*_oracle_args(w), w.grad_out)
+    e = max_rel(gv.cpu().numpy(), base.cpu().numpy() + rv)
+    assert e <= BWD_TOL
+
+
+def test_fused_empty(msda):
+    _say("fused empty")
+    w = workloads.fused_case(701, 1, SHAPES, 0, 2, 8, 3)
+    x = dev_inputs(w)
+    out = msda.forward_fused(**x)
+    assert out.shape == (1, 0, 16)
+    g = torch.zeros((1, 0, 16), device="cuda")
+    gv, goff, gz, gref = msda.backward_fused(**x, grad_out=g)
+    torch.cuda.synchronize()
+    assert float(gv.abs().max()) == 0.0 and goff.numel() == 0 and gref.numel() == 0
+
+
+def test_fused_autograd_function(msda):
+    _say("fused autograd")
+    w = workloads.fused_case(801, 2, SHAPES, 21, 2, 16, 3)
+    x = dev_inputs(w)
+    leaves = {k: x[k].clone().requires_grad_(True)
+              for k in ("value", "reference_points", "sampling_offsets", "attn_logits")}
+    out = msda.ms_deform_attn_fused(leaves["value"], x["spatial_shapes"],
+                                    x["level_start_index"], leaves["reference_points"],
+                                    leaves["sampling_offsets"], leaves["attn_logits"],
+                                    per_level=True)
+    out.backward(torch.from_numpy(w.grad_out).cuda())
+    torch.cuda.synchronize()
+    rv, roff, rz, rref = ofused.backward(*_oracle_args(w), w.grad_out, per_level=True)
+    for name, r in (("value", rv), ("sampling_offsets", roff), ("attn_logits", rz),
+                    ("reference_points", rref)):
+        e = max_rel(leaves[name].grad.cpu().numpy(), r)
+        assert e <= BWD_TOL, f"{name}: {e:.3e}"
+
+
+def test_fused_stage_events(msda):
+    _say("fused stage events")
+    w = workloads.fused_case(901, 2, SHAPES, 33, 2, 32, 4)
+    x = dev_inputs(w)
+    g = torch.from_numpy(w.grad_out).cuda()
+    ev = msda.make_events(fused=True)
+    gv, goff, gz, gref = msda.backward_fused(**x, grad_out=g, events=ev)
+    torch.cuda.synchronize()
+    t = msda.stage_times(ev)
+    assert len(t) == len(msda.BWD_FUSED_STAGES) and all(v is not None and v >= 0 for v in t)
+    rv, roff, rz, rref = ofused.backward(*_oracle_args(w), w.grad_out)
+    assert max_rel(gz.cpu().numpy(), rz) <= BWD_TOL
+
+
+def test_fused_encoder(msda):
+    # the encoder-shape workload (B=2, 22,223 queries on the DETR levels,
+    # M=8, D=32, L=4, K=4) in the fused input form, forward and backward in full
+    _say("fused encoder B=2 Nq=Nv=22223")
+    w = workloads.make_fused(3)
+    check(msda, w, per_level=False)
+
+
+def test_fused_train_bf16_per_level(msda):
+    # B=4, K=8, bf16 value; the per-level softmax of the first page's text
+    _say("fused train_bf16 B=4 K=8 per_level")
+    w = workloads.make_fused(4)
+    check(msda, w, per_level=True, bf16=True)
