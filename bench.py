@@ -21,7 +21,8 @@ its average duration there give "achieved", against the 8 TB/s HBM peak.
 "traffic" is the HBM byte count rocprofv3 measured for that kernel
 (profiles/traffic.json), when it was taken on the current kernel source.
 "cpu_baseline" times the CPU oracle on the same workload on this host's
-cores.  --extra adds the decoder and bf16 training shapes.
+cores.  --extra adds the decoder and bf16 training shapes and the fused
+prologue (reference points + pixel offsets + logits) at the encoder shape.
 """
 from __future__ import annotations
 
@@ -169,6 +170,78 @@ def measure_config(torch, msda, w, bf16, reps, flush, label):
     return res, x, g, bm
 
 
+def measure_fused(torch, msda, reps, flush):
+    """The fused prologue at the encoder shape (reference points, pixel
+    offsets, logits): its forward and backward kernels, and one fwd+bwd
+    autograd step of it against the same step with the prologue written in
+    torch ops around the core entry points."""
+    import workloads
+    w = workloads.make_fused(3)
+    d = torch.device("cuda")
+    t = lambda a: torch.from_numpy(a).to(d)
+    x = dict(value=t(w.value), spatial_shapes=t(w.spatial_shapes),
+             level_start_index=t(w.level_start_index), reference_points=t(w.reference_points),
+             sampling_offsets=t(w.sampling_offsets), attn_logits=t(w.attn_logits))
+    g = t(w.grad_out)
+    dims = w.dims
+    B, Nq, M, L, K = dims["B"], dims["Nq"], dims["M"], dims["L"], dims["K"]
+    out = torch.empty(B, Nq, M * dims["D"], device=d)
+    fwd = lambda: msda.forward_fused(**x, out=out, validate=False)
+    for _ in range(3):
+        fwd()
+    res = {"points": w.points, "forward": {"us_cold": time_forward(torch, fwd, reps, flush),
+                                           "us_warm": time_forward(torch, fwd, reps, None)}}
+    gv = torch.empty(tuple(w.value.shape), dtype=torch.float32, device=d)
+    for _ in range(3):
+        msda.backward_fused(**x, grad_out=g, grad_value=gv, validate=False)
+    sets = [msda.make_events(fused=True) for _ in range(reps)]
+    for ev in sets:
+        msda.backward_fused(**x, grad_out=g, grad_value=gv, validate=False, events=ev)
+    torch.cuda.synchronize()
+    acc = [0.0] * len(msda.BWD_FUSED_STAGES)
+    for ev in sets:
+        acc = [a + b for a, b in zip(acc, msda.stage_times(ev))]
+    stages = {k: v / reps for k, v in zip(msda.BWD_FUSED_STAGES, acc)}
+    res["backward"] = {"us_warm": time_forward(
+        torch, lambda: msda.backward_fused(**x, grad_out=g, grad_value=gv, validate=False),
+        reps, None), "stages_us_warm": stages}
+    # a training step: the forward stores the locations and weights, the
+    # backward reads them instead of recomputing them
+    saved = msda.forward_fused(**x, validate=False, save=True)[1:]
+    res["forward_saving"] = {"us_warm": time_forward(
+        torch, lambda: msda.forward_fused(**x, validate=False, save=True), reps, None)}
+    res["backward_saved"] = {"us_warm": time_forward(
+        torch, lambda: msda.backward_fused(**x, grad_out=g, grad_value=gv, validate=False,
+                                           saved=saved), reps, None)}
+
+    leaves = {k: x[k].clone().requires_grad_(True)
+              for k in ("value", "reference_points", "sampling_offsets", "attn_logits")}
+    wh = torch.tensor([[W, H] for H, W in w.spatial_shapes.tolist()], dtype=torch.float32,
+                      device=d)
+
+    def fused_step():
+        o = msda.ms_deform_attn_fused(leaves["value"], x["spatial_shapes"],
+                                      x["level_start_index"], leaves["reference_points"],
+                                      leaves["sampling_offsets"], leaves["attn_logits"])
+        o.backward(g)
+
+    def unfused_step():
+        loc = (leaves["reference_points"][:, :, None, :, None, :] +
+               leaves["sampling_offsets"] / wh[None, None, None, :, None, :])
+        a = torch.softmax(leaves["attn_logits"], dim=-1).view(B, Nq, M, L, K)
+        o = msda.ms_deform_attn(leaves["value"], x["spatial_shapes"], x["level_start_index"],
+                                loc, a)
+        o.backward(g)
+
+    for name, fn in (("autograd_step_fused_us", fused_step),
+                     ("autograd_step_torch_prologue_us", unfused_step)):
+        for _ in range(3):
+            fn()
+        res[name] = time_forward(torch, fn, reps, None)
+    log(f"fused: {json.dumps(res)}")
+    return res
+
+
 def cpu_baseline(w, min_seconds=10.0):
     import oracle
     pts = w.points
@@ -304,6 +377,7 @@ def main():
         trn, _, _, _ = measure_config(torch, msda, workloads.make(4), True, max(5, args.reps // 3),
                                       flush, "train_bf16")
         extra["train_bf16"] = trn
+        extra["fused_encoder"] = measure_fused(torch, msda, args.reps, flush)
 
     result = {
         "metric": "sampled points/s (fwd+bwd) at the DETR encoder shape",

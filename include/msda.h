@@ -213,11 +213,16 @@ msda_status msda_backward_events(const void *value, int value_dtype,
  *
  * msda_forward_fused: out is overwritten.  flags: MSDA_ALIGN_CORNERS and/or
  * MSDA_SOFTMAX_PER_LEVEL.  Errors and limits as msda_forward.
+ * sampling_loc_out [B,Nq,M,L,K,2] and attn_weight_out [B,Nq,M,L,K] (fp32) are
+ * optional (both NULL, or both given: else MSDA_ERR_NULL): when given they
+ * receive the locations and weights the forward formed, for a training step
+ * to hand to msda_backward_fused instead of having them recomputed.
  */
 msda_status msda_forward_fused(const void *value, int value_dtype,
                                const int64_t *spatial_shapes, const int64_t *level_start_index,
                                const float *reference_points, const float *sampling_offsets,
                                const float *attn_logits, float *out,
+                               float *sampling_loc_out, float *attn_weight_out,
                                int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
                                int64_t L, int64_t K, uint32_t flags, void *stream);
 
@@ -239,19 +244,26 @@ size_t msda_backward_fused_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int
  * computed, e.g. for fixed encoder reference points); every other pointer is
  * required.  flags: MSDA_BWD_ACCUMULATE, MSDA_ALIGN_CORNERS and
  * MSDA_SOFTMAX_PER_LEVEL, the last two as given to the forward.
+ * sampling_loc / attn_weight: both NULL (the locations and weights are
+ * recomputed from the raw inputs into the workspace), or both the arrays
+ * msda_forward_fused stored for these same inputs and flags (then they are
+ * read instead; anything else gives the gradients at those locations and
+ * weights, not at the raw inputs').
  * workspace: at least msda_backward_fused_workspace_size(...) bytes, 256-byte
  * aligned, as for msda_backward.
  * events: NULL, or 2 * MSDA_BWD_FUSED_STAGES caller-owned HIP events recorded
  * around the stages as msda_backward_events does (null entries skipped):
  * stages 0-6 as there, 7 the prologue (locations and weights into the
- * workspace), 8 the epilogue (logit and reference-point gradients).
+ * workspace; empty when they are passed in), 8 the epilogue (what remains of
+ * the logit and reference-point gradients; empty when nothing remains).
  * The same side stream as msda_backward is used.
  */
 #define MSDA_BWD_FUSED_STAGES (MSDA_BWD_STAGES + 2)
 msda_status msda_backward_fused(const void *value, int value_dtype,
                                 const int64_t *spatial_shapes, const int64_t *level_start_index,
                                 const float *reference_points, const float *sampling_offsets,
-                                const float *attn_logits, const float *grad_out,
+                                const float *attn_logits, const float *sampling_loc,
+                                const float *attn_weight, const float *grad_out,
                                 float *grad_value, float *grad_sampling_offsets,
                                 float *grad_attn_logits, float *grad_reference_points,
                                 int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,

@@ -61,23 +61,28 @@ class MSDeformAttnFusedFunction(torch.autograd.Function):
     @staticmethod
     def forward(ctx, value, spatial_shapes, level_start_index, reference_points,
                 sampling_offsets, attn_logits, per_level=False, align_corners=False):
-        out = forward_fused(value, spatial_shapes, level_start_index, reference_points,
+        # with a backward to come, the forward also stores the locations and
+        # weights it forms, so the backward does not recompute them
+        save = any(ctx.needs_input_grad)
+        res = forward_fused(value, spatial_shapes, level_start_index, reference_points,
                             sampling_offsets, attn_logits, per_level=per_level,
-                            align_corners=align_corners)
+                            align_corners=align_corners, save=save)
+        out, loc, attn = res if save else (res, None, None)
         ctx.save_for_backward(value, spatial_shapes, level_start_index, reference_points,
-                              sampling_offsets, attn_logits)
+                              sampling_offsets, attn_logits, loc, attn)
         ctx.per_level = per_level
         ctx.align_corners = align_corners
         return out
 
     @staticmethod
     def backward(ctx, grad_out):
-        value, ss, st, ref, off, logits = ctx.saved_tensors
+        value, ss, st, ref, off, logits, loc, attn = ctx.saved_tensors
         gv, goff, gz, gref = backward_fused(value, ss, st, ref, off, logits,
                                             grad_out.contiguous(), validate=False,
                                             need_grad_ref=ctx.needs_input_grad[3],
                                             per_level=ctx.per_level,
-                                            align_corners=ctx.align_corners)
+                                            align_corners=ctx.align_corners,
+                                            saved=None if loc is None else (loc, attn))
         return gv, None, None, gref, goff, gz, None, None
 
 

@@ -68,11 +68,11 @@ def load():
     lib.msda_backward_events.restype = ci
     lib.msda_backward_workspace_size.argtypes = [i64] * 7
     lib.msda_backward_workspace_size.restype = ctypes.c_size_t
-    lib.msda_forward_fused.argtypes = [p, ci, p, p, p, p, p, p] + [i64] * 7 + [u32, p]
+    lib.msda_forward_fused.argtypes = [p, ci, p, p, p, p, p, p, p, p] + [i64] * 7 + [u32, p]
     lib.msda_forward_fused.restype = ci
     lib.msda_backward_fused_workspace_size.argtypes = [i64] * 7
     lib.msda_backward_fused_workspace_size.restype = ctypes.c_size_t
-    lib.msda_backward_fused.argtypes = ([p, ci, p, p, p, p, p, p, p, p, p, p] + [i64] * 7 +
+    lib.msda_backward_fused.argtypes = ([p, ci, p, p, p, p, p, p, p, p, p, p, p, p] + [i64] * 7 +
                                         [p, ctypes.c_size_t, u32, p, p])
     lib.msda_backward_fused.restype = ci
     lib.msda_validate_host.argtypes = [p, p] + [i64] * 7
@@ -322,11 +322,14 @@ def forward_fused(value: torch.Tensor, spatial_shapes: torch.Tensor,
                   level_start_index: torch.Tensor, reference_points: torch.Tensor,
                   sampling_offsets: torch.Tensor, attn_logits: torch.Tensor,
                   out: Optional[torch.Tensor] = None, validate: bool = True,
-                  per_level: bool = False, align_corners: bool = False) -> torch.Tensor:
+                  per_level: bool = False, align_corners: bool = False,
+                  save: bool = False):
     """msda_forward_fused: out[B, Nq, M*D] (fp32) from reference points
     [B,Nq,L,2], pixel offsets [B,Nq,M,L,K,2] and logits [B,Nq,M,L*K].
     per_level=True normalizes the logits over each level's K points instead
-    of all L*K; align_corners as in forward()."""
+    of all L*K; align_corners as in forward().  save=True returns
+    (out, sampling_loc, attn_weight): the locations and weights it formed, to
+    pass to backward_fused(saved=...)."""
     lib = load()
     dev, (B, Nv, Nq, M, D, L, K) = _check_fused_inputs(
         value, spatial_shapes, level_start_index, reference_points, sampling_offsets,
@@ -335,16 +338,19 @@ def forward_fused(value: torch.Tensor, spatial_shapes: torch.Tensor,
         out = torch.empty((B, Nq, M * D), dtype=torch.float32, device=dev)
     else:
         _need(out, "out", torch.float32, dev, (B, Nq, M * D))
+    loc = torch.empty((B, Nq, M, L, K, 2), dtype=torch.float32, device=dev) if save else None
+    attn = torch.empty((B, Nq, M, L, K), dtype=torch.float32, device=dev) if save else None
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         rc = lib.msda_forward_fused(_ptr(value), _dtype_code(value), _ptr(spatial_shapes),
                                     _ptr(level_start_index), _ptr(reference_points),
                                     _ptr(sampling_offsets), _ptr(attn_logits), _ptr(out),
-                                    B, Nv, Nq, M, D, L, K, _fused_flags(per_level, align_corners),
+                                    _ptr(loc), _ptr(attn), B, Nv, Nq, M, D, L, K,
+                                    _fused_flags(per_level, align_corners),
                                     ctypes.c_void_p(stream))
     if rc != MSDA_OK:
         raise MSDAError(rc, "msda_forward_fused")
-    return out
+    return (out, loc, attn) if save else out
 
 
 def fused_workspace_size(B, Nv, Nq, M, D, L, K) -> int:
@@ -359,9 +365,11 @@ def backward_fused(value: torch.Tensor, spatial_shapes: torch.Tensor,
                    accumulate: bool = False, need_grad_ref: bool = True,
                    validate: bool = True, workspace: Optional[torch.Tensor] = None,
                    events: Optional[list] = None, per_level: bool = False,
-                   align_corners: bool = False):
+                   align_corners: bool = False, saved: Optional[tuple] = None):
     """msda_backward_fused: (grad_value, grad_sampling_offsets, grad_attn_logits,
     grad_reference_points or None when need_grad_ref is False).
+    saved: the (sampling_loc, attn_weight) forward_fused(save=True) returned
+    for these inputs, or None to recompute them.
     events: 2 * len(BWD_FUSED_STAGES) timing events or None (see stage_times)."""
     lib = load()
     dev, (B, Nv, Nq, M, D, L, K) = _check_fused_inputs(
@@ -374,6 +382,11 @@ def backward_fused(value: torch.Tensor, spatial_shapes: torch.Tensor,
         grad_value = torch.empty((B, Nv, M, D), dtype=torch.float32, device=dev)
     else:
         _need(grad_value, "grad_value", torch.float32, dev, (B, Nv, M, D))
+    s_loc = s_attn = None
+    if saved is not None:
+        s_loc, s_attn = saved
+        _need(s_loc, "saved sampling_loc", torch.float32, dev, (B, Nq, M, L, K, 2))
+        _need(s_attn, "saved attn_weight", torch.float32, dev, (B, Nq, M, L, K))
     g_off = torch.empty_like(sampling_offsets)
     g_logits = torch.empty_like(attn_logits)
     g_ref = torch.empty_like(reference_points) if need_grad_ref else None
@@ -389,7 +402,8 @@ def backward_fused(value: torch.Tensor, spatial_shapes: torch.Tensor,
         handles = None if events is None else _event_handles(events, len(BWD_FUSED_STAGES))
         rc = lib.msda_backward_fused(
             _ptr(value), _dtype_code(value), _ptr(spatial_shapes), _ptr(level_start_index),
-            _ptr(reference_points), _ptr(sampling_offsets), _ptr(attn_logits), _ptr(grad_out),
+            _ptr(reference_points), _ptr(sampling_offsets), _ptr(attn_logits), _ptr(s_loc),
+            _ptr(s_attn), _ptr(grad_out),
             _ptr(grad_value), _ptr(g_off), _ptr(g_logits), _ptr(g_ref), B, Nv, Nq, M, D, L, K,
             _ptr(workspace), ws_bytes, flags, stream, handles)
     if rc != MSDA_OK:

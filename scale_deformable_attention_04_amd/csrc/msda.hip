@@ -295,6 +295,7 @@ struct Dims {
     int nblocks;     // query blocks of the launch (dots kernel)
     int align;       // pixel convention: x = u*(W-1) instead of u*W - 0.5
     int loc_div;     // dots kernel: location gradients divided by (W, H) (offset gradients)
+    int softmax_run; // dots kernel: softmax backward over runs of this many points (0: none)
 };
 
 // Workspace of the backward pipeline (all 32-bit words).
@@ -318,7 +319,44 @@ struct Prologue {
     const float *off;     // [B, Nq, M, L, K, 2]
     const float *logits;  // [B, Nq, M, L * K]
     int per_level;
+    // the softmax groups are runs of a power-of-two number (<= 64) of
+    // consecutive points that the point loop hands to consecutive lanes of one
+    // wave: the group max and sum are taken with lane shuffles
+    int shfl;
+    float *loc_out;   // forward: also store the locations [pts][2] and weights
+    float *attn_out;  // [pts] it computed (for the backward), or nullptr
 };
+
+// Max / sum over aligned runs of n consecutive lanes (n a power of two <= 64);
+// every lane of a run receives the result.  The whole run must be active.
+// Within 16 lanes the partners come from DPP (lane ^ 1, lane ^ 2, then the
+// mirrored quad and half-row, which pair the partial results the same way),
+// beyond that from cross-row shuffles.
+__device__ __forceinline__ float run_max(float v, int n) {
+    if (n >= 2) v = fmaxf(v, dpp<0xB1>(v));
+    if (n >= 4) v = fmaxf(v, dpp<0x4E>(v));
+    if (n >= 8) v = fmaxf(v, dpp<0x141>(v));
+    if (n >= 16) v = fmaxf(v, dpp<0x140>(v));
+    if (n >= 32) v = fmaxf(v, __shfl_xor(v, 16, 64));
+    if (n >= 64) v = fmaxf(v, __shfl_xor(v, 32, 64));
+    return v;
+}
+
+__device__ __forceinline__ float run_sum(float v, int n) {
+    if (n >= 2) v += dpp<0xB1>(v);
+    if (n >= 4) v += dpp<0x4E>(v);
+    if (n >= 8) v += dpp<0x141>(v);
+    if (n >= 16) v += dpp<0x140>(v);
+    if (n >= 32) v += __shfl_xor(v, 16, 64);
+    if (n >= 64) v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+// Softmax weight of the point holding logit z inside its run of n lanes.
+__device__ __forceinline__ float run_softmax(float z, int n) {
+    const float e = expf(z - run_max(z, n));
+    return e / run_sum(e, n);
+}
 
 // (max, 1 / sum exp(z - max)) over the n logits at z.
 __device__ __forceinline__ float2 softmax_stats(const float *__restrict__ z, int n) {
@@ -382,8 +420,10 @@ msda_fwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
     const size_t pt0 = ((size_t)b * NqM + item0) * LK;
     const int ng = pr.per_level ? dm.L : 1;
     if constexpr (FUSED) {
-        stage_softmax_stats(s_st, pr, pt0, nitems, dm.L, K);
-        __syncthreads();
+        if (!pr.shfl) {
+            stage_softmax_stats(s_st, pr, pt0, nitems, dm.L, K);
+            __syncthreads();
+        }
     }
 
     const int it = threadIdx.x / G, c = threadIdx.x % G;
@@ -404,8 +444,17 @@ msda_fwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
                     reinterpret_cast<const float2 *>(pr.ref)[((size_t)b * dm.Nq + q) * dm.L + l];
                 uv = prologue_location(r, reinterpret_cast<const float2 *>(pr.off)[p],
                                        s_lv.lvl[l]);
-                const float2 st = s_st[i1 * ng + (pr.per_level ? l : 0)];
-                A = expf(pr.logits[p] - st.x) * st.y;
+                const float z = pr.logits[p];
+                if (pr.shfl) {  // one chunk holds whole items: runs never straddle waves
+                    A = run_softmax(z, pr.per_level ? K : LK);
+                } else {
+                    const float2 st = s_st[i1 * ng + (pr.per_level ? l : 0)];
+                    A = expf(z - st.x) * st.y;
+                }
+                if (pr.loc_out) {
+                    reinterpret_cast<float2 *>(pr.loc_out)[p] = uv;
+                    pr.attn_out[p] = A;
+                }
             } else {
                 uv = reinterpret_cast<const float2 *>(loc)[p];
                 A = attn[p];
@@ -456,7 +505,8 @@ __global__ void __launch_bounds__(kThreads)
 bwd_dots_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes,
                 const int64_t *__restrict__ starts, const float *__restrict__ loc,
                 const float *__restrict__ attn, const float *__restrict__ grad_out,
-                float *__restrict__ grad_loc, float *__restrict__ grad_attn, Dims dm) {
+                float *__restrict__ grad_loc, float *__restrict__ grad_attn,
+                float *__restrict__ ref_part, Dims dm) {
     constexpr int G = D / 4;
     constexpr int IPB = kThreads / G;
     __shared__ LevelLds s_lv;
@@ -465,7 +515,20 @@ bwd_dots_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
     float4 *s_aux = reinterpret_cast<float4 *>(s_off + IPB * dm.PS);
 
     const int M = dm.M, K = dm.K, LK = dm.L * dm.K, Nq = dm.Nq;
+    // per level, d pixel / d (location or offset): (W, H) or (W-1, H-1), over
+    // (W, H) for offsets
+    __shared__ float2 s_scale[kMaxLevels];
     stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, 0x7fffffff);
+    if (threadIdx.x < dm.L) {
+        const int4 lvl = s_lv.lvl[threadIdx.x];
+        float sx = pixel_scale(lvl.y, dm.align), sy = pixel_scale(lvl.x, dm.align);
+        if (dm.loc_div && lvl.y > 0) {  // d loc / d offset = 1 / (W, H)
+            sx /= (float)lvl.y;
+            sy /= (float)lvl.x;
+        }
+        s_scale[threadIdx.x] = make_float2(sx, sy);
+    }
+    __syncthreads();
     // blocks of IPB queries of one (batch, head), dm.nblk per (batch, head);
     // workgroup g takes blocks g, g + grid, ...
     const int total = dm.nblocks;
@@ -546,16 +609,27 @@ bwd_dots_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
                 const float fx = ax.x, fy = ax.y, A = ax.z;
                 const float4 w = tent_weights(fx, fy, valid);
                 ga = w.x * d0 + w.y * d1 + w.z * d2 + w.w * d3;
-                float sx = pixel_scale(lvl.y, dm.align), sy = pixel_scale(lvl.x, dm.align);
-                if (dm.loc_div) {  // d loc / d offset = 1 / (W, H)
-                    sx /= (float)lvl.y;
-                    sy /= (float)lvl.x;
-                }
-                gx = A * sx * ((1.f - fy) * (d1 - d0) + fy * (d3 - d2));
-                gy = A * sy * ((1.f - fx) * (d2 - d0) + fx * (d3 - d1));
+                const float2 sc = s_scale[j / K];
+                gx = A * sc.x * ((1.f - fy) * (d1 - d0) + fy * (d3 - d2));
+                gy = A * sc.y * ((1.f - fx) * (d2 - d0) + fx * (d3 - d1));
+            }
+            // Fused prologue, when the chunk holds whole items (runs of
+            // consecutive lanes are the items' softmax groups and levels):
+            // the logit gradient A * (grad_A - sum over the group of A * grad_A)
+            // replaces grad_A, and each level's sum of location gradients is
+            // stored per item for the reference-point gradient.
+            if (dm.softmax_run) {
+                const float A = ax.z;
+                ga = A * (ga - run_sum(A * ga, dm.softmax_run));
             }
             grad_attn[p] = ga;
             reinterpret_cast<float2 *>(grad_loc)[p] = make_float2(gx, gy);
+            if (ref_part) {
+                const float rx = run_sum(gx, K), ry = run_sum(gy, K);
+                if (j % K == 0)  // offset gradients times (W, H): location gradients
+                    reinterpret_cast<float2 *>(ref_part)[(row0 + (size_t)i1 * M) * dm.L + j / K] =
+                        make_float2(rx * (float)lvl.y, ry * (float)lvl.x);
+            }
         }
     }
     }
@@ -1116,12 +1190,16 @@ fused_prologue_kernel(const int64_t *__restrict__ shapes, const int64_t *__restr
     const int ng = pr.per_level ? L : 1;
     const int64_t blocks = (items + kProItems - 1) / kProItems;
     for (int64_t blk = blockIdx.x; blk < blocks; blk += gridDim.x) {
-        if (blk != (int64_t)blockIdx.x) __syncthreads();  // s_st is reused
         const int64_t item0 = blk * kProItems;
         const int nitems = (int)min((int64_t)kProItems, items - item0);
         const size_t pt0 = (size_t)item0 * LK;
-        stage_softmax_stats(s_st, pr, pt0, nitems, L, K);
-        __syncthreads();
+        if (!pr.shfl) {
+            if (blk != (int64_t)blockIdx.x) __syncthreads();  // s_st is reused
+            stage_softmax_stats(s_st, pr, pt0, nitems, L, K);
+            __syncthreads();
+        }
+        // idx runs over whole items, 256 at a time: with shfl every softmax run
+        // lies inside one wave and is active or inactive as a whole
         for (int idx = threadIdx.x; idx < nitems * LK; idx += kThreads) {
             const int i1 = idx / LK, j = idx - i1 * LK, l = j / K;
             const size_t p = pt0 + idx;
@@ -1129,8 +1207,13 @@ fused_prologue_kernel(const int64_t *__restrict__ shapes, const int64_t *__restr
             const float2 r = reinterpret_cast<const float2 *>(pr.ref)[bq * L + l];
             reinterpret_cast<float2 *>(loc)[p] =
                 prologue_location(r, reinterpret_cast<const float2 *>(pr.off)[p], s_lv.lvl[l]);
-            const float2 st = s_st[i1 * ng + (pr.per_level ? l : 0)];
-            attn[p] = expf(pr.logits[p] - st.x) * st.y;
+            const float z = pr.logits[p];
+            if (pr.shfl) {
+                attn[p] = run_softmax(z, pr.per_level ? K : LK);
+            } else {
+                const float2 st = s_st[i1 * ng + (pr.per_level ? l : 0)];
+                attn[p] = expf(z - st.x) * st.y;
+            }
         }
     }
 }
@@ -1138,26 +1221,81 @@ fused_prologue_kernel(const int64_t *__restrict__ shapes, const int64_t *__restr
 __global__ void __launch_bounds__(kThreads)
 fused_epilogue_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ starts,
                       const float *__restrict__ attn, float *__restrict__ grad_logits,
-                      const float *__restrict__ grad_off, float *__restrict__ grad_ref,
-                      int per_level, int64_t groups, int64_t refs, Dims dm) {
+                      const float *__restrict__ grad_off, const float *__restrict__ ref_part,
+                      float *__restrict__ grad_ref, int per_level, int shfl, int64_t groups,
+                      int64_t refs, Dims dm) {
     __shared__ LevelLds s_lv;
     stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, 0x7fffffff);
     const int M = dm.M, K = dm.K, L = dm.L, LK = L * K;
     const int gs = per_level ? K : LK;
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     const int64_t t0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    for (int64_t u = t0; u < groups; u += stride) {
-        const size_t p0 = (size_t)u * gs;  // the groups tile the points in order
-        float s = 0.f;
-        for (int j = 0; j < gs; ++j) s = __builtin_fmaf(attn[p0 + j], grad_logits[p0 + j], s);
-        for (int j = 0; j < gs; ++j) grad_logits[p0 + j] = attn[p0 + j] * (grad_logits[p0 + j] - s);
+    if (ref_part) {
+        // the dots kernel did the softmax backward and the per-(item, level)
+        // sums: only the sum over heads is left
+        const float2 *g = reinterpret_cast<const float2 *>(ref_part);
+        for (int64_t u = t0; u < refs; u += stride) {
+            const int64_t bq = u / L;
+            const int l = (int)(u - bq * L);
+            float gx = 0.f, gy = 0.f;
+            for (int m = 0; m < M; ++m) {
+                const float2 v = g[((size_t)bq * M + m) * L + l];
+                gx += v.x;
+                gy += v.y;
+            }
+            reinterpret_cast<float2 *>(grad_ref)[u] = make_float2(gx, gy);
+        }
+        return;
+    }
+    if (shfl) {
+        // one point per lane, in order; a run of gs lanes is one softmax group
+        // (gs divides 64 and the stride, so runs never straddle waves)
+        const int64_t n = groups * gs;
+        for (int64_t p = t0; p < n; p += stride) {
+            const float a = attn[p], ga = grad_logits[p];
+            const float s = run_sum(a * ga, gs);
+            grad_logits[p] = a * (ga - s);
+        }
+    } else {
+        for (int64_t u = t0; u < groups; u += stride) {
+            const size_t p0 = (size_t)u * gs;  // the groups tile the points in order
+            float s = 0.f;
+            for (int j = 0; j < gs; ++j) s = __builtin_fmaf(attn[p0 + j], grad_logits[p0 + j], s);
+            for (int j = 0; j < gs; ++j)
+                grad_logits[p0 + j] = attn[p0 + j] * (grad_logits[p0 + j] - s);
+        }
     }
     if (!grad_ref) return;
+    const float2 *g2 = reinterpret_cast<const float2 *>(grad_off);
+    if (shfl && (K & (K - 1)) == 0 && K <= 64) {
+        // lane per (b, q, l, k): the sum over heads in a register, then over
+        // the K lanes of the level
+        const int64_t n = refs * K;
+        for (int64_t u = t0; u < n; u += stride) {
+            const int64_t bq = u / LK;
+            const int r = (int)(u - bq * LK), l = r / K;
+            const float2 *g = g2 + (size_t)bq * M * LK + r;
+            float gx = 0.f, gy = 0.f;
+            for (int m = 0; m < M; ++m) {
+                const float2 v = g[(size_t)m * LK];
+                gx += v.x;
+                gy += v.y;
+            }
+            gx = run_sum(gx, K);
+            gy = run_sum(gy, K);
+            if (r == l * K) {
+                const int4 lvl = s_lv.lvl[l];
+                reinterpret_cast<float2 *>(grad_ref)[bq * L + l] =
+                    make_float2(gx * (float)lvl.y, gy * (float)lvl.x);
+            }
+        }
+        return;
+    }
     for (int64_t u = t0; u < refs; u += stride) {
         const int64_t bq = u / L;
         const int l = (int)(u - bq * L);
         const int4 lvl = s_lv.lvl[l];
-        const float2 *g = reinterpret_cast<const float2 *>(grad_off) + ((size_t)bq * M * L + l) * K;
+        const float2 *g = g2 + ((size_t)bq * M * L + l) * K;
         float gx = 0.f, gy = 0.f;
         for (int m = 0; m < M; ++m)
             for (int k = 0; k < K; ++k) {
@@ -1250,6 +1388,9 @@ Launch plan(int64_t D, int64_t L, int64_t K, int bytes_per_point, int reserve = 
     return p;
 }
 
+// A softmax group that lane shuffles can reduce: a power of two <= 64.
+bool pow2_run(int64_t n) { return n >= 1 && n <= 64 && (n & (n - 1)) == 0; }
+
 FastDiv make_fastdiv(uint32_t d) {  // d >= 1
     uint32_t shift = 0;
     while (shift < 31 && (1u << shift) < d) ++shift;
@@ -1279,11 +1420,19 @@ msda_status launch_fwd(const void *value, const int64_t *shapes, const int64_t *
                        int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t L, int64_t K,
                        bool align, hipStream_t s) {
     const int ipb = (int)(kThreads / (D / 4));
-    const int ng = pr ? (pr->per_level ? (int)L : 1) : 0;
-    const int st_bytes = ipb * ng * (int)sizeof(float2);  // softmax stats per (item, group)
-    const Launch p = plan(D, L, K, 32, st_bytes);
+    Prologue prv = pr ? *pr : Prologue{nullptr, nullptr, nullptr, 0, 0, nullptr, nullptr};
+    int st_bytes = 0;
+    Launch p = plan(D, L, K, 32);
+    if (pr) {
+        // softmax by lane shuffles when the items' points come in one chunk and
+        // the groups are power-of-two runs of at most 64; else statistics in LDS
+        prv.shfl = (p.pc == L * K && pow2_run(pr->per_level ? K : L * K)) ? 1 : 0;
+        if (!prv.shfl) {
+            st_bytes = ipb * (pr->per_level ? (int)L : 1) * (int)sizeof(float2);
+            p = plan(D, L, K, 32, st_bytes);
+        }
+    }
     const size_t lds = p.lds + (size_t)st_bytes;
-    const Prologue prv = pr ? *pr : Prologue{nullptr, nullptr, nullptr, 0};
     const int64_t items = Nq * M;
     const int64_t gx = (items + p.ipb - 1) / p.ipb;
     const int64_t bchunk = batch_chunk(gx, B);
@@ -1330,6 +1479,16 @@ struct Exec {
     }
 };
 
+// The fused prologue's backward, as far as the dots kernel takes it: it
+// writes offset gradients (location gradients / (W, H)) always; with in_dots
+// also the logit gradients (softmax runs of softmax_run points) and, given
+// ref_part, the per-(item, level) location-gradient sums [B][Nq][M][L][2].
+struct FusedBwd {
+    int softmax_run;  // requested run length (0: the runs do not fit lane shuffles)
+    float *ref_part;  // nullptr: no reference-point gradient wanted
+    bool in_dots;     // set by the launch: the dots kernel did both
+};
+
 // One side stream per device, created on first use (default priority,
 // non-blocking with respect to the null stream).  The mutex is held while a
 // backward enqueues, so the fork / join events are never shared between two
@@ -1372,7 +1531,7 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
                        const float *loc, const float *attn, const float *gout, float *gval,
                        float *gloc, float *gattn, int64_t B, int64_t Nv, int64_t Nq, int64_t M,
                        int64_t L, int64_t K, const WorkLayout &wl, unsigned char *ws,
-                       bool accumulate, bool align, bool loc_div, const Exec &ex) {
+                       bool accumulate, bool align, FusedBwd *fz, const Exec &ex) {
     const hipStream_t s = ex.s;
     Work w;
     w.counts = reinterpret_cast<uint32_t *>(ws + wl.off_counts);
@@ -1388,6 +1547,10 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
     const hipStream_t ds = ex.side ? ex.side : s;
     const Launch p = plan(D, L, K, 32);
     const int64_t gq = (Nq + p.ipb - 1) / p.ipb;
+    // the dots kernel finishes the fused prologue's backward itself when its
+    // point table holds whole items and the softmax runs fit a wave
+    if (fz) fz->in_dots = fz->softmax_run > 0 && p.pc == L * K;
+    float *ref_part = fz && fz->in_dots ? fz->ref_part : nullptr;
     auto per_batch = [&](int64_t per_b, auto &&launch) -> msda_status {
         const int64_t bchunk = batch_chunk(per_b, B);
         for (int64_t b0 = 0; b0 < B; b0 += bchunk) {
@@ -1403,13 +1566,14 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
         Dims d2{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, p.pc, p.ps, (int)b0, (int)gq, 0, 0};
         d2.nblocks = (int)grid;
         d2.align = align ? 1 : 0;
-        d2.loc_div = loc_div ? 1 : 0;
+        d2.loc_div = fz ? 1 : 0;
+        d2.softmax_run = fz && fz->in_dots ? fz->softmax_run : 0;
         // a few workgroups per CU suffice for this gather-bound kernel, and leave
         // room for the grad_value kernels running beside it
         const unsigned g = grid > (unsigned)kDotsGrid ? (unsigned)kDotsGrid : grid;
         hipLaunchKernelGGL((bwd_dots_kernel<D, VT>), dim3(g), dim3(kThreads), p.lds, ds,
                            static_cast<const VT *>(value), shapes, starts, loc, attn, gout, gloc,
-                           gattn, d2);
+                           gattn, ref_part, d2);
     });
     if (st != MSDA_OK) return st;
     ex.stamp(1, true, ds);
@@ -1498,11 +1662,11 @@ msda_status dispatch_bwd(int64_t D, const void *value, const int64_t *shapes,
                          const float *gout, float *gval, float *gloc, float *gattn, int64_t B,
                          int64_t Nv, int64_t Nq, int64_t M, int64_t L, int64_t K,
                          const WorkLayout &wl, unsigned char *ws, bool acc, bool align,
-                         bool loc_div, const Exec &ex) {
+                         FusedBwd *fz, const Exec &ex) {
 #define MSDA_BWD_CASE(DD)                                                                      \
     case DD:                                                                                   \
         return launch_bwd<DD, VT>(value, shapes, starts, loc, attn, gout, gval, gloc, gattn, B, \
-                                  Nv, Nq, M, L, K, wl, ws, acc, align, loc_div, ex);
+                                  Nv, Nq, M, L, K, wl, ws, acc, align, fz, ex);
     switch (D) {
         MSDA_BWD_CASE(4)
         MSDA_BWD_CASE(8)
@@ -1544,9 +1708,10 @@ msda_status msda_forward(const void *value, int value_dtype, const int64_t *spat
 msda_status msda_forward_fused(const void *value, int value_dtype,
                                const int64_t *spatial_shapes, const int64_t *level_start_index,
                                const float *reference_points, const float *sampling_offsets,
-                               const float *attn_logits, float *out, int64_t B, int64_t Nv,
-                               int64_t Nq, int64_t M, int64_t D, int64_t L, int64_t K,
-                               uint32_t flags, void *stream) {
+                               const float *attn_logits, float *out, float *sampling_loc_out,
+                               float *attn_weight_out, int64_t B, int64_t Nv, int64_t Nq,
+                               int64_t M, int64_t D, int64_t L, int64_t K, uint32_t flags,
+                               void *stream) {
     msda_status st = check_sizes(value_dtype, B, Nv, Nq, M, D, L, K);
     if (st != MSDA_OK) return st;
     if (flags & ~(MSDA_ALIGN_CORNERS | MSDA_SOFTMAX_PER_LEVEL)) return MSDA_ERR_UNSUPPORTED;
@@ -1556,8 +1721,10 @@ msda_status msda_forward_fused(const void *value, int value_dtype,
     if (!value || !spatial_shapes || !level_start_index || !reference_points ||
         !sampling_offsets || !attn_logits || !out)
         return MSDA_ERR_NULL;
+    if ((sampling_loc_out == nullptr) != (attn_weight_out == nullptr)) return MSDA_ERR_NULL;
     const Prologue pr{reference_points, sampling_offsets, attn_logits,
-                      (flags & MSDA_SOFTMAX_PER_LEVEL) ? 1 : 0};
+                      (flags & MSDA_SOFTMAX_PER_LEVEL) ? 1 : 0, 0, sampling_loc_out,
+                      attn_weight_out};
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (value_dtype == MSDA_F32)
         return dispatch_fwd<float>(D, value, spatial_shapes, level_start_index, nullptr, nullptr,
@@ -1583,7 +1750,7 @@ msda_status backward_impl(const void *value, int value_dtype, const int64_t *spa
                           float *grad_sampling_loc, float *grad_attn_weight, int64_t B,
                           int64_t Nv, int64_t Nq, int64_t M, int64_t D, int64_t L, int64_t K,
                           void *workspace, size_t workspace_bytes, uint32_t flags,
-                          bool loc_div, hipStream_t s, hipEvent_t *ev) {
+                          FusedBwd *fz, hipStream_t s, hipEvent_t *ev) {
     msda_status st = check_sizes(value_dtype, B, Nv, Nq, M, D, L, K);
     if (st != MSDA_OK) return st;
     if (flags & ~(MSDA_BWD_ACCUMULATE | MSDA_ALIGN_CORNERS)) return MSDA_ERR_UNSUPPORTED;
@@ -1653,17 +1820,17 @@ msda_status backward_impl(const void *value, int value_dtype, const int64_t *spa
         return dispatch_bwd<float>(D, value, spatial_shapes, level_start_index, sampling_loc,
                                    attn_weight, grad_out, grad_value, grad_sampling_loc,
                                    grad_attn_weight, B, Nv, Nq, M, L, K, wl, ws, acc, align,
-                                   loc_div, ex);
+                                   fz, ex);
     return dispatch_bwd<uint16_t>(D, value, spatial_shapes, level_start_index, sampling_loc,
                                   attn_weight, grad_out, grad_value, grad_sampling_loc,
                                   grad_attn_weight, B, Nv, Nq, M, L, K, wl, ws, acc, align,
-                                  loc_div, ex);
+                                  fz, ex);
 }
 
 // Workspace of the fused backward: the core's, then the locations [pts][2]
 // and weights [pts] the prologue writes.
 struct FusedLayout {
-    size_t core, off_loc, off_attn, bytes;
+    size_t core, off_loc, off_attn, off_part, bytes;
 };
 
 FusedLayout fused_layout(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t L, int64_t K) {
@@ -1673,13 +1840,15 @@ FusedLayout fused_layout(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t L
     f.core = work_layout(B, Nv, Nq, M, L, K).bytes;
     f.off_loc = f.core;
     f.off_attn = align(f.off_loc + 8 * pts);
-    f.bytes = align(f.off_attn + 4 * pts);
+    f.off_part = align(f.off_attn + 4 * pts);
+    f.bytes = align(f.off_part + 8 * (size_t)(B * Nq * M * L));
     return f;
 }
 
 msda_status backward_fused_impl(const void *value, int value_dtype, const int64_t *shapes,
                                 const int64_t *starts, const float *ref, const float *off,
-                                const float *logits, const float *grad_out, float *grad_value,
+                                const float *logits, const float *saved_loc,
+                                const float *saved_attn, const float *grad_out, float *grad_value,
                                 float *grad_off, float *grad_logits, float *grad_ref, int64_t B,
                                 int64_t Nv, int64_t Nq, int64_t M, int64_t D, int64_t L,
                                 int64_t K, void *workspace, size_t workspace_bytes,
@@ -1697,9 +1866,10 @@ msda_status backward_fused_impl(const void *value, int value_dtype, const int64_
     if (!work) {
         stamp(MSDA_BWD_STAGES, false);
         stamp(MSDA_BWD_STAGES, true);
+        FusedBwd none{0, nullptr, false};
         st = backward_impl(value, value_dtype, shapes, starts, nullptr, nullptr, grad_out,
                            grad_value, nullptr, nullptr, B, Nv, Nq, M, D, L, K, workspace,
-                           workspace_bytes, core_flags, true, s, ev);
+                           workspace_bytes, core_flags, &none, s, ev);
         stamp(MSDA_BWD_STAGES + 1, false);
         stamp(MSDA_BWD_STAGES + 1, true);
         return st;
@@ -1708,22 +1878,25 @@ msda_status backward_fused_impl(const void *value, int value_dtype, const int64_
     if (!value || !shapes || !starts || !ref || !off || !logits || !grad_out || !grad_value ||
         !grad_off || !grad_logits)
         return MSDA_ERR_NULL;
+    if ((saved_loc == nullptr) != (saved_attn == nullptr)) return MSDA_ERR_NULL;
     if (!workspace) return MSDA_ERR_NULL;
     const FusedLayout fl = fused_layout(B, Nv, Nq, M, L, K);
     if (workspace_bytes < fl.bytes) return MSDA_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return MSDA_ERR_WORKSPACE;
     unsigned char *ws = static_cast<unsigned char *>(workspace);
+    const bool saved = saved_loc != nullptr;
     float *loc = reinterpret_cast<float *>(ws + fl.off_loc);
     float *attn = reinterpret_cast<float *>(ws + fl.off_attn);
-    const Prologue pr{ref, off, logits, per_level ? 1 : 0};
+    const int shfl = pow2_run(per_level ? K : L * K) ? 1 : 0;
+    const Prologue pr{ref, off, logits, per_level ? 1 : 0, shfl, nullptr, nullptr};
     Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, 0, 0, 0, 0, 0, 0};
     const int64_t items = B * Nq * M;
 
     stamp(MSDA_BWD_STAGES, false);
-    {
+    if (!saved) {
         const int64_t blocks = (items + kProItems - 1) / kProItems;
         const unsigned grid = (unsigned)(blocks < (1 << 20) ? blocks : (1 << 20));
-        const size_t lds = (size_t)kProItems * (per_level ? L : 1) * sizeof(float2);
+        const size_t lds = shfl ? 0 : (size_t)kProItems * (per_level ? L : 1) * sizeof(float2);
         hipLaunchKernelGGL(fused_prologue_kernel, dim3(grid), dim3(kThreads), lds, s, shapes,
                            starts, pr, loc, attn, items, dm);
         st = hip_status(hipGetLastError());
@@ -1731,21 +1904,36 @@ msda_status backward_fused_impl(const void *value, int value_dtype, const int64_
     }
     stamp(MSDA_BWD_STAGES, true);
 
-    st = backward_impl(value, value_dtype, shapes, starts, loc, attn, grad_out, grad_value,
-                       grad_off, grad_logits, B, Nv, Nq, M, D, L, K, ws, fl.core, core_flags,
-                       true, s, ev);
+    FusedBwd fz{shfl ? (int)(per_level ? K : L * K) : 0,
+                grad_ref ? reinterpret_cast<float *>(ws + fl.off_part) : nullptr, false};
+    const float *use_loc = saved ? saved_loc : loc, *use_attn = saved ? saved_attn : attn;
+    st = backward_impl(value, value_dtype, shapes, starts, use_loc, use_attn, grad_out,
+                       grad_value, grad_off, grad_logits, B, Nv, Nq, M, D, L, K, ws, fl.core,
+                       core_flags, &fz, s, ev);
     if (st != MSDA_OK) return st;
 
     stamp(MSDA_BWD_STAGES + 1, false);
-    {
+    if (fz.in_dots) {
+        if (grad_ref) {
+            const int64_t refs = B * Nq * L;
+            int64_t blocks = (refs + kThreads - 1) / kThreads;
+            blocks = blocks < (1 << 16) ? blocks : (1 << 16);
+            hipLaunchKernelGGL(fused_epilogue_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
+                               s, shapes, starts, use_attn, grad_logits, grad_off, fz.ref_part,
+                               grad_ref, per_level ? 1 : 0, shfl, (int64_t)0, refs, dm);
+            st = hip_status(hipGetLastError());
+        }
+    } else {
         const int64_t groups = items * (per_level ? L : 1);
         const int64_t refs = grad_ref ? B * Nq * L : 0;
-        const int64_t units = groups > refs ? groups : refs;
+        // lanes per unit of work: a point (shuffle path) or a group / reference
+        const int64_t gl = shfl ? (per_level ? K : L * K) : 1, rl = shfl ? K : 1;
+        const int64_t units = groups * gl > refs * rl ? groups * gl : refs * rl;
         int64_t blocks = (units + kThreads - 1) / kThreads;
         blocks = blocks < (1 << 16) ? blocks : (1 << 16);
         hipLaunchKernelGGL(fused_epilogue_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s,
-                           shapes, starts, attn, grad_logits, grad_off, grad_ref,
-                           per_level ? 1 : 0, groups, refs, dm);
+                           shapes, starts, use_attn, grad_logits, grad_off, nullptr, grad_ref,
+                           per_level ? 1 : 0, shfl, groups, refs, dm);
         st = hip_status(hipGetLastError());
     }
     stamp(MSDA_BWD_STAGES + 1, true);
@@ -1765,7 +1953,7 @@ msda_status msda_backward(const void *value, int value_dtype, const int64_t *spa
                           void *stream) {
     return backward_impl(value, value_dtype, spatial_shapes, level_start_index, sampling_loc,
                          attn_weight, grad_out, grad_value, grad_sampling_loc, grad_attn_weight,
-                         B, Nv, Nq, M, D, L, K, workspace, workspace_bytes, flags, false,
+                         B, Nv, Nq, M, D, L, K, workspace, workspace_bytes, flags, nullptr,
                          static_cast<hipStream_t>(stream), nullptr);
 }
 
@@ -1782,7 +1970,7 @@ msda_status msda_backward_events(const void *value, int value_dtype,
     for (int i = 0; i < 2 * MSDA_BWD_STAGES; ++i) ev[i] = static_cast<hipEvent_t>(events[i]);
     return backward_impl(value, value_dtype, spatial_shapes, level_start_index, sampling_loc,
                          attn_weight, grad_out, grad_value, grad_sampling_loc, grad_attn_weight,
-                         B, Nv, Nq, M, D, L, K, workspace, workspace_bytes, flags, false,
+                         B, Nv, Nq, M, D, L, K, workspace, workspace_bytes, flags, nullptr,
                          static_cast<hipStream_t>(stream), ev);
 }
 
@@ -1796,7 +1984,8 @@ size_t msda_backward_fused_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int
 msda_status msda_backward_fused(const void *value, int value_dtype,
                                 const int64_t *spatial_shapes, const int64_t *level_start_index,
                                 const float *reference_points, const float *sampling_offsets,
-                                const float *attn_logits, const float *grad_out,
+                                const float *attn_logits, const float *sampling_loc,
+                                const float *attn_weight, const float *grad_out,
                                 float *grad_value, float *grad_sampling_offsets,
                                 float *grad_attn_logits, float *grad_reference_points, int64_t B,
                                 int64_t Nv, int64_t Nq, int64_t M, int64_t D, int64_t L,
@@ -1807,7 +1996,8 @@ msda_status msda_backward_fused(const void *value, int value_dtype,
         for (int i = 0; i < 2 * MSDA_BWD_FUSED_STAGES; ++i)
             ev[i] = static_cast<hipEvent_t>(events[i]);
     return backward_fused_impl(value, value_dtype, spatial_shapes, level_start_index,
-                               reference_points, sampling_offsets, attn_logits, grad_out,
+                               reference_points, sampling_offsets, attn_logits, sampling_loc,
+                               attn_weight, grad_out,
                                grad_value, grad_sampling_offsets, grad_attn_logits,
                                grad_reference_points, B, Nv, Nq, M, D, L, K, workspace,
                                workspace_bytes, flags, static_cast<hipStream_t>(stream),

@@ -89,6 +89,20 @@ def test_fused_random_shapes(msda, D, per_level):
     check(msda, w, per_level=per_level)
 
 
+# power-of-two softmax groups of at most 64 points are reduced with lane
+# shuffles (when the forward's point table holds whole items); the others, as
+# in the cases above (L*K = 9 or 15), with per-group statistics in LDS
+@pytest.mark.parametrize("D,L,K", [(16, 4, 4), (64, 2, 32), (64, 1, 64), (32, 2, 8), (8, 4, 16),
+                                   (32, 1, 1)])
+@pytest.mark.parametrize("per_level", [False, True])
+def test_fused_shuffle_groups(msda, D, L, K, per_level):
+    _say(f"fused groups D={D} L={L} K={K} per_level={per_level}")
+    shapes = ((11, 13), (6, 5), (4, 3), (2, 2))[:L]
+    w = workloads.fused_case(1000 + D + L + K, 2, shapes, 27, 2, D, K, ref_low=-0.05,
+                             ref_high=1.05)
+    check(msda, w, per_level=per_level)
+
+
 @pytest.mark.parametrize("per_level,align", [(False, True), (True, True)])
 def test_fused_align_corners(msda, per_level, align):
     _say(f"fused align per_level={per_level}")
@@ -119,6 +133,32 @@ def test_fused_sixteen_levels_small_head(msda):
     w = workloads.fused_case(501, 2, shapes, 19, 2, 4, 2)
     check(msda, w, per_level=True)
     check(msda, w, per_level=False)
+
+
+@pytest.mark.parametrize("D,K,per_level", [(32, 4, False), (4, 2, True), (16, 3, False)])
+def test_fused_saved_locations(msda, D, K, per_level):
+    # forward_fused(save=True) stores the locations -- bit for bit the fp32
+    # division and addition of the oracle -- and the weights; the backward
+    # reading them gives the same gradients as the one recomputing them
+    _say(f"fused saved locations D={D} K={K} per_level={per_level}")
+    w = workloads.fused_case(1101 + D, 2, SHAPES, 31, 2, D, K, ref_low=-0.05, ref_high=1.05)
+    x = dev_inputs(w)
+    out, loc, attn = msda.forward_fused(**x, per_level=per_level, save=True)
+    torch.cuda.synchronize()
+    r_loc = ofused.locations(w.reference_points, w.sampling_offsets, w.spatial_shapes)
+    assert np.array_equal(loc.cpu().numpy().view(np.uint32), r_loc.view(np.uint32))
+    r_attn = ofused.weights(w.attn_logits, SHAPES.__len__(), K, per_level)
+    assert float(np.max(np.abs(attn.cpu().numpy() - r_attn))) <= 1e-6
+    plain = msda.forward_fused(**x, per_level=per_level)
+    assert torch.equal(out, plain)
+    g = torch.from_numpy(w.grad_out).cuda()
+    a = msda.backward_fused(**x, grad_out=g, per_level=per_level, saved=(loc, attn))
+    torch.cuda.synchronize()
+    rv, roff, rz, rref = ofused.backward(*_oracle_args(w), w.grad_out, per_level=per_level)
+    for name, got, r in zip(("grad_value", "grad_offsets", "grad_logits", "grad_ref"), a,
+                            (rv, roff, rz, rref)):
+        e = max_rel(got.cpu().numpy(), r)
+        assert e <= BWD_TOL, f"{name}: {e:.3e}"
 
 
 def test_fused_accumulate(msda):
