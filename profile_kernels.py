@@ -1,13 +1,18 @@
 #!/usr/bin/env python3
 """rocprofv3 driver and summarizer for the sampling-core kernels.
 
-Two modes:
+Modes:
 
   python3 profile_kernels.py run
       The workload the two counter passes are pointed at: the encoder-shape
       forward and backward (3 calls each), then an elementwise multiply that
       reads 256 MiB and writes 256 MiB, used to calibrate the FETCH_SIZE /
       WRITE_SIZE counters (bytes known / counter reading).
+
+  python3 profile_kernels.py run-fused
+      The same for the fused prologue at the encoder shape: forward storing
+      the locations and weights + backward reading them (5 each), backward
+      recomputing them (5), then the calibration multiply.
 
   python3 profile_kernels.py summarize --stats DIR --fetch DIR --write DIR
       Reads the CSV output of three rocprofv3 runs (kernel-trace stats of the
@@ -16,10 +21,17 @@ Two modes:
       and profiles/traffic.json (HBM bytes per launch of each kernel, scaled by
       the multiply's calibration, tagged with the kernel source hash).
 
+  python3 profile_kernels.py summarize-fused --stats DIR --fetch DIR --write DIR
+      The same from the three runs of `run-fused`: profiles/fused_encoder_kernels.txt
+      and profiles/fused_traffic.json.
+
 The GPU commands (run from /tmp with TMPDIR=/tmp, outputs under gpurun_out):
   rocprofv3 --kernel-trace --stats --output-format csv -d OUT/stats -o run -- python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline
   rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/fetch -o run -- python3 profile_kernels.py run
   rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/write -o run -- python3 profile_kernels.py run
+  rocprofv3 --kernel-trace --stats --output-format csv -d OUT/fstats -o run -- python3 profile_kernels.py run-fused
+  rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/ffetch -o run -- python3 profile_kernels.py run-fused
+  rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/fwrite -o run -- python3 profile_kernels.py run-fused
 """
 from __future__ import annotations
 
@@ -71,6 +83,31 @@ def run():
     print("profile workload done", flush=True)
 
 
+def run_fused():
+    import torch
+    import scale_deformable_attention_04_amd as msda
+    import workloads
+    w = workloads.make_fused(3)
+    d = torch.device("cuda:0")
+    t = lambda a: torch.from_numpy(a).to(d)
+    x = dict(value=t(w.value), spatial_shapes=t(w.spatial_shapes),
+             level_start_index=t(w.level_start_index), reference_points=t(w.reference_points),
+             sampling_offsets=t(w.sampling_offsets), attn_logits=t(w.attn_logits))
+    g = t(w.grad_out)
+    for _ in range(5):
+        out, loc, attn = msda.forward_fused(**x, validate=False, save=True)
+        msda.backward_fused(**x, grad_out=g, validate=False, saved=(loc, attn))
+    for _ in range(5):
+        msda.backward_fused(**x, grad_out=g, validate=False)
+    torch.cuda.synchronize()
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=d)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 2.0, out=dst)
+    torch.cuda.synchronize()
+    print("profile workload done", flush=True)
+
+
 def _rows(path_glob):
     rows = []
     for f in sorted(glob.glob(path_glob, recursive=True)):
@@ -86,20 +123,30 @@ def _counter_means(dirpath, counter):
     return {k: sum(v) / len(v) for k, v in per.items()}
 
 
-def summarize(stats_dir, fetch_dir, write_dir, commands):
+HEADERS = {
+    "encoder": ["# rocprofv3 --kernel-trace --stats of bench.py: encoder workload (B=2, Nq=Nv=22223,",
+                "# M=8, D=32, L=4, K=4, fp32), forward and backward (its grad_attn/grad_loc kernel on",
+                "# a side stream, concurrent with the grad_value kernels)"],
+    "fused_encoder": ["# rocprofv3 --kernel-trace --stats of profile_kernels.py run-fused: the fused",
+                      "# prologue at the encoder shape (B=2, Nq=Nv=22223, M=8, D=32, L=4, K=4, fp32;",
+                      "# reference points + pixel offsets + logits): 5 x (forward storing the",
+                      "# locations and weights, backward reading them), 5 x backward recomputing",
+                      "# them (prologue kernel), then the 256 MiB calibration multiply"],
+}
+
+
+def summarize(stats_dir, fetch_dir, write_dir, commands, name="encoder"):
     stats = _rows(os.path.join(stats_dir, "**", "*kernel_stats.csv"))
-    lines = ["# rocprofv3 --kernel-trace --stats of bench.py: encoder workload (B=2, Nq=Nv=22223,",
-             "# M=8, D=32, L=4, K=4, fp32), forward and backward (its grad_attn/grad_loc kernel on",
-             "# a side stream, concurrent with the grad_value kernels); kernel source sha " +
-             source_sha(),
-             "# command: " + commands["stats"], "",
-             f"{'kernel':46s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}"]
+    head = list(HEADERS[name])
+    head[-1] += "; kernel source sha " + source_sha()
+    lines = head + ["# command: " + commands["stats"], "",
+                    f"{'kernel':46s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}"]
     for r in stats:
         lines.append(f"{short_name(r['Name'])[:46]:46s} {int(r['Calls']):6d} "
                      f"{float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
                      f"{float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):6.2f}")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    open(os.path.join(ROOT, "profiles", "encoder_kernels.txt"), "w").write("\n".join(lines) + "\n")
+    open(os.path.join(ROOT, "profiles", f"{name}_kernels.txt"), "w").write("\n".join(lines) + "\n")
 
     fetch = _counter_means(fetch_dir, "FETCH_SIZE")
     write = _counter_means(write_dir, "WRITE_SIZE")
@@ -114,7 +161,8 @@ def summarize(stats_dir, fetch_dir, write_dir, commands):
             continue
         out["kernels"][k] = {"fetch_bytes": fetch.get(k, 0.0) * f_scale,
                              "write_bytes": write.get(k, 0.0) * w_scale}
-    json.dump(out, open(os.path.join(ROOT, "profiles", "traffic.json"), "w"), indent=1)
+    tname = "traffic.json" if name == "encoder" else f"{name.split('_')[0]}_traffic.json"
+    json.dump(out, open(os.path.join(ROOT, "profiles", tname), "w"), indent=1)
     print("\n".join(lines))
     print(json.dumps(out, indent=1))
 
@@ -123,18 +171,26 @@ def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
     sub.add_parser("run")
-    s = sub.add_parser("summarize")
-    s.add_argument("--stats", required=True)
-    s.add_argument("--fetch", required=True)
-    s.add_argument("--write", required=True)
+    sub.add_parser("run-fused")
+    for mode in ("summarize", "summarize-fused"):
+        s = sub.add_parser(mode)
+        s.add_argument("--stats", required=True)
+        s.add_argument("--fetch", required=True)
+        s.add_argument("--write", required=True)
     a = ap.parse_args()
     if a.mode == "run":
         run()
+    elif a.mode == "run-fused":
+        run_fused()
     else:
-        doc = __doc__.split("The GPU commands")[1].splitlines()[1:4]
+        doc = __doc__.split("The GPU commands")[1].splitlines()[1:7]
         cmds = [c.strip() for c in doc]
-        summarize(a.stats, a.fetch, a.write,
-                  {"stats": cmds[0], "fetch": cmds[1], "write": cmds[2]})
+        if a.mode == "summarize":
+            summarize(a.stats, a.fetch, a.write,
+                      {"stats": cmds[0], "fetch": cmds[1], "write": cmds[2]})
+        else:
+            summarize(a.stats, a.fetch, a.write,
+                      {"stats": cmds[3], "fetch": cmds[4], "write": cmds[5]}, "fused_encoder")
 
 
 if __name__ == "__main__":
