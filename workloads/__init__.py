@@ -273,3 +273,67 @@ def make_fused(config: int | str = "encoder_bwd", batch: Optional[int] = None) -
         return FusedWorkload(name, bf16_to_f32(bits).reshape(vals.shape), ss, st, ref, off,
                              logits, g, value_bf16=bits.reshape(vals.shape))
     return FusedWorkload(name, vals, ss, st, ref, off, logits, g)
+
+
+# ---------------------------------------------------------------------------
+# 3-D (trilinear) variant: voxel pyramids
+# ---------------------------------------------------------------------------
+VOXEL_LEVELS: Tuple[Tuple[int, int, int], ...] = ((4, 128, 128), (2, 64, 64), (1, 32, 32))
+
+
+def volume_table(shapes: Sequence[Tuple[int, int, int]]):
+    """(shapes int64 [L,3] rows (Z,H,W), level_start_index int64 [L])."""
+    ss = np.asarray(shapes, dtype=np.int64).reshape(-1, 3)
+    sizes = ss[:, 0] * ss[:, 1] * ss[:, 2]
+    start = np.zeros(len(ss), dtype=np.int64)
+    if len(ss) > 1:
+        start[1:] = np.cumsum(sizes)[:-1]
+    return ss, start
+
+
+def volume_case(seed: int, B: int, shapes, Nq: int, M: int, D: int, K: int,
+                loc_low: float = -0.1, loc_high: float = 1.1, bf16: bool = False) -> Workload:
+    """Small random 3-D case: locations [B,Nq,M,L,K,3] iid uniform per coordinate."""
+    ss, st = volume_table(shapes)
+    Nv = int(ss.prod(axis=1).sum()) if len(shapes) else 0
+    L = len(shapes)
+    r = _rng(seed)
+    vals = r.standard_normal((B, Nv, M, D)).astype(np.float32)
+    loc = r.uniform(loc_low, loc_high, (B, Nq, M, L, K, 3)).astype(np.float32)
+    logits = r.standard_normal((B, Nq, M, L * K))
+    w = softmax_lastaxis(logits).reshape(B, Nq, M, L, K).astype(np.float32)
+    g = r.standard_normal((B, Nq, M * D)).astype(np.float32)
+    name = f"volume_random(seed={seed})"
+    if bf16:
+        bits = bf16_bits(vals)
+        return Workload(name, bf16_to_f32(bits).reshape(vals.shape), ss, st, loc, w, g,
+                        value_bf16=bits.reshape(vals.shape), value_unrounded=vals)
+    return Workload(name, vals, ss, st, loc, w, g)
+
+
+def make_volume(batch: int = 1) -> Workload:
+    """The voxel workload of the 3-D variant: a three-level voxel pyramid
+    (Z,H,W) = 4x128x128, 2x64x64, 1x32x32 (74,752 voxels), one query per
+    cell of the 128x128 bird's-eye grid (Nq = 16,384) whose reference is the
+    cell centre at a height drawn U(0.1, 0.9), offsets N(0, 2 voxels of each
+    level) on every axis, M=8, D=32, K=4, softmax weights, fp32.  Seeds
+    9000 + tensor id."""
+    shapes = VOXEL_LEVELS
+    ss, st = volume_table(shapes)
+    Nv = int(ss.prod(axis=1).sum())
+    L, M, D, K = len(shapes), 8, 32, 4
+    Hq = Wq = 128
+    Nq = Hq * Wq
+    B = int(batch)
+    base = 9000
+    vals = _rng(base + 0).standard_normal((B, Nv, M, D)).astype(np.float32)
+    ys, xs = np.meshgrid((np.arange(Hq) + 0.5) / Hq, (np.arange(Wq) + 0.5) / Wq, indexing="ij")
+    zs = _rng(base + 1).uniform(0.1, 0.9, (B, Nq))
+    ref = np.stack([np.broadcast_to(xs.ravel(), (B, Nq)), np.broadcast_to(ys.ravel(), (B, Nq)),
+                    zs], axis=-1)                                             # [B, Nq, 3]
+    off = _rng(base + 2).standard_normal((B, Nq, M, L, K, 3)) * 2.0
+    whz = np.array([[w, h, z] for (z, h, w) in shapes], dtype=np.float64)   # [L, 3] (W,H,Z)
+    loc = (ref[:, :, None, None, None, :] + off / whz[None, None, None, :, None, :])
+    w = _weights(base + 3, B, Nq, M, L, K)
+    g = _rng(base + 4).standard_normal((B, Nq, M * D)).astype(np.float32)
+    return Workload("volume", vals, ss, st, loc.astype(np.float32), w, g)
