@@ -40,7 +40,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 FLUSH_BYTES = 512 << 20   # > the 256 MB Infinity Cache
-KERNEL_SOURCE = os.path.join(ROOT, "scale_deformable_attention_04_amd", "csrc", "msda.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "scale_deformable_attention_04_amd", "csrc", f)
+                  for f in ("common.h", "msda.hip", "msda3d.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 # kernel names as rocprofv3 reports them, per stage of a step
@@ -61,7 +62,7 @@ def log(msg):
 
 
 def source_sha() -> str:
-    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+    return hashlib.sha256(b"".join(open(f, "rb").read() for f in KERNEL_SOURCES)).hexdigest()[:16]
 
 
 def byte_model(B, Nv, Nq, M, D, L, K, value_bytes=4):

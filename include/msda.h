@@ -271,6 +271,59 @@ msda_status msda_backward_fused(const void *value, int value_dtype,
                                 uint32_t flags, void *stream, void *const *events);
 
 /*
+ * 3-D (trilinear) variant.  "Deformable attention: multi-scale sparse
+ * sampling and detection practice", section 5.3: for point-cloud detection
+ * the points fall on voxel (or BEV) features, the offsets gain a z
+ * component and bilinear interpolation becomes trilinear -- the 2-D core with
+ * one more coordinate:
+ *
+ *     out[b, q, m*D + d] = sum_l sum_k A[b,q,m,l,k] * T_l(value[b, :, m, d], loc[b,q,m,l,k])
+ *
+ * Level l is a Z_l x H_l x W_l volume flattened z-major (voxel (x, y, z) is
+ * row start_l + (z*H_l + y)*W_l + x); a location is normalized (u, v, w) along
+ * (x, y, z) and maps to the voxel coordinate x = u*W_l - 0.5, y = v*H_l - 0.5,
+ * z = w*Z_l - 0.5 (each one fp32 fused multiply-add, then floored), or with
+ * MSDA_ALIGN_CORNERS x = u*(W_l - 1) etc.  T_l sums the eight integer
+ * neighbours with the product of the three tent weights; neighbours outside
+ * the volume contribute zero.
+ *
+ * Layouts as the 2-D core except
+ *   volume_shapes      [L, 3]  int64, rows (Z_l, H_l, W_l)
+ *   sampling_loc       [B, Nq, M, L, K, 3]    fp32, last axis (x, y, z) = (u, v, w)
+ *   grad_sampling_loc  [B, Nq, M, L, K, 3]
+ * with Nv = sum_l Z_l*H_l*W_l.  Limits as the 2-D core, with
+ * Nq*M*L*K*3 < 2^31 and each extent < 2^24.
+ *
+ * msda3d_forward: out is overwritten; flags 0 or MSDA_ALIGN_CORNERS.
+ * msda3d_backward: the exact derivatives, as for the 2-D core with the
+ * eight neighbours (grad_loc.z carries the factor Z_l, or Z_l - 1 with
+ * MSDA_ALIGN_CORNERS).  grad_value is zero-filled first unless flags has
+ * MSDA_BWD_ACCUMULATE, and receives the scatter through fp32 atomic adds,
+ * so its summation order is not fixed; grad_sampling_loc and
+ * grad_attn_weight are overwritten and deterministic.  No workspace and no
+ * side stream: everything runs on `stream`.
+ */
+msda_status msda3d_forward(const void *value, int value_dtype,
+                           const int64_t *volume_shapes, const int64_t *level_start_index,
+                           const float *sampling_loc, const float *attn_weight, float *out,
+                           int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
+                           int64_t L, int64_t K, uint32_t flags, void *stream);
+
+msda_status msda3d_backward(const void *value, int value_dtype,
+                            const int64_t *volume_shapes, const int64_t *level_start_index,
+                            const float *sampling_loc, const float *attn_weight,
+                            const float *grad_out, float *grad_value,
+                            float *grad_sampling_loc, float *grad_attn_weight,
+                            int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
+                            int64_t L, int64_t K, uint32_t flags, void *stream);
+
+/* msda_validate_host for the 3-D variant: a HOST copy of volume_shapes [L, 3]. */
+msda_status msda3d_validate_host(const int64_t *volume_shapes_host,
+                                 const int64_t *level_start_host,
+                                 int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
+                                 int64_t L, int64_t K);
+
+/*
  * Pure host check of the sizes and of a HOST copy of the level table:
  * H_l, W_l >= 1, level_start_host[l] = sum of H*W of levels before l,
  * Nv = sum H*W, plus every limit msda_forward/msda_backward check.

@@ -47,12 +47,13 @@ import sys
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
-KERNEL_SOURCE = os.path.join(ROOT, "scale_deformable_attention_04_amd", "csrc", "msda.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "scale_deformable_attention_04_amd", "csrc", f)
+                  for f in ("common.h", "msda.hip", "msda3d.hip")]
 COPY_BYTES = 256 << 20
 
 
 def source_sha() -> str:
-    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+    return hashlib.sha256(b"".join(open(f, "rb").read() for f in KERNEL_SOURCES)).hexdigest()[:16]
 
 
 def short_name(name: str) -> str:

@@ -12,16 +12,17 @@ from ._binding import (BWD_FUSED_STAGES, BWD_STAGES, EXPORTED, LIB_PATH, MSDA_AL
                        MSDA_BF16, MSDA_BWD_ACCUMULATE, MSDA_ERR_DTYPE,
                        MSDA_ERR_HIP, MSDA_ERR_NULL, MSDA_ERR_SHAPE, MSDA_ERR_UNSUPPORTED,
                        MSDA_ERR_WORKSPACE, MSDA_F32, MSDA_OK, MSDA_SOFTMAX_PER_LEVEL, MSDAError,
-                       backward, backward_fused, forward, forward_fused, fused_workspace_size,
-                       load, make_events, stage_times, status_string, validate_host,
-                       workspace_size)
+                       backward, backward3d, backward_fused, forward, forward3d, forward_fused,
+                       fused_workspace_size, load, make_events, stage_times, status_string,
+                       validate_host, validate_host3d, workspace_size)
 
 __all__ = ["forward", "backward", "forward_fused", "backward_fused", "BWD_STAGES",
            "BWD_FUSED_STAGES", "make_events", "stage_times", "workspace_size",
            "fused_workspace_size", "validate_host", "status_string", "load",
            "MSDAError",
            "ms_deform_attn", "MSDeformAttnFunction", "ms_deform_attn_fused",
-           "MSDeformAttnFusedFunction", "LIB_PATH", "EXPORTED"]
+           "MSDeformAttnFusedFunction", "forward3d", "backward3d", "validate_host3d",
+           "ms_deform_attn_3d", "MSDeformAttn3dFunction", "LIB_PATH", "EXPORTED"]
 
 
 class MSDeformAttnFunction(torch.autograd.Function):
@@ -91,3 +92,29 @@ def ms_deform_attn_fused(value, spatial_shapes, level_start_index, reference_poi
     return MSDeformAttnFusedFunction.apply(value, spatial_shapes, level_start_index,
                                            reference_points, sampling_offsets, attn_logits,
                                            per_level, align_corners)
+
+
+class MSDeformAttn3dFunction(torch.autograd.Function):
+    """The 3-D (trilinear) core with the library's backward."""
+
+    @staticmethod
+    def forward(ctx, value, volume_shapes, level_start_index, sampling_loc, attn_weight,
+                align_corners=False):
+        out = forward3d(value, volume_shapes, level_start_index, sampling_loc, attn_weight,
+                        align_corners=align_corners)
+        ctx.save_for_backward(value, volume_shapes, level_start_index, sampling_loc, attn_weight)
+        ctx.align_corners = align_corners
+        return out
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        value, ss, st, loc, attn = ctx.saved_tensors
+        gv, gl, ga = backward3d(value, ss, st, loc, attn, grad_out.contiguous(), validate=False,
+                                align_corners=ctx.align_corners)
+        return gv, None, None, gl, ga, None
+
+
+def ms_deform_attn_3d(value, volume_shapes, level_start_index, sampling_loc, attn_weight,
+                      align_corners=False):
+    return MSDeformAttn3dFunction.apply(value, volume_shapes, level_start_index, sampling_loc,
+                                        attn_weight, align_corners)

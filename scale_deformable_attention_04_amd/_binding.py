@@ -31,8 +31,8 @@ MSDA_SOFTMAX_PER_LEVEL = 4
 
 EXPORTED = ("msda_forward", "msda_backward_workspace_size", "msda_backward",
             "msda_backward_events", "msda_forward_fused", "msda_backward_fused_workspace_size",
-            "msda_backward_fused", "msda_validate_host", "msda_status_string",
-            "msda_last_hip_error")
+            "msda_backward_fused", "msda3d_forward", "msda3d_backward", "msda3d_validate_host",
+            "msda_validate_host", "msda_status_string", "msda_last_hip_error")
 BWD_STAGES = ("fill_grad_value", "dots", "clear_bins", "count", "scan", "scatter", "tiles")
 BWD_FUSED_STAGES = BWD_STAGES + ("prologue", "epilogue")
 
@@ -75,6 +75,12 @@ def load():
     lib.msda_backward_fused.argtypes = ([p, ci, p, p, p, p, p, p, p, p, p, p, p, p] + [i64] * 7 +
                                         [p, ctypes.c_size_t, u32, p, p])
     lib.msda_backward_fused.restype = ci
+    lib.msda3d_forward.argtypes = [p, ci, p, p, p, p, p] + [i64] * 7 + [u32, p]
+    lib.msda3d_forward.restype = ci
+    lib.msda3d_backward.argtypes = [p, ci, p, p, p, p, p, p, p, p] + [i64] * 7 + [u32, p]
+    lib.msda3d_backward.restype = ci
+    lib.msda3d_validate_host.argtypes = [p, p] + [i64] * 7
+    lib.msda3d_validate_host.restype = ci
     lib.msda_validate_host.argtypes = [p, p] + [i64] * 7
     lib.msda_validate_host.restype = ci
     lib.msda_status_string.argtypes = [ci]
@@ -409,3 +415,93 @@ def backward_fused(value: torch.Tensor, spatial_shapes: torch.Tensor,
     if rc != MSDA_OK:
         raise MSDAError(rc, "msda_backward_fused")
     return grad_value, g_off, g_logits, g_ref
+
+
+# ---------------------------------------------------------------------------
+# 3-D (trilinear) variant
+# ---------------------------------------------------------------------------
+def validate_host3d(volume_shapes, level_start_index, B, Nv, Nq, M, D, L, K) -> int:
+    """msda3d_validate_host on host copies of the level table; returns the status code."""
+    ss = torch.as_tensor(volume_shapes, dtype=torch.int64).cpu().contiguous()
+    st = torch.as_tensor(level_start_index, dtype=torch.int64).cpu().contiguous()
+    return int(load().msda3d_validate_host(_ptr(ss), _ptr(st), B, Nv, Nq, M, D, L, K))
+
+
+def _check_inputs3d(value, volume_shapes, level_start_index, sampling_loc, attn_weight,
+                    validate):
+    dev = value.device
+    if dev.type != "cuda":
+        raise ValueError(f"value must be a GPU tensor, got device {dev}")
+    _dtype_code(value)
+    if value.dim() != 4:
+        raise ValueError(f"value must be [B, Nv, M, D], got {tuple(value.shape)}")
+    if volume_shapes.dim() != 2 or volume_shapes.shape[1] != 3:
+        raise ValueError("volume_shapes must be [L, 3]")
+    if sampling_loc.dim() != 6 or sampling_loc.shape[-1] != 3:
+        raise ValueError("sampling_loc must be [B, Nq, M, L, K, 3]")
+    B, Nv, M, D = (int(v) for v in value.shape)
+    L = int(volume_shapes.shape[0])
+    Nq, K = int(sampling_loc.shape[1]), int(sampling_loc.shape[4])
+    _need(value, "value", value.dtype, dev)
+    _need(volume_shapes, "volume_shapes", torch.int64, dev, (L, 3))
+    _need(level_start_index, "level_start_index", torch.int64, dev, (L,))
+    _need(sampling_loc, "sampling_loc", torch.float32, dev, (B, Nq, M, L, K, 3))
+    _need(attn_weight, "attn_weight", torch.float32, dev, (B, Nq, M, L, K))
+    if validate:
+        rc = validate_host3d(volume_shapes, level_start_index, B, Nv, Nq, M, D, L, K)
+        if rc != MSDA_OK:
+            raise MSDAError(rc, "msda3d_validate_host")
+    return dev, (B, Nv, Nq, M, D, L, K)
+
+
+def forward3d(value: torch.Tensor, volume_shapes: torch.Tensor, level_start_index: torch.Tensor,
+              sampling_loc: torch.Tensor, attn_weight: torch.Tensor,
+              out: Optional[torch.Tensor] = None, validate: bool = True,
+              align_corners: bool = False) -> torch.Tensor:
+    """msda3d_forward: out[B, Nq, M*D] (fp32) on torch's current stream."""
+    lib = load()
+    dev, (B, Nv, Nq, M, D, L, K) = _check_inputs3d(value, volume_shapes, level_start_index,
+                                                  sampling_loc, attn_weight, validate)
+    if out is None:
+        out = torch.empty((B, Nq, M * D), dtype=torch.float32, device=dev)
+    else:
+        _need(out, "out", torch.float32, dev, (B, Nq, M * D))
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = lib.msda3d_forward(_ptr(value), _dtype_code(value), _ptr(volume_shapes),
+                                _ptr(level_start_index), _ptr(sampling_loc), _ptr(attn_weight),
+                                _ptr(out), B, Nv, Nq, M, D, L, K,
+                                MSDA_ALIGN_CORNERS if align_corners else 0,
+                                ctypes.c_void_p(stream))
+    if rc != MSDA_OK:
+        raise MSDAError(rc, "msda3d_forward")
+    return out
+
+
+def backward3d(value: torch.Tensor, volume_shapes: torch.Tensor, level_start_index: torch.Tensor,
+               sampling_loc: torch.Tensor, attn_weight: torch.Tensor, grad_out: torch.Tensor,
+               grad_value: Optional[torch.Tensor] = None, accumulate: bool = False,
+               validate: bool = True, align_corners: bool = False):
+    """msda3d_backward: (grad_value fp32 [B,Nv,M,D], grad_sampling_loc, grad_attn_weight)."""
+    lib = load()
+    dev, (B, Nv, Nq, M, D, L, K) = _check_inputs3d(value, volume_shapes, level_start_index,
+                                                  sampling_loc, attn_weight, validate)
+    _need(grad_out, "grad_out", torch.float32, dev, (B, Nq, M * D))
+    if grad_value is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs a grad_value to add into")
+        grad_value = torch.empty((B, Nv, M, D), dtype=torch.float32, device=dev)
+    else:
+        _need(grad_value, "grad_value", torch.float32, dev, (B, Nv, M, D))
+    g_loc = torch.empty_like(sampling_loc)
+    g_attn = torch.empty_like(attn_weight)
+    flags = (MSDA_BWD_ACCUMULATE if accumulate else 0) | (MSDA_ALIGN_CORNERS if align_corners else 0)
+    with torch.cuda.device(dev):
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        rc = lib.msda3d_backward(_ptr(value), _dtype_code(value), _ptr(volume_shapes),
+                                 _ptr(level_start_index), _ptr(sampling_loc), _ptr(attn_weight),
+                                 _ptr(grad_out), _ptr(grad_value), _ptr(g_loc), _ptr(g_attn),
+                                 B, Nv, Nq, M, D, L, K, flags, stream)
+    if rc != MSDA_OK:
+        raise MSDAError(rc, "msda3d_backward")
+    return grad_value, g_loc, g_attn

@@ -8,6 +8,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "msda.hip")
+SOURCES = [SRC, os.path.join(PKG, "csrc", "msda3d.hip")]
+DEPS = SOURCES + [os.path.join(PKG, "csrc", "common.h")]
 HEADER = os.path.join(ROOT, "include", "msda.h")
 LIB = os.path.join(PKG, "libmsda.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -21,7 +23,8 @@ FLAGS = [
 
 
 def build(verbose: bool = False, extra=()) -> str:
-    cmd = [HIPCC, *FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-o", LIB + ".tmp", SRC]
+    cmd = [HIPCC, *FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-o", LIB + ".tmp",
+           *SOURCES]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
@@ -33,7 +36,7 @@ def stale() -> bool:
     if not os.path.exists(LIB):
         return True
     t = os.path.getmtime(LIB)
-    return any(os.path.getmtime(f) > t for f in (SRC, HEADER))
+    return any(os.path.getmtime(f) > t for f in (*DEPS, HEADER))
 
 
 if __name__ == "__main__":

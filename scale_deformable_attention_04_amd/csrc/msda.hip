@@ -41,19 +41,16 @@
 // same range check keeps an inconsistent level table from touching other
 // memory.
 
-#include <hip/hip_runtime.h>
 #include <mutex>
 #include <type_traits>
-#include <stdint.h>
 
-#include "msda.h"
+#include "common.h"
+
+// hipError_t of the last MSDA_ERR_HIP on this thread, for every translation unit
+thread_local int msda_internal_last_hip_error = 0;
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kMaxLevels = 16;
-constexpr uint32_t kOOB = 0x80000000u;     // byte offset past every slice (slices < 2^31 B)
-constexpr int kRsrcWord3 = 0x00020000;     // gfx9 buffer descriptor word 3 (raw, 32-bit data)
 constexpr int kSetupLdsBytes = 36 * 1024;  // per-workgroup budget for the point tables
 constexpr int kTileShift = 3;              // grad_value tiles of 8x8 pixels
 constexpr int kTile = 1 << kTileShift;
@@ -63,51 +60,6 @@ constexpr int kHistLds = 4096;             // bins of one (batch, head) kept in 
 constexpr int kScanThreads = 1024;
 constexpr int kTileGrid = 16384;           // workgroups of the tile kernel, at most
 constexpr int kDotsGrid = 512;             // workgroups of the dots kernel, at most
-
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                             kRsrcWord3);
-}
-
-// Four consecutive channels of a value row, widened to fp32.  `off32` is the
-// row's byte offset in fp32 units (row index * D * 4), `ch` the first channel.
-template <typename VT> struct Row4;
-
-template <> struct Row4<float> {
-    __device__ __forceinline__ static float4 load(rsrc_t r, uint32_t off32, int ch) {
-        auto u = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off32 + 4u * ch), 0, 0);
-        return make_float4(__uint_as_float(u[0]), __uint_as_float(u[1]),
-                           __uint_as_float(u[2]), __uint_as_float(u[3]));
-    }
-};
-
-// bfloat16 bits in uint16_t: widening is a 16-bit left shift, exact.
-template <> struct Row4<uint16_t> {
-    __device__ __forceinline__ static float4 load(rsrc_t r, uint32_t off32, int ch) {
-        auto u = __builtin_amdgcn_raw_buffer_load_b64(r, (int)((off32 >> 1) + 2u * ch), 0, 0);
-        return make_float4(__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u),
-                           __uint_as_float(u[1] << 16), __uint_as_float(u[1] & 0xffff0000u));
-    }
-};
-
-template <int CTRL> __device__ __forceinline__ float dpp(float v) {
-    return __builtin_bit_cast(
-        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-
-// Sum over the G lanes of an aligned lane group (G a power of two <= 64);
-// every lane of the group receives the sum.
-template <int G> __device__ __forceinline__ float group_sum(float v) {
-    if constexpr (G >= 2) v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]: lane ^ 1
-    if constexpr (G >= 4) v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]: lane ^ 2
-    if constexpr (G >= 8) v += dpp<0x141>(v);   // row_half_mirror: the other quad of 8
-    if constexpr (G >= 16) v += dpp<0x140>(v);  // row_mirror: the other half of 16
-    if constexpr (G >= 32) v += __shfl_xor(v, 16, 64);
-    if constexpr (G >= 64) v += __shfl_xor(v, 32, 64);
-    return v;
-}
 
 template <int CTRL, int ROWS>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
@@ -243,30 +195,6 @@ __device__ __forceinline__ TileMask point_tile_mask(const Neighbours &n) {
     const uint32_t m2 = sy & (bl | (nsx & br));
     const uint32_t m3 = sx & sy & br;
     return TileMask{tx0, ty0, m0 | (m1 << 1) | (m2 << 2) | (m3 << 3)};
-}
-
-__device__ __forceinline__ void fma4(float4 &acc, float w, const float4 &v) {
-    acc.x = __builtin_fmaf(w, v.x, acc.x);
-    acc.y = __builtin_fmaf(w, v.y, acc.y);
-    acc.z = __builtin_fmaf(w, v.z, acc.z);
-    acc.w = __builtin_fmaf(w, v.w, acc.w);
-}
-
-__device__ __forceinline__ float dot4(const float4 &a, const float4 &b) {
-    return __builtin_fmaf(a.w, b.w, __builtin_fmaf(a.z, b.z, __builtin_fmaf(a.y, b.y, a.x * b.x)));
-}
-
-// Workgroup ids are dispatched round-robin over the 8 XCDs (workgroup k runs
-// on XCD k % 8), and each XCD has its own L2.  Mapping id k to the logical
-// index below gives every XCD one contiguous range of the work, so the value
-// rows, grad_out rows and points one XCD touches stay together in its L2.
-// The mapping is a permutation of [0, total): results never depend on it.
-constexpr int kXcds = 8;
-
-__device__ __forceinline__ int xcd_contiguous(int k, int total) {
-    const int per = total / kXcds, rem = total % kXcds;
-    const int x = k % kXcds, j = k / kXcds;
-    return x * per + min(x, rem) + j;
 }
 
 // Division by a divisor fixed at launch: n / d = (umulhi(n, mul) + n) >> shift
@@ -1160,11 +1088,6 @@ grad_value_tile_kernel(const int64_t *__restrict__ shapes, const int64_t *__rest
     }
 }
 
-__global__ void __launch_bounds__(kThreads) fill_zero_kernel(float4 *__restrict__ p, size_t n4) {
-    const size_t stride = (size_t)gridDim.x * kThreads;
-    for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += stride)
-        p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-}
 
 // ---------------------------------------------------------------------------
 // fused prologue, backward side
@@ -1310,12 +1233,6 @@ fused_epilogue_kernel(const int64_t *__restrict__ shapes, const int64_t *__restr
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-thread_local int g_last_hip_error = 0;
-
-bool supported_d(int64_t D) {
-    return D == 4 || D == 8 || D == 16 || D == 32 || D == 64 || D == 128 || D == 256;
-}
-
 msda_status check_sizes(int value_dtype, int64_t B, int64_t Nv, int64_t Nq, int64_t M,
                         int64_t D, int64_t L, int64_t K) {
     if (value_dtype != MSDA_F32 && value_dtype != MSDA_BF16) return MSDA_ERR_DTYPE;
@@ -1398,20 +1315,6 @@ FastDiv make_fastdiv(uint32_t d) {  // d >= 1
     return FastDiv{(uint32_t)mul, shift};
 }
 
-msda_status hip_status(hipError_t e) {
-    if (e == hipSuccess) return MSDA_OK;
-    g_last_hip_error = (int)e;
-    return MSDA_ERR_HIP;
-}
-
-// Batches per launch so that a 1-D grid of per_batch workgroups per batch
-// stays below 2^23 workgroups (2^31 threads).
-int64_t batch_chunk(int64_t per_batch, int64_t B) {
-    int64_t c = ((int64_t)1 << 23) / (per_batch > 0 ? per_batch : 1);
-    c = c < 1 ? 1 : c;
-    return c < B ? c : B;
-}
-
 // pr == nullptr: locations and weights from loc / attn; otherwise from the
 // prologue inputs (loc and attn unused).
 template <int D, typename VT>
@@ -1453,16 +1356,6 @@ msda_status launch_fwd(const void *value, const int64_t *shapes, const int64_t *
         if (st != MSDA_OK) return st;
     }
     return MSDA_OK;
-}
-
-// Zero n4 float4s (16-byte units) at p.
-msda_status fill_zero(void *p, size_t n4, hipStream_t s) {
-    if (n4 == 0) return MSDA_OK;
-    size_t blocks = (n4 + kThreads - 1) / kThreads;
-    if (blocks > 8192) blocks = 8192;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s,
-                       reinterpret_cast<float4 *>(p), n4);
-    return hip_status(hipGetLastError());
 }
 
 // Where the backward enqueues: the caller's stream, an optional side stream
@@ -2040,6 +1933,6 @@ const char *msda_status_string(int status) {
     }
 }
 
-int msda_last_hip_error(void) { return g_last_hip_error; }
+int msda_last_hip_error(void) { return msda_internal_last_hip_error; }
 
 }  // extern "C"

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared():
     src = open(os.path.join(ROOT, "include", "msda.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(msda_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(msda(?:3d)?_[a-z_]+)\s*\(", src)))
 
 
 def test_header_declares_the_binding_names():
@@ -170,6 +170,32 @@ def test_backward_fused_rejects_before_launch():
     assert bwd(0, 0, *dims, ws=ctypes.c_void_p((1 << 20) + 8), nbytes=need) == B_.MSDA_ERR_WORKSPACE
     # B = 0: nothing to do at all
     assert bwd(0, B_.MSDA_SOFTMAX_PER_LEVEL, 0, 80, 16, 2, 8, 2, 2) == B_.MSDA_OK
+
+
+def test_volume_entry_points_reject_before_launch():
+    lib = msda.load()
+    z = ctypes.c_void_p(0)
+    fwd = lambda dt, *dims, flags=0: lib.msda3d_forward(z, dt, z, z, z, z, z, *dims, flags, z)
+    assert fwd(5, 1, 80, 16, 2, 8, 2, 2) == B_.MSDA_ERR_DTYPE
+    assert fwd(0, 1, 80, 16, 2, 12, 2, 2) == B_.MSDA_ERR_UNSUPPORTED
+    assert fwd(0, 1, 80, 16, 2, 8, 2, 2) == B_.MSDA_ERR_NULL
+    assert fwd(0, 0, 80, 16, 2, 8, 2, 2) == B_.MSDA_OK
+    assert fwd(0, 1, 80, 16, 2, 8, 2, 2, flags=B_.MSDA_SOFTMAX_PER_LEVEL) == B_.MSDA_ERR_UNSUPPORTED
+    bwd = lambda dt, flags, *dims: lib.msda3d_backward(z, dt, z, z, z, z, z, z, z, z, *dims,
+                                                        flags, z)
+    assert bwd(0, 8, 1, 80, 16, 2, 8, 2, 2) == B_.MSDA_ERR_UNSUPPORTED
+    assert bwd(0, 0, 1, 80, 16, 2, 8, 2, 2) == B_.MSDA_ERR_NULL
+    assert bwd(0, 0, 0, 80, 16, 2, 8, 2, 2) == B_.MSDA_OK          # nothing to do
+    # the level table: rows (Z, H, W)
+    ss = _i64([[2, 4, 8], [1, 2, 4]])
+    st = _i64([0, 64])
+    v3 = lambda s, t, Nv: lib.msda3d_validate_host(s.ctypes.data_as(ctypes.c_void_p),
+                                                   t.ctypes.data_as(ctypes.c_void_p),
+                                                   1, Nv, 16, 2, 8, 2, 2)
+    assert v3(ss, st, 72) == B_.MSDA_OK
+    assert v3(ss, st, 71) == B_.MSDA_ERR_SHAPE
+    assert v3(ss, _i64([0, 63]), 72) == B_.MSDA_ERR_SHAPE
+    assert v3(_i64([[0, 4, 8], [1, 2, 4]]), st, 72) == B_.MSDA_ERR_SHAPE
 
 
 def test_status_strings():
