@@ -22,7 +22,8 @@ its average duration there give "achieved", against the 8 TB/s HBM peak.
 (profiles/traffic.json), when it was taken on the current kernel source.
 "cpu_baseline" times the CPU oracle on the same workload on this host's
 cores.  --extra adds the decoder and bf16 training shapes and the fused
-prologue (reference points + pixel offsets + logits) at the encoder shape.
+prologue (reference points + pixel offsets + logits) at the encoder shape,
+and the 3-D trilinear variant on a voxel workload.
 """
 from __future__ import annotations
 
@@ -243,6 +244,47 @@ def measure_fused(torch, msda, reps, flush):
     return res
 
 
+def measure_volume(torch, msda, reps, flush):
+    """The 3-D trilinear variant on the voxel workload (workloads.make_volume):
+    forward cold/warm and backward warm, with algorithmic bytes."""
+    import workloads
+    w = workloads.make_volume()
+    d = torch.device("cuda")
+    t = lambda a: torch.from_numpy(a).to(d)
+    x = dict(value=t(w.value), volume_shapes=t(w.spatial_shapes),
+             level_start_index=t(w.level_start_index), sampling_loc=t(w.sampling_loc),
+             attn_weight=t(w.attn_weight))
+    g = t(w.grad_out)
+    dims = w.dims
+    B, Nv, Nq, M, D, L, K = (dims[k] for k in ("B", "Nv", "Nq", "M", "D", "L", "K"))
+    pts = w.points
+    val, loc, attn, rows = B * Nv * M * D * 4, pts * 12, pts * 4, B * Nq * M * D * 4
+    fwd_bytes = val + loc + attn + rows
+    # backward: value, loc, attn, grad_out read; grad_loc, grad_attn written;
+    # grad_value zero-filled and then read-modify-written once
+    bwd_bytes = val + loc + attn + rows + loc + attn + 2 * val
+    out = torch.empty(B, Nq, M * D, device=d)
+    fwd = lambda: msda.forward3d(**x, out=out, validate=False)
+    for _ in range(3):
+        fwd()
+    gv = torch.empty(tuple(w.value.shape), dtype=torch.float32, device=d)
+    bwd = lambda: msda.backward3d(**x, grad_out=g, grad_value=gv, validate=False)
+    for _ in range(3):
+        bwd()
+    cold = time_forward(torch, fwd, reps, flush)
+    warm = time_forward(torch, fwd, reps, None)
+    bw = time_forward(torch, bwd, reps, None)
+    res = {"points": pts, "workload": "voxel pyramid 4x128x128, 2x64x64, 1x32x32; Nq=16384, "
+                                      "M=8, D=32, K=4, fp32",
+           "forward": {"us_cold": cold, "us_warm": warm, "algorithmic_bytes": fwd_bytes,
+                       "algorithmic_GBps": fwd_bytes / cold / 1e3},
+           "backward": {"us_warm": bw, "algorithmic_bytes": bwd_bytes,
+                        "algorithmic_GBps": bwd_bytes / bw / 1e3,
+                        "grad_value_atomic_adds": pts * 8 * D}}
+    log(f"volume: {json.dumps(res)}")
+    return res
+
+
 def cpu_baseline(w, min_seconds=10.0):
     import oracle
     pts = w.points
@@ -379,6 +421,7 @@ def main():
                                       flush, "train_bf16")
         extra["train_bf16"] = trn
         extra["fused_encoder"] = measure_fused(torch, msda, args.reps, flush)
+        extra["volume"] = measure_volume(torch, msda, args.reps, flush)
 
     result = {
         "metric": "sampled points/s (fwd+bwd) at the DETR encoder shape",

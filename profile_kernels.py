@@ -14,6 +14,10 @@ Modes:
       the locations and weights + backward reading them (5 each), backward
       recomputing them (5), then the calibration multiply.
 
+  python3 profile_kernels.py run-volume
+      The 3-D trilinear variant on the voxel workload: forward and backward
+      (5 each), then the calibration multiply.
+
   python3 profile_kernels.py summarize --stats DIR --fetch DIR --write DIR
       Reads the CSV output of three rocprofv3 runs (kernel-trace stats of the
       bench command itself; --pmc FETCH_SIZE and --pmc WRITE_SIZE of `run`)
@@ -25,6 +29,10 @@ Modes:
       The same from the three runs of `run-fused`: profiles/fused_encoder_kernels.txt
       and profiles/fused_traffic.json.
 
+  python3 profile_kernels.py summarize-volume --stats DIR --fetch DIR --write DIR
+      The same from the three runs of `run-volume`: profiles/volume_kernels.txt and
+      profiles/volume_traffic.json.
+
 The GPU commands (run from /tmp with TMPDIR=/tmp, outputs under gpurun_out):
   rocprofv3 --kernel-trace --stats --output-format csv -d OUT/stats -o run -- python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline
   rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/fetch -o run -- python3 profile_kernels.py run
@@ -32,6 +40,9 @@ The GPU commands (run from /tmp with TMPDIR=/tmp, outputs under gpurun_out):
   rocprofv3 --kernel-trace --stats --output-format csv -d OUT/fstats -o run -- python3 profile_kernels.py run-fused
   rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/ffetch -o run -- python3 profile_kernels.py run-fused
   rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/fwrite -o run -- python3 profile_kernels.py run-fused
+  rocprofv3 --kernel-trace --stats --output-format csv -d OUT/vstats -o run -- python3 profile_kernels.py run-volume
+  rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/vfetch -o run -- python3 profile_kernels.py run-volume
+  rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/vwrite -o run -- python3 profile_kernels.py run-volume
 """
 from __future__ import annotations
 
@@ -109,6 +120,29 @@ def run_fused():
     print("profile workload done", flush=True)
 
 
+def run_volume():
+    import torch
+    import scale_deformable_attention_04_amd as msda
+    import workloads
+    w = workloads.make_volume()
+    d = torch.device("cuda:0")
+    t = lambda a: torch.from_numpy(a).to(d)
+    x = dict(value=t(w.value), volume_shapes=t(w.spatial_shapes),
+             level_start_index=t(w.level_start_index), sampling_loc=t(w.sampling_loc),
+             attn_weight=t(w.attn_weight))
+    g = t(w.grad_out)
+    for _ in range(5):
+        msda.forward3d(**x, validate=False)
+        msda.backward3d(**x, grad_out=g, validate=False)
+    torch.cuda.synchronize()
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=d)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 2.0, out=dst)
+    torch.cuda.synchronize()
+    print("profile workload done", flush=True)
+
+
 def _rows(path_glob):
     rows = []
     for f in sorted(glob.glob(path_glob, recursive=True)):
@@ -133,6 +167,10 @@ HEADERS = {
                       "# reference points + pixel offsets + logits): 5 x (forward storing the",
                       "# locations and weights, backward reading them), 5 x backward recomputing",
                       "# them (prologue kernel), then the 256 MiB calibration multiply"],
+    "volume": ["# rocprofv3 --kernel-trace --stats of profile_kernels.py run-volume: the 3-D",
+               "# trilinear variant on the voxel workload (pyramid 4x128x128, 2x64x64, 1x32x32;",
+               "# Nq=16384, M=8, D=32, K=4, fp32): 5 x (forward, backward with its grad_value",
+               "# zero-fill), then the 256 MiB calibration multiply"],
 }
 
 
@@ -173,7 +211,8 @@ def main():
     sub = ap.add_subparsers(dest="mode", required=True)
     sub.add_parser("run")
     sub.add_parser("run-fused")
-    for mode in ("summarize", "summarize-fused"):
+    sub.add_parser("run-volume")
+    for mode in ("summarize", "summarize-fused", "summarize-volume"):
         s = sub.add_parser(mode)
         s.add_argument("--stats", required=True)
         s.add_argument("--fetch", required=True)
@@ -183,15 +222,20 @@ def main():
         run()
     elif a.mode == "run-fused":
         run_fused()
+    elif a.mode == "run-volume":
+        run_volume()
     else:
-        doc = __doc__.split("The GPU commands")[1].splitlines()[1:7]
+        doc = __doc__.split("The GPU commands")[1].splitlines()[1:10]
         cmds = [c.strip() for c in doc]
         if a.mode == "summarize":
             summarize(a.stats, a.fetch, a.write,
                       {"stats": cmds[0], "fetch": cmds[1], "write": cmds[2]})
-        else:
+        elif a.mode == "summarize-fused":
             summarize(a.stats, a.fetch, a.write,
                       {"stats": cmds[3], "fetch": cmds[4], "write": cmds[5]}, "fused_encoder")
+        else:
+            summarize(a.stats, a.fetch, a.write,
+                      {"stats": cmds[6], "fetch": cmds[7], "write": cmds[8]}, "volume")
 
 
 if __name__ == "__main__":
