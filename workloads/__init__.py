@@ -337,3 +337,68 @@ def make_volume(batch: int = 1) -> Workload:
     w = _weights(base + 3, B, Nq, M, L, K)
     g = _rng(base + 4).standard_normal((B, Nq, M * D)).astype(np.float32)
     return Workload("volume", vals, ss, st, loc.astype(np.float32), w, g)
+
+
+# ---------------------------------------------------------------------------
+# DAT sampled-key attention
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass
+class DatWorkload:
+    """Inputs of DAT's deformable sampling and of its attention."""
+    name: str
+    x: np.ndarray                     # [B, H*W, G, Dg] float32 features, channel-last
+    hw: Tuple[int, int]               # (H, W)
+    pos: np.ndarray                   # [B, Ns, G, 2] float32 normalized sampling positions (u, v)
+    q: np.ndarray                     # [B, N, Hh, d] float32
+    k: np.ndarray                     # [B, Ns, Hh, d] float32
+    v: np.ndarray                     # [B, Ns, Hh, d] float32
+    bias: Optional[np.ndarray]        # [B, Hh, N, Ns] float32 or None
+    grad_out: np.ndarray              # [B, N, Hh, d] float32
+    grad_sampled: np.ndarray          # [B, Ns, G*Dg] float32
+
+    @property
+    def dims(self):
+        B, N, Hh, d = self.q.shape
+        Ns = self.k.shape[1]
+        _, _, G, Dg = self.x.shape
+        return dict(B=B, N=N, Ns=Ns, Hh=Hh, d=d, G=G, Dg=Dg, H=self.hw[0], W=self.hw[1])
+
+
+DAT_CONFIGS = {
+    # DAT-T stage 3 at 224x224 (14x14 tokens, 384 channels, 12 heads of 32,
+    # 6 offset groups, reference grid 7x7 = 49 sampled keys), batch 64
+    "dat_cls": dict(B=64, H=14, W=14, C=384, heads=12, G=6, r=2),
+    # the same stage at 1024x1024 input for detection (64x64 tokens,
+    # reference grid 16x16 = 256 keys), batch 2
+    "dat_det": dict(B=2, H=64, W=64, C=384, heads=12, G=6, r=4),
+}
+
+
+def dat_case(seed: int, B: int, H: int, W: int, C: int, heads: int, G: int, Hk: int, Wk: int,
+             with_bias: bool = True, offset_cells: float = 0.5, name: str = "") -> DatWorkload:
+    """Features N(0,1); sampling positions = reference-grid cell centres plus
+    N(0, offset_cells) cells; q, k, v N(0,1) (the projections are outside
+    this path); bias N(0, 0.5) when asked for; upstream gradients N(0,1)."""
+    r = _rng(seed)
+    Dg, d = C // G, C // heads
+    N, Ns = H * W, Hk * Wk
+    x = r.standard_normal((B, N, G, Dg)).astype(np.float32)
+    gy, gx = np.meshgrid((np.arange(Hk) + 0.5) / Hk, (np.arange(Wk) + 0.5) / Wk, indexing="ij")
+    ref = np.stack([gx.ravel(), gy.ravel()], axis=-1)                      # [Ns, 2] (u, v)
+    off = r.standard_normal((B, Ns, G, 2)) * offset_cells / np.array([Wk, Hk])
+    pos = (ref[None, :, None, :] + off).astype(np.float32)
+    q = r.standard_normal((B, N, heads, d)).astype(np.float32)
+    k = r.standard_normal((B, Ns, heads, d)).astype(np.float32)
+    v = r.standard_normal((B, Ns, heads, d)).astype(np.float32)
+    bias = (r.standard_normal((B, heads, N, Ns)) * 0.5).astype(np.float32) if with_bias else None
+    g = r.standard_normal((B, N, heads, d)).astype(np.float32)
+    gs = r.standard_normal((B, Ns, C)).astype(np.float32)
+    return DatWorkload(name or f"dat(seed={seed})", x, (H, W), pos, q, k, v, bias, g, gs)
+
+
+def make_dat(name: str = "dat_det", with_bias: bool = False) -> DatWorkload:
+    """One of DAT_CONFIGS (seed 8000 / 8100)."""
+    c = DAT_CONFIGS[name]
+    seed = 8000 if name == "dat_cls" else 8100
+    return dat_case(seed, c["B"], c["H"], c["W"], c["C"], c["heads"], c["G"], c["H"] // c["r"],
+                    c["W"] // c["r"], with_bias=with_bias, name=name)
