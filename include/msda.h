@@ -324,6 +324,57 @@ msda_status msda3d_validate_host(const int64_t *volume_shapes_host,
                                  int64_t L, int64_t K);
 
 /*
+ * DAT sampled-key attention.  DAT (the Deformable Attention Transformer; its
+ * DAttentionBaseline walk-through, sections 2.1 to 2.3, and the first page's
+ * section 5.1) samples Ns keys/values per offset group at reference points
+ * moved by predicted offsets -- msda_forward / msda_backward with L = 1,
+ * K = 1, attention weight 1 and MSDA_ALIGN_CORNERS, the grid_sample call of
+ * its section 2.2 -- and then runs standard multi-head attention of all N
+ * query tokens against them (section 2.3).  These two calls are that
+ * attention, per batch b and head h:
+ *
+ *     S = scale * Q K^T + bias,   P = softmax of S over the Ns keys,   O = P V
+ *
+ * bias is the deformable relative-position bias, whose construction the page
+ * elides: an optional dense input here (NULL = none).  fp32 throughout, the
+ * products on the matrix cores (fp32 MFMA), accumulation in fp32.
+ *
+ * Layouts (dense, row-major, channel-last, device pointers, caller-owned):
+ *   q, out, grad_q, grad_out     [B, N, heads, head_dim]   fp32
+ *   k, v, grad_k, grad_v         [B, Ns, heads, head_dim]  fp32
+ *   bias, grad_bias              [B, heads, N, Ns]         fp32 (optional)
+ *   lse                          [B, heads, N]             fp32: log sum_keys exp(S), written
+ *                                by the forward, read by the backward
+ * Limits: head_dim in {16, 32, 64}; 1 <= Ns <= 256 (<= 240 for head_dim 64:
+ * one (b, head)'s keys fit 64 KB of LDS); B*heads < 65536; N*Ns < 2^31.
+ * B or N may be 0.
+ *
+ * msda_dat_attention_forward: out and lse are overwritten.
+ * msda_dat_attention_backward: grad_q, grad_k, grad_v and (when grad_bias is
+ * not NULL; then bias must not be NULL either, and Ns % 4 == 0 keeps its
+ * stores vectorized) grad_bias are overwritten.  grad_k and grad_v may be
+ * summed with fp32 atomics over ranges of queries, so their last bits may
+ * differ between calls.  workspace: at least
+ * msda_dat_attention_workspace_size(...) bytes of device memory (4 bytes per
+ * (b, head, query): rowsum(dO * O)), contents irrelevant.
+ */
+msda_status msda_dat_attention_forward(const float *q, const float *k, const float *v,
+                                       const float *bias, float *out, float *lse,
+                                       int64_t B, int64_t N, int64_t Ns, int64_t heads,
+                                       int64_t head_dim, float scale, void *stream);
+
+size_t msda_dat_attention_workspace_size(int64_t B, int64_t N, int64_t Ns, int64_t heads,
+                                         int64_t head_dim);
+
+msda_status msda_dat_attention_backward(const float *q, const float *k, const float *v,
+                                        const float *bias, const float *out, const float *lse,
+                                        const float *grad_out, float *grad_q, float *grad_k,
+                                        float *grad_v, float *grad_bias, void *workspace,
+                                        size_t workspace_bytes, int64_t B, int64_t N,
+                                        int64_t Ns, int64_t heads, int64_t head_dim,
+                                        float scale, void *stream);
+
+/*
  * Pure host check of the sizes and of a HOST copy of the level table:
  * H_l, W_l >= 1, level_start_host[l] = sum of H*W of levels before l,
  * Nv = sum H*W, plus every limit msda_forward/msda_backward check.

@@ -12,9 +12,11 @@ from ._binding import (BWD_FUSED_STAGES, BWD_STAGES, EXPORTED, LIB_PATH, MSDA_AL
                        MSDA_BF16, MSDA_BWD_ACCUMULATE, MSDA_ERR_DTYPE,
                        MSDA_ERR_HIP, MSDA_ERR_NULL, MSDA_ERR_SHAPE, MSDA_ERR_UNSUPPORTED,
                        MSDA_ERR_WORKSPACE, MSDA_F32, MSDA_OK, MSDA_SOFTMAX_PER_LEVEL, MSDAError,
-                       backward, backward3d, backward_fused, forward, forward3d, forward_fused,
-                       fused_workspace_size, load, make_events, stage_times, status_string,
-                       validate_host, validate_host3d, workspace_size)
+                       backward, backward3d, backward_fused, dat_attention,
+                       dat_attention_backward, dat_sample, dat_sample_backward, forward,
+                       forward3d, forward_fused, fused_workspace_size, load, make_events,
+                       stage_times, status_string, validate_host, validate_host3d,
+                       workspace_size)
 
 __all__ = ["forward", "backward", "forward_fused", "backward_fused", "BWD_STAGES",
            "BWD_FUSED_STAGES", "make_events", "stage_times", "workspace_size",
@@ -22,7 +24,9 @@ __all__ = ["forward", "backward", "forward_fused", "backward_fused", "BWD_STAGES
            "MSDAError",
            "ms_deform_attn", "MSDeformAttnFunction", "ms_deform_attn_fused",
            "MSDeformAttnFusedFunction", "forward3d", "backward3d", "validate_host3d",
-           "ms_deform_attn_3d", "MSDeformAttn3dFunction", "LIB_PATH", "EXPORTED"]
+           "ms_deform_attn_3d", "MSDeformAttn3dFunction", "dat_sample", "dat_sample_backward",
+           "dat_attention", "dat_attention_backward", "DATSampleFunction",
+           "DATAttentionFunction", "dat_deformable_attention", "LIB_PATH", "EXPORTED"]
 
 
 class MSDeformAttnFunction(torch.autograd.Function):
@@ -118,3 +122,43 @@ def ms_deform_attn_3d(value, volume_shapes, level_start_index, sampling_loc, att
                       align_corners=False):
     return MSDeformAttn3dFunction.apply(value, volume_shapes, level_start_index, sampling_loc,
                                         attn_weight, align_corners)
+
+
+class DATSampleFunction(torch.autograd.Function):
+    """DAT's deformable sampling: features [B, H*W, G, Dg] at positions
+    [B, Ns, G, 2] -> [B, Ns, G*Dg], with gradients for both."""
+
+    @staticmethod
+    def forward(ctx, x, hw, pos):
+        ctx.save_for_backward(x, pos)
+        ctx.hw = tuple(int(v) for v in hw)
+        return dat_sample(x, ctx.hw, pos, validate=False)
+
+    @staticmethod
+    def backward(ctx, grad):
+        x, pos = ctx.saved_tensors
+        gx, gp = dat_sample_backward(x, ctx.hw, pos, grad, validate=False)
+        return gx, None, gp
+
+
+class DATAttentionFunction(torch.autograd.Function):
+    """softmax(scale * Q K^T + bias) V per (batch, head) on the matrix cores."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, bias=None, scale=None):
+        out, lse = dat_attention(q, k, v, bias, scale)
+        ctx.save_for_backward(q, k, v, bias, out, lse)
+        ctx.scale = scale
+        return out
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        q, k, v, bias, out, lse = ctx.saved_tensors
+        need_b = bias is not None and ctx.needs_input_grad[3]
+        gq, gk, gv, gb = dat_attention_backward(q, k, v, out, lse, grad_out.contiguous(), bias,
+                                                need_grad_bias=need_b, scale=ctx.scale)
+        return gq, gk, gv, gb, None
+
+
+def dat_deformable_attention(q, k, v, bias=None, scale=None):
+    return DATAttentionFunction.apply(q, k, v, bias, scale)

@@ -32,6 +32,8 @@ MSDA_SOFTMAX_PER_LEVEL = 4
 EXPORTED = ("msda_forward", "msda_backward_workspace_size", "msda_backward",
             "msda_backward_events", "msda_forward_fused", "msda_backward_fused_workspace_size",
             "msda_backward_fused", "msda3d_forward", "msda3d_backward", "msda3d_validate_host",
+            "msda_dat_attention_forward", "msda_dat_attention_workspace_size",
+            "msda_dat_attention_backward",
             "msda_validate_host", "msda_status_string", "msda_last_hip_error")
 BWD_STAGES = ("fill_grad_value", "dots", "clear_bins", "count", "scan", "scatter", "tiles")
 BWD_FUSED_STAGES = BWD_STAGES + ("prologue", "epilogue")
@@ -81,6 +83,14 @@ def load():
     lib.msda3d_backward.restype = ci
     lib.msda3d_validate_host.argtypes = [p, p] + [i64] * 7
     lib.msda3d_validate_host.restype = ci
+    f32 = ctypes.c_float
+    lib.msda_dat_attention_forward.argtypes = [p] * 6 + [i64] * 5 + [f32, p]
+    lib.msda_dat_attention_forward.restype = ci
+    lib.msda_dat_attention_workspace_size.argtypes = [i64] * 5
+    lib.msda_dat_attention_workspace_size.restype = ctypes.c_size_t
+    lib.msda_dat_attention_backward.argtypes = ([p] * 12 + [ctypes.c_size_t] + [i64] * 5 +
+                                                [f32, p])
+    lib.msda_dat_attention_backward.restype = ci
     lib.msda_validate_host.argtypes = [p, p] + [i64] * 7
     lib.msda_validate_host.restype = ci
     lib.msda_status_string.argtypes = [ci]
@@ -505,3 +515,97 @@ def backward3d(value: torch.Tensor, volume_shapes: torch.Tensor, level_start_ind
     if rc != MSDA_OK:
         raise MSDAError(rc, "msda3d_backward")
     return grad_value, g_loc, g_attn
+
+
+# ---------------------------------------------------------------------------
+# DAT: deformable sampling of keys/values and the attention against them
+# ---------------------------------------------------------------------------
+def _level_of(hw, dev):
+    H, W = (int(v) for v in hw)
+    return (torch.tensor([[H, W]], dtype=torch.int64, device=dev),
+            torch.zeros(1, dtype=torch.int64, device=dev))
+
+
+def dat_sample(x: torch.Tensor, hw, pos: torch.Tensor, validate: bool = True) -> torch.Tensor:
+    """DAT's sampling step through msda_forward: x [B, H*W, G, Dg] (fp32 or
+    bf16, channel-last), pos [B, Ns, G, 2] normalized (u, v); returns the
+    sampled features [B, Ns, G*Dg] (bilinear, align_corners=True, zeros)."""
+    B, Nv, G, Dg = x.shape
+    Ns = pos.shape[1]
+    ss, st = _level_of(hw, x.device)
+    ones = torch.ones((B, Ns, G, 1, 1), dtype=torch.float32, device=x.device)
+    return forward(x, ss, st, pos.reshape(B, Ns, G, 1, 1, 2), ones, validate=validate,
+                   align_corners=True)
+
+
+def dat_sample_backward(x: torch.Tensor, hw, pos: torch.Tensor, grad_sampled: torch.Tensor,
+                        validate: bool = True):
+    """(grad_x [B, H*W, G, Dg] fp32, grad_pos [B, Ns, G, 2]) through msda_backward."""
+    B, Nv, G, Dg = x.shape
+    Ns = pos.shape[1]
+    ss, st = _level_of(hw, x.device)
+    ones = torch.ones((B, Ns, G, 1, 1), dtype=torch.float32, device=x.device)
+    gx, gl, _ = backward(x, ss, st, pos.reshape(B, Ns, G, 1, 1, 2), ones,
+                         grad_sampled.contiguous(), validate=validate, align_corners=True)
+    return gx, gl.reshape(B, Ns, G, 2)
+
+
+def _attn_dims(q, k, v, bias):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, N, heads, d] and k, v [B, Ns, heads, d]")
+    B, N, Hh, d = (int(t) for t in q.shape)
+    Ns = int(k.shape[1])
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError(f"q must be a GPU tensor, got device {dev}")
+    _need(q, "q", torch.float32, dev)
+    _need(k, "k", torch.float32, dev, (B, Ns, Hh, d))
+    _need(v, "v", torch.float32, dev, (B, Ns, Hh, d))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, dev, (B, Hh, N, Ns))
+    return dev, (B, N, Ns, Hh, d)
+
+
+def dat_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                  bias: Optional[torch.Tensor] = None, scale: Optional[float] = None):
+    """msda_dat_attention_forward: (out [B, N, heads, d], lse [B, heads, N])."""
+    lib = load()
+    dev, (B, N, Ns, Hh, d) = _attn_dims(q, k, v, bias)
+    scale = d ** -0.5 if scale is None else float(scale)
+    out = torch.empty((B, N, Hh, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hh, N), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        rc = lib.msda_dat_attention_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(out),
+                                            _ptr(lse), B, N, Ns, Hh, d, scale, stream)
+    if rc != MSDA_OK:
+        raise MSDAError(rc, "msda_dat_attention_forward")
+    return out, lse
+
+
+def dat_attention_backward(q, k, v, out, lse, grad_out, bias=None, need_grad_bias=False,
+                           scale=None, workspace: Optional[torch.Tensor] = None):
+    """msda_dat_attention_backward: (grad_q, grad_k, grad_v, grad_bias or None)."""
+    lib = load()
+    dev, (B, N, Ns, Hh, d) = _attn_dims(q, k, v, bias)
+    scale = d ** -0.5 if scale is None else float(scale)
+    _need(out, "out", torch.float32, dev, (B, N, Hh, d))
+    _need(lse, "lse", torch.float32, dev, (B, Hh, N))
+    _need(grad_out, "grad_out", torch.float32, dev, (B, N, Hh, d))
+    gq, gk, gv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    gb = torch.empty_like(bias) if (need_grad_bias and bias is not None) else None
+    need = int(lib.msda_dat_attention_workspace_size(B, N, Ns, Hh, d))
+    if workspace is None:
+        workspace = _workspace(dev, need)
+    elif workspace.device != dev or workspace.dtype != torch.uint8 or workspace.numel() < need:
+        raise ValueError(f"workspace must be a uint8 tensor on {dev} of >= {need} bytes")
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    with torch.cuda.device(dev):
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        rc = lib.msda_dat_attention_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(out),
+                                             _ptr(lse), _ptr(grad_out), _ptr(gq), _ptr(gk),
+                                             _ptr(gv), _ptr(gb), _ptr(workspace), ws_bytes,
+                                             B, N, Ns, Hh, d, scale, stream)
+    if rc != MSDA_OK:
+        raise MSDAError(rc, "msda_dat_attention_backward")
+    return gq, gk, gv, gb

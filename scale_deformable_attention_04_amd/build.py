@@ -8,7 +8,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "msda.hip")
-SOURCES = [SRC, os.path.join(PKG, "csrc", "msda3d.hip")]
+SOURCES = [SRC, os.path.join(PKG, "csrc", "msda3d.hip"), os.path.join(PKG, "csrc", "dat_attn.hip")]
 DEPS = SOURCES + [os.path.join(PKG, "csrc", "common.h")]
 HEADER = os.path.join(ROOT, "include", "msda.h")
 LIB = os.path.join(PKG, "libmsda.so")

@@ -198,6 +198,29 @@ def test_volume_entry_points_reject_before_launch():
     assert v3(_i64([[0, 4, 8], [1, 2, 4]]), st, 72) == B_.MSDA_ERR_SHAPE
 
 
+def test_dat_attention_rejects_before_launch():
+    lib = msda.load()
+    z = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(1 << 20)
+    fwd = lambda *dims: lib.msda_dat_attention_forward(z, z, z, z, z, z, *dims, 0.25, z)
+    assert fwd(1, 16, 8, 2, 32) == B_.MSDA_ERR_NULL
+    assert fwd(1, 16, 8, 2, 24) == B_.MSDA_ERR_UNSUPPORTED          # head_dim
+    assert fwd(1, 16, 257, 2, 32) == B_.MSDA_ERR_UNSUPPORTED         # keys beyond 256
+    assert fwd(1, 16, 241, 2, 64) == B_.MSDA_ERR_UNSUPPORTED         # 64 KB of LDS
+    assert fwd(1, 16, 240, 2, 64) == B_.MSDA_ERR_NULL
+    assert fwd(1, 16, 0, 2, 32) == B_.MSDA_ERR_SHAPE
+    assert fwd(0, 16, 8, 2, 32) == B_.MSDA_OK and fwd(2, 0, 8, 2, 32) == B_.MSDA_OK
+    assert lib.msda_dat_attention_workspace_size(2, 100, 8, 3, 32) == 4 * 2 * 3 * 100
+    assert lib.msda_dat_attention_workspace_size(2, 100, 8, 3, 48) == 0
+    bwd = lambda ws, nbytes, gb=z, bias=z: lib.msda_dat_attention_backward(
+        fake, fake, fake, bias, fake, fake, fake, fake, fake, fake, gb, ws, nbytes,
+        1, 16, 8, 2, 32, 0.25, z)
+    need = lib.msda_dat_attention_workspace_size(1, 16, 8, 2, 32)
+    assert bwd(z, need) == B_.MSDA_ERR_NULL
+    assert bwd(fake, need - 1) == B_.MSDA_ERR_WORKSPACE
+    assert bwd(fake, need, gb=fake) == B_.MSDA_ERR_NULL              # dbias needs the bias
+
+
 def test_status_strings():
     for code in (0, -1, -2, -3, -4, -5, -6):
         s = msda.status_string(code)
