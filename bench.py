@@ -23,7 +23,8 @@ its average duration there give "achieved", against the 8 TB/s HBM peak.
 "cpu_baseline" times the CPU oracle on the same workload on this host's
 cores.  --extra adds the decoder and bf16 training shapes and the fused
 prologue (reference points + pixel offsets + logits) at the encoder shape,
-and the 3-D trilinear variant on a voxel workload.
+the 3-D trilinear variant on a voxel workload, and DAT's sampled-key
+attention (sampling and MFMA attention) at its two configurations.
 """
 from __future__ import annotations
 
@@ -285,6 +286,54 @@ def measure_volume(torch, msda, reps, flush):
     return res
 
 
+MFMA_FP32_PEAK_TFLOPS = 157.3
+
+
+def measure_dat(torch, msda, reps, flush):
+    """DAT's sampled-key attention at both DAT configurations, without the
+    optional bias: the sampling step (core with one level and point) forward
+    and backward, and the MFMA attention forward and backward, with the
+    attention's algorithmic flops (2 per multiply-add: QK^T and PV forward;
+    S, dP recomputed twice, dQ, dK, dV backward) against the fp32 MFMA peak."""
+    import workloads
+    res = {}
+    for name in ("dat_cls", "dat_det"):
+        w = workloads.make_dat(name)
+        dims = w.dims
+        B, N, Ns, Hh, d = (dims[k] for k in ("B", "N", "Ns", "Hh", "d"))
+        t = lambda a: torch.from_numpy(a).cuda()
+        x, pos, gs = t(w.x), t(w.pos), t(w.grad_sampled)
+        q, k, v, g = t(w.q), t(w.k), t(w.v), t(w.grad_out)
+        smp = lambda: msda.dat_sample(x, w.hw, pos, validate=False)
+        smp_b = lambda: msda.dat_sample_backward(x, w.hw, pos, gs, validate=False)
+        out, lse = msda.dat_attention(q, k, v)
+        att = lambda: msda.dat_attention(q, k, v)
+        att_b = lambda: msda.dat_attention_backward(q, k, v, out, lse, g)
+        for fn in (smp, smp_b, att, att_b):
+            for _ in range(3):
+                fn()
+        mm = 2.0 * B * Hh * N * Ns * d            # flops of one N x Ns x d product
+        r = {"B": B, "N": N, "Ns": Ns, "heads": Hh, "head_dim": d, "groups": dims["G"],
+             "sample_fwd_us": time_forward(torch, smp, reps, None),
+             "sample_bwd_us": time_forward(torch, smp_b, reps, None),
+             "attn_fwd_us": time_forward(torch, att, reps, flush),
+             "attn_bwd_us": time_forward(torch, att_b, reps, None)}
+        # where the sampling backward's time goes (the core's stage events)
+        ss, st = msda._binding._level_of(w.hw, x.device)
+        ones = msda._binding._ones_of((B, Ns, dims["G"], 1, 1), x.device)
+        loc = pos.reshape(B, Ns, dims["G"], 1, 1, 2)
+        ev = msda.make_events()
+        msda.backward(x, ss, st, loc, ones, gs, validate=False, align_corners=True, events=ev)
+        torch.cuda.synchronize()
+        r["sample_bwd_stages_us"] = dict(zip(msda.BWD_STAGES, msda.stage_times(ev)))
+        r["attn_fwd_tflops"] = 2 * mm / r["attn_fwd_us"] / 1e6
+        r["attn_bwd_tflops"] = 7 * mm / r["attn_bwd_us"] / 1e6
+        r["attn_fwd_frac_of_fp32_mfma_peak"] = r["attn_fwd_tflops"] / MFMA_FP32_PEAK_TFLOPS
+        res[name] = r
+    log(f"dat: {json.dumps(res)}")
+    return res
+
+
 def cpu_baseline(w, min_seconds=10.0):
     import oracle
     pts = w.points
@@ -422,6 +471,7 @@ def main():
         extra["train_bf16"] = trn
         extra["fused_encoder"] = measure_fused(torch, msda, args.reps, flush)
         extra["volume"] = measure_volume(torch, msda, args.reps, flush)
+        extra["dat"] = measure_dat(torch, msda, args.reps, flush)
 
     result = {
         "metric": "sampled points/s (fwd+bwd) at the DETR encoder shape",

@@ -520,10 +520,26 @@ def backward3d(value: torch.Tensor, volume_shapes: torch.Tensor, level_start_ind
 # ---------------------------------------------------------------------------
 # DAT: deformable sampling of keys/values and the attention against them
 # ---------------------------------------------------------------------------
+_dat_cache = {}
+
+
 def _level_of(hw, dev):
+    """The one-level table (H, W), start 0 on dev, built once per (H, W, device)
+    (building it is a host-to-device copy)."""
     H, W = (int(v) for v in hw)
-    return (torch.tensor([[H, W]], dtype=torch.int64, device=dev),
-            torch.zeros(1, dtype=torch.int64, device=dev))
+    key = ("level", H, W, dev.type, dev.index)
+    if key not in _dat_cache:
+        _dat_cache[key] = (torch.tensor([[H, W]], dtype=torch.int64, device=dev),
+                           torch.zeros(1, dtype=torch.int64, device=dev))
+    return _dat_cache[key]
+
+
+def _ones_of(shape, dev):
+    """A cached all-ones fp32 weight tensor of this shape on dev."""
+    key = ("ones", tuple(shape), dev.type, dev.index)
+    if key not in _dat_cache:
+        _dat_cache[key] = torch.ones(shape, dtype=torch.float32, device=dev)
+    return _dat_cache[key]
 
 
 def dat_sample(x: torch.Tensor, hw, pos: torch.Tensor, validate: bool = True) -> torch.Tensor:
@@ -533,7 +549,7 @@ def dat_sample(x: torch.Tensor, hw, pos: torch.Tensor, validate: bool = True) ->
     B, Nv, G, Dg = x.shape
     Ns = pos.shape[1]
     ss, st = _level_of(hw, x.device)
-    ones = torch.ones((B, Ns, G, 1, 1), dtype=torch.float32, device=x.device)
+    ones = _ones_of((B, Ns, G, 1, 1), x.device)
     return forward(x, ss, st, pos.reshape(B, Ns, G, 1, 1, 2), ones, validate=validate,
                    align_corners=True)
 
@@ -544,7 +560,7 @@ def dat_sample_backward(x: torch.Tensor, hw, pos: torch.Tensor, grad_sampled: to
     B, Nv, G, Dg = x.shape
     Ns = pos.shape[1]
     ss, st = _level_of(hw, x.device)
-    ones = torch.ones((B, Ns, G, 1, 1), dtype=torch.float32, device=x.device)
+    ones = _ones_of((B, Ns, G, 1, 1), x.device)
     gx, gl, _ = backward(x, ss, st, pos.reshape(B, Ns, G, 1, 1, 2), ones,
                          grad_sampled.contiguous(), validate=validate, align_corners=True)
     return gx, gl.reshape(B, Ns, G, 2)

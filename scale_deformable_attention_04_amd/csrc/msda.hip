@@ -642,8 +642,9 @@ bin_count_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__
 // backward: scan of the bin counts, work list
 // One workgroup of kScanThreads.  Bins are visited in (batch, tile, head)
 // order, which is also their order in memory: the bins of batch b are the
-// nbins * M words from b * nb_max * M on.  Each bin of n > 0 points becomes
-// ceil(n / kChunk) work items (bin, first record, records, whole bin).
+// nbins * M words from b * nb_max * M on; all batches form one flat scan.
+// Each bin of n > 0 points becomes ceil(n / kChunk) work items (bin, first
+// record, records, whole bin).
 // ---------------------------------------------------------------------------
 // Exclusive scan of (a, b) pairs over the kScanThreads threads of the block:
 // wave-level scans with lane shuffles, then one scan of the wave totals.
@@ -679,41 +680,44 @@ bin_scan_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ 
     __shared__ LevelLds s_lv;
     __shared__ uint2 s_wave[kScanThreads / 64 + 1];
     stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
+    // the used bins of every batch as one flat sequence f = b * per_b + (tile * M + m),
+    // scanned in one pass (the bins of batch b start at b * nb_max * M in memory)
     const uint32_t per_b = (uint32_t)s_lv.nbins * (uint32_t)dm.M;
+    const uint32_t stride_b = (uint32_t)dm.nb_max * (uint32_t)dm.M;
+    const uint32_t nf = per_b * (uint32_t)B;
     uint32_t carry_e = 0, carry_c = 0;
-    for (int b = 0; b < B; ++b) {
-        const uint32_t off_b = (uint32_t)b * (uint32_t)dm.nb_max * (uint32_t)dm.M;
-        for (uint32_t base = 0; base < per_b; base += kScanThreads * kPer) {
-            const uint32_t g0 = base + threadIdx.x * kPer;
-            uint32_t cnt[kPer], e = 0, ch = 0;
+    for (uint32_t base = 0; base < nf; base += kScanThreads * kPer) {
+        const uint32_t g0 = base + threadIdx.x * kPer;
+        uint32_t cnt[kPer], bin[kPer], e = 0, ch = 0;
 #pragma unroll
-            for (int i = 0; i < kPer; ++i) {
-                cnt[i] = g0 + i < per_b ? counts[off_b + g0 + i] : 0u;
-                e += cnt[i];
-                ch += (cnt[i] + kChunk - 1) / kChunk;
-            }
-            uint32_t tot_e, tot_c;
-            block_exclusive_scan2(e, ch, s_wave, tot_e, tot_c);
-            e += carry_e;
-            ch += carry_c;
-#pragma unroll
-            for (int i = 0; i < kPer; ++i) {
-                if (g0 + i < per_b) {
-                    const uint32_t bin = off_b + g0 + i;
-                    start[bin] = e;
-                    cursor[bin] = e;
-                    const uint32_t nch = (cnt[i] + kChunk - 1) / kChunk;
-                    for (uint32_t k = 0; k < nch; ++k)
-                        items[ch + k] = make_uint4(bin, e + k * kChunk,
-                                                   min((uint32_t)kChunk, cnt[i] - k * kChunk),
-                                                   nch == 1 ? 1u : 0u);
-                    e += cnt[i];
-                    ch += nch;
-                }
-            }
-            carry_e += tot_e;
-            carry_c += tot_c;
+        for (int i = 0; i < kPer; ++i) {
+            const uint32_t f = g0 + i;
+            const uint32_t b = per_b ? f / per_b : 0u;
+            bin[i] = b * stride_b + (f - b * per_b);
+            cnt[i] = f < nf ? counts[bin[i]] : 0u;
+            e += cnt[i];
+            ch += (cnt[i] + kChunk - 1) / kChunk;
         }
+        uint32_t tot_e, tot_c;
+        block_exclusive_scan2(e, ch, s_wave, tot_e, tot_c);
+        e += carry_e;
+        ch += carry_c;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            if (g0 + i < nf) {
+                start[bin[i]] = e;
+                cursor[bin[i]] = e;
+                const uint32_t nch = (cnt[i] + kChunk - 1) / kChunk;
+                for (uint32_t k = 0; k < nch; ++k)
+                    items[ch + k] = make_uint4(bin[i], e + k * kChunk,
+                                               min((uint32_t)kChunk, cnt[i] - k * kChunk),
+                                               nch == 1 ? 1u : 0u);
+                e += cnt[i];
+                ch += nch;
+            }
+        }
+        carry_e += tot_e;
+        carry_c += tot_c;
     }
     if (threadIdx.x == 0) *work_total = carry_c;
 }
