@@ -18,6 +18,11 @@ Modes:
       The 3-D trilinear variant on the voxel workload: forward and backward
       (5 each), then the calibration multiply.
 
+  python3 profile_kernels.py run-dat
+      DAT's sampled-key attention at its detection configuration (B=2, 4096
+      tokens, 256 keys, 12 heads of 32, 6 groups): sampling forward/backward
+      and attention forward/backward (5 each), then the calibration multiply.
+
   python3 profile_kernels.py summarize --stats DIR --fetch DIR --write DIR
       Reads the CSV output of three rocprofv3 runs (kernel-trace stats of the
       bench command itself; --pmc FETCH_SIZE and --pmc WRITE_SIZE of `run`)
@@ -33,6 +38,10 @@ Modes:
       The same from the three runs of `run-volume`: profiles/volume_kernels.txt and
       profiles/volume_traffic.json.
 
+  python3 profile_kernels.py summarize-dat --stats DIR --fetch DIR --write DIR
+      The same from the three runs of `run-dat`: profiles/dat_kernels.txt and
+      profiles/dat_traffic.json.
+
 The GPU commands (run from /tmp with TMPDIR=/tmp, outputs under gpurun_out):
   rocprofv3 --kernel-trace --stats --output-format csv -d OUT/stats -o run -- python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline
   rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/fetch -o run -- python3 profile_kernels.py run
@@ -43,6 +52,9 @@ The GPU commands (run from /tmp with TMPDIR=/tmp, outputs under gpurun_out):
   rocprofv3 --kernel-trace --stats --output-format csv -d OUT/vstats -o run -- python3 profile_kernels.py run-volume
   rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/vfetch -o run -- python3 profile_kernels.py run-volume
   rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/vwrite -o run -- python3 profile_kernels.py run-volume
+  rocprofv3 --kernel-trace --stats --output-format csv -d OUT/dstats -o run -- python3 profile_kernels.py run-dat
+  rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/dfetch -o run -- python3 profile_kernels.py run-dat
+  rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/dwrite -o run -- python3 profile_kernels.py run-dat
 """
 from __future__ import annotations
 
@@ -143,6 +155,28 @@ def run_volume():
     print("profile workload done", flush=True)
 
 
+def run_dat():
+    import torch
+    import scale_deformable_attention_04_amd as msda
+    import workloads
+    w = workloads.make_dat("dat_det")
+    t = lambda a: torch.from_numpy(a).cuda()
+    x, pos, gs = t(w.x), t(w.pos), t(w.grad_sampled)
+    q, k, v, g = t(w.q), t(w.k), t(w.v), t(w.grad_out)
+    for _ in range(5):
+        msda.dat_sample(x, w.hw, pos, validate=False)
+        msda.dat_sample_backward(x, w.hw, pos, gs, validate=False)
+        out, lse = msda.dat_attention(q, k, v)
+        msda.dat_attention_backward(q, k, v, out, lse, g)
+    torch.cuda.synchronize()
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 2.0, out=dst)
+    torch.cuda.synchronize()
+    print("profile workload done", flush=True)
+
+
 def _rows(path_glob):
     rows = []
     for f in sorted(glob.glob(path_glob, recursive=True)):
@@ -171,6 +205,11 @@ HEADERS = {
                "# trilinear variant on the voxel workload (pyramid 4x128x128, 2x64x64, 1x32x32;",
                "# Nq=16384, M=8, D=32, K=4, fp32): 5 x (forward, backward with its grad_value",
                "# zero-fill), then the 256 MiB calibration multiply"],
+    "dat": ["# rocprofv3 --kernel-trace --stats of profile_kernels.py run-dat: DAT's",
+            "# sampled-key attention at the detection configuration (B=2, 64x64 tokens, 16x16",
+            "# = 256 sampled keys, 12 heads of 32, 6 offset groups of 64 channels, fp32): 5 x",
+            "# (sampling forward and backward through the core, attention forward and",
+            "# backward), then the 256 MiB calibration multiply"],
 }
 
 
@@ -212,7 +251,8 @@ def main():
     sub.add_parser("run")
     sub.add_parser("run-fused")
     sub.add_parser("run-volume")
-    for mode in ("summarize", "summarize-fused", "summarize-volume"):
+    sub.add_parser("run-dat")
+    for mode in ("summarize", "summarize-fused", "summarize-volume", "summarize-dat"):
         s = sub.add_parser(mode)
         s.add_argument("--stats", required=True)
         s.add_argument("--fetch", required=True)
@@ -224,8 +264,10 @@ def main():
         run_fused()
     elif a.mode == "run-volume":
         run_volume()
+    elif a.mode == "run-dat":
+        run_dat()
     else:
-        doc = __doc__.split("The GPU commands")[1].splitlines()[1:10]
+        doc = __doc__.split("The GPU commands")[1].splitlines()[1:13]
         cmds = [c.strip() for c in doc]
         if a.mode == "summarize":
             summarize(a.stats, a.fetch, a.write,
@@ -233,9 +275,12 @@ def main():
         elif a.mode == "summarize-fused":
             summarize(a.stats, a.fetch, a.write,
                       {"stats": cmds[3], "fetch": cmds[4], "write": cmds[5]}, "fused_encoder")
-        else:
+        elif a.mode == "summarize-volume":
             summarize(a.stats, a.fetch, a.write,
                       {"stats": cmds[6], "fetch": cmds[7], "write": cmds[8]}, "volume")
+        else:
+            summarize(a.stats, a.fetch, a.write,
+                      {"stats": cmds[9], "fetch": cmds[10], "write": cmds[11]}, "dat")
 
 
 if __name__ == "__main__":
