@@ -43,7 +43,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 FLUSH_BYTES = 512 << 20   # > the 256 MB Infinity Cache
 KERNEL_SOURCES = [os.path.join(ROOT, "scale_deformable_attention_04_amd", "csrc", f)
-                  for f in ("common.h", "msda.hip", "msda3d.hip", "dat_attn.hip")]
+                  for f in ("common.h", "bins.h", "msda.hip", "msda3d.hip", "dat_attn.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 # kernel names as rocprofv3 reports them, per stage of a step

@@ -71,7 +71,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 KERNEL_SOURCES = [os.path.join(ROOT, "scale_deformable_attention_04_amd", "csrc", f)
-                  for f in ("common.h", "msda.hip", "msda3d.hip", "dat_attn.hip")]
+                  for f in ("common.h", "bins.h", "msda.hip", "msda3d.hip", "dat_attn.hip")]
 COPY_BYTES = 256 << 20
 
 

@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "msda.hip")
 SOURCES = [SRC, os.path.join(PKG, "csrc", "msda3d.hip"), os.path.join(PKG, "csrc", "dat_attn.hip")]
-DEPS = SOURCES + [os.path.join(PKG, "csrc", "common.h")]
+DEPS = SOURCES + [os.path.join(PKG, "csrc", f) for f in ("common.h", "bins.h")]
 HEADER = os.path.join(ROOT, "include", "msda.h")
 LIB = os.path.join(PKG, "libmsda.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
