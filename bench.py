@@ -262,7 +262,7 @@ def measure_volume(torch, msda, reps, flush):
     val, loc, attn, rows = B * Nv * M * D * 4, pts * 12, pts * 4, B * Nq * M * D * 4
     fwd_bytes = val + loc + attn + rows
     # backward: value, loc, attn, grad_out read; grad_loc, grad_attn written;
-    # grad_value zero-filled and then read-modify-written once
+    # grad_value zero-filled and then written once per voxel
     bwd_bytes = val + loc + attn + rows + loc + attn + 2 * val
     out = torch.empty(B, Nq, M * D, device=d)
     fwd = lambda: msda.forward3d(**x, out=out, validate=False)
@@ -280,8 +280,7 @@ def measure_volume(torch, msda, reps, flush):
            "forward": {"us_cold": cold, "us_warm": warm, "algorithmic_bytes": fwd_bytes,
                        "algorithmic_GBps": fwd_bytes / cold / 1e3},
            "backward": {"us_warm": bw, "algorithmic_bytes": bwd_bytes,
-                        "algorithmic_GBps": bwd_bytes / bw / 1e3,
-                        "grad_value_atomic_adds": pts * 8 * D}}
+                        "algorithmic_GBps": bwd_bytes / bw / 1e3}}
     log(f"volume: {json.dumps(res)}")
     return res
 

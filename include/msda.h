@@ -298,11 +298,19 @@ msda_status msda_backward_fused(const void *value, int value_dtype,
  * msda3d_backward: the exact derivatives, as for the 2-D core with the
  * eight neighbours (grad_loc.z carries the factor Z_l, or Z_l - 1 with
  * MSDA_ALIGN_CORNERS).  grad_value is zero-filled first unless flags has
- * MSDA_BWD_ACCUMULATE, and receives the scatter through fp32 atomic adds,
- * so its summation order is not fixed; grad_sampling_loc and
- * grad_attn_weight are overwritten and deterministic.  No workspace and no
- * side stream: everything runs on `stream`.
+ * MSDA_BWD_ACCUMULATE; it is summed per 8x8 tile of each plane as in the 2-D
+ * backward (atomic adds only where a tile is split), so its last bits may
+ * differ between calls; grad_sampling_loc and grad_attn_weight are
+ * overwritten and deterministic.  workspace: at least
+ * msda3d_backward_workspace_size(...) bytes (128 bytes per point -- up to
+ * eight 16-byte records, two planes of four tiles -- plus about 12 bytes
+ * per voxel and head), 256-byte aligned, caller-owned, contents irrelevant.
+ * The backward uses the library's side stream as msda_backward does; also
+ * needs Nq <= 2^25.
  */
+size_t msda3d_backward_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
+                                      int64_t L, int64_t K);
+
 msda_status msda3d_forward(const void *value, int value_dtype,
                            const int64_t *volume_shapes, const int64_t *level_start_index,
                            const float *sampling_loc, const float *attn_weight, float *out,
@@ -315,7 +323,8 @@ msda_status msda3d_backward(const void *value, int value_dtype,
                             const float *grad_out, float *grad_value,
                             float *grad_sampling_loc, float *grad_attn_weight,
                             int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
-                            int64_t L, int64_t K, uint32_t flags, void *stream);
+                            int64_t L, int64_t K, void *workspace, size_t workspace_bytes,
+                            uint32_t flags, void *stream);
 
 /* msda_validate_host for the 3-D variant: a HOST copy of volume_shapes [L, 3]. */
 msda_status msda3d_validate_host(const int64_t *volume_shapes_host,

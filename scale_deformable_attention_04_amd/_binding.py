@@ -31,7 +31,8 @@ MSDA_SOFTMAX_PER_LEVEL = 4
 
 EXPORTED = ("msda_forward", "msda_backward_workspace_size", "msda_backward",
             "msda_backward_events", "msda_forward_fused", "msda_backward_fused_workspace_size",
-            "msda_backward_fused", "msda3d_forward", "msda3d_backward", "msda3d_validate_host",
+            "msda_backward_fused", "msda3d_forward", "msda3d_backward_workspace_size",
+            "msda3d_backward", "msda3d_validate_host",
             "msda_dat_attention_forward", "msda_dat_attention_workspace_size",
             "msda_dat_attention_backward",
             "msda_validate_host", "msda_status_string", "msda_last_hip_error")
@@ -79,7 +80,10 @@ def load():
     lib.msda_backward_fused.restype = ci
     lib.msda3d_forward.argtypes = [p, ci, p, p, p, p, p] + [i64] * 7 + [u32, p]
     lib.msda3d_forward.restype = ci
-    lib.msda3d_backward.argtypes = [p, ci, p, p, p, p, p, p, p, p] + [i64] * 7 + [u32, p]
+    lib.msda3d_backward.argtypes = ([p, ci, p, p, p, p, p, p, p, p] + [i64] * 7 +
+                                    [p, ctypes.c_size_t, u32, p])
+    lib.msda3d_backward_workspace_size.argtypes = [i64] * 7
+    lib.msda3d_backward_workspace_size.restype = ctypes.c_size_t
     lib.msda3d_backward.restype = ci
     lib.msda3d_validate_host.argtypes = [p, p] + [i64] * 7
     lib.msda3d_validate_host.restype = ci
@@ -488,10 +492,16 @@ def forward3d(value: torch.Tensor, volume_shapes: torch.Tensor, level_start_inde
     return out
 
 
+def workspace_size3d(B, Nv, Nq, M, D, L, K) -> int:
+    """msda3d_backward_workspace_size."""
+    return int(load().msda3d_backward_workspace_size(B, Nv, Nq, M, D, L, K))
+
+
 def backward3d(value: torch.Tensor, volume_shapes: torch.Tensor, level_start_index: torch.Tensor,
                sampling_loc: torch.Tensor, attn_weight: torch.Tensor, grad_out: torch.Tensor,
                grad_value: Optional[torch.Tensor] = None, accumulate: bool = False,
-               validate: bool = True, align_corners: bool = False):
+               validate: bool = True, align_corners: bool = False,
+               workspace: Optional[torch.Tensor] = None):
     """msda3d_backward: (grad_value fp32 [B,Nv,M,D], grad_sampling_loc, grad_attn_weight)."""
     lib = load()
     dev, (B, Nv, Nq, M, D, L, K) = _check_inputs3d(value, volume_shapes, level_start_index,
@@ -506,12 +516,18 @@ def backward3d(value: torch.Tensor, volume_shapes: torch.Tensor, level_start_ind
     g_loc = torch.empty_like(sampling_loc)
     g_attn = torch.empty_like(attn_weight)
     flags = (MSDA_BWD_ACCUMULATE if accumulate else 0) | (MSDA_ALIGN_CORNERS if align_corners else 0)
+    need = workspace_size3d(B, Nv, Nq, M, D, L, K)
+    if workspace is None:
+        workspace = _workspace(dev, need)
+    elif workspace.device != dev or workspace.dtype != torch.uint8 or workspace.numel() < need:
+        raise ValueError(f"workspace must be a uint8 tensor on {dev} of >= {need} bytes")
+    ws_bytes = workspace.numel() if workspace is not None else 0
     with torch.cuda.device(dev):
         stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
         rc = lib.msda3d_backward(_ptr(value), _dtype_code(value), _ptr(volume_shapes),
                                  _ptr(level_start_index), _ptr(sampling_loc), _ptr(attn_weight),
                                  _ptr(grad_out), _ptr(grad_value), _ptr(g_loc), _ptr(g_attn),
-                                 B, Nv, Nq, M, D, L, K, flags, stream)
+                                 B, Nv, Nq, M, D, L, K, _ptr(workspace), ws_bytes, flags, stream)
     if rc != MSDA_OK:
         raise MSDAError(rc, "msda3d_backward")
     return grad_value, g_loc, g_attn

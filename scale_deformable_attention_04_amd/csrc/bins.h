@@ -59,10 +59,15 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
 // Level table staged in LDS.  lvl[l] = (H, W, start, first bin of the level);
 // a level whose pixels do not fit inside value, or whose tiles would not fit
 // the bin stride, becomes (0, 0, 0, first bin) and has no pixel and no bin.
+// For volumes (the 3-D variant) a level is zp[l] planes of H x W voxels, the
+// plane z starting at row start + z*H*W, and its bins are the tiles of its
+// planes, plane-major (tpp[l] tiles per plane).
 struct LevelLds {
     int4 lvl[kMaxLevels];
-    int tw[kMaxLevels];  // tiles along W
-    int nbins;           // bins of one (batch, head)
+    int tw[kMaxLevels];   // tiles along W
+    int zp[kMaxLevels];   // planes (volumes only)
+    int tpp[kMaxLevels];  // tiles per plane (volumes only)
+    int nbins;            // bins of one (batch, head)
 };
 
 __device__ __forceinline__ void stage_levels(LevelLds *s, const int64_t *shapes,
@@ -93,6 +98,74 @@ __device__ __forceinline__ void stage_levels(LevelLds *s, const int64_t *shapes,
         s->nbins = tb;
     }
     __syncthreads();
+}
+
+// The same for a volume level table [L, 3] with rows (Z, H, W).
+__device__ __forceinline__ void stage_volume_levels(LevelLds *s, const int64_t *shapes,
+                                                    const int64_t *starts, int L, int Nv,
+                                                    int nb_max) {
+    const int t = threadIdx.x;
+    if (t < L) {
+        const int64_t Z = shapes[3 * t], H = shapes[3 * t + 1], W = shapes[3 * t + 2];
+        const int64_t S = starts[t];
+        const bool dims_ok = Z >= 1 && H >= 1 && W >= 1 && Z <= Nv && H <= Nv && W <= Nv;
+        const bool ok = dims_ok && S >= 0 && S <= Nv && H * W <= Nv && Z * (H * W) <= Nv - S;
+        s->lvl[t] = ok ? make_int4((int)H, (int)W, (int)S, 0) : make_int4(0, 0, 0, 0);
+        s->zp[t] = ok ? (int)Z : 0;
+    }
+    __syncthreads();
+    if (t == 0) {
+        int tb = 0;
+        for (int l = 0; l < L; ++l) {
+            int4 v = s->lvl[l];
+            const int tw = (v.y + kTile - 1) >> kTileShift, th = (v.x + kTile - 1) >> kTileShift;
+            const int tpp = tw * th;
+            // every tile holds a voxel, so a level has at most as many bins as voxels (< 2^31)
+            int n = tpp * s->zp[l];
+            if (n > nb_max - tb) {  // keep every bin inside the caller's workspace
+                v = make_int4(0, 0, 0, 0);
+                n = 0;
+            }
+            v.w = tb;
+            s->lvl[l] = v;
+            s->tw[l] = n ? tw : 0;
+            s->tpp[l] = n ? tpp : 0;
+            s->zp[l] = n ? s->zp[l] : 0;
+            tb += n;
+        }
+        s->nbins = tb;
+    }
+    __syncthreads();
+}
+
+template <bool VOL>
+__device__ __forceinline__ void stage_bin_levels(LevelLds *s, const int64_t *shapes,
+                                                 const int64_t *starts, int L, int Nv, int nb_max) {
+    if constexpr (VOL)
+        stage_volume_levels(s, shapes, starts, L, Nv, nb_max);
+    else
+        stage_levels(s, shapes, starts, L, Nv, nb_max);
+}
+
+// The two planes a volume point's neighbours lie in: z0 (bit 0 of the mask)
+// and z0 + 1 (bit 1), those inside [0, Z); fz is the fractional part of the
+// voxel coordinate z = w*Z - 0.5 (or w*(Z - 1) with align_corners), formed
+// like x and y.
+struct Planes {
+    int z0;          // clamped to [-1, Z]
+    uint32_t mask;
+    float fz;
+};
+
+__device__ __forceinline__ Planes point_planes(float w, int Z, bool align) {
+    const float zc = __builtin_fmaf(w, align ? (float)(Z - 1) : (float)Z, align ? 0.f : -0.5f);
+    const float z0 = floorf(zc);
+    Planes p;
+    p.fz = zc - z0;
+    const bool v0 = z0 >= 0.f && z0 <= (float)(Z - 1), v1 = z0 >= -1.f && z0 <= (float)(Z - 2);
+    p.mask = (v0 ? 1u : 0u) | (v1 ? 2u : 0u);
+    p.z0 = (int)fminf(fmaxf(z0, -1.f), (float)Z);
+    return p;
 }
 
 // Neighbours of one sampling point, in the order TL (x0,y0), TR (x0+1,y0),
@@ -221,6 +294,9 @@ struct Work {
 constexpr int kBinPPT = 16;
 constexpr int kBinPoints = kBinPPT * kThreads;
 
+// VOL: volume levels; a location is (u, v, w) and a point feeds the tiles of
+// its two planes.
+template <bool VOL>
 __global__ void __launch_bounds__(kThreads)
 bin_count_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ starts,
                  const float *__restrict__ loc, uint32_t *__restrict__ counts, int hist_cap,
@@ -238,16 +314,24 @@ bin_count_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__
     const size_t row0 = (size_t)b * Nq * M + m;  // item row of query 0
 
     float2 uv[kBinPPT];
+    float wz[kBinPPT];  // VOL: the z coordinate
 #pragma unroll
     for (int r = 0; r < kBinPPT; ++r) {
         const int f = f0 + threadIdx.x + r * kThreads;
         uv[r] = make_float2(0.f, 0.f);
+        wz[r] = 0.f;
         if (f < nf) {
             const int q = (int)fdiv((uint32_t)f, dm.div_lk), j = f - q * LK;
-            uv[r] = reinterpret_cast<const float2 *>(loc)[(row0 + (size_t)q * M) * LK + j];
+            const size_t p = (row0 + (size_t)q * M) * LK + j;
+            if constexpr (VOL) {
+                uv[r] = make_float2(loc[3 * p], loc[3 * p + 1]);
+                wz[r] = loc[3 * p + 2];
+            } else {
+                uv[r] = reinterpret_cast<const float2 *>(loc)[p];
+            }
         }
     }
-    stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
+    stage_bin_levels<VOL>(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
     const int nbins = s_lv.nbins;
     const bool lds = nbins <= hist_cap;
     uint32_t *gcount = counts + (size_t)b * dm.nb_max * M + m;  // tile i at gcount[i * M]
@@ -265,16 +349,26 @@ bin_count_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__
             const TileMask tm = point_tile_mask(n);
             const int tw = s_lv.tw[l];
             const int b00 = s_lv.lvl[l].w + tm.ty0 * tw + tm.tx0;
-            if (lds) {
-                if (tm.mask & 1u) atomicAdd(&s_cnt[b00], 1u);
-                if (tm.mask & 2u) atomicAdd(&s_cnt[b00 + 1], 1u);
-                if (tm.mask & 4u) atomicAdd(&s_cnt[b00 + tw], 1u);
-                if (tm.mask & 8u) atomicAdd(&s_cnt[b00 + tw + 1], 1u);
+            auto add = [&](int bb) {
+                if (lds) {
+                    if (tm.mask & 1u) atomicAdd(&s_cnt[bb], 1u);
+                    if (tm.mask & 2u) atomicAdd(&s_cnt[bb + 1], 1u);
+                    if (tm.mask & 4u) atomicAdd(&s_cnt[bb + tw], 1u);
+                    if (tm.mask & 8u) atomicAdd(&s_cnt[bb + tw + 1], 1u);
+                } else {
+                    if (tm.mask & 1u) atomicAdd(&gcount[(size_t)bb * M], 1u);
+                    if (tm.mask & 2u) atomicAdd(&gcount[(size_t)(bb + 1) * M], 1u);
+                    if (tm.mask & 4u) atomicAdd(&gcount[(size_t)(bb + tw) * M], 1u);
+                    if (tm.mask & 8u) atomicAdd(&gcount[(size_t)(bb + tw + 1) * M], 1u);
+                }
+            };
+            if constexpr (VOL) {
+                const Planes pl = point_planes(wz[r], s_lv.zp[l], dm.align);
+                const int tpp = s_lv.tpp[l];
+                if (pl.mask & 1u) add(b00 + pl.z0 * tpp);
+                if (pl.mask & 2u) add(b00 + (pl.z0 + 1) * tpp);
             } else {
-                if (tm.mask & 1u) atomicAdd(&gcount[(size_t)b00 * M], 1u);
-                if (tm.mask & 2u) atomicAdd(&gcount[(size_t)(b00 + 1) * M], 1u);
-                if (tm.mask & 4u) atomicAdd(&gcount[(size_t)(b00 + tw) * M], 1u);
-                if (tm.mask & 8u) atomicAdd(&gcount[(size_t)(b00 + tw + 1) * M], 1u);
+                add(b00);
             }
         }
     }
@@ -320,6 +414,7 @@ __device__ __forceinline__ void block_exclusive_scan2(uint32_t &a, uint32_t &b, 
     __syncthreads();  // s_wave is reused by the next call
 }
 
+template <bool VOL>
 __global__ void __launch_bounds__(kScanThreads)
 bin_scan_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ starts,
                 const uint32_t *__restrict__ counts, uint32_t *__restrict__ start,
@@ -328,7 +423,7 @@ bin_scan_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ 
     constexpr int kPer = 8;
     __shared__ LevelLds s_lv;
     __shared__ uint2 s_wave[kScanThreads / 64 + 1];
-    stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
+    stage_bin_levels<VOL>(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
     // the used bins of every batch as one flat sequence f = b * per_b + (tile * M + m),
     // scanned in one pass (the bins of batch b start at b * nb_max * M in memory)
     const uint32_t per_b = (uint32_t)s_lv.nbins * (uint32_t)dm.M;
@@ -382,6 +477,7 @@ constexpr int kCellsW = kTile + 1;
 constexpr int kCells = kCellsW * kCellsW;
 constexpr int kRecQueryShift = 7;  // cells < 128
 
+template <bool VOL>
 __global__ void __launch_bounds__(kThreads)
 bin_scatter_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ starts,
                    const float *__restrict__ loc, const float *__restrict__ attn,
@@ -403,19 +499,26 @@ bin_scatter_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict
     // the thread's points: coordinates and weights, kept for both passes
     float2 uv[kBinPPT];
     float aw[kBinPPT];
+    float wz[kBinPPT];  // VOL: the z coordinate
 #pragma unroll
     for (int r = 0; r < kBinPPT; ++r) {
         const int f = f0 + threadIdx.x + r * kThreads;
         uv[r] = make_float2(0.f, 0.f);
         aw[r] = 0.f;
+        wz[r] = 0.f;
         if (f < nf) {
             const int q = (int)fdiv((uint32_t)f, dm.div_lk), j = f - q * LK;
             const size_t p = (row0 + (size_t)q * M) * LK + j;
-            uv[r] = reinterpret_cast<const float2 *>(loc)[p];
+            if constexpr (VOL) {
+                uv[r] = make_float2(loc[3 * p], loc[3 * p + 1]);
+                wz[r] = loc[3 * p + 2];
+            } else {
+                uv[r] = reinterpret_cast<const float2 *>(loc)[p];
+            }
             aw[r] = attn[p];
         }
     }
-    stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
+    stage_bin_levels<VOL>(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
     const int nbins = s_lv.nbins;
     const bool lds = nbins <= hist_cap;
     uint32_t *gcur = cursor + (size_t)b * dm.nb_max * M + m;  // tile i at gcur[i * M]
@@ -432,10 +535,20 @@ bin_scatter_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict
                 const TileMask tm = point_tile_mask(n);
                 const int tw = s_lv.tw[l];
                 const int b00 = s_lv.lvl[l].w + tm.ty0 * tw + tm.tx0;
-                if (tm.mask & 1u) atomicAdd(&s_cnt[b00], 1u);
-                if (tm.mask & 2u) atomicAdd(&s_cnt[b00 + 1], 1u);
-                if (tm.mask & 4u) atomicAdd(&s_cnt[b00 + tw], 1u);
-                if (tm.mask & 8u) atomicAdd(&s_cnt[b00 + tw + 1], 1u);
+                auto add = [&](int bb) {
+                    if (tm.mask & 1u) atomicAdd(&s_cnt[bb], 1u);
+                    if (tm.mask & 2u) atomicAdd(&s_cnt[bb + 1], 1u);
+                    if (tm.mask & 4u) atomicAdd(&s_cnt[bb + tw], 1u);
+                    if (tm.mask & 8u) atomicAdd(&s_cnt[bb + tw + 1], 1u);
+                };
+                if constexpr (VOL) {
+                    const Planes pl = point_planes(wz[r], s_lv.zp[l], dm.align);
+                    const int tpp = s_lv.tpp[l];
+                    if (pl.mask & 1u) add(b00 + pl.z0 * tpp);
+                    if (pl.mask & 2u) add(b00 + (pl.z0 + 1) * tpp);
+                } else {
+                    add(b00);
+                }
             }
         }
         __syncthreads();
@@ -456,22 +569,34 @@ bin_scatter_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict
             const TileMask tm = point_tile_mask(n);
             const int tw = s_lv.tw[l];
             const int b00 = s_lv.lvl[l].w + tm.ty0 * tw + tm.tx0;
-            const uint32_t a0 = __float_as_uint(aw[r] * (1.f - n.fx));
-            const uint32_t a1 = __float_as_uint(aw[r] * n.fx);
             const uint32_t fy = __float_as_uint(n.fy);
             // cell of the top-left neighbour relative to tile (tx0, ty0); one
             // tile to the right is 8 cells left, one tile down is 72 cells up
             const uint32_t key = ((uint32_t)q << kRecQueryShift);
             const int c00 = (n.xi - tm.tx0 * kTile + 1) + kCellsW * (n.yi - tm.ty0 * kTile + 1);
+            // the records of one plane: bins from bb, weight a = A (times the
+            // plane's z tent for volumes)
+            auto put = [&](int bb, float a) {
+                const uint32_t a0 = __float_as_uint(a * (1.f - n.fx));
+                const uint32_t a1 = __float_as_uint(a * n.fx);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                if (tm.mask & (1u << c)) {
-                    const int bin = b00 + (c & 1) + (c >> 1) * tw;
-                    const uint32_t slot = lds ? s_base[bin] + atomicAdd(&s_cnt[bin], 1u)
-                                              : atomicAdd(&gcur[(size_t)bin * M], 1u);
-                    const int cell = c00 - (c & 1) * kTile - (c >> 1) * kTile * kCellsW;
-                    recs[slot] = make_uint4(key | (uint32_t)cell, a0, a1, fy);
+                for (int c = 0; c < 4; ++c) {
+                    if (tm.mask & (1u << c)) {
+                        const int bin = bb + (c & 1) + (c >> 1) * tw;
+                        const uint32_t slot = lds ? s_base[bin] + atomicAdd(&s_cnt[bin], 1u)
+                                                  : atomicAdd(&gcur[(size_t)bin * M], 1u);
+                        const int cell = c00 - (c & 1) * kTile - (c >> 1) * kTile * kCellsW;
+                        recs[slot] = make_uint4(key | (uint32_t)cell, a0, a1, fy);
+                    }
                 }
+            };
+            if constexpr (VOL) {
+                const Planes pl = point_planes(wz[r], s_lv.zp[l], dm.align);
+                const int tpp = s_lv.tpp[l];
+                if (pl.mask & 1u) put(b00 + pl.z0 * tpp, aw[r] * (1.f - pl.fz));
+                if (pl.mask & 2u) put(b00 + (pl.z0 + 1) * tpp, aw[r] * pl.fz);
+            } else {
+                put(b00, aw[r]);
             }
         }
     }
@@ -533,7 +658,7 @@ __device__ __forceinline__ void pull_range(float4 &acc, const float *__restrict_
     for (; e < e2; ++e) fma4(acc, w[4 * e + (e < e1 ? r0 : r1)], g[e * kQuads]);
 }
 
-template <int D>
+template <int D, bool VOL>
 __global__ void __launch_bounds__(kTileThreads)
 grad_value_tile_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ starts,
                        const float *__restrict__ grad_out, const uint4 *__restrict__ items,
@@ -558,7 +683,7 @@ grad_value_tile_kernel(const int64_t *__restrict__ shapes, const int64_t *__rest
     const uint32_t total = *work_total;
     const uint32_t grid = gridDim.x;
     if (blockIdx.x >= total) return;  // the grid is sized for the largest possible list
-    stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
+    stage_bin_levels<VOL>(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
     if (tid < kCells) s_tmp[tid] = 0u;
 
     // Sub-chunk k (summed), k+1 (sorted, rows loading), k+2 (records loading),
@@ -684,7 +809,14 @@ grad_value_tile_kernel(const int64_t *__restrict__ shapes, const int64_t *__rest
                 while (l + 1 < dm.L && s_lv.lvl[l + 1].w <= lb) ++l;
                 const int4 lvl = s_lv.lvl[l];
                 const int tw = s_lv.tw[l];
-                const int ty = (lb - lvl.w) / tw, tx = (lb - lvl.w) - ty * tw;
+                int rel = lb - lvl.w;
+                int plane0 = lvl.z;  // first row of the tile's map (volumes: of its plane)
+                if constexpr (VOL) {
+                    const int zpl = rel / s_lv.tpp[l];
+                    rel -= zpl * s_lv.tpp[l];
+                    plane0 += zpl * lvl.x * lvl.y;
+                }
+                const int ty = rel / tw, tx = rel - ty * tw;
                 const size_t slice = (size_t)dm.Nv * M * D;
                 float *gv = grad_value + (size_t)b * slice + (size_t)m * D;
 #pragma unroll
@@ -697,7 +829,7 @@ grad_value_tile_kernel(const int64_t *__restrict__ shapes, const int64_t *__rest
                     float4 a = acc[o];
                     acc[o] = make_float4(0.f, 0.f, 0.f, 0.f);
                     if (gy >= lvl.x || gx >= lvl.y) continue;
-                    float *dst = gv + (size_t)(lvl.z + gy * lvl.y + gx) * M * D + 4 * q;
+                    float *dst = gv + (size_t)(plane0 + gy * lvl.y + gx) * M * D + 4 * q;
                     if (A.it.w) {
                         // this work item alone owns the pixel: plain read-add-write
                         float4 *d4 = reinterpret_cast<float4 *>(dst);
@@ -754,12 +886,17 @@ struct WorkLayout {
     size_t off_counts, off_start, off_cursor, off_items, off_total, off_sorted, bytes;
 };
 
-WorkLayout work_layout(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t L, int64_t K) {
+// The workspace of the pipeline.  2-D levels (vol = false): at most four
+// records per point and bins_bound(Nv, L) bins per (batch, head).  Volumes:
+// two planes of four tiles, so eight records per point, and at most one bin
+// per voxel (every tile of a plane holds a voxel).
+WorkLayout work_layout(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t L, int64_t K,
+                       bool vol = false) {
     WorkLayout w;
-    w.nb_max = bins_bound(Nv, L);
+    w.nb_max = vol ? Nv + 1 : bins_bound(Nv, L);
     w.bm_bins = B * M * w.nb_max;
     const int64_t pts = B * Nq * M * L * K;
-    w.sorted_max = 4 * pts;
+    w.sorted_max = (vol ? 8 : 4) * pts;
     w.work_max = w.bm_bins + (w.sorted_max + kChunk - 1) / kChunk;
     auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
     size_t o = 0;

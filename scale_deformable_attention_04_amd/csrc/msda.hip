@@ -725,14 +725,14 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
     st = per_batch(gb * M, [&](int64_t b0, unsigned grid) {
         Dims d2 = dm;
         d2.b0 = (int)b0;
-        hipLaunchKernelGGL(bin_count_kernel, dim3(grid), dim3(kThreads), 4 * (size_t)hist_cap, s,
+        hipLaunchKernelGGL(bin_count_kernel<false>, dim3(grid), dim3(kThreads), 4 * (size_t)hist_cap, s,
                            shapes, starts, loc, w.counts, hist_cap, d2);
     });
     if (st != MSDA_OK) return st;
     ex.stamp(3, true, s);
 
     ex.stamp(4, false, s);
-    hipLaunchKernelGGL(bin_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, shapes, starts,
+    hipLaunchKernelGGL(bin_scan_kernel<false>, dim3(1), dim3(kScanThreads), 0, s, shapes, starts,
                        w.counts, w.start, w.cursor, w.items, w.work_total, (int)B, dm);
     st = hip_status(hipGetLastError());
     if (st != MSDA_OK) return st;
@@ -742,7 +742,7 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
     st = per_batch(gb * M, [&](int64_t b0, unsigned grid) {
         Dims d2 = dm;
         d2.b0 = (int)b0;
-        hipLaunchKernelGGL(bin_scatter_kernel, dim3(grid), dim3(kThreads), 8 * (size_t)hist_cap,
+        hipLaunchKernelGGL(bin_scatter_kernel<false>, dim3(grid), dim3(kThreads), 8 * (size_t)hist_cap,
                            s, shapes, starts, loc, attn, w.cursor, w.recs, hist_cap, d2);
     });
     if (st != MSDA_OK) return st;
@@ -754,7 +754,7 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
         if (st != MSDA_OK) return st;
     }
     ex.stamp(6, false, s);
-    hipLaunchKernelGGL((grad_value_tile_kernel<D>), dim3((unsigned)grid), dim3(kTileThreads), 0, s,
+    hipLaunchKernelGGL((grad_value_tile_kernel<D, false>), dim3((unsigned)grid), dim3(kTileThreads), 0, s,
                        shapes, starts, gout, w.items, w.work_total, w.recs, gval, dm);
     st = hip_status(hipGetLastError());
     ex.stamp(6, true, s);

@@ -12,14 +12,18 @@
 // Forward (msda3d_fwd_kernel): per item, the sum over its points of A times
 // the trilinear sample, accumulated in registers, one store per item.
 //
-// Backward (msda3d_bwd_kernel): per point, the eight <grad_out row, neighbour
-// row> dot products (DPP reductions over the lane group) give grad_attn and
-// the three location gradients; grad_value receives A * w_c * grad_out in
-// each of the eight neighbour rows through range-checked buffer atomics (a
-// neighbour outside the volume has an offset beyond the buffer, so its add is
-// dropped by the hardware).
+// Backward:
+//   msda3d_dots_kernel (on the backward's side stream): per point, the eight
+//      <grad_out row, neighbour row> dot products (DPP reductions over the
+//      lane group) give grad_attn and the three location gradients.
+//   grad_value, concurrently, by the binned pipeline of the 2-D core (bins.h)
+//   with volume levels: a point's eight neighbours are the bilinear
+//   neighbours of (x, y) in its two planes z0 and z0 + 1, so it becomes two
+//   plane points of weights A (1 - fz) and A fz, whose records go to the 8x8
+//   tiles of those planes; the tile kernel then sums every voxel in
+//   registers, with no atomics except for tiles split over several work items.
 
-#include "common.h"
+#include "bins.h"
 
 namespace {
 
@@ -200,27 +204,16 @@ msda3d_fwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shap
 }
 
 // ---------------------------------------------------------------------------
-// backward: one kernel.  Workgroup = (batch b, head m, IPB consecutive
-// queries).  Per point the table holds the eight row offsets (later
-// overwritten by the eight dot products) and (fx, fy, fz, A).
+// backward: grad_attn_weight and grad_sampling_loc.  Workgroup = (batch b,
+// head m, IPB consecutive queries).  Per point the table holds the eight row
+// offsets (later overwritten by the eight dot products) and (fx, fy, fz, A).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void atomic_add4(rsrc_t r, uint32_t off32, int ch, float s,
-                                            const float4 &g) {
-    // one fp32 add per channel; an offset beyond the buffer (kOOB) is dropped
-    const int o = (int)(off32 + 4u * ch);
-    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(s * g.x, r, o, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(s * g.y, r, o + 4, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(s * g.z, r, o + 8, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(s * g.w, r, o + 12, 0, 0);
-}
-
 template <int D, typename VT>
 __global__ void __launch_bounds__(kThreads)
-msda3d_bwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes,
-                  const int64_t *__restrict__ starts, const float *__restrict__ loc,
-                  const float *__restrict__ attn, const float *__restrict__ grad_out,
-                  float *__restrict__ grad_value, float *__restrict__ grad_loc,
-                  float *__restrict__ grad_attn, Dims3 dm) {
+msda3d_dots_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes,
+                   const int64_t *__restrict__ starts, const float *__restrict__ loc,
+                   const float *__restrict__ attn, const float *__restrict__ grad_out,
+                   float *__restrict__ grad_loc, float *__restrict__ grad_attn, Dims3 dm) {
     constexpr int G = D / 4;
     constexpr int IPB = kThreads / G;
     __shared__ VolumeLds s_lv;
@@ -240,7 +233,6 @@ msda3d_bwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shap
 
     const size_t slice = (size_t)dm.Nv * M * D;
     const rsrc_t vr = make_rsrc(value + (size_t)b * slice, (uint32_t)(slice * sizeof(VT)));
-    const rsrc_t gr = make_rsrc(grad_value + (size_t)b * slice, (uint32_t)(slice * 4));
     const size_t row0 = ((size_t)b * Nq + q0) * M + m;  // item row of query q0
     const size_t pt0 = row0 * LK;
 
@@ -277,7 +269,6 @@ msda3d_bwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shap
             for (int jj = 0; jj < pc; ++jj) {
                 const int e = it * dm.PS + jj;
                 const uint4 lo = s_off[2 * e], hi = s_off[2 * e + 1];
-                const float4 ax = s_aux[e];
                 const float4 v0 = Row4<VT>::load(vr, lo.x, 4 * c);
                 const float4 v1 = Row4<VT>::load(vr, lo.y, 4 * c);
                 const float4 v2 = Row4<VT>::load(vr, lo.z, 4 * c);
@@ -286,22 +277,6 @@ msda3d_bwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shap
                 const float4 v5 = Row4<VT>::load(vr, hi.y, 4 * c);
                 const float4 v6 = Row4<VT>::load(vr, hi.z, 4 * c);
                 const float4 v7 = Row4<VT>::load(vr, hi.w, 4 * c);
-                Corners cn;
-                cn.lo = lo;
-                cn.hi = hi;
-                cn.fx = ax.x;
-                cn.fy = ax.y;
-                cn.fz = ax.z;
-                float4 wl, wh;
-                trilinear_weights(cn, ax.w, wl, wh);
-                atomic_add4(gr, lo.x, 4 * c, wl.x, g4);
-                atomic_add4(gr, lo.y, 4 * c, wl.y, g4);
-                atomic_add4(gr, lo.z, 4 * c, wl.z, g4);
-                atomic_add4(gr, lo.w, 4 * c, wl.w, g4);
-                atomic_add4(gr, hi.x, 4 * c, wh.x, g4);
-                atomic_add4(gr, hi.y, 4 * c, wh.y, g4);
-                atomic_add4(gr, hi.z, 4 * c, wh.z, g4);
-                atomic_add4(gr, hi.w, 4 * c, wh.w, g4);
                 const float d0 = group_sum<G>(dot4(g4, v0)), d1 = group_sum<G>(dot4(g4, v1));
                 const float d2 = group_sum<G>(dot4(g4, v2)), d3 = group_sum<G>(dot4(g4, v3));
                 const float d4 = group_sum<G>(dot4(g4, v4)), d5 = group_sum<G>(dot4(g4, v5));
@@ -409,22 +384,79 @@ template <int D, typename VT>
 msda_status launch3_bwd(const void *value, const int64_t *shapes, const int64_t *starts,
                         const float *loc, const float *attn, const float *gout, float *gval,
                         float *gloc, float *gattn, int64_t B, int64_t Nv, int64_t Nq, int64_t M,
-                        int64_t L, int64_t K, bool align, hipStream_t s) {
+                        int64_t L, int64_t K, bool align, bool accumulate, const WorkLayout &wl,
+                        unsigned char *ws, const Exec &ex) {
+    const hipStream_t s = ex.s;
+    Work w;
+    w.counts = reinterpret_cast<uint32_t *>(ws + wl.off_counts);
+    w.start = reinterpret_cast<uint32_t *>(ws + wl.off_start);
+    w.cursor = reinterpret_cast<uint32_t *>(ws + wl.off_cursor);
+    w.items = reinterpret_cast<uint4 *>(ws + wl.off_items);
+    w.work_total = reinterpret_cast<uint32_t *>(ws + wl.off_total);
+    w.recs = reinterpret_cast<uint4 *>(ws + wl.off_sorted);
+    auto per_batch = [&](int64_t per_b, auto &&launch) -> msda_status {
+        const int64_t bchunk = batch_chunk(per_b, B);
+        for (int64_t b0 = 0; b0 < B; b0 += bchunk) {
+            const int64_t nb = (B - b0) < bchunk ? (B - b0) : bchunk;
+            launch(b0, (unsigned)(per_b * nb));
+            const msda_status e = hip_status(hipGetLastError());
+            if (e != MSDA_OK) return e;
+        }
+        return MSDA_OK;
+    };
+    // grad_attn_weight and grad_sampling_loc on the side stream (when there is one)
+    const hipStream_t ds = ex.side ? ex.side : s;
     const Plan3 p = plan3(D, L, K, 48);
     const int64_t gq = (Nq + p.ipb - 1) / p.ipb;
-    const int64_t per_b = gq * M;
-    const int64_t bchunk = batch_chunk(per_b, B);
-    for (int64_t b0 = 0; b0 < B; b0 += bchunk) {
-        const int64_t nb = (B - b0) < bchunk ? (B - b0) : bchunk;
+    msda_status st = per_batch(gq * M, [&](int64_t b0, unsigned grid) {
         const Dims3 dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, p.pc, p.ps, (int)b0, (int)gq,
                        align ? 1 : 0};
-        hipLaunchKernelGGL((msda3d_bwd_kernel<D, VT>), dim3((unsigned)(per_b * nb)),
-                           dim3(kThreads), p.lds, s, static_cast<const VT *>(value), shapes,
-                           starts, loc, attn, gout, gval, gloc, gattn, dm);
-        const msda_status st = hip_status(hipGetLastError());
+        hipLaunchKernelGGL((msda3d_dots_kernel<D, VT>), dim3(grid), dim3(kThreads), p.lds, ds,
+                           static_cast<const VT *>(value), shapes, starts, loc, attn, gout, gloc,
+                           gattn, dm);
+    });
+    if (st != MSDA_OK) return st;
+    if (ex.side) {
+        st = hip_status(hipEventRecord(ex.join, ex.side));
         if (st != MSDA_OK) return st;
     }
-    return MSDA_OK;
+    // grad_value: the binned pipeline over volume levels
+    st = fill_zero(w.counts, (wl.off_start - wl.off_counts) / 16, s);
+    if (st != MSDA_OK) return st;
+    const int hist_cap = (int)(wl.nb_max < kHistLds ? wl.nb_max : kHistLds);
+    const int64_t gb = (Nq * L * K + kBinPoints - 1) / kBinPoints;  // per (batch, head)
+    Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, 0, 0, 0, (int)gb, (int)wl.nb_max,
+            accumulate ? 1 : 0, make_fastdiv((uint32_t)(L * K)), make_fastdiv((uint32_t)K)};
+    dm.align = align ? 1 : 0;
+    st = per_batch(gb * M, [&](int64_t b0, unsigned grid) {
+        Dims d2 = dm;
+        d2.b0 = (int)b0;
+        hipLaunchKernelGGL(bin_count_kernel<true>, dim3(grid), dim3(kThreads), 4 * (size_t)hist_cap,
+                           s, shapes, starts, loc, w.counts, hist_cap, d2);
+    });
+    if (st != MSDA_OK) return st;
+    hipLaunchKernelGGL(bin_scan_kernel<true>, dim3(1), dim3(kScanThreads), 0, s, shapes, starts,
+                       w.counts, w.start, w.cursor, w.items, w.work_total, (int)B, dm);
+    st = hip_status(hipGetLastError());
+    if (st != MSDA_OK) return st;
+    st = per_batch(gb * M, [&](int64_t b0, unsigned grid) {
+        Dims d2 = dm;
+        d2.b0 = (int)b0;
+        hipLaunchKernelGGL(bin_scatter_kernel<true>, dim3(grid), dim3(kThreads),
+                           8 * (size_t)hist_cap, s, shapes, starts, loc, attn, w.cursor, w.recs,
+                           hist_cap, d2);
+    });
+    if (st != MSDA_OK) return st;
+    if (ex.fill_on_side) {
+        st = hip_status(hipStreamWaitEvent(s, ex.filled, 0));
+        if (st != MSDA_OK) return st;
+    }
+    const int64_t grid = wl.work_max < kTileGrid ? wl.work_max : kTileGrid;
+    hipLaunchKernelGGL((grad_value_tile_kernel<D, true>), dim3((unsigned)grid), dim3(kTileThreads),
+                       0, s, shapes, starts, gout, w.items, w.work_total, w.recs, gval, dm);
+    st = hip_status(hipGetLastError());
+    if (st == MSDA_OK && ex.side) st = hip_status(hipStreamWaitEvent(s, ex.join, 0));
+    return st;
 }
 
 #define MSDA3D_DISPATCH(FN, VT, ...)                                                           \
@@ -453,9 +485,9 @@ msda_status dispatch3_bwd(int64_t D, const void *value, const int64_t *shapes,
                           const int64_t *starts, const float *loc, const float *attn,
                           const float *gout, float *gval, float *gloc, float *gattn, int64_t B,
                           int64_t Nv, int64_t Nq, int64_t M, int64_t L, int64_t K, bool align,
-                          hipStream_t s) {
+                          bool acc, const WorkLayout &wl, unsigned char *ws, const Exec &ex) {
     MSDA3D_DISPATCH(launch3_bwd, VT, value, shapes, starts, loc, attn, gout, gval, gloc, gattn,
-                    B, Nv, Nq, M, L, K, align, s)
+                    B, Nv, Nq, M, L, K, align, acc, wl, ws, ex)
 }
 
 #undef MSDA3D_DISPATCH
@@ -485,38 +517,80 @@ msda_status msda3d_forward(const void *value, int value_dtype, const int64_t *vo
                                    attn_weight, out, B, Nv, Nq, M, L, K, align, s);
 }
 
+size_t msda3d_backward_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
+                                      int64_t L, int64_t K) {
+    if (check_sizes3(MSDA_F32, B, Nv, Nq, M, D, L, K) != MSDA_OK) return 0;
+    if (B == 0 || Nq == 0) return 0;
+    return work_layout(B, Nv, Nq, M, L, K, true).bytes;
+}
+
 msda_status msda3d_backward(const void *value, int value_dtype, const int64_t *volume_shapes,
                             const int64_t *level_start_index, const float *sampling_loc,
                             const float *attn_weight, const float *grad_out, float *grad_value,
                             float *grad_sampling_loc, float *grad_attn_weight, int64_t B,
                             int64_t Nv, int64_t Nq, int64_t M, int64_t D, int64_t L, int64_t K,
-                            uint32_t flags, void *stream) {
+                            void *workspace, size_t workspace_bytes, uint32_t flags,
+                            void *stream) {
     msda_status st = check_sizes3(value_dtype, B, Nv, Nq, M, D, L, K);
     if (st != MSDA_OK) return st;
     if (flags & ~(MSDA_BWD_ACCUMULATE | MSDA_ALIGN_CORNERS)) return MSDA_ERR_UNSUPPORTED;
+    // a grad_value record stores the query index in 25 bits
+    if (Nq > ((int64_t)1 << (32 - kRecQueryShift))) return MSDA_ERR_UNSUPPORTED;
     const int64_t nval = B * Nv * M * D;
     if (nval > 0 && !grad_value) return MSDA_ERR_NULL;
     const bool work = B > 0 && Nq > 0;
+    WorkLayout wl{};
     if (work) {
         if (Nv < 1) return MSDA_ERR_SHAPE;
         if (!value || !volume_shapes || !level_start_index || !sampling_loc || !attn_weight ||
             !grad_out || !grad_sampling_loc || !grad_attn_weight)
             return MSDA_ERR_NULL;
+        wl = work_layout(B, Nv, Nq, M, L, K, true);
+        if (wl.bm_bins >= ((int64_t)1 << 31) || wl.work_max >= ((int64_t)1 << 31) ||
+            wl.sorted_max >= ((int64_t)1 << 32))
+            return MSDA_ERR_UNSUPPORTED;
+        if (!workspace) return MSDA_ERR_NULL;
+        if (workspace_bytes < wl.bytes) return MSDA_ERR_WORKSPACE;
+        if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return MSDA_ERR_WORKSPACE;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (!(flags & MSDA_BWD_ACCUMULATE)) {
-        st = fill_zero(grad_value, (size_t)nval / 4, s);  // D % 4 == 0
+    Exec ex{s, nullptr, nullptr, nullptr, nullptr, nullptr, false};
+    std::unique_lock<std::mutex> lock(msda_side::mutex(), std::defer_lock);
+    if (work) {
+        lock.lock();
+        if (msda_side::SideStream *ss = msda_side::get()) {
+            ex.side = ss->s;
+            ex.fork = ss->fork;
+            ex.filled = ss->filled;
+            ex.join = ss->join;
+        }
+    }
+    if (ex.side) {
+        st = hip_status(hipEventRecord(ex.fork, s));
+        if (st == MSDA_OK) st = hip_status(hipStreamWaitEvent(ex.side, ex.fork, 0));
+        if (st != MSDA_OK) return st;
+    }
+    const bool acc = (flags & MSDA_BWD_ACCUMULATE) != 0;
+    if (!acc) {
+        // with a side stream the fill runs there, and the tile kernel waits for it
+        const hipStream_t fs = ex.side ? ex.side : s;
+        st = fill_zero(grad_value, (size_t)nval / 4, fs);  // D % 4 == 0
+        if (st == MSDA_OK && ex.side) {
+            st = hip_status(hipEventRecord(ex.filled, ex.side));
+            ex.fill_on_side = true;
+        }
         if (st != MSDA_OK) return st;
     }
     if (!work) return MSDA_OK;
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
     const bool align = (flags & MSDA_ALIGN_CORNERS) != 0;
     if (value_dtype == MSDA_F32)
         return dispatch3_bwd<float>(D, value, volume_shapes, level_start_index, sampling_loc,
                                     attn_weight, grad_out, grad_value, grad_sampling_loc,
-                                    grad_attn_weight, B, Nv, Nq, M, L, K, align, s);
+                                    grad_attn_weight, B, Nv, Nq, M, L, K, align, acc, wl, ws, ex);
     return dispatch3_bwd<uint16_t>(D, value, volume_shapes, level_start_index, sampling_loc,
                                    attn_weight, grad_out, grad_value, grad_sampling_loc,
-                                   grad_attn_weight, B, Nv, Nq, M, L, K, align, s);
+                                   grad_attn_weight, B, Nv, Nq, M, L, K, align, acc, wl, ws, ex);
 }
 
 msda_status msda3d_validate_host(const int64_t *volume_shapes_host,

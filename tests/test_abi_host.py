@@ -181,11 +181,21 @@ def test_volume_entry_points_reject_before_launch():
     assert fwd(0, 1, 80, 16, 2, 8, 2, 2) == B_.MSDA_ERR_NULL
     assert fwd(0, 0, 80, 16, 2, 8, 2, 2) == B_.MSDA_OK
     assert fwd(0, 1, 80, 16, 2, 8, 2, 2, flags=B_.MSDA_SOFTMAX_PER_LEVEL) == B_.MSDA_ERR_UNSUPPORTED
-    bwd = lambda dt, flags, *dims: lib.msda3d_backward(z, dt, z, z, z, z, z, z, z, z, *dims,
-                                                        flags, z)
+    bwd = lambda dt, flags, *dims, ws=z, nb=0: lib.msda3d_backward(
+        z, dt, z, z, z, z, z, z, z, z, *dims, ws, nb, flags, z)
     assert bwd(0, 8, 1, 80, 16, 2, 8, 2, 2) == B_.MSDA_ERR_UNSUPPORTED
     assert bwd(0, 0, 1, 80, 16, 2, 8, 2, 2) == B_.MSDA_ERR_NULL
     assert bwd(0, 0, 0, 80, 16, 2, 8, 2, 2) == B_.MSDA_OK          # nothing to do
+    # workspace: eight 16-byte records per point plus the bin tables
+    need = lib.msda3d_backward_workspace_size(1, 80, 16, 2, 8, 2, 2)
+    pts = 16 * 2 * 2 * 2
+    assert 128 * pts <= need <= 128 * pts + 64 * 80 * 2 + 4096
+    assert lib.msda3d_backward_workspace_size(0, 80, 16, 2, 8, 2, 2) == 0
+    fake = ctypes.c_void_p(1 << 20)
+    b2 = lambda ws, nb: lib.msda3d_backward(fake, 0, fake, fake, fake, fake, fake, fake, fake,
+                                            fake, 1, 80, 16, 2, 8, 2, 2, ws, nb, 0, z)
+    assert b2(z, need) == B_.MSDA_ERR_NULL
+    assert b2(fake, need - 1) == B_.MSDA_ERR_WORKSPACE
     # the level table: rows (Z, H, W)
     ss = _i64([[2, 4, 8], [1, 2, 4]])
     st = _i64([0, 64])
