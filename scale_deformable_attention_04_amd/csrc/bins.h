@@ -446,7 +446,9 @@ bin_scan_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ 
         block_exclusive_scan2(e, ch, s_wave, tot_e, tot_c);
         e += carry_e;
         ch += carry_c;
-#pragma unroll
+        // a rolled loop: this kernel is one workgroup on the critical path,
+        // and its instruction fetches are not hidden by other waves
+#pragma unroll 1
         for (int i = 0; i < kPer; ++i) {
             if (g0 + i < nf) {
                 start[bin[i]] = e;

@@ -28,6 +28,7 @@
 namespace {
 
 constexpr int kVolTableBytes = 48 * 1024;  // per-workgroup budget for the point tables
+constexpr int kDots3Grid = 512;            // workgroups of the dots kernel, at most
 
 // Level table in LDS: lvl[l] = (Z, H, W, start); a level whose voxels do not
 // fit inside value becomes (0, 0, 0, 0) and has no voxel.
@@ -120,6 +121,7 @@ struct Dims3 {
     int b0;    // first batch of this launch
     int nblk;  // workgroups per batch (forward) or per (batch, head) (backward)
     int align;
+    int nblocks;  // query blocks of the launch (dots kernel, a persistent grid)
 };
 
 // ---------------------------------------------------------------------------
@@ -222,14 +224,19 @@ msda3d_dots_kernel(const VT *__restrict__ value, const int64_t *__restrict__ sha
     float4 *s_aux = reinterpret_cast<float4 *>(s_off + 2 * IPB * dm.PS);  // [IPB][PS]
 
     const int M = dm.M, K = dm.K, LK = dm.L * dm.K, Nq = dm.Nq;
-    const int wg = xcd_contiguous(blockIdx.x, gridDim.x);
+    stage_volumes(&s_lv, shapes, starts, dm.L, dm.Nv);
+    // blocks of IPB queries of one (batch, head); workgroup g takes blocks g,
+    // g + grid, ... (a few workgroups per CU leave room for the grad_value
+    // kernels running beside this one)
+    for (int blk = blockIdx.x; blk < dm.nblocks; blk += gridDim.x) {
+    if (blk != (int)blockIdx.x) __syncthreads();  // the point tables are reused
+    const int wg = xcd_contiguous(blk, dm.nblocks);
     const int bm = wg / dm.nblk + dm.b0 * M;
     const int m = bm % M, b = bm / M;
     const int q0 = (wg % dm.nblk) * IPB;
     const int nitems = min(IPB, Nq - q0);
     const uint32_t row_stride = (uint32_t)M * D * 4u;
     const uint32_t head_off = (uint32_t)m * D * 4u;
-    stage_volumes(&s_lv, shapes, starts, dm.L, dm.Nv);
 
     const size_t slice = (size_t)dm.Nv * M * D;
     const rsrc_t vr = make_rsrc(value + (size_t)b * slice, (uint32_t)(slice * sizeof(VT)));
@@ -322,6 +329,7 @@ msda3d_dots_kernel(const VT *__restrict__ value, const int64_t *__restrict__ sha
             grad_loc[3 * p + 2] = lz;
         }
     }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -410,8 +418,9 @@ msda_status launch3_bwd(const void *value, const int64_t *shapes, const int64_t 
     const int64_t gq = (Nq + p.ipb - 1) / p.ipb;
     msda_status st = per_batch(gq * M, [&](int64_t b0, unsigned grid) {
         const Dims3 dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, p.pc, p.ps, (int)b0, (int)gq,
-                       align ? 1 : 0};
-        hipLaunchKernelGGL((msda3d_dots_kernel<D, VT>), dim3(grid), dim3(kThreads), p.lds, ds,
+                       align ? 1 : 0, (int)grid};
+        const unsigned g = grid > (unsigned)kDots3Grid ? (unsigned)kDots3Grid : grid;
+        hipLaunchKernelGGL((msda3d_dots_kernel<D, VT>), dim3(g), dim3(kThreads), p.lds, ds,
                            static_cast<const VT *>(value), shapes, starts, loc, attn, gout, gloc,
                            gattn, dm);
     });
