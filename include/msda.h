@@ -355,7 +355,7 @@ msda_status msda3d_validate_host(const int64_t *volume_shapes_host,
  *   lse                          [B, heads, N]             fp32: log sum_keys exp(S), written
  *                                by the forward, read by the backward
  * Limits: head_dim in {16, 32, 64}; 1 <= Ns <= 256 (<= 240 for head_dim 64:
- * one (b, head)'s keys fit 64 KB of LDS); B*heads < 65536; N*Ns < 2^31.
+ * one (b, head)'s keys fit 64 KB of LDS); B*heads < 65536; N*Ns < 2^29.
  * B or N may be 0.
  *
  * msda_dat_attention_forward: out and lse are overwritten.

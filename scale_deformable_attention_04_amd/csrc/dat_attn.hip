@@ -10,7 +10,7 @@
 // 16x16 tile of C per 64-lane wave; lane l supplies A[l%16][l/16] and
 // B[l/16][l%16] and holds C[4*(l/16) + r][l%16] in register r).
 //
-// Forward (dat_attn_fwd_kernel): a wave owns 16 queries.  It computes the
+// Forward (dat_attn_fwd_kernel): a wave owns tiles of 16 queries.  It computes the
 // transposed scores S^T = K Q^T one 16-key block at a time (keys in LDS,
 // its queries' rows in registers), so each lane holds four keys of one query
 // for every block; the row max and sum are lane-local plus two cross-row
@@ -36,31 +36,49 @@ namespace {
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kAttnThreads = 256;  // four waves
+constexpr int kAttnMinWaves = 4;   // per SIMD: at most 128 VGPRs a lane
 constexpr int kMaxKeys = 256;      // keys per (batch, head), at most
-constexpr int kMaxKeyBlocks = kMaxKeys / 16;
 constexpr int kQueryChunk = 64;    // queries staged per step of the dK/dV kernel
 
 __device__ __forceinline__ v4f mfma16x4(float a, float b, v4f c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Rows of (b, h) from a [B, T, heads, DH] tensor into LDS rows of RS floats;
-// rows n..npad-1 are zero-filled (their keys are masked, but a product with
-// them must stay finite).
-template <int DH, int RS>
+// Rows n0 .. n0+npad-1 of (b, h) from a [B, T, heads, DH] tensor into LDS
+// rows of RS floats; rows n..npad-1 are zero-filled (their keys are masked,
+// but a product with them must stay finite).  npad <= MAXROWS.  Each thread
+// issues up to BATCH float4 loads before it writes any, so a staging waits
+// for memory once per batch rather than once per float4 (a smaller BATCH
+// where many registers are live).
+template <int DH, int RS, int MAXROWS, int BATCH = 8>
 __device__ __forceinline__ void stage_rows(float *s, const float *__restrict__ src, int b, int h,
                                            int T, int heads, int n0, int n, int npad) {
-    for (int i = threadIdx.x; i < npad * (DH / 4); i += blockDim.x) {
-        const int row = i / (DH / 4), c4 = i - row * (DH / 4);
-        float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (row < n)
-            val = reinterpret_cast<const float4 *>(
-                src + (((size_t)b * T + n0 + row) * heads + h) * DH)[c4];
-        float *d = s + row * RS + 4 * c4;
-        d[0] = val.x;
-        d[1] = val.y;
-        d[2] = val.z;
-        d[3] = val.w;
+    constexpr int C4 = DH / 4;
+    constexpr int ITEMS = (MAXROWS * C4 + kAttnThreads - 1) / kAttnThreads;
+#pragma unroll
+    for (int i0 = 0; i0 < ITEMS; i0 += BATCH) {
+        float4 val[BATCH];
+#pragma unroll
+        for (int it = 0; it < BATCH; ++it) {
+            const int i = threadIdx.x + (i0 + it) * kAttnThreads;
+            const int row = i / C4, c4 = i - row * C4;
+            val[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (i0 + it < ITEMS && row < n)
+                val[it] = reinterpret_cast<const float4 *>(
+                    src + (((size_t)b * T + n0 + row) * heads + h) * DH)[c4];
+        }
+#pragma unroll
+        for (int it = 0; it < BATCH; ++it) {
+            const int i = threadIdx.x + (i0 + it) * kAttnThreads;
+            const int row = i / C4, c4 = i - row * C4;
+            if (i0 + it < ITEMS && row < npad) {
+                float *d = s + row * RS + 4 * c4;
+                d[0] = val[it].x;
+                d[1] = val[it].y;
+                d[2] = val[it].z;
+                d[3] = val[it].w;
+            }
+        }
     }
 }
 
@@ -77,196 +95,286 @@ __device__ __forceinline__ float cross_sum(float v) {
 }
 
 // ---------------------------------------------------------------------------
-// forward
+// scores of one tile of 16 queries
+// NKB: key blocks of 16 the kernel is built for (the host takes the smallest
+// of 1, 2, 4, 8, 16 that covers ceil(Ns / 16)); blocks past the staged ones
+// skip their products (a uniform branch) and score -inf.
 // ---------------------------------------------------------------------------
-template <int DH>
-__global__ void __launch_bounds__(kAttnThreads)
-dat_attn_fwd_kernel(const float *__restrict__ q, const float *__restrict__ k,
-                    const float *__restrict__ v, const float *__restrict__ bias,
-                    float *__restrict__ out, float *__restrict__ lse, int N, int Ns, int heads,
-                    float scale) {
-    constexpr int RS = DH + 2;  // LDS row stride: conflict-free reads of A[l%16][4s + l/16]
-    constexpr int KS = DH / 4;  // k-steps of the score product
-    extern __shared__ float s_kv[];  // [nkb * 16][RS]: K, then V
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
-    const int bh = blockIdx.y, b = bh / heads, h = bh % heads;
-    const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 4, j = l & 15;
-    const int qi = blockIdx.x * 64 + wave * 16 + j;  // this lane's query
-    const bool qok = qi < N;
-    const int nkb = (Ns + 15) >> 4;
-
-    stage_rows<DH, RS>(s_kv, k, b, h, Ns, heads, 0, Ns, nkb * 16);
-    float qr[KS];
+// sc[kb][r] = log2(e) * scale * q.k for key kb*16 + 4g + r of this lane's
+// query (exp2 of a difference of these is exp of the natural one); -inf for
+// keys >= Ns, added from s_mask (0 below Ns, -inf from Ns on) rather than
+// by per-lane compares, whose masks the compiler would keep across tiles.
+template <int DH, int RS, int NKB>
+__device__ __forceinline__ void tile_scores(v4f (&sc)[NKB], const float *s_k, const float *s_mask,
+                                            const float (&qr)[DH / 4], int nkb, float scale2,
+                                            int g, int j) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-        qr[s] = qok ? q[(((size_t)b * N + qi) * heads + h) * DH + 4 * s + g] : 0.f;
-    __syncthreads();
-
-    // scores: sc[kb][r] = S[query qi][key kb*16 + 4g + r]
-    v4f sc[kMaxKeyBlocks];
-    const float *brow = bias ? bias + ((size_t)bh * N + (qok ? qi : 0)) * Ns : nullptr;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < kMaxKeyBlocks; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb) {
+        v4f acc = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
         if (kb < nkb) {
-            v4f acc = {0.f, 0.f, 0.f, 0.f};
-            const float *krow = s_kv + (kb * 16 + j) * RS + g;
+            v4f c = {0.f, 0.f, 0.f, 0.f};
+            const float *krow = s_k + (kb * 16 + j) * RS + g;
 #pragma unroll
-            for (int s = 0; s < KS; ++s) acc = mfma16x4(krow[4 * s], qr[s], acc);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = kb * 16 + 4 * g + r;
-                float x = acc[r] * scale;
-                if (brow && qok && key < Ns) x += brow[key];
-                x = key < Ns ? x : -INFINITY;
-                acc[r] = x;
-                mx = fmaxf(mx, x);
-            }
-            sc[kb] = acc;
+            for (int s = 0; s < DH / 4; ++s) c = mfma16x4(krow[4 * s], qr[s], c);
+            const float4 m = reinterpret_cast<const float4 *>(s_mask + kb * 16)[g];
+            acc = v4f{fmaf(c[0], scale2, m.x), fmaf(c[1], scale2, m.y), fmaf(c[2], scale2, m.z),
+                      fmaf(c[3], scale2, m.w)};
         }
+        sc[kb] = acc;
     }
-    mx = cross_max(mx);
-    float sum = 0.f;
+}
+
+// sc += log2(e) * bias.  brs: buffer over the (b, h)'s bias rows [N][Ns];
+// roff: byte offset of this lane's query row.  The key's offset is an
+// immediate of the load; keys past Ns read the next row (or nothing: past the
+// buffer a load returns 0) and stay -inf.
+template <int NKB>
+__device__ __forceinline__ void add_bias(v4f (&sc)[NKB], rsrc_t brs, uint32_t roff, int nkb,
+                                         int g) {
+    const int base = (int)(roff + 16u * g);
 #pragma unroll
-    for (int kb = 0; kb < kMaxKeyBlocks; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb) {
         if (kb < nkb) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float p = expf(sc[kb][r] - mx);
-                sc[kb][r] = p;
-                sum += p;
+                const float bv = __builtin_bit_cast(
+                    float, __builtin_amdgcn_raw_buffer_load_b32(brs, base + kb * 64 + 4 * r, 0, 0));
+                sc[kb][r] = fmaf(bv, kLog2e, sc[kb][r]);
             }
-        }
-    }
-    sum = cross_sum(sum);
-    if (qok && g == 0) lse[(size_t)bh * N + qi] = mx + logf(sum);
-    const float inv = 1.f / sum;
-
-    __syncthreads();  // every wave is done with K
-    stage_rows<DH, RS>(s_kv, v, b, h, Ns, heads, 0, Ns, nkb * 16);
-    __syncthreads();
-
-    // O^T[dim db*16 + 4g + r][query] = sum over keys of V^T P^T
-#pragma unroll
-    for (int db = 0; db < DH / 16; ++db) {
-        v4f acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < kMaxKeyBlocks; ++kb) {
-            if (kb < nkb) {
-                const float *vcol = s_kv + (kb * 16 + 4 * g) * RS + db * 16 + j;
-#pragma unroll
-                for (int s = 0; s < 4; ++s) acc = mfma16x4(vcol[s * RS], sc[kb][s], acc);
-            }
-        }
-        if (qok) {
-            float4 o = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
-            reinterpret_cast<float4 *>(out + (((size_t)b * N + qi) * heads + h) * DH +
-                                       db * 16)[g] = o;
         }
     }
 }
 
+// LDS of the forward and dQ kernels: the key mask, then K (and V)
+__device__ __forceinline__ void stage_mask(float *s_mask, int Ns, int nkb) {
+    for (int i = threadIdx.x; i < nkb * 16; i += blockDim.x) s_mask[i] = i < Ns ? 0.f : -INFINITY;
+}
+
 // ---------------------------------------------------------------------------
-// backward, part 1: delta, dQ, dbias (query blocks, as the forward)
+// forward
+// RESIDENT: K and V of the (b, h) are staged once, side by side, and each
+// wave walks `tiles` tiles of 16 queries (a workgroup covers 64 * tiles
+// consecutive queries).  Otherwise (keys too many for both to fit the LDS
+// budget) one buffer holds K, then V, and tiles == 1.  Lanes past the last
+// query compute on a copy of the last query's row and store nothing.
 // ---------------------------------------------------------------------------
-template <int DH>
-__global__ void __launch_bounds__(kAttnThreads)
+template <int DH, int NKB, bool RESIDENT>
+__global__ void __launch_bounds__(kAttnThreads, kAttnMinWaves)
+dat_attn_fwd_kernel(const float *__restrict__ q, const float *__restrict__ k,
+                    const float *__restrict__ v, const float *__restrict__ bias,
+                    float *__restrict__ out, float *__restrict__ lse, int N, int Ns, int heads,
+                    float scale, int tiles) {
+    constexpr int RS = DH + 2;  // LDS row stride: conflict-free reads of A[l%16][4s + l/16]
+    constexpr int KS = DH / 4;  // k-steps of the score product
+    extern __shared__ float s_kv[];
+
+    const int bh = blockIdx.y, b = bh / heads, h = bh % heads;
+    const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 4, j = l & 15;
+    const int nkb = (Ns + 15) >> 4;
+    const float scale2 = scale * kLog2e;
+    float *s_mask = s_kv;  // [nkb * 16]
+    float *s_k = s_kv + nkb * 16;
+    float *s_v = RESIDENT ? s_k + nkb * 16 * RS : s_k;
+    stage_mask(s_mask, Ns, nkb);
+    if constexpr (RESIDENT) {
+        stage_rows<DH, RS, NKB * 16>(s_k, k, b, h, Ns, heads, 0, Ns, nkb * 16);
+        stage_rows<DH, RS, NKB * 16>(s_v, v, b, h, Ns, heads, 0, Ns, nkb * 16);
+        __syncthreads();
+    }
+
+    for (int t = 0; t < (RESIDENT ? tiles : 1); ++t) {  // one tile unless resident
+        const int q0 = ((blockIdx.x * tiles + t) * 4 + wave) * 16;  // the tile's first query
+        if constexpr (RESIDENT) {
+            if (q0 >= N) break;  // wave-uniform; no barrier follows in this mode
+        }
+        const int qi = q0 + j;  // this lane's query
+        const bool qok = qi < N;
+        const int qc = qok ? qi : N - 1;
+        const size_t qrow = (((size_t)b * N + qc) * heads + h) * DH;
+        if constexpr (!RESIDENT)
+            stage_rows<DH, RS, NKB * 16>(s_k, k, b, h, Ns, heads, 0, Ns, nkb * 16);
+        float qr[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) qr[s] = q[qrow + 4 * s + g];
+        if constexpr (!RESIDENT) __syncthreads();
+
+        // scores: sc[kb][r] ~ S[query qi][key kb*16 + 4g + r]
+        v4f sc[NKB];
+        tile_scores<DH, RS, NKB>(sc, s_k, s_mask, qr, nkb, scale2, g, j);
+        if (bias)
+            add_bias<NKB>(sc, make_rsrc(bias + (size_t)bh * N * Ns, (uint32_t)N * Ns * 4),
+                          (uint32_t)qc * Ns * 4, nkb, g);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[kb][r]);
+        mx = cross_max(mx);
+        float sum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float p = __builtin_amdgcn_exp2f(sc[kb][r] - mx);
+                sc[kb][r] = p;
+                sum += p;
+            }
+        }
+        sum = cross_sum(sum);
+        if (qok && g == 0) lse[(size_t)bh * N + qi] = (mx + log2f(sum)) * kLn2;
+        const float inv = 1.f / sum;
+
+        if constexpr (!RESIDENT) {
+            __syncthreads();  // every wave is done with K
+            stage_rows<DH, RS, NKB * 16, 4>(s_v, v, b, h, Ns, heads, 0, Ns, nkb * 16);
+            __syncthreads();
+        }
+
+        // O^T[dim db*16 + 4g + r][query] = sum over keys of V^T P^T
+#pragma unroll
+        for (int db = 0; db < DH / 16; ++db) {
+            v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                if (kb < nkb) {
+                    const float *vcol = s_v + (kb * 16 + 4 * g) * RS + db * 16 + j;
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) acc = mfma16x4(vcol[s * RS], sc[kb][s], acc);
+                }
+            }
+            if (qok) {
+                float4 o = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+                reinterpret_cast<float4 *>(out + qrow + db * 16)[g] = o;
+            }
+        }
+        if constexpr (!RESIDENT) __syncthreads();  // V is replaced by the next tile's K
+    }
+}
+
+// ---------------------------------------------------------------------------
+// backward, part 1: delta, dQ, dbias (query tiles, as the forward; RESIDENT
+// as there, otherwise K, V, then K again through one buffer)
+// ---------------------------------------------------------------------------
+template <int DH, int NKB, bool RESIDENT>
+__global__ void __launch_bounds__(kAttnThreads, kAttnMinWaves)
 dat_attn_dq_kernel(const float *__restrict__ q, const float *__restrict__ k,
                    const float *__restrict__ v, const float *__restrict__ bias,
                    const float *__restrict__ out, const float *__restrict__ lse,
                    const float *__restrict__ gout, float *__restrict__ gq,
                    float *__restrict__ gbias, float *__restrict__ delta, int N, int Ns, int heads,
-                   float scale) {
+                   float scale, int tiles) {
     constexpr int RS = DH + 2;
     constexpr int KS = DH / 4;
     extern __shared__ float s_kv[];
 
     const int bh = blockIdx.y, b = bh / heads, h = bh % heads;
     const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 4, j = l & 15;
-    const int qi = blockIdx.x * 64 + wave * 16 + j;
-    const bool qok = qi < N;
     const int nkb = (Ns + 15) >> 4;
-    const size_t qrow = (((size_t)b * N + (qok ? qi : 0)) * heads + h) * DH;
-
-    stage_rows<DH, RS>(s_kv, k, b, h, Ns, heads, 0, Ns, nkb * 16);
-    float qr[KS], dr[KS];
-    float dpart = 0.f;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        qr[s] = qok ? q[qrow + 4 * s + g] : 0.f;
-        dr[s] = qok ? gout[qrow + 4 * s + g] : 0.f;
-        dpart += qok ? dr[s] * out[qrow + 4 * s + g] : 0.f;
+    const float scale2 = scale * kLog2e;
+    float *s_mask = s_kv;  // [nkb * 16]
+    float *s_k = s_kv + nkb * 16;
+    float *s_v = RESIDENT ? s_k + nkb * 16 * RS : s_k;
+    stage_mask(s_mask, Ns, nkb);
+    if constexpr (RESIDENT) {
+        stage_rows<DH, RS, NKB * 16>(s_k, k, b, h, Ns, heads, 0, Ns, nkb * 16);
+        stage_rows<DH, RS, NKB * 16>(s_v, v, b, h, Ns, heads, 0, Ns, nkb * 16);
+        __syncthreads();
     }
-    const float dl = cross_sum(dpart);  // delta = rowsum(dO * O)
-    if (qok && g == 0) delta[(size_t)bh * N + qi] = dl;
-    const float lq = qok ? lse[(size_t)bh * N + qi] : 0.f;
-    __syncthreads();
 
-    const float *brow = bias ? bias + ((size_t)bh * N + (qok ? qi : 0)) * Ns : nullptr;
-    v4f pt[kMaxKeyBlocks];  // P^T, then dS^T
-#pragma unroll
-    for (int kb = 0; kb < kMaxKeyBlocks; ++kb) {
-        if (kb < nkb) {
-            v4f acc = {0.f, 0.f, 0.f, 0.f};
-            const float *krow = s_kv + (kb * 16 + j) * RS + g;
-#pragma unroll
-            for (int s = 0; s < KS; ++s) acc = mfma16x4(krow[4 * s], qr[s], acc);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = kb * 16 + 4 * g + r;
-                float x = acc[r] * scale;
-                if (brow && qok && key < Ns) x += brow[key];
-                acc[r] = (key < Ns && qok) ? expf(x - lq) : 0.f;
-            }
-            pt[kb] = acc;
+    for (int t = 0; t < (RESIDENT ? tiles : 1); ++t) {  // one tile unless resident
+        const int q0 = ((blockIdx.x * tiles + t) * 4 + wave) * 16;
+        if constexpr (RESIDENT) {
+            if (q0 >= N) break;
         }
-    }
-    __syncthreads();
-    stage_rows<DH, RS>(s_kv, v, b, h, Ns, heads, 0, Ns, nkb * 16);
-    __syncthreads();
-    // dP^T = V dO^T (same layout as S^T); dS = P (dP - delta)
+        const int qi = q0 + j;
+        const bool qok = qi < N;
+        const int qc = qok ? qi : N - 1;
+        const size_t qrow = (((size_t)b * N + qc) * heads + h) * DH;
+
+        if constexpr (!RESIDENT)
+            stage_rows<DH, RS, NKB * 16>(s_k, k, b, h, Ns, heads, 0, Ns, nkb * 16);
+        float qr[KS], dr[KS];
+        float dpart = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < kMaxKeyBlocks; ++kb) {
-        if (kb < nkb) {
-            v4f acc = {0.f, 0.f, 0.f, 0.f};
-            const float *vrow = s_kv + (kb * 16 + j) * RS + g;
+        for (int s = 0; s < KS; ++s) {
+            qr[s] = q[qrow + 4 * s + g];
+            dr[s] = gout[qrow + 4 * s + g];
+            dpart += dr[s] * out[qrow + 4 * s + g];
+        }
+        const float dl = cross_sum(dpart);  // delta = rowsum(dO * O)
+        if (qok && g == 0) delta[(size_t)bh * N + qi] = dl;
+        const float lq2 = lse[(size_t)bh * N + qc] * kLog2e;
+        if constexpr (!RESIDENT) __syncthreads();
+
+        v4f pt[NKB];  // P^T, then dS^T
+        tile_scores<DH, RS, NKB>(pt, s_k, s_mask, qr, nkb, scale2, g, j);
+        if (bias)
+            add_bias<NKB>(pt, make_rsrc(bias + (size_t)bh * N * Ns, (uint32_t)N * Ns * 4),
+                          (uint32_t)qc * Ns * 4, nkb, g);
 #pragma unroll
-            for (int s = 0; s < KS; ++s) acc = mfma16x4(vrow[4 * s], dr[s], acc);
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) pt[kb][r] = pt[kb][r] * (acc[r] - dl);
-            if (gbias && qok) {
-                float4 *dst = reinterpret_cast<float4 *>(gbias + ((size_t)bh * N + qi) * Ns +
-                                                         kb * 16 + 4 * g);
-                if (kb * 16 + 4 * g + 3 < Ns && (Ns & 3) == 0) {
-                    *dst = make_float4(pt[kb][0], pt[kb][1], pt[kb][2], pt[kb][3]);
-                } else {
-                    float *d = gbias + ((size_t)bh * N + qi) * Ns;
+            for (int r = 0; r < 4; ++r) pt[kb][r] = __builtin_amdgcn_exp2f(pt[kb][r] - lq2);
+        if constexpr (!RESIDENT) {
+            __syncthreads();
+            stage_rows<DH, RS, NKB * 16, 4>(s_v, v, b, h, Ns, heads, 0, Ns, nkb * 16);
+            __syncthreads();
+        }
+        // dP^T = V dO^T (same layout as S^T); dS = P (dP - delta)
+        float *grow = gbias ? gbias + ((size_t)bh * N + qc) * Ns : nullptr;
+        // keys of this lane's dbias row to store: kb*16 + 4g + r < lim (none
+        // past the last query; a per-tile bound keeps the compares per tile)
+        const int lim = qok ? Ns - 4 * g : -64;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (kb * 16 + 4 * g + r < Ns) d[kb * 16 + 4 * g + r] = pt[kb][r];
+        for (int kb = 0; kb < NKB; ++kb) {
+            if (kb < nkb) {
+                v4f acc = {0.f, 0.f, 0.f, 0.f};
+                const float *vrow = s_v + (kb * 16 + j) * RS + g;
+#pragma unroll
+                for (int s = 0; s < KS; ++s) acc = mfma16x4(vrow[4 * s], dr[s], acc);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) pt[kb][r] = pt[kb][r] * (acc[r] - dl);
+                if (gbias) {
+                    const int k0 = kb * 16 + 4 * g;
+                    if ((Ns & 3) == 0) {  // whole float4s: four keys in or out together
+                        if (kb * 16 < lim)
+                            *reinterpret_cast<float4 *>(grow + k0) =
+                                make_float4(pt[kb][0], pt[kb][1], pt[kb][2], pt[kb][3]);
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (kb * 16 + r < lim) grow[k0 + r] = pt[kb][r];
+                    }
                 }
             }
         }
-    }
-    __syncthreads();
-    stage_rows<DH, RS>(s_kv, k, b, h, Ns, heads, 0, Ns, nkb * 16);
-    __syncthreads();
-    // dQ^T = scale K^T dS^T
+        if constexpr (!RESIDENT) {
+            __syncthreads();
+            stage_rows<DH, RS, NKB * 16, 4>(s_k, k, b, h, Ns, heads, 0, Ns, nkb * 16);
+            __syncthreads();
+        }
+        // dQ^T = scale K^T dS^T
 #pragma unroll
-    for (int db = 0; db < DH / 16; ++db) {
-        v4f acc = {0.f, 0.f, 0.f, 0.f};
+        for (int db = 0; db < DH / 16; ++db) {
+            v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < kMaxKeyBlocks; ++kb) {
-            if (kb < nkb) {
-                const float *kcol = s_kv + (kb * 16 + 4 * g) * RS + db * 16 + j;
+            for (int kb = 0; kb < NKB; ++kb) {
+                if (kb < nkb) {
+                    const float *kcol = s_k + (kb * 16 + 4 * g) * RS + db * 16 + j;
 #pragma unroll
-                for (int s = 0; s < 4; ++s) acc = mfma16x4(kcol[s * RS], pt[kb][s], acc);
+                    for (int s = 0; s < 4; ++s) acc = mfma16x4(kcol[s * RS], pt[kb][s], acc);
+                }
+            }
+            if (qok) {
+                float4 o = make_float4(acc[0] * scale, acc[1] * scale, acc[2] * scale,
+                                       acc[3] * scale);
+                reinterpret_cast<float4 *>(gq + qrow + db * 16)[g] = o;
             }
         }
-        if (qok) {
-            float4 o = make_float4(acc[0] * scale, acc[1] * scale, acc[2] * scale, acc[3] * scale);
-            reinterpret_cast<float4 *>(gq + qrow + db * 16)[g] = o;
-        }
+        if constexpr (!RESIDENT) __syncthreads();  // K is replaced by the next tile's
     }
 }
 
@@ -294,6 +402,7 @@ dat_attn_dkdv_kernel(const float *__restrict__ q, const float *__restrict__ k,
     const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 4, j = l & 15;
     const int key = blockIdx.x * 64 + wave * 16 + j;  // this lane's key (column)
     const bool kok = key < Ns;
+    const float scale2 = scale * kLog2e;
     const int q_begin = blockIdx.z * queries_per_split;
     const int q_end = min(N, q_begin + queries_per_split);
 
@@ -315,11 +424,11 @@ dat_attn_dkdv_kernel(const float *__restrict__ q, const float *__restrict__ k,
     for (int c0 = q_begin; c0 < q_end; c0 += kQueryChunk) {
         const int nq = min(kQueryChunk, q_end - c0);
         __syncthreads();  // the previous chunk is consumed
-        stage_rows<DH, RS>(s_q, q, b, h, N, heads, c0, nq, kQueryChunk);
-        stage_rows<DH, RS>(s_do, gout, b, h, N, heads, c0, nq, kQueryChunk);
+        stage_rows<DH, RS, kQueryChunk>(s_q, q, b, h, N, heads, c0, nq, kQueryChunk);
+        stage_rows<DH, RS, kQueryChunk>(s_do, gout, b, h, N, heads, c0, nq, kQueryChunk);
         if (threadIdx.x < kQueryChunk) {
             const bool ok = (int)threadIdx.x < nq;
-            s_lse[threadIdx.x] = ok ? lse[(size_t)bh * N + c0 + threadIdx.x] : 0.f;
+            s_lse[threadIdx.x] = ok ? lse[(size_t)bh * N + c0 + threadIdx.x] * kLog2e : 0.f;
             s_dl[threadIdx.x] = ok ? delta[(size_t)bh * N + c0 + threadIdx.x] : 0.f;
         }
         __syncthreads();
@@ -337,10 +446,13 @@ dat_attn_dkdv_kernel(const float *__restrict__ q, const float *__restrict__ k,
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = t0 + 4 * g + r;
-                const int qq = c0 + t;
-                float x = sa[r] * scale;
-                if (bias && kok && t < nq) x += bias[((size_t)bh * N + qq) * Ns + key];
-                p[r] = (kok && t < nq) ? expf(x - s_lse[t]) : 0.f;
+                const bool ok = kok && t < nq;
+                float x = sa[r] * scale2;
+                if (bias) {
+                    const int qq = c0 + (t < nq ? t : nq - 1);
+                    x = fmaf(bias[((size_t)bh * N + qq) * Ns + (kok ? key : Ns - 1)], kLog2e, x);
+                }
+                p[r] = ok ? __builtin_amdgcn_exp2f(x - s_lse[t]) : 0.f;
                 ds[r] = p[r] * (pa[r] - s_dl[t]);
             }
             // dV^T += dO^T P, dK^T += Q^T dS over this tile's 16 queries
@@ -384,25 +496,113 @@ msda_status check_attn(int64_t B, int64_t N, int64_t Ns, int64_t heads, int64_t 
     // every tensor of one launch is addressed with 64-bit offsets, but the
     // grid's y extent and the per-(b, h) row counts stay 32-bit
     if (B * heads >= 65536 || N >= lim / 64 || N > lim / (heads * DH)) return MSDA_ERR_UNSUPPORTED;
-    if (N * Ns >= lim) return MSDA_ERR_UNSUPPORTED;
-    // the keys (then values) of one (b, h) in LDS: at most 64 KB per workgroup
-    if ((((Ns + 15) / 16) * 16) * (DH + 2) * (int64_t)sizeof(float) > 65536)
+    // one (b, h)'s bias rows are read through a buffer of 32-bit byte offsets
+    if (N * Ns >= lim / 4) return MSDA_ERR_UNSUPPORTED;
+    // the keys (then values) of one (b, h) and their mask in LDS: at most 64 KB
+    // per workgroup
+    if ((((Ns + 15) / 16) * 16) * (DH + 3) * (int64_t)sizeof(float) > 65536)
         return MSDA_ERR_UNSUPPORTED;
     return MSDA_OK;
 }
 
+// LDS of one of K, V (rows padded to whole 16-key blocks) and of the key mask
 template <int DH>
 size_t attn_lds(int64_t Ns) {
     return (size_t)(((Ns + 15) / 16) * 16) * (DH + 2) * sizeof(float);
+}
+
+inline size_t mask_lds(int64_t Ns) { return (size_t)(((Ns + 15) / 16) * 16) * sizeof(float); }
+
+// Query tiling of the forward and dQ kernels: K and V stay resident when both
+// fit 64 KB of LDS, and then each wave may take several tiles of 16 queries
+// (K and V are staged once per workgroup instead of once per 64 queries):
+// the largest power of two that still leaves >= 1024 workgroups (four per
+// CU), when there are at least 2048 workgroups of one tile.
+struct AttnTiling {
+    bool resident;
+    int tiles;
+    int nkb;  // key blocks the kernel is built for: 1, 2, 4, 8 or 16
+    dim3 grid;
+    size_t lds;
+};
+
+template <int DH>
+AttnTiling attn_tiling(int64_t B, int64_t N, int64_t Ns, int64_t heads) {
+    AttnTiling t;
+    const size_t one = attn_lds<DH>(Ns), mask = mask_lds(Ns);
+    t.resident = 2 * one + mask <= 65536;
+    const int64_t qblocks = (N + 63) / 64;
+    int64_t tiles = 1;
+    if (t.resident && B * heads * qblocks >= 2048)
+        while (tiles * 2 <= qblocks &&
+               B * heads * ((qblocks + tiles * 2 - 1) / (tiles * 2)) >= 1024)
+            tiles *= 2;
+    t.tiles = (int)tiles;
+    const int64_t nkb = (Ns + 15) / 16;
+    t.nkb = nkb <= 1 ? 1 : nkb <= 2 ? 2 : nkb <= 4 ? 4 : nkb <= 8 ? 8 : 16;
+    t.grid = dim3((unsigned)((N + 64 * tiles - 1) / (64 * tiles)), (unsigned)(B * heads));
+    t.lds = (t.resident ? 2 * one : one) + mask;
+    return t;
+}
+
+// whether every Ns that maps to NKB key blocks keeps K and V resident
+template <int DH, int NKB>
+constexpr bool always_resident() {
+    return (2 * NKB * 16 * (DH + 2) + NKB * 16) * (int)sizeof(float) <= 65536;
+}
+
+template <int DH, int NKB>
+msda_status attn_fwd_nkb(const AttnTiling &t, const float *q, const float *k, const float *v,
+                         const float *bias, float *out, float *lse, int N, int Ns, int heads,
+                         float scale, hipStream_t s) {
+    if constexpr (always_resident<DH, NKB>()) {
+        hipLaunchKernelGGL((dat_attn_fwd_kernel<DH, NKB, true>), t.grid, dim3(kAttnThreads), t.lds,
+                           s, q, k, v, bias, out, lse, N, Ns, heads, scale, t.tiles);
+    } else {
+        if (t.resident)
+            hipLaunchKernelGGL((dat_attn_fwd_kernel<DH, NKB, true>), t.grid, dim3(kAttnThreads),
+                               t.lds, s, q, k, v, bias, out, lse, N, Ns, heads, scale, t.tiles);
+        else
+            hipLaunchKernelGGL((dat_attn_fwd_kernel<DH, NKB, false>), t.grid, dim3(kAttnThreads),
+                               t.lds, s, q, k, v, bias, out, lse, N, Ns, heads, scale, t.tiles);
+    }
+    return hip_status(hipGetLastError());
 }
 
 template <int DH>
 msda_status attn_fwd(const float *q, const float *k, const float *v, const float *bias,
                      float *out, float *lse, int64_t B, int64_t N, int64_t Ns, int64_t heads,
                      float scale, hipStream_t s) {
-    const dim3 grid((unsigned)((N + 63) / 64), (unsigned)(B * heads));
-    hipLaunchKernelGGL((dat_attn_fwd_kernel<DH>), grid, dim3(kAttnThreads), attn_lds<DH>(Ns), s,
-                       q, k, v, bias, out, lse, (int)N, (int)Ns, (int)heads, scale);
+    const AttnTiling t = attn_tiling<DH>(B, N, Ns, heads);
+    const int n = (int)N, ns = (int)Ns, hh = (int)heads;
+    switch (t.nkb) {
+    case 1: return attn_fwd_nkb<DH, 1>(t, q, k, v, bias, out, lse, n, ns, hh, scale, s);
+    case 2: return attn_fwd_nkb<DH, 2>(t, q, k, v, bias, out, lse, n, ns, hh, scale, s);
+    case 4: return attn_fwd_nkb<DH, 4>(t, q, k, v, bias, out, lse, n, ns, hh, scale, s);
+    case 8: return attn_fwd_nkb<DH, 8>(t, q, k, v, bias, out, lse, n, ns, hh, scale, s);
+    default: return attn_fwd_nkb<DH, 16>(t, q, k, v, bias, out, lse, n, ns, hh, scale, s);
+    }
+}
+
+template <int DH, int NKB>
+msda_status attn_dq_nkb(const AttnTiling &t, const float *q, const float *k, const float *v,
+                        const float *bias, const float *out, const float *lse, const float *gout,
+                        float *gq, float *gbias, float *delta, int N, int Ns, int heads,
+                        float scale, hipStream_t s) {
+    if constexpr (always_resident<DH, NKB>()) {
+        hipLaunchKernelGGL((dat_attn_dq_kernel<DH, NKB, true>), t.grid, dim3(kAttnThreads), t.lds,
+                           s, q, k, v, bias, out, lse, gout, gq, gbias, delta, N, Ns, heads,
+                           scale, t.tiles);
+    } else {
+        if (t.resident)
+            hipLaunchKernelGGL((dat_attn_dq_kernel<DH, NKB, true>), t.grid, dim3(kAttnThreads),
+                               t.lds, s, q, k, v, bias, out, lse, gout, gq, gbias, delta, N, Ns,
+                               heads, scale, t.tiles);
+        else
+            hipLaunchKernelGGL((dat_attn_dq_kernel<DH, NKB, false>), t.grid, dim3(kAttnThreads),
+                               t.lds, s, q, k, v, bias, out, lse, gout, gq, gbias, delta, N, Ns,
+                               heads, scale, t.tiles);
+    }
     return hip_status(hipGetLastError());
 }
 
@@ -411,11 +611,31 @@ msda_status attn_bwd(const float *q, const float *k, const float *v, const float
                      const float *out, const float *lse, const float *gout, float *gq, float *gk,
                      float *gv, float *gbias, float *delta, int64_t B, int64_t N, int64_t Ns,
                      int64_t heads, float scale, hipStream_t s) {
-    const dim3 g1((unsigned)((N + 63) / 64), (unsigned)(B * heads));
-    hipLaunchKernelGGL((dat_attn_dq_kernel<DH>), g1, dim3(kAttnThreads), attn_lds<DH>(Ns), s, q,
-                       k, v, bias, out, lse, gout, gq, gbias, delta, (int)N, (int)Ns,
-                       (int)heads, scale);
-    msda_status st = hip_status(hipGetLastError());
+    const AttnTiling t = attn_tiling<DH>(B, N, Ns, heads);
+    const int n = (int)N, ns = (int)Ns, hh = (int)heads;
+    msda_status st;
+    switch (t.nkb) {
+    case 1:
+        st = attn_dq_nkb<DH, 1>(t, q, k, v, bias, out, lse, gout, gq, gbias, delta, n, ns, hh,
+                                 scale, s);
+        break;
+    case 2:
+        st = attn_dq_nkb<DH, 2>(t, q, k, v, bias, out, lse, gout, gq, gbias, delta, n, ns, hh,
+                                 scale, s);
+        break;
+    case 4:
+        st = attn_dq_nkb<DH, 4>(t, q, k, v, bias, out, lse, gout, gq, gbias, delta, n, ns, hh,
+                                 scale, s);
+        break;
+    case 8:
+        st = attn_dq_nkb<DH, 8>(t, q, k, v, bias, out, lse, gout, gq, gbias, delta, n, ns, hh,
+                                 scale, s);
+        break;
+    default:
+        st = attn_dq_nkb<DH, 16>(t, q, k, v, bias, out, lse, gout, gq, gbias, delta, n, ns, hh,
+                                 scale, s);
+        break;
+    }
     if (st != MSDA_OK) return st;
     // split the queries so that the grid holds about two workgroups per CU;
     // split ranges are whole chunks, and more than one split adds atomically
