@@ -42,8 +42,12 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 FLUSH_BYTES = 512 << 20   # > the 256 MB Infinity Cache
-KERNEL_SOURCES = [os.path.join(ROOT, "scale_deformable_attention_04_amd", "csrc", f)
+CSRC = os.path.join(ROOT, "scale_deformable_attention_04_amd", "csrc")
+KERNEL_SOURCES = [os.path.join(CSRC, f)
                   for f in ("common.h", "bins.h", "msda.hip", "msda3d.hip", "dat_attn.hip")]
+# the sources the 2-D kernels are built from: the traffic counters of
+# profiles/traffic.json hold while these are unchanged
+ENCODER_SOURCES = [os.path.join(CSRC, f) for f in ("common.h", "bins.h", "msda.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 # kernel names as rocprofv3 reports them, per stage of a step
@@ -51,11 +55,11 @@ KERNELS = {
     "forward": "msda_fwd_kernel<32, float, false>",
     "fill_grad_value": "fill_zero_kernel",
     "clear_bins": "fill_zero_kernel",
-    "count": "bin_count_kernel",
+    "count": "bin_count_kernel<false>",
     "dots": "bwd_dots_kernel<32, float>",
-    "scan": "bin_scan_kernel",
-    "scatter": "bin_scatter_kernel",
-    "tiles": "grad_value_tile_kernel<32>",
+    "scan": "bin_scan_kernel<false>",
+    "scatter": "bin_scatter_kernel<false>",
+    "tiles": "grad_value_tile_kernel<32, false>",
 }
 
 
@@ -63,8 +67,9 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def source_sha() -> str:
-    return hashlib.sha256(b"".join(open(f, "rb").read() for f in KERNEL_SOURCES)).hexdigest()[:16]
+def source_sha(files=None) -> str:
+    files = KERNEL_SOURCES if files is None else files
+    return hashlib.sha256(b"".join(open(f, "rb").read() for f in files)).hexdigest()[:16]
 
 
 def byte_model(B, Nv, Nq, M, D, L, K, value_bytes=4):
@@ -357,7 +362,7 @@ def traffic_for(kernel_name: str):
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if t.get("source_sha") != source_sha():
+    if t.get("source_sha") != source_sha(ENCODER_SOURCES):
         return None
     k = t.get("kernels", {}).get(kernel_name)
     if not k:

@@ -70,13 +70,21 @@ import sys
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
-KERNEL_SOURCES = [os.path.join(ROOT, "scale_deformable_attention_04_amd", "csrc", f)
-                  for f in ("common.h", "bins.h", "msda.hip", "msda3d.hip", "dat_attn.hip")]
+CSRC = os.path.join(ROOT, "scale_deformable_attention_04_amd", "csrc")
+# per profile family, the sources its kernels are built from (the summaries
+# are tagged with their hash, so a change elsewhere leaves them valid)
+FAMILY_SOURCES = {
+    "encoder": ("common.h", "bins.h", "msda.hip"),
+    "fused_encoder": ("common.h", "bins.h", "msda.hip"),
+    "volume": ("common.h", "bins.h", "msda3d.hip"),
+    "dat": ("common.h", "bins.h", "msda.hip", "dat_attn.hip"),
+}
 COPY_BYTES = 256 << 20
 
 
-def source_sha() -> str:
-    return hashlib.sha256(b"".join(open(f, "rb").read() for f in KERNEL_SOURCES)).hexdigest()[:16]
+def source_sha(name: str = "encoder") -> str:
+    files = [os.path.join(CSRC, f) for f in FAMILY_SOURCES[name]]
+    return hashlib.sha256(b"".join(open(f, "rb").read() for f in files)).hexdigest()[:16]
 
 
 def short_name(name: str) -> str:
@@ -216,7 +224,7 @@ HEADERS = {
 def summarize(stats_dir, fetch_dir, write_dir, commands, name="encoder"):
     stats = _rows(os.path.join(stats_dir, "**", "*kernel_stats.csv"))
     head = list(HEADERS[name])
-    head[-1] += "; kernel source sha " + source_sha()
+    head[-1] += "; kernel source sha " + source_sha(name)
     lines = head + ["# command: " + commands["stats"], "",
                     f"{'kernel':46s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}"]
     for r in stats:
@@ -231,7 +239,8 @@ def summarize(stats_dir, fetch_dir, write_dir, commands, name="encoder"):
     copy_name = next((k for k in fetch if "MulFunctor" in k), None)
     f_scale = COPY_BYTES / fetch[copy_name] if copy_name and fetch.get(copy_name) else 1.0
     w_scale = COPY_BYTES / write[copy_name] if copy_name and write.get(copy_name) else 1.0
-    out = {"source_sha": source_sha(), "calibration_kernel": copy_name,
+    out = {"source_sha": source_sha(name), "sources": list(FAMILY_SOURCES[name]),
+           "calibration_kernel": copy_name,
            "calibration_bytes": COPY_BYTES, "fetch_scale": f_scale, "write_scale": w_scale,
            "commands": commands, "kernels": {}}
     for k in sorted(set(fetch) | set(write)):
