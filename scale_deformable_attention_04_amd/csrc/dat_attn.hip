@@ -38,7 +38,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kAttnThreads = 256;  // four waves
 constexpr int kAttnMinWaves = 4;   // per SIMD: at most 128 VGPRs a lane
 constexpr int kMaxKeys = 256;      // keys per (batch, head), at most
-constexpr int kQueryChunk = 64;    // queries staged per step of the dK/dV kernel
+constexpr int kQueryChunk = 64;    // queries per split unit of the dK/dV kernel
 
 __device__ __forceinline__ v4f mfma16x4(float a, float b, v4f c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -81,6 +81,45 @@ __device__ __forceinline__ void stage_rows(float *s, const float *__restrict__ s
         }
     }
 }
+
+// A chunk of ROWS rows of (b, h) held in registers between its loads and its
+// LDS stores, so that a kernel can load the next chunk while it computes on
+// the current one.  Rows n..ROWS-1 are stored as zeros.
+template <int DH, int ROWS>
+struct RowChunk {
+    static constexpr int C4 = DH / 4;
+    static constexpr int ITEMS = (ROWS * C4 + kAttnThreads - 1) / kAttnThreads;
+    float4 val[ITEMS];
+
+    __device__ __forceinline__ void load(const float *__restrict__ src, int b, int h, int T,
+                                         int heads, int n0, int n) {
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) {
+            const int i = threadIdx.x + it * kAttnThreads;
+            const int row = i / C4, c4 = i - row * C4;
+            val[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (row < n)
+                val[it] = reinterpret_cast<const float4 *>(
+                    src + (((size_t)b * T + n0 + row) * heads + h) * DH)[c4];
+        }
+    }
+
+    template <int RS>
+    __device__ __forceinline__ void store(float *s) const {
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) {
+            const int i = threadIdx.x + it * kAttnThreads;
+            const int row = i / C4, c4 = i - row * C4;
+            if (row < ROWS) {
+                float *d = s + row * RS + 4 * c4;
+                d[0] = val[it].x;
+                d[1] = val[it].y;
+                d[2] = val[it].z;
+                d[3] = val[it].w;
+            }
+        }
+    }
+};
 
 // Max and sum over the four lanes l, l^16, l^32, l^48 (the lane groups that
 // hold the other keys of the same query).
@@ -381,7 +420,9 @@ dat_attn_dq_kernel(const float *__restrict__ q, const float *__restrict__ k,
 // ---------------------------------------------------------------------------
 // backward, part 2: dK, dV.  Workgroup = (b, h, 64 keys, one range of
 // queries); wave w owns keys kb0 + 16w .. +15 and loops over the range in
-// chunks of kQueryChunk queries staged through LDS (Q, dO, lse, delta).
+// chunks of kQueryChunk queries (half that at head_dim 64) staged through
+// LDS (Q, dO, lse, delta), two buffers: the next chunk's loads are in flight while the current one is
+// consumed, and one barrier per chunk hands the buffers over.
 // ---------------------------------------------------------------------------
 template <int DH>
 __global__ void __launch_bounds__(kAttnThreads)
@@ -393,10 +434,11 @@ dat_attn_dkdv_kernel(const float *__restrict__ q, const float *__restrict__ k,
                      int queries_per_split) {
     constexpr int RS = DH + 2;
     constexpr int KS = DH / 4;
-    __shared__ float s_q[kQueryChunk * RS];
-    __shared__ float s_do[kQueryChunk * RS];
-    __shared__ float s_lse[kQueryChunk];
-    __shared__ float s_dl[kQueryChunk];
+    constexpr int QC = DH == 64 ? kQueryChunk / 2 : kQueryChunk;  // two buffers within 64 KB
+    __shared__ float s_q[2][QC * RS];
+    __shared__ float s_do[2][QC * RS];
+    __shared__ float s_lse[2][QC];
+    __shared__ float s_dl[2][QC];
 
     const int bh = blockIdx.y, b = bh / heads, h = bh % heads;
     const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 4, j = l & 15;
@@ -421,22 +463,43 @@ dat_attn_dkdv_kernel(const float *__restrict__ q, const float *__restrict__ k,
         dv[db] = v4f{0.f, 0.f, 0.f, 0.f};
     }
 
-    for (int c0 = q_begin; c0 < q_end; c0 += kQueryChunk) {
-        const int nq = min(kQueryChunk, q_end - c0);
-        __syncthreads();  // the previous chunk is consumed
-        stage_rows<DH, RS, kQueryChunk>(s_q, q, b, h, N, heads, c0, nq, kQueryChunk);
-        stage_rows<DH, RS, kQueryChunk>(s_do, gout, b, h, N, heads, c0, nq, kQueryChunk);
-        if (threadIdx.x < kQueryChunk) {
+    RowChunk<DH, QC> cq, cd;
+    float vl = 0.f, vd = 0.f;
+    auto load_chunk = [&](int c0) {
+        const int nq = min(QC, q_end - c0);
+        cq.load(q, b, h, N, heads, c0, nq);
+        cd.load(gout, b, h, N, heads, c0, nq);
+        if (threadIdx.x < QC) {
             const bool ok = (int)threadIdx.x < nq;
-            s_lse[threadIdx.x] = ok ? lse[(size_t)bh * N + c0 + threadIdx.x] * kLog2e : 0.f;
-            s_dl[threadIdx.x] = ok ? delta[(size_t)bh * N + c0 + threadIdx.x] : 0.f;
+            vl = ok ? lse[(size_t)bh * N + c0 + threadIdx.x] * kLog2e : 0.f;
+            vd = ok ? delta[(size_t)bh * N + c0 + threadIdx.x] : 0.f;
         }
-        __syncthreads();
+    };
+    auto store_chunk = [&](int buf) {
+        cq.template store<RS>(s_q[buf]);
+        cd.template store<RS>(s_do[buf]);
+        if (threadIdx.x < QC) {
+            s_lse[buf][threadIdx.x] = vl;
+            s_dl[buf][threadIdx.x] = vd;
+        }
+    };
+    if (q_begin < q_end) {
+        load_chunk(q_begin);
+        store_chunk(0);
+    }
+    __syncthreads();
+
+    int buf = 0;
+    for (int c0 = q_begin; c0 < q_end; c0 += QC, buf ^= 1) {
+        const int nq = min(QC, q_end - c0);
+        const bool more = c0 + QC < q_end;
+        if (more) load_chunk(c0 + QC);
+        const float *sq = s_q[buf], *sd = s_do[buf], *sl = s_lse[buf], *sdl = s_dl[buf];
         for (int t0 = 0; t0 < nq; t0 += 16) {
             // S[query t0 + 4g + r][key] and dP[query t0 + 4g + r][key]
             v4f sa = {0.f, 0.f, 0.f, 0.f}, pa = {0.f, 0.f, 0.f, 0.f};
-            const float *qa = s_q + (t0 + j) * RS + g;
-            const float *da = s_do + (t0 + j) * RS + g;
+            const float *qa = sq + (t0 + j) * RS + g;
+            const float *da = sd + (t0 + j) * RS + g;
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 sa = mfma16x4(qa[4 * s], kr[s], sa);
@@ -452,14 +515,14 @@ dat_attn_dkdv_kernel(const float *__restrict__ q, const float *__restrict__ k,
                     const int qq = c0 + (t < nq ? t : nq - 1);
                     x = fmaf(bias[((size_t)bh * N + qq) * Ns + (kok ? key : Ns - 1)], kLog2e, x);
                 }
-                p[r] = ok ? __builtin_amdgcn_exp2f(x - s_lse[t]) : 0.f;
-                ds[r] = p[r] * (pa[r] - s_dl[t]);
+                p[r] = ok ? __builtin_amdgcn_exp2f(x - sl[t]) : 0.f;
+                ds[r] = p[r] * (pa[r] - sdl[t]);
             }
             // dV^T += dO^T P, dK^T += Q^T dS over this tile's 16 queries
 #pragma unroll
             for (int db = 0; db < DH / 16; ++db) {
-                const float *dcol = s_do + (t0 + 4 * g) * RS + db * 16 + j;
-                const float *qcol = s_q + (t0 + 4 * g) * RS + db * 16 + j;
+                const float *dcol = sd + (t0 + 4 * g) * RS + db * 16 + j;
+                const float *qcol = sq + (t0 + 4 * g) * RS + db * 16 + j;
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     dv[db] = mfma16x4(dcol[s * RS], p[s], dv[db]);
@@ -467,6 +530,10 @@ dat_attn_dkdv_kernel(const float *__restrict__ q, const float *__restrict__ k,
                 }
             }
         }
+        // the other buffer was last read in the previous chunk, before the
+        // barrier that ended it
+        if (more) store_chunk(buf ^ 1);
+        __syncthreads();
     }
     if (!kok) return;
     float *gkr = gk + krow, *gvr = gv + krow;
@@ -637,10 +704,10 @@ msda_status attn_bwd(const float *q, const float *k, const float *v, const float
         break;
     }
     if (st != MSDA_OK) return st;
-    // split the queries so that the grid holds about two workgroups per CU;
+    // split the queries so that the grid holds about four workgroups per CU;
     // split ranges are whole chunks, and more than one split adds atomically
     const int64_t key_blocks = (Ns + 63) / 64, chunks = (N + kQueryChunk - 1) / kQueryChunk;
-    int64_t splits = 512 / (B * heads * key_blocks);
+    int64_t splits = 1024 / (B * heads * key_blocks);
     splits = splits < 1 ? 1 : (splits > chunks ? chunks : splits);
     const int64_t per = ((chunks + splits - 1) / splits) * kQueryChunk;
     splits = (N + per - 1) / per;
