@@ -95,6 +95,25 @@ def test_dat_attention_max_keys(msda):
     check_attention(msda, w)
 
 
+# key counts that select each kernel build (key blocks 2, 8, 16) and LDS mode:
+# K and V resident together, or one buffer (head_dim 64 with >= 113 keys,
+# head_dim 32 with > 240); Ns % 4 != 0 reads the bias rows unaligned
+@pytest.mark.parametrize("heads,C,khw", [(2, 64, (5, 5)), (1, 64, (16, 15)), (2, 128, (8, 16)),
+                                         (2, 128, (7, 17)), (1, 16, (16, 16))])
+def test_dat_attention_key_blocks(msda, heads, C, khw):
+    _say(f"dat attention key blocks heads={heads} C={C} Ns={khw}")
+    w = workloads.dat_case(3701 + C + khw[0] * khw[1], 2, 7, 9, C, heads, 1, khw[0], khw[1])
+    check_attention(msda, w)
+
+
+def test_dat_attention_query_tiles(msda):
+    # 8 * 16 (batch, head) pairs of 1000 queries: enough workgroups that each
+    # wave takes two 16-query tiles, the last workgroup of each pair ragged
+    _say("dat attention several query tiles per wave")
+    w = workloads.dat_case(3801, 8, 25, 40, 256, 16, 1, 3, 5)
+    check_attention(msda, w)
+
+
 def test_dat_attention_empty(msda):
     _say("dat attention N=0")
     k = torch.randn(2, 5, 2, 32, device="cuda")
