@@ -152,14 +152,14 @@ __device__ __forceinline__ float2 prologue_location(float2 r, float2 o, int4 lvl
     return make_float2(r.x + o.x / (float)lvl.y, r.y + o.y / (float)lvl.x);
 }
 
-// Softmax statistics of the groups of nitems consecutive items starting at
-// point pt0 into s_st[item * groups + group].
+// Softmax statistics of the groups of nitems items, the first at point pt0
+// and the others istride points apart, into s_st[item * groups + group].
 __device__ __forceinline__ void stage_softmax_stats(float2 *s_st, const Prologue &pr, size_t pt0,
-                                                    int nitems, int L, int K) {
+                                                    size_t istride, int nitems, int L, int K) {
     const int LK = L * K, ng = pr.per_level ? L : 1, gs = pr.per_level ? K : LK;
     for (int idx = threadIdx.x; idx < nitems * ng; idx += blockDim.x) {
         const int i1 = idx / ng, g = idx - i1 * ng;
-        s_st[idx] = softmax_stats(pr.logits + pt0 + (size_t)i1 * LK + (size_t)g * gs, gs);
+        s_st[idx] = softmax_stats(pr.logits + pt0 + (size_t)i1 * istride + (size_t)g * gs, gs);
     }
 }
 
@@ -184,22 +184,28 @@ msda_fwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
     float2 *s_st = reinterpret_cast<float2 *>(s_w + IPB * dm.PS);  // FUSED: softmax stats
 
     const int M = dm.M, K = dm.K, LK = dm.L * dm.K;
-    const int NqM = dm.Nq * M;
+    // blocks of IPB queries of one (batch, head), dm.nblk per (batch, head),
+    // in (batch, head, block) order: each XCD takes a contiguous range, so
+    // one or two heads, whose value rows then stay in that XCD's L2
     const int wg = xcd_contiguous(blockIdx.x, gridDim.x);
-    const int b = wg / dm.nblk + dm.b0;
-    const int item0 = (wg % dm.nblk) * IPB;
-    const int nitems = min(IPB, NqM - item0);
+    const int bm = wg / dm.nblk + dm.b0 * M;
+    const int m = bm % M, b = bm / M;
+    const int q0 = (wg % dm.nblk) * IPB;
+    const int nitems = min(IPB, dm.Nq - q0);
     const uint32_t row_stride = (uint32_t)M * D * 4u;
+    const uint32_t head_off = (uint32_t)m * D * 4u;
 
     stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, 0x7fffffff);
 
     const size_t slice = (size_t)dm.Nv * M * D;
     const rsrc_t vr = make_rsrc(value + (size_t)b * slice, (uint32_t)(slice * sizeof(VT)));
-    const size_t pt0 = ((size_t)b * NqM + item0) * LK;
+    const size_t row0 = ((size_t)b * dm.Nq + q0) * M + m;  // item row of query q0
+    const size_t pt0 = row0 * LK;
+    const size_t istride = (size_t)M * LK;  // points between consecutive queries' items
     const int ng = pr.per_level ? dm.L : 1;
     if constexpr (FUSED) {
         if (!pr.shfl) {
-            stage_softmax_stats(s_st, pr, pt0, nitems, dm.L, K);
+            stage_softmax_stats(s_st, pr, pt0, istride, nitems, dm.L, K);
             __syncthreads();
         }
     }
@@ -212,12 +218,12 @@ msda_fwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
         if (j0) __syncthreads();  // previous chunk consumed
         for (int idx = threadIdx.x; idx < nitems * pc; idx += kThreads) {
             const int i1 = idx / pc, jj = idx - i1 * pc, j = j0 + jj;
-            const size_t p = pt0 + (size_t)i1 * LK + j;
+            const size_t p = pt0 + (size_t)i1 * istride + j;
             const int l = j / K;
             float2 uv;
             float A;
             if constexpr (FUSED) {
-                const int q = (item0 + i1) / M;
+                const int q = q0 + i1;
                 const float2 r =
                     reinterpret_cast<const float2 *>(pr.ref)[((size_t)b * dm.Nq + q) * dm.L + l];
                 uv = prologue_location(r, reinterpret_cast<const float2 *>(pr.off)[p],
@@ -237,9 +243,7 @@ msda_fwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
                 uv = reinterpret_cast<const float2 *>(loc)[p];
                 A = attn[p];
             }
-            const int m = (item0 + i1) % M;
-            Neighbours n = neighbours(uv.x, uv.y, s_lv.lvl[l], row_stride,
-                                      (uint32_t)m * D * 4u, dm.align);
+            Neighbours n = neighbours(uv.x, uv.y, s_lv.lvl[l], row_stride, head_off, dm.align);
             s_off[i1 * dm.PS + jj] = n.off;
             // skip outside neighbours outright, so a non-finite A cannot leak through them
             s_w[i1 * dm.PS + jj] = make_float4((n.valid & 1u) ? A * n.w.x : 0.f,
@@ -267,7 +271,7 @@ msda_fwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
         }
     }
     if (it < nitems) {
-        float4 *o = reinterpret_cast<float4 *>(out + ((size_t)b * NqM + item0 + it) * D) + c;
+        float4 *o = reinterpret_cast<float4 *>(out + (row0 + (size_t)it * M) * D) + c;
         *o = acc;
     }
 }
@@ -442,7 +446,7 @@ fused_prologue_kernel(const int64_t *__restrict__ shapes, const int64_t *__restr
         const size_t pt0 = (size_t)item0 * LK;
         if (!pr.shfl) {
             if (blk != (int64_t)blockIdx.x) __syncthreads();  // s_st is reused
-            stage_softmax_stats(s_st, pr, pt0, nitems, L, K);
+            stage_softmax_stats(s_st, pr, pt0, (size_t)LK, nitems, L, K);
             __syncthreads();
         }
         // idx runs over whole items, 256 at a time: with shfl every softmax run
@@ -620,14 +624,13 @@ msda_status launch_fwd(const void *value, const int64_t *shapes, const int64_t *
         }
     }
     const size_t lds = p.lds + (size_t)st_bytes;
-    const int64_t items = Nq * M;
-    const int64_t gx = (items + p.ipb - 1) / p.ipb;
-    const int64_t bchunk = batch_chunk(gx, B);
+    const int64_t gx = (Nq + p.ipb - 1) / p.ipb;  // query blocks per (batch, head)
+    const int64_t bchunk = batch_chunk(gx * M, B);
     for (int64_t b0 = 0; b0 < B; b0 += bchunk) {
         const int64_t nb = (B - b0) < bchunk ? (B - b0) : bchunk;
         Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, p.pc, p.ps, (int)b0, (int)gx, 0, 0};
         dm.align = align ? 1 : 0;
-        const dim3 grid((unsigned)(gx * nb));
+        const dim3 grid((unsigned)(gx * M * nb));
         if (pr)
             hipLaunchKernelGGL((msda_fwd_kernel<D, VT, true>), grid, dim3(kThreads), lds, s,
                                static_cast<const VT *>(value), shapes, starts, loc, attn, prv,
