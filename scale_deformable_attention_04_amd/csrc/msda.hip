@@ -85,6 +85,7 @@ namespace {
 
 constexpr int kSetupLdsBytes = 36 * 1024;  // per-workgroup budget for the point tables
 constexpr int kDotsGrid = 512;             // workgroups of the dots kernel, at most
+constexpr int kDotsBatch = 4;              // points whose row loads the dots kernel overlaps
 
 // Raw inputs of the fused prologue, which computes the sampling location and
 // the attention weight of each point from them:
@@ -359,7 +360,38 @@ bwd_dots_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
         __syncthreads();
         if (it < nitems) {
             const int base = it * dm.PS;
-            for (int jj = 0; jj < pc; ++jj) {
+            // kDotsBatch points at a time: their 4 * kDotsBatch row loads are in
+            // flight together (this kernel runs at low occupancy beside the
+            // grad_value kernels, so one point's four loads would leave the
+            // wave waiting on each point's latency)
+            int jj = 0;
+            for (; jj + kDotsBatch <= pc; jj += kDotsBatch) {
+                uint4 o[kDotsBatch];
+                float4 v[kDotsBatch][4];
+#pragma unroll
+                for (int u = 0; u < kDotsBatch; ++u) o[u] = s_off[base + jj + u];
+#pragma unroll
+                for (int u = 0; u < kDotsBatch; ++u) {
+                    v[u][0] = Row4<VT>::load(vr, o[u].x, 4 * c);
+                    v[u][1] = Row4<VT>::load(vr, o[u].y, 4 * c);
+                    v[u][2] = Row4<VT>::load(vr, o[u].z, 4 * c);
+                    v[u][3] = Row4<VT>::load(vr, o[u].w, 4 * c);
+                }
+                uint4 d[kDotsBatch];
+#pragma unroll
+                for (int u = 0; u < kDotsBatch; ++u)
+                    d[u] = make_uint4(__float_as_uint(group_sum<G>(dot4(g4, v[u][0]))),
+                                      __float_as_uint(group_sum<G>(dot4(g4, v[u][1]))),
+                                      __float_as_uint(group_sum<G>(dot4(g4, v[u][2]))),
+                                      __float_as_uint(group_sum<G>(dot4(g4, v[u][3]))));
+                // the group's lanes are one wave: every lane has read the
+                // offsets before lane 0 overwrites them
+                if (c == 0) {
+#pragma unroll
+                    for (int u = 0; u < kDotsBatch; ++u) s_off[base + jj + u] = d[u];
+                }
+            }
+            for (; jj < pc; ++jj) {
                 const uint4 o = s_off[base + jj];
                 const float4 v0 = Row4<VT>::load(vr, o.x, 4 * c);
                 const float4 v1 = Row4<VT>::load(vr, o.y, 4 * c);
@@ -369,8 +401,6 @@ bwd_dots_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
                 const float d1 = group_sum<G>(dot4(g4, v1));
                 const float d2 = group_sum<G>(dot4(g4, v2));
                 const float d3 = group_sum<G>(dot4(g4, v3));
-                // the group's lanes are one wave: every lane has read the
-                // offsets before lane 0 overwrites them
                 if (c == 0)
                     s_off[base + jj] = make_uint4(__float_as_uint(d0), __float_as_uint(d1),
                                                   __float_as_uint(d2), __float_as_uint(d3));
