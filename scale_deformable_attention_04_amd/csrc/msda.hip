@@ -84,6 +84,10 @@ SideStream *get() {
 namespace {
 
 constexpr int kSetupLdsBytes = 36 * 1024;  // per-workgroup budget for the point tables
+// the forward's budget when an item has more than 16 points: half, so that
+// 8 workgroups fit a CU's LDS, with the points in chunks of at least 16 (the
+// dots kernel, capped at 2 workgroups per CU, keeps whole items instead)
+constexpr int kFwdLdsBytes = 18 * 1024;
 constexpr int kDotsGrid = 512;             // workgroups of the dots kernel, at most
 constexpr int kDotsBatch = 4;              // points whose row loads the dots kernel overlaps
 
@@ -617,15 +621,25 @@ struct Launch {
 };
 
 // `reserve`: LDS bytes taken from the point-table budget for other uses.
-Launch plan(int64_t D, int64_t L, int64_t K, int bytes_per_point, int reserve = 0) {
+Launch plan(int64_t D, int64_t L, int64_t K, int bytes_per_point, int reserve = 0,
+            int budget = kSetupLdsBytes) {
     Launch p;
     p.ipb = (int)(kThreads / (D / 4));
     const int lk = (int)(L * K);
-    int pc = (kSetupLdsBytes - reserve) / (p.ipb * bytes_per_point) - 2;
+    int pc = (budget - reserve) / (p.ipb * bytes_per_point) - 2;
     pc = pc < 1 ? 1 : pc;
     p.pc = pc < lk ? pc : lk;
     p.ps = p.pc + ((p.pc % 2 == 0) ? 1 : 2);
     p.lds = (size_t)p.ipb * p.ps * bytes_per_point;
+    return p;
+}
+
+Launch fwd_plan(int64_t D, int64_t L, int64_t K, int reserve = 0) {
+    Launch p = plan(D, L, K, 32, reserve);
+    if (L * K > 16) {
+        const Launch half = plan(D, L, K, 32, reserve, kFwdLdsBytes);
+        if (half.pc >= 16) p = half;
+    }
     return p;
 }
 
@@ -643,14 +657,14 @@ msda_status launch_fwd(const void *value, const int64_t *shapes, const int64_t *
     const int ipb = (int)(kThreads / (D / 4));
     Prologue prv = pr ? *pr : Prologue{nullptr, nullptr, nullptr, 0, 0, nullptr, nullptr};
     int st_bytes = 0;
-    Launch p = plan(D, L, K, 32);
+    Launch p = fwd_plan(D, L, K);
     if (pr) {
         // softmax by lane shuffles when the items' points come in one chunk and
         // the groups are power-of-two runs of at most 64; else statistics in LDS
         prv.shfl = (p.pc == L * K && pow2_run(pr->per_level ? K : L * K)) ? 1 : 0;
         if (!prv.shfl) {
             st_bytes = ipb * (pr->per_level ? (int)L : 1) * (int)sizeof(float2);
-            p = plan(D, L, K, 32, st_bytes);
+            p = fwd_plan(D, L, K, st_bytes);
         }
     }
     const size_t lds = p.lds + (size_t)st_bytes;
