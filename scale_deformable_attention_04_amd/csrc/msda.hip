@@ -11,7 +11,8 @@
 // into LDS, and the lane groups read it from there.
 //
 // Forward (msda_fwd_kernel): per item, sum over its points of A * bilinear
-// sample, accumulated in registers, one store per item.
+// sample, accumulated in registers, one store per item.  A workgroup takes
+// consecutive queries of one (batch, head).
 //
 // Backward (msda_backward):
 //   bwd_dots_kernel (on a side stream, concurrently with the rest): per
