@@ -795,10 +795,10 @@ grad_value_tile_kernel(const int64_t *__restrict__ shapes, const int64_t *__rest
                 const int cT = (y + 1) * kCellsW + x, cB = y * kCellsW + x;
                 // cells (x, y+1) then (x+1, y+1): top-right, then top-left roles;
                 // cells (x, y) then (x+1, y): bottom-right, then bottom-left roles
-                pull_range<kQuads>(acc[o], wP, gP + q, (int)stP[cT], (int)stP[cT + 1], (int)stP[cT + 2],
-                           1, 0);
-                pull_range<kQuads>(acc[o], wP, gP + q, (int)stP[cB], (int)stP[cB + 1], (int)stP[cB + 2],
-                           3, 2);
+                pull_range<kQuads>(acc[o], wP, gP + q, (int)stP[cT], (int)stP[cT + 1],
+                                   (int)stP[cT + 2], 1, 0);
+                pull_range<kQuads>(acc[o], wP, gP + q, (int)stP[cB], (int)stP[cB + 1],
+                                   (int)stP[cB + 2], 3, 2);
             }
             // 6. the item ends with A: write its tile
             if (A.off + kSub >= A.it.z) {

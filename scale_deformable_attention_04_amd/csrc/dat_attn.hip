@@ -10,19 +10,21 @@
 // 16x16 tile of C per 64-lane wave; lane l supplies A[l%16][l/16] and
 // B[l/16][l%16] and holds C[4*(l/16) + r][l%16] in register r).
 //
-// Forward (dat_attn_fwd_kernel): a wave owns tiles of 16 queries.  It computes the
-// transposed scores S^T = K Q^T one 16-key block at a time (keys in LDS,
-// its queries' rows in registers), so each lane holds four keys of one query
-// for every block; the row max and sum are lane-local plus two cross-row
-// shuffles.  O^T = V^T P^T then takes P^T straight from those registers: its
-// k-step s covers keys {4g + s : g = 0..3} of the block, which lane group g
-// already holds as its register s.
+// Forward (dat_attn_fwd_kernel): a wave owns tiles of 16 queries.  It
+// computes the transposed scores S^T = K Q^T one 16-key block at a time
+// (keys in LDS, its queries' rows in registers), so each lane holds four keys
+// of one query for every block; the row max and sum are lane-local plus two
+// cross-row shuffles.  O^T = V^T P^T then takes P^T straight from those
+// registers: its k-step s covers keys {4g + s : g = 0..3} of the block, which
+// lane group g already holds as its register s.  The kernels are built per
+// count of 16-key blocks (1, 2, 4, 8, 16), so the score registers are a fixed
+// array; scores are kept in base-2 units (log2 e folded into the scale).
 //
 // Backward: dat_attn_dq_kernel (per query block, like the forward) forms
 // delta = rowsum(dO * O), P from the saved log-sum-exp, dP^T = V dO^T,
 // dS = P (dP - delta), dQ = scale dS K and, when asked for, dbias = dS.
 // dat_attn_dkdv_kernel (per 64-key block, the four waves one 16-key block
-// each, queries in chunks staged through LDS) computes S = Q K^T and dP =
+// each, queries in double-buffered chunks staged through LDS) computes S = Q K^T and dP =
 // dO V^T with keys as columns, so that dV^T = dO^T P and dK^T = scale Q^T dS
 // contract over the queries with the same register trick; chunks of the
 // query range from several workgroups add into dK, dV with fp32 atomics.
@@ -421,8 +423,9 @@ dat_attn_dq_kernel(const float *__restrict__ q, const float *__restrict__ k,
 // backward, part 2: dK, dV.  Workgroup = (b, h, 64 keys, one range of
 // queries); wave w owns keys kb0 + 16w .. +15 and loops over the range in
 // chunks of kQueryChunk queries (half that at head_dim 64) staged through
-// LDS (Q, dO, lse, delta), two buffers: the next chunk's loads are in flight while the current one is
-// consumed, and one barrier per chunk hands the buffers over.
+// LDS (Q, dO, lse, delta), two buffers: the next chunk's loads are in flight
+// while the current one is consumed, and one barrier per chunk hands the
+// buffers over.
 // ---------------------------------------------------------------------------
 template <int DH>
 __global__ void __launch_bounds__(kAttnThreads)

@@ -773,8 +773,8 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
     st = per_batch(gb * M, [&](int64_t b0, unsigned grid) {
         Dims d2 = dm;
         d2.b0 = (int)b0;
-        hipLaunchKernelGGL(bin_count_kernel<false>, dim3(grid), dim3(kThreads), 4 * (size_t)hist_cap, s,
-                           shapes, starts, loc, w.counts, hist_cap, d2);
+        hipLaunchKernelGGL(bin_count_kernel<false>, dim3(grid), dim3(kThreads),
+                           4 * (size_t)hist_cap, s, shapes, starts, loc, w.counts, hist_cap, d2);
     });
     if (st != MSDA_OK) return st;
     ex.stamp(3, true, s);
@@ -790,8 +790,9 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
     st = per_batch(gb * M, [&](int64_t b0, unsigned grid) {
         Dims d2 = dm;
         d2.b0 = (int)b0;
-        hipLaunchKernelGGL(bin_scatter_kernel<false>, dim3(grid), dim3(kThreads), 8 * (size_t)hist_cap,
-                           s, shapes, starts, loc, attn, w.cursor, w.recs, hist_cap, d2);
+        hipLaunchKernelGGL(bin_scatter_kernel<false>, dim3(grid), dim3(kThreads),
+                           8 * (size_t)hist_cap, s, shapes, starts, loc, attn, w.cursor, w.recs,
+                           hist_cap, d2);
     });
     if (st != MSDA_OK) return st;
     ex.stamp(5, true, s);
@@ -802,8 +803,9 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
         if (st != MSDA_OK) return st;
     }
     ex.stamp(6, false, s);
-    hipLaunchKernelGGL((grad_value_tile_kernel<D, false>), dim3((unsigned)grid), dim3(kTileThreads), 0, s,
-                       shapes, starts, gout, w.items, w.work_total, w.recs, gval, dm);
+    hipLaunchKernelGGL((grad_value_tile_kernel<D, false>), dim3((unsigned)grid),
+                       dim3(kTileThreads), 0, s, shapes, starts, gout, w.items, w.work_total,
+                       w.recs, gval, dm);
     st = hip_status(hipGetLastError());
     ex.stamp(6, true, s);
     if (st == MSDA_OK && ex.side) st = hip_status(hipStreamWaitEvent(s, ex.join, 0));

@@ -83,7 +83,8 @@ __device__ __forceinline__ Corners corners3(float u, float v, float w, int4 lvl,
     const int yi = (int)fminf(fmaxf(y0, -1.f), (float)H);
     const int zi = (int)fminf(fmaxf(z0, -1.f), (float)Z);
     const uint32_t o = (uint32_t)(S + (zi * H + yi) * W + xi) * row_stride + head_off;
-    const uint32_t sx = row_stride, sy = (uint32_t)W * row_stride, sz = (uint32_t)(H * W) * row_stride;
+    const uint32_t sx = row_stride, sy = (uint32_t)W * row_stride;
+    const uint32_t sz = (uint32_t)(H * W) * row_stride;
     const bool z0v = vz0, z1v = vz1;
     c.lo.x = (vx0 && vy0 && z0v) ? o : kOOB;
     c.lo.y = (vx1 && vy0 && z0v) ? o + sx : kOOB;
@@ -317,11 +318,14 @@ msda3d_dots_kernel(const VT *__restrict__ value, const int64_t *__restrict__ sha
                 ga = gz * (gy * (gx * d0 + fx * d1) + fy * (gx * d2 + fx * d3)) +
                      fz * (gy * (gx * d4 + fx * d5) + fy * (gx * d6 + fx * d7));
                 lx = A * voxel_scale(lvl.z, dm.align) *
-                     (gz * (gy * (d1 - d0) + fy * (d3 - d2)) + fz * (gy * (d5 - d4) + fy * (d7 - d6)));
+                     (gz * (gy * (d1 - d0) + fy * (d3 - d2)) +
+                      fz * (gy * (d5 - d4) + fy * (d7 - d6)));
                 ly = A * voxel_scale(lvl.y, dm.align) *
-                     (gz * (gx * (d2 - d0) + fx * (d3 - d1)) + fz * (gx * (d6 - d4) + fx * (d7 - d5)));
+                     (gz * (gx * (d2 - d0) + fx * (d3 - d1)) +
+                      fz * (gx * (d6 - d4) + fx * (d7 - d5)));
                 lz = A * voxel_scale(lvl.x, dm.align) *
-                     (gy * (gx * (d4 - d0) + fx * (d5 - d1)) + fy * (gx * (d6 - d2) + fx * (d7 - d3)));
+                     (gy * (gx * (d4 - d0) + fx * (d5 - d1)) +
+                      fy * (gx * (d6 - d2) + fx * (d7 - d3)));
             }
             grad_attn[p] = ga;
             grad_loc[3 * p] = lx;
