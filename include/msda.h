@@ -98,6 +98,7 @@ typedef enum msda_dtype {
 #define MSDA_BWD_ACCUMULATE 1u /* backward: add into grad_value instead of overwriting  */
 #define MSDA_ALIGN_CORNERS 2u  /* both: x = u*(W-1), y = v*(H-1) (align_corners=True)   */
 #define MSDA_SOFTMAX_PER_LEVEL 4u /* fused entry points: softmax over each level's K points */
+#define MSDA_BWD_BINNED 8u     /* backward: the binned grad_value pipeline at any size      */
 
 /*
  * Forward: out = MSDeformAttn core(value, level table, sampling_loc, attn_weight).
@@ -139,11 +140,16 @@ size_t msda_backward_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int64_t M
  * separate workspaces.
  *
  * flags: MSDA_BWD_ACCUMULATE and/or MSDA_ALIGN_CORNERS (the latter as given to
- * the forward).  grad_value is overwritten (zero-filled first) unless flags has
- * MSDA_BWD_ACCUMULATE, in which case the gradient is added to it.  Its
- * summation order is not fixed, so repeated calls may differ in the last
- * bits.  grad_sampling_loc and grad_attn_weight are overwritten and
+ * the forward), MSDA_BWD_BINNED.  grad_value is overwritten (zero-filled
+ * first) unless flags has MSDA_BWD_ACCUMULATE, in which case the gradient is
+ * added to it.  Its summation order is not fixed, so repeated calls may differ
+ * in the last bits.  grad_sampling_loc and grad_attn_weight are overwritten and
  * deterministic.
+ *
+ * Heads of at most 256 points (Nq * L * K <= 256 per (batch, head)) run as
+ * one kernel, a workgroup per (batch, head, 256 pixels); all others, and
+ * every call with MSDA_BWD_BINNED, run the binned pipeline.  Both compute the
+ * same gradients; the workspace is required either way.
  */
 msda_status msda_backward(const void *value, int value_dtype,
                           const int64_t *spatial_shapes, const int64_t *level_start_index,
@@ -167,6 +173,8 @@ msda_status msda_backward(const void *value, int value_dtype,
  *   1 grad_attn_weight / grad_sampling_loc   2 workspace clear
  *   3 points per value tile   4 count scan   5 record scatter into tiles
  *   6 grad_value tiles
+ * A small problem (see msda_backward) runs as one kernel, recorded as stage 1;
+ * its other stages are empty.
  * events: 2 * MSDA_BWD_STAGES hipEvent_t created by the caller (with timing);
  * a null entry is skipped (an event record costs the stream a few
  * microseconds, so a caller timing one stage passes only its two events).

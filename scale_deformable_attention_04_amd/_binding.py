@@ -28,6 +28,7 @@ MSDA_BF16 = 1
 MSDA_BWD_ACCUMULATE = 1
 MSDA_ALIGN_CORNERS = 2
 MSDA_SOFTMAX_PER_LEVEL = 4
+MSDA_BWD_BINNED = 8
 
 EXPORTED = ("msda_forward", "msda_backward_workspace_size", "msda_backward",
             "msda_backward_events", "msda_forward_fused", "msda_backward_fused_workspace_size",
@@ -255,12 +256,14 @@ def backward(value: torch.Tensor, spatial_shapes: torch.Tensor, level_start_inde
              grad_attn_weight: Optional[torch.Tensor] = None,
              accumulate: bool = False, validate: bool = True,
              workspace: Optional[torch.Tensor] = None, events: Optional[list] = None,
-             align_corners: bool = False
+             align_corners: bool = False, binned: bool = False
              ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """msda_backward: (grad_value fp32 [B,Nv,M,D], grad_sampling_loc, grad_attn_weight).
 
     accumulate=True adds into the given grad_value instead of overwriting it.
     align_corners must be the value given to the forward.
+    binned=True runs the binned grad_value pipeline even where the library
+    would take its one-kernel path for small problems.
     workspace: a uint8 device tensor of at least workspace_size(...) bytes; by
     default a per-device buffer cached by this module is used (calls on
     different streams that overlap in time must pass their own).
@@ -285,7 +288,8 @@ def backward(value: torch.Tensor, spatial_shapes: torch.Tensor, level_start_inde
         grad_attn_weight = torch.empty_like(attn_weight)
     else:
         _need(grad_attn_weight, "grad_attn_weight", torch.float32, dev, attn_weight.shape)
-    flags = (MSDA_BWD_ACCUMULATE if accumulate else 0) | (MSDA_ALIGN_CORNERS if align_corners else 0)
+    flags = ((MSDA_BWD_ACCUMULATE if accumulate else 0) |
+             (MSDA_ALIGN_CORNERS if align_corners else 0) | (MSDA_BWD_BINNED if binned else 0))
     need = workspace_size(B, Nv, Nq, M, D, L, K)
     if workspace is None:
         workspace = _workspace(dev, need)

@@ -91,6 +91,11 @@ constexpr int kSetupLdsBytes = 36 * 1024;  // per-workgroup budget for the point
 constexpr int kFwdLdsBytes = 18 * 1024;
 constexpr int kDotsGrid = 512;             // workgroups of the dots kernel, at most
 constexpr int kDotsBatch = 4;              // points whose row loads the dots kernel overlaps
+// the one-kernel backward of heads with few points: at most kSmallPoints
+// points per (batch, head), workgroups of kSmallPixels pixels
+constexpr int kSmallPoints = 256;
+constexpr int kSmallPixels = 256;
+static_assert(kSmallPoints <= kThreads, "one thread per point builds the point table");
 
 // Raw inputs of the fused prologue, which computes the sampling location and
 // the attention weight of each point from them:
@@ -449,6 +454,194 @@ bwd_dots_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
             }
         }
     }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// backward of heads with few points, in one kernel
+// Workgroup = (batch b, head m, range of kSmallPixels pixels).  Every point of
+// the head (at most kSmallPoints) is tabled once (neighbours, weights); its
+// neighbours inside the range are counting-sorted by pixel in LDS, and a lane
+// owning (pixel, 4-channel quad) sums A * w * grad_out over its pixel's
+// entries in registers and writes the pixel once -- the binned pipeline's
+// gather form with one bin per range, no float atomics (which run at a few
+// hundred G lane-ops/s on this chip, in LDS too).  The range's workgroup also
+// computes grad_attn_weight and grad_sampling_loc for every nsplit-th point,
+// as the dots kernel does.  For DAT's sampling step and other small problems
+// the binned pipeline's seven launches would cost more than the work.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *s_w,
+                                                         uint32_t &total) {
+    constexpr int kWaves = kThreads / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t inc = wave_inclusive_scan(v);
+    if (lane == 63) s_w[wave] = inc;
+    __syncthreads();
+    uint32_t base = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const uint32_t x = s_w[w];
+        base += w < wave ? x : 0u;
+        tot += x;
+    }
+    total = tot;
+    __syncthreads();  // s_w is free again
+    return base + inc - v;
+}
+
+template <int D, typename VT>
+__global__ void __launch_bounds__(kThreads)
+bwd_small_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes,
+                 const int64_t *__restrict__ starts, const float *__restrict__ loc,
+                 const float *__restrict__ attn, const float *__restrict__ grad_out,
+                 float *__restrict__ grad_value, float *__restrict__ grad_loc,
+                 float *__restrict__ grad_attn, Dims dm) {
+    constexpr int G = D / 4;
+    constexpr int NG = kThreads / G;      // lane groups
+    constexpr int CPT = kSmallPixels / kThreads;  // pixel counts per thread in the scan
+    __shared__ LevelLds s_lv;
+    __shared__ float2 s_scale[kMaxLevels];
+    __shared__ uint4 s_off[kSmallPoints];      // neighbour row offsets
+    __shared__ float4 s_aux[kSmallPoints];     // fx, fy, A, valid bits
+    __shared__ uint32_t s_cnt[kSmallPixels + 1];  // entries per pixel, then first entry
+    __shared__ uint32_t s_ent[4 * kSmallPoints];  // point << 2 | neighbour, by pixel
+    __shared__ uint32_t s_w[kThreads / 64];
+
+    const int M = dm.M, LK = dm.L * dm.K, Nq = dm.Nq, Nv = dm.Nv;
+    const int nsplit = dm.nblk;  // pixel ranges per (batch, head)
+    const int bm = (int)blockIdx.x / nsplit + dm.b0 * M, sp = (int)blockIdx.x % nsplit;
+    const int m = bm % M, b = bm / M;
+    const int px0 = sp * kSmallPixels, npx = min(kSmallPixels, Nv - px0);
+    const int npts = Nq * LK;
+    const uint32_t row_stride = (uint32_t)M * D * 4u;
+    const uint32_t head_off = (uint32_t)m * D * 4u;
+    stage_levels(&s_lv, shapes, starts, dm.L, Nv, 0x7fffffff);
+    if (threadIdx.x < dm.L) {
+        const int4 lvl = s_lv.lvl[threadIdx.x];
+        s_scale[threadIdx.x] =
+            make_float2(pixel_scale(lvl.y, dm.align), pixel_scale(lvl.x, dm.align));
+    }
+    for (int i = threadIdx.x; i <= kSmallPixels; i += kThreads) s_cnt[i] = 0u;
+    __syncthreads();
+
+    // 1. the point table, and slots for the neighbours inside the range
+    const size_t row0 = (size_t)b * Nq * M + m;  // item row of query 0
+    int pix[4] = {-1, -1, -1, -1};
+    uint32_t slot[4] = {0u, 0u, 0u, 0u};
+    if ((int)threadIdx.x < npts) {
+        const int qq = threadIdx.x / LK, j = threadIdx.x - qq * LK;
+        const size_t p = (row0 + (size_t)qq * M) * LK + j;
+        const float2 uv = reinterpret_cast<const float2 *>(loc)[p];
+        const float A = attn[p];
+        const int4 lvl = s_lv.lvl[j / dm.K];
+        const Neighbours n = neighbours(uv.x, uv.y, lvl, row_stride, head_off, dm.align);
+        s_off[threadIdx.x] = n.off;
+        s_aux[threadIdx.x] = make_float4(n.fx, n.fy, A, __uint_as_float(n.valid));
+        const int pTL = lvl.z + n.yi * lvl.y + n.xi;
+        const int nb[4] = {pTL, pTL + 1, pTL + lvl.y, pTL + lvl.y + 1};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int r = nb[k] - px0;
+            if ((n.valid & (1u << k)) && r >= 0 && r < npx) {
+                pix[k] = r;
+                slot[k] = atomicAdd(&s_cnt[r], 1u);
+            }
+        }
+    }
+    __syncthreads();
+    // 2. first entry of each pixel (exclusive scan of the counts)
+    {
+        uint32_t c[CPT], sum = 0;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            c[i] = s_cnt[threadIdx.x * CPT + i];
+            sum += c[i];
+        }
+        uint32_t total;
+        uint32_t e = block_exclusive_scan(sum, s_w, total);
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            s_cnt[threadIdx.x * CPT + i] = e;
+            e += c[i];
+        }
+        if (threadIdx.x == 0) s_cnt[kSmallPixels] = total;
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < npts) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (pix[k] >= 0) s_ent[s_cnt[pix[k]] + slot[k]] = (threadIdx.x << 2) | (uint32_t)k;
+    }
+    __syncthreads();
+
+    // 3. grad_attn_weight and grad_sampling_loc of every nsplit-th point
+    const size_t slice = (size_t)Nv * M * D;
+    const rsrc_t vr = make_rsrc(value + (size_t)b * slice, (uint32_t)(slice * sizeof(VT)));
+    // the grad_out rows of the head, read through a buffer (see the dots kernel)
+    const rsrc_t go =
+        make_rsrc(grad_out + row0 * D, (uint32_t)(((size_t)(Nq - 1) * M + 1) * D * 4));
+    auto g_row = [&](int qq, int c) {
+        auto u = __builtin_amdgcn_raw_buffer_load_b128(
+            go, (int)((uint32_t)qq * M * D * 4u + 16u * c), 0, 0);
+        return make_float4(__uint_as_float(u[0]), __uint_as_float(u[1]), __uint_as_float(u[2]),
+                           __uint_as_float(u[3]));
+    };
+    {
+        const int grp = threadIdx.x / G, c = threadIdx.x % G;
+        for (int pt = sp + grp * nsplit; pt < npts; pt += NG * nsplit) {
+            const int qq = pt / LK, j = pt - qq * LK;
+            const float4 g4 = g_row(qq, c);
+            const uint4 o = s_off[pt];
+            const float4 v0 = Row4<VT>::load(vr, o.x, 4 * c);
+            const float4 v1 = Row4<VT>::load(vr, o.y, 4 * c);
+            const float4 v2 = Row4<VT>::load(vr, o.z, 4 * c);
+            const float4 v3 = Row4<VT>::load(vr, o.w, 4 * c);
+            const float d0 = group_sum<G>(dot4(g4, v0));
+            const float d1 = group_sum<G>(dot4(g4, v1));
+            const float d2 = group_sum<G>(dot4(g4, v2));
+            const float d3 = group_sum<G>(dot4(g4, v3));
+            if (c == 0) {
+                const float4 ax = s_aux[pt];
+                const uint32_t valid = __float_as_uint(ax.w);
+                const float fx = ax.x, fy = ax.y, A = ax.z;
+                float ga = 0.f, gx = 0.f, gy = 0.f;
+                if (valid != 0u) {
+                    const float4 w = tent_weights(fx, fy, valid);
+                    ga = w.x * d0 + w.y * d1 + w.z * d2 + w.w * d3;
+                    const float2 sc = s_scale[j / dm.K];
+                    gx = A * sc.x * ((1.f - fy) * (d1 - d0) + fy * (d3 - d2));
+                    gy = A * sc.y * ((1.f - fx) * (d2 - d0) + fx * (d3 - d1));
+                }
+                const size_t p = (row0 + (size_t)qq * M) * LK + j;
+                grad_attn[p] = ga;
+                reinterpret_cast<float2 *>(grad_loc)[p] = make_float2(gx, gy);
+            }
+        }
+    }
+
+    // 4. grad_value of the range: lane = (pixel, quad), its entries summed
+    float *gvb = grad_value + (size_t)b * slice + (size_t)m * D;
+    for (int i = threadIdx.x; i < npx * G; i += kThreads) {
+        const int px = i / G, c = i - px * G;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        const uint32_t e1 = s_cnt[px + 1];
+        for (uint32_t e = s_cnt[px]; e < e1; ++e) {
+            const uint32_t ent = s_ent[e];
+            const int pt = (int)(ent >> 2), k = (int)(ent & 3u);
+            const float4 ax = s_aux[pt];
+            const float gx = 1.f - ax.x, gy = 1.f - ax.y;
+            const float wk = (k & 1 ? ax.x : gx) * (k & 2 ? ax.y : gy);
+            fma4(acc, ax.z * wk, g_row(pt / LK, c));
+        }
+        float4 *d4 = reinterpret_cast<float4 *>(gvb + (size_t)(px0 + px) * M * D) + c;
+        if (dm.accumulate) {
+            const float4 v = *d4;
+            acc.x += v.x;
+            acc.y += v.y;
+            acc.z += v.z;
+            acc.w += v.w;
+        }
+        *d4 = acc;
     }
 }
 
@@ -834,6 +1027,51 @@ msda_status dispatch_fwd(int64_t D, const void *value, const int64_t *shapes,
 #undef MSDA_FWD_CASE
 }
 
+template <int D, typename VT>
+msda_status launch_bwd_small(const void *value, const int64_t *shapes, const int64_t *starts,
+                             const float *loc, const float *attn, const float *gout, float *gval,
+                             float *gloc, float *gattn, int64_t B, int64_t Nv, int64_t Nq,
+                             int64_t M, int64_t L, int64_t K, bool acc, bool align,
+                             hipStream_t s) {
+    const int64_t nsplit = (Nv + kSmallPixels - 1) / kSmallPixels;
+    const int64_t bchunk = batch_chunk(M * nsplit, B);
+    for (int64_t b0 = 0; b0 < B; b0 += bchunk) {
+        const int64_t nb = (B - b0) < bchunk ? (B - b0) : bchunk;
+        Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, 0, 0, (int)b0, (int)nsplit, 0,
+                acc ? 1 : 0};
+        dm.align = align ? 1 : 0;
+        hipLaunchKernelGGL((bwd_small_kernel<D, VT>), dim3((unsigned)(nb * M * nsplit)),
+                           dim3(kThreads), 0, s, static_cast<const VT *>(value), shapes, starts,
+                           loc, attn, gout, gval, gloc, gattn, dm);
+        const msda_status st = hip_status(hipGetLastError());
+        if (st != MSDA_OK) return st;
+    }
+    return MSDA_OK;
+}
+
+template <typename VT>
+msda_status dispatch_small(int64_t D, const void *value, const int64_t *shapes,
+                           const int64_t *starts, const float *loc, const float *attn,
+                           const float *gout, float *gval, float *gloc, float *gattn, int64_t B,
+                           int64_t Nv, int64_t Nq, int64_t M, int64_t L, int64_t K, bool acc,
+                           bool align, hipStream_t s) {
+#define MSDA_SMALL_CASE(DD)                                                                   \
+    case DD:                                                                                  \
+        return launch_bwd_small<DD, VT>(value, shapes, starts, loc, attn, gout, gval, gloc,   \
+                                        gattn, B, Nv, Nq, M, L, K, acc, align, s);
+    switch (D) {
+        MSDA_SMALL_CASE(4)
+        MSDA_SMALL_CASE(8)
+        MSDA_SMALL_CASE(16)
+        MSDA_SMALL_CASE(32)
+        MSDA_SMALL_CASE(64)
+        MSDA_SMALL_CASE(128)
+        MSDA_SMALL_CASE(256)
+    default: return MSDA_ERR_UNSUPPORTED;
+    }
+#undef MSDA_SMALL_CASE
+}
+
 template <typename VT>
 msda_status dispatch_bwd(int64_t D, const void *value, const int64_t *shapes,
                          const int64_t *starts, const float *loc, const float *attn,
@@ -931,7 +1169,8 @@ msda_status backward_impl(const void *value, int value_dtype, const int64_t *spa
                           FusedBwd *fz, hipStream_t s, hipEvent_t *ev) {
     msda_status st = check_sizes(value_dtype, B, Nv, Nq, M, D, L, K);
     if (st != MSDA_OK) return st;
-    if (flags & ~(MSDA_BWD_ACCUMULATE | MSDA_ALIGN_CORNERS)) return MSDA_ERR_UNSUPPORTED;
+    if (flags & ~(MSDA_BWD_ACCUMULATE | MSDA_ALIGN_CORNERS | MSDA_BWD_BINNED))
+        return MSDA_ERR_UNSUPPORTED;
     // a grad_value record stores the query index in 25 bits
     if (Nq > ((int64_t)1 << (32 - kRecQueryShift))) return MSDA_ERR_UNSUPPORTED;
     const int64_t nval = B * Nv * M * D;
@@ -952,6 +1191,30 @@ msda_status backward_impl(const void *value, int value_dtype, const int64_t *spa
         if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return MSDA_ERR_WORKSPACE;
     }
     Exec ex{s, nullptr, nullptr, nullptr, nullptr, ev, false};
+    const bool acc = (flags & MSDA_BWD_ACCUMULATE) != 0;
+    const bool align = (flags & MSDA_ALIGN_CORNERS) != 0;
+    // heads of few points: the whole backward in one kernel, recorded as
+    // stage 1 (the other stages are empty)
+    if (work && !fz && !(flags & MSDA_BWD_BINNED) && Nq * L * K <= kSmallPoints) {
+        ex.stamp(0, false, s);
+        ex.stamp(0, true, s);
+        ex.stamp(1, false, s);
+        st = value_dtype == MSDA_F32
+                 ? dispatch_small<float>(D, value, spatial_shapes, level_start_index,
+                                         sampling_loc, attn_weight, grad_out, grad_value,
+                                         grad_sampling_loc, grad_attn_weight, B, Nv, Nq, M, L, K,
+                                         acc, align, s)
+                 : dispatch_small<uint16_t>(D, value, spatial_shapes, level_start_index,
+                                            sampling_loc, attn_weight, grad_out, grad_value,
+                                            grad_sampling_loc, grad_attn_weight, B, Nv, Nq, M, L,
+                                            K, acc, align, s);
+        ex.stamp(1, true, s);
+        for (int i = 2; i < MSDA_BWD_STAGES; ++i) {
+            ex.stamp(i, false, s);
+            ex.stamp(i, true, s);
+        }
+        return st;
+    }
     std::unique_lock<std::mutex> lock(msda_side::mutex(), std::defer_lock);
     if (work) {
         lock.lock();
@@ -992,8 +1255,6 @@ msda_status backward_impl(const void *value, int value_dtype, const int64_t *spa
         return MSDA_OK;
     }
     unsigned char *ws = static_cast<unsigned char *>(workspace);
-    const bool acc = (flags & MSDA_BWD_ACCUMULATE) != 0;
-    const bool align = (flags & MSDA_ALIGN_CORNERS) != 0;
     if (value_dtype == MSDA_F32)
         return dispatch_bwd<float>(D, value, spatial_shapes, level_start_index, sampling_loc,
                                    attn_weight, grad_out, grad_value, grad_sampling_loc,

@@ -101,6 +101,8 @@ def test_backward_rejects_before_launch():
                                                       z, 0, flags, z)
     assert bwd(2, 0, 1, 80, 16, 2, 8, 2, 2) == B_.MSDA_ERR_DTYPE
     assert bwd(0, 4, 1, 80, 16, 2, 8, 2, 2) == B_.MSDA_ERR_UNSUPPORTED  # unknown flag
+    assert bwd(0, 16, 1, 80, 16, 2, 8, 2, 2) == B_.MSDA_ERR_UNSUPPORTED
+    assert bwd(0, B_.MSDA_BWD_BINNED, 1, 80, 16, 2, 8, 2, 2) == B_.MSDA_ERR_NULL  # known
     assert bwd(0, 0, 1, 80, 16, 2, 8, 2, 2) == B_.MSDA_ERR_NULL
     assert bwd(0, 0, 1, 80, 16, 2, 24, 2, 2) == B_.MSDA_ERR_UNSUPPORTED
     assert bwd(0, 0, 0, 80, 16, 2, 8, 2, 2) == B_.MSDA_OK            # B = 0: nothing to fill

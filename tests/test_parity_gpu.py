@@ -261,6 +261,35 @@ def test_out_of_map_and_nonfinite(msda):
         close(x, r, BWD_TOL)
 
 
+# ---------------------------------------------------------------------------
+# small problems: the one-kernel backward and the binned pipeline
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("D,bf16,acc,align", [(4, False, False, False), (32, False, True, False),
+                                              (64, True, False, True), (256, False, False, False)])
+def test_small_backward_both_paths(msda, D, bf16, acc, align):
+    """Heads of at most 256 points take the one-kernel backward (workgroups of
+    256 pixels: several per head on the 33x40 level); binned=True forces the
+    pipeline.  Both against the oracle, with points outside the maps and a
+    ragged query count."""
+    shapes = ((33, 40), (5, 7), (3, 4)) if D <= 64 else ((4, 5), (2, 3))
+    w = workloads.random_case(800 + D, 3, shapes, 19, 3, D, 3, -0.2, 1.2, bf16=bf16)
+    _say(f"small backward D={D} bf16={bf16} accumulate={acc} align={align}")
+    x = dev_inputs(w, bf16)
+    g = torch.from_numpy(w.grad_out).cuda()
+    mode = oracle.SPEC | (oracle.ALIGN if align else 0)
+    rv, rl, ra = oracle_bwd(w, mode=mode)
+    base = torch.randn(tuple(x["value"].shape), generator=torch.Generator().manual_seed(D)).cuda()
+    for binned in (False, True):
+        gv = base.clone()
+        gv, gl, ga = msda.backward(**x, grad_out=g, grad_value=gv, accumulate=acc,
+                                   align_corners=align, binned=binned)
+        torch.cuda.synchronize()
+        dv = gv.cpu().numpy() - (base.cpu().numpy() if acc else 0.0)
+        close(dv, rv, BWD_TOL, f"grad_value binned={binned}")
+        close(gl.cpu().numpy(), rl, BWD_TOL, f"grad_sampling_loc binned={binned}")
+        close(ga.cpu().numpy(), ra, BWD_TOL, f"grad_attn_weight binned={binned}")
+
+
 def test_empty_inputs(msda):
     d = torch.device("cuda:0")
     _say("empty")
