@@ -264,8 +264,9 @@ def test_out_of_map_and_nonfinite(msda):
 # ---------------------------------------------------------------------------
 # small problems: the one-kernel backward and the binned pipeline
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("D,bf16,acc,align", [(4, False, False, False), (32, False, True, False),
-                                              (64, True, False, True), (256, False, False, False)])
+@pytest.mark.parametrize("D,bf16,acc,align", [(4, False, False, False), (16, False, False, True),
+                                              (32, False, True, False), (64, True, False, True),
+                                              (128, True, True, False), (256, False, False, False)])
 def test_small_backward_both_paths(msda, D, bf16, acc, align):
     """Heads of at most 256 points take the one-kernel backward (workgroups of
     256 pixels: several per head on the 33x40 level); binned=True forces the
