@@ -96,6 +96,7 @@ constexpr int kDotsBatch = 4;              // points whose row loads the dots ke
 constexpr int kSmallPoints = 256;
 constexpr int kSmallPixels = 256;
 static_assert(kSmallPoints <= kThreads, "one thread per point builds the point table");
+static_assert(kSmallPixels % kThreads == 0, "each thread scans kSmallPixels / kThreads counts");
 
 // Raw inputs of the fused prologue, which computes the sampling location and
 // the attention weight of each point from them:
