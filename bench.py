@@ -52,7 +52,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 # kernel names as rocprofv3 reports them, per stage of a step
 KERNELS = {
-    "forward": "msda_fwd_kernel<32, float, false>",
+    "forward": "msda_fwd_kernel<32, float, false, 1>",
     "fill_grad_value": "fill_zero_kernel",
     "clear_bins": "fill_zero_kernel",
     "count": "bin_count_kernel<false>",

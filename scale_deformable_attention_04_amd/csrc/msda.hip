@@ -182,13 +182,23 @@ __device__ __forceinline__ void stage_softmax_stats(float2 *s_st, const Prologue
 // (loc and attn are unused): per item the softmax statistics of its logits
 // are staged in LDS first, then each point's location and weight are formed
 // where the plain kernel loads them.
-template <int D, typename VT, bool FUSED>
+// SPLIT lane groups share an item, each taking every SPLIT-th point, and
+// their sums are added across lanes at the end: for problems too small to
+// fill the chip with one group per item (the decoder's 300 queries), it
+// gives 4x the workgroups and a quarter of the dependent row loads per lane.
+template <int D>
+constexpr int fwd_split() {
+    return D <= 64 ? 4 : (D == 128 ? 2 : 1);  // SPLIT * D / 4 lanes stay within a wave
+}
+
+template <int D, typename VT, bool FUSED, int SPLIT>
 __global__ void __launch_bounds__(kThreads)
 msda_fwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes,
                 const int64_t *__restrict__ starts, const float *__restrict__ loc,
                 const float *__restrict__ attn, Prologue pr, float *__restrict__ out, Dims dm) {
     constexpr int G = D / 4;
-    constexpr int IPB = kThreads / G;
+    constexpr int IPB = kThreads / (G * SPLIT);
+    static_assert(G * SPLIT <= 64, "an item's lanes lie in one wave");
     __shared__ LevelLds s_lv;
     extern __shared__ __align__(16) unsigned char smem[];
     uint4 *s_off = reinterpret_cast<uint4 *>(smem);
@@ -222,7 +232,7 @@ msda_fwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
         }
     }
 
-    const int it = threadIdx.x / G, c = threadIdx.x % G;
+    const int it = threadIdx.x / (G * SPLIT), sub = (threadIdx.x / G) % SPLIT, c = threadIdx.x % G;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 
     for (int j0 = 0; j0 < LK; j0 += dm.PC) {
@@ -268,7 +278,7 @@ msda_fwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
             const uint4 *po = s_off + it * dm.PS;
             const float4 *pw = s_w + it * dm.PS;
 #pragma unroll 4
-            for (int jj = 0; jj < pc; ++jj) {
+            for (int jj = sub; jj < pc; jj += SPLIT) {
                 const uint4 o = po[jj];
                 const float4 w = pw[jj];
                 const float4 v0 = Row4<VT>::load(vr, o.x, 4 * c);
@@ -282,7 +292,16 @@ msda_fwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
             }
         }
     }
-    if (it < nitems) {
+    if constexpr (SPLIT > 1) {  // the item's groups are lanes G apart in one wave
+#pragma unroll
+        for (int o = G; o < G * SPLIT; o <<= 1) {
+            acc.x += __shfl_xor(acc.x, o, 64);
+            acc.y += __shfl_xor(acc.y, o, 64);
+            acc.z += __shfl_xor(acc.z, o, 64);
+            acc.w += __shfl_xor(acc.w, o, 64);
+        }
+    }
+    if (it < nitems && sub == 0) {
         float4 *o = reinterpret_cast<float4 *>(out + (row0 + (size_t)it * M) * D) + c;
         *o = acc;
     }
@@ -817,9 +836,9 @@ struct Launch {
 
 // `reserve`: LDS bytes taken from the point-table budget for other uses.
 Launch plan(int64_t D, int64_t L, int64_t K, int bytes_per_point, int reserve = 0,
-            int budget = kSetupLdsBytes) {
+            int budget = kSetupLdsBytes, int split = 1) {
     Launch p;
-    p.ipb = (int)(kThreads / (D / 4));
+    p.ipb = (int)(kThreads / (D / 4 * split));
     const int lk = (int)(L * K);
     int pc = (budget - reserve) / (p.ipb * bytes_per_point) - 2;
     pc = pc < 1 ? 1 : pc;
@@ -829,10 +848,10 @@ Launch plan(int64_t D, int64_t L, int64_t K, int bytes_per_point, int reserve = 
     return p;
 }
 
-Launch fwd_plan(int64_t D, int64_t L, int64_t K, int reserve = 0) {
-    Launch p = plan(D, L, K, 32, reserve);
+Launch fwd_plan(int64_t D, int64_t L, int64_t K, int reserve = 0, int split = 1) {
+    Launch p = plan(D, L, K, 32, reserve, kSetupLdsBytes, split);
     if (L * K > 16) {
-        const Launch half = plan(D, L, K, 32, reserve, kFwdLdsBytes);
+        const Launch half = plan(D, L, K, 32, reserve, kFwdLdsBytes, split);
         if (half.pc >= 16) p = half;
     }
     return p;
@@ -849,17 +868,22 @@ msda_status launch_fwd(const void *value, const int64_t *shapes, const int64_t *
                        const float *loc, const float *attn, const Prologue *pr, float *out,
                        int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t L, int64_t K,
                        bool align, hipStream_t s) {
-    const int ipb = (int)(kThreads / (D / 4));
+    // one lane group per item, or fwd_split of them when one per item would
+    // leave fewer than two workgroups per CU
+    constexpr int kSplit = fwd_split<D>();
+    const int64_t ipb1 = kThreads / (D / 4);
+    const int split = (kSplit > 1 && B * M * ((Nq + ipb1 - 1) / ipb1) < 512) ? kSplit : 1;
+    const int ipb = (int)(ipb1 / split);
     Prologue prv = pr ? *pr : Prologue{nullptr, nullptr, nullptr, 0, 0, nullptr, nullptr};
     int st_bytes = 0;
-    Launch p = fwd_plan(D, L, K);
+    Launch p = fwd_plan(D, L, K, 0, split);
     if (pr) {
         // softmax by lane shuffles when the items' points come in one chunk and
         // the groups are power-of-two runs of at most 64; else statistics in LDS
         prv.shfl = (p.pc == L * K && pow2_run(pr->per_level ? K : L * K)) ? 1 : 0;
         if (!prv.shfl) {
             st_bytes = ipb * (pr->per_level ? (int)L : 1) * (int)sizeof(float2);
-            p = fwd_plan(D, L, K, st_bytes);
+            p = fwd_plan(D, L, K, st_bytes, split);
         }
     }
     const size_t lds = p.lds + (size_t)st_bytes;
@@ -870,14 +894,19 @@ msda_status launch_fwd(const void *value, const int64_t *shapes, const int64_t *
         Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, p.pc, p.ps, (int)b0, (int)gx, 0, 0};
         dm.align = align ? 1 : 0;
         const dim3 grid((unsigned)(gx * M * nb));
-        if (pr)
-            hipLaunchKernelGGL((msda_fwd_kernel<D, VT, true>), grid, dim3(kThreads), lds, s,
-                               static_cast<const VT *>(value), shapes, starts, loc, attn, prv,
-                               out, dm);
+        const VT *vp = static_cast<const VT *>(value);
+        if (pr && split > 1)
+            hipLaunchKernelGGL((msda_fwd_kernel<D, VT, true, kSplit>), grid, dim3(kThreads), lds,
+                               s, vp, shapes, starts, loc, attn, prv, out, dm);
+        else if (pr)
+            hipLaunchKernelGGL((msda_fwd_kernel<D, VT, true, 1>), grid, dim3(kThreads), lds, s,
+                               vp, shapes, starts, loc, attn, prv, out, dm);
+        else if (split > 1)
+            hipLaunchKernelGGL((msda_fwd_kernel<D, VT, false, kSplit>), grid, dim3(kThreads),
+                               lds, s, vp, shapes, starts, loc, attn, prv, out, dm);
         else
-            hipLaunchKernelGGL((msda_fwd_kernel<D, VT, false>), grid, dim3(kThreads), lds, s,
-                               static_cast<const VT *>(value), shapes, starts, loc, attn, prv,
-                               out, dm);
+            hipLaunchKernelGGL((msda_fwd_kernel<D, VT, false, 1>), grid, dim3(kThreads), lds, s,
+                               vp, shapes, starts, loc, attn, prv, out, dm);
         msda_status st = hip_status(hipGetLastError());
         if (st != MSDA_OK) return st;
     }
