@@ -556,6 +556,175 @@ dat_attn_dkdv_kernel(const float *__restrict__ q, const float *__restrict__ k,
 }
 
 // ---------------------------------------------------------------------------
+// backward in one kernel when a (b, h) has 49..64 keys (four 16-key blocks)
+// Workgroup = (b, h); wave w owns key block w for every query, so dK and dV
+// are complete in its registers at the end (no atomics, no second kernel).
+// Per tile of 16 queries the workgroup stages Q, dO, lse and delta (loaded
+// one tile ahead); each wave forms S, P, dP, dS for its block with keys as
+// columns (the dK/dV kernel's layout), adds dV^T += dO^T P and
+// dK^T += Q^T dS, and its part of dQ = dS K, for which dS goes through LDS
+// transposed (16 x 16 per wave); the four parts are summed in LDS.  Five
+// products per (tile, block) instead of the seven the dQ and dK/dV kernels
+// make together.
+// ---------------------------------------------------------------------------
+template <int DH>
+__global__ void __launch_bounds__(kAttnThreads)
+dat_attn_bwd_fused_kernel(const float *__restrict__ q, const float *__restrict__ k,
+                          const float *__restrict__ v, const float *__restrict__ bias,
+                          const float *__restrict__ out, const float *__restrict__ lse,
+                          const float *__restrict__ gout, float *__restrict__ gq,
+                          float *__restrict__ gk, float *__restrict__ gv,
+                          float *__restrict__ gbias, int N, int Ns, int heads, float scale) {
+    constexpr int RS = DH + 2;
+    constexpr int KS = DH / 4;
+    constexpr int TS = 17;  // row stride of the transposed dS tiles
+    __shared__ float s_k[64 * RS];      // the four key blocks' K rows
+    __shared__ float s_q[16 * RS];      // the tile's Q rows
+    __shared__ float s_do[16 * RS];     // the tile's dO rows
+    __shared__ float s_l[16], s_d[16];  // log2(e) * lse and delta of the tile's queries
+    __shared__ float s_dq[4][16 * RS];  // the waves' parts of the tile's dQ [query][dim]
+    __shared__ float s_t[4][16 * TS];   // the waves' dS [query][key]
+
+    const int bh = blockIdx.x, b = bh / heads, h = bh % heads;
+    const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 4, j = l & 15;
+    const float scale2 = scale * kLog2e;
+    const int key = wave * 16 + j;  // this lane's key (column)
+    const bool kok = key < Ns;
+    const bool live = wave * 16 < Ns;  // the wave's block holds a key (uniform)
+
+    stage_rows<DH, RS, 64>(s_k, k, b, h, Ns, heads, 0, Ns, 64);
+    float kr[KS], vr[KS];
+    const size_t krow = (((size_t)b * Ns + (kok ? key : 0)) * heads + h) * DH;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        kr[s] = kok ? k[krow + 4 * s + g] : 0.f;
+        vr[s] = kok ? v[krow + 4 * s + g] : 0.f;
+    }
+    v4f dk[DH / 16], dv[DH / 16];  // dK^T, dV^T [dim db*16 + 4g + r][key]
+#pragma unroll
+    for (int db = 0; db < DH / 16; ++db) {
+        dk[db] = v4f{0.f, 0.f, 0.f, 0.f};
+        dv[db] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // the tile's rows are loaded into registers one tile ahead and stored
+    // into LDS between the tiles: Q, dO, O (for delta = rowsum(dO * O)), lse
+    RowChunk<DH, 16> cq, cd, co;
+    float cl = 0.f;
+    auto load_tile = [&](int t0) {
+        const int nq = min(16, N - t0);
+        cq.load(q, b, h, N, heads, t0, nq);
+        cd.load(gout, b, h, N, heads, t0, nq);
+        co.load(out, b, h, N, heads, t0, nq);
+        if (threadIdx.x < 16)
+            cl = (int)threadIdx.x < nq ? lse[(size_t)bh * N + t0 + threadIdx.x] * kLog2e : 0.f;
+    };
+    auto store_tile = [&]() {
+        cq.template store<RS>(s_q);
+        cd.template store<RS>(s_do);
+        // delta: thread i holds quad i % (DH/4) of row i / (DH/4); the row's
+        // quads are DH/4 consecutive lanes
+        constexpr int C4 = DH / 4;
+#pragma unroll
+        for (int it = 0; it < RowChunk<DH, 16>::ITEMS; ++it) {
+            const float4 a = cd.val[it], o = co.val[it];
+            float dp = a.x * o.x + a.y * o.y + a.z * o.z + a.w * o.w;
+#pragma unroll
+            for (int m = C4 / 2; m >= 1; m >>= 1) dp += __shfl_xor(dp, m, C4);
+            const int i = threadIdx.x + it * kAttnThreads;
+            if (i % C4 == 0 && i / C4 < 16) s_d[i / C4] = dp;
+        }
+        if (threadIdx.x < 16) s_l[threadIdx.x] = cl;
+    };
+    load_tile(0);
+    store_tile();
+    __syncthreads();
+
+    for (int t0 = 0; t0 < N; t0 += 16) {
+        const int nq = min(16, N - t0);
+        const bool more = t0 + 16 < N;
+        if (more) load_tile(t0 + 16);  // in flight while this tile is computed
+        if (live) {
+            // 2. S and dP with keys as columns: lane (j, g) holds rows 4g + r
+            v4f sa = {0.f, 0.f, 0.f, 0.f}, pa = {0.f, 0.f, 0.f, 0.f};
+            const float *qa = s_q + j * RS + g;
+            const float *da = s_do + j * RS + g;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                sa = mfma16x4(qa[4 * s], kr[s], sa);
+                pa = mfma16x4(da[4 * s], vr[s], pa);
+            }
+            float p[4], ds[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tq = 4 * g + r;
+                const bool ok = kok && tq < nq;
+                float x = sa[r] * scale2;
+                if (bias)
+                    x = fmaf(bias[((size_t)bh * N + t0 + (tq < nq ? tq : nq - 1)) * Ns +
+                                  (kok ? key : Ns - 1)],
+                             kLog2e, x);
+                p[r] = ok ? __builtin_amdgcn_exp2f(x - s_l[tq]) : 0.f;
+                ds[r] = p[r] * (pa[r] - s_d[tq]);
+                if (gbias && ok) gbias[((size_t)bh * N + t0 + tq) * Ns + key] = ds[r];
+            }
+            // 3. dV^T += dO^T P, dK^T += Q^T dS over the tile's queries
+#pragma unroll
+            for (int db = 0; db < DH / 16; ++db) {
+                const float *dcol = s_do + (4 * g) * RS + db * 16 + j;
+                const float *qcol = s_q + (4 * g) * RS + db * 16 + j;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    dv[db] = mfma16x4(dcol[s * RS], p[s], dv[db]);
+                    dk[db] = mfma16x4(qcol[s * RS], ds[s], dk[db]);
+                }
+            }
+            // 4. dS transposed (query-major) for this wave's part of dQ; the
+            // wave reads back only what it wrote, in order
+            float *st = s_t[wave];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) st[(4 * g + r) * TS + j] = ds[r];
+            // dQ^T[dim][query] = sum over the block's keys of K^T dS^T
+            float *dq = s_dq[wave];
+#pragma unroll
+            for (int db = 0; db < DH / 16; ++db) {
+                v4f acc = {0.f, 0.f, 0.f, 0.f};
+                const float *kcol = s_k + (wave * 16 + 4 * g) * RS + db * 16 + j;
+                // k-step s, lane group g: key 4g + s in both operands
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    acc = mfma16x4(kcol[s * RS], st[j * TS + 4 * g + s], acc);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dq[j * RS + db * 16 + 4 * g + r] = acc[r];
+            }
+        }
+        __syncthreads();
+        // 5. dQ of the tile: the live waves' parts summed; then the next
+        // tile's rows into the buffers every wave has finished reading
+        for (int i = threadIdx.x; i < nq * DH; i += kAttnThreads) {
+            const int qt = i / DH, d = i - qt * DH;
+            float a = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                if (w * 16 < Ns) a += s_dq[w][qt * RS + d];
+            gq[(((size_t)b * N + t0 + qt) * heads + h) * DH + d] = a * scale;
+        }
+        if (more) store_tile();
+        __syncthreads();
+    }
+    if (!kok) return;
+    float *gkr = gk + krow, *gvr = gv + krow;
+#pragma unroll
+    for (int db = 0; db < DH / 16; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int dim = db * 16 + 4 * g + r;
+            gkr[dim] = dk[db][r] * scale;
+            gvr[dim] = dv[db][r];
+        }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 msda_status check_attn(int64_t B, int64_t N, int64_t Ns, int64_t heads, int64_t DH) {
@@ -681,6 +850,14 @@ msda_status attn_bwd(const float *q, const float *k, const float *v, const float
                      const float *out, const float *lse, const float *gout, float *gq, float *gk,
                      float *gv, float *gbias, float *delta, int64_t B, int64_t N, int64_t Ns,
                      int64_t heads, float scale, hipStream_t s) {
+    // 49..64 keys and enough (b, h) pairs to fill the chip with one workgroup
+    // each over at most 1024 queries: the one-kernel backward
+    if (Ns > 48 && Ns <= 64 && B * heads >= 256 && N <= 1024) {
+        hipLaunchKernelGGL((dat_attn_bwd_fused_kernel<DH>), dim3((unsigned)(B * heads)),
+                           dim3(kAttnThreads), 0, s, q, k, v, bias, out, lse, gout, gq, gk, gv,
+                           gbias, (int)N, (int)Ns, (int)heads, scale);
+        return hip_status(hipGetLastError());
+    }
     const AttnTiling t = attn_tiling<DH>(B, N, Ns, heads);
     const int n = (int)N, ns = (int)Ns, hh = (int)heads;
     msda_status st;

@@ -114,6 +114,16 @@ def test_dat_attention_query_tiles(msda):
     check_attention(msda, w)
 
 
+@pytest.mark.parametrize("C,heads,khw,hw", [(64, 4, (7, 7), (7, 9)), (128, 4, (8, 8), (5, 13)),
+                                             (256, 4, (7, 8), (4, 4))])
+def test_dat_attention_one_kernel_backward(msda, C, heads, khw, hw):
+    # 49..64 keys and >= 256 (batch, head) pairs: the one-kernel backward
+    # (head widths 16, 32, 64; ragged query tiles; bias and its gradient)
+    _say(f"dat attention one-kernel backward C={C} heads={heads} Ns={khw} N={hw}")
+    w = workloads.dat_case(3901 + C, 64, hw[0], hw[1], C, heads, 1, khw[0], khw[1])
+    check_attention(msda, w)
+
+
 def test_dat_attention_empty(msda):
     _say("dat attention N=0")
     k = torch.randn(2, 5, 2, 32, device="cuda")
