@@ -291,6 +291,45 @@ def test_small_backward_both_paths(msda, D, bf16, acc, align):
         close(ga.cpu().numpy(), ra, BWD_TOL, f"grad_attn_weight binned={binned}")
 
 
+# ---------------------------------------------------------------------------
+# a seeded sweep of random small problems through every backward path
+# ---------------------------------------------------------------------------
+def _sweep_case(i):
+    """Shape i of the sweep: 1-4 levels of 1..40 x 1..40, Nq 1..150, M 1..6,
+    any supported D, K 1..6, fp32 or bf16 value, either pixel convention."""
+    rng = np.random.Generator(np.random.PCG64(9000 + i))
+    L = int(rng.integers(1, 5))
+    shapes = tuple((int(rng.integers(1, 41)), int(rng.integers(1, 41))) for _ in range(L))
+    D = int(rng.choice([4, 8, 16, 32, 64, 128, 256]))
+    B, Nq, M, K = (int(rng.integers(1, 4)), int(rng.integers(1, 151)), int(rng.integers(1, 7)),
+                   int(rng.integers(1, 7)))
+    bf16, align = bool(rng.integers(2)), bool(rng.integers(2))
+    return shapes, B, Nq, M, D, K, bf16, align
+
+
+@pytest.mark.parametrize("i", range(48))
+def test_random_sweep(msda, i):
+    """Forward and both backward paths (the one-kernel path where the heads
+    have <= 256 points, the binned pipeline always) against the oracle."""
+    shapes, B, Nq, M, D, K, bf16, align = _sweep_case(i)
+    _say(f"sweep {i}: shapes={shapes} B={B} Nq={Nq} M={M} D={D} K={K} bf16={bf16} "
+         f"align={align}")
+    w = workloads.random_case(9100 + i, B, shapes, Nq, M, D, K, -0.15, 1.15, bf16=bf16)
+    x = dev_inputs(w, bf16)
+    mode = oracle.SPEC | (oracle.ALIGN if align else 0)
+    out = msda.forward(**x, align_corners=align)
+    g = torch.from_numpy(w.grad_out).cuda()
+    torch.cuda.synchronize()
+    close(out.cpu().numpy(), oracle_fwd(w, mode=mode).reshape(out.shape), FWD_TOL, "forward")
+    rv, rl, ra = oracle_bwd(w, mode=mode)
+    for binned in (False, True):
+        gv, gl, ga = msda.backward(**x, grad_out=g, align_corners=align, binned=binned)
+        torch.cuda.synchronize()
+        close(gv.cpu().numpy(), rv, BWD_TOL, f"grad_value binned={binned}")
+        close(gl.cpu().numpy(), rl, BWD_TOL, f"grad_sampling_loc binned={binned}")
+        close(ga.cpu().numpy(), ra, BWD_TOL, f"grad_attn_weight binned={binned}")
+
+
 def test_empty_inputs(msda):
     d = torch.device("cuda:0")
     _say("empty")
