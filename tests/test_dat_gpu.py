@@ -124,6 +124,25 @@ def test_dat_attention_one_kernel_backward(msda, C, heads, khw, hw):
     check_attention(msda, w)
 
 
+@pytest.mark.parametrize("i", range(24))
+def test_dat_attention_sweep(msda, i):
+    # seeded random shapes across the kernels' builds: 1..256 keys, head
+    # widths 16/32/64 (keys <= 240 at 64), 1..600 queries, 1..48 (b, head)
+    # pairs, with or without the bias
+    rng = np.random.Generator(np.random.PCG64(9500 + i))
+    d = int(rng.choice([16, 32, 64]))
+    hk, wk = int(rng.integers(1, 17)), int(rng.integers(1, 17))
+    while hk * wk > (240 if d == 64 else 256):
+        hk -= 1
+    H, W = int(rng.integers(1, 25)), int(rng.integers(1, 26))
+    heads, B = int(rng.integers(1, 5)), int(rng.integers(1, 13))
+    with_bias = bool(rng.integers(2))
+    _say(f"dat attention sweep {i}: B={B} N={H * W} Ns={hk * wk} heads={heads} d={d} "
+         f"bias={with_bias}")
+    w = workloads.dat_case(9600 + i, B, H, W, heads * d, heads, 1, hk, wk, with_bias=with_bias)
+    check_attention(msda, w)
+
+
 def test_dat_attention_empty(msda):
     _say("dat attention N=0")
     k = torch.randn(2, 5, 2, 32, device="cuda")
