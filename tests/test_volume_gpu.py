@@ -112,6 +112,25 @@ def test_volume_out_of_volume_and_nonfinite(msda):
     check(msda, w)
 
 
+@pytest.mark.parametrize("i", range(16))
+def test_volume_sweep(msda, i):
+    # seeded random volumes: 1-3 levels of up to 6 x 12 x 12, every head
+    # width, 1..6 points, fp32 or bf16 value, either convention
+    rng = np.random.Generator(np.random.PCG64(9800 + i))
+    L = int(rng.integers(1, 4))
+    shapes = tuple((int(rng.integers(1, 7)), int(rng.integers(1, 13)), int(rng.integers(1, 13)))
+                   for _ in range(L))
+    D = int(rng.choice([4, 8, 16, 32, 64, 128, 256]))
+    B, Nq, M, K = (int(rng.integers(1, 3)), int(rng.integers(1, 60)), int(rng.integers(1, 5)),
+                   int(rng.integers(1, 7)))
+    bf16, align = bool(rng.integers(2)), bool(rng.integers(2))
+    _say(f"volume sweep {i}: shapes={shapes} B={B} Nq={Nq} M={M} D={D} K={K} bf16={bf16} "
+         f"align={align}")
+    w = workloads.volume_case(9900 + i, B, shapes, Nq, M, D, K, bf16=bf16,
+                              loc_low=-0.15, loc_high=1.15)
+    check(msda, w, bf16=bf16, align=align)
+
+
 def test_volume_empty(msda):
     _say("volume empty")
     w = workloads.volume_case(2501, 2, SHAPES, 0, 2, 8, 3)
