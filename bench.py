@@ -19,7 +19,7 @@ stream in every step (an event record costs the stream a few microseconds);
 its algorithmic bytes (each tensor it must touch read or written once) over
 its average duration there give "achieved", against the 8 TB/s HBM peak.
 "traffic" is the HBM byte count rocprofv3 measured for that kernel
-(profiles/traffic.json), when it was taken on the current kernel source.
+(profiles/traffic.json), when it was taken on the current 2-D kernel sources.
 "cpu_baseline" times the CPU oracle on the same workload on this host's
 cores.  --extra adds the decoder and bf16 training shapes and the fused
 prologue (reference points + pixel offsets + logits) at the encoder shape,
@@ -377,7 +377,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--reps", type=int, default=30, help="launches per kernel timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--extra", action="store_true", help="also measure the decoder and bf16 configs")
+    ap.add_argument("--extra", action="store_true",
+                    help="also measure the decoder, bf16 training, fused prologue, 3-D and DAT")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
