@@ -877,6 +877,233 @@ grad_value_tile_kernel(const int64_t *__restrict__ shapes, const int64_t *__rest
 
 
 // ---------------------------------------------------------------------------
+// backward: grad_value by gathering, one 8x8 tile (and chunk of its records)
+// per work item, for heads of up to kGatherMaxD channels
+//
+// The item's records are counting-sorted by cell once, into LDS.  A lane
+// owns one (cell, 4-channel quad) pair and walks the records of its cell,
+// loading that quad of each record's grad_out row straight from global
+// memory: the cell's D/4 lanes read the row together, so every record's row
+// is fetched once, and up to kGatherBatch rows per lane are in flight.  For
+// cell (x, y) -- top-left neighbour at tile pixel (x-1, y-1) -- the lane keeps
+// one sum per neighbour role:
+//   top-left     (weight A (1-fx)(1-fy)) for pixel (x-1, y-1),
+//   top-right    (A fx (1-fy))           for pixel (x,   y-1),
+//   bottom-left  (A (1-fx) fy)           for pixel (x-1, y),
+//   bottom-right (A fx fy)               for pixel (x,   y),
+// and drops the roles whose pixel lies outside the tile.  Every pixel of the
+// tile receives exactly one sum of each role, so the sums are exchanged
+// through LDS without conflicts and each pixel is written once.
+// ---------------------------------------------------------------------------
+constexpr int kGatherMaxD = 32;
+constexpr int kGatherThreads = kCells * (kGatherMaxD / 4);  // 648: 81 cells x 8 quads
+constexpr int kGatherBatch = 4;
+constexpr int kGatherPer = (kChunk + kGatherThreads - 1) / kGatherThreads;  // records per thread
+
+template <int D, bool VOL>
+__global__ void __launch_bounds__(kGatherThreads)
+grad_value_gather_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ starts,
+                         const float *__restrict__ grad_out, const uint4 *__restrict__ items,
+                         const uint32_t *__restrict__ work_total, const uint4 *__restrict__ recs,
+                         float *__restrict__ grad_value, Dims dm) {
+    static_assert(D <= kGatherMaxD && D % 4 == 0, "one (cell, quad) pair per lane");
+    constexpr int kQuads = D / 4;
+    constexpr int kPairs = kCells * kQuads;
+    static_assert(4 * kTilePx * kQuads <= kChunk, "the role sums fit the record table");
+    __shared__ LevelLds s_lv;
+    __shared__ uint32_t s_cnt[kCells];     // records per cell
+    __shared__ uint32_t s_st[kCells + 1];  // first sorted slot of each cell, and the total
+    __shared__ uint4 s_tab[kChunk];        // the item's records in cell order
+    // after the gather, the role sums: [role][pixel][quad]
+    float4 *s_red = reinterpret_cast<float4 *>(s_tab);
+
+    const int M = dm.M, Nq = dm.Nq;
+    const int tid = threadIdx.x;
+    const uint32_t total = *work_total;
+    if (blockIdx.x >= total) return;  // the grid is sized for the largest possible list
+    stage_bin_levels<VOL>(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
+    if (tid < kCells) s_cnt[tid] = 0u;
+
+    const bool owner = tid < kPairs;
+    const int cell = tid / kQuads, quad = tid - cell * kQuads;
+    const int cx = cell % kCellsW, cy = cell / kCellsW;
+    const uint32_t row_stride = (uint32_t)M * D * 4u;
+    // one batch of grad_out; the host keeps it below 2^32 bytes, and an
+    // offset of `slice` reads zeros (outside the descriptor's range)
+    const uint32_t slice = (uint32_t)((size_t)Nq * M * D * 4);
+    __syncthreads();
+
+    // Workgroup g takes items g, g + grid, ... counted from the end of the
+    // list (the coarse levels' bins, the largest, first).  The list is in
+    // (batch, level, tile, head) order, so with 8 heads the workgroups of
+    // one XCD (g % 8) mostly see one head, whose grad_out rows stay in that L2.
+    for (uint32_t w = blockIdx.x; w < total; w += gridDim.x) {
+        const uint4 it = items[total - 1u - w];  // (bin, first record, records, whole bin)
+        const int n = (int)min(it.z, (uint32_t)kChunk);
+        // 1. the records, and each one's rank within its cell
+        uint4 rec[kGatherPer];
+        uint32_t rank[kGatherPer];
+#pragma unroll
+        for (int r = 0; r < kGatherPer; ++r) {
+            const int i = tid + r * kGatherThreads;
+            rec[r] = i < n ? recs[it.y + i] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < kGatherPer; ++r) {
+            const int i = tid + r * kGatherThreads;
+            rank[r] = i < n ? atomicAdd(&s_cnt[rec[r].x & ((1u << kRecQueryShift) - 1u)], 1u) : 0u;
+        }
+        __syncthreads();
+        // 2. exclusive scan of the 81 counts by one wave, 2 cells a lane
+        if (tid < 64) {
+            const int c0 = 2 * tid, c1 = 2 * tid + 1;
+            const uint32_t v0 = c0 < kCells ? s_cnt[c0] : 0u;
+            const uint32_t v1 = c1 < kCells ? s_cnt[c1] : 0u;
+            const uint32_t incl = wave_inclusive_scan(v0 + v1);
+            const uint32_t ex = incl - v0 - v1;
+            if (c0 < kCells) s_st[c0] = ex;
+            if (c1 < kCells) s_st[c1] = ex + v0;
+            if (tid == 63) s_st[kCells] = incl;
+        }
+        __syncthreads();
+        // 3. the records in cell order (ranks are below their cell's count,
+        // so every slot is below n); the counts are free for the next item
+        if (tid < kCells) s_cnt[tid] = 0u;
+#pragma unroll
+        for (int r = 0; r < kGatherPer; ++r) {
+            const int i = tid + r * kGatherThreads;
+            if (i < n) {
+                const uint32_t c = rec[r].x & ((1u << kRecQueryShift) - 1u);
+                s_tab[min(s_st[c] + rank[r], (uint32_t)kChunk - 1u)] = rec[r];
+            }
+        }
+        __syncthreads();
+
+        // 4. the lane's cell: four role sums of A * w * grad_out
+        const uint32_t bin = it.x;  // (b * nb_max + tile) * M + m
+        const int m = (int)(bin % (uint32_t)M);
+        const uint32_t bt = bin / (uint32_t)M;
+        const int b = (int)(bt / (uint32_t)dm.nb_max);
+        float4 acc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (owner) {
+            const rsrc_t go = make_rsrc(grad_out + (size_t)b * Nq * M * D, slice);
+            const uint32_t lane_off = (uint32_t)m * D * 4u + 16u * (uint32_t)quad;
+            const int e0 = (int)s_st[cell], e1 = (int)s_st[cell + 1];
+            for (int e = e0; e < e1; e += kGatherBatch) {
+                uint4 t[kGatherBatch];
+                float4 g[kGatherBatch];
+#pragma unroll
+                for (int u = 0; u < kGatherBatch; ++u) t[u] = s_tab[min(e + u, e1 - 1)];
+#pragma unroll
+                for (int u = 0; u < kGatherBatch; ++u) {
+                    const uint32_t q = min(t[u].x >> kRecQueryShift, (uint32_t)Nq - 1u);
+                    const uint32_t off = e + u < e1 ? q * row_stride + lane_off : slice;
+                    auto v = __builtin_amdgcn_raw_buffer_load_b128(go, (int)off, 0, 0);
+                    g[u] = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]),
+                                       __uint_as_float(v[2]), __uint_as_float(v[3]));
+                }
+#pragma unroll
+                for (int u = 0; u < kGatherBatch; ++u) {
+                    const float a0 = __uint_as_float(t[u].y), a1 = __uint_as_float(t[u].z);
+                    const float fy = __uint_as_float(t[u].w), gy = 1.f - fy;
+                    fma4(acc[0], a0 * gy, g[u]);
+                    fma4(acc[1], a1 * gy, g[u]);
+                    fma4(acc[2], a0 * fy, g[u]);
+                    fma4(acc[3], a1 * fy, g[u]);
+                }
+            }
+        }
+        __syncthreads();  // the record table is free: it takes the role sums
+        if (owner) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int px = cx - 1 + (r & 1), py = cy - 1 + (r >> 1);
+                if (px >= 0 && px < kTile && py >= 0 && py < kTile)
+                    s_red[(r * kTilePx + py * kTile + px) * kQuads + quad] = acc[r];
+            }
+        }
+        __syncthreads();
+        // 5. write the tile: pixel = the four roles' sums
+        if (tid < kTilePx * kQuads) {
+            const int px = tid / kQuads, q = tid - px * kQuads;
+            float4 a = s_red[px * kQuads + q];
+#pragma unroll
+            for (int r = 1; r < 4; ++r) {
+                const float4 v = s_red[(r * kTilePx + px) * kQuads + q];
+                a.x += v.x;
+                a.y += v.y;
+                a.z += v.z;
+                a.w += v.w;
+            }
+            const int lb = (int)(bt - (uint32_t)b * dm.nb_max);
+            int l = 0;
+            while (l + 1 < dm.L && s_lv.lvl[l + 1].w <= lb) ++l;
+            const int4 lvl = s_lv.lvl[l];
+            const int tw = s_lv.tw[l];
+            int rel = lb - lvl.w;
+            int plane0 = lvl.z;  // first row of the tile's map (volumes: of its plane)
+            if constexpr (VOL) {
+                const int zpl = rel / s_lv.tpp[l];
+                rel -= zpl * s_lv.tpp[l];
+                plane0 += zpl * lvl.x * lvl.y;
+            }
+            const int ty = rel / tw, tx = rel - ty * tw;
+            const int gx = tx * kTile + (px & (kTile - 1));
+            const int gy = ty * kTile + (px >> kTileShift);
+            if (gy < lvl.x && gx < lvl.y) {
+                const size_t slice_v = (size_t)dm.Nv * M * D;
+                float *dst = grad_value + (size_t)b * slice_v + (size_t)m * D +
+                             (size_t)(plane0 + gy * lvl.y + gx) * M * D + 4 * q;
+                if (it.w) {
+                    // this work item alone owns the pixel: plain read-add-write
+                    float4 *d4 = reinterpret_cast<float4 *>(dst);
+                    if (dm.accumulate) {
+                        const float4 v = *d4;
+                        a.x += v.x;
+                        a.y += v.y;
+                        a.z += v.z;
+                        a.w += v.w;
+                    }
+                    *d4 = a;
+                } else {
+                    atomicAdd(dst + 0, a.x);
+                    atomicAdd(dst + 1, a.y);
+                    atomicAdd(dst + 2, a.z);
+                    atomicAdd(dst + 3, a.w);
+                }
+            }
+        }
+        // the next item's first barrier orders these reads of s_red before
+        // its records overwrite the table
+    }
+}
+
+// The grad_value stage: the gather kernel for heads of up to kGatherMaxD
+// channels whose grad_out batch is 32-bit addressable, else the tile kernel.
+template <int D, bool VOL>
+hipError_t launch_grad_value(int64_t work_max, int64_t Nq, int64_t M, const int64_t *shapes,
+                             const int64_t *starts, const float *gout, const uint4 *items,
+                             const uint32_t *work_total, const uint4 *recs, float *gval,
+                             const Dims &dm, hipStream_t s) {
+    const int64_t grid = work_max < kTileGrid ? work_max : kTileGrid;
+    if constexpr (D <= kGatherMaxD) {
+        if (Nq * M * D * 4 < ((int64_t)1 << 32) - 64) {
+            hipLaunchKernelGGL((grad_value_gather_kernel<D, VOL>), dim3((unsigned)grid),
+                               dim3(kGatherThreads), 0, s, shapes, starts, gout, items,
+                               work_total, recs, gval, dm);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((grad_value_tile_kernel<D, VOL>), dim3((unsigned)grid),
+                       dim3(kTileThreads), 0, s, shapes, starts, gout, items, work_total, recs,
+                       gval, dm);
+    return hipGetLastError();
+}
+
+
+// ---------------------------------------------------------------------------
 // host side of the pipeline
 // ---------------------------------------------------------------------------
 // Upper bound of the number of 8x8 tiles over all levels, from Nv and L only:

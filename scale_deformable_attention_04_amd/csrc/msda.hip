@@ -30,11 +30,17 @@
 //   bin_scatter_kernel: one 16-byte record per (point, bin) it touches,
 //      written into its bin (LDS ranks, one global reservation per bin and
 //      workgroup).
-//   grad_value_tile_kernel: per work item, the records are counting-sorted
-//      by the cell of their top-left neighbour and their grad_out rows are
-//      staged in LDS in that order; a lane owns (pixel, channel quad) pairs
-//      and sums over the four cells that feed its pixel, in registers.  Only
-//      bins split over several chunks add into grad_value atomically.
+//   grad_value_gather_kernel (heads of up to 32 channels): per work item,
+//      the records are counting-sorted once by the cell of their top-left
+//      neighbour; a lane owns a (cell, channel quad) pair, gathers the
+//      grad_out row of each of its cell's records from memory and keeps one
+//      sum per neighbour role; the role sums meet in LDS, each pixel
+//      written once.
+//   grad_value_tile_kernel (wider heads): the records are sorted per
+//      sub-chunk and their grad_out rows staged in LDS in that order; a lane
+//      owns (pixel, channel quad) pairs and sums over the four cells that
+//      feed its pixel.  In both, only bins split over several chunks add
+//      into grad_value atomically.
 //
 // value and grad_value are addressed through raw buffer descriptors whose
 // size is the batch slice.  A neighbour outside the map gets the offset
@@ -1020,16 +1026,13 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
     if (st != MSDA_OK) return st;
     ex.stamp(5, true, s);
 
-    const int64_t grid = wl.work_max < kTileGrid ? wl.work_max : kTileGrid;
     if (ex.fill_on_side) {
         st = hip_status(hipStreamWaitEvent(s, ex.filled, 0));
         if (st != MSDA_OK) return st;
     }
     ex.stamp(6, false, s);
-    hipLaunchKernelGGL((grad_value_tile_kernel<D, false>), dim3((unsigned)grid),
-                       dim3(kTileThreads), 0, s, shapes, starts, gout, w.items, w.work_total,
-                       w.recs, gval, dm);
-    st = hip_status(hipGetLastError());
+    st = hip_status(launch_grad_value<D, false>(wl.work_max, Nq, M, shapes, starts, gout, w.items,
+                                                 w.work_total, w.recs, gval, dm, s));
     ex.stamp(6, true, s);
     if (st == MSDA_OK && ex.side) st = hip_status(hipStreamWaitEvent(s, ex.join, 0));
     return st;

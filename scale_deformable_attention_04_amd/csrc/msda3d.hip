@@ -464,10 +464,8 @@ msda_status launch3_bwd(const void *value, const int64_t *shapes, const int64_t 
         st = hip_status(hipStreamWaitEvent(s, ex.filled, 0));
         if (st != MSDA_OK) return st;
     }
-    const int64_t grid = wl.work_max < kTileGrid ? wl.work_max : kTileGrid;
-    hipLaunchKernelGGL((grad_value_tile_kernel<D, true>), dim3((unsigned)grid), dim3(kTileThreads),
-                       0, s, shapes, starts, gout, w.items, w.work_total, w.recs, gval, dm);
-    st = hip_status(hipGetLastError());
+    st = hip_status(launch_grad_value<D, true>(wl.work_max, Nq, M, shapes, starts, gout, w.items,
+                                                w.work_total, w.recs, gval, dm, s));
     if (st == MSDA_OK && ex.side) st = hip_status(hipStreamWaitEvent(s, ex.join, 0));
     return st;
 }
