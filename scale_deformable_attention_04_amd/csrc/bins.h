@@ -896,19 +896,25 @@ grad_value_tile_kernel(const int64_t *__restrict__ shapes, const int64_t *__rest
 // through LDS without conflicts and each pixel is written once.
 // ---------------------------------------------------------------------------
 constexpr int kGatherMaxD = 32;
-constexpr int kGatherThreads = kCells * (kGatherMaxD / 4);  // 648: 81 cells x 8 quads
-constexpr int kGatherBatch = 4;
-constexpr int kGatherPer = (kChunk + kGatherThreads - 1) / kGatherThreads;  // records per thread
+constexpr int kGatherCPL = 16;  // channels per lane (four quads): 81 cells x 2 lanes at D = 32
+constexpr int kGatherBatch = 2;  // records whose rows a lane loads together
 
-template <int D, bool VOL>
-__global__ void __launch_bounds__(kGatherThreads)
+template <int CPL> constexpr int gather_threads() { return kCells * (kGatherMaxD / CPL); }
+
+template <int D, bool VOL, int CPL>
+__global__ void __launch_bounds__(gather_threads<CPL>())
 grad_value_gather_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ starts,
                          const float *__restrict__ grad_out, const uint4 *__restrict__ items,
                          const uint32_t *__restrict__ work_total, const uint4 *__restrict__ recs,
                          float *__restrict__ grad_value, Dims dm) {
-    static_assert(D <= kGatherMaxD && D % 4 == 0, "one (cell, quad) pair per lane");
+    static_assert(D <= kGatherMaxD && D % 4 == 0, "one (cell, channel group) pair per lane");
+    constexpr int kT = gather_threads<CPL>();
     constexpr int kQuads = D / 4;
-    constexpr int kPairs = kCells * kQuads;
+    constexpr int kQPL = (CPL < D ? CPL : D) / 4;  // quads per lane
+    constexpr int kGroups = kQuads / kQPL;          // lanes per cell
+    constexpr int kPairs = kCells * kGroups;
+    constexpr int kPer = (kChunk + kT - 1) / kT;     // records per thread in the sort
+    static_assert(kPairs <= kT, "every (cell, channel group) pair has a lane");
     static_assert(4 * kTilePx * kQuads <= kChunk, "the role sums fit the record table");
     __shared__ LevelLds s_lv;
     __shared__ uint32_t s_cnt[kCells];     // records per cell
@@ -925,7 +931,7 @@ grad_value_gather_kernel(const int64_t *__restrict__ shapes, const int64_t *__re
     if (tid < kCells) s_cnt[tid] = 0u;
 
     const bool owner = tid < kPairs;
-    const int cell = tid / kQuads, quad = tid - cell * kQuads;
+    const int cell = tid / kGroups, grp = tid - cell * kGroups;
     const int cx = cell % kCellsW, cy = cell / kCellsW;
     const uint32_t row_stride = (uint32_t)M * D * 4u;
     // one batch of grad_out; the host keeps it below 2^32 bytes, and an
@@ -941,16 +947,16 @@ grad_value_gather_kernel(const int64_t *__restrict__ shapes, const int64_t *__re
         const uint4 it = items[total - 1u - w];  // (bin, first record, records, whole bin)
         const int n = (int)min(it.z, (uint32_t)kChunk);
         // 1. the records, and each one's rank within its cell
-        uint4 rec[kGatherPer];
-        uint32_t rank[kGatherPer];
+        uint4 rec[kPer];
+        uint32_t rank[kPer];
 #pragma unroll
-        for (int r = 0; r < kGatherPer; ++r) {
-            const int i = tid + r * kGatherThreads;
+        for (int r = 0; r < kPer; ++r) {
+            const int i = tid + r * kT;
             rec[r] = i < n ? recs[it.y + i] : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
-        for (int r = 0; r < kGatherPer; ++r) {
-            const int i = tid + r * kGatherThreads;
+        for (int r = 0; r < kPer; ++r) {
+            const int i = tid + r * kT;
             rank[r] = i < n ? atomicAdd(&s_cnt[rec[r].x & ((1u << kRecQueryShift) - 1u)], 1u) : 0u;
         }
         __syncthreads();
@@ -970,8 +976,8 @@ grad_value_gather_kernel(const int64_t *__restrict__ shapes, const int64_t *__re
         // so every slot is below n); the counts are free for the next item
         if (tid < kCells) s_cnt[tid] = 0u;
 #pragma unroll
-        for (int r = 0; r < kGatherPer; ++r) {
-            const int i = tid + r * kGatherThreads;
+        for (int r = 0; r < kPer; ++r) {
+            const int i = tid + r * kT;
             if (i < n) {
                 const uint32_t c = rec[r].x & ((1u << kRecQueryShift) - 1u);
                 s_tab[min(s_st[c] + rank[r], (uint32_t)kChunk - 1u)] = rec[r];
@@ -984,34 +990,43 @@ grad_value_gather_kernel(const int64_t *__restrict__ shapes, const int64_t *__re
         const int m = (int)(bin % (uint32_t)M);
         const uint32_t bt = bin / (uint32_t)M;
         const int b = (int)(bt / (uint32_t)dm.nb_max);
-        float4 acc[4];
+        float4 acc[4][kQPL];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int k = 0; k < kQPL; ++k) acc[r][k] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (owner) {
             const rsrc_t go = make_rsrc(grad_out + (size_t)b * Nq * M * D, slice);
-            const uint32_t lane_off = (uint32_t)m * D * 4u + 16u * (uint32_t)quad;
+            const uint32_t lane_off = (uint32_t)m * D * 4u + 16u * (uint32_t)(grp * kQPL);
             const int e0 = (int)s_st[cell], e1 = (int)s_st[cell + 1];
             for (int e = e0; e < e1; e += kGatherBatch) {
                 uint4 t[kGatherBatch];
-                float4 g[kGatherBatch];
+                float4 g[kGatherBatch][kQPL];
 #pragma unroll
                 for (int u = 0; u < kGatherBatch; ++u) t[u] = s_tab[min(e + u, e1 - 1)];
 #pragma unroll
                 for (int u = 0; u < kGatherBatch; ++u) {
                     const uint32_t q = min(t[u].x >> kRecQueryShift, (uint32_t)Nq - 1u);
                     const uint32_t off = e + u < e1 ? q * row_stride + lane_off : slice;
-                    auto v = __builtin_amdgcn_raw_buffer_load_b128(go, (int)off, 0, 0);
-                    g[u] = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]),
-                                       __uint_as_float(v[2]), __uint_as_float(v[3]));
+#pragma unroll
+                    for (int k = 0; k < kQPL; ++k) {
+                        auto v = __builtin_amdgcn_raw_buffer_load_b128(go, (int)(off + 16u * k), 0, 0);
+                        g[u][k] = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]),
+                                              __uint_as_float(v[2]), __uint_as_float(v[3]));
+                    }
                 }
 #pragma unroll
                 for (int u = 0; u < kGatherBatch; ++u) {
                     const float a0 = __uint_as_float(t[u].y), a1 = __uint_as_float(t[u].z);
                     const float fy = __uint_as_float(t[u].w), gy = 1.f - fy;
-                    fma4(acc[0], a0 * gy, g[u]);
-                    fma4(acc[1], a1 * gy, g[u]);
-                    fma4(acc[2], a0 * fy, g[u]);
-                    fma4(acc[3], a1 * fy, g[u]);
+                    const float w0 = a0 * gy, w1 = a1 * gy, w2 = a0 * fy, w3 = a1 * fy;
+#pragma unroll
+                    for (int k = 0; k < kQPL; ++k) {
+                        fma4(acc[0][k], w0, g[u][k]);
+                        fma4(acc[1][k], w1, g[u][k]);
+                        fma4(acc[2][k], w2, g[u][k]);
+                        fma4(acc[3][k], w3, g[u][k]);
+                    }
                 }
             }
         }
@@ -1020,14 +1035,33 @@ grad_value_gather_kernel(const int64_t *__restrict__ shapes, const int64_t *__re
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int px = cx - 1 + (r & 1), py = cy - 1 + (r >> 1);
-                if (px >= 0 && px < kTile && py >= 0 && py < kTile)
-                    s_red[(r * kTilePx + py * kTile + px) * kQuads + quad] = acc[r];
+                if (px >= 0 && px < kTile && py >= 0 && py < kTile) {
+#pragma unroll
+                    for (int k = 0; k < kQPL; ++k)
+                        s_red[(r * kTilePx + py * kTile + px) * kQuads + grp * kQPL + k] =
+                            acc[r][k];
+                }
             }
         }
         __syncthreads();
         // 5. write the tile: pixel = the four roles' sums
-        if (tid < kTilePx * kQuads) {
-            const int px = tid / kQuads, q = tid - px * kQuads;
+        const int lb = (int)(bt - (uint32_t)b * dm.nb_max);
+        int l = 0;
+        while (l + 1 < dm.L && s_lv.lvl[l + 1].w <= lb) ++l;
+        const int4 lvl = s_lv.lvl[l];
+        const int tw = s_lv.tw[l];
+        int rel = lb - lvl.w;
+        int plane0 = lvl.z;  // first row of the tile's map (volumes: of its plane)
+        if constexpr (VOL) {
+            const int zpl = rel / s_lv.tpp[l];
+            rel -= zpl * s_lv.tpp[l];
+            plane0 += zpl * lvl.x * lvl.y;
+        }
+        const int ty = rel / tw, tx = rel - ty * tw;
+        const size_t slice_v = (size_t)dm.Nv * M * D;
+        float *gv = grad_value + (size_t)b * slice_v + (size_t)m * D;
+        for (int i = tid; i < kTilePx * kQuads; i += kT) {
+            const int px = i / kQuads, q = i - px * kQuads;
             float4 a = s_red[px * kQuads + q];
 #pragma unroll
             for (int r = 1; r < 4; ++r) {
@@ -1037,42 +1071,26 @@ grad_value_gather_kernel(const int64_t *__restrict__ shapes, const int64_t *__re
                 a.z += v.z;
                 a.w += v.w;
             }
-            const int lb = (int)(bt - (uint32_t)b * dm.nb_max);
-            int l = 0;
-            while (l + 1 < dm.L && s_lv.lvl[l + 1].w <= lb) ++l;
-            const int4 lvl = s_lv.lvl[l];
-            const int tw = s_lv.tw[l];
-            int rel = lb - lvl.w;
-            int plane0 = lvl.z;  // first row of the tile's map (volumes: of its plane)
-            if constexpr (VOL) {
-                const int zpl = rel / s_lv.tpp[l];
-                rel -= zpl * s_lv.tpp[l];
-                plane0 += zpl * lvl.x * lvl.y;
-            }
-            const int ty = rel / tw, tx = rel - ty * tw;
             const int gx = tx * kTile + (px & (kTile - 1));
             const int gy = ty * kTile + (px >> kTileShift);
-            if (gy < lvl.x && gx < lvl.y) {
-                const size_t slice_v = (size_t)dm.Nv * M * D;
-                float *dst = grad_value + (size_t)b * slice_v + (size_t)m * D +
-                             (size_t)(plane0 + gy * lvl.y + gx) * M * D + 4 * q;
-                if (it.w) {
-                    // this work item alone owns the pixel: plain read-add-write
-                    float4 *d4 = reinterpret_cast<float4 *>(dst);
-                    if (dm.accumulate) {
-                        const float4 v = *d4;
-                        a.x += v.x;
-                        a.y += v.y;
-                        a.z += v.z;
-                        a.w += v.w;
-                    }
-                    *d4 = a;
-                } else {
-                    atomicAdd(dst + 0, a.x);
-                    atomicAdd(dst + 1, a.y);
-                    atomicAdd(dst + 2, a.z);
-                    atomicAdd(dst + 3, a.w);
+            if (gy >= lvl.x || gx >= lvl.y) continue;
+            float *dst = gv + (size_t)(plane0 + gy * lvl.y + gx) * M * D + 4 * q;
+            if (it.w) {
+                // this work item alone owns the pixel: plain read-add-write
+                float4 *d4 = reinterpret_cast<float4 *>(dst);
+                if (dm.accumulate) {
+                    const float4 v = *d4;
+                    a.x += v.x;
+                    a.y += v.y;
+                    a.z += v.z;
+                    a.w += v.w;
                 }
+                *d4 = a;
+            } else {
+                atomicAdd(dst + 0, a.x);
+                atomicAdd(dst + 1, a.y);
+                atomicAdd(dst + 2, a.z);
+                atomicAdd(dst + 3, a.w);
             }
         }
         // the next item's first barrier orders these reads of s_red before
@@ -1090,9 +1108,9 @@ hipError_t launch_grad_value(int64_t work_max, int64_t Nq, int64_t M, const int6
     const int64_t grid = work_max < kTileGrid ? work_max : kTileGrid;
     if constexpr (D <= kGatherMaxD) {
         if (Nq * M * D * 4 < ((int64_t)1 << 32) - 64) {
-            hipLaunchKernelGGL((grad_value_gather_kernel<D, VOL>), dim3((unsigned)grid),
-                               dim3(kGatherThreads), 0, s, shapes, starts, gout, items,
-                               work_total, recs, gval, dm);
+            hipLaunchKernelGGL((grad_value_gather_kernel<D, VOL, kGatherCPL>),
+                               dim3((unsigned)grid), dim3(gather_threads<kGatherCPL>()), 0, s,
+                               shapes, starts, gout, items, work_total, recs, gval, dm);
             return hipGetLastError();
         }
     }
