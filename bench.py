@@ -59,7 +59,7 @@ KERNELS = {
     "dots": "bwd_dots_kernel<32, float>",
     "scan": "bin_scan_kernel<false>",
     "scatter": "bin_scatter_kernel<false>",
-    "tiles": "grad_value_tile_kernel<32, false>",
+    "tiles": "grad_value_gather_kernel<32, false, 16>",
 }
 
 
