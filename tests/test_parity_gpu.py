@@ -364,6 +364,28 @@ def test_accumulate_adds_into_grad_value(msda):
     close(gv.cpu().numpy() - base.cpu().numpy(), rv, BWD_TOL)
 
 
+@pytest.mark.parametrize("D", [8, 32])
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("acc", [False, True])
+def test_split_bins(msda, D, bf16, acc):
+    # a 5x6 level is one 8x8 tile: 1500 queries x 4 points per head put ~6000
+    # records in its bin, which the work list splits into three items whose
+    # partial tiles are added atomically (onto earlier contents with acc)
+    w = workloads.random_case(1900 + D, 2, ((5, 6), (12, 10)), 1500, 2, D, 4, bf16=bf16)
+    x = dev_inputs(w, bf16)
+    g = torch.from_numpy(w.grad_out).cuda()
+    base = torch.randn(w.value.shape, device="cuda") if acc else None
+    _say(f"split bins D={D} bf16={bf16} acc={acc}")
+    gv, gl, ga = msda.backward(**x, grad_out=g, grad_value=base.clone() if acc else None,
+                               accumulate=acc)
+    torch.cuda.synchronize()
+    rv, rl, ra = oracle_bwd(w)
+    got_v = gv.cpu().numpy() - (base.cpu().numpy() if acc else 0.0)
+    close(got_v, rv, BWD_TOL, "grad_value")
+    close(gl.cpu().numpy(), rl, BWD_TOL, "grad_sampling_loc")
+    close(ga.cpu().numpy(), ra, BWD_TOL, "grad_attn_weight")
+
+
 def test_runs_on_the_callers_stream(msda):
     w = workloads.random_case(700, 2, ((9, 9), (4, 4)), 90, 4, 32, 4)
     x = dev_inputs(w)
