@@ -1010,7 +1010,8 @@ grad_value_gather_kernel(const int64_t *__restrict__ shapes, const int64_t *__re
                     const uint32_t off = e + u < e1 ? q * row_stride + lane_off : slice;
 #pragma unroll
                     for (int k = 0; k < kQPL; ++k) {
-                        auto v = __builtin_amdgcn_raw_buffer_load_b128(go, (int)(off + 16u * k), 0, 0);
+                        auto v = __builtin_amdgcn_raw_buffer_load_b128(
+                            go, (int)(off + 16u * k), 0, 0);
                         g[u][k] = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]),
                                               __uint_as_float(v[2]), __uint_as_float(v[3]));
                     }
