@@ -881,10 +881,11 @@ grad_value_tile_kernel(const int64_t *__restrict__ shapes, const int64_t *__rest
 // per work item, for heads of up to kGatherMaxD channels
 //
 // The item's records are counting-sorted by cell once, into LDS.  A lane
-// owns one (cell, 4-channel quad) pair and walks the records of its cell,
-// loading that quad of each record's grad_out row straight from global
-// memory: the cell's D/4 lanes read the row together, so every record's row
-// is fetched once, and up to kGatherBatch rows per lane are in flight.  For
+// owns one (cell, group of kGatherCPL channels) pair and walks the records
+// of its cell, loading its channels of each record's grad_out row straight
+// from global memory: the cell's lanes (two at D = 32) read the row together,
+// so every record's row is fetched once, and kGatherBatch records per lane
+// are in flight.  For
 // cell (x, y) -- top-left neighbour at tile pixel (x-1, y-1) -- the lane keeps
 // one sum per neighbour role:
 //   top-left     (weight A (1-fx)(1-fy)) for pixel (x-1, y-1),
