@@ -42,7 +42,7 @@ Modes:
       The same from the three runs of `run-dat`: profiles/dat_kernels.txt and
       profiles/dat_traffic.json.
 
-The GPU commands (run from /tmp with TMPDIR=/tmp, outputs under gpurun_out):
+The GPU commands (run from /tmp with TMPDIR=/tmp; OUT is any output directory):
   rocprofv3 --kernel-trace --stats --output-format csv -d OUT/stats -o run -- python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline
   rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/fetch -o run -- python3 profile_kernels.py run
   rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/write -o run -- python3 profile_kernels.py run
