@@ -2,8 +2,8 @@
 """Throughput of the MSDeformAttn sampling core on one MI355X.
 
 A step is one pass of the whole hot path over one batch: the forward
-(msda_forward) and the backward (msda_backward: grad_value fill, gradient
-pipeline) at the Deformable-DETR encoder shape -- B=2, four levels 100x167,
+(msda_forward) and the backward (msda_backward: grad_attn/grad_loc kernel
+beside the grad_value pipeline) at the Deformable-DETR encoder shape -- B=2, four levels 100x167,
 50x84, 25x42, 13x21 (Nv = 22,223), every pixel a query (Nq = Nv), M=8 heads,
 D=32, K=4, fp32.  Inputs are seeded synthetic data (workloads.make) resident
 in HBM before the timed region.
@@ -53,7 +53,6 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # kernel names as rocprofv3 reports them, per stage of a step
 KERNELS = {
     "forward": "msda_fwd_kernel<32, float, false, 1>",
-    "fill_grad_value": "fill_zero_kernel",
     "clear_bins": "fill_zero_kernel",
     "count": "bin_count_kernel<false>",
     "dots": "bwd_dots_kernel<32, float>",
@@ -82,8 +81,7 @@ def byte_model(B, Nv, Nq, M, D, L, K, value_bytes=4):
     return {
         "points": pts,
         "forward": value + loc + attn + rows,
-        "backward": value + loc + attn + rows + gvalue + loc + attn + gvalue,  # + fill
-        "fill_grad_value": gvalue,
+        "backward": value + loc + attn + rows + gvalue + loc + attn,
         "count": loc,
         "dots": value + loc + attn + rows + loc + attn,    # grad_loc, grad_attn written
         "scatter": loc + attn,

@@ -43,18 +43,24 @@
  * Memory and ownership.  Every tensor pointer, spatial_shapes and
  * level_start_index included, is a DEVICE pointer on the current HIP device;
  * the caller allocates and owns all of them, and the backward's scratch
- * workspace too.  The library allocates no memory; its only state is the
- * backward's side stream per device (see below).  Outputs must not alias
- * inputs.
+ * workspace too.  The library allocates no memory and keeps no state between
+ * calls.  Outputs must not alias inputs.  Calls on different streams may run
+ * concurrently when each has its own outputs and workspace.
  *
  * Streams and errors.  `stream` is a hipStream_t (NULL = the null stream).
  * Work is enqueued on it and the call returns without synchronizing; a
  * kernel fault therefore surfaces at the caller's next synchronization.
- * msda_backward also uses one side stream per device, created on its first
- * call on that device and kept until the process ends: it is forked from
- * `stream` and joined back into it with events inside the call, so work
+ * The backward entry points can also use a second, caller-owned stream
+ * (side_stream, with two caller-created hipEvent_t in side_events[0..1]):
+ * the grad_attn_weight / grad_sampling_loc kernel then runs there,
+ * concurrently with the grad_value kernels on `stream`.  The call forks
+ * side_stream from `stream` (side_events[0]) and joins it back into `stream`
+ * (side_events[1]) before returning -- on its error paths too -- so work
  * enqueued on `stream` afterwards sees every output complete (this also
- * holds under stream capture).
+ * holds under stream capture).  side_stream NULL (or equal to `stream`):
+ * everything runs on `stream`, side_events is ignored.  A side stream and its
+ * events must not be used by two calls in flight at once (one set per caller
+ * stream).  Priorities other than the default are not needed.
  * Every function returns an msda_status; nothing is thrown across the ABI.
  * The launch-time checks cover null pointers, negative sizes, 1 <= L <= 16,
  * the supported head widths and dtypes, and the 32-bit addressing limit.
@@ -67,7 +73,7 @@
  * Limits.  D in {4, 8, 16, 32, 64, 128, 256}; 1 <= L <= 16; K >= 1;
  * Nv*M*D*4 < 2^31 bytes (one batch slice of grad_value); Nq*M*L*K*2 < 2^31;
  * B*Nq*M*L*K*4 < 2^32.  msda_backward also needs Nq <= 2^25.
- * B, Nq may be 0 (nothing is launched, except the grad_value fill).
+ * B, Nq may be 0 (nothing is launched, except the zero fill of grad_value).
  */
 #ifndef MSDA_H
 #define MSDA_H
@@ -116,7 +122,7 @@ msda_status msda_forward(const void *value, int value_dtype,
  * nothing is launched or the sizes are invalid).  It depends on the sizes
  * only, not on the level table: 64 bytes per sampling point (room for one
  * 16-byte record per 8x8 value tile the point's neighbours touch, at most
- * four) plus about 16 bytes per tile bound and head.
+ * four) plus about 32 bytes per tile bound and head.
  */
 size_t msda_backward_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
                                     int64_t L, int64_t K);
@@ -140,16 +146,20 @@ size_t msda_backward_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int64_t M
  * separate workspaces.
  *
  * flags: MSDA_BWD_ACCUMULATE and/or MSDA_ALIGN_CORNERS (the latter as given to
- * the forward), MSDA_BWD_BINNED.  grad_value is overwritten (zero-filled
- * first) unless flags has MSDA_BWD_ACCUMULATE, in which case the gradient is
- * added to it.  Its summation order is not fixed, so repeated calls may differ
- * in the last bits.  grad_sampling_loc and grad_attn_weight are overwritten and
- * deterministic.
+ * the forward), MSDA_BWD_BINNED.  grad_value is overwritten unless flags has
+ * MSDA_BWD_ACCUMULATE, in which case the gradient is added to it.  Its
+ * summation order is not fixed, so repeated calls may differ in the last
+ * bits.  grad_sampling_loc and grad_attn_weight are overwritten and
+ * deterministic.  With a level table msda_validate_host rejects, the
+ * gradients are unspecified (memory outside the tensors is still never
+ * touched).
+ *
+ * stream, side_stream, side_events: see "Streams and errors" above.
  *
  * Heads of at most 256 points (Nq * L * K <= 256 per (batch, head)) run as
- * one kernel, a workgroup per (batch, head, 256 pixels); all others, and
- * every call with MSDA_BWD_BINNED, run the binned pipeline.  Both compute the
- * same gradients; the workspace is required either way.
+ * one kernel on `stream`, a workgroup per (batch, head, 256 pixels); all
+ * others, and every call with MSDA_BWD_BINNED, run the binned pipeline.  Both
+ * compute the same gradients; the workspace is required either way.
  */
 msda_status msda_backward(const void *value, int value_dtype,
                           const int64_t *spatial_shapes, const int64_t *level_start_index,
@@ -158,22 +168,23 @@ msda_status msda_backward(const void *value, int value_dtype,
                           float *grad_sampling_loc, float *grad_attn_weight,
                           int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
                           int64_t L, int64_t K, void *workspace, size_t workspace_bytes,
-                          uint32_t flags, void *stream);
+                          uint32_t flags, void *stream, void *side_stream,
+                          void *const *side_events);
 
 /*
  * Measurement entry point: msda_backward with the same arguments and the same
  * work on the same streams, which in addition records caller-owned HIP events
  * around each of its MSDA_BWD_STAGES stages: events[2i] just before the
  * stage's kernel and events[2i + 1] just after it, on the stream that runs it
- * (stages 0 and 1 run on the library's side stream when it has one, the
- * others on `stream`).  Nothing is synchronized; once the caller has waited
- * for `stream`, hipEventElapsedTime(events[2i], events[2i + 1]) is the
- * duration of stage i.  Stages:
- *   0 grad_value zero-fill (empty with MSDA_BWD_ACCUMULATE)
- *   1 grad_attn_weight / grad_sampling_loc   2 workspace clear
- *   3 points per value tile   4 count scan   5 record scatter into tiles
- *   6 grad_value tiles
- * A small problem (see msda_backward) runs as one kernel, recorded as stage 1;
+ * (stage 0 runs on side_stream when one is given, the others on `stream`).
+ * Nothing is synchronized; once the caller has waited for `stream`,
+ * hipEventElapsedTime(events[2i], events[2i + 1]) is the duration of stage i.
+ * Stages:
+ *   0 grad_attn_weight / grad_sampling_loc   1 workspace clear
+ *   2 points per value tile   3 count scan (work list; in overwrite mode the
+ *   list of tiles to zero)   4 zeroing of the listed tiles, then the record
+ *   scatter into tiles   5 grad_value tiles
+ * A small problem (see msda_backward) runs as one kernel, recorded as stage 0;
  * its other stages are empty.
  * events: 2 * MSDA_BWD_STAGES hipEvent_t created by the caller (with timing);
  * a null entry is skipped (an event record costs the stream a few
@@ -181,7 +192,7 @@ msda_status msda_backward(const void *value, int value_dtype,
  * events itself must not be NULL (MSDA_ERR_NULL).  The library keeps no
  * reference to them.
  */
-#define MSDA_BWD_STAGES 7
+#define MSDA_BWD_STAGES 6
 msda_status msda_backward_events(const void *value, int value_dtype,
                                  const int64_t *spatial_shapes, const int64_t *level_start_index,
                                  const float *sampling_loc, const float *attn_weight,
@@ -189,7 +200,8 @@ msda_status msda_backward_events(const void *value, int value_dtype,
                                  float *grad_sampling_loc, float *grad_attn_weight,
                                  int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
                                  int64_t L, int64_t K, void *workspace, size_t workspace_bytes,
-                                 uint32_t flags, void *stream, void *const *events);
+                                 uint32_t flags, void *stream, void *side_stream,
+                                 void *const *side_events, void *const *events);
 
 /*
  * Fused prologue.  The module around the core ("Deformable attention:
@@ -261,10 +273,10 @@ size_t msda_backward_fused_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int
  * aligned, as for msda_backward.
  * events: NULL, or 2 * MSDA_BWD_FUSED_STAGES caller-owned HIP events recorded
  * around the stages as msda_backward_events does (null entries skipped):
- * stages 0-6 as there, 7 the prologue (locations and weights into the
- * workspace; empty when they are passed in), 8 the epilogue (what remains of
+ * stages 0-5 as there, 6 the prologue (locations and weights into the
+ * workspace; empty when they are passed in), 7 the epilogue (what remains of
  * the logit and reference-point gradients; empty when nothing remains).
- * The same side stream as msda_backward is used.
+ * stream, side_stream, side_events as for msda_backward.
  */
 #define MSDA_BWD_FUSED_STAGES (MSDA_BWD_STAGES + 2)
 msda_status msda_backward_fused(const void *value, int value_dtype,
@@ -276,7 +288,8 @@ msda_status msda_backward_fused(const void *value, int value_dtype,
                                 float *grad_attn_logits, float *grad_reference_points,
                                 int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
                                 int64_t L, int64_t K, void *workspace, size_t workspace_bytes,
-                                uint32_t flags, void *stream, void *const *events);
+                                uint32_t flags, void *stream, void *side_stream,
+                                void *const *side_events, void *const *events);
 
 /*
  * 3-D (trilinear) variant.  "Deformable attention: multi-scale sparse
@@ -305,16 +318,16 @@ msda_status msda_backward_fused(const void *value, int value_dtype,
  * msda3d_forward: out is overwritten; flags 0 or MSDA_ALIGN_CORNERS.
  * msda3d_backward: the exact derivatives, as for the 2-D core with the
  * eight neighbours (grad_loc.z carries the factor Z_l, or Z_l - 1 with
- * MSDA_ALIGN_CORNERS).  grad_value is zero-filled first unless flags has
+ * MSDA_ALIGN_CORNERS).  grad_value is overwritten unless flags has
  * MSDA_BWD_ACCUMULATE; it is summed per 8x8 tile of each plane as in the 2-D
  * backward (atomic adds only where a tile is split), so its last bits may
  * differ between calls; grad_sampling_loc and grad_attn_weight are
  * overwritten and deterministic.  workspace: at least
  * msda3d_backward_workspace_size(...) bytes (128 bytes per point -- up to
- * eight 16-byte records, two planes of four tiles -- plus about 12 bytes
+ * eight 16-byte records, two planes of four tiles -- plus about 16 bytes
  * per voxel and head), 256-byte aligned, caller-owned, contents irrelevant.
- * The backward uses the library's side stream as msda_backward does; also
- * needs Nq <= 2^25.
+ * stream, side_stream, side_events as for msda_backward; also needs
+ * Nq <= 2^25.
  */
 size_t msda3d_backward_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
                                       int64_t L, int64_t K);
@@ -332,7 +345,8 @@ msda_status msda3d_backward(const void *value, int value_dtype,
                             float *grad_sampling_loc, float *grad_attn_weight,
                             int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
                             int64_t L, int64_t K, void *workspace, size_t workspace_bytes,
-                            uint32_t flags, void *stream);
+                            uint32_t flags, void *stream, void *side_stream,
+                            void *const *side_events);
 
 /* msda_validate_host for the 3-D variant: a HOST copy of volume_shapes [L, 3]. */
 msda_status msda3d_validate_host(const int64_t *volume_shapes_host,

@@ -37,7 +37,7 @@ EXPORTED = ("msda_forward", "msda_backward_workspace_size", "msda_backward",
             "msda_dat_attention_forward", "msda_dat_attention_workspace_size",
             "msda_dat_attention_backward",
             "msda_validate_host", "msda_status_string", "msda_last_hip_error")
-BWD_STAGES = ("fill_grad_value", "dots", "clear_bins", "count", "scan", "scatter", "tiles")
+BWD_STAGES = ("dots", "clear_bins", "count", "scan", "scatter", "tiles")
 BWD_FUSED_STAGES = BWD_STAGES + ("prologue", "epilogue")
 
 _lib = None
@@ -65,10 +65,10 @@ def load():
     lib.msda_forward.argtypes = [p, ci, p, p, p, p, p] + [i64] * 7 + [u32, p]
     lib.msda_forward.restype = ci
     lib.msda_backward.argtypes = ([p, ci, p, p, p, p, p, p, p, p] + [i64] * 7 +
-                                  [p, ctypes.c_size_t, u32, p])
+                                  [p, ctypes.c_size_t, u32, p, p, p])
     lib.msda_backward.restype = ci
     lib.msda_backward_events.argtypes = ([p, ci, p, p, p, p, p, p, p, p] + [i64] * 7 +
-                                         [p, ctypes.c_size_t, u32, p, p])
+                                         [p, ctypes.c_size_t, u32, p, p, p, p])
     lib.msda_backward_events.restype = ci
     lib.msda_backward_workspace_size.argtypes = [i64] * 7
     lib.msda_backward_workspace_size.restype = ctypes.c_size_t
@@ -77,12 +77,12 @@ def load():
     lib.msda_backward_fused_workspace_size.argtypes = [i64] * 7
     lib.msda_backward_fused_workspace_size.restype = ctypes.c_size_t
     lib.msda_backward_fused.argtypes = ([p, ci, p, p, p, p, p, p, p, p, p, p, p, p] + [i64] * 7 +
-                                        [p, ctypes.c_size_t, u32, p, p])
+                                        [p, ctypes.c_size_t, u32, p, p, p, p])
     lib.msda_backward_fused.restype = ci
     lib.msda3d_forward.argtypes = [p, ci, p, p, p, p, p] + [i64] * 7 + [u32, p]
     lib.msda3d_forward.restype = ci
     lib.msda3d_backward.argtypes = ([p, ci, p, p, p, p, p, p, p, p] + [i64] * 7 +
-                                    [p, ctypes.c_size_t, u32, p])
+                                    [p, ctypes.c_size_t, u32, p, p, p])
     lib.msda3d_backward_workspace_size.argtypes = [i64] * 7
     lib.msda3d_backward_workspace_size.restype = ctypes.c_size_t
     lib.msda3d_backward.restype = ci
@@ -156,6 +156,7 @@ def validate_host(spatial_shapes, level_start_index, B, Nv, Nq, M, D, L, K) -> i
 
 
 _workspaces = {}
+_sides = {}
 
 
 def workspace_size(B, Nv, Nq, M, D, L, K) -> int:
@@ -164,15 +165,43 @@ def workspace_size(B, Nv, Nq, M, D, L, K) -> int:
 
 
 def _workspace(dev: torch.device, nbytes: int) -> Optional[torch.Tensor]:
-    """A cached device buffer of at least nbytes (256-byte aligned, torch-owned)."""
+    """A device buffer of at least nbytes (256-byte aligned, torch-owned),
+    cached per (device, current stream): calls on one stream run in order and
+    share it, calls on different streams get different buffers."""
     if nbytes == 0:
         return None
-    key = (dev.type, dev.index)
+    key = (dev.type, dev.index, torch.cuda.current_stream(dev).cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         _workspaces[key] = ws
     return ws
+
+
+def _side_args(dev: torch.device, side_stream):
+    """(side hipStream_t, hipEvent_t[2]) for a backward on torch's current stream.
+
+    side_stream="auto": a second stream this module keeps for the current
+    stream (created on first use, default priority), so that backwards issued
+    on different streams each have their own; None: everything runs on the
+    current stream; a torch.cuda.Stream: that stream.  The fork/join events
+    are kept per (current stream, side stream) pair."""
+    if side_stream is None:
+        return ctypes.c_void_p(0), None
+    cur = torch.cuda.current_stream(dev)
+    auto = isinstance(side_stream, str)
+    if auto and side_stream != "auto":
+        raise ValueError("side_stream must be 'auto', None or a torch.cuda.Stream")
+    key = (dev.index, cur.cuda_stream, None if auto else side_stream.cuda_stream)
+    ent = _sides.get(key)
+    if ent is None:
+        side = torch.cuda.Stream(device=dev) if auto else side_stream
+        evs = [torch.cuda.Event(), torch.cuda.Event()]
+        for e in evs:
+            e.record(side)  # torch creates the HIP event at its first record
+        ent = (side, evs, (ctypes.c_void_p * 2)(*[e.cuda_event for e in evs]))
+        _sides[key] = ent
+    return ctypes.c_void_p(ent[0].cuda_stream), ent[2]
 
 
 def _check_inputs(value, spatial_shapes, level_start_index, sampling_loc, attn_weight, validate):
@@ -256,7 +285,7 @@ def backward(value: torch.Tensor, spatial_shapes: torch.Tensor, level_start_inde
              grad_attn_weight: Optional[torch.Tensor] = None,
              accumulate: bool = False, validate: bool = True,
              workspace: Optional[torch.Tensor] = None, events: Optional[list] = None,
-             align_corners: bool = False, binned: bool = False
+             align_corners: bool = False, binned: bool = False, side_stream="auto"
              ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """msda_backward: (grad_value fp32 [B,Nv,M,D], grad_sampling_loc, grad_attn_weight).
 
@@ -265,11 +294,12 @@ def backward(value: torch.Tensor, spatial_shapes: torch.Tensor, level_start_inde
     binned=True runs the binned grad_value pipeline even where the library
     would take its one-kernel path for small problems.
     workspace: a uint8 device tensor of at least workspace_size(...) bytes; by
-    default a per-device buffer cached by this module is used (calls on
-    different streams that overlap in time must pass their own).
+    default a buffer this module caches per (device, current stream).
     events: 2 * len(BWD_STAGES) torch.cuda.Event(enable_timing=True) objects
     or None; if given, msda_backward_events is called instead, which records
-    events 2i and 2i + 1 around stage i (see stage_times), skipping None."""
+    events 2i and 2i + 1 around stage i (see stage_times), skipping None.
+    side_stream: where the grad_attn_weight / grad_sampling_loc kernel runs
+    (see _side_args): "auto" (default), None, or a torch.cuda.Stream."""
     lib = load()
     dev, (B, Nv, Nq, M, D, L, K) = _check_inputs(value, spatial_shapes, level_start_index,
                                                 sampling_loc, attn_weight, validate)
@@ -302,12 +332,13 @@ def backward(value: torch.Tensor, spatial_shapes: torch.Tensor, level_start_inde
             _ptr(workspace), ws_bytes, flags]
     with torch.cuda.device(dev):
         stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        side, side_ev = _side_args(dev, side_stream)
         if events is None:
-            rc = lib.msda_backward(*args, stream)
+            rc = lib.msda_backward(*args, stream, side, side_ev)
             where = "msda_backward"
         else:
             handles = _event_handles(events, len(BWD_STAGES))
-            rc = lib.msda_backward_events(*args, stream, handles)
+            rc = lib.msda_backward_events(*args, stream, side, side_ev, handles)
             where = "msda_backward_events"
     if rc != MSDA_OK:
         raise MSDAError(rc, where)
@@ -389,9 +420,11 @@ def backward_fused(value: torch.Tensor, spatial_shapes: torch.Tensor,
                    accumulate: bool = False, need_grad_ref: bool = True,
                    validate: bool = True, workspace: Optional[torch.Tensor] = None,
                    events: Optional[list] = None, per_level: bool = False,
-                   align_corners: bool = False, saved: Optional[tuple] = None):
+                   align_corners: bool = False, saved: Optional[tuple] = None,
+                   side_stream="auto"):
     """msda_backward_fused: (grad_value, grad_sampling_offsets, grad_attn_logits,
     grad_reference_points or None when need_grad_ref is False).
+    side_stream as for backward().
     saved: the (sampling_loc, attn_weight) forward_fused(save=True) returned
     for these inputs, or None to recompute them.
     events: 2 * len(BWD_FUSED_STAGES) timing events or None (see stage_times)."""
@@ -424,12 +457,13 @@ def backward_fused(value: torch.Tensor, spatial_shapes: torch.Tensor,
     with torch.cuda.device(dev):
         stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
         handles = None if events is None else _event_handles(events, len(BWD_FUSED_STAGES))
+        side, side_ev = _side_args(dev, side_stream)
         rc = lib.msda_backward_fused(
             _ptr(value), _dtype_code(value), _ptr(spatial_shapes), _ptr(level_start_index),
             _ptr(reference_points), _ptr(sampling_offsets), _ptr(attn_logits), _ptr(s_loc),
             _ptr(s_attn), _ptr(grad_out),
             _ptr(grad_value), _ptr(g_off), _ptr(g_logits), _ptr(g_ref), B, Nv, Nq, M, D, L, K,
-            _ptr(workspace), ws_bytes, flags, stream, handles)
+            _ptr(workspace), ws_bytes, flags, stream, side, side_ev, handles)
     if rc != MSDA_OK:
         raise MSDAError(rc, "msda_backward_fused")
     return grad_value, g_off, g_logits, g_ref
@@ -505,8 +539,9 @@ def backward3d(value: torch.Tensor, volume_shapes: torch.Tensor, level_start_ind
                sampling_loc: torch.Tensor, attn_weight: torch.Tensor, grad_out: torch.Tensor,
                grad_value: Optional[torch.Tensor] = None, accumulate: bool = False,
                validate: bool = True, align_corners: bool = False,
-               workspace: Optional[torch.Tensor] = None):
-    """msda3d_backward: (grad_value fp32 [B,Nv,M,D], grad_sampling_loc, grad_attn_weight)."""
+               workspace: Optional[torch.Tensor] = None, side_stream="auto"):
+    """msda3d_backward: (grad_value fp32 [B,Nv,M,D], grad_sampling_loc, grad_attn_weight).
+    side_stream as for backward()."""
     lib = load()
     dev, (B, Nv, Nq, M, D, L, K) = _check_inputs3d(value, volume_shapes, level_start_index,
                                                   sampling_loc, attn_weight, validate)
@@ -528,10 +563,12 @@ def backward3d(value: torch.Tensor, volume_shapes: torch.Tensor, level_start_ind
     ws_bytes = workspace.numel() if workspace is not None else 0
     with torch.cuda.device(dev):
         stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        side, side_ev = _side_args(dev, side_stream)
         rc = lib.msda3d_backward(_ptr(value), _dtype_code(value), _ptr(volume_shapes),
                                  _ptr(level_start_index), _ptr(sampling_loc), _ptr(attn_weight),
                                  _ptr(grad_out), _ptr(grad_value), _ptr(g_loc), _ptr(g_attn),
-                                 B, Nv, Nq, M, D, L, K, _ptr(workspace), ws_bytes, flags, stream)
+                                 B, Nv, Nq, M, D, L, K, _ptr(workspace), ws_bytes, flags, stream,
+                                 side, side_ev)
     if rc != MSDA_OK:
         raise MSDAError(rc, "msda3d_backward")
     return grad_value, g_loc, g_attn

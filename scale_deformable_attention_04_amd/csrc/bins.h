@@ -2,31 +2,13 @@
 // (count -> scan -> scatter -> tile kernels) and the point geometry it shares
 // with the sampling kernels: level tables in LDS, the bilinear neighbours of
 // a point, the tiles they touch.  Included by the translation units of
-// libmsda.so; everything has internal linkage except the per-device side
-// stream (msda_side), of which there is one per process.
+// libmsda.so; everything has internal linkage.
 #ifndef MSDA_CSRC_BINS_H
 #define MSDA_CSRC_BINS_H
 
-#include <mutex>
 #include <type_traits>
 
 #include "common.h"
-
-// One side stream per device, created on first use (default priority,
-// non-blocking with respect to the null stream), shared by every backward
-// of the library.  The mutex is held while a backward enqueues, so the fork /
-// join events are never shared between two calls in flight on the host.
-namespace msda_side {
-constexpr int kMaxDevices = 64;
-struct SideStream {
-    bool tried = false;
-    hipStream_t s = nullptr;
-    hipEvent_t fork = nullptr, filled = nullptr, join = nullptr;
-};
-std::mutex &mutex();
-// Call with mutex() held.  nullptr when no side stream can be had.
-SideStream *get();
-}  // namespace msda_side
 
 namespace {
 
@@ -282,9 +264,65 @@ struct Work {
     uint32_t *start;       // [B][nb_max][M] first entry of each bin in `sorted`
     uint32_t *cursor;      // [B][nb_max][M] next free entry while scattering
     uint4 *items;          // [work_max] (bin, first record, records, whole bin)
-    uint32_t *work_total;  // [1]
+    uint32_t *work_total;  // [2]: work items, bins on the zero list
+    uint32_t *zero;        // [B * nb_max * M] bins whose tiles are zeroed before the
+                           // grad_value kernel runs (overwrite mode): empty or split bins
     uint4 *recs;           // [4 * points] records grouped by bin
 };
+
+// The tile of a bin (b * nb_max + tile) * M + m: its batch and head, its
+// level's map and the tile's origin.  For volumes the tile lies in one
+// plane of its level, whose first row is row0.
+struct BinTile {
+    int b, m;
+    int H, W;    // the level's map
+    int row0;    // first row of the map (volumes: of the tile's plane) in a batch slice
+    int x0, y0;  // pixel of the tile's top-left corner
+};
+
+template <bool VOL>
+__device__ __forceinline__ BinTile bin_tile(uint32_t bin, const LevelLds &lv, int M, int nb_max,
+                                            int L) {
+    BinTile t;
+    t.m = (int)(bin % (uint32_t)M);
+    const uint32_t bt = bin / (uint32_t)M;
+    t.b = (int)(bt / (uint32_t)nb_max);
+    const int lb = (int)(bt - (uint32_t)t.b * nb_max);
+    // levels left out of the table own no bins; their first-bin entry equals the next one's
+    int l = 0;
+    while (l + 1 < L && lv.lvl[l + 1].w <= lb) ++l;
+    const int4 lvl = lv.lvl[l];
+    int rel = lb - lvl.w;
+    t.row0 = lvl.z;
+    if constexpr (VOL) {
+        const int zpl = rel / lv.tpp[l];
+        rel -= zpl * lv.tpp[l];
+        t.row0 += zpl * lvl.x * lvl.y;
+    }
+    const int tw = lv.tw[l];
+    const int ty = rel / tw;
+    t.x0 = (rel - ty * tw) * kTile;
+    t.y0 = ty * kTile;
+    t.H = lvl.x;
+    t.W = lvl.y;
+    return t;
+}
+
+// Zero the channels of head t.m of the tile's pixels inside the map, with
+// NT threads (thread index tid); D channels per head, M heads per row.
+template <int NT>
+__device__ __forceinline__ void zero_tile(float *__restrict__ grad_value, const BinTile &t,
+                                          size_t slice_v, int M, int D, int tid) {
+    const int quads = D >> 2;
+    float *gv = grad_value + (size_t)t.b * slice_v + (size_t)t.m * D;
+    for (int i = tid; i < kTilePx * quads; i += NT) {
+        const int px = i / quads, q = i - px * quads;
+        const int gx = t.x0 + (px & (kTile - 1)), gy = t.y0 + (px >> kTileShift);
+        if (gy < t.H && gx < t.W)
+            reinterpret_cast<float4 *>(gv + (size_t)(t.row0 + gy * t.W + gx) * M * D)[q] =
+                make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+}
 // ---------------------------------------------------------------------------
 // backward: points per bin
 // Workgroup = (batch b, head m, kBinPoints consecutive points of the
@@ -382,35 +420,40 @@ bin_count_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__
 }
 
 // ---------------------------------------------------------------------------
-// backward: scan of the bin counts, work list
+// backward: scan of the bin counts, work list, zero list
 // One workgroup of kScanThreads.  Bins are visited in (batch, tile, head)
 // order, which is also their order in memory: the bins of batch b are the
 // nbins * M words from b * nb_max * M on; all batches form one flat scan.
 // Each bin of n > 0 points becomes ceil(n / kChunk) work items (bin, first
-// record, records, whole bin).
+// record, records, whole bin).  In overwrite mode the bins whose pixels no
+// single work item writes outright -- empty bins and bins split over several
+// items -- go on the zero list, and their tiles are zeroed before the
+// grad_value kernel adds into them.
 // ---------------------------------------------------------------------------
-// Exclusive scan of (a, b) pairs over the kScanThreads threads of the block:
-// wave-level scans with lane shuffles, then one scan of the wave totals.
-// The block totals are returned in tot_a, tot_b.
-__device__ __forceinline__ void block_exclusive_scan2(uint32_t &a, uint32_t &b, uint2 *s_wave,
-                                                      uint32_t &tot_a, uint32_t &tot_b) {
+// Exclusive scan of (a, b, c) over the kScanThreads threads of the block:
+// wave-level scans with DPP, then one scan of the wave totals.  The block
+// totals are returned in tot.
+__device__ __forceinline__ void block_exclusive_scan3(uint32_t &a, uint32_t &b, uint32_t &c,
+                                                      uint4 *s_wave, uint3 &tot) {
     constexpr int kWaves = kScanThreads / 64;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const uint32_t ia = wave_inclusive_scan(a), ib = wave_inclusive_scan(b);
-    if (lane == 63) s_wave[wave] = make_uint2(ia, ib);
+    const uint32_t ic = wave_inclusive_scan(c);
+    if (lane == 63) s_wave[wave] = make_uint4(ia, ib, ic, 0u);
     __syncthreads();
     if (wave == 0) {
-        const uint2 v = lane < kWaves ? s_wave[lane] : make_uint2(0u, 0u);
+        const uint4 v = lane < kWaves ? s_wave[lane] : make_uint4(0u, 0u, 0u, 0u);
         const uint32_t sa = wave_inclusive_scan(v.x), sb = wave_inclusive_scan(v.y);
-        if (lane < kWaves) s_wave[lane] = make_uint2(sa - v.x, sb - v.y);  // exclusive
-        if (lane == kWaves - 1) s_wave[kWaves] = make_uint2(sa, sb);
+        const uint32_t sc = wave_inclusive_scan(v.z);
+        if (lane < kWaves) s_wave[lane] = make_uint4(sa - v.x, sb - v.y, sc - v.z, 0u);
+        if (lane == kWaves - 1) s_wave[kWaves] = make_uint4(sa, sb, sc, 0u);
     }
     __syncthreads();
-    const uint2 base = s_wave[wave];
-    tot_a = s_wave[kWaves].x;
-    tot_b = s_wave[kWaves].y;
+    const uint4 base = s_wave[wave];
+    tot = make_uint3(s_wave[kWaves].x, s_wave[kWaves].y, s_wave[kWaves].z);
     a = base.x + ia - a;
     b = base.y + ib - b;
+    c = base.z + ic - c;
     __syncthreads();  // s_wave is reused by the next call
 }
 
@@ -419,20 +462,21 @@ __global__ void __launch_bounds__(kScanThreads)
 bin_scan_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ starts,
                 const uint32_t *__restrict__ counts, uint32_t *__restrict__ start,
                 uint32_t *__restrict__ cursor, uint4 *__restrict__ items,
-                uint32_t *__restrict__ work_total, int B, Dims dm) {
+                uint32_t *__restrict__ work_total, uint32_t *__restrict__ zero, int B, Dims dm) {
     constexpr int kPer = 8;
     __shared__ LevelLds s_lv;
-    __shared__ uint2 s_wave[kScanThreads / 64 + 1];
+    __shared__ uint4 s_wave[kScanThreads / 64 + 1];
     stage_bin_levels<VOL>(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
     // the used bins of every batch as one flat sequence f = b * per_b + (tile * M + m),
     // scanned in one pass (the bins of batch b start at b * nb_max * M in memory)
     const uint32_t per_b = (uint32_t)s_lv.nbins * (uint32_t)dm.M;
     const uint32_t stride_b = (uint32_t)dm.nb_max * (uint32_t)dm.M;
     const uint32_t nf = per_b * (uint32_t)B;
-    uint32_t carry_e = 0, carry_c = 0;
+    const bool zeroing = !dm.accumulate;
+    uint32_t carry_e = 0, carry_c = 0, carry_z = 0;
     for (uint32_t base = 0; base < nf; base += kScanThreads * kPer) {
         const uint32_t g0 = base + threadIdx.x * kPer;
-        uint32_t cnt[kPer], bin[kPer], e = 0, ch = 0;
+        uint32_t cnt[kPer], bin[kPer], e = 0, ch = 0, z = 0;
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const uint32_t f = g0 + i;
@@ -441,11 +485,13 @@ bin_scan_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ 
             cnt[i] = f < nf ? counts[bin[i]] : 0u;
             e += cnt[i];
             ch += (cnt[i] + kChunk - 1) / kChunk;
+            z += (zeroing && f < nf && (cnt[i] == 0u || cnt[i] > (uint32_t)kChunk)) ? 1u : 0u;
         }
-        uint32_t tot_e, tot_c;
-        block_exclusive_scan2(e, ch, s_wave, tot_e, tot_c);
+        uint3 tot;
+        block_exclusive_scan3(e, ch, z, s_wave, tot);
         e += carry_e;
         ch += carry_c;
+        z += carry_z;
         // a rolled loop: this kernel is one workgroup on the critical path,
         // and its instruction fetches are not hidden by other waves
 #pragma unroll 1
@@ -458,14 +504,19 @@ bin_scan_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ 
                     items[ch + k] = make_uint4(bin[i], e + k * kChunk,
                                                min((uint32_t)kChunk, cnt[i] - k * kChunk),
                                                nch == 1 ? 1u : 0u);
+                if (zeroing && nch != 1u) zero[z++] = bin[i];
                 e += cnt[i];
                 ch += nch;
             }
         }
-        carry_e += tot_e;
-        carry_c += tot_c;
+        carry_e += tot.x;
+        carry_c += tot.y;
+        carry_z += tot.z;
     }
-    if (threadIdx.x == 0) *work_total = carry_c;
+    if (threadIdx.x == 0) {
+        work_total[0] = carry_c;
+        work_total[1] = carry_z;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -479,12 +530,22 @@ constexpr int kCellsW = kTile + 1;
 constexpr int kCells = kCellsW * kCellsW;
 constexpr int kRecQueryShift = 7;  // cells < 128
 
+// Zeroing (zero != nullptr, one launch per call): before its own points,
+// workgroup g zeroes the tiles of zero-list entries g, g + grid, ... -- the
+// grad_value kernel, launched after this one, then adds into them.
+struct ZeroList {
+    const uint32_t *zero;        // bins, or nullptr: nothing to zero
+    const uint32_t *work_total;  // [2]: work items, entries on the list
+    float *grad_value;
+    int D;
+};
+
 template <bool VOL>
 __global__ void __launch_bounds__(kThreads)
 bin_scatter_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ starts,
                    const float *__restrict__ loc, const float *__restrict__ attn,
                    uint32_t *__restrict__ cursor, uint4 *__restrict__ recs, int hist_cap,
-                   Dims dm) {
+                   ZeroList zl, Dims dm) {
     __shared__ LevelLds s_lv;
     extern __shared__ __align__(16) unsigned char smem[];
     uint32_t *s_cnt = reinterpret_cast<uint32_t *>(smem);  // [hist_cap] counts, then ranks
@@ -521,6 +582,13 @@ bin_scatter_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict
         }
     }
     stage_bin_levels<VOL>(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
+    if (zl.zero) {
+        const uint32_t nz = zl.work_total[1];
+        const size_t slice_v = (size_t)dm.Nv * M * zl.D;
+        for (uint32_t zi = blockIdx.x; zi < nz; zi += gridDim.x)
+            zero_tile<kThreads>(zl.grad_value, bin_tile<VOL>(zl.zero[zi], s_lv, M, dm.nb_max, dm.L),
+                                slice_v, M, zl.D, threadIdx.x);
+    }
     const int nbins = s_lv.nbins;
     const bool lds = nbins <= hist_cap;
     uint32_t *gcur = cursor + (size_t)b * dm.nb_max * M + m;  // tile i at gcur[i * M]
@@ -802,36 +870,20 @@ grad_value_tile_kernel(const int64_t *__restrict__ shapes, const int64_t *__rest
             }
             // 6. the item ends with A: write its tile
             if (A.off + kSub >= A.it.z) {
-                const uint32_t bin = A.it.x;
-                const int m = (int)(bin % (uint32_t)M);
-                const uint32_t bt = bin / (uint32_t)M;
-                const int b = (int)(bt / (uint32_t)dm.nb_max);
-                const int lb = (int)(bt - (uint32_t)b * dm.nb_max);
-                int l = 0;
-                while (l + 1 < dm.L && s_lv.lvl[l + 1].w <= lb) ++l;
-                const int4 lvl = s_lv.lvl[l];
-                const int tw = s_lv.tw[l];
-                int rel = lb - lvl.w;
-                int plane0 = lvl.z;  // first row of the tile's map (volumes: of its plane)
-                if constexpr (VOL) {
-                    const int zpl = rel / s_lv.tpp[l];
-                    rel -= zpl * s_lv.tpp[l];
-                    plane0 += zpl * lvl.x * lvl.y;
-                }
-                const int ty = rel / tw, tx = rel - ty * tw;
+                const BinTile t = bin_tile<VOL>(A.it.x, s_lv, M, dm.nb_max, dm.L);
                 const size_t slice = (size_t)dm.Nv * M * D;
-                float *gv = grad_value + (size_t)b * slice + (size_t)m * D;
+                float *gv = grad_value + (size_t)t.b * slice + (size_t)t.m * D;
 #pragma unroll
                 for (int o = 0; o < kOwn; ++o) {
                     const int pair = tid + o * kTileThreads;
                     if (pair >= kTilePx * kQuads) break;
                     const int px = pair / kQuads, q = pair - px * kQuads;
-                    const int gx = tx * kTile + (px & (kTile - 1));
-                    const int gy = ty * kTile + (px >> kTileShift);
+                    const int gx = t.x0 + (px & (kTile - 1));
+                    const int gy = t.y0 + (px >> kTileShift);
                     float4 a = acc[o];
                     acc[o] = make_float4(0.f, 0.f, 0.f, 0.f);
-                    if (gy >= lvl.x || gx >= lvl.y) continue;
-                    float *dst = gv + (size_t)(plane0 + gy * lvl.y + gx) * M * D + 4 * q;
+                    if (gy >= t.H || gx >= t.W) continue;
+                    float *dst = gv + (size_t)(t.row0 + gy * t.W + gx) * M * D + 4 * q;
                     if (A.it.w) {
                         // this work item alone owns the pixel: plain read-add-write
                         float4 *d4 = reinterpret_cast<float4 *>(dst);
@@ -1047,19 +1099,7 @@ grad_value_gather_kernel(const int64_t *__restrict__ shapes, const int64_t *__re
         }
         __syncthreads();
         // 5. write the tile: pixel = the four roles' sums
-        const int lb = (int)(bt - (uint32_t)b * dm.nb_max);
-        int l = 0;
-        while (l + 1 < dm.L && s_lv.lvl[l + 1].w <= lb) ++l;
-        const int4 lvl = s_lv.lvl[l];
-        const int tw = s_lv.tw[l];
-        int rel = lb - lvl.w;
-        int plane0 = lvl.z;  // first row of the tile's map (volumes: of its plane)
-        if constexpr (VOL) {
-            const int zpl = rel / s_lv.tpp[l];
-            rel -= zpl * s_lv.tpp[l];
-            plane0 += zpl * lvl.x * lvl.y;
-        }
-        const int ty = rel / tw, tx = rel - ty * tw;
+        const BinTile tile = bin_tile<VOL>(bin, s_lv, M, dm.nb_max, dm.L);
         const size_t slice_v = (size_t)dm.Nv * M * D;
         float *gv = grad_value + (size_t)b * slice_v + (size_t)m * D;
         for (int i = tid; i < kTilePx * kQuads; i += kT) {
@@ -1073,10 +1113,10 @@ grad_value_gather_kernel(const int64_t *__restrict__ shapes, const int64_t *__re
                 a.z += v.z;
                 a.w += v.w;
             }
-            const int gx = tx * kTile + (px & (kTile - 1));
-            const int gy = ty * kTile + (px >> kTileShift);
-            if (gy >= lvl.x || gx >= lvl.y) continue;
-            float *dst = gv + (size_t)(plane0 + gy * lvl.y + gx) * M * D + 4 * q;
+            const int gx = tile.x0 + (px & (kTile - 1));
+            const int gy = tile.y0 + (px >> kTileShift);
+            if (gy >= tile.H || gx >= tile.W) continue;
+            float *dst = gv + (size_t)(tile.row0 + gy * tile.W + gx) * M * D + 4 * q;
             if (it.w) {
                 // this work item alone owns the pixel: plain read-add-write
                 float4 *d4 = reinterpret_cast<float4 *>(dst);
@@ -1132,7 +1172,7 @@ int64_t bins_bound(int64_t Nv, int64_t L) { return (15 * Nv + 49 * L) / 64 + 1; 
 
 struct WorkLayout {
     int64_t nb_max, bm_bins, work_max, sorted_max;
-    size_t off_counts, off_start, off_cursor, off_items, off_total, off_sorted, bytes;
+    size_t off_counts, off_start, off_cursor, off_items, off_total, off_zero, off_sorted, bytes;
 };
 
 // The workspace of the pipeline.  2-D levels (vol = false): at most four
@@ -1158,10 +1198,24 @@ WorkLayout work_layout(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t L, 
     w.off_items = o;
     o = align(o + 16 * (size_t)w.work_max);
     w.off_total = o;
-    o = align(o + 4);
+    o = align(o + 8);
+    w.off_zero = o;
+    o = align(o + 4 * (size_t)w.bm_bins);
     w.off_sorted = o;
     o = align(o + 16 * (size_t)w.sorted_max);
     w.bytes = o;
+    return w;
+}
+
+Work work_at(const WorkLayout &wl, unsigned char *ws) {
+    Work w;
+    w.counts = reinterpret_cast<uint32_t *>(ws + wl.off_counts);
+    w.start = reinterpret_cast<uint32_t *>(ws + wl.off_start);
+    w.cursor = reinterpret_cast<uint32_t *>(ws + wl.off_cursor);
+    w.items = reinterpret_cast<uint4 *>(ws + wl.off_items);
+    w.work_total = reinterpret_cast<uint32_t *>(ws + wl.off_total);
+    w.zero = reinterpret_cast<uint32_t *>(ws + wl.off_zero);
+    w.recs = reinterpret_cast<uint4 *>(ws + wl.off_sorted);
     return w;
 }
 
@@ -1172,19 +1226,131 @@ FastDiv make_fastdiv(uint32_t d) {  // d >= 1
     return FastDiv{(uint32_t)mul, shift};
 }
 
-// Where the backward enqueues: the caller's stream, an optional side stream
-// (with its fork / join events) and optional per-stage timing events.
+// Stages of the backward, for the caller's timing events (msda.h).
+constexpr int kStageDots = 0, kStageClear = 1, kStageCount = 2, kStageScan = 3,
+              kStageScatter = 4, kStageGather = 5;
+static_assert(kStageGather + 1 == MSDA_BWD_STAGES, "stage numbering matches msda.h");
+
+// Where the backward enqueues: the caller's stream s and, optionally, a
+// second caller-owned stream for the grad_attn / grad_loc kernel, forked
+// from s and joined back into it with the caller's two events; optional
+// per-stage timing events.
 struct Exec {
     hipStream_t s;
-    hipStream_t side;
-    hipEvent_t fork, filled, join;  // fork from s; grad_value zeroed; side work done
-    hipEvent_t *ev;                 // optional: 2 * MSDA_BWD_STAGES caller events (start, end)
-    bool fill_on_side;              // the grad_value zero-fill was enqueued on `side`
+    hipStream_t side;         // nullptr: everything on s
+    hipEvent_t fork, join;
+    hipEvent_t *ev;           // optional: 2 * stages caller events (start, end)
     // record the start (end = false) or end event of stage i on stream `on`
     void stamp(int i, bool end, hipStream_t on) const {
         if (ev && ev[2 * i + (end ? 1 : 0)]) (void)hipEventRecord(ev[2 * i + (end ? 1 : 0)], on);
     }
+    hipStream_t dots_stream() const { return side ? side : s; }
 };
+
+// Check and take the caller's side stream and its two events.  A NULL
+// side_stream, or one equal to the caller's stream, means one stream.
+inline msda_status exec_side(Exec &ex, void *side_stream, void *const *side_events) {
+    ex.side = nullptr;
+    ex.fork = ex.join = nullptr;
+    hipStream_t side = static_cast<hipStream_t>(side_stream);
+    if (!side || side == ex.s) return MSDA_OK;
+    if (!side_events || !side_events[0] || !side_events[1]) return MSDA_ERR_NULL;
+    ex.side = side;
+    ex.fork = static_cast<hipEvent_t>(side_events[0]);
+    ex.join = static_cast<hipEvent_t>(side_events[1]);
+    return MSDA_OK;
+}
+
+// The side stream waits for everything enqueued on s so far.
+inline msda_status exec_fork(const Exec &ex) {
+    if (!ex.side) return MSDA_OK;
+    msda_status st = hip_status(hipEventRecord(ex.fork, ex.s));
+    if (st == MSDA_OK) st = hip_status(hipStreamWaitEvent(ex.side, ex.fork, 0));
+    return st;
+}
+
+// s waits for everything enqueued on the side stream so far.  Called after a
+// successful fork on every path, failures included, so the side stream never
+// runs ahead of work the caller enqueues on s later.
+inline msda_status exec_join(const Exec &ex) {
+    if (!ex.side) return MSDA_OK;
+    msda_status st = hip_status(hipEventRecord(ex.join, ex.side));
+    if (st == MSDA_OK) st = hip_status(hipStreamWaitEvent(ex.s, ex.join, 0));
+    return st;
+}
+
+// Launches of per_b workgroups per batch, in chunks of batches that keep a
+// grid below 2^23 workgroups; launch(b0, grid) enqueues one chunk.
+template <typename F>
+msda_status per_batch(int64_t B, int64_t per_b, F &&launch) {
+    const int64_t bchunk = batch_chunk(per_b, B);
+    for (int64_t b0 = 0; b0 < B; b0 += bchunk) {
+        const int64_t nb = (B - b0) < bchunk ? (B - b0) : bchunk;
+        launch(b0, (unsigned)(per_b * nb));
+        const msda_status e = hip_status(hipGetLastError());
+        if (e != MSDA_OK) return e;
+    }
+    return MSDA_OK;
+}
+
+// The grad_value pipeline on the caller's stream: clear the bin counters,
+// count, scan (work list, zero list), scatter the records (zeroing the
+// listed tiles first, in overwrite mode), and the grad_value kernel.
+template <int D, bool VOL>
+msda_status run_bins(const int64_t *shapes, const int64_t *starts, const float *loc,
+                     const float *attn, const float *gout, float *gval, int64_t B, int64_t Nv,
+                     int64_t Nq, int64_t M, int64_t L, int64_t K, const WorkLayout &wl,
+                     unsigned char *ws, bool accumulate, bool align, const Exec &ex) {
+    const hipStream_t s = ex.s;
+    const Work w = work_at(wl, ws);
+    // the counts region is padded to 256 bytes, so whole float4s can be cleared
+    ex.stamp(kStageClear, false, s);
+    msda_status st = fill_zero(w.counts, (wl.off_start - wl.off_counts) / 16, s);
+    if (st != MSDA_OK) return st;
+    ex.stamp(kStageClear, true, s);
+
+    const int hist_cap = (int)(wl.nb_max < kHistLds ? wl.nb_max : kHistLds);
+    const int64_t gb = (Nq * L * K + kBinPoints - 1) / kBinPoints;  // per (batch, head)
+    Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, 0, 0, 0, (int)gb, (int)wl.nb_max,
+            accumulate ? 1 : 0, make_fastdiv((uint32_t)(L * K)), make_fastdiv((uint32_t)K)};
+    dm.align = align ? 1 : 0;
+    ex.stamp(kStageCount, false, s);
+    st = per_batch(B, gb * M, [&](int64_t b0, unsigned grid) {
+        Dims d2 = dm;
+        d2.b0 = (int)b0;
+        hipLaunchKernelGGL(bin_count_kernel<VOL>, dim3(grid), dim3(kThreads),
+                           4 * (size_t)hist_cap, s, shapes, starts, loc, w.counts, hist_cap, d2);
+    });
+    if (st != MSDA_OK) return st;
+    ex.stamp(kStageCount, true, s);
+
+    ex.stamp(kStageScan, false, s);
+    hipLaunchKernelGGL(bin_scan_kernel<VOL>, dim3(1), dim3(kScanThreads), 0, s, shapes, starts,
+                       w.counts, w.start, w.cursor, w.items, w.work_total, w.zero, (int)B, dm);
+    st = hip_status(hipGetLastError());
+    if (st != MSDA_OK) return st;
+    ex.stamp(kStageScan, true, s);
+
+    ex.stamp(kStageScatter, false, s);
+    st = per_batch(B, gb * M, [&](int64_t b0, unsigned grid) {
+        Dims d2 = dm;
+        d2.b0 = (int)b0;
+        // the first launch zeroes every listed tile of the whole problem
+        const ZeroList zl{(!accumulate && b0 == 0) ? w.zero : nullptr, w.work_total, gval,
+                          (int)D};
+        hipLaunchKernelGGL(bin_scatter_kernel<VOL>, dim3(grid), dim3(kThreads),
+                           8 * (size_t)hist_cap, s, shapes, starts, loc, attn, w.cursor, w.recs,
+                           hist_cap, zl, d2);
+    });
+    if (st != MSDA_OK) return st;
+    ex.stamp(kStageScatter, true, s);
+
+    ex.stamp(kStageGather, false, s);
+    st = hip_status(launch_grad_value<D, VOL>(wl.work_max, Nq, M, shapes, starts, gout, w.items,
+                                               w.work_total, w.recs, gval, dm, s));
+    ex.stamp(kStageGather, true, s);
+    return st;
+}
 
 }  // namespace
 

@@ -56,38 +56,6 @@
 // hipError_t of the last MSDA_ERR_HIP on this thread, for every translation unit
 thread_local int msda_internal_last_hip_error = 0;
 
-namespace msda_side {
-namespace {
-std::mutex g_side_mu;
-SideStream g_side[kMaxDevices];
-}  // namespace
-
-std::mutex &mutex() { return g_side_mu; }
-
-SideStream *get() {
-    int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-    SideStream &ss = g_side[dev];
-    if (!ss.tried) {
-        ss.tried = true;
-        bool ok = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) == hipSuccess;
-        ok = ok && hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess;
-        ok = ok && hipEventCreateWithFlags(&ss.filled, hipEventDisableTiming) == hipSuccess;
-        ok = ok && hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) == hipSuccess;
-        if (!ok) {
-            if (ss.join) (void)hipEventDestroy(ss.join);
-            if (ss.filled) (void)hipEventDestroy(ss.filled);
-            if (ss.fork) (void)hipEventDestroy(ss.fork);
-            if (ss.s) (void)hipStreamDestroy(ss.s);
-            ss.s = nullptr;
-            ss.fork = ss.filled = ss.join = nullptr;
-            (void)hipGetLastError();
-        }
-    }
-    return ss.s ? &ss : nullptr;
-}
-}  // namespace msda_side
-
 namespace {
 
 constexpr int kSetupLdsBytes = 36 * 1024;  // per-workgroup budget for the point tables
@@ -937,37 +905,17 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
                        float *gloc, float *gattn, int64_t B, int64_t Nv, int64_t Nq, int64_t M,
                        int64_t L, int64_t K, const WorkLayout &wl, unsigned char *ws,
                        bool accumulate, bool align, FusedBwd *fz, const Exec &ex) {
-    const hipStream_t s = ex.s;
-    Work w;
-    w.counts = reinterpret_cast<uint32_t *>(ws + wl.off_counts);
-    w.start = reinterpret_cast<uint32_t *>(ws + wl.off_start);
-    w.cursor = reinterpret_cast<uint32_t *>(ws + wl.off_cursor);
-    w.items = reinterpret_cast<uint4 *>(ws + wl.off_items);
-    w.work_total = reinterpret_cast<uint32_t *>(ws + wl.off_total);
-    w.recs = reinterpret_cast<uint4 *>(ws + wl.off_sorted);
     // grad_attn_weight and grad_sampling_loc do not depend on the bin
-    // pipeline: with a side stream (forked from the caller's stream before
-    // anything else) they are computed there, concurrently, and the caller's
-    // stream waits for them at the end
-    const hipStream_t ds = ex.side ? ex.side : s;
+    // pipeline: with a side stream they are computed there, concurrently
+    const hipStream_t ds = ex.dots_stream();
     const Launch p = plan(D, L, K, 32);
     const int64_t gq = (Nq + p.ipb - 1) / p.ipb;
     // the dots kernel finishes the fused prologue's backward itself when its
     // point table holds whole items and the softmax runs fit a wave
     if (fz) fz->in_dots = fz->softmax_run > 0 && p.pc == L * K;
     float *ref_part = fz && fz->in_dots ? fz->ref_part : nullptr;
-    auto per_batch = [&](int64_t per_b, auto &&launch) -> msda_status {
-        const int64_t bchunk = batch_chunk(per_b, B);
-        for (int64_t b0 = 0; b0 < B; b0 += bchunk) {
-            const int64_t nb = (B - b0) < bchunk ? (B - b0) : bchunk;
-            launch(b0, (unsigned)(per_b * nb));
-            const msda_status e = hip_status(hipGetLastError());
-            if (e != MSDA_OK) return e;
-        }
-        return MSDA_OK;
-    };
-    ex.stamp(1, false, ds);
-    msda_status st = per_batch(gq * M, [&](int64_t b0, unsigned grid) {
+    ex.stamp(kStageDots, false, ds);
+    msda_status st = per_batch(B, gq * M, [&](int64_t b0, unsigned grid) {
         Dims d2{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, p.pc, p.ps, (int)b0, (int)gq, 0, 0};
         d2.nblocks = (int)grid;
         d2.align = align ? 1 : 0;
@@ -981,61 +929,9 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
                            gattn, ref_part, d2);
     });
     if (st != MSDA_OK) return st;
-    ex.stamp(1, true, ds);
-    if (ex.side) {
-        st = hip_status(hipEventRecord(ex.join, ex.side));
-        if (st != MSDA_OK) return st;
-    }
-
-    // the counts region is padded to 256 bytes, so whole float4s can be cleared
-    ex.stamp(2, false, s);
-    st = fill_zero(w.counts, (wl.off_start - wl.off_counts) / 16, s);
-    if (st != MSDA_OK) return st;
-    ex.stamp(2, true, s);
-
-    const int hist_cap = (int)(wl.nb_max < kHistLds ? wl.nb_max : kHistLds);
-    const int64_t gb = (Nq * L * K + kBinPoints - 1) / kBinPoints;  // per (batch, head)
-    Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, 0, 0, 0, (int)gb, (int)wl.nb_max,
-            accumulate ? 1 : 0, make_fastdiv((uint32_t)(L * K)), make_fastdiv((uint32_t)K)};
-    dm.align = align ? 1 : 0;
-    ex.stamp(3, false, s);
-    st = per_batch(gb * M, [&](int64_t b0, unsigned grid) {
-        Dims d2 = dm;
-        d2.b0 = (int)b0;
-        hipLaunchKernelGGL(bin_count_kernel<false>, dim3(grid), dim3(kThreads),
-                           4 * (size_t)hist_cap, s, shapes, starts, loc, w.counts, hist_cap, d2);
-    });
-    if (st != MSDA_OK) return st;
-    ex.stamp(3, true, s);
-
-    ex.stamp(4, false, s);
-    hipLaunchKernelGGL(bin_scan_kernel<false>, dim3(1), dim3(kScanThreads), 0, s, shapes, starts,
-                       w.counts, w.start, w.cursor, w.items, w.work_total, (int)B, dm);
-    st = hip_status(hipGetLastError());
-    if (st != MSDA_OK) return st;
-    ex.stamp(4, true, s);
-
-    ex.stamp(5, false, s);
-    st = per_batch(gb * M, [&](int64_t b0, unsigned grid) {
-        Dims d2 = dm;
-        d2.b0 = (int)b0;
-        hipLaunchKernelGGL(bin_scatter_kernel<false>, dim3(grid), dim3(kThreads),
-                           8 * (size_t)hist_cap, s, shapes, starts, loc, attn, w.cursor, w.recs,
-                           hist_cap, d2);
-    });
-    if (st != MSDA_OK) return st;
-    ex.stamp(5, true, s);
-
-    if (ex.fill_on_side) {
-        st = hip_status(hipStreamWaitEvent(s, ex.filled, 0));
-        if (st != MSDA_OK) return st;
-    }
-    ex.stamp(6, false, s);
-    st = hip_status(launch_grad_value<D, false>(wl.work_max, Nq, M, shapes, starts, gout, w.items,
-                                                 w.work_total, w.recs, gval, dm, s));
-    ex.stamp(6, true, s);
-    if (st == MSDA_OK && ex.side) st = hip_status(hipStreamWaitEvent(s, ex.join, 0));
-    return st;
+    ex.stamp(kStageDots, true, ds);
+    return run_bins<D, false>(shapes, starts, loc, attn, gout, gval, B, Nv, Nq, M, L, K, wl, ws,
+                              accumulate, align, ex);
 }
 
 template <typename VT>
@@ -1199,7 +1095,8 @@ msda_status backward_impl(const void *value, int value_dtype, const int64_t *spa
                           float *grad_sampling_loc, float *grad_attn_weight, int64_t B,
                           int64_t Nv, int64_t Nq, int64_t M, int64_t D, int64_t L, int64_t K,
                           void *workspace, size_t workspace_bytes, uint32_t flags,
-                          FusedBwd *fz, hipStream_t s, hipEvent_t *ev) {
+                          FusedBwd *fz, hipStream_t s, void *side_stream,
+                          void *const *side_events, hipEvent_t *ev) {
     msda_status st = check_sizes(value_dtype, B, Nv, Nq, M, D, L, K);
     if (st != MSDA_OK) return st;
     if (flags & ~(MSDA_BWD_ACCUMULATE | MSDA_ALIGN_CORNERS | MSDA_BWD_BINNED))
@@ -1209,6 +1106,9 @@ msda_status backward_impl(const void *value, int value_dtype, const int64_t *spa
     const int64_t nval = B * Nv * M * D;
     if (nval > 0 && !grad_value) return MSDA_ERR_NULL;
     const bool work = B > 0 && Nq > 0;
+    Exec ex{s, nullptr, nullptr, nullptr, ev};
+    st = exec_side(ex, side_stream, side_events);
+    if (st != MSDA_OK) return st;
     WorkLayout wl{};
     if (work) {
         if (Nv < 1) return MSDA_ERR_SHAPE;
@@ -1223,15 +1123,20 @@ msda_status backward_impl(const void *value, int value_dtype, const int64_t *spa
         if (workspace_bytes < wl.bytes) return MSDA_ERR_WORKSPACE;
         if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return MSDA_ERR_WORKSPACE;
     }
-    Exec ex{s, nullptr, nullptr, nullptr, nullptr, ev, false};
     const bool acc = (flags & MSDA_BWD_ACCUMULATE) != 0;
     const bool align = (flags & MSDA_ALIGN_CORNERS) != 0;
-    // heads of few points: the whole backward in one kernel, recorded as
-    // stage 1 (the other stages are empty)
-    if (work && !fz && !(flags & MSDA_BWD_BINNED) && Nq * L * K <= kSmallPoints) {
-        ex.stamp(0, false, s);
-        ex.stamp(0, true, s);
-        ex.stamp(1, false, s);
+    if (!work) {
+        // no point: the gradient of value is zero
+        for (int i = 0; i < MSDA_BWD_STAGES; ++i) {
+            ex.stamp(i, false, s);
+            ex.stamp(i, true, s);
+        }
+        return acc ? MSDA_OK : fill_zero(grad_value, (size_t)nval / 4, s);  // D % 4 == 0
+    }
+    // heads of few points: the whole backward in one kernel on the caller's
+    // stream, recorded as the first stage (the other stages are empty)
+    if (!fz && !(flags & MSDA_BWD_BINNED) && Nq * L * K <= kSmallPoints) {
+        ex.stamp(kStageDots, false, s);
         st = value_dtype == MSDA_F32
                  ? dispatch_small<float>(D, value, spatial_shapes, level_start_index,
                                          sampling_loc, attn_weight, grad_out, grad_value,
@@ -1241,62 +1146,28 @@ msda_status backward_impl(const void *value, int value_dtype, const int64_t *spa
                                             sampling_loc, attn_weight, grad_out, grad_value,
                                             grad_sampling_loc, grad_attn_weight, B, Nv, Nq, M, L,
                                             K, acc, align, s);
-        ex.stamp(1, true, s);
-        for (int i = 2; i < MSDA_BWD_STAGES; ++i) {
+        ex.stamp(kStageDots, true, s);
+        for (int i = kStageDots + 1; i < MSDA_BWD_STAGES; ++i) {
             ex.stamp(i, false, s);
             ex.stamp(i, true, s);
         }
         return st;
     }
-    std::unique_lock<std::mutex> lock(msda_side::mutex(), std::defer_lock);
-    if (work) {
-        lock.lock();
-        if (msda_side::SideStream *ss = msda_side::get()) {
-            ex.side = ss->s;
-            ex.fork = ss->fork;
-            ex.filled = ss->filled;
-            ex.join = ss->join;
-        }
-    }
-    if (ex.side) {
-        st = hip_status(hipEventRecord(ex.fork, s));
-        if (st == MSDA_OK) st = hip_status(hipStreamWaitEvent(ex.side, ex.fork, 0));
-        if (st != MSDA_OK) return st;
-    }
-    if (!(flags & MSDA_BWD_ACCUMULATE)) {
-        // with a side stream the fill runs there, ahead of the dots kernel, and
-        // the tile kernel waits for it
-        const hipStream_t fs = ex.side ? ex.side : s;
-        ex.stamp(0, false, fs);
-        st = fill_zero(grad_value, (size_t)nval / 4, fs);  // D % 4 == 0
-        ex.stamp(0, true, fs);
-        if (st == MSDA_OK && ex.side) {
-            st = hip_status(hipEventRecord(ex.filled, ex.side));
-            ex.fill_on_side = true;
-        }
-        if (st != MSDA_OK) return st;
-    }
-    if (flags & MSDA_BWD_ACCUMULATE) {  // no fill: an empty stage
-        ex.stamp(0, false, s);
-        ex.stamp(0, true, s);
-    }
-    if (!work) {
-        for (int i = 1; i < MSDA_BWD_STAGES; ++i) {
-            ex.stamp(i, false, s);
-            ex.stamp(i, true, s);
-        }
-        return MSDA_OK;
-    }
+    st = exec_fork(ex);
+    if (st != MSDA_OK) return st;
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     if (value_dtype == MSDA_F32)
-        return dispatch_bwd<float>(D, value, spatial_shapes, level_start_index, sampling_loc,
-                                   attn_weight, grad_out, grad_value, grad_sampling_loc,
-                                   grad_attn_weight, B, Nv, Nq, M, L, K, wl, ws, acc, align,
-                                   fz, ex);
-    return dispatch_bwd<uint16_t>(D, value, spatial_shapes, level_start_index, sampling_loc,
-                                  attn_weight, grad_out, grad_value, grad_sampling_loc,
-                                  grad_attn_weight, B, Nv, Nq, M, L, K, wl, ws, acc, align,
-                                  fz, ex);
+        st = dispatch_bwd<float>(D, value, spatial_shapes, level_start_index, sampling_loc,
+                                 attn_weight, grad_out, grad_value, grad_sampling_loc,
+                                 grad_attn_weight, B, Nv, Nq, M, L, K, wl, ws, acc, align, fz,
+                                 ex);
+    else
+        st = dispatch_bwd<uint16_t>(D, value, spatial_shapes, level_start_index, sampling_loc,
+                                    attn_weight, grad_out, grad_value, grad_sampling_loc,
+                                    grad_attn_weight, B, Nv, Nq, M, L, K, wl, ws, acc, align, fz,
+                                    ex);
+    const msda_status js = exec_join(ex);
+    return st != MSDA_OK ? st : js;
 }
 
 // Workspace of the fused backward: the core's, then the locations [pts][2]
@@ -1324,7 +1195,8 @@ msda_status backward_fused_impl(const void *value, int value_dtype, const int64_
                                 float *grad_off, float *grad_logits, float *grad_ref, int64_t B,
                                 int64_t Nv, int64_t Nq, int64_t M, int64_t D, int64_t L,
                                 int64_t K, void *workspace, size_t workspace_bytes,
-                                uint32_t flags, hipStream_t s, hipEvent_t *ev) {
+                                uint32_t flags, hipStream_t s, void *side_stream,
+                                void *const *side_events, hipEvent_t *ev) {
     msda_status st = check_sizes(value_dtype, B, Nv, Nq, M, D, L, K);
     if (st != MSDA_OK) return st;
     if (flags & ~(MSDA_BWD_ACCUMULATE | MSDA_ALIGN_CORNERS | MSDA_SOFTMAX_PER_LEVEL))
@@ -1341,7 +1213,7 @@ msda_status backward_fused_impl(const void *value, int value_dtype, const int64_
         FusedBwd none{0, nullptr, false};
         st = backward_impl(value, value_dtype, shapes, starts, nullptr, nullptr, grad_out,
                            grad_value, nullptr, nullptr, B, Nv, Nq, M, D, L, K, workspace,
-                           workspace_bytes, core_flags, &none, s, ev);
+                           workspace_bytes, core_flags, &none, s, side_stream, side_events, ev);
         stamp(MSDA_BWD_STAGES + 1, false);
         stamp(MSDA_BWD_STAGES + 1, true);
         return st;
@@ -1381,7 +1253,7 @@ msda_status backward_fused_impl(const void *value, int value_dtype, const int64_
     const float *use_loc = saved ? saved_loc : loc, *use_attn = saved ? saved_attn : attn;
     st = backward_impl(value, value_dtype, shapes, starts, use_loc, use_attn, grad_out,
                        grad_value, grad_off, grad_logits, B, Nv, Nq, M, D, L, K, ws, fl.core,
-                       core_flags, &fz, s, ev);
+                       core_flags, &fz, s, side_stream, side_events, ev);
     if (st != MSDA_OK) return st;
 
     stamp(MSDA_BWD_STAGES + 1, false);
@@ -1422,11 +1294,11 @@ msda_status msda_backward(const void *value, int value_dtype, const int64_t *spa
                           float *grad_sampling_loc, float *grad_attn_weight, int64_t B,
                           int64_t Nv, int64_t Nq, int64_t M, int64_t D, int64_t L, int64_t K,
                           void *workspace, size_t workspace_bytes, uint32_t flags,
-                          void *stream) {
+                          void *stream, void *side_stream, void *const *side_events) {
     return backward_impl(value, value_dtype, spatial_shapes, level_start_index, sampling_loc,
                          attn_weight, grad_out, grad_value, grad_sampling_loc, grad_attn_weight,
                          B, Nv, Nq, M, D, L, K, workspace, workspace_bytes, flags, nullptr,
-                         static_cast<hipStream_t>(stream), nullptr);
+                         static_cast<hipStream_t>(stream), side_stream, side_events, nullptr);
 }
 
 msda_status msda_backward_events(const void *value, int value_dtype,
@@ -1436,14 +1308,15 @@ msda_status msda_backward_events(const void *value, int value_dtype,
                                  float *grad_sampling_loc, float *grad_attn_weight, int64_t B,
                                  int64_t Nv, int64_t Nq, int64_t M, int64_t D, int64_t L,
                                  int64_t K, void *workspace, size_t workspace_bytes,
-                                 uint32_t flags, void *stream, void *const *events) {
+                                 uint32_t flags, void *stream, void *side_stream,
+                                 void *const *side_events, void *const *events) {
     if (!events) return MSDA_ERR_NULL;
     hipEvent_t ev[2 * MSDA_BWD_STAGES];
     for (int i = 0; i < 2 * MSDA_BWD_STAGES; ++i) ev[i] = static_cast<hipEvent_t>(events[i]);
     return backward_impl(value, value_dtype, spatial_shapes, level_start_index, sampling_loc,
                          attn_weight, grad_out, grad_value, grad_sampling_loc, grad_attn_weight,
                          B, Nv, Nq, M, D, L, K, workspace, workspace_bytes, flags, nullptr,
-                         static_cast<hipStream_t>(stream), ev);
+                         static_cast<hipStream_t>(stream), side_stream, side_events, ev);
 }
 
 size_t msda_backward_fused_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int64_t M,
@@ -1462,7 +1335,8 @@ msda_status msda_backward_fused(const void *value, int value_dtype,
                                 float *grad_attn_logits, float *grad_reference_points, int64_t B,
                                 int64_t Nv, int64_t Nq, int64_t M, int64_t D, int64_t L,
                                 int64_t K, void *workspace, size_t workspace_bytes,
-                                uint32_t flags, void *stream, void *const *events) {
+                                uint32_t flags, void *stream, void *side_stream,
+                                void *const *side_events, void *const *events) {
     hipEvent_t ev[2 * MSDA_BWD_FUSED_STAGES];
     if (events)
         for (int i = 0; i < 2 * MSDA_BWD_FUSED_STAGES; ++i)
@@ -1473,7 +1347,7 @@ msda_status msda_backward_fused(const void *value, int value_dtype,
                                grad_value, grad_sampling_offsets, grad_attn_logits,
                                grad_reference_points, B, Nv, Nq, M, D, L, K, workspace,
                                workspace_bytes, flags, static_cast<hipStream_t>(stream),
-                               events ? ev : nullptr);
+                               side_stream, side_events, events ? ev : nullptr);
 }
 
 msda_status msda_validate_host(const int64_t *spatial_shapes_host, const int64_t *level_start_host,

@@ -398,29 +398,11 @@ msda_status launch3_bwd(const void *value, const int64_t *shapes, const int64_t 
                         float *gloc, float *gattn, int64_t B, int64_t Nv, int64_t Nq, int64_t M,
                         int64_t L, int64_t K, bool align, bool accumulate, const WorkLayout &wl,
                         unsigned char *ws, const Exec &ex) {
-    const hipStream_t s = ex.s;
-    Work w;
-    w.counts = reinterpret_cast<uint32_t *>(ws + wl.off_counts);
-    w.start = reinterpret_cast<uint32_t *>(ws + wl.off_start);
-    w.cursor = reinterpret_cast<uint32_t *>(ws + wl.off_cursor);
-    w.items = reinterpret_cast<uint4 *>(ws + wl.off_items);
-    w.work_total = reinterpret_cast<uint32_t *>(ws + wl.off_total);
-    w.recs = reinterpret_cast<uint4 *>(ws + wl.off_sorted);
-    auto per_batch = [&](int64_t per_b, auto &&launch) -> msda_status {
-        const int64_t bchunk = batch_chunk(per_b, B);
-        for (int64_t b0 = 0; b0 < B; b0 += bchunk) {
-            const int64_t nb = (B - b0) < bchunk ? (B - b0) : bchunk;
-            launch(b0, (unsigned)(per_b * nb));
-            const msda_status e = hip_status(hipGetLastError());
-            if (e != MSDA_OK) return e;
-        }
-        return MSDA_OK;
-    };
     // grad_attn_weight and grad_sampling_loc on the side stream (when there is one)
-    const hipStream_t ds = ex.side ? ex.side : s;
+    const hipStream_t ds = ex.dots_stream();
     const Plan3 p = plan3(D, L, K, 48);
     const int64_t gq = (Nq + p.ipb - 1) / p.ipb;
-    msda_status st = per_batch(gq * M, [&](int64_t b0, unsigned grid) {
+    msda_status st = per_batch(B, gq * M, [&](int64_t b0, unsigned grid) {
         const Dims3 dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, p.pc, p.ps, (int)b0, (int)gq,
                        align ? 1 : 0, (int)grid};
         const unsigned g = grid > (unsigned)kDots3Grid ? (unsigned)kDots3Grid : grid;
@@ -429,45 +411,9 @@ msda_status launch3_bwd(const void *value, const int64_t *shapes, const int64_t 
                            gattn, dm);
     });
     if (st != MSDA_OK) return st;
-    if (ex.side) {
-        st = hip_status(hipEventRecord(ex.join, ex.side));
-        if (st != MSDA_OK) return st;
-    }
     // grad_value: the binned pipeline over volume levels
-    st = fill_zero(w.counts, (wl.off_start - wl.off_counts) / 16, s);
-    if (st != MSDA_OK) return st;
-    const int hist_cap = (int)(wl.nb_max < kHistLds ? wl.nb_max : kHistLds);
-    const int64_t gb = (Nq * L * K + kBinPoints - 1) / kBinPoints;  // per (batch, head)
-    Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, 0, 0, 0, (int)gb, (int)wl.nb_max,
-            accumulate ? 1 : 0, make_fastdiv((uint32_t)(L * K)), make_fastdiv((uint32_t)K)};
-    dm.align = align ? 1 : 0;
-    st = per_batch(gb * M, [&](int64_t b0, unsigned grid) {
-        Dims d2 = dm;
-        d2.b0 = (int)b0;
-        hipLaunchKernelGGL(bin_count_kernel<true>, dim3(grid), dim3(kThreads), 4 * (size_t)hist_cap,
-                           s, shapes, starts, loc, w.counts, hist_cap, d2);
-    });
-    if (st != MSDA_OK) return st;
-    hipLaunchKernelGGL(bin_scan_kernel<true>, dim3(1), dim3(kScanThreads), 0, s, shapes, starts,
-                       w.counts, w.start, w.cursor, w.items, w.work_total, (int)B, dm);
-    st = hip_status(hipGetLastError());
-    if (st != MSDA_OK) return st;
-    st = per_batch(gb * M, [&](int64_t b0, unsigned grid) {
-        Dims d2 = dm;
-        d2.b0 = (int)b0;
-        hipLaunchKernelGGL(bin_scatter_kernel<true>, dim3(grid), dim3(kThreads),
-                           8 * (size_t)hist_cap, s, shapes, starts, loc, attn, w.cursor, w.recs,
-                           hist_cap, d2);
-    });
-    if (st != MSDA_OK) return st;
-    if (ex.fill_on_side) {
-        st = hip_status(hipStreamWaitEvent(s, ex.filled, 0));
-        if (st != MSDA_OK) return st;
-    }
-    st = hip_status(launch_grad_value<D, true>(wl.work_max, Nq, M, shapes, starts, gout, w.items,
-                                                w.work_total, w.recs, gval, dm, s));
-    if (st == MSDA_OK && ex.side) st = hip_status(hipStreamWaitEvent(s, ex.join, 0));
-    return st;
+    return run_bins<D, true>(shapes, starts, loc, attn, gout, gval, B, Nv, Nq, M, L, K, wl, ws,
+                             accumulate, align, ex);
 }
 
 #define MSDA3D_DISPATCH(FN, VT, ...)                                                           \
@@ -541,7 +487,7 @@ msda_status msda3d_backward(const void *value, int value_dtype, const int64_t *v
                             float *grad_sampling_loc, float *grad_attn_weight, int64_t B,
                             int64_t Nv, int64_t Nq, int64_t M, int64_t D, int64_t L, int64_t K,
                             void *workspace, size_t workspace_bytes, uint32_t flags,
-                            void *stream) {
+                            void *stream, void *side_stream, void *const *side_events) {
     msda_status st = check_sizes3(value_dtype, B, Nv, Nq, M, D, L, K);
     if (st != MSDA_OK) return st;
     if (flags & ~(MSDA_BWD_ACCUMULATE | MSDA_ALIGN_CORNERS)) return MSDA_ERR_UNSUPPORTED;
@@ -565,43 +511,26 @@ msda_status msda3d_backward(const void *value, int value_dtype, const int64_t *v
         if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return MSDA_ERR_WORKSPACE;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
-    Exec ex{s, nullptr, nullptr, nullptr, nullptr, nullptr, false};
-    std::unique_lock<std::mutex> lock(msda_side::mutex(), std::defer_lock);
-    if (work) {
-        lock.lock();
-        if (msda_side::SideStream *ss = msda_side::get()) {
-            ex.side = ss->s;
-            ex.fork = ss->fork;
-            ex.filled = ss->filled;
-            ex.join = ss->join;
-        }
-    }
-    if (ex.side) {
-        st = hip_status(hipEventRecord(ex.fork, s));
-        if (st == MSDA_OK) st = hip_status(hipStreamWaitEvent(ex.side, ex.fork, 0));
-        if (st != MSDA_OK) return st;
-    }
+    Exec ex{s, nullptr, nullptr, nullptr, nullptr};
+    st = exec_side(ex, side_stream, side_events);
+    if (st != MSDA_OK) return st;
     const bool acc = (flags & MSDA_BWD_ACCUMULATE) != 0;
-    if (!acc) {
-        // with a side stream the fill runs there, and the tile kernel waits for it
-        const hipStream_t fs = ex.side ? ex.side : s;
-        st = fill_zero(grad_value, (size_t)nval / 4, fs);  // D % 4 == 0
-        if (st == MSDA_OK && ex.side) {
-            st = hip_status(hipEventRecord(ex.filled, ex.side));
-            ex.fill_on_side = true;
-        }
-        if (st != MSDA_OK) return st;
-    }
-    if (!work) return MSDA_OK;
+    if (!work) return acc ? MSDA_OK : fill_zero(grad_value, (size_t)nval / 4, s);  // D % 4 == 0
+    st = exec_fork(ex);
+    if (st != MSDA_OK) return st;
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     const bool align = (flags & MSDA_ALIGN_CORNERS) != 0;
     if (value_dtype == MSDA_F32)
-        return dispatch3_bwd<float>(D, value, volume_shapes, level_start_index, sampling_loc,
-                                    attn_weight, grad_out, grad_value, grad_sampling_loc,
-                                    grad_attn_weight, B, Nv, Nq, M, L, K, align, acc, wl, ws, ex);
-    return dispatch3_bwd<uint16_t>(D, value, volume_shapes, level_start_index, sampling_loc,
-                                   attn_weight, grad_out, grad_value, grad_sampling_loc,
-                                   grad_attn_weight, B, Nv, Nq, M, L, K, align, acc, wl, ws, ex);
+        st = dispatch3_bwd<float>(D, value, volume_shapes, level_start_index, sampling_loc,
+                                  attn_weight, grad_out, grad_value, grad_sampling_loc,
+                                  grad_attn_weight, B, Nv, Nq, M, L, K, align, acc, wl, ws, ex);
+    else
+        st = dispatch3_bwd<uint16_t>(D, value, volume_shapes, level_start_index, sampling_loc,
+                                     attn_weight, grad_out, grad_value, grad_sampling_loc,
+                                     grad_attn_weight, B, Nv, Nq, M, L, K, align, acc, wl, ws,
+                                     ex);
+    const msda_status js = exec_join(ex);
+    return st != MSDA_OK ? st : js;
 }
 
 msda_status msda3d_validate_host(const int64_t *volume_shapes_host,

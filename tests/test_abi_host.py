@@ -98,7 +98,7 @@ def test_backward_rejects_before_launch():
     lib = msda.load()
     z = ctypes.c_void_p(0)
     bwd = lambda dt, flags, *dims: lib.msda_backward(z, dt, z, z, z, z, z, z, z, z, *dims,
-                                                      z, 0, flags, z)
+                                                      z, 0, flags, z, z, None)
     assert bwd(2, 0, 1, 80, 16, 2, 8, 2, 2) == B_.MSDA_ERR_DTYPE
     assert bwd(0, 4, 1, 80, 16, 2, 8, 2, 2) == B_.MSDA_ERR_UNSUPPORTED  # unknown flag
     assert bwd(0, 16, 1, 80, 16, 2, 8, 2, 2) == B_.MSDA_ERR_UNSUPPORTED
@@ -120,13 +120,17 @@ def test_backward_workspace_checks():
     assert 64 * pts <= n <= 64 * pts + (4 << 20)
     z = ctypes.c_void_p(0)
     fake = ctypes.c_void_p(1 << 20)   # never dereferenced: the checks fail first
-    bwd = lambda ws, nbytes: lib.msda_backward(fake, 0, fake, fake, fake, fake, fake, fake,
-                                               fake, fake, 1, 80, 16, 2, 8, 2, 2, ws, nbytes,
-                                               0, z)
+    bwd = lambda ws, nbytes, side=z, sev=None: lib.msda_backward(
+        fake, 0, fake, fake, fake, fake, fake, fake, fake, fake, 1, 80, 16, 2, 8, 2, 2, ws,
+        nbytes, 0, z, side, sev)
     need = lib.msda_backward_workspace_size(1, 80, 16, 2, 8, 2, 2)
     assert bwd(z, need) == B_.MSDA_ERR_NULL
     assert bwd(fake, need - 1) == B_.MSDA_ERR_WORKSPACE
     assert bwd(ctypes.c_void_p((1 << 20) + 4), need) == B_.MSDA_ERR_WORKSPACE
+    # a side stream needs its two events (checked before anything is enqueued)
+    assert bwd(fake, need, side=fake) == B_.MSDA_ERR_NULL
+    half = (ctypes.c_void_p * 2)(1 << 20, 0)
+    assert bwd(fake, need, side=fake, sev=half) == B_.MSDA_ERR_NULL
 
 
 def test_forward_fused_rejects_before_launch():
@@ -156,7 +160,7 @@ def test_backward_fused_rejects_before_launch():
     fake = ctypes.c_void_p(1 << 20)   # never dereferenced: the checks fail first
     bwd = lambda dt, flags, *dims, ws=z, nbytes=0, ref=fake, gref=fake, sl=z, sa=z: \
         lib.msda_backward_fused(fake, dt, fake, fake, ref, fake, fake, sl, sa, fake, fake, fake,
-                                fake, gref, *dims, ws, nbytes, flags, z, None)
+                                fake, gref, *dims, ws, nbytes, flags, z, z, None, None)
     dims = (1, 80, 16, 2, 8, 2, 2)
     need = lib.msda_backward_fused_workspace_size(*dims)
     core = lib.msda_backward_workspace_size(*dims)
@@ -184,18 +188,18 @@ def test_volume_entry_points_reject_before_launch():
     assert fwd(0, 0, 80, 16, 2, 8, 2, 2) == B_.MSDA_OK
     assert fwd(0, 1, 80, 16, 2, 8, 2, 2, flags=B_.MSDA_SOFTMAX_PER_LEVEL) == B_.MSDA_ERR_UNSUPPORTED
     bwd = lambda dt, flags, *dims, ws=z, nb=0: lib.msda3d_backward(
-        z, dt, z, z, z, z, z, z, z, z, *dims, ws, nb, flags, z)
+        z, dt, z, z, z, z, z, z, z, z, *dims, ws, nb, flags, z, z, None)
     assert bwd(0, 8, 1, 80, 16, 2, 8, 2, 2) == B_.MSDA_ERR_UNSUPPORTED
     assert bwd(0, 0, 1, 80, 16, 2, 8, 2, 2) == B_.MSDA_ERR_NULL
     assert bwd(0, 0, 0, 80, 16, 2, 8, 2, 2) == B_.MSDA_OK          # nothing to do
     # workspace: eight 16-byte records per point plus the bin tables
     need = lib.msda3d_backward_workspace_size(1, 80, 16, 2, 8, 2, 2)
     pts = 16 * 2 * 2 * 2
-    assert 128 * pts <= need <= 128 * pts + 64 * 80 * 2 + 4096
+    assert 128 * pts <= need <= 128 * pts + 80 * 80 * 2 + 4096
     assert lib.msda3d_backward_workspace_size(0, 80, 16, 2, 8, 2, 2) == 0
     fake = ctypes.c_void_p(1 << 20)
     b2 = lambda ws, nb: lib.msda3d_backward(fake, 0, fake, fake, fake, fake, fake, fake, fake,
-                                            fake, 1, 80, 16, 2, 8, 2, 2, ws, nb, 0, z)
+                                            fake, 1, 80, 16, 2, 8, 2, 2, ws, nb, 0, z, z, None)
     assert b2(z, need) == B_.MSDA_ERR_NULL
     assert b2(fake, need - 1) == B_.MSDA_ERR_WORKSPACE
     # the level table: rows (Z, H, W)

@@ -119,6 +119,26 @@ def test_encoder_bwd(msda):
     check_bwd(msda, workloads.make(3))
 
 
+def test_decoder_bwd(msda):
+    """The decoder shape's backward (300 object queries over the encoder's
+    4-level value: 4,800 points per head, so the binned pipeline), fp32 and
+    with a bf16 value."""
+    _say("decoder bwd B=2 Nq=300 fp32")
+    w = workloads.make(2)
+    check_bwd(msda, w)
+    _say("decoder bwd B=2 Nq=300 bf16 value")
+    bits = workloads.bf16_bits(w.value)
+    wb = workloads.Workload(w.name + " bf16", workloads.bf16_to_f32(bits).reshape(w.value.shape),
+                            w.spatial_shapes, w.level_start_index, w.sampling_loc,
+                            w.attn_weight, w.grad_out, value_bf16=bits.reshape(w.value.shape),
+                            value_unrounded=w.value)
+    gv, gl, ga = gpu_backward(msda, wb, bf16=True)
+    for x, r in zip((gv, gl, ga), oracle_bwd(wb)):             # bf16-rounded value
+        close(x, r, BWD_TOL)
+    for x, r in zip((gv, gl, ga), oracle_bwd(wb, wb.value_unrounded)):  # pass/fail bar
+        close(x, r, BF16_TOL)
+
+
 def test_train_bf16_fwd_bwd(msda):
     _say("train bf16 B=4 K=8 fwd+bwd")
     w = workloads.make(4)
@@ -446,8 +466,7 @@ def test_backward_repeatability(msda):
 @pytest.mark.parametrize("accumulate", [False, True])
 def test_backward_with_stage_events(msda, accumulate):
     """msda_backward_events gives the same gradients as the oracle and records a
-    start and an end event around every stage (empty fill stage when
-    accumulating)."""
+    start and an end event around every stage."""
     w = workloads.random_case(900, 2, ((9, 13), (5, 7)), 70, 4, 32, 4)
     x = dev_inputs(w)
     g = torch.from_numpy(w.grad_out).cuda()
@@ -461,5 +480,50 @@ def test_backward_with_stage_events(msda, accumulate):
     assert st[msda.BWD_STAGES.index("tiles")] > 0.0 and st[msda.BWD_STAGES.index("dots")] > 0.0
     rv, rl, ra = oracle_bwd(w)
     close(gv.cpu().numpy(), rv, BWD_TOL, "grad_value")
+    close(gl.cpu().numpy(), rl, BWD_TOL, "grad_sampling_loc")
+    close(ga.cpu().numpy(), ra, BWD_TOL, "grad_attn_weight")
+
+
+def test_two_streams_backward_concurrently(msda):
+    """Two backwards issued on two torch streams without a host wait between
+    them, each with its own workspace (and, by default, its own side stream
+    kept by the binding), compared with the oracle: the library holds no state
+    that the two calls share."""
+    wa = workloads.random_case(1200, 2, ((40, 52), (20, 26), (10, 13)), 900, 4, 32, 4)
+    wb = workloads.random_case(1201, 1, ((33, 17), (9, 9)), 1300, 8, 16, 3, -0.2, 1.2)
+    xa, xb = dev_inputs(wa), dev_inputs(wb)
+    ga, gb = torch.from_numpy(wa.grad_out).cuda(), torch.from_numpy(wb.grad_out).cuda()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    _say("two streams, concurrent backwards")
+    with torch.cuda.stream(sa):
+        ra = msda.backward(**xa, grad_out=ga, validate=False)
+    with torch.cuda.stream(sb):
+        rb = msda.backward(**xb, grad_out=gb, validate=False)
+    torch.cuda.synchronize()
+    for got, w in ((ra, wa), (rb, wb)):
+        for x, r, n in zip(got, oracle_bwd(w), ("grad_value", "grad_sampling_loc",
+                                                "grad_attn_weight")):
+            close(x.cpu().numpy(), r, BWD_TOL, f"{w.name} {n}")
+
+
+@pytest.mark.parametrize("side", ["auto", None])
+def test_overwrite_replaces_every_element(msda, side):
+    """Overwrite mode writes every element of grad_value: a NaN-filled buffer
+    comes back equal to the oracle.  The points crowd into a corner of each
+    map, so most 8x8 tiles receive nothing (zeroed from the zero list), and
+    the small coarse level's one tile is split over several work items."""
+    w = workloads.random_case(1300, 2, ((48, 64), (24, 32), (5, 6)), 1500, 2, 32, 4,
+                              0.0, 0.3)
+    x = dev_inputs(w)
+    g = torch.from_numpy(w.grad_out).cuda()
+    _say(f"overwrite of a NaN-filled grad_value, side_stream={side}")
+    gv = torch.full(tuple(w.value.shape), float("nan"), device="cuda")
+    gv, gl, ga = msda.backward(**x, grad_out=g, grad_value=gv, side_stream=side)
+    torch.cuda.synchronize()
+    rv, rl, ra = oracle_bwd(w)
+    got = gv.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    close(got, rv, BWD_TOL, "grad_value")
     close(gl.cpu().numpy(), rl, BWD_TOL, "grad_sampling_loc")
     close(ga.cpu().numpy(), ra, BWD_TOL, "grad_attn_weight")

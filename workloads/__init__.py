@@ -164,7 +164,7 @@ def make(config: int | str, batch: Optional[int] = None) -> Workload:
     loc = _locations(ref, base + 2, M, shapes, K, sigma)
     w = _weights(base + 3, B, Nq, M, L, K)
     g = None
-    if idx in (3, 4):
+    if idx in (2, 3, 4):
         g = _rng(base + 4).standard_normal((B, Nq, M * D)).astype(np.float32)
     if idx == 4:
         bits = bf16_bits(vals)
