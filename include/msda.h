@@ -44,8 +44,9 @@
  * level_start_index included, is a DEVICE pointer on the current HIP device;
  * the caller allocates and owns all of them, and the backward's scratch
  * workspace too.  The library allocates no memory and keeps no state between
- * calls.  Outputs must not alias inputs.  Calls on different streams may run
- * concurrently when each has its own outputs and workspace.
+ * calls, except msda_backward_noalloc's static scratch (see there).  Outputs
+ * must not alias inputs.  Calls on different streams may run concurrently
+ * when each has its own outputs and workspace.
  *
  * Streams and errors.  `stream` is a hipStream_t (NULL = the null stream).
  * Work is enqueued on it and the call returns without synchronizing; a
@@ -92,7 +93,9 @@ typedef enum msda_status {
     MSDA_ERR_DTYPE = -3,       /* value_dtype is not an msda_dtype                    */
     MSDA_ERR_UNSUPPORTED = -4, /* valid but outside the limits above (D, L, size)     */
     MSDA_ERR_HIP = -5,         /* the HIP runtime refused a launch (see msda_last_hip_error) */
-    MSDA_ERR_WORKSPACE = -6    /* workspace too small or not 256-byte aligned             */
+    MSDA_ERR_WORKSPACE = -6,   /* workspace too small or not 256-byte aligned             */
+    MSDA_ERR_SCRATCH = -7      /* msda_backward_noalloc: the problem needs more scratch
+                                  than MSDA_NOALLOC_SCRATCH_BYTES                      */
 } msda_status;
 
 typedef enum msda_dtype {
@@ -170,6 +173,30 @@ msda_status msda_backward(const void *value, int value_dtype,
                           int64_t L, int64_t K, void *workspace, size_t workspace_bytes,
                           uint32_t flags, void *stream, void *side_stream,
                           void *const *side_events);
+
+/*
+ * msda_backward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same computation, stream behaviour
+ * and results as msda_backward, with the workspace taken from a static
+ * device array of MSDA_NOALLOC_SCRATCH_BYTES bytes that the library holds on
+ * each GPU it runs on until the process ends.  The call allocates nothing
+ * (the array's address is looked up once per device, on the first call with
+ * that device current).  Problems whose msda_backward_workspace_size exceeds
+ * MSDA_NOALLOC_SCRATCH_BYTES are rejected with MSDA_ERR_SCRATCH before any
+ * work is enqueued.  Every call on one GPU uses the same array, and each call
+ * clears what it needs: calls that overlap in time on one GPU (other streams,
+ * other threads) race on it and must not be made.
+ */
+#define MSDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+msda_status msda_backward_noalloc(const void *value, int value_dtype,
+                                  const int64_t *spatial_shapes, const int64_t *level_start_index,
+                                  const float *sampling_loc, const float *attn_weight,
+                                  const float *grad_out, float *grad_value,
+                                  float *grad_sampling_loc, float *grad_attn_weight,
+                                  int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
+                                  int64_t L, int64_t K, uint32_t flags, void *stream,
+                                  void *side_stream, void *const *side_events);
 
 /*
  * Measurement entry point: msda_backward with the same arguments and the same

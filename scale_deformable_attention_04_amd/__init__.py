@@ -10,15 +10,17 @@ import torch
 
 from ._binding import (BWD_FUSED_STAGES, BWD_STAGES, EXPORTED, LIB_PATH, MSDA_ALIGN_CORNERS,
                        MSDA_BF16, MSDA_BWD_ACCUMULATE, MSDA_ERR_DTYPE,
-                       MSDA_ERR_HIP, MSDA_ERR_NULL, MSDA_ERR_SHAPE, MSDA_ERR_UNSUPPORTED,
-                       MSDA_ERR_WORKSPACE, MSDA_F32, MSDA_OK, MSDA_SOFTMAX_PER_LEVEL, MSDAError,
-                       backward, backward3d, backward_fused, dat_attention,
+                       MSDA_ERR_HIP, MSDA_ERR_NULL, MSDA_ERR_SCRATCH, MSDA_ERR_SHAPE,
+                       MSDA_ERR_UNSUPPORTED, MSDA_ERR_WORKSPACE, MSDA_F32, MSDA_OK,
+                       MSDA_SOFTMAX_PER_LEVEL, MSDAError, NOALLOC_SCRATCH_BYTES,
+                       backward, backward3d, backward_fused, backward_noalloc, dat_attention,
                        dat_attention_backward, dat_sample, dat_sample_backward, forward,
                        forward3d, forward_fused, fused_workspace_size, load, make_events,
                        stage_times, status_string, validate_host, validate_host3d,
                        workspace_size)
 
-__all__ = ["forward", "backward", "forward_fused", "backward_fused", "BWD_STAGES",
+__all__ = ["forward", "backward", "backward_noalloc", "NOALLOC_SCRATCH_BYTES",
+           "forward_fused", "backward_fused", "BWD_STAGES",
            "BWD_FUSED_STAGES", "make_events", "stage_times", "workspace_size",
            "fused_workspace_size", "validate_host", "status_string", "load",
            "MSDAError",

@@ -23,6 +23,8 @@ MSDA_ERR_DTYPE = -3
 MSDA_ERR_UNSUPPORTED = -4
 MSDA_ERR_HIP = -5
 MSDA_ERR_WORKSPACE = -6
+MSDA_ERR_SCRATCH = -7
+NOALLOC_SCRATCH_BYTES = 64 << 20
 MSDA_F32 = 0
 MSDA_BF16 = 1
 MSDA_BWD_ACCUMULATE = 1
@@ -31,7 +33,7 @@ MSDA_SOFTMAX_PER_LEVEL = 4
 MSDA_BWD_BINNED = 8
 
 EXPORTED = ("msda_forward", "msda_backward_workspace_size", "msda_backward",
-            "msda_backward_events", "msda_forward_fused", "msda_backward_fused_workspace_size",
+            "msda_backward_noalloc", "msda_backward_events", "msda_forward_fused", "msda_backward_fused_workspace_size",
             "msda_backward_fused", "msda3d_forward", "msda3d_backward_workspace_size",
             "msda3d_backward", "msda3d_validate_host",
             "msda_dat_attention_forward", "msda_dat_attention_workspace_size",
@@ -67,6 +69,9 @@ def load():
     lib.msda_backward.argtypes = ([p, ci, p, p, p, p, p, p, p, p] + [i64] * 7 +
                                   [p, ctypes.c_size_t, u32, p, p, p])
     lib.msda_backward.restype = ci
+    lib.msda_backward_noalloc.argtypes = ([p, ci, p, p, p, p, p, p, p, p] + [i64] * 7 +
+                                          [u32, p, p, p])
+    lib.msda_backward_noalloc.restype = ci
     lib.msda_backward_events.argtypes = ([p, ci, p, p, p, p, p, p, p, p] + [i64] * 7 +
                                          [p, ctypes.c_size_t, u32, p, p, p, p])
     lib.msda_backward_events.restype = ci
@@ -343,6 +348,40 @@ def backward(value: torch.Tensor, spatial_shapes: torch.Tensor, level_start_inde
     if rc != MSDA_OK:
         raise MSDAError(rc, where)
     return grad_value, grad_sampling_loc, grad_attn_weight
+
+
+def backward_noalloc(value: torch.Tensor, spatial_shapes: torch.Tensor,
+                     level_start_index: torch.Tensor, sampling_loc: torch.Tensor,
+                     attn_weight: torch.Tensor, grad_out: torch.Tensor,
+                     grad_value: torch.Tensor, grad_sampling_loc: torch.Tensor,
+                     grad_attn_weight: torch.Tensor, accumulate: bool = False,
+                     align_corners: bool = False, binned: bool = False, side_stream=None
+                     ) -> None:
+    """msda_backward_noalloc into caller-allocated outputs: the backward with its
+    workspace in the library's static per-GPU scratch (problems needing more
+    than NOALLOC_SCRATCH_BYTES raise MSDAError with MSDA_ERR_SCRATCH).  The
+    call itself allocates nothing; calls overlapping in time on one GPU must
+    not be made.  side_stream defaults to None here (everything on the
+    current stream); a torch.cuda.Stream or "auto" work as for backward()."""
+    lib = load()
+    dev, (B, Nv, Nq, M, D, L, K) = _check_inputs(value, spatial_shapes, level_start_index,
+                                                sampling_loc, attn_weight, False)
+    _need(grad_out, "grad_out", torch.float32, dev, (B, Nq, M * D))
+    _need(grad_value, "grad_value", torch.float32, dev, (B, Nv, M, D))
+    _need(grad_sampling_loc, "grad_sampling_loc", torch.float32, dev, sampling_loc.shape)
+    _need(grad_attn_weight, "grad_attn_weight", torch.float32, dev, attn_weight.shape)
+    flags = ((MSDA_BWD_ACCUMULATE if accumulate else 0) |
+             (MSDA_ALIGN_CORNERS if align_corners else 0) | (MSDA_BWD_BINNED if binned else 0))
+    with torch.cuda.device(dev):
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        side, side_ev = _side_args(dev, side_stream)
+        rc = lib.msda_backward_noalloc(
+            _ptr(value), _dtype_code(value), _ptr(spatial_shapes), _ptr(level_start_index),
+            _ptr(sampling_loc), _ptr(attn_weight), _ptr(grad_out), _ptr(grad_value),
+            _ptr(grad_sampling_loc), _ptr(grad_attn_weight), B, Nv, Nq, M, D, L, K, flags,
+            stream, side, side_ev)
+    if rc != MSDA_OK:
+        raise MSDAError(rc, "msda_backward_noalloc")
 
 
 # ---------------------------------------------------------------------------

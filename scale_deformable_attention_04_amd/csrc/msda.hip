@@ -1286,6 +1286,41 @@ msda_status backward_fused_impl(const void *value, int value_dtype, const int64_
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// msda_backward_noalloc: msda_backward with its workspace in a static device
+// array instead of a caller buffer, for callers that cannot allocate.  Each
+// GPU holds its own copy of the array; its address is looked up once per
+// device, with that device current, and kept.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[MSDA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void *g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The current device's copy of `scratch`.  In host code the array's name is
+// only a stand-in for the symbol: kernels and copies get this address.
+msda_status scratch_of_current_device(void **ptr) {
+    int dev = -1;
+    msda_status st = hip_status(hipGetDevice(&dev));
+    if (st != MSDA_OK) return st;
+    if (dev < 0 || dev >= kMaxDevices) return MSDA_ERR_UNSUPPORTED;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_err[dev] = e;
+        g_scratch_ptr[dev] = e == hipSuccess ? p : nullptr;
+    });
+    if (g_scratch_err[dev] != hipSuccess) return hip_status(g_scratch_err[dev]);
+    *ptr = g_scratch_ptr[dev];
+    return MSDA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 msda_status msda_backward(const void *value, int value_dtype, const int64_t *spatial_shapes,
@@ -1350,6 +1385,36 @@ msda_status msda_backward_fused(const void *value, int value_dtype,
                                side_stream, side_events, events ? ev : nullptr);
 }
 
+msda_status msda_backward_noalloc(const void *value, int value_dtype,
+                                  const int64_t *spatial_shapes, const int64_t *level_start_index,
+                                  const float *sampling_loc, const float *attn_weight,
+                                  const float *grad_out, float *grad_value,
+                                  float *grad_sampling_loc, float *grad_attn_weight, int64_t B,
+                                  int64_t Nv, int64_t Nq, int64_t M, int64_t D, int64_t L,
+                                  int64_t K, uint32_t flags, void *stream, void *side_stream,
+                                  void *const *side_events) {
+    msda_status st = check_sizes(value_dtype, B, Nv, Nq, M, D, L, K);
+    if (st != MSDA_OK) return st;
+    const bool work = B > 0 && Nq > 0;
+    const size_t need = work ? work_layout(B, Nv, Nq, M, L, K).bytes : 0;
+    if (need > MSDA_NOALLOC_SCRATCH_BYTES) return MSDA_ERR_SCRATCH;
+    // the pointer checks of msda_backward, before the one-time symbol lookup
+    if (B * Nv * M * D > 0 && !grad_value) return MSDA_ERR_NULL;
+    if (work && (!value || !spatial_shapes || !level_start_index || !sampling_loc ||
+                 !attn_weight || !grad_out || !grad_sampling_loc || !grad_attn_weight))
+        return MSDA_ERR_NULL;
+    void *ws = nullptr;
+    if (work) {
+        st = scratch_of_current_device(&ws);
+        if (st != MSDA_OK) return st;
+    }
+    return backward_impl(value, value_dtype, spatial_shapes, level_start_index, sampling_loc,
+                         attn_weight, grad_out, grad_value, grad_sampling_loc, grad_attn_weight,
+                         B, Nv, Nq, M, D, L, K, ws, work ? (size_t)MSDA_NOALLOC_SCRATCH_BYTES : 0,
+                         flags, nullptr, static_cast<hipStream_t>(stream), side_stream,
+                         side_events, nullptr);
+}
+
 msda_status msda_validate_host(const int64_t *spatial_shapes_host, const int64_t *level_start_host,
                                int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D, int64_t L,
                                int64_t K) {
@@ -1382,6 +1447,9 @@ const char *msda_status_string(int status) {
     case MSDA_ERR_HIP: return "the HIP runtime refused a launch";
     case MSDA_ERR_WORKSPACE:
         return "workspace smaller than msda_backward_workspace_size or not 256-byte aligned";
+    case MSDA_ERR_SCRATCH:
+        return "the problem needs more scratch than msda_backward_noalloc's static buffer "
+               "(MSDA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown msda status";
     }
 }

@@ -254,3 +254,21 @@ def test_binding_refuses_cpu_tensors():
     a = torch.zeros(1, 16, 2, 2, 2)
     with pytest.raises(ValueError):
         msda.forward(v, ss, st, loc, a)
+
+
+def test_backward_noalloc_rejects_before_launch():
+    """The no-allocation backward rejects a problem whose workspace exceeds its
+    static scratch, and missing pointers, before touching the GPU."""
+    lib = msda.load()
+    z = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(1 << 20)
+    bwd = lambda *dims, ptr=fake: lib.msda_backward_noalloc(
+        ptr, 0, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, *dims, 0, z, z, None)
+    big = (2, 22223, 22223, 8, 32, 4, 4)   # the encoder shape: ~365 MB of workspace
+    assert lib.msda_backward_workspace_size(*big) > msda.NOALLOC_SCRATCH_BYTES
+    assert bwd(*big) == B_.MSDA_ERR_SCRATCH
+    small = (2, 22223, 300, 8, 32, 4, 4)   # the decoder shape fits
+    assert 0 < lib.msda_backward_workspace_size(*small) <= msda.NOALLOC_SCRATCH_BYTES
+    assert bwd(*small, ptr=z) == B_.MSDA_ERR_NULL
+    assert bwd(2, 22223, 300, 8, 24, 4, 4) == B_.MSDA_ERR_UNSUPPORTED   # D
+    assert "scratch" in msda.status_string(B_.MSDA_ERR_SCRATCH)
