@@ -16,10 +16,16 @@ practice"), written out in plain numpy:
     with one softmax over all L*K points; section 2.2 (text) describes a
     softmax over the K points of each level.  Both are offered
     (per_level=False / True).
+  - the "Deformable DETR" tutorial, section 3.3 (multi-scale formula): each
+    sampled term is weighted by S_qlk * A_qlk, where S_qlk is a separately
+    predicted scale attention for level l.  Optional here (scale=None means
+    S = 1); when given it is an input of the same shape as the weights,
+    [B,Nq,M,L,K], and the core receives the product S * A.
 
-The backward is the chain rule through those two steps, in fp64:
+The backward is the chain rule through those steps, in fp64:
 grad_offsets = grad_loc / (W_l, H_l); grad_ref[b,q,l] = sum over heads and
-points of grad_loc; grad_logits = A * (grad_A - sum_group A * grad_A) over the
+points of grad_loc; with g = grad of the product S * A from the core,
+grad_scale = A * g and grad_logits = A * (S g - sum_group A * S g) over the
 softmax group.
 """
 from __future__ import annotations
@@ -57,30 +63,42 @@ def weights(logits, L: int, K: int, per_level: bool = False) -> np.ndarray:
     return (e / e.sum(axis=-1, keepdims=True)).reshape(B, Nq, M, L, K)
 
 
+def scaled_weights(logits, L: int, K: int, per_level: bool = False, scale=None) -> np.ndarray:
+    """S * A [B,Nq,M,L,K] float64: the softmax weights times the scale
+    attention (scale=None: S = 1)."""
+    A = weights(logits, L, K, per_level)
+    return A if scale is None else A * np.asarray(scale, dtype=np.float64)
+
+
 def forward(value, spatial_shapes, level_start_index, ref, offsets, logits,
-            per_level: bool = False, mode: int = SPEC) -> np.ndarray:
+            per_level: bool = False, mode: int = SPEC, scale=None) -> np.ndarray:
     """out[B, Nq, M*D] float64 of the core on the fused inputs."""
     L, K = np.asarray(offsets).shape[3], np.asarray(offsets).shape[4]
     loc = locations(ref, offsets, spatial_shapes)
-    A = weights(logits, L, K, per_level).astype(np.float32)
+    A = scaled_weights(logits, L, K, per_level, scale).astype(np.float32)
     return _core.forward(value, spatial_shapes, level_start_index, loc, A, mode=mode)
 
 
 def backward(value, spatial_shapes, level_start_index, ref, offsets, logits, grad_out,
-             per_level: bool = False, mode: int = SPEC):
-    """(grad_value, grad_offsets, grad_logits, grad_ref), float64."""
+             per_level: bool = False, mode: int = SPEC, scale=None):
+    """(grad_value, grad_offsets, grad_logits, grad_ref), float64, and
+    grad_scale as a fifth element when scale is given."""
     off = np.asarray(offsets)
     B, Nq, M, L, K, _ = off.shape
     loc = locations(ref, offsets, spatial_shapes)
     A64 = weights(logits, L, K, per_level)
+    S64 = np.ones_like(A64) if scale is None else np.asarray(scale, dtype=np.float64)
     gv, gl, ga = _core.backward(value, spatial_shapes, level_start_index, loc,
-                               A64.astype(np.float32), grad_out, mode=mode)
+                               (S64 * A64).astype(np.float32), grad_out, mode=mode)
     nrm = normalizer(spatial_shapes).astype(np.float64)
     g_off = gl / nrm[None, None, None, :, None, :]
     g_ref = gl.sum(axis=(2, 4))                                  # [B, Nq, L, 2]
+    gA = S64 * ga                                                # through S * A
     if per_level:
-        s = (A64 * ga).sum(axis=-1, keepdims=True)               # per (b, q, m, l)
+        s = (A64 * gA).sum(axis=-1, keepdims=True)               # per (b, q, m, l)
     else:
-        s = (A64 * ga).sum(axis=(-2, -1), keepdims=True)         # per (b, q, m)
-    g_logits = (A64 * (ga - s)).reshape(B, Nq, M, L * K)
-    return gv, g_off, g_logits, g_ref
+        s = (A64 * gA).sum(axis=(-2, -1), keepdims=True)         # per (b, q, m)
+    g_logits = (A64 * (gA - s)).reshape(B, Nq, M, L * K)
+    if scale is None:
+        return gv, g_off, g_logits, g_ref
+    return gv, g_off, g_logits, g_ref, A64 * ga

@@ -24,6 +24,14 @@ pages or the mathematics fix:
   pin_fused_finite_differences central differences along random directions of
                            the offsets, the references and the logits, with
                            every location kept inside its bilinear cell
+  pin_fused_scale_autograd the scale attention S of the "Deformable DETR"
+                           tutorial (section 3.3, weight S * A): torch CPU fp64
+                           autograd through the module's steps with the extra
+                           factor, forward and every gradient including S's
+  pin_fused_scale_identity S = 1 gives exactly the unscaled results
+  pin_fused_scale_linear   the output is linear in S (superposition, S = 0
+                           samples nothing) and central differences along S,
+                           exact for a linear map, equal <grad_scale, dS>
 """
 from __future__ import annotations
 
@@ -41,8 +49,9 @@ def _case(seed=11, K=3, **kw):
     return workloads.fused_case(seed, 2, SHAPES, 5, 2, 4, K, **kw)
 
 
-def _torch_fused(w, per_level, align):
-    """fp64 autograd of the module's forward steps written with torch ops."""
+def _torch_fused(w, per_level, align, scale=None):
+    """fp64 autograd of the module's forward steps written with torch ops
+    (with scale: the weights are S * softmax; S's gradient is returned last)."""
     B, Nq, M, L, K, _ = w.sampling_offsets.shape
     v = torch.tensor(w.value, dtype=torch.float64, requires_grad=True)
     ref = torch.tensor(w.reference_points, dtype=torch.float64, requires_grad=True)
@@ -52,10 +61,15 @@ def _torch_fused(w, per_level, align):
     loc = ref[:, :, None, :, None, :] + off / wh[None, None, None, :, None, :]
     groups = z.view(B, Nq, M, L, K) if per_level else z.view(B, Nq, M, 1, L * K)
     A = torch.softmax(groups, dim=-1).reshape(B, Nq, M, L, K)
+    S = None
+    if scale is not None:
+        S = torch.tensor(scale, dtype=torch.float64, requires_grad=True)
+        A = S * A
     out = grid_sample_core(v, w.spatial_shapes, w.level_start_index, loc, A, align)
     out.backward(torch.tensor(w.grad_out, dtype=torch.float64).reshape(out.shape))
-    return (out.detach().numpy(), v.grad.numpy(), off.grad.numpy(), z.grad.numpy(),
-            ref.grad.numpy())
+    res = (out.detach().numpy(), v.grad.numpy(), off.grad.numpy(), z.grad.numpy(),
+           ref.grad.numpy())
+    return res if S is None else res + (S.grad.numpy(),)
 
 
 def _args(w):
@@ -224,6 +238,66 @@ def pin_fused_finite_differences(impl):
             assert abs(fd - an) <= 2e-3 * abs(an) + 1e-6, (name, per_level, fd, an)
 
 
+def pin_fused_scale_autograd(impl):
+    for per_level, align in ((False, False), (True, False), (False, True)):
+        w = _case(seed=91 + 2 * per_level + align, ref_low=-0.05, ref_high=1.05,
+                  with_scale=True)
+        S = w.attn_scale
+        mode = oracle.DOUBLE | (oracle.ALIGN if align else 0)
+        t_out, t_gv, t_goff, t_gz, t_gref, t_gs = _torch_fused(w, per_level, align, S)
+        out = impl.forward(*_args(w), per_level=per_level, mode=mode, scale=S)
+        res = impl.backward(*_args(w), w.grad_out, per_level=per_level, mode=mode, scale=S)
+        tag = f"scale per_level={per_level} align={align}"
+        assert len(res) == 5, tag
+        gv, goff, gz, gref, gs = res
+        # the oracle rounds S * A and the locations to fp32: tolerances allow for it
+        assert max_rel(out, t_out) < 1e-6, tag
+        assert max_rel(gv, t_gv) < 1e-6, tag
+        assert goff.shape == t_goff.shape and max_rel(goff, t_goff) < 1e-5, tag
+        assert gz.shape == t_gz.shape and max_rel(gz, t_gz) < 1e-5, tag
+        assert gref.shape == t_gref.shape and max_rel(gref, t_gref) < 1e-5, tag
+        assert gs.shape == t_gs.shape and max_rel(gs, t_gs) < 1e-5, tag
+
+
+def pin_fused_scale_identity(impl):
+    w = _case(seed=101)
+    ones = np.ones(w.sampling_offsets.shape[:-1], np.float32)
+    for per_level in (False, True):
+        a = impl.forward(*_args(w), per_level=per_level)
+        b = impl.forward(*_args(w), per_level=per_level, scale=ones)
+        assert np.array_equal(a, b), f"S = 1 forward, per_level={per_level}"
+        ga = impl.backward(*_args(w), w.grad_out, per_level=per_level)
+        gb = impl.backward(*_args(w), w.grad_out, per_level=per_level, scale=ones)
+        for x, y in zip(ga, gb[:4]):
+            assert np.array_equal(x, y), f"S = 1 backward, per_level={per_level}"
+
+
+def pin_fused_scale_linear(impl):
+    w = _case(seed=111)
+    shp = w.sampling_offsets.shape[:-1]
+    r = np.random.Generator(np.random.PCG64(9))
+    # S on a 2^-8 grid, so that s1 + s2 is exact in fp32
+    s1 = (np.round(r.uniform(-1, 1, shp) * 256) / 256).astype(np.float32)
+    s2 = (np.round(r.uniform(-1, 1, shp) * 256) / 256).astype(np.float32)
+    g = w.grad_out.astype(np.float64)
+    for per_level in (False, True):
+        f = lambda S: impl.forward(*_args(w), per_level=per_level, mode=oracle.DOUBLE, scale=S)
+        o1, o2, o12 = f(s1), f(s2), f((s1 + s2).astype(np.float32))
+        assert max_rel(o12, o1 + o2) < 1e-6, f"superposition, per_level={per_level}"
+        assert np.all(f(np.zeros(shp, np.float32)) == 0.0), "S = 0 samples nothing"
+        # central difference along dS: exact for a map linear in S
+        gs = impl.backward(*_args(w), w.grad_out, per_level=per_level, mode=oracle.DOUBLE,
+                           scale=s1)[4]
+        dS = r.standard_normal(shp)
+        h = 0.25
+        fp = float(np.sum(f((s1 + h * dS).astype(np.float32)).reshape(g.shape) * g))
+        fm = float(np.sum(f((s1 - h * dS).astype(np.float32)).reshape(g.shape) * g))
+        fd = (fp - fm) / (2 * h)
+        an = float(np.sum(gs * dS))
+        assert abs(fd - an) <= 1e-5 * abs(an) + 1e-9, (per_level, fd, an)
+
+
 ALL_FUSED_PINS = [pin_fused_autograd, pin_fused_initial_state, pin_fused_logit_shift,
                   pin_fused_translation, pin_fused_softmax_grad, pin_fused_shift_gradient,
-                  pin_fused_finite_differences]
+                  pin_fused_finite_differences, pin_fused_scale_autograd,
+                  pin_fused_scale_identity, pin_fused_scale_linear]

@@ -30,9 +30,16 @@ MUTANTS = [
     ("grad_offsets_unscaled", "g_off = gl / nrm[None, None, None, :, None, :]", "g_off = gl", 1),
     ("grad_ref_over_levels", "g_ref = gl.sum(axis=(2, 4))", "g_ref = gl.sum(axis=(2, 4)) * 0 + gl.sum(axis=(2, 3, 4))[:, :, None]", 1),
     ("grad_ref_one_head", "g_ref = gl.sum(axis=(2, 4))", "g_ref = gl[:, :, 0].sum(axis=3)", 1),
-    ("grad_logits_no_centering", "(A64 * (ga - s))", "(A64 * ga)", 1),
-    ("grad_logits_global_sum_per_level", "s = (A64 * ga).sum(axis=-1, keepdims=True)", "s = (A64 * ga).sum(axis=(-2, -1), keepdims=True)", 1),
-    ("grad_logits_no_A", "(A64 * (ga - s))", "(ga - s)", 1),
+    ("grad_logits_no_centering", "(A64 * (gA - s))", "(A64 * gA)", 1),
+    ("grad_logits_global_sum_per_level", "s = (A64 * gA).sum(axis=-1, keepdims=True)", "s = (A64 * gA).sum(axis=(-2, -1), keepdims=True)", 1),
+    ("grad_logits_no_A", "(A64 * (gA - s))", "(gA - s)", 1),
+    # the scale attention S (weights S * A)
+    ("scale_ignored", "return A if scale is None else A * np.asarray(scale, dtype=np.float64)", "return A", 1),
+    ("scale_squared", "return A if scale is None else A * np.asarray(scale, dtype=np.float64)", "return A if scale is None else A * np.asarray(scale, dtype=np.float64) ** 2", 1),
+    ("grad_logits_skip_scale", "gA = S64 * ga", "gA = ga", 1),
+    ("grad_scale_without_A", "return gv, g_off, g_logits, g_ref, A64 * ga", "return gv, g_off, g_logits, g_ref, ga", 1),
+    ("grad_scale_times_S", "return gv, g_off, g_logits, g_ref, A64 * ga", "return gv, g_off, g_logits, g_ref, S64 * A64 * ga", 1),
+    ("grad_scale_of_gA", "return gv, g_off, g_logits, g_ref, A64 * ga", "return gv, g_off, g_logits, g_ref, A64 * gA", 1),
 ]
 
 

@@ -18,7 +18,7 @@ random references/offsets for learned ones.
 
 Random numbers: numpy Generator(PCG64(seed)) with seed = 1000*config + tensor
 id (0 value, 1 reference, 2 offsets, 3 logits, 4 grad_out, 5 direct
-locations).  Draws are float64 and rounded to float32 with round-to-nearest-
+locations, 6 scale attention).  Draws are float64 and rounded to float32 with round-to-nearest-
 even; bfloat16 values are round-to-nearest-even from those float32 values.
 Attention weights are a softmax over the L*K logits of one (query, head), as
 in the first page's module (section 3.2); locations are reference + offset,
@@ -207,6 +207,7 @@ class FusedWorkload:
     attn_logits: np.ndarray           # [B,Nq,M,L*K] float32
     grad_out: Optional[np.ndarray]    # [B,Nq,M*D] float32
     value_bf16: Optional[np.ndarray] = None   # [B,Nv,M,D] uint16 bits
+    attn_scale: Optional[np.ndarray] = None   # [B,Nq,M,L,K] float32 scale attention S
 
     @property
     def dims(self):
@@ -220,12 +221,19 @@ class FusedWorkload:
         return d["B"] * d["Nq"] * d["M"] * d["L"] * d["K"]
 
 
+def scale_attention(seed: int, shape) -> np.ndarray:
+    """A scale attention S [B,Nq,M,L,K] for the fused prologue: U(0, 2), a
+    predicted per-point factor (the pages give no distribution)."""
+    return _rng(seed).uniform(0.0, 2.0, shape).astype(np.float32)
+
+
 def fused_case(seed: int, B: int, shapes, Nq: int, M: int, D: int, K: int,
                ref_low: float = 0.0, ref_high: float = 1.0, sigma_px: float = 2.0,
-               logit_scale: float = 1.0, bf16: bool = False) -> FusedWorkload:
+               logit_scale: float = 1.0, bf16: bool = False,
+               with_scale: bool = False) -> FusedWorkload:
     """Small random case for the fused prologue: references uniform in
     [ref_low, ref_high) per level, offsets N(0, sigma_px) pixels, logits
-    N(0, logit_scale)."""
+    N(0, logit_scale); with_scale adds a scale attention (seed + 6)."""
     ss, st = level_table(shapes)
     Nv = int(ss.prod(axis=1).sum()) if len(shapes) else 0
     L = len(shapes)
@@ -235,19 +243,22 @@ def fused_case(seed: int, B: int, shapes, Nq: int, M: int, D: int, K: int,
     off = (r.standard_normal((B, Nq, M, L, K, 2)) * sigma_px).astype(np.float32)
     logits = (r.standard_normal((B, Nq, M, L * K)) * logit_scale).astype(np.float32)
     g = r.standard_normal((B, Nq, M * D)).astype(np.float32)
+    S = scale_attention(seed + 6, (B, Nq, M, L, K)) if with_scale else None
     name = f"fused_random(seed={seed})"
     if bf16:
         bits = bf16_bits(vals)
         return FusedWorkload(name, bf16_to_f32(bits).reshape(vals.shape), ss, st, ref, off,
-                             logits, g, value_bf16=bits.reshape(vals.shape))
-    return FusedWorkload(name, vals, ss, st, ref, off, logits, g)
+                             logits, g, value_bf16=bits.reshape(vals.shape), attn_scale=S)
+    return FusedWorkload(name, vals, ss, st, ref, off, logits, g, attn_scale=S)
 
 
-def make_fused(config: int | str = "encoder_bwd", batch: Optional[int] = None) -> FusedWorkload:
+def make_fused(config: int | str = "encoder_bwd", batch: Optional[int] = None,
+               with_scale: bool = False) -> FusedWorkload:
     """The encoder-shape configurations in the fused prologue's input form:
     every flattened pixel is a query whose reference point is its own pixel
     centre on every level, offsets N(0, sigma) pixels of each level and
-    logits N(0, 1) (seeds 1000*config + 2 and + 3, as in make())."""
+    logits N(0, 1) (seeds 1000*config + 2 and + 3, as in make()); with_scale
+    adds a scale attention (seed 1000*config + 6)."""
     idx = CONFIG_NAMES.index(config) if isinstance(config, str) else int(config)
     if idx not in (1, 3, 4):
         raise ValueError("fused inputs are defined for the encoder-shape configurations")
@@ -267,12 +278,13 @@ def make_fused(config: int | str = "encoder_bwd", batch: Optional[int] = None) -
     off = (_rng(base + 2).standard_normal((B, Nq, M, L, K, 2)) * sigma).astype(np.float32)
     logits = _rng(base + 3).standard_normal((B, Nq, M, L * K)).astype(np.float32)
     g = _rng(base + 4).standard_normal((B, Nq, M * D)).astype(np.float32)
+    S = scale_attention(base + 6, (B, Nq, M, L, K)) if with_scale else None
     name = CONFIG_NAMES[idx] + "_fused"
     if idx == 4:
         bits = bf16_bits(vals)
         return FusedWorkload(name, bf16_to_f32(bits).reshape(vals.shape), ss, st, ref, off,
-                             logits, g, value_bf16=bits.reshape(vals.shape))
-    return FusedWorkload(name, vals, ss, st, ref, off, logits, g)
+                             logits, g, value_bf16=bits.reshape(vals.shape), attn_scale=S)
+    return FusedWorkload(name, vals, ss, st, ref, off, logits, g, attn_scale=S)
 
 
 # ---------------------------------------------------------------------------
