@@ -239,22 +239,30 @@ msda_status msda_backward_events(const void *value, int value_dtype,
  * (W_l, H_l), and the weights are a softmax of the logits:
  *
  *   loc[b,q,m,l,k] = reference_points[b,q,l] + sampling_offsets[b,q,m,l,k] / (W_l, H_l)
- *   A[b,q,m,l,k]   = softmax of attn_logits[b,q,m,:] over its L*K entries, or
- *                    (MSDA_SOFTMAX_PER_LEVEL) over the K entries of level l
+ *   A[b,q,m,l,k]   = S[b,q,m,l,k] * P[b,q,m,l,k], where P is the softmax of
+ *                    attn_logits[b,q,m,:] over its L*K entries, or
+ *                    (MSDA_SOFTMAX_PER_LEVEL) over the K entries of level l,
+ *                    and S the optional scale attention attn_scale (NULL:
+ *                    S = 1): the "Deformable DETR" tutorial's multi-scale
+ *                    formula (section 3.3) weights each sampled term by a
+ *                    separately predicted scale attention S_qlk times A_qlk
  *
  * The module's code normalizes over all L*K points, the same page's text
  * over the K points of each level (section 2.2); both are offered.  The
  * location is computed in fp32 as one correctly rounded division and one
- * addition per coordinate; the softmax in fp32 with its maximum subtracted.
- * These entry points evaluate exactly the core above on those locations and
- * weights, without storing them in the forward.
+ * addition per coordinate; the softmax in fp32 with its maximum subtracted,
+ * then one fp32 product with S.  These entry points evaluate exactly the
+ * core above on those locations and weights, without storing them in the
+ * forward (unless asked to).
  *
  * Layouts (dense, row-major, device pointers, caller-owned):
  *   reference_points        [B, Nq, L, 2]        fp32, (x, y) normalized
  *   sampling_offsets        [B, Nq, M, L, K, 2]  fp32, (x, y) in pixels of level l
  *   attn_logits             [B, Nq, M, L*K]      fp32 (level-major: index l*K + k)
+ *   attn_scale              [B, Nq, M, L, K]     fp32, optional
  *   grad_sampling_offsets   like sampling_offsets
  *   grad_attn_logits        like attn_logits
+ *   grad_attn_scale         like attn_scale
  *   grad_reference_points   like reference_points
  * value, the level table, out, grad_out and grad_value as above.
  *
@@ -262,13 +270,14 @@ msda_status msda_backward_events(const void *value, int value_dtype,
  * MSDA_SOFTMAX_PER_LEVEL.  Errors and limits as msda_forward.
  * sampling_loc_out [B,Nq,M,L,K,2] and attn_weight_out [B,Nq,M,L,K] (fp32) are
  * optional (both NULL, or both given: else MSDA_ERR_NULL): when given they
- * receive the locations and weights the forward formed, for a training step
- * to hand to msda_backward_fused instead of having them recomputed.
+ * receive the locations and weights (S * P) the forward formed, for a
+ * training step to hand to msda_backward_fused instead of having them
+ * recomputed.
  */
 msda_status msda_forward_fused(const void *value, int value_dtype,
                                const int64_t *spatial_shapes, const int64_t *level_start_index,
                                const float *reference_points, const float *sampling_offsets,
-                               const float *attn_logits, float *out,
+                               const float *attn_logits, const float *attn_scale, float *out,
                                float *sampling_loc_out, float *attn_weight_out,
                                int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
                                int64_t L, int64_t K, uint32_t flags, void *stream);
@@ -284,12 +293,15 @@ size_t msda_backward_fused_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int
  * Backward of msda_forward_fused: the chain rule through the prologue on top
  * of the core's gradients (msda_backward):
  *   grad_sampling_offsets = grad_loc / (W_l, H_l)
- *   grad_attn_logits      = A * (grad_A - sum over the softmax group of A * grad_A)
+ *   grad_attn_logits      = P * (S grad_A - sum over the softmax group of P * S grad_A)
+ *   grad_attn_scale       = P * grad_A
  *   grad_reference_points[b,q,l] = sum over heads m and points k of grad_loc
  * grad_value is overwritten, or added to with MSDA_BWD_ACCUMULATE; the other
  * gradients are overwritten.  grad_reference_points may be NULL (not
- * computed, e.g. for fixed encoder reference points); every other pointer is
- * required.  flags: MSDA_BWD_ACCUMULATE, MSDA_ALIGN_CORNERS and
+ * computed, e.g. for fixed encoder reference points); attn_scale and
+ * grad_attn_scale are both NULL (no scale attention) or both given (else
+ * MSDA_ERR_NULL), and attn_scale must be the one given to the forward; every
+ * other pointer is required.  flags: MSDA_BWD_ACCUMULATE, MSDA_ALIGN_CORNERS and
  * MSDA_SOFTMAX_PER_LEVEL, the last two as given to the forward.
  * sampling_loc / attn_weight: both NULL (the locations and weights are
  * recomputed from the raw inputs into the workspace), or both the arrays
@@ -309,10 +321,11 @@ size_t msda_backward_fused_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int
 msda_status msda_backward_fused(const void *value, int value_dtype,
                                 const int64_t *spatial_shapes, const int64_t *level_start_index,
                                 const float *reference_points, const float *sampling_offsets,
-                                const float *attn_logits, const float *sampling_loc,
-                                const float *attn_weight, const float *grad_out,
-                                float *grad_value, float *grad_sampling_offsets,
-                                float *grad_attn_logits, float *grad_reference_points,
+                                const float *attn_logits, const float *attn_scale,
+                                const float *sampling_loc, const float *attn_weight,
+                                const float *grad_out, float *grad_value,
+                                float *grad_sampling_offsets, float *grad_attn_logits,
+                                float *grad_attn_scale, float *grad_reference_points,
                                 int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
                                 int64_t L, int64_t K, void *workspace, size_t workspace_bytes,
                                 uint32_t flags, void *stream, void *side_stream,

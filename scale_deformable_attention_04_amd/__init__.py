@@ -34,13 +34,15 @@ __all__ = ["forward", "backward", "backward_noalloc", "NOALLOC_SCRATCH_BYTES",
 class MSDeformAttnFunction(torch.autograd.Function):
     """out = core(value, level table, sampling_loc, attn_weight) with the
     library's backward.  grad_value comes back in fp32; autograd casts it to
-    value's dtype."""
+    value's dtype.  The level table is checked on the host only with
+    validate=True (a device-to-host copy); the kernels never touch memory
+    outside the tensors whatever it holds."""
 
     @staticmethod
     def forward(ctx, value, spatial_shapes, level_start_index, sampling_loc, attn_weight,
-                align_corners=False):
+                align_corners=False, validate=False):
         out = forward(value, spatial_shapes, level_start_index, sampling_loc, attn_weight,
-                      align_corners=align_corners)
+                      align_corners=align_corners, validate=validate)
         ctx.save_for_backward(value, spatial_shapes, level_start_index, sampling_loc,
                               attn_weight)
         ctx.align_corners = align_corners
@@ -51,63 +53,68 @@ class MSDeformAttnFunction(torch.autograd.Function):
         value, ss, st, loc, attn = ctx.saved_tensors
         gv, gl, ga = backward(value, ss, st, loc, attn, grad_out.contiguous(), validate=False,
                               align_corners=ctx.align_corners)
-        return gv, None, None, gl, ga, None
+        return gv, None, None, gl, ga, None, None
 
 
 def ms_deform_attn(value, spatial_shapes, level_start_index, sampling_loc, attn_weight,
-                   align_corners=False):
+                   align_corners=False, validate=False):
     return MSDeformAttnFunction.apply(value, spatial_shapes, level_start_index, sampling_loc,
-                                      attn_weight, align_corners)
+                                      attn_weight, align_corners, validate)
 
 
 class MSDeformAttnFusedFunction(torch.autograd.Function):
-    """out = core(value, level table, ref + offsets / (W_l, H_l), softmax(logits))
-    computed by the fused entry points; the backward returns the gradients of
-    value, reference_points, sampling_offsets and attn_logits."""
+    """out = core(value, level table, ref + offsets / (W_l, H_l), S * softmax(logits))
+    computed by the fused entry points (scale S optional); the backward
+    returns the gradients of value, reference_points, sampling_offsets,
+    attn_logits and scale."""
 
     @staticmethod
     def forward(ctx, value, spatial_shapes, level_start_index, reference_points,
-                sampling_offsets, attn_logits, per_level=False, align_corners=False):
+                sampling_offsets, attn_logits, per_level=False, align_corners=False,
+                scale=None, validate=False):
         # with a backward to come, the forward also stores the locations and
         # weights it forms, so the backward does not recompute them
         save = any(ctx.needs_input_grad)
         res = forward_fused(value, spatial_shapes, level_start_index, reference_points,
                             sampling_offsets, attn_logits, per_level=per_level,
-                            align_corners=align_corners, save=save)
+                            align_corners=align_corners, save=save, scale=scale,
+                            validate=validate)
         out, loc, attn = res if save else (res, None, None)
         ctx.save_for_backward(value, spatial_shapes, level_start_index, reference_points,
-                              sampling_offsets, attn_logits, loc, attn)
+                              sampling_offsets, attn_logits, loc, attn, scale)
         ctx.per_level = per_level
         ctx.align_corners = align_corners
         return out
 
     @staticmethod
     def backward(ctx, grad_out):
-        value, ss, st, ref, off, logits, loc, attn = ctx.saved_tensors
-        gv, goff, gz, gref = backward_fused(value, ss, st, ref, off, logits,
-                                            grad_out.contiguous(), validate=False,
-                                            need_grad_ref=ctx.needs_input_grad[3],
-                                            per_level=ctx.per_level,
-                                            align_corners=ctx.align_corners,
-                                            saved=None if loc is None else (loc, attn))
-        return gv, None, None, gref, goff, gz, None, None
+        value, ss, st, ref, off, logits, loc, attn, scale = ctx.saved_tensors
+        res = backward_fused(value, ss, st, ref, off, logits, grad_out.contiguous(),
+                             validate=False, need_grad_ref=ctx.needs_input_grad[3],
+                             per_level=ctx.per_level, align_corners=ctx.align_corners,
+                             saved=None if loc is None else (loc, attn), scale=scale)
+        gv, goff, gz, gref = res[:4]
+        gs = res[4] if scale is not None else None
+        return gv, None, None, gref, goff, gz, None, None, gs, None
 
 
 def ms_deform_attn_fused(value, spatial_shapes, level_start_index, reference_points,
-                         sampling_offsets, attn_logits, per_level=False, align_corners=False):
+                         sampling_offsets, attn_logits, per_level=False, align_corners=False,
+                         scale=None, validate=False):
     return MSDeformAttnFusedFunction.apply(value, spatial_shapes, level_start_index,
                                            reference_points, sampling_offsets, attn_logits,
-                                           per_level, align_corners)
+                                           per_level, align_corners, scale, validate)
 
 
 class MSDeformAttn3dFunction(torch.autograd.Function):
-    """The 3-D (trilinear) core with the library's backward."""
+    """The 3-D (trilinear) core with the library's backward (validate as for
+    MSDeformAttnFunction)."""
 
     @staticmethod
     def forward(ctx, value, volume_shapes, level_start_index, sampling_loc, attn_weight,
-                align_corners=False):
+                align_corners=False, validate=False):
         out = forward3d(value, volume_shapes, level_start_index, sampling_loc, attn_weight,
-                        align_corners=align_corners)
+                        align_corners=align_corners, validate=validate)
         ctx.save_for_backward(value, volume_shapes, level_start_index, sampling_loc, attn_weight)
         ctx.align_corners = align_corners
         return out
@@ -117,13 +124,13 @@ class MSDeformAttn3dFunction(torch.autograd.Function):
         value, ss, st, loc, attn = ctx.saved_tensors
         gv, gl, ga = backward3d(value, ss, st, loc, attn, grad_out.contiguous(), validate=False,
                                 align_corners=ctx.align_corners)
-        return gv, None, None, gl, ga, None
+        return gv, None, None, gl, ga, None, None
 
 
 def ms_deform_attn_3d(value, volume_shapes, level_start_index, sampling_loc, attn_weight,
-                      align_corners=False):
+                      align_corners=False, validate=False):
     return MSDeformAttn3dFunction.apply(value, volume_shapes, level_start_index, sampling_loc,
-                                        attn_weight, align_corners)
+                                        attn_weight, align_corners, validate)
 
 
 class DATSampleFunction(torch.autograd.Function):

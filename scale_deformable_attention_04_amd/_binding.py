@@ -77,11 +77,12 @@ def load():
     lib.msda_backward_events.restype = ci
     lib.msda_backward_workspace_size.argtypes = [i64] * 7
     lib.msda_backward_workspace_size.restype = ctypes.c_size_t
-    lib.msda_forward_fused.argtypes = [p, ci, p, p, p, p, p, p, p, p] + [i64] * 7 + [u32, p]
+    lib.msda_forward_fused.argtypes = [p, ci, p, p, p, p, p, p, p, p, p] + [i64] * 7 + [u32, p]
     lib.msda_forward_fused.restype = ci
     lib.msda_backward_fused_workspace_size.argtypes = [i64] * 7
     lib.msda_backward_fused_workspace_size.restype = ctypes.c_size_t
-    lib.msda_backward_fused.argtypes = ([p, ci, p, p, p, p, p, p, p, p, p, p, p, p] + [i64] * 7 +
+    lib.msda_backward_fused.argtypes = ([p, ci, p, p, p, p, p, p, p, p, p, p, p, p, p, p] +
+                                        [i64] * 7 +
                                         [p, ctypes.c_size_t, u32, p, p, p, p])
     lib.msda_backward_fused.restype = ci
     lib.msda3d_forward.argtypes = [p, ci, p, p, p, p, p] + [i64] * 7 + [u32, p]
@@ -388,7 +389,7 @@ def backward_noalloc(value: torch.Tensor, spatial_shapes: torch.Tensor,
 # fused prologue: reference points + pixel offsets + attention logits
 # ---------------------------------------------------------------------------
 def _check_fused_inputs(value, spatial_shapes, level_start_index, reference_points,
-                        sampling_offsets, attn_logits, validate):
+                        sampling_offsets, attn_logits, validate, scale=None):
     dev = value.device
     if dev.type != "cuda":
         raise ValueError(f"value must be a GPU tensor, got device {dev}")
@@ -400,6 +401,8 @@ def _check_fused_inputs(value, spatial_shapes, level_start_index, reference_poin
     _need(reference_points, "reference_points", torch.float32, dev, (B, Nq, L, 2))
     _need(sampling_offsets, "sampling_offsets", torch.float32, dev, (B, Nq, M, L, K, 2))
     _need(attn_logits, "attn_logits", torch.float32, dev, (B, Nq, M, L * K))
+    if scale is not None:
+        _need(scale, "scale", torch.float32, dev, (B, Nq, M, L, K))
     if validate:
         rc = validate_host(spatial_shapes, level_start_index, B, Nv, Nq, M, D, L, K)
         if rc != MSDA_OK:
@@ -417,17 +420,18 @@ def forward_fused(value: torch.Tensor, spatial_shapes: torch.Tensor,
                   sampling_offsets: torch.Tensor, attn_logits: torch.Tensor,
                   out: Optional[torch.Tensor] = None, validate: bool = True,
                   per_level: bool = False, align_corners: bool = False,
-                  save: bool = False):
+                  save: bool = False, scale: Optional[torch.Tensor] = None):
     """msda_forward_fused: out[B, Nq, M*D] (fp32) from reference points
     [B,Nq,L,2], pixel offsets [B,Nq,M,L,K,2] and logits [B,Nq,M,L*K].
     per_level=True normalizes the logits over each level's K points instead
-    of all L*K; align_corners as in forward().  save=True returns
-    (out, sampling_loc, attn_weight): the locations and weights it formed, to
-    pass to backward_fused(saved=...)."""
+    of all L*K; align_corners as in forward(); scale: an optional scale
+    attention S [B,Nq,M,L,K] multiplying the softmax weights.  save=True
+    returns (out, sampling_loc, attn_weight): the locations and weights it
+    formed, to pass to backward_fused(saved=...)."""
     lib = load()
     dev, (B, Nv, Nq, M, D, L, K) = _check_fused_inputs(
         value, spatial_shapes, level_start_index, reference_points, sampling_offsets,
-        attn_logits, validate)
+        attn_logits, validate, scale)
     if out is None:
         out = torch.empty((B, Nq, M * D), dtype=torch.float32, device=dev)
     else:
@@ -438,8 +442,8 @@ def forward_fused(value: torch.Tensor, spatial_shapes: torch.Tensor,
         stream = torch.cuda.current_stream(dev).cuda_stream
         rc = lib.msda_forward_fused(_ptr(value), _dtype_code(value), _ptr(spatial_shapes),
                                     _ptr(level_start_index), _ptr(reference_points),
-                                    _ptr(sampling_offsets), _ptr(attn_logits), _ptr(out),
-                                    _ptr(loc), _ptr(attn), B, Nv, Nq, M, D, L, K,
+                                    _ptr(sampling_offsets), _ptr(attn_logits), _ptr(scale),
+                                    _ptr(out), _ptr(loc), _ptr(attn), B, Nv, Nq, M, D, L, K,
                                     _fused_flags(per_level, align_corners),
                                     ctypes.c_void_p(stream))
     if rc != MSDA_OK:
@@ -460,9 +464,10 @@ def backward_fused(value: torch.Tensor, spatial_shapes: torch.Tensor,
                    validate: bool = True, workspace: Optional[torch.Tensor] = None,
                    events: Optional[list] = None, per_level: bool = False,
                    align_corners: bool = False, saved: Optional[tuple] = None,
-                   side_stream="auto"):
+                   side_stream="auto", scale: Optional[torch.Tensor] = None):
     """msda_backward_fused: (grad_value, grad_sampling_offsets, grad_attn_logits,
-    grad_reference_points or None when need_grad_ref is False).
+    grad_reference_points or None when need_grad_ref is False), and
+    grad_scale as a fifth element when scale (the forward's) is given.
     side_stream as for backward().
     saved: the (sampling_loc, attn_weight) forward_fused(save=True) returned
     for these inputs, or None to recompute them.
@@ -470,7 +475,7 @@ def backward_fused(value: torch.Tensor, spatial_shapes: torch.Tensor,
     lib = load()
     dev, (B, Nv, Nq, M, D, L, K) = _check_fused_inputs(
         value, spatial_shapes, level_start_index, reference_points, sampling_offsets,
-        attn_logits, validate)
+        attn_logits, validate, scale)
     _need(grad_out, "grad_out", torch.float32, dev, (B, Nq, M * D))
     if grad_value is None:
         if accumulate:
@@ -486,6 +491,7 @@ def backward_fused(value: torch.Tensor, spatial_shapes: torch.Tensor,
     g_off = torch.empty_like(sampling_offsets)
     g_logits = torch.empty_like(attn_logits)
     g_ref = torch.empty_like(reference_points) if need_grad_ref else None
+    g_scale = torch.empty_like(scale) if scale is not None else None
     flags = _fused_flags(per_level, align_corners) | (MSDA_BWD_ACCUMULATE if accumulate else 0)
     need = fused_workspace_size(B, Nv, Nq, M, D, L, K)
     if workspace is None:
@@ -499,12 +505,14 @@ def backward_fused(value: torch.Tensor, spatial_shapes: torch.Tensor,
         side, side_ev = _side_args(dev, side_stream)
         rc = lib.msda_backward_fused(
             _ptr(value), _dtype_code(value), _ptr(spatial_shapes), _ptr(level_start_index),
-            _ptr(reference_points), _ptr(sampling_offsets), _ptr(attn_logits), _ptr(s_loc),
-            _ptr(s_attn), _ptr(grad_out),
-            _ptr(grad_value), _ptr(g_off), _ptr(g_logits), _ptr(g_ref), B, Nv, Nq, M, D, L, K,
+            _ptr(reference_points), _ptr(sampling_offsets), _ptr(attn_logits), _ptr(scale),
+            _ptr(s_loc), _ptr(s_attn), _ptr(grad_out), _ptr(grad_value), _ptr(g_off),
+            _ptr(g_logits), _ptr(g_scale), _ptr(g_ref), B, Nv, Nq, M, D, L, K,
             _ptr(workspace), ws_bytes, flags, stream, side, side_ev, handles)
     if rc != MSDA_OK:
         raise MSDAError(rc, "msda_backward_fused")
+    if scale is not None:
+        return grad_value, g_off, g_logits, g_ref, g_scale
     return grad_value, g_off, g_logits, g_ref
 
 

@@ -77,11 +77,13 @@ static_assert(kSmallPixels % kThreads == 0, "each thread scans kSmallPixels / kT
 //   loc = ref[b, q, l] + off[b, q, m, l, k] / (W_l, H_l)   (fp32: one IEEE
 //         division and one addition per coordinate)
 //   A   = softmax of the logits over the L*K points of (b, q, m), or over the
-//         K points of each level when per_level is set.
+//         K points of each level when per_level is set, times the scale
+//         attention S of the point when one is given.
 struct Prologue {
     const float *ref;     // [B, Nq, L, 2]
     const float *off;     // [B, Nq, M, L, K, 2]
     const float *logits;  // [B, Nq, M, L * K]
+    const float *scale;   // [B, Nq, M, L, K] or nullptr (S = 1)
     int per_level;
     // the softmax groups are runs of a power-of-two number (<= 64) of
     // consecutive points that the point loop hands to consecutive lanes of one
@@ -231,6 +233,7 @@ msda_fwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
                     const float2 st = s_st[i1 * ng + (pr.per_level ? l : 0)];
                     A = expf(z - st.x) * st.y;
                 }
+                if (pr.scale) A *= pr.scale[p];
                 if (pr.loc_out) {
                     reinterpret_cast<float2 *>(pr.loc_out)[p] = uv;
                     pr.attn_out[p] = A;
@@ -287,13 +290,23 @@ msda_fwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
 // table holds the four row offsets (later overwritten by the four dot
 // products <grad_out row, value row>) and (fx, fy, A, valid bits).
 // ---------------------------------------------------------------------------
+// The fused prologue's scale attention in the softmax backward: the weight
+// the core used is A = S * P with P the softmax of the logits, so with
+// g = d/dA, d/dS = P g and d/dlogit = P (S g - sum over the group of P S g)
+// = A g - P sum(A g).  P is formed again from the logits.
+struct ScaleBwd {
+    const float *logits;  // [pts]
+    const float *scale;   // [pts], or nullptr: no scale attention
+    float *grad_scale;    // [pts]
+};
+
 template <int D, typename VT>
 __global__ void __launch_bounds__(kThreads)
 bwd_dots_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes,
                 const int64_t *__restrict__ starts, const float *__restrict__ loc,
                 const float *__restrict__ attn, const float *__restrict__ grad_out,
                 float *__restrict__ grad_loc, float *__restrict__ grad_attn,
-                float *__restrict__ ref_part, Dims dm) {
+                float *__restrict__ ref_part, ScaleBwd sb, Dims dm) {
     constexpr int G = D / 4;
     constexpr int IPB = kThreads / G;
     __shared__ LevelLds s_lv;
@@ -432,11 +445,19 @@ bwd_dots_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
             // Fused prologue, when the chunk holds whole items (runs of
             // consecutive lanes are the items' softmax groups and levels):
             // the logit gradient A * (grad_A - sum over the group of A * grad_A)
-            // replaces grad_A, and each level's sum of location gradients is
-            // stored per item for the reference-point gradient.
+            // replaces grad_A (with a scale attention, see ScaleBwd), and each
+            // level's sum of location gradients is stored per item for the
+            // reference-point gradient.
             if (dm.softmax_run) {
                 const float A = ax.z;
-                ga = A * (ga - run_sum(A * ga, dm.softmax_run));
+                const float t = run_sum(A * ga, dm.softmax_run);
+                if (sb.scale) {
+                    const float P = run_softmax(sb.logits[p], dm.softmax_run);
+                    sb.grad_scale[p] = P * ga;
+                    ga = A * ga - P * t;
+                } else {
+                    ga = A * (ga - t);
+                }
             }
             grad_attn[p] = ga;
             reinterpret_cast<float2 *>(grad_loc)[p] = make_float2(gx, gy);
@@ -645,7 +666,8 @@ bwd_small_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shape
 //    to the workspace for the backward pipeline (the same arithmetic as the
 //    fused forward).  Workgroup = kProItems consecutive items (b, q, m).
 // fused_epilogue_kernel: grad_logits = A * (grad_A - sum over the softmax
-//    group of A * grad_A), in place over grad_A; and, when asked for,
+//    group of A * grad_A), in place over grad_A (with a scale attention, see
+//    ScaleBwd: A g - P sum(A g), and grad_scale = P g); and, when asked for,
 //    grad_ref[b, q, l] = sum over heads and points of the location gradient
 //    (the offset gradient times (W_l, H_l)).
 // ---------------------------------------------------------------------------
@@ -681,12 +703,14 @@ fused_prologue_kernel(const int64_t *__restrict__ shapes, const int64_t *__restr
             reinterpret_cast<float2 *>(loc)[p] =
                 prologue_location(r, reinterpret_cast<const float2 *>(pr.off)[p], s_lv.lvl[l]);
             const float z = pr.logits[p];
+            float A;
             if (pr.shfl) {
-                attn[p] = run_softmax(z, pr.per_level ? K : LK);
+                A = run_softmax(z, pr.per_level ? K : LK);
             } else {
                 const float2 st = s_st[i1 * ng + (pr.per_level ? l : 0)];
-                attn[p] = expf(z - st.x) * st.y;
+                A = expf(z - st.x) * st.y;
             }
+            attn[p] = pr.scale ? A * pr.scale[p] : A;
         }
     }
 }
@@ -696,7 +720,7 @@ fused_epilogue_kernel(const int64_t *__restrict__ shapes, const int64_t *__restr
                       const float *__restrict__ attn, float *__restrict__ grad_logits,
                       const float *__restrict__ grad_off, const float *__restrict__ ref_part,
                       float *__restrict__ grad_ref, int per_level, int shfl, int64_t groups,
-                      int64_t refs, Dims dm) {
+                      int64_t refs, ScaleBwd sb, Dims dm) {
     __shared__ LevelLds s_lv;
     stage_levels(&s_lv, shapes, starts, dm.L, dm.Nv, 0x7fffffff);
     const int M = dm.M, K = dm.K, L = dm.L, LK = L * K;
@@ -727,15 +751,31 @@ fused_epilogue_kernel(const int64_t *__restrict__ shapes, const int64_t *__restr
         for (int64_t p = t0; p < n; p += stride) {
             const float a = attn[p], ga = grad_logits[p];
             const float s = run_sum(a * ga, gs);
-            grad_logits[p] = a * (ga - s);
+            if (sb.scale) {
+                const float P = run_softmax(sb.logits[p], gs);
+                sb.grad_scale[p] = P * ga;
+                grad_logits[p] = a * ga - P * s;
+            } else {
+                grad_logits[p] = a * (ga - s);
+            }
         }
     } else {
         for (int64_t u = t0; u < groups; u += stride) {
             const size_t p0 = (size_t)u * gs;  // the groups tile the points in order
             float s = 0.f;
             for (int j = 0; j < gs; ++j) s = __builtin_fmaf(attn[p0 + j], grad_logits[p0 + j], s);
-            for (int j = 0; j < gs; ++j)
-                grad_logits[p0 + j] = attn[p0 + j] * (grad_logits[p0 + j] - s);
+            if (sb.scale) {
+                const float2 st = softmax_stats(sb.logits + p0, gs);
+                for (int j = 0; j < gs; ++j) {
+                    const float P = expf(sb.logits[p0 + j] - st.x) * st.y;
+                    const float ga = grad_logits[p0 + j];
+                    sb.grad_scale[p0 + j] = P * ga;
+                    grad_logits[p0 + j] = attn[p0 + j] * ga - P * s;
+                }
+            } else {
+                for (int j = 0; j < gs; ++j)
+                    grad_logits[p0 + j] = attn[p0 + j] * (grad_logits[p0 + j] - s);
+            }
         }
     }
     if (!grad_ref) return;
@@ -848,7 +888,7 @@ msda_status launch_fwd(const void *value, const int64_t *shapes, const int64_t *
     const int64_t ipb1 = kThreads / (D / 4);
     const int split = (kSplit > 1 && B * M * ((Nq + ipb1 - 1) / ipb1) < 512) ? kSplit : 1;
     const int ipb = (int)(ipb1 / split);
-    Prologue prv = pr ? *pr : Prologue{nullptr, nullptr, nullptr, 0, 0, nullptr, nullptr};
+    Prologue prv = pr ? *pr : Prologue{nullptr, nullptr, nullptr, nullptr, 0, 0, nullptr, nullptr};
     int st_bytes = 0;
     Launch p = fwd_plan(D, L, K, 0, split);
     if (pr) {
@@ -896,6 +936,7 @@ struct FusedBwd {
     int softmax_run;  // requested run length (0: the runs do not fit lane shuffles)
     float *ref_part;  // nullptr: no reference-point gradient wanted
     bool in_dots;     // set by the launch: the dots kernel did both
+    ScaleBwd scale;   // the scale attention (scale.scale == nullptr: none)
 };
 
 
@@ -914,6 +955,7 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
     // point table holds whole items and the softmax runs fit a wave
     if (fz) fz->in_dots = fz->softmax_run > 0 && p.pc == L * K;
     float *ref_part = fz && fz->in_dots ? fz->ref_part : nullptr;
+    const ScaleBwd sb = fz && fz->in_dots ? fz->scale : ScaleBwd{nullptr, nullptr, nullptr};
     ex.stamp(kStageDots, false, ds);
     msda_status st = per_batch(B, gq * M, [&](int64_t b0, unsigned grid) {
         Dims d2{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, p.pc, p.ps, (int)b0, (int)gq, 0, 0};
@@ -926,7 +968,7 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
         const unsigned g = grid > (unsigned)kDotsGrid ? (unsigned)kDotsGrid : grid;
         hipLaunchKernelGGL((bwd_dots_kernel<D, VT>), dim3(g), dim3(kThreads), p.lds, ds,
                            static_cast<const VT *>(value), shapes, starts, loc, attn, gout, gloc,
-                           gattn, ref_part, d2);
+                           gattn, ref_part, sb, d2);
     });
     if (st != MSDA_OK) return st;
     ex.stamp(kStageDots, true, ds);
@@ -1053,7 +1095,8 @@ msda_status msda_forward(const void *value, int value_dtype, const int64_t *spat
 msda_status msda_forward_fused(const void *value, int value_dtype,
                                const int64_t *spatial_shapes, const int64_t *level_start_index,
                                const float *reference_points, const float *sampling_offsets,
-                               const float *attn_logits, float *out, float *sampling_loc_out,
+                               const float *attn_logits, const float *attn_scale, float *out,
+                               float *sampling_loc_out,
                                float *attn_weight_out, int64_t B, int64_t Nv, int64_t Nq,
                                int64_t M, int64_t D, int64_t L, int64_t K, uint32_t flags,
                                void *stream) {
@@ -1067,7 +1110,7 @@ msda_status msda_forward_fused(const void *value, int value_dtype,
         !sampling_offsets || !attn_logits || !out)
         return MSDA_ERR_NULL;
     if ((sampling_loc_out == nullptr) != (attn_weight_out == nullptr)) return MSDA_ERR_NULL;
-    const Prologue pr{reference_points, sampling_offsets, attn_logits,
+    const Prologue pr{reference_points, sampling_offsets, attn_logits, attn_scale,
                       (flags & MSDA_SOFTMAX_PER_LEVEL) ? 1 : 0, 0, sampling_loc_out,
                       attn_weight_out};
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1190,9 +1233,10 @@ FusedLayout fused_layout(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t L
 
 msda_status backward_fused_impl(const void *value, int value_dtype, const int64_t *shapes,
                                 const int64_t *starts, const float *ref, const float *off,
-                                const float *logits, const float *saved_loc,
+                                const float *logits, const float *scale, const float *saved_loc,
                                 const float *saved_attn, const float *grad_out, float *grad_value,
-                                float *grad_off, float *grad_logits, float *grad_ref, int64_t B,
+                                float *grad_off, float *grad_logits, float *grad_scale,
+                                float *grad_ref, int64_t B,
                                 int64_t Nv, int64_t Nq, int64_t M, int64_t D, int64_t L,
                                 int64_t K, void *workspace, size_t workspace_bytes,
                                 uint32_t flags, hipStream_t s, void *side_stream,
@@ -1210,7 +1254,7 @@ msda_status backward_fused_impl(const void *value, int value_dtype, const int64_
     if (!work) {
         stamp(MSDA_BWD_STAGES, false);
         stamp(MSDA_BWD_STAGES, true);
-        FusedBwd none{0, nullptr, false};
+        FusedBwd none{0, nullptr, false, ScaleBwd{nullptr, nullptr, nullptr}};
         st = backward_impl(value, value_dtype, shapes, starts, nullptr, nullptr, grad_out,
                            grad_value, nullptr, nullptr, B, Nv, Nq, M, D, L, K, workspace,
                            workspace_bytes, core_flags, &none, s, side_stream, side_events, ev);
@@ -1223,6 +1267,7 @@ msda_status backward_fused_impl(const void *value, int value_dtype, const int64_
         !grad_off || !grad_logits)
         return MSDA_ERR_NULL;
     if ((saved_loc == nullptr) != (saved_attn == nullptr)) return MSDA_ERR_NULL;
+    if ((scale == nullptr) != (grad_scale == nullptr)) return MSDA_ERR_NULL;
     if (!workspace) return MSDA_ERR_NULL;
     const FusedLayout fl = fused_layout(B, Nv, Nq, M, L, K);
     if (workspace_bytes < fl.bytes) return MSDA_ERR_WORKSPACE;
@@ -1232,7 +1277,7 @@ msda_status backward_fused_impl(const void *value, int value_dtype, const int64_
     float *loc = reinterpret_cast<float *>(ws + fl.off_loc);
     float *attn = reinterpret_cast<float *>(ws + fl.off_attn);
     const int shfl = pow2_run(per_level ? K : L * K) ? 1 : 0;
-    const Prologue pr{ref, off, logits, per_level ? 1 : 0, shfl, nullptr, nullptr};
+    const Prologue pr{ref, off, logits, scale, per_level ? 1 : 0, shfl, nullptr, nullptr};
     Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, 0, 0, 0, 0, 0, 0};
     const int64_t items = B * Nq * M;
 
@@ -1249,7 +1294,8 @@ msda_status backward_fused_impl(const void *value, int value_dtype, const int64_
     stamp(MSDA_BWD_STAGES, true);
 
     FusedBwd fz{shfl ? (int)(per_level ? K : L * K) : 0,
-                grad_ref ? reinterpret_cast<float *>(ws + fl.off_part) : nullptr, false};
+                grad_ref ? reinterpret_cast<float *>(ws + fl.off_part) : nullptr, false,
+                ScaleBwd{logits, scale, grad_scale}};
     const float *use_loc = saved ? saved_loc : loc, *use_attn = saved ? saved_attn : attn;
     st = backward_impl(value, value_dtype, shapes, starts, use_loc, use_attn, grad_out,
                        grad_value, grad_off, grad_logits, B, Nv, Nq, M, D, L, K, ws, fl.core,
@@ -1264,7 +1310,8 @@ msda_status backward_fused_impl(const void *value, int value_dtype, const int64_
             blocks = blocks < (1 << 16) ? blocks : (1 << 16);
             hipLaunchKernelGGL(fused_epilogue_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
                                s, shapes, starts, use_attn, grad_logits, grad_off, fz.ref_part,
-                               grad_ref, per_level ? 1 : 0, shfl, (int64_t)0, refs, dm);
+                               grad_ref, per_level ? 1 : 0, shfl, (int64_t)0, refs,
+                               ScaleBwd{nullptr, nullptr, nullptr}, dm);
             st = hip_status(hipGetLastError());
         }
     } else {
@@ -1277,7 +1324,7 @@ msda_status backward_fused_impl(const void *value, int value_dtype, const int64_
         blocks = blocks < (1 << 16) ? blocks : (1 << 16);
         hipLaunchKernelGGL(fused_epilogue_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s,
                            shapes, starts, use_attn, grad_logits, grad_off, nullptr, grad_ref,
-                           per_level ? 1 : 0, shfl, groups, refs, dm);
+                           per_level ? 1 : 0, shfl, groups, refs, fz.scale, dm);
         st = hip_status(hipGetLastError());
     }
     stamp(MSDA_BWD_STAGES + 1, true);
@@ -1364,10 +1411,11 @@ size_t msda_backward_fused_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int
 msda_status msda_backward_fused(const void *value, int value_dtype,
                                 const int64_t *spatial_shapes, const int64_t *level_start_index,
                                 const float *reference_points, const float *sampling_offsets,
-                                const float *attn_logits, const float *sampling_loc,
-                                const float *attn_weight, const float *grad_out,
-                                float *grad_value, float *grad_sampling_offsets,
-                                float *grad_attn_logits, float *grad_reference_points, int64_t B,
+                                const float *attn_logits, const float *attn_scale,
+                                const float *sampling_loc, const float *attn_weight,
+                                const float *grad_out, float *grad_value,
+                                float *grad_sampling_offsets, float *grad_attn_logits,
+                                float *grad_attn_scale, float *grad_reference_points, int64_t B,
                                 int64_t Nv, int64_t Nq, int64_t M, int64_t D, int64_t L,
                                 int64_t K, void *workspace, size_t workspace_bytes,
                                 uint32_t flags, void *stream, void *side_stream,
@@ -1377,9 +1425,9 @@ msda_status msda_backward_fused(const void *value, int value_dtype,
         for (int i = 0; i < 2 * MSDA_BWD_FUSED_STAGES; ++i)
             ev[i] = static_cast<hipEvent_t>(events[i]);
     return backward_fused_impl(value, value_dtype, spatial_shapes, level_start_index,
-                               reference_points, sampling_offsets, attn_logits, sampling_loc,
-                               attn_weight, grad_out,
-                               grad_value, grad_sampling_offsets, grad_attn_logits,
+                               reference_points, sampling_offsets, attn_logits, attn_scale,
+                               sampling_loc, attn_weight, grad_out, grad_value,
+                               grad_sampling_offsets, grad_attn_logits, grad_attn_scale,
                                grad_reference_points, B, Nv, Nq, M, D, L, K, workspace,
                                workspace_bytes, flags, static_cast<hipStream_t>(stream),
                                side_stream, side_events, events ? ev : nullptr);

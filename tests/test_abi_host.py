@@ -136,7 +136,7 @@ def test_backward_workspace_checks():
 def test_forward_fused_rejects_before_launch():
     lib = msda.load()
     z = ctypes.c_void_p(0)
-    fwd = lambda dt, *dims, flags=0: lib.msda_forward_fused(z, dt, z, z, z, z, z, z, z, z,
+    fwd = lambda dt, *dims, flags=0: lib.msda_forward_fused(z, dt, z, z, z, z, z, z, z, z, z,
                                                             *dims, flags, z)
     assert fwd(7, 1, 80, 16, 2, 8, 2, 2) == B_.MSDA_ERR_DTYPE
     assert fwd(0, 1, 80, 16, 2, 12, 2, 2) == B_.MSDA_ERR_UNSUPPORTED
@@ -147,7 +147,7 @@ def test_forward_fused_rejects_before_launch():
     assert fwd(0, 1, 80, 16, 2, 8, 2, 2, flags=B_.MSDA_BWD_ACCUMULATE) == B_.MSDA_ERR_UNSUPPORTED
     # the stored locations and weights come as a pair
     fake = ctypes.c_void_p(1 << 20)
-    assert lib.msda_forward_fused(fake, 0, fake, fake, fake, fake, fake, fake, fake, z,
+    assert lib.msda_forward_fused(fake, 0, fake, fake, fake, fake, fake, z, fake, fake, z,
                                   1, 80, 16, 2, 8, 2, 2, 0, z) == B_.MSDA_ERR_NULL
     # the plain forward does not take the softmax flag
     assert lib.msda_forward(z, 0, z, z, z, z, z, 0, 80, 16, 2, 8, 2, 2,
@@ -158,9 +158,9 @@ def test_backward_fused_rejects_before_launch():
     lib = msda.load()
     z = ctypes.c_void_p(0)
     fake = ctypes.c_void_p(1 << 20)   # never dereferenced: the checks fail first
-    bwd = lambda dt, flags, *dims, ws=z, nbytes=0, ref=fake, gref=fake, sl=z, sa=z: \
-        lib.msda_backward_fused(fake, dt, fake, fake, ref, fake, fake, sl, sa, fake, fake, fake,
-                                fake, gref, *dims, ws, nbytes, flags, z, z, None, None)
+    bwd = lambda dt, flags, *dims, ws=z, nbytes=0, ref=fake, gref=fake, sl=z, sa=z, sc=z, gsc=z: \
+        lib.msda_backward_fused(fake, dt, fake, fake, ref, fake, fake, sc, sl, sa, fake, fake,
+                                fake, fake, gsc, gref, *dims, ws, nbytes, flags, z, z, None, None)
     dims = (1, 80, 16, 2, 8, 2, 2)
     need = lib.msda_backward_fused_workspace_size(*dims)
     core = lib.msda_backward_workspace_size(*dims)
@@ -172,6 +172,9 @@ def test_backward_fused_rejects_before_launch():
     assert bwd(0, 0, *dims, ws=fake, nbytes=need, ref=z) == B_.MSDA_ERR_NULL
     assert bwd(0, 0, *dims) == B_.MSDA_ERR_NULL                      # no workspace
     assert bwd(0, 0, *dims, ws=fake, nbytes=need, sl=fake) == B_.MSDA_ERR_NULL  # half a pair
+    # the scale attention and its gradient come as a pair
+    assert bwd(0, 0, *dims, ws=fake, nbytes=need, sc=fake) == B_.MSDA_ERR_NULL
+    assert bwd(0, 0, *dims, ws=fake, nbytes=need, gsc=fake) == B_.MSDA_ERR_NULL
     assert bwd(0, 0, *dims, ws=fake, nbytes=need - 1) == B_.MSDA_ERR_WORKSPACE
     assert bwd(0, 0, *dims, ws=ctypes.c_void_p((1 << 20) + 8), nbytes=need) == B_.MSDA_ERR_WORKSPACE
     # B = 0: nothing to do at all

@@ -52,23 +52,36 @@ def _oracle_args(w):
             w.sampling_offsets, w.attn_logits)
 
 
-def check(m, w, per_level=False, align=False, bf16=False, backward=True, need_grad_ref=True):
+def check(m, w, per_level=False, align=False, bf16=False, backward=True, need_grad_ref=True,
+          saved=False):
+    """Forward and backward against the oracle; with w.attn_scale set, the
+    scale attention and its gradient too; saved=True hands the forward's
+    locations and weights to the backward."""
     x = dev_inputs(w, bf16)
-    out = m.forward_fused(**x, per_level=per_level, align_corners=align)
+    S = w.attn_scale
+    sx = {} if S is None else {"scale": torch.from_numpy(S).cuda()}
+    res = m.forward_fused(**x, per_level=per_level, align_corners=align, save=saved, **sx)
+    out = res[0] if saved else res
     torch.cuda.synchronize()
-    r_out = ofused.forward(*_oracle_args(w), per_level=per_level, mode=_mode(align))
+    r_out = ofused.forward(*_oracle_args(w), per_level=per_level, mode=_mode(align), scale=S)
     e = max_rel(out.cpu().numpy(), r_out.reshape(out.shape))
     assert e <= FWD_TOL, f"{w.name}: fused forward max rel {e:.3e}"
     if not backward:
         return
     g = torch.from_numpy(w.grad_out).cuda()
-    gv, goff, gz, gref = m.backward_fused(**x, grad_out=g, per_level=per_level,
-                                          align_corners=align, need_grad_ref=need_grad_ref)
+    res = m.backward_fused(**x, grad_out=g, per_level=per_level, align_corners=align,
+                           need_grad_ref=need_grad_ref, saved=tuple(res[1:]) if saved else None,
+                           **sx)
     torch.cuda.synchronize()
-    rv, roff, rz, rref = ofused.backward(*_oracle_args(w), w.grad_out, per_level=per_level,
-                                         mode=_mode(align))
+    ref = ofused.backward(*_oracle_args(w), w.grad_out, per_level=per_level, mode=_mode(align),
+                          scale=S)
+    assert len(res) == len(ref)
+    gv, goff, gz, gref = res[:4]
+    rv, roff, rz, rref = ref[:4]
     got = [("grad_value", gv, rv), ("grad_sampling_offsets", goff, roff),
            ("grad_attn_logits", gz, rz)]
+    if S is not None:
+        got.append(("grad_scale", res[4], ref[4]))
     if need_grad_ref:
         got.append(("grad_reference_points", gref, rref))
     else:
@@ -233,3 +246,56 @@ def test_fused_train_bf16_per_level(msda):
     _say("fused train_bf16 B=4 K=8 per_level")
     w = workloads.make_fused(4)
     check(msda, w, per_level=True, bf16=True)
+
+
+# ---------------------------------------------------------------------------
+# the scale attention S of the multi-scale formula (weights S * softmax)
+# ---------------------------------------------------------------------------
+# softmax groups of 16 or 32 points are finished in the dots kernel (lane
+# shuffles); groups of 9 or 15 points, and items whose points span several
+# table chunks (L*K = 64 at D = 64), in the epilogue kernel
+@pytest.mark.parametrize("D,L,K", [(16, 4, 4), (32, 4, 8), (32, 3, 3), (8, 3, 5), (64, 2, 32)])
+@pytest.mark.parametrize("per_level", [False, True])
+def test_fused_scale_attention(msda, D, L, K, per_level):
+    _say(f"fused scale attention D={D} L={L} K={K} per_level={per_level}")
+    shapes = ((11, 13), (6, 5), (4, 3), (2, 2))[:L]
+    w = workloads.fused_case(1100 + D + 7 * L + K, 2, shapes, 33, 3, D, K, ref_low=-0.05,
+                             ref_high=1.05, with_scale=True)
+    check(msda, w, per_level=per_level)
+
+
+@pytest.mark.parametrize("per_level,align,bf16", [(False, False, False), (True, True, True)])
+def test_fused_scale_saved_and_conventions(msda, per_level, align, bf16):
+    _say(f"fused scale saved per_level={per_level} align={align} bf16={bf16}")
+    w = workloads.fused_case(1201, 2, SHAPES, 41, 4, 32, 4, with_scale=True, bf16=bf16)
+    check(msda, w, per_level=per_level, align=align, bf16=bf16, saved=True)
+    check(msda, w, per_level=per_level, align=align, bf16=bf16, need_grad_ref=False)
+
+
+def test_fused_scale_encoder(msda):
+    # the encoder-shape workload with a scale attention, forward and backward
+    _say("fused scale encoder B=2 Nq=Nv=22223")
+    check(msda, workloads.make_fused(3, with_scale=True), saved=True)
+
+
+def test_fused_scale_autograd(msda):
+    _say("fused scale autograd")
+    w = workloads.fused_case(1301, 2, SHAPES, 19, 2, 16, 4, with_scale=True)
+    x = dev_inputs(w)
+    leaves = {k: x[k].clone().requires_grad_(True)
+              for k in ("value", "reference_points", "sampling_offsets", "attn_logits")}
+    S = torch.from_numpy(w.attn_scale).cuda().requires_grad_(True)
+    out = msda.ms_deform_attn_fused(leaves["value"], x["spatial_shapes"], x["level_start_index"],
+                                    leaves["reference_points"], leaves["sampling_offsets"],
+                                    leaves["attn_logits"], scale=S)
+    out.backward(torch.from_numpy(w.grad_out).cuda())
+    rv, roff, rz, rref, rs = ofused.backward(*_oracle_args(w), w.grad_out, scale=w.attn_scale)
+    r_out = ofused.forward(*_oracle_args(w), scale=w.attn_scale)
+    assert max_rel(out.detach().cpu().numpy(), r_out.reshape(out.shape)) <= FWD_TOL
+    for name, t, r in (("value", leaves["value"].grad, rv),
+                       ("sampling_offsets", leaves["sampling_offsets"].grad, roff),
+                       ("attn_logits", leaves["attn_logits"].grad, rz),
+                       ("reference_points", leaves["reference_points"].grad, rref),
+                       ("scale", S.grad, rs)):
+        e = max_rel(t.cpu().numpy(), r)
+        assert e <= BWD_TOL, f"{name}: {e:.3e}"
