@@ -3,10 +3,11 @@
 
 A step is one pass of the whole hot path over one batch: the forward
 (msda_forward) and the backward (msda_backward: grad_attn/grad_loc kernel
-beside the grad_value pipeline) at the Deformable-DETR encoder shape -- B=2, four levels 100x167,
-50x84, 25x42, 13x21 (Nv = 22,223), every pixel a query (Nq = Nv), M=8 heads,
-D=32, K=4, fp32.  Inputs are seeded synthetic data (workloads.make) resident
-in HBM before the timed region.
+beside the grad_value pipeline) at the Deformable-DETR encoder shape -- B=2,
+four levels 100x167, 50x84, 25x42, 13x21 (Nv = 22,223), every pixel a query
+(Nq = Nv), M=8 heads, D=32, K=4, fp32.  Inputs are seeded synthetic data
+(workloads.make) resident in HBM before the timed region; their SHA-256s are
+in the line.
 
 Printed: one JSON line.  value = sampled points (B*Nq*M*L*K) per second of
 fwd+bwd steps, timed with HIP events over `--steps` back-to-back steps.
@@ -19,12 +20,17 @@ stream in every step (an event record costs the stream a few microseconds);
 its algorithmic bytes (each tensor it must touch read or written once) over
 its average duration there give "achieved", against the 8 TB/s HBM peak.
 "traffic" is the HBM byte count rocprofv3 measured for that kernel
-(profiles/traffic.json), when it was taken on the current 2-D kernel sources.
-"cpu_baseline" times the CPU oracle on the same workload on this host's
-cores.  --extra adds the decoder and bf16 training shapes and the fused
-prologue (reference points + pixel offsets + logits) at the encoder shape,
-the 3-D trilinear variant on a voxel workload, and DAT's sampled-key
-attention (sampling and MFMA attention) at its two configurations.
+(profiles/traffic.json) and "counters" its L2 hit rate and atomic requests
+(profiles/counters.json), each when taken on the current 2-D kernel sources.
+"roofline.forward" places the forward against both of its ceilings: the HBM
+roofline (cold and warm) and the row-gather rate of the vector memory path,
+measured here by the probe kernel of libmsda_probe.so ("gather_ceiling").
+"stream_copy" is a streaming 16-byte copy, the achievable HBM bandwidth.
+"decoder" and "train_bf16" are the other two configurations (forward and
+backward each).  "cpu_baseline" times the CPU oracle on this host's cores
+and on one core.  --extra adds the fused prologue at the encoder shape, the
+3-D trilinear variant on a voxel workload, and DAT's sampled-key attention
+(sampling and MFMA attention) at its two configurations.
 """
 from __future__ import annotations
 
@@ -44,11 +50,13 @@ HBM_PEAK_GBS = 8000.0
 FLUSH_BYTES = 512 << 20   # > the 256 MB Infinity Cache
 CSRC = os.path.join(ROOT, "scale_deformable_attention_04_amd", "csrc")
 KERNEL_SOURCES = [os.path.join(CSRC, f)
-                  for f in ("common.h", "bins.h", "msda.hip", "msda3d.hip", "dat_attn.hip")]
+                  for f in ("common.h", "bins.h", "msda.hip", "msda3d.hip", "dat_attn.hip",
+                            "probe.hip")]
 # the sources the 2-D kernels are built from: the traffic counters of
 # profiles/traffic.json hold while these are unchanged
 ENCODER_SOURCES = [os.path.join(CSRC, f) for f in ("common.h", "bins.h", "msda.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
 
 # kernel names as rocprofv3 reports them, per stage of a step
 KERNELS = {
@@ -336,36 +344,184 @@ def measure_dat(torch, msda, reps, flush):
     return res
 
 
-def cpu_baseline(w, min_seconds=10.0):
+def cpu_info() -> dict:
+    """The host the oracle runs on: model name, logical CPUs, the CPUs this
+    process may use, and OMP_NUM_THREADS as set."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = None
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "usable_cpus": usable,
+            "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
+
+
+def _time_oracle(w, threads, min_seconds, max_runs):
     import oracle
-    pts = w.points
     args = (w.value, w.spatial_shapes, w.level_start_index, w.sampling_loc, w.attn_weight)
     times = []
     t_start = time.perf_counter()
-    while len(times) < 2 or (time.perf_counter() - t_start < min_seconds and len(times) < 10):
+    while len(times) < 2 or (time.perf_counter() - t_start < min_seconds and len(times) < max_runs):
         t0 = time.perf_counter()
-        oracle.forward(*args)
-        oracle.backward(*args, w.grad_out)
+        oracle.forward(*args, threads=threads)
+        oracle.backward(*args, w.grad_out, threads=threads)
         times.append(time.perf_counter() - t0)
-    med = statistics.median(times)
-    return {"value": pts / med, "unit": "points/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
+    return statistics.median(times), len(times)
+
+
+def cpu_baseline(w, min_seconds=10.0):
+    """The oracle (fp64 accumulation, OpenMP over independent outputs) on the
+    whole encoder workload, forward + backward: on every core this process
+    may use, then on one core."""
+    import oracle
+    pts = w.points
+    med, n = _time_oracle(w, 0, min_seconds, 10)
+    cores = oracle.max_threads()
+    med1, n1 = _time_oracle(w, 1, 0.0, 2)
+    return {"value": pts / med, "unit": "points/s", "cores": cores, "kind": "oracle",
             "sample": f"the whole encoder workload ({pts} points), forward + backward, "
-                      f"{len(times)} runs, median {med:.2f} s per step, fp64 accumulation"}
+                      f"{n} runs, median {med:.2f} s per step, fp64 accumulation",
+            "single_core": {"value": pts / med1, "unit": "points/s", "cores": 1,
+                            "sample": f"the same, {n1} runs on one thread, median "
+                                      f"{med1:.2f} s per step"},
+            **cpu_info()}
 
 
-def traffic_for(kernel_name: str):
-    """HBM bytes per launch measured by rocprofv3 for this kernel on this source."""
+# ---------------------------------------------------------------------------
+# ceilings: the row-gather rate and a streaming copy (libmsda_probe.so)
+# ---------------------------------------------------------------------------
+PROBE_GRID = 2048      # workgroups of 256 lanes per probe launch
+PROBE_ITERS = 256      # rows per lane group per launch
+
+
+def probe_lib():
+    import ctypes
+    import scale_deformable_attention_04_amd.build as b
+    lib = ctypes.CDLL(b.PROBE_LIB)
+    p, u32, u64 = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint64
+    lib.msda_probe_row_gather.argtypes = [p, u32, u32, u32, u32, u32, u32, p, p]
+    lib.msda_probe_row_gather.restype = ctypes.c_int
+    lib.msda_probe_copy.argtypes = [p, p, u64, p]
+    lib.msda_probe_copy.restype = ctypes.c_int
+    return lib
+
+
+def _time_launches(torch, launch, reps):
+    s = torch.cuda.current_stream()
+    for _ in range(2):
+        launch()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(reps):
+        launch()
+    e1.record(s)
+    e1.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps  # us per launch
+
+
+def gather_ceiling(torch, reps=10):
+    """Rows per second the chip gathers with the sampling kernels' access
+    pattern (lane groups reading whole pseudo-random rows, 16 or 8 bytes per
+    lane, four rows in flight), from buffers resident in L1 (16 KiB), in one
+    XCD's L2 (2 MiB), in the Infinity Cache (64 MiB) and beyond it (1 GiB)."""
+    import ctypes
+    lib = probe_lib()
+    dev = torch.device("cuda")
+    sink = torch.empty(PROBE_GRID * 256, dtype=torch.int32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    out = {"method": f"{PROBE_GRID} workgroups x 256 lanes, {PROBE_ITERS} rows per lane group "
+                     "per launch, 4 rows in flight, buffer-load instructions as in the kernels"}
+    cases = (("rows_128B_16B_lanes", 128, 16, ("16KiB", "2MiB", "64MiB", "1GiB")),
+             ("rows_64B_8B_lanes", 64, 8, ("2MiB",)))
+    size = {"16KiB": 16 << 10, "2MiB": 2 << 20, "64MiB": 64 << 20, "1GiB": 1 << 30}
+    for name, row_bytes, lane_bytes, bufs in cases:
+        res = {}
+        for b in bufs:
+            buf = torch.randint(0, 1 << 30, (size[b] // 4,), dtype=torch.int32, device=dev)
+            rows = size[b] // row_bytes
+            groups = PROBE_GRID * 256 // (row_bytes // lane_bytes)
+
+            def launch():
+                rc = lib.msda_probe_row_gather(ctypes.c_void_p(buf.data_ptr()), rows, row_bytes,
+                                               lane_bytes, PROBE_ITERS, PROBE_GRID, 12345,
+                                               ctypes.c_void_p(sink.data_ptr()), stream)
+                if rc != 0:
+                    raise RuntimeError(f"msda_probe_row_gather: hipError_t {rc}")
+            us = _time_launches(torch, launch, reps)
+            rate = groups * PROBE_ITERS / us * 1e6
+            res[b] = {"rows_per_s": rate, "bytes_per_s": rate * row_bytes, "us_per_launch": us}
+            del buf
+        out[name] = res
+    log(f"gather ceiling: {json.dumps(out)}")
+    return out
+
+
+def stream_copy(torch, nbytes=1 << 30, reps=10):
+    """A streaming copy of nbytes with 16-byte loads and stores: bytes read +
+    written per second, the achievable counterpart of the 8 TB/s peak."""
+    import ctypes
+    lib = probe_lib()
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def launch():
+        rc = lib.msda_probe_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                 nbytes, stream)
+        if rc != 0:
+            raise RuntimeError(f"msda_probe_copy: hipError_t {rc}")
+    us = _time_launches(torch, launch, reps)
+    res = {"bytes_per_copy": 2 * nbytes, "us": us, "GBps": 2 * nbytes / us / 1e3,
+           "frac_of_peak": 2 * nbytes / us / 1e3 / HBM_PEAK_GBS}
+    log(f"stream copy: {json.dumps(res)}")
+    return res
+
+
+def forward_roofline(enc_fwd, pts, ceiling):
+    """The forward against the HBM roofline (cold and warm) and against the
+    L2-resident row-gather ceiling: it must gather 4 rows per point."""
+    rows = 4 * pts
+    rate = ceiling["rows_128B_16B_lanes"]["2MiB"]["rows_per_s"]
+    ceil_us = rows / rate * 1e6
+    b = enc_fwd["algorithmic_bytes"]
+    cold, warm = enc_fwd["us_cold"], enc_fwd["us_warm"]
+    return {"kernel": KERNELS["forward"], "algorithmic_bytes": b, "us_cold": cold,
+            "us_warm": warm, "hbm_frac_cold": b / cold / 1e3 / HBM_PEAK_GBS,
+            "hbm_frac_warm": b / warm / 1e3 / HBM_PEAK_GBS, "rows_gathered": rows,
+            "rows_per_s_warm": rows / warm * 1e6, "gather_ceiling_rows_per_s": rate,
+            "gather_ceiling_us": ceil_us, "frac_of_gather_ceiling_warm": ceil_us / warm,
+            "frac_of_gather_ceiling_cold": ceil_us / cold,
+            "hbm_frac_at_gather_ceiling": b / ceil_us / 1e3 / HBM_PEAK_GBS}
+
+
+def _profile_for(path, kernel_name):
+    """The entry of a profiles/ summary for this kernel, when it was taken on
+    the current 2-D kernel sources."""
     try:
-        t = json.load(open(TRAFFIC_FILE))
+        t = json.load(open(path))
     except (OSError, ValueError):
         return None
     if t.get("source_sha") != source_sha(ENCODER_SOURCES):
         return None
-    k = t.get("kernels", {}).get(kernel_name)
-    if not k:
-        return None
-    return int(k["fetch_bytes"] + k["write_bytes"])
+    return t.get("kernels", {}).get(kernel_name)
+
+
+def traffic_for(kernel_name: str):
+    """HBM bytes per launch measured by rocprofv3 for this kernel on this source."""
+    k = _profile_for(TRAFFIC_FILE, kernel_name)
+    return int(k["fetch_bytes"] + k["write_bytes"]) if k else None
+
+
+def counters_for(kernel_name: str):
+    """L2 hit rate and atomic requests per launch (rocprofv3) for this kernel."""
+    return _profile_for(COUNTERS_FILE, kernel_name)
 
 
 def main():
@@ -376,7 +532,7 @@ def main():
     ap.add_argument("--reps", type=int, default=30, help="launches per kernel timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extra", action="store_true",
-                    help="also measure the decoder, bf16 training, fused prologue, 3-D and DAT")
+                    help="also measure the fused prologue, the 3-D variant and DAT")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -459,19 +615,29 @@ def main():
         us = statistics.mean(msda.stage_times(ev)[k] for ev in ev_sets)
     log(f"dominant kernel {KERNELS[dom]}: {us:.2f} us per launch in the timed region")
     achieved = bm[dom] / us / 1e3
+    # the ceilings: row-gather rate and a streaming copy
+    ceiling = gather_ceiling(torch)
+    copy = stream_copy(torch)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic_for(KERNELS[dom]), "kernel": KERNELS[dom],
-                "algorithmic_bytes_per_launch": bm[dom], "avg_launch_us": round(us, 2)}
+                "algorithmic_bytes_per_launch": bm[dom], "avg_launch_us": round(us, 2),
+                "counters": counters_for(KERNELS[dom]),
+                "achievable_copy_GBps": round(copy["GBps"], 1),
+                "forward": forward_roofline(enc["forward"], bm["points"], ceiling)}
+    roofline["forward"]["counters"] = counters_for(KERNELS["forward"])
+
+    # the other two configurations: the decoder and the bf16 training shape
+    dec_w = workloads.make(2)
+    dec, _, _, _ = measure_config(torch, msda, dec_w, False, args.reps, flush, "decoder")
+    trn_w = workloads.make(4)
+    trn, _, _, _ = measure_config(torch, msda, trn_w, True, max(5, args.reps // 3), flush,
+                                  "train_bf16")
+    inputs_sha = {"encoder": w.sha256(), "decoder": dec_w.sha256(), "train_bf16": trn_w.sha256()}
+    del trn_w
 
     extra = {}
     if args.extra:
-        dec, _, _, _ = measure_config(torch, msda, workloads.make(2), False, args.reps, flush,
-                                      "decoder")
-        extra["decoder"] = dec
-        trn, _, _, _ = measure_config(torch, msda, workloads.make(4), True, max(5, args.reps // 3),
-                                      flush, "train_bf16")
-        extra["train_bf16"] = trn
         extra["fused_encoder"] = measure_fused(torch, msda, args.reps, flush)
         extra["volume"] = measure_volume(torch, msda, args.reps, flush)
         extra["dat"] = measure_dat(torch, msda, args.reps, flush)
@@ -496,6 +662,13 @@ def main():
                    "points_per_step": bm["points"]},
         "roofline": roofline,
         "encoder": enc,
+        "decoder": dict(dec, config="B=2, Nq=300 object queries over the encoder's 4-level "
+                                    "value, M=8, D=32, K=4, fp32"),
+        "train_bf16": dict(trn, config="B=4, Nq=Nv=22223, M=8, D=32, L=4, K=8, bf16 value, "
+                                       "fp32 locations, weights, accumulation and gradients"),
+        "gather_ceiling": ceiling,
+        "stream_copy": copy,
+        "inputs_sha256": inputs_sha,
         "kernel_source_sha": source_sha(),
         **extra,
     }

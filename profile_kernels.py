@@ -24,11 +24,19 @@ Modes:
       and attention forward/backward (5 each), then the calibration multiply.
 
   python3 profile_kernels.py summarize --stats DIR --fetch DIR --write DIR
-      Reads the CSV output of three rocprofv3 runs (kernel-trace stats of the
-      bench command itself; --pmc FETCH_SIZE and --pmc WRITE_SIZE of `run`)
-      and writes profiles/encoder_kernels.txt (per-kernel average durations)
-      and profiles/traffic.json (HBM bytes per launch of each kernel, scaled by
+      Reads the CSV output of three rocprofv3 runs (kernel trace of the bench
+      command itself; --pmc FETCH_SIZE and --pmc WRITE_SIZE of `run`) and
+      writes profiles/encoder_kernels.txt (per-kernel durations, one line per
+      kernel and grid size: the bench also runs the decoder and bf16 shapes,
+      whose launches of the same kernels have other grids) and
+      profiles/traffic.json (HBM bytes per launch of each kernel, scaled by
       the multiply's calibration, tagged with the kernel source hash).
+
+  python3 profile_kernels.py summarize-counters --hit DIR --atomic DIR
+      Reads two --pmc runs of `run` (L2 hits and misses; L2 atomics, atomics
+      sent beyond L2, atomic requests from the vector L1) and writes
+      profiles/counters.json: per kernel and launch, the L2 hit rate and the
+      atomic counts, tagged with the kernel source hash.
 
   python3 profile_kernels.py summarize-fused --stats DIR --fetch DIR --write DIR
       The same from the three runs of `run-fused`: profiles/fused_encoder_kernels.txt
@@ -55,6 +63,8 @@ The GPU commands (run from /tmp with TMPDIR=/tmp; OUT is any output directory):
   rocprofv3 --kernel-trace --stats --output-format csv -d OUT/dstats -o run -- python3 profile_kernels.py run-dat
   rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/dfetch -o run -- python3 profile_kernels.py run-dat
   rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/dwrite -o run -- python3 profile_kernels.py run-dat
+  rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum --output-format csv -d OUT/hit -o run -- python3 profile_kernels.py run
+  rocprofv3 --pmc TCC_ATOMIC_sum TCC_EA0_ATOMIC_sum TCP_TCC_ATOMIC_WITH_RET_REQ_sum TCP_TCC_ATOMIC_WITHOUT_RET_REQ_sum --output-format csv -d OUT/atomic -o run -- python3 profile_kernels.py run
 """
 from __future__ import annotations
 
@@ -192,12 +202,27 @@ def _rows(path_glob):
     return rows
 
 
-def _counter_means(dirpath, counter):
+def _counter_means(dirpath, counter, scale=1024.0):
+    """Mean per launch of a counter, by kernel (FETCH_SIZE / WRITE_SIZE read
+    in KiB: scale 1024 gives bytes)."""
     per = collections.defaultdict(list)
     for r in _rows(os.path.join(dirpath, "**", "*counter_collection.csv")):
         if r["Counter_Name"] == counter:
-            per[short_name(r["Kernel_Name"])].append(float(r["Counter_Value"]) * 1024.0)
+            per[short_name(r["Kernel_Name"])].append(float(r["Counter_Value"]) * scale)
     return {k: sum(v) / len(v) for k, v in per.items()}
+
+
+def _trace_stats(dirpath):
+    """Per (kernel, workgroups) launch statistics from a kernel trace."""
+    per = collections.defaultdict(list)
+    for r in _rows(os.path.join(dirpath, "**", "*kernel_trace.csv")):
+        wgs = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        per[(short_name(r["Kernel_Name"]), wgs)].append(dur)
+    total = sum(sum(v) for v in per.values()) or 1.0
+    out = [(k, len(v), sum(v) / len(v), min(v), max(v), 100.0 * sum(v) / total)
+           for k, v in per.items()]
+    return sorted(out, key=lambda e: -e[1] * e[2])
 
 
 HEADERS = {
@@ -222,15 +247,14 @@ HEADERS = {
 
 
 def summarize(stats_dir, fetch_dir, write_dir, commands, name="encoder"):
-    stats = _rows(os.path.join(stats_dir, "**", "*kernel_stats.csv"))
     head = list(HEADERS[name])
     head[-1] += "; kernel source sha " + source_sha(name)
     lines = head + ["# command: " + commands["stats"], "",
-                    f"{'kernel':46s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}"]
-    for r in stats:
-        lines.append(f"{short_name(r['Name'])[:46]:46s} {int(r['Calls']):6d} "
-                     f"{float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
-                     f"{float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):6.2f}")
+                    f"{'kernel':46s} {'wgs':>7s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} "
+                    f"{'max_us':>10s} {'pct':>6s}"]
+    for (k, wgs), calls, avg, mn, mx, pct in _trace_stats(stats_dir):
+        lines.append(f"{k[:46]:46s} {wgs:7d} {calls:6d} {avg:10.2f} {mn:10.2f} {mx:10.2f} "
+                     f"{pct:6.2f}")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     open(os.path.join(ROOT, "profiles", f"{name}_kernels.txt"), "w").write("\n".join(lines) + "\n")
 
@@ -254,6 +278,31 @@ def summarize(stats_dir, fetch_dir, write_dir, commands, name="encoder"):
     print(json.dumps(out, indent=1))
 
 
+COUNTERS = {  # output key: rocprofv3 counter
+    "l2_hit": "TCC_HIT_sum", "l2_miss": "TCC_MISS_sum", "l2_atomic": "TCC_ATOMIC_sum",
+    "atomic_beyond_l2": "TCC_EA0_ATOMIC_sum",
+    "l1_atomic_with_return": "TCP_TCC_ATOMIC_WITH_RET_REQ_sum",
+    "l1_atomic_without_return": "TCP_TCC_ATOMIC_WITHOUT_RET_REQ_sum"}
+
+
+def summarize_counters(hit_dir, atomic_dir, commands, name="encoder"):
+    vals = {}
+    for key, counter in COUNTERS.items():
+        d = hit_dir if key in ("l2_hit", "l2_miss") else atomic_dir
+        vals[key] = _counter_means(d, counter, scale=1.0)
+    kernels = sorted(set().union(*[set(v) for v in vals.values()]))
+    out = {"source_sha": source_sha(name), "sources": list(FAMILY_SOURCES[name]),
+           "counters": COUNTERS, "commands": commands,
+           "note": "per launch means; l2_hit_rate = l2_hit / (l2_hit + l2_miss)", "kernels": {}}
+    for k in kernels:
+        e = {key: vals[key].get(k) for key in COUNTERS}
+        h, m = e.get("l2_hit"), e.get("l2_miss")
+        e["l2_hit_rate"] = h / (h + m) if h is not None and m is not None and h + m > 0 else None
+        out["kernels"][k] = e
+    json.dump(out, open(os.path.join(ROOT, "profiles", "counters.json"), "w"), indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -266,6 +315,9 @@ def main():
         s.add_argument("--stats", required=True)
         s.add_argument("--fetch", required=True)
         s.add_argument("--write", required=True)
+    c = sub.add_parser("summarize-counters")
+    c.add_argument("--hit", required=True)
+    c.add_argument("--atomic", required=True)
     a = ap.parse_args()
     if a.mode == "run":
         run()
@@ -276,9 +328,11 @@ def main():
     elif a.mode == "run-dat":
         run_dat()
     else:
-        doc = __doc__.split("The GPU commands")[1].splitlines()[1:13]
+        doc = __doc__.split("The GPU commands")[1].splitlines()[1:15]
         cmds = [c.strip() for c in doc]
-        if a.mode == "summarize":
+        if a.mode == "summarize-counters":
+            summarize_counters(a.hit, a.atomic, {"hit": cmds[12], "atomic": cmds[13]})
+        elif a.mode == "summarize":
             summarize(a.stats, a.fetch, a.write,
                       {"stats": cmds[0], "fetch": cmds[1], "write": cmds[2]})
         elif a.mode == "summarize-fused":

@@ -1,4 +1,7 @@
-"""Build the HIP library libmsda.so in-tree for gfx950 (MI355X)."""
+"""Build the HIP libraries in-tree for gfx950 (MI355X): libmsda.so (the
+sampling core and its C ABI) and libmsda_probe.so (measurement kernels the
+benchmark uses for the roofline).  Sources are compiled in parallel, then
+linked."""
 from __future__ import annotations
 
 import os
@@ -7,39 +10,64 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "msda.hip")
-SOURCES = [SRC, os.path.join(PKG, "csrc", "msda3d.hip"), os.path.join(PKG, "csrc", "dat_attn.hip")]
-DEPS = SOURCES + [os.path.join(PKG, "csrc", f) for f in ("common.h", "bins.h")]
+CSRC = os.path.join(PKG, "csrc")
+SOURCES = [os.path.join(CSRC, f) for f in ("msda.hip", "msda3d.hip", "dat_attn.hip")]
+PROBE_SOURCES = [os.path.join(CSRC, "probe.hip")]
+DEPS = SOURCES + [os.path.join(CSRC, f) for f in ("common.h", "bins.h")]
 HEADER = os.path.join(ROOT, "include", "msda.h")
 LIB = os.path.join(PKG, "libmsda.so")
+PROBE_LIB = os.path.join(PKG, "libmsda_probe.so")
+OBJ_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # no packed fp32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    cmd = [HIPCC, *FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-o", LIB + ".tmp",
-           *SOURCES]
+def _objects(sources, verbose, extra):
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    procs, objs = [], []
+    for src in sources:
+        obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
+        cmd = [HIPCC, *FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-c", "-o", obj, src]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((subprocess.Popen(cmd), cmd))
+        objs.append(obj)
+    for p, cmd in procs:
+        if p.wait() != 0:
+            raise subprocess.CalledProcessError(p.returncode, cmd)
+    return objs
+
+
+def _link(objs, out, verbose):
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", out + ".tmp", *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
+    os.replace(out + ".tmp", out)
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    objs = _objects(SOURCES + PROBE_SOURCES, verbose, extra)
+    _link(objs[:len(SOURCES)], LIB, verbose)
+    _link(objs[len(SOURCES):], PROBE_LIB, verbose)
     return LIB
 
 
 def stale() -> bool:
-    if not os.path.exists(LIB):
+    if not (os.path.exists(LIB) and os.path.exists(PROBE_LIB)):
         return True
-    t = os.path.getmtime(LIB)
-    return any(os.path.getmtime(f) > t for f in (*DEPS, HEADER))
+    t = min(os.path.getmtime(LIB), os.path.getmtime(PROBE_LIB))
+    return any(os.path.getmtime(f) > t for f in (*DEPS, *PROBE_SOURCES, HEADER))
 
 
 if __name__ == "__main__":
     build(verbose=True)
     print(LIB)
+    print(PROBE_LIB)
     sys.exit(0)

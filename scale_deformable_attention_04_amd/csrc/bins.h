@@ -256,6 +256,7 @@ struct Dims {
     int align;       // pixel convention: x = u*(W-1) instead of u*W - 0.5
     int loc_div;     // dots kernel: location gradients divided by (W, H) (offset gradients)
     int softmax_run; // dots kernel: softmax backward over runs of this many points (0: none)
+    int zero_list;   // scan: list the bins to zero (overwrite mode, grad_value not filled)
 };
 
 // Workspace of the backward pipeline (all 32-bit words).
@@ -472,7 +473,7 @@ bin_scan_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ 
     const uint32_t per_b = (uint32_t)s_lv.nbins * (uint32_t)dm.M;
     const uint32_t stride_b = (uint32_t)dm.nb_max * (uint32_t)dm.M;
     const uint32_t nf = per_b * (uint32_t)B;
-    const bool zeroing = !dm.accumulate;
+    const bool zeroing = dm.zero_list != 0;
     uint32_t carry_e = 0, carry_c = 0, carry_z = 0;
     for (uint32_t base = 0; base < nf; base += kScanThreads * kPer) {
         const uint32_t g0 = base + threadIdx.x * kPer;
@@ -1295,7 +1296,12 @@ msda_status per_batch(int64_t B, int64_t per_b, F &&launch) {
 
 // The grad_value pipeline on the caller's stream: clear the bin counters,
 // count, scan (work list, zero list), scatter the records (zeroing the
-// listed tiles first, in overwrite mode), and the grad_value kernel.
+// listed tiles first), and the grad_value kernel.  In overwrite mode the
+// tiles no single work item writes -- empty and split bins -- must start at
+// zero: with at least two points per pixel and head most bins are full and
+// the scan lists the few others; sparser problems (the decoder's 300
+// queries) leave most bins empty, and grad_value is then zero-filled whole
+// first, by many workgroups at streaming speed.
 template <int D, bool VOL>
 msda_status run_bins(const int64_t *shapes, const int64_t *starts, const float *loc,
                      const float *attn, const float *gout, float *gval, int64_t B, int64_t Nv,
@@ -1303,9 +1309,12 @@ msda_status run_bins(const int64_t *shapes, const int64_t *starts, const float *
                      unsigned char *ws, bool accumulate, bool align, const Exec &ex) {
     const hipStream_t s = ex.s;
     const Work w = work_at(wl, ws);
+    const bool zero_list = !accumulate && Nq * L * K >= 2 * Nv;
     // the counts region is padded to 256 bytes, so whole float4s can be cleared
     ex.stamp(kStageClear, false, s);
     msda_status st = fill_zero(w.counts, (wl.off_start - wl.off_counts) / 16, s);
+    if (st == MSDA_OK && !accumulate && !zero_list)
+        st = fill_zero(gval, (size_t)(B * Nv * M * D) / 4, s);
     if (st != MSDA_OK) return st;
     ex.stamp(kStageClear, true, s);
 
@@ -1314,6 +1323,7 @@ msda_status run_bins(const int64_t *shapes, const int64_t *starts, const float *
     Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, 0, 0, 0, (int)gb, (int)wl.nb_max,
             accumulate ? 1 : 0, make_fastdiv((uint32_t)(L * K)), make_fastdiv((uint32_t)K)};
     dm.align = align ? 1 : 0;
+    dm.zero_list = zero_list ? 1 : 0;
     ex.stamp(kStageCount, false, s);
     st = per_batch(B, gb * M, [&](int64_t b0, unsigned grid) {
         Dims d2 = dm;
@@ -1336,7 +1346,7 @@ msda_status run_bins(const int64_t *shapes, const int64_t *starts, const float *
         Dims d2 = dm;
         d2.b0 = (int)b0;
         // the first launch zeroes every listed tile of the whole problem
-        const ZeroList zl{(!accumulate && b0 == 0) ? w.zero : nullptr, w.work_total, gval,
+        const ZeroList zl{(zero_list && b0 == 0) ? w.zero : nullptr, w.work_total, gval,
                           (int)D};
         hipLaunchKernelGGL(bin_scatter_kernel<VOL>, dim3(grid), dim3(kThreads),
                            8 * (size_t)hist_cap, s, shapes, starts, loc, attn, w.cursor, w.recs,

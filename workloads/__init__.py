@@ -94,11 +94,12 @@ class Workload:
         return d["B"] * d["Nq"] * d["M"] * d["L"] * d["K"]
 
     def sha256(self) -> dict:
+        """SHA-256 of each input array's bytes (C order), by field name."""
         out = {}
         for f in ("value", "sampling_loc", "attn_weight", "grad_out", "value_bf16"):
             a = getattr(self, f)
             if a is not None:
-                out[f] = hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()[:16]
+                out[f] = hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
         return out
 
 
