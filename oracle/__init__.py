@@ -28,10 +28,11 @@ DOUBLE = 1  # every coordinate step in fp64
 ALIGN = 2   # flag: x = u*(W-1), y = v*(H-1) (align_corners=True); combine with SPEC/DOUBLE
 
 
-def build(verbose: bool = False, src: str = _SRC, out: str = _LIB_PATH) -> str:
-    """Compile the oracle with gcc (-O2, no FMA contraction, OpenMP)."""
+def build(verbose: bool = False, src: str = _SRC, out: str = _LIB_PATH, extra=()) -> str:
+    """Compile the oracle with gcc (-O2, no FMA contraction, OpenMP); extra
+    flags are appended (the CPU sanitizer build passes its own)."""
     cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
-           "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra", "-o",
+           "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra", *extra, "-o",
            out + ".tmp", src, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)

@@ -22,8 +22,8 @@ SPEC, DOUBLE, ALIGN = _core.SPEC, _core.DOUBLE, _core.ALIGN
 _default = None
 
 
-def build(verbose: bool = False, src: str = SRC, out: str = LIB_PATH) -> str:
-    return _core.build(verbose=verbose, src=src, out=out)
+def build(verbose: bool = False, src: str = SRC, out: str = LIB_PATH, extra=()) -> str:
+    return _core.build(verbose=verbose, src=src, out=out, extra=extra)
 
 
 class VolumeLib:

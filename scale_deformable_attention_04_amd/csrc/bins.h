@@ -15,7 +15,7 @@ namespace {
 constexpr int kTileShift = 3;              // grad_value tiles of 8x8 pixels
 constexpr int kTile = 1 << kTileShift;
 constexpr int kTilePx = kTile * kTile;
-constexpr int kChunk = 2048;               // points per grad_value work item, at most
+using msda_host::kChunk;                   // records per grad_value work item, at most
 constexpr int kHistLds = 4096;             // bins of one (batch, head) kept in an LDS histogram
 constexpr int kScanThreads = 1024;
 constexpr int kTileGrid = 16384;           // workgroups of the tile kernel, at most
@@ -529,7 +529,7 @@ bin_scan_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ 
 // ---------------------------------------------------------------------------
 constexpr int kCellsW = kTile + 1;
 constexpr int kCells = kCellsW * kCellsW;
-constexpr int kRecQueryShift = 7;  // cells < 128
+using msda_host::kRecQueryShift;   // cells < 128
 
 // Zeroing (zero != nullptr, one launch per call): before its own points,
 // workgroup g zeroes the tiles of zero-list entries g, g + grid, ... -- the
@@ -1167,46 +1167,8 @@ hipError_t launch_grad_value(int64_t work_max, int64_t Nq, int64_t M, const int6
 // ---------------------------------------------------------------------------
 // host side of the pipeline
 // ---------------------------------------------------------------------------
-// Upper bound of the number of 8x8 tiles over all levels, from Nv and L only:
-// sum ceil(H/8)*ceil(W/8) <= sum (HW + 7(H+W) + 49)/64 <= (15 Nv + 49 L)/64.
-int64_t bins_bound(int64_t Nv, int64_t L) { return (15 * Nv + 49 * L) / 64 + 1; }
-
-struct WorkLayout {
-    int64_t nb_max, bm_bins, work_max, sorted_max;
-    size_t off_counts, off_start, off_cursor, off_items, off_total, off_zero, off_sorted, bytes;
-};
-
-// The workspace of the pipeline.  2-D levels (vol = false): at most four
-// records per point and bins_bound(Nv, L) bins per (batch, head).  Volumes:
-// two planes of four tiles, so eight records per point, and at most one bin
-// per voxel (every tile of a plane holds a voxel).
-WorkLayout work_layout(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t L, int64_t K,
-                       bool vol = false) {
-    WorkLayout w;
-    w.nb_max = vol ? Nv + 1 : bins_bound(Nv, L);
-    w.bm_bins = B * M * w.nb_max;
-    const int64_t pts = B * Nq * M * L * K;
-    w.sorted_max = (vol ? 8 : 4) * pts;
-    w.work_max = w.bm_bins + (w.sorted_max + kChunk - 1) / kChunk;
-    auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    size_t o = 0;
-    w.off_counts = o;
-    o = align(o + 4 * (size_t)w.bm_bins);
-    w.off_start = o;
-    o = align(o + 4 * (size_t)w.bm_bins);
-    w.off_cursor = o;
-    o = align(o + 4 * (size_t)w.bm_bins);
-    w.off_items = o;
-    o = align(o + 16 * (size_t)w.work_max);
-    w.off_total = o;
-    o = align(o + 8);
-    w.off_zero = o;
-    o = align(o + 4 * (size_t)w.bm_bins);
-    w.off_sorted = o;
-    o = align(o + 16 * (size_t)w.sorted_max);
-    w.bytes = o;
-    return w;
-}
+using msda_host::WorkLayout;
+using msda_host::work_layout;
 
 Work work_at(const WorkLayout &wl, unsigned char *ws) {
     Work w;

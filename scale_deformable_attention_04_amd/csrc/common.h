@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "host_checks.h"
 #include "msda.h"
 
 // hipError_t of the last MSDA_ERR_HIP returned on this thread (msda.hip)
@@ -14,8 +15,10 @@ extern thread_local int msda_internal_last_hip_error;
 
 namespace {
 
+using msda_host::kMaxLevels;
+using msda_host::supported_d;
+
 constexpr int kThreads = 256;
-constexpr int kMaxLevels = 16;
 constexpr uint32_t kOOB = 0x80000000u;     // byte offset past every slice (slices < 2^31 B)
 constexpr int kRsrcWord3 = 0x00020000;     // gfx9 buffer descriptor word 3 (raw, 32-bit data)
 
@@ -93,10 +96,6 @@ __device__ __forceinline__ int xcd_contiguous(int k, int total) {
 // ---------------------------------------------------------------------------
 // host helpers
 // ---------------------------------------------------------------------------
-inline bool supported_d(int64_t D) {
-    return D == 4 || D == 8 || D == 16 || D == 32 || D == 64 || D == 128 || D == 256;
-}
-
 inline msda_status hip_status(hipError_t e) {
     if (e == hipSuccess) return MSDA_OK;
     msda_internal_last_hip_error = (int)e;

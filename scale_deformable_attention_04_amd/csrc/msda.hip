@@ -823,25 +823,9 @@ fused_epilogue_kernel(const int64_t *__restrict__ shapes, const int64_t *__restr
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-msda_status check_sizes(int value_dtype, int64_t B, int64_t Nv, int64_t Nq, int64_t M,
-                        int64_t D, int64_t L, int64_t K) {
-    if (value_dtype != MSDA_F32 && value_dtype != MSDA_BF16) return MSDA_ERR_DTYPE;
-    if (B < 0 || Nv < 0 || Nq < 0 || M < 1 || D < 1 || L < 1 || K < 1) return MSDA_ERR_SHAPE;
-    if (L > kMaxLevels || !supported_d(D)) return MSDA_ERR_UNSUPPORTED;
-    const int64_t lim = (int64_t)1 << 31;
-    // the rows of one workgroup's queries stay 31-bit addressable
-    if (M > ((int64_t)1 << 20) / D) return MSDA_ERR_UNSUPPORTED;
-    // one batch slice of grad_value (fp32) and of the point arrays must be 31-bit addressable
-    if (Nv > lim / (M * D * 4) || Nv * M * D * 4 >= lim) return MSDA_ERR_UNSUPPORTED;
-    if (K > lim / L || Nq > lim / (M * L * K * 2) || Nq * M * L * K * 2 >= lim)
-        return MSDA_ERR_UNSUPPORTED;
-    // the backward stores point indices of the whole problem, four per point, in 32 bits
-    if (B > 0 && Nq > 0 && B > (((int64_t)1 << 32) - 1) / (Nq * M * L * K * 4))
-        return MSDA_ERR_UNSUPPORTED;
-    // one launch covers Nq*M items with D/4 lanes each: keep the grid under 2^31 threads
-    if (Nq * M > lim / (D / 4)) return MSDA_ERR_UNSUPPORTED;
-    return MSDA_OK;
-}
+using msda_host::check_sizes;
+using msda_host::fused_layout;
+using msda_host::FusedLayout;
 
 struct Launch {
     int ipb, pc, ps;
@@ -1121,12 +1105,6 @@ msda_status msda_forward_fused(const void *value, int value_dtype,
                                   &pr, out, B, Nv, Nq, M, L, K, align, s);
 }
 
-size_t msda_backward_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
-                                    int64_t L, int64_t K) {
-    if (check_sizes(MSDA_F32, B, Nv, Nq, M, D, L, K) != MSDA_OK) return 0;
-    if (B == 0 || Nq == 0) return 0;
-    return work_layout(B, Nv, Nq, M, L, K).bytes;
-}
 
 }  // extern "C"
 
@@ -1211,24 +1189,6 @@ msda_status backward_impl(const void *value, int value_dtype, const int64_t *spa
                                     ex);
     const msda_status js = exec_join(ex);
     return st != MSDA_OK ? st : js;
-}
-
-// Workspace of the fused backward: the core's, then the locations [pts][2]
-// and weights [pts] the prologue writes.
-struct FusedLayout {
-    size_t core, off_loc, off_attn, off_part, bytes;
-};
-
-FusedLayout fused_layout(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t L, int64_t K) {
-    auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    const size_t pts = (size_t)(B * Nq * M * L * K);
-    FusedLayout f;
-    f.core = work_layout(B, Nv, Nq, M, L, K).bytes;
-    f.off_loc = f.core;
-    f.off_attn = align(f.off_loc + 8 * pts);
-    f.off_part = align(f.off_attn + 4 * pts);
-    f.bytes = align(f.off_part + 8 * (size_t)(B * Nq * M * L));
-    return f;
 }
 
 msda_status backward_fused_impl(const void *value, int value_dtype, const int64_t *shapes,
@@ -1401,12 +1361,6 @@ msda_status msda_backward_events(const void *value, int value_dtype,
                          static_cast<hipStream_t>(stream), side_stream, side_events, ev);
 }
 
-size_t msda_backward_fused_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int64_t M,
-                                          int64_t D, int64_t L, int64_t K) {
-    if (check_sizes(MSDA_F32, B, Nv, Nq, M, D, L, K) != MSDA_OK) return 0;
-    if (B == 0 || Nq == 0) return 0;
-    return fused_layout(B, Nv, Nq, M, L, K).bytes;
-}
 
 msda_status msda_backward_fused(const void *value, int value_dtype,
                                 const int64_t *spatial_shapes, const int64_t *level_start_index,
@@ -1461,45 +1415,6 @@ msda_status msda_backward_noalloc(const void *value, int value_dtype,
                          B, Nv, Nq, M, D, L, K, ws, work ? (size_t)MSDA_NOALLOC_SCRATCH_BYTES : 0,
                          flags, nullptr, static_cast<hipStream_t>(stream), side_stream,
                          side_events, nullptr);
-}
-
-msda_status msda_validate_host(const int64_t *spatial_shapes_host, const int64_t *level_start_host,
-                               int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D, int64_t L,
-                               int64_t K) {
-    msda_status st = check_sizes(MSDA_F32, B, Nv, Nq, M, D, L, K);
-    if (st != MSDA_OK) return st;
-    if (!spatial_shapes_host || !level_start_host) return MSDA_ERR_NULL;
-    int64_t total = 0;
-    for (int64_t l = 0; l < L; ++l) {
-        const int64_t H = spatial_shapes_host[2 * l], W = spatial_shapes_host[2 * l + 1];
-        if (H < 1 || W < 1) return MSDA_ERR_SHAPE;
-        // pixel coordinates are formed in fp32: keep them exact integers
-        if (H >= ((int64_t)1 << 24) || W >= ((int64_t)1 << 24)) return MSDA_ERR_UNSUPPORTED;
-        if (level_start_host[l] != total) return MSDA_ERR_SHAPE;
-        if (H > Nv / W) return MSDA_ERR_SHAPE;
-        total += H * W;
-        if (total > Nv) return MSDA_ERR_SHAPE;
-    }
-    if (total != Nv) return MSDA_ERR_SHAPE;
-    return MSDA_OK;
-}
-
-const char *msda_status_string(int status) {
-    switch (status) {
-    case MSDA_OK: return "ok";
-    case MSDA_ERR_NULL: return "a required pointer is NULL";
-    case MSDA_ERR_SHAPE: return "sizes are negative or inconsistent with the level table";
-    case MSDA_ERR_DTYPE: return "unknown value dtype";
-    case MSDA_ERR_UNSUPPORTED:
-        return "outside the supported limits (D in {4,8,...,256}, 1 <= L <= 16, 31-bit slices)";
-    case MSDA_ERR_HIP: return "the HIP runtime refused a launch";
-    case MSDA_ERR_WORKSPACE:
-        return "workspace smaller than msda_backward_workspace_size or not 256-byte aligned";
-    case MSDA_ERR_SCRATCH:
-        return "the problem needs more scratch than msda_backward_noalloc's static buffer "
-               "(MSDA_NOALLOC_SCRATCH_BYTES)";
-    default: return "unknown msda status";
-    }
 }
 
 int msda_last_hip_error(void) { return msda_internal_last_hip_error; }

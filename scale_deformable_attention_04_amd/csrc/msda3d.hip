@@ -339,21 +339,7 @@ msda3d_dots_kernel(const VT *__restrict__ value, const int64_t *__restrict__ sha
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-msda_status check_sizes3(int value_dtype, int64_t B, int64_t Nv, int64_t Nq, int64_t M,
-                         int64_t D, int64_t L, int64_t K) {
-    if (value_dtype != MSDA_F32 && value_dtype != MSDA_BF16) return MSDA_ERR_DTYPE;
-    if (B < 0 || Nv < 0 || Nq < 0 || M < 1 || D < 1 || L < 1 || K < 1) return MSDA_ERR_SHAPE;
-    if (L > kMaxLevels || !supported_d(D)) return MSDA_ERR_UNSUPPORTED;
-    const int64_t lim = (int64_t)1 << 31;
-    if (M > ((int64_t)1 << 20) / D) return MSDA_ERR_UNSUPPORTED;
-    // one batch slice of value / grad_value (fp32) is 31-bit addressable
-    if (Nv > lim / (M * D * 4) || Nv * M * D * 4 >= lim) return MSDA_ERR_UNSUPPORTED;
-    // the point arrays of one batch (3 floats per location) are 31-bit indexable
-    if (K > lim / L || Nq > lim / (M * L * K * 3) || Nq * M * L * K * 3 >= lim)
-        return MSDA_ERR_UNSUPPORTED;
-    if (Nq * M > lim / (D / 4)) return MSDA_ERR_UNSUPPORTED;
-    return MSDA_OK;
-}
+using msda_host::check_sizes3;
 
 struct Plan3 {
     int ipb, pc, ps;
@@ -474,12 +460,6 @@ msda_status msda3d_forward(const void *value, int value_dtype, const int64_t *vo
                                    attn_weight, out, B, Nv, Nq, M, L, K, align, s);
 }
 
-size_t msda3d_backward_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
-                                      int64_t L, int64_t K) {
-    if (check_sizes3(MSDA_F32, B, Nv, Nq, M, D, L, K) != MSDA_OK) return 0;
-    if (B == 0 || Nq == 0) return 0;
-    return work_layout(B, Nv, Nq, M, L, K, true).bytes;
-}
 
 msda_status msda3d_backward(const void *value, int value_dtype, const int64_t *volume_shapes,
                             const int64_t *level_start_index, const float *sampling_loc,
@@ -531,29 +511,6 @@ msda_status msda3d_backward(const void *value, int value_dtype, const int64_t *v
                                      ex);
     const msda_status js = exec_join(ex);
     return st != MSDA_OK ? st : js;
-}
-
-msda_status msda3d_validate_host(const int64_t *volume_shapes_host,
-                                 const int64_t *level_start_host, int64_t B, int64_t Nv,
-                                 int64_t Nq, int64_t M, int64_t D, int64_t L, int64_t K) {
-    msda_status st = check_sizes3(MSDA_F32, B, Nv, Nq, M, D, L, K);
-    if (st != MSDA_OK) return st;
-    if (!volume_shapes_host || !level_start_host) return MSDA_ERR_NULL;
-    int64_t total = 0;
-    for (int64_t l = 0; l < L; ++l) {
-        const int64_t Z = volume_shapes_host[3 * l], H = volume_shapes_host[3 * l + 1];
-        const int64_t W = volume_shapes_host[3 * l + 2];
-        if (Z < 1 || H < 1 || W < 1) return MSDA_ERR_SHAPE;
-        // voxel coordinates are formed in fp32: keep them exact integers
-        if (Z >= ((int64_t)1 << 24) || H >= ((int64_t)1 << 24) || W >= ((int64_t)1 << 24))
-            return MSDA_ERR_UNSUPPORTED;
-        if (level_start_host[l] != total) return MSDA_ERR_SHAPE;
-        if (H > Nv / W || Z > Nv / (H * W)) return MSDA_ERR_SHAPE;
-        total += Z * H * W;
-        if (total > Nv) return MSDA_ERR_SHAPE;
-    }
-    if (total != Nv) return MSDA_ERR_SHAPE;
-    return MSDA_OK;
 }
 
 }  // extern "C"
