@@ -17,7 +17,7 @@ constexpr int kTile = 1 << kTileShift;
 constexpr int kTilePx = kTile * kTile;
 using msda_host::kChunk;                   // records per grad_value work item, at most
 constexpr int kHistLds = 4096;             // bins of one (batch, head) kept in an LDS histogram
-constexpr int kScanThreads = 1024;
+constexpr int kScanThreads = 512;           // placed sooner beside the dots kernel than 1024
 constexpr int kTileGrid = 16384;           // workgroups of the tile kernel, at most
 
 template <int CTRL, int ROWS>

@@ -63,7 +63,6 @@ constexpr int kSetupLdsBytes = 36 * 1024;  // per-workgroup budget for the point
 // 8 workgroups fit a CU's LDS, with the points in chunks of at least 16 (the
 // dots kernel, capped at 2 workgroups per CU, keeps whole items instead)
 constexpr int kFwdLdsBytes = 18 * 1024;
-constexpr int kDotsGrid = 512;             // workgroups of the dots kernel, at most
 constexpr int kDotsBatch = 4;              // points whose row loads the dots kernel overlaps
 // the one-kernel backward of heads with few points: at most kSmallPoints
 // points per (batch, head), workgroups of kSmallPixels pixels
@@ -378,9 +377,9 @@ bwd_dots_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
         if (it < nitems) {
             const int base = it * dm.PS;
             // kDotsBatch points at a time: their 4 * kDotsBatch row loads are in
-            // flight together (this kernel runs at low occupancy beside the
-            // grad_value kernels, so one point's four loads would leave the
-            // wave waiting on each point's latency)
+            // flight together (this kernel shares the CUs with the grad_value
+            // kernels, so one point's four loads would leave the wave waiting
+            // on each point's latency)
             int jj = 0;
             for (; jj + kDotsBatch <= pc; jj += kDotsBatch) {
                 uint4 o[kDotsBatch];
@@ -947,10 +946,10 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
         d2.align = align ? 1 : 0;
         d2.loc_div = fz ? 1 : 0;
         d2.softmax_run = fz && fz->in_dots ? fz->softmax_run : 0;
-        // a few workgroups per CU suffice for this gather-bound kernel, and leave
-        // room for the grad_value kernels running beside it
-        const unsigned g = grid > (unsigned)kDotsGrid ? (unsigned)kDotsGrid : grid;
-        hipLaunchKernelGGL((bwd_dots_kernel<D, VT>), dim3(g), dim3(kThreads), p.lds, ds,
+        // one workgroup per block of queries: beside the grad_value kernels the
+        // backward takes the same time with a capped persistent grid (measured:
+        // 512 workgroups), and this kernel finishes sooner uncapped
+        hipLaunchKernelGGL((bwd_dots_kernel<D, VT>), dim3(grid), dim3(kThreads), p.lds, ds,
                            static_cast<const VT *>(value), shapes, starts, loc, attn, gout, gloc,
                            gattn, ref_part, sb, d2);
     });
