@@ -257,6 +257,7 @@ struct Dims {
     int loc_div;     // dots kernel: location gradients divided by (W, H) (offset gradients)
     int softmax_run; // dots kernel: softmax backward over runs of this many points (0: none)
     int zero_list;   // scan: list the bins to zero (overwrite mode, grad_value not filled)
+    int combine;     // split bins: partial tiles added up by the combine kernel
 };
 
 // Workspace of the backward pipeline (all 32-bit words).
@@ -265,9 +266,12 @@ struct Work {
     uint32_t *start;       // [B][nb_max][M] first entry of each bin in `sorted`
     uint32_t *cursor;      // [B][nb_max][M] next free entry while scattering
     uint4 *items;          // [work_max] (bin, first record, records, whole bin)
-    uint32_t *work_total;  // [2]: work items, bins on the zero list
+    uint32_t *work_total;  // [3]: work items, bins on the zero list, split bins listed
     uint32_t *zero;        // [B * nb_max * M] bins whose tiles are zeroed before the
-                           // grad_value kernel runs (overwrite mode): empty or split bins
+                           // grad_value kernel runs (overwrite mode): empty bins, and
+                           // split bins when their items add into grad_value atomically
+    uint32_t *split;       // [B * nb_max * M] split bins whose items leave partial
+                           // tiles, added up by the combine kernel
     uint4 *recs;           // [4 * points] records grouped by bin
 };
 
@@ -423,13 +427,15 @@ bin_count_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__
 // ---------------------------------------------------------------------------
 // backward: scan of the bin counts, work list, zero list
 // One workgroup of kScanThreads.  Bins are visited in (batch, tile, head)
-// order, which is also their order in memory: the bins of batch b are the
-// nbins * M words from b * nb_max * M on; all batches form one flat scan.
+// order, which is also their order in memory: bin (b * nb_max + tile) * M + m;
+// all batches form one flat scan.
 // Each bin of n > 0 points becomes ceil(n / kChunk) work items (bin, first
 // record, records, whole bin).  In overwrite mode the bins whose pixels no
-// single work item writes outright -- empty bins and bins split over several
-// items -- go on the zero list, and their tiles are zeroed before the
-// grad_value kernel adds into them.
+// single work item writes outright -- empty bins, and bins split over several
+// items that add into grad_value atomically -- go on the zero list, and their
+// tiles are zeroed before the grad_value kernel adds into them.  When the
+// items of split bins leave partial tiles instead (dm.combine), those bins go
+// on the split list of the combine kernel.
 // ---------------------------------------------------------------------------
 // Exclusive scan of (a, b, c) over the kScanThreads threads of the block:
 // wave-level scans with DPP, then one scan of the wave totals.  The block
@@ -458,41 +464,78 @@ __device__ __forceinline__ void block_exclusive_scan3(uint32_t &a, uint32_t &b, 
     __syncthreads();  // s_wave is reused by the next call
 }
 
+// The items of a bin of cnt > kChunk records: nch = ceil(cnt / kChunk) of
+// them, item k taking records [floor(k cnt / nch), floor((k+1) cnt / nch)),
+// so that each holds between kChunk / 2 and kChunk records.  The bounds are
+// stepped through as k cq + floor(k cr / nch), cnt = cq nch + cr, without
+// 64-bit products.
+struct ChunkStep {
+    uint32_t nch, cq, cr, first, rem;
+    __device__ __forceinline__ ChunkStep(uint32_t cnt, uint32_t s0)
+        : nch((cnt + kChunk - 1) / kChunk), cq(0), cr(0), first(s0), rem(0) {
+        cq = cnt / nch;
+        cr = cnt - cq * nch;
+    }
+    // first record of the next item
+    __device__ __forceinline__ void next() {
+        rem += cr;
+        first += cq + (rem >= nch ? 1u : 0u);
+        rem -= rem >= nch ? nch : 0u;
+    }
+};
+
 template <bool VOL>
 __global__ void __launch_bounds__(kScanThreads)
 bin_scan_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ starts,
                 const uint32_t *__restrict__ counts, uint32_t *__restrict__ start,
                 uint32_t *__restrict__ cursor, uint4 *__restrict__ items,
-                uint32_t *__restrict__ work_total, uint32_t *__restrict__ zero, int B, Dims dm) {
+                uint32_t *__restrict__ work_total, uint32_t *__restrict__ zero,
+                uint32_t *__restrict__ split, int B, Dims dm) {
     constexpr int kPer = 8;
     __shared__ LevelLds s_lv;
     __shared__ uint4 s_wave[kScanThreads / 64 + 1];
     stage_bin_levels<VOL>(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
-    // the used bins of every batch as one flat sequence f = b * per_b + (tile * M + m),
+    // the used bins of every batch as one flat sequence f = (b * nbins + tile) * M + m,
     // scanned in one pass (the bins of batch b start at b * nb_max * M in memory)
-    const uint32_t per_b = (uint32_t)s_lv.nbins * (uint32_t)dm.M;
-    const uint32_t stride_b = (uint32_t)dm.nb_max * (uint32_t)dm.M;
-    const uint32_t nf = per_b * (uint32_t)B;
-    const bool zeroing = dm.zero_list != 0;
-    uint32_t carry_e = 0, carry_c = 0, carry_z = 0;
+    const uint32_t nbins = (uint32_t)s_lv.nbins, nb = (uint32_t)B;
+    const uint32_t Mu = (uint32_t)dm.M, nbm = (uint32_t)dm.nb_max;
+    const uint32_t nf = nbins * nb * Mu;
+    const bool zeroing = dm.zero_list != 0, combine = dm.combine != 0;
+    // split bins need zeroed tiles only when their items add atomically
+    const uint32_t zero_above = combine ? 0xffffffffu : (uint32_t)kChunk;
+    // records, items, zero-list and split-list entries so far; the two lists'
+    // counts of one pass (at most kScanThreads * kPer each) share a word in
+    // the scan, 16 bits each
+    uint32_t carry_e = 0, carry_c = 0, carry_z = 0, carry_s = 0;
     for (uint32_t base = 0; base < nf; base += kScanThreads * kPer) {
         const uint32_t g0 = base + threadIdx.x * kPer;
-        uint32_t cnt[kPer], bin[kPer], e = 0, ch = 0, z = 0;
+        uint32_t cnt[kPer], bin[kPer], e = 0, ch = 0, zs = 0;
+        // (b, tile, m) of f = g0, then stepped along
+        const uint32_t bt = g0 / Mu;
+        uint32_t m = g0 - bt * Mu, b = nbins ? bt / nbins : 0u, tile = bt - b * nbins;
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const uint32_t f = g0 + i;
-            const uint32_t b = per_b ? f / per_b : 0u;
-            bin[i] = b * stride_b + (f - b * per_b);
+            bin[i] = (b * nbm + tile) * Mu + m;
+            if (++m == Mu) {
+                m = 0;
+                if (++tile == nbins) {
+                    tile = 0;
+                    ++b;
+                }
+            }
             cnt[i] = f < nf ? counts[bin[i]] : 0u;
             e += cnt[i];
             ch += (cnt[i] + kChunk - 1) / kChunk;
-            z += (zeroing && f < nf && (cnt[i] == 0u || cnt[i] > (uint32_t)kChunk)) ? 1u : 0u;
+            zs += (zeroing && f < nf && (cnt[i] == 0u || cnt[i] > zero_above)) ? 1u : 0u;
+            zs += (combine && cnt[i] > (uint32_t)kChunk) ? 1u << 16 : 0u;
         }
+        static_assert(kScanThreads * kPer < (1 << 16), "list counts of one pass fit 16 bits");
         uint3 tot;
-        block_exclusive_scan3(e, ch, z, s_wave, tot);
+        block_exclusive_scan3(e, ch, zs, s_wave, tot);
         e += carry_e;
         ch += carry_c;
-        z += carry_z;
+        uint32_t z = (zs & 0xffffu) + carry_z, sp = (zs >> 16) + carry_s;
         // a rolled loop: this kernel is one workgroup on the critical path,
         // and its instruction fetches are not hidden by other waves
 #pragma unroll 1
@@ -500,23 +543,33 @@ bin_scan_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ 
             if (g0 + i < nf) {
                 start[bin[i]] = e;
                 cursor[bin[i]] = e;
+                // nch balanced items: item k takes records [k cnt / nch, (k+1) cnt / nch)
                 const uint32_t nch = (cnt[i] + kChunk - 1) / kChunk;
-                for (uint32_t k = 0; k < nch; ++k)
-                    items[ch + k] = make_uint4(bin[i], e + k * kChunk,
-                                               min((uint32_t)kChunk, cnt[i] - k * kChunk),
-                                               nch == 1 ? 1u : 0u);
-                if (zeroing && nch != 1u) zero[z++] = bin[i];
+                if (nch == 1u) {
+                    items[ch] = make_uint4(bin[i], e, cnt[i], 1u);
+                } else if (nch > 1u) {
+                    ChunkStep cs(cnt[i], e);
+                    for (uint32_t k = 0; k < nch; ++k) {
+                        const uint32_t r0 = cs.first;
+                        cs.next();
+                        items[ch + k] = make_uint4(bin[i], r0, cs.first - r0, 0u);
+                    }
+                    if (combine) split[sp++] = bin[i];
+                }
+                if (zeroing && (cnt[i] == 0u || cnt[i] > zero_above)) zero[z++] = bin[i];
                 e += cnt[i];
                 ch += nch;
             }
         }
         carry_e += tot.x;
         carry_c += tot.y;
-        carry_z += tot.z;
+        carry_z += tot.z & 0xffffu;
+        carry_s += tot.z >> 16;
     }
     if (threadIdx.x == 0) {
         work_total[0] = carry_c;
         work_total[1] = carry_z;
+        work_total[2] = carry_s;
     }
 }
 
@@ -952,6 +1005,8 @@ grad_value_tile_kernel(const int64_t *__restrict__ shapes, const int64_t *__rest
 constexpr int kGatherMaxD = 32;
 constexpr int kGatherCPL = 16;  // channels per lane (four quads): 81 cells x 2 lanes at D = 32
 constexpr int kGatherBatch = 2;  // records whose rows a lane loads together
+constexpr int kCombineGrid = 1024;  // combine kernel: workgroups, at most
+constexpr int kCombineBatch = 4;    // combine kernel: partial tiles loaded together
 
 template <int CPL> constexpr int gather_threads() { return kCells * (kGatherMaxD / CPL); }
 
@@ -959,7 +1014,7 @@ template <int D, bool VOL, int CPL>
 __global__ void __launch_bounds__(gather_threads<CPL>())
 grad_value_gather_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ starts,
                          const float *__restrict__ grad_out, const uint4 *__restrict__ items,
-                         const uint32_t *__restrict__ work_total, const uint4 *__restrict__ recs,
+                         const uint32_t *__restrict__ work_total, uint4 *__restrict__ recs,
                          float *__restrict__ grad_value, Dims dm) {
     static_assert(D <= kGatherMaxD && D % 4 == 0, "one (cell, channel group) pair per lane");
     constexpr int kT = gather_threads<CPL>();
@@ -970,6 +1025,7 @@ grad_value_gather_kernel(const int64_t *__restrict__ shapes, const int64_t *__re
     constexpr int kPer = (kChunk + kT - 1) / kT;     // records per thread in the sort
     static_assert(kPairs <= kT, "every (cell, channel group) pair has a lane");
     static_assert(4 * kTilePx * kQuads <= kChunk, "the role sums fit the record table");
+    static_assert(kTilePx * kQuads <= kChunk / 2, "a partial tile fits an item's records");
     __shared__ LevelLds s_lv;
     __shared__ uint32_t s_cnt[kCells];     // records per cell
     __shared__ uint32_t s_st[kCells + 1];  // first sorted slot of each cell, and the total
@@ -994,9 +1050,10 @@ grad_value_gather_kernel(const int64_t *__restrict__ shapes, const int64_t *__re
     __syncthreads();
 
     // Workgroup g takes items g, g + grid, ... counted from the end of the
-    // list (the coarse levels' bins, the largest, first).  The list is in
-    // (batch, level, tile, head) order, so with 8 heads the workgroups of
-    // one XCD (g % 8) mostly see one head, whose grad_out rows stay in that L2.
+    // list (the coarse levels' bins, the largest, first): the whole chip
+    // works through one stretch of the list, and of the records, at a time.
+    // (Cutting the list into one contiguous stretch per XCD, by head or by
+    // tile range, was measured slower.)
     for (uint32_t w = blockIdx.x; w < total; w += gridDim.x) {
         const uint4 it = items[total - 1u - w];  // (bin, first record, records, whole bin)
         const int n = (int)min(it.z, (uint32_t)kChunk);
@@ -1099,61 +1156,133 @@ grad_value_gather_kernel(const int64_t *__restrict__ shapes, const int64_t *__re
             }
         }
         __syncthreads();
-        // 5. write the tile: pixel = the four roles' sums
+        // 5. the tile: pixel = the four roles' sums
         const BinTile tile = bin_tile<VOL>(bin, s_lv, M, dm.nb_max, dm.L);
         const size_t slice_v = (size_t)dm.Nv * M * D;
         float *gv = grad_value + (size_t)b * slice_v + (size_t)m * D;
-        for (int i = tid; i < kTilePx * kQuads; i += kT) {
-            const int px = i / kQuads, q = i - px * kQuads;
-            float4 a = s_red[px * kQuads + q];
+        auto tile_sum = [&](int i) {  // i = pixel * kQuads + quad
+            float4 a = s_red[i];
 #pragma unroll
-            for (int r = 1; r < 4; ++r) {
-                const float4 v = s_red[(r * kTilePx + px) * kQuads + q];
-                a.x += v.x;
-                a.y += v.y;
-                a.z += v.z;
-                a.w += v.w;
-            }
+            for (int r = 1; r < 4; ++r) add4(a, s_red[r * kTilePx * kQuads + i]);
+            return a;
+        };
+        auto write_px = [&](int i, float4 a) {
+            const int px = i / kQuads, q = i - px * kQuads;
             const int gx = tile.x0 + (px & (kTile - 1));
             const int gy = tile.y0 + (px >> kTileShift);
-            if (gy >= tile.H || gx >= tile.W) continue;
-            float *dst = gv + (size_t)(tile.row0 + gy * tile.W + gx) * M * D + 4 * q;
-            if (it.w) {
-                // this work item alone owns the pixel: plain read-add-write
-                float4 *d4 = reinterpret_cast<float4 *>(dst);
-                if (dm.accumulate) {
-                    const float4 v = *d4;
-                    a.x += v.x;
-                    a.y += v.y;
-                    a.z += v.z;
-                    a.w += v.w;
-                }
-                *d4 = a;
-            } else {
-                atomicAdd(dst + 0, a.x);
-                atomicAdd(dst + 1, a.y);
-                atomicAdd(dst + 2, a.z);
-                atomicAdd(dst + 3, a.w);
-            }
+            if (gy >= tile.H || gx >= tile.W) return;
+            float4 *d4 = reinterpret_cast<float4 *>(
+                gv + (size_t)(tile.row0 + gy * tile.W + gx) * M * D + 4 * q);
+            if (dm.accumulate) add4(a, *d4);
+            *d4 = a;
+        };
+        if (it.w) {
+            // this work item alone owns the tile
+            for (int i = tid; i < kTilePx * kQuads; i += kT) write_px(i, tile_sum(i));
+        } else {
+            // one item of a split bin: the partial tile goes into the item's
+            // own records, read already, for the combine kernel
+            float4 *part = reinterpret_cast<float4 *>(recs + it.y);
+            for (int i = tid; i < kTilePx * kQuads; i += kT) part[i] = tile_sum(i);
         }
         // the next item's first barrier orders these reads of s_red before
         // its records overwrite the table
     }
 }
 
-// The grad_value stage: the gather kernel for heads of up to kGatherMaxD
-// channels whose grad_out batch is 32-bit addressable, else the tile kernel.
+using msda_host::WorkLayout;
+using msda_host::work_layout;
+
+// The tiles of split bins after the gather kernel: one workgroup per listed
+// bin adds up, in item order, the partial tiles its items left at the start
+// of their records, and writes the tile (adding to grad_value in accumulate
+// mode).  Every pixel of the tile is written by one thread, once.
 template <int D, bool VOL>
-hipError_t launch_grad_value(int64_t work_max, int64_t Nq, int64_t M, const int64_t *shapes,
-                             const int64_t *starts, const float *gout, const uint4 *items,
-                             const uint32_t *work_total, const uint4 *recs, float *gval,
-                             const Dims &dm, hipStream_t s) {
-    const int64_t grid = work_max < kTileGrid ? work_max : kTileGrid;
+__global__ void __launch_bounds__(kThreads)
+split_combine_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ starts,
+                     const uint32_t *__restrict__ split, const uint32_t *__restrict__ work_total,
+                     const uint32_t *__restrict__ counts, const uint32_t *__restrict__ start,
+                     const uint4 *__restrict__ recs, float *__restrict__ grad_value, Dims dm) {
+    constexpr int kQuads = D / 4;
+    constexpr int kPerT = (kTilePx * kQuads + kThreads - 1) / kThreads;
+    __shared__ LevelLds s_lv;
+    const uint32_t total = work_total[2];
+    if (blockIdx.x >= total) return;  // the grid is sized for the largest possible list
+    stage_bin_levels<VOL>(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
+    const int M = dm.M;
+    for (uint32_t w = blockIdx.x; w < total; w += gridDim.x) {
+        const uint32_t bin = split[w];
+        ChunkStep cs(counts[bin], start[bin]);
+        const uint32_t nch = cs.nch;
+        float4 a[kPerT];
+#pragma unroll
+        for (int u = 0; u < kPerT; ++u) a[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (uint32_t k = 0; k < nch; k += kCombineBatch) {
+            float4 v[kCombineBatch][kPerT];
+#pragma unroll
+            for (int c = 0; c < kCombineBatch; ++c) {
+                const bool in = k + c < nch;
+                const float4 *part = reinterpret_cast<const float4 *>(recs + cs.first);
+#pragma unroll
+                for (int u = 0; u < kPerT; ++u) {
+                    const int i = threadIdx.x + u * kThreads;
+                    v[c][u] = in && i < kTilePx * kQuads ? part[i]
+                                                         : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+                cs.next();
+            }
+#pragma unroll
+            for (int c = 0; c < kCombineBatch; ++c)
+#pragma unroll
+                for (int u = 0; u < kPerT; ++u) add4(a[u], v[c][u]);
+        }
+        const BinTile tile = bin_tile<VOL>(bin, s_lv, M, dm.nb_max, dm.L);
+        float *gv = grad_value + (size_t)tile.b * dm.Nv * M * D + (size_t)tile.m * D;
+#pragma unroll
+        for (int u = 0; u < kPerT; ++u) {
+            const int i = threadIdx.x + u * kThreads;
+            const int px = i / kQuads, q = i - px * kQuads;
+            const int gx = tile.x0 + (px & (kTile - 1));
+            const int gy = tile.y0 + (px >> kTileShift);
+            if (i >= kTilePx * kQuads || gy >= tile.H || gx >= tile.W) continue;
+            float4 *d4 = reinterpret_cast<float4 *>(
+                gv + (size_t)(tile.row0 + gy * tile.W + gx) * M * D + 4 * q);
+            if (dm.accumulate) add4(a[u], *d4);
+            *d4 = a[u];
+        }
+    }
+}
+
+// The grad_value stage: the gather kernel for heads of up to kGatherMaxD
+// channels whose grad_out batch is 32-bit addressable (then the combine
+// kernel writes the tiles of split bins), else the tile kernel (whose
+// split-bin items add into zeroed tiles atomically).
+template <int D>
+bool uses_gather(int64_t Nq, int64_t M) {
+    return D <= kGatherMaxD && Nq * M * D * 4 < ((int64_t)1 << 32) - 64;
+}
+
+template <int D, bool VOL>
+hipError_t launch_grad_value(const WorkLayout &wl, int64_t Nq, int64_t M, const int64_t *shapes,
+                             const int64_t *starts, const float *gout, const Work &w,
+                             float *gval, const Dims &dm, hipStream_t s) {
+    const int64_t grid = wl.work_max < kTileGrid ? wl.work_max : kTileGrid;
+    const uint4 *items = w.items, *recs = w.recs;
+    const uint32_t *work_total = w.work_total;
     if constexpr (D <= kGatherMaxD) {
-        if (Nq * M * D * 4 < ((int64_t)1 << 32) - 64) {
+        if (uses_gather<D>(Nq, M)) {
             hipLaunchKernelGGL((grad_value_gather_kernel<D, VOL, kGatherCPL>),
                                dim3((unsigned)grid), dim3(gather_threads<kGatherCPL>()), 0, s,
-                               shapes, starts, gout, items, work_total, recs, gval, dm);
+                               shapes, starts, gout, items, work_total, w.recs, gval, dm);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            // split bins: more than kChunk records each, and at most one per bin
+            int64_t nsplit = wl.sorted_max / (kChunk + 1) + 1;
+            nsplit = nsplit < wl.bm_bins ? nsplit : wl.bm_bins;
+            const unsigned cgrid = (unsigned)(nsplit < kCombineGrid ? nsplit : kCombineGrid);
+            hipLaunchKernelGGL((split_combine_kernel<D, VOL>), dim3(cgrid), dim3(kThreads), 0, s,
+                               shapes, starts, w.split, work_total, w.counts, w.start, recs,
+                               gval, dm);
             return hipGetLastError();
         }
     }
@@ -1167,8 +1296,6 @@ hipError_t launch_grad_value(int64_t work_max, int64_t Nq, int64_t M, const int6
 // ---------------------------------------------------------------------------
 // host side of the pipeline
 // ---------------------------------------------------------------------------
-using msda_host::WorkLayout;
-using msda_host::work_layout;
 
 Work work_at(const WorkLayout &wl, unsigned char *ws) {
     Work w;
@@ -1178,6 +1305,7 @@ Work work_at(const WorkLayout &wl, unsigned char *ws) {
     w.items = reinterpret_cast<uint4 *>(ws + wl.off_items);
     w.work_total = reinterpret_cast<uint32_t *>(ws + wl.off_total);
     w.zero = reinterpret_cast<uint32_t *>(ws + wl.off_zero);
+    w.split = reinterpret_cast<uint32_t *>(ws + wl.off_split);
     w.recs = reinterpret_cast<uint4 *>(ws + wl.off_sorted);
     return w;
 }
@@ -1286,6 +1414,7 @@ msda_status run_bins(const int64_t *shapes, const int64_t *starts, const float *
             accumulate ? 1 : 0, make_fastdiv((uint32_t)(L * K)), make_fastdiv((uint32_t)K)};
     dm.align = align ? 1 : 0;
     dm.zero_list = zero_list ? 1 : 0;
+    dm.combine = uses_gather<D>(Nq, M) ? 1 : 0;
     ex.stamp(kStageCount, false, s);
     st = per_batch(B, gb * M, [&](int64_t b0, unsigned grid) {
         Dims d2 = dm;
@@ -1298,7 +1427,8 @@ msda_status run_bins(const int64_t *shapes, const int64_t *starts, const float *
 
     ex.stamp(kStageScan, false, s);
     hipLaunchKernelGGL(bin_scan_kernel<VOL>, dim3(1), dim3(kScanThreads), 0, s, shapes, starts,
-                       w.counts, w.start, w.cursor, w.items, w.work_total, w.zero, (int)B, dm);
+                       w.counts, w.start, w.cursor, w.items, w.work_total, w.zero, w.split,
+                       (int)B, dm);
     st = hip_status(hipGetLastError());
     if (st != MSDA_OK) return st;
     ex.stamp(kStageScan, true, s);
@@ -1318,8 +1448,7 @@ msda_status run_bins(const int64_t *shapes, const int64_t *starts, const float *
     ex.stamp(kStageScatter, true, s);
 
     ex.stamp(kStageGather, false, s);
-    st = hip_status(launch_grad_value<D, VOL>(wl.work_max, Nq, M, shapes, starts, gout, w.items,
-                                               w.work_total, w.recs, gval, dm, s));
+    st = hip_status(launch_grad_value<D, VOL>(wl, Nq, M, shapes, starts, gout, w, gval, dm, s));
     ex.stamp(kStageGather, true, s);
     return st;
 }

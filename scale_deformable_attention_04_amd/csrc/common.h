@@ -68,6 +68,13 @@ template <int G> __device__ __forceinline__ float group_sum(float v) {
 }
 
 
+__device__ __forceinline__ void add4(float4 &acc, const float4 &v) {
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+}
+
 __device__ __forceinline__ void fma4(float4 &acc, float w, const float4 &v) {
     acc.x = __builtin_fmaf(w, v.x, acc.x);
     acc.y = __builtin_fmaf(w, v.y, acc.y);

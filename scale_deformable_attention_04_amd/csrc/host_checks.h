@@ -94,13 +94,14 @@ inline msda_status validate_levels(const int64_t *shapes, const int64_t *starts,
 inline int64_t bins_bound(int64_t Nv, int64_t L) { return (15 * Nv + 49 * L) / 64 + 1; }
 
 // The workspace of the backward's grad_value pipeline: bin counters, starts
-// and cursors [B][nb_max][M], the work list, its totals, the zero list and
-// the records.  2-D levels (vol = false): at most four records per point and
+// and cursors [B][nb_max][M], the work list, its totals, the zero list, the
+// list of split bins and the records.  2-D levels (vol = false): at most four records per point and
 // bins_bound(Nv, L) bins per (batch, head).  Volumes: two planes of four
 // tiles, so eight records per point, and at most one bin per voxel.
 struct WorkLayout {
     int64_t nb_max, bm_bins, work_max, sorted_max;
-    size_t off_counts, off_start, off_cursor, off_items, off_total, off_zero, off_sorted, bytes;
+    size_t off_counts, off_start, off_cursor, off_items, off_total, off_zero, off_split,
+        off_sorted, bytes;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -123,8 +124,10 @@ inline WorkLayout work_layout(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int6
     w.off_items = o;
     o = align256(o + 16 * (size_t)w.work_max);
     w.off_total = o;
-    o = align256(o + 8);
+    o = align256(o + 16);
     w.off_zero = o;
+    o = align256(o + 4 * (size_t)w.bm_bins);
+    w.off_split = o;
     o = align256(o + 4 * (size_t)w.bm_bins);
     w.off_sorted = o;
     o = align256(o + 16 * (size_t)w.sorted_max);

@@ -384,20 +384,43 @@ def test_accumulate_adds_into_grad_value(msda):
     close(gv.cpu().numpy() - base.cpu().numpy(), rv, BWD_TOL)
 
 
-@pytest.mark.parametrize("D", [8, 32])
+@pytest.mark.parametrize("D", [8, 32, 64])
 @pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("acc", [False, True])
 def test_split_bins(msda, D, bf16, acc):
     # a 5x6 level is one 8x8 tile: 1500 queries x 4 points per head put ~6000
-    # records in its bin, which the work list splits into three items whose
-    # partial tiles are added atomically (onto earlier contents with acc)
+    # records in its bin, which the work list splits into three items; their
+    # partial tiles are added up by the combine kernel (D <= 32) or atomically
+    # into the zeroed tile (D = 64), onto earlier contents with acc
     w = workloads.random_case(1900 + D, 2, ((5, 6), (12, 10)), 1500, 2, D, 4, bf16=bf16)
     x = dev_inputs(w, bf16)
     g = torch.from_numpy(w.grad_out).cuda()
     base = torch.randn(w.value.shape, device="cuda") if acc else None
     _say(f"split bins D={D} bf16={bf16} acc={acc}")
-    gv, gl, ga = msda.backward(**x, grad_out=g, grad_value=base.clone() if acc else None,
-                               accumulate=acc)
+    # overwrite mode starts from NaN: every element must be written
+    gv0 = base.clone() if acc else torch.full(tuple(w.value.shape), float("nan"), device="cuda")
+    gv, gl, ga = msda.backward(**x, grad_out=g, grad_value=gv0, accumulate=acc)
+    torch.cuda.synchronize()
+    rv, rl, ra = oracle_bwd(w)
+    got_v = gv.cpu().numpy() - (base.cpu().numpy() if acc else 0.0)
+    close(got_v, rv, BWD_TOL, "grad_value")
+    close(gl.cpu().numpy(), rl, BWD_TOL, "grad_sampling_loc")
+    close(ga.cpu().numpy(), ra, BWD_TOL, "grad_attn_weight")
+
+
+@pytest.mark.parametrize("acc", [False, True])
+def test_split_bins_many_items(msda, acc):
+    # one level of one tile: 6000 queries x 4 points per head, 24000 points
+    # and up to four records each in one bin, split into a dozen or more
+    # items of unequal, balanced sizes
+    w = workloads.random_case(1950, 1, ((5, 6),), 6000, 2, 32, 4)
+    x = dev_inputs(w)
+    g = torch.from_numpy(w.grad_out).cuda()
+    base = torch.randn(w.value.shape, device="cuda") if acc else None
+    _say(f"split bins, many items, acc={acc}")
+    # overwrite mode starts from NaN: every element must be written
+    gv0 = base.clone() if acc else torch.full(tuple(w.value.shape), float("nan"), device="cuda")
+    gv, gl, ga = msda.backward(**x, grad_out=g, grad_value=gv0, accumulate=acc)
     torch.cuda.synchronize()
     rv, rl, ra = oracle_bwd(w)
     got_v = gv.cpu().numpy() - (base.cpu().numpy() if acc else 0.0)
