@@ -492,79 +492,99 @@ bin_scan_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ 
                 uint32_t *__restrict__ work_total, uint32_t *__restrict__ zero,
                 uint32_t *__restrict__ split, int B, Dims dm) {
     constexpr int kPer = 8;
+    constexpr uint32_t kPass = kScanThreads * kPer;  // bins per pass
+    static_assert(kPass < (1 << 16), "list counts of one pass fit 16 bits");
     __shared__ LevelLds s_lv;
     __shared__ uint4 s_wave[kScanThreads / 64 + 1];
+    // one pass of bins in flat order: their counts; for each thread's kPer
+    // bins, the first record, first item, and zero- and split-list positions
+    // (16 bits each) of the first.  Little LDS, so that the workgroup finds a
+    // place beside the kernel on the other stream.
+    __shared__ uint32_t s_cnt[kPass], s_e[kScanThreads], s_ch[kScanThreads], s_zs[kScanThreads];
     stage_bin_levels<VOL>(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
-    // the used bins of every batch as one flat sequence f = (b * nbins + tile) * M + m,
-    // scanned in one pass (the bins of batch b start at b * nb_max * M in memory)
-    const uint32_t nbins = (uint32_t)s_lv.nbins, nb = (uint32_t)B;
-    const uint32_t Mu = (uint32_t)dm.M, nbm = (uint32_t)dm.nb_max;
-    const uint32_t nf = nbins * nb * Mu;
+    // The used bins of every batch as one flat sequence f = (b * nbins + tile) * M + m,
+    // scanned in passes of kPass.  Bin f is at f + b * gap in memory (the
+    // bins of batch b start at b * nb_max * M).  Counts are loaded and the
+    // results stored with consecutive lanes on consecutive bins; in between,
+    // each thread sums kPer consecutive bins, through LDS.
+    const uint32_t nbins = (uint32_t)s_lv.nbins, Mu = (uint32_t)dm.M;
+    const uint32_t per_b = nbins * Mu, gap = ((uint32_t)dm.nb_max - nbins) * Mu;
+    const uint32_t nf = per_b * (uint32_t)B;
     const bool zeroing = dm.zero_list != 0, combine = dm.combine != 0;
     // split bins need zeroed tiles only when their items add atomically
     const uint32_t zero_above = combine ? 0xffffffffu : (uint32_t)kChunk;
-    // records, items, zero-list and split-list entries so far; the two lists'
-    // counts of one pass (at most kScanThreads * kPer each) share a word in
-    // the scan, 16 bits each
+    auto listed = [&](uint32_t c) {  // zero-list entry | split-list entry << 16
+        return ((zeroing && (c == 0u || c > zero_above)) ? 1u : 0u) |
+               ((combine && c > (uint32_t)kChunk) ? 1u << 16 : 0u);
+    };
+    // records, items, zero-list and split-list entries of the passes before
     uint32_t carry_e = 0, carry_c = 0, carry_z = 0, carry_s = 0;
-    for (uint32_t base = 0; base < nf; base += kScanThreads * kPer) {
-        const uint32_t g0 = base + threadIdx.x * kPer;
-        uint32_t cnt[kPer], bin[kPer], e = 0, ch = 0, zs = 0;
-        // (b, tile, m) of f = g0, then stepped along
-        const uint32_t bt = g0 / Mu;
-        uint32_t m = g0 - bt * Mu, b = nbins ? bt / nbins : 0u, tile = bt - b * nbins;
+    for (uint32_t base = 0; base < nf; base += kPass) {
+        // 1. the pass's counts, coalesced, into LDS (zero past the end)
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
-            const uint32_t f = g0 + i;
-            bin[i] = (b * nbm + tile) * Mu + m;
-            if (++m == Mu) {
-                m = 0;
-                if (++tile == nbins) {
-                    tile = 0;
-                    ++b;
-                }
-            }
-            cnt[i] = f < nf ? counts[bin[i]] : 0u;
+            const uint32_t f = base + threadIdx.x + i * kScanThreads;
+            s_cnt[f - base] = f < nf ? counts[f + f / per_b * gap] : 0u;
+        }
+        __syncthreads();
+        // 2. thread t: bins t * kPer ... of the pass
+        const uint32_t j0 = threadIdx.x * kPer;
+        uint32_t cnt[kPer], e = 0, ch = 0, zs = 0;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            cnt[i] = s_cnt[j0 + i];
             e += cnt[i];
             ch += (cnt[i] + kChunk - 1) / kChunk;
-            zs += (zeroing && f < nf && (cnt[i] == 0u || cnt[i] > zero_above)) ? 1u : 0u;
-            zs += (combine && cnt[i] > (uint32_t)kChunk) ? 1u << 16 : 0u;
+            zs += base + j0 + i < nf ? listed(cnt[i]) : 0u;
         }
-        static_assert(kScanThreads * kPer < (1 << 16), "list counts of one pass fit 16 bits");
         uint3 tot;
         block_exclusive_scan3(e, ch, zs, s_wave, tot);
-        e += carry_e;
-        ch += carry_c;
-        uint32_t z = (zs & 0xffffu) + carry_z, sp = (zs >> 16) + carry_s;
-        // a rolled loop: this kernel is one workgroup on the critical path,
-        // and its instruction fetches are not hidden by other waves
+        s_e[threadIdx.x] = e;
+        s_ch[threadIdx.x] = ch;
+        s_zs[threadIdx.x] = zs;
+        __syncthreads();
+        // 3. bin starts, cursors, work items and list entries, coalesced;
+        // a rolled loop, since this one workgroup's instruction fetches are
+        // not hidden by other waves
+        {
 #pragma unroll 1
-        for (int i = 0; i < kPer; ++i) {
-            if (g0 + i < nf) {
-                start[bin[i]] = e;
-                cursor[bin[i]] = e;
-                // nch balanced items: item k takes records [k cnt / nch, (k+1) cnt / nch)
-                const uint32_t nch = (cnt[i] + kChunk - 1) / kChunk;
+            for (uint32_t f = base + threadIdx.x; f < nf && f < base + kPass; f += kScanThreads) {
+                const uint32_t j = f - base, bin = f + f / per_b * gap, c = s_cnt[j];
+                // this bin's offsets: its group's, plus the bins before it in the
+                // group (all below nf)
+                const uint32_t g = j / kPer, o = j - g * kPer;
+                uint32_t e0 = s_e[g] + carry_e, c0 = s_ch[g] + carry_c, zs0 = s_zs[g];
+#pragma unroll
+                for (uint32_t i = 0; i < kPer - 1; ++i) {
+                    const uint32_t ci = i < o ? s_cnt[g * kPer + i] : 0u;
+                    e0 += ci;
+                    c0 += (ci + kChunk - 1) / kChunk;
+                    zs0 += i < o ? listed(ci) : 0u;
+                }
+                start[bin] = e0;
+                cursor[bin] = e0;
+                // nch balanced items: item k takes records [k c / nch, (k+1) c / nch)
+                const uint32_t nch = (c + kChunk - 1) / kChunk;
                 if (nch == 1u) {
-                    items[ch] = make_uint4(bin[i], e, cnt[i], 1u);
+                    items[c0] = make_uint4(bin, e0, c, 1u);
                 } else if (nch > 1u) {
-                    ChunkStep cs(cnt[i], e);
+                    ChunkStep cs(c, e0);
                     for (uint32_t k = 0; k < nch; ++k) {
                         const uint32_t r0 = cs.first;
                         cs.next();
-                        items[ch + k] = make_uint4(bin[i], r0, cs.first - r0, 0u);
+                        items[c0 + k] = make_uint4(bin, r0, cs.first - r0, 0u);
                     }
-                    if (combine) split[sp++] = bin[i];
                 }
-                if (zeroing && (cnt[i] == 0u || cnt[i] > zero_above)) zero[z++] = bin[i];
-                e += cnt[i];
-                ch += nch;
+                const uint32_t l = listed(c);
+                if (l & 1u) zero[carry_z + (zs0 & 0xffffu)] = bin;
+                if (l >> 16) split[carry_s + (zs0 >> 16)] = bin;
             }
         }
         carry_e += tot.x;
         carry_c += tot.y;
         carry_z += tot.z & 0xffffu;
         carry_s += tot.z >> 16;
+        __syncthreads();  // the LDS arrays are refilled by the next pass
     }
     if (threadIdx.x == 0) {
         work_total[0] = carry_c;
