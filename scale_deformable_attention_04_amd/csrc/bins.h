@@ -1050,8 +1050,11 @@ grad_value_gather_kernel(const int64_t *__restrict__ shapes, const int64_t *__re
     __shared__ uint32_t s_cnt[kCells];     // records per cell
     __shared__ uint32_t s_st[kCells + 1];  // first sorted slot of each cell, and the total
     __shared__ uint4 s_tab[kChunk];        // the item's records in cell order
-    // after the gather, the role sums: [role][pixel][quad]
+    // after the gather, the role sums: [role][pixel][quad], the quads of pixel
+    // p rotated by p (quad q at slot q ^ (p mod kQuads)), so that the lanes
+    // writing one quad of consecutive pixels hit different banks
     float4 *s_red = reinterpret_cast<float4 *>(s_tab);
+    auto red_slot = [](int i) { return i ^ ((i / kQuads) & (kQuads - 1)); };  // i = p * kQuads + q
 
     const int M = dm.M, Nq = dm.Nq;
     const int tid = threadIdx.x;
@@ -1170,8 +1173,8 @@ grad_value_gather_kernel(const int64_t *__restrict__ shapes, const int64_t *__re
                 if (px >= 0 && px < kTile && py >= 0 && py < kTile) {
 #pragma unroll
                     for (int k = 0; k < kQPL; ++k)
-                        s_red[(r * kTilePx + py * kTile + px) * kQuads + grp * kQPL + k] =
-                            acc[r][k];
+                        s_red[r * kTilePx * kQuads +
+                              red_slot((py * kTile + px) * kQuads + grp * kQPL + k)] = acc[r][k];
                 }
             }
         }
@@ -1181,9 +1184,10 @@ grad_value_gather_kernel(const int64_t *__restrict__ shapes, const int64_t *__re
         const size_t slice_v = (size_t)dm.Nv * M * D;
         float *gv = grad_value + (size_t)b * slice_v + (size_t)m * D;
         auto tile_sum = [&](int i) {  // i = pixel * kQuads + quad
-            float4 a = s_red[i];
+            const int j = red_slot(i);
+            float4 a = s_red[j];
 #pragma unroll
-            for (int r = 1; r < 4; ++r) add4(a, s_red[r * kTilePx * kQuads + i]);
+            for (int r = 1; r < 4; ++r) add4(a, s_red[r * kTilePx * kQuads + j]);
             return a;
         };
         auto write_px = [&](int i, float4 a) {
