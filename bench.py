@@ -113,6 +113,9 @@ def to_device(w, torch, bf16=False):
 
 
 def time_forward(torch, fn, reps, flush):
+    """Mean us of one call timed alone (events around it, synchronized after
+    it); with `flush` a 512 MB fill runs before each call, evicting L2 and the
+    Infinity Cache (cold)."""
     s = torch.cuda.current_stream()
     times = []
     for _ in range(reps):
@@ -126,6 +129,13 @@ def time_forward(torch, fn, reps, flush):
         e1.synchronize()
         times.append(e0.elapsed_time(e1) * 1e3)
     return statistics.mean(times)
+
+
+def time_warm(torch, fn, reps):
+    """Mean us per call of `reps` calls back to back on torch's stream (warm
+    caches; the launch gaps of a steady stream of work, as in a training
+    step and as the gather-ceiling probe is timed)."""
+    return _time_launches(torch, fn, reps)
 
 
 def time_backward_stages(torch, msda, x, g, bufs, reps):
@@ -164,7 +174,7 @@ def measure_config(torch, msda, w, bf16, reps, flush, label):
     for _ in range(3):
         fwd()
     cold = time_forward(torch, fwd, reps, flush)
-    warm = time_forward(torch, fwd, reps, None)
+    warm = time_warm(torch, fwd, reps)
     res["forward"] = {"us_cold": cold, "us_warm": warm, "points_per_s": bm["points"] / cold * 1e6,
                       "algorithmic_GBps": bm["forward"] / cold / 1e3,
                       "algorithmic_bytes": bm["forward"]}
@@ -204,7 +214,7 @@ def measure_fused(torch, msda, reps, flush):
     for _ in range(3):
         fwd()
     res = {"points": w.points, "forward": {"us_cold": time_forward(torch, fwd, reps, flush),
-                                           "us_warm": time_forward(torch, fwd, reps, None)}}
+                                           "us_warm": time_warm(torch, fwd, reps)}}
     gv = torch.empty(tuple(w.value.shape), dtype=torch.float32, device=d)
     for _ in range(3):
         msda.backward_fused(**x, grad_out=g, grad_value=gv, validate=False)
@@ -216,17 +226,17 @@ def measure_fused(torch, msda, reps, flush):
     for ev in sets:
         acc = [a + b for a, b in zip(acc, msda.stage_times(ev))]
     stages = {k: v / reps for k, v in zip(msda.BWD_FUSED_STAGES, acc)}
-    res["backward"] = {"us_warm": time_forward(
+    res["backward"] = {"us_warm": time_warm(
         torch, lambda: msda.backward_fused(**x, grad_out=g, grad_value=gv, validate=False),
-        reps, None), "stages_us_warm": stages}
+        reps), "stages_us_warm": stages}
     # a training step: the forward stores the locations and weights, the
     # backward reads them instead of recomputing them
     saved = msda.forward_fused(**x, validate=False, save=True)[1:]
-    res["forward_saving"] = {"us_warm": time_forward(
-        torch, lambda: msda.forward_fused(**x, validate=False, save=True), reps, None)}
-    res["backward_saved"] = {"us_warm": time_forward(
+    res["forward_saving"] = {"us_warm": time_warm(
+        torch, lambda: msda.forward_fused(**x, validate=False, save=True), reps)}
+    res["backward_saved"] = {"us_warm": time_warm(
         torch, lambda: msda.backward_fused(**x, grad_out=g, grad_value=gv, validate=False,
-                                           saved=saved), reps, None)}
+                                           saved=saved), reps)}
 
     leaves = {k: x[k].clone().requires_grad_(True)
               for k in ("value", "reference_points", "sampling_offsets", "attn_logits")}
@@ -251,7 +261,7 @@ def measure_fused(torch, msda, reps, flush):
                      ("autograd_step_torch_prologue_us", unfused_step)):
         for _ in range(3):
             fn()
-        res[name] = time_forward(torch, fn, reps, None)
+        res[name] = time_warm(torch, fn, reps)
     log(f"fused: {json.dumps(res)}")
     return res
 
@@ -284,8 +294,8 @@ def measure_volume(torch, msda, reps, flush):
     for _ in range(3):
         bwd()
     cold = time_forward(torch, fwd, reps, flush)
-    warm = time_forward(torch, fwd, reps, None)
-    bw = time_forward(torch, bwd, reps, None)
+    warm = time_warm(torch, fwd, reps)
+    bw = time_warm(torch, bwd, reps)
     res = {"points": pts, "workload": "voxel pyramid 4x128x128, 2x64x64, 1x32x32; Nq=16384, "
                                       "M=8, D=32, K=4, fp32",
            "forward": {"us_cold": cold, "us_warm": warm, "algorithmic_bytes": fwd_bytes,
@@ -324,10 +334,10 @@ def measure_dat(torch, msda, reps, flush):
                 fn()
         mm = 2.0 * B * Hh * N * Ns * d            # flops of one N x Ns x d product
         r = {"B": B, "N": N, "Ns": Ns, "heads": Hh, "head_dim": d, "groups": dims["G"],
-             "sample_fwd_us": time_forward(torch, smp, reps, None),
-             "sample_bwd_us": time_forward(torch, smp_b, reps, None),
+             "sample_fwd_us": time_warm(torch, smp, reps),
+             "sample_bwd_us": time_warm(torch, smp_b, reps),
              "attn_fwd_us": time_forward(torch, att, reps, flush),
-             "attn_bwd_us": time_forward(torch, att_b, reps, None)}
+             "attn_bwd_us": time_warm(torch, att_b, reps)}
         # where the sampling backward's time goes (the core's stage events)
         ss, st = msda._binding._level_of(w.hw, x.device)
         ones = msda._binding._ones_of((B, Ns, dims["G"], 1, 1), x.device)
