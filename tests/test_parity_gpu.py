@@ -429,6 +429,29 @@ def test_split_bins_many_items(msda, acc):
     close(ga.cpu().numpy(), ra, BWD_TOL, "grad_attn_weight")
 
 
+@pytest.mark.parametrize("D", [32, 64])
+@pytest.mark.parametrize("acc", [False, True])
+def test_scan_two_passes(msda, D, acc):
+    # 2 batches x 8 heads x (256 + 1) tiles = 4112 bins: the scan takes two
+    # passes of 4096, and both hold empty bins (the points crowd into a corner
+    # of the 128x128 level) and split bins (the 5x6 level is one tile with
+    # ~6000 records per head); overwrite mode starts from NaN
+    w = workloads.random_case(1970 + D, 2, ((128, 128), (5, 6)), 1500, 8, D, 4, 0.0, 0.3)
+    x = dev_inputs(w)
+    g = torch.from_numpy(w.grad_out).cuda()
+    base = torch.randn(w.value.shape, device="cuda") if acc else None
+    _say(f"two-pass scan D={D} acc={acc}")
+    gv0 = base.clone() if acc else torch.full(tuple(w.value.shape), float("nan"), device="cuda")
+    gv, gl, ga = msda.backward(**x, grad_out=g, grad_value=gv0, accumulate=acc)
+    torch.cuda.synchronize()
+    rv, rl, ra = oracle_bwd(w)
+    got_v = gv.cpu().numpy() - (base.cpu().numpy() if acc else 0.0)
+    assert np.all(np.isfinite(got_v))
+    close(got_v, rv, BWD_TOL, "grad_value")
+    close(gl.cpu().numpy(), rl, BWD_TOL, "grad_sampling_loc")
+    close(ga.cpu().numpy(), ra, BWD_TOL, "grad_attn_weight")
+
+
 def test_runs_on_the_callers_stream(msda):
     w = workloads.random_case(700, 2, ((9, 9), (4, 4)), 90, 4, 32, 4)
     x = dev_inputs(w)

@@ -163,6 +163,27 @@ def test_volume_accumulate_and_autograd(msda):
         assert max_rel(leaves[name].grad.cpu().numpy(), r) <= BWD_TOL, name
 
 
+@pytest.mark.parametrize("D", [32, 64])
+def test_volume_split_bins(msda, D):
+    # one 1x5x6 level: a single plane tile takes ~1500 x 4 points' records
+    # per head, split over several items (partial tiles combined at D = 32,
+    # atomic adds into zeroed tiles at D = 64); overwrite mode from NaN
+    w = workloads.volume_case(2700 + D, 2, ((1, 5, 6), (2, 8, 9)), 1500, 2, D, 4)
+    x = dev_inputs(w)
+    g = torch.from_numpy(w.grad_out).cuda()
+    _say(f"volume split bins D={D}")
+    gv0 = torch.full(tuple(w.value.shape), float("nan"), device="cuda")
+    gv, gl, ga = msda.backward3d(**x, grad_out=g, grad_value=gv0)
+    torch.cuda.synchronize()
+    rv, rl, ra = ov.backward(*_args(w), w.grad_out, mode=oracle.SPEC)
+    got = gv.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    for name, a, r in (("grad_value", got, rv), ("grad_sampling_loc", gl.cpu().numpy(), rl),
+                       ("grad_attn_weight", ga.cpu().numpy(), ra)):
+        e = max_rel(a, r)
+        assert e <= BWD_TOL, f"{w.name}: {name} max rel {e:.3e}"
+
+
 def test_volume_workload(msda):
     # the voxel workload: pyramid 4x128x128, 2x64x64, 1x32x32, 16,384 bird's-eye
     # queries, M=8, D=32, K=4, forward and backward in full
