@@ -256,7 +256,9 @@ msda_fwd_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
         if (it < nitems) {
             const uint4 *po = s_off + it * dm.PS;
             const float4 *pw = s_w + it * dm.PS;
-#pragma unroll 4
+            // two points (eight rows) per step: measured against 1, 3 and 4 at
+            // the encoder shape (98 us vs 102) and the bf16 training shape (406 vs 425-461)
+#pragma unroll 2
             for (int jj = sub; jj < pc; jj += SPLIT) {
                 const uint4 o = po[jj];
                 const float4 w = pw[jj];
