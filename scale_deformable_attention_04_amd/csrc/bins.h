@@ -267,9 +267,9 @@ struct Work {
     uint32_t *cursor;      // [B][nb_max][M] next free entry while scattering
     uint4 *items;          // [work_max] (bin, first record, records, whole bin)
     uint32_t *work_total;  // [3]: work items, bins on the zero list, split bins listed
-    uint32_t *zero;        // [B * nb_max * M] bins whose tiles are zeroed before the
-                           // grad_value kernel runs (overwrite mode): empty bins, and
-                           // split bins when their items add into grad_value atomically
+    uint32_t *zero;        // [B * nb_max * M] bins whose tiles no work item writes
+                           // outright (overwrite mode): empty bins, and split bins when
+                           // their items add into grad_value atomically
     uint32_t *split;       // [B * nb_max * M] split bins whose items leave partial
                            // tiles, added up by the combine kernel
     uint4 *recs;           // [4 * points] records grouped by bin
@@ -433,9 +433,10 @@ bin_count_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__
 // record, records, whole bin).  In overwrite mode the bins whose pixels no
 // single work item writes outright -- empty bins, and bins split over several
 // items that add into grad_value atomically -- go on the zero list, and their
-// tiles are zeroed before the grad_value kernel adds into them.  When the
-// items of split bins leave partial tiles instead (dm.combine), those bins go
-// on the split list of the combine kernel.
+// tiles are zeroed (by the gather kernel after its items, or by the scatter
+// kernel before the tile kernel adds into them).  When the items of split
+// bins leave partial tiles instead (dm.combine), those bins go on the split
+// list of the combine kernel.
 // ---------------------------------------------------------------------------
 // Exclusive scan of (a, b, c) over the kScanThreads threads of the block:
 // wave-level scans with DPP, then one scan of the wave totals.  The block
@@ -609,7 +610,7 @@ using msda_host::kRecQueryShift;   // cells < 128
 // grad_value kernel, launched after this one, then adds into them.
 struct ZeroList {
     const uint32_t *zero;        // bins, or nullptr: nothing to zero
-    const uint32_t *work_total;  // [2]: work items, entries on the list
+    const uint32_t *work_total;  // [3]: work items, entries on the list, split bins
     float *grad_value;
     int D;
 };
@@ -1035,7 +1036,8 @@ __global__ void __launch_bounds__(gather_threads<CPL>())
 grad_value_gather_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ starts,
                          const float *__restrict__ grad_out, const uint4 *__restrict__ items,
                          const uint32_t *__restrict__ work_total, uint4 *__restrict__ recs,
-                         float *__restrict__ grad_value, Dims dm) {
+                         const uint32_t *__restrict__ zero, float *__restrict__ grad_value,
+                         Dims dm) {
     static_assert(D <= kGatherMaxD && D % 4 == 0, "one (cell, channel group) pair per lane");
     constexpr int kT = gather_threads<CPL>();
     constexpr int kQuads = D / 4;
@@ -1058,8 +1060,10 @@ grad_value_gather_kernel(const int64_t *__restrict__ shapes, const int64_t *__re
 
     const int M = dm.M, Nq = dm.Nq;
     const int tid = threadIdx.x;
-    const uint32_t total = *work_total;
-    if (blockIdx.x >= total) return;  // the grid is sized for the largest possible list
+    // the work items, then (overwrite mode) the tiles of the zero list
+    const uint32_t total = work_total[0];
+    const uint32_t nz = zero ? work_total[1] : 0u;
+    if (blockIdx.x >= total + nz) return;  // the grid is sized for the largest possible list
     stage_bin_levels<VOL>(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
     if (tid < kCells) s_cnt[tid] = 0u;
 
@@ -1077,7 +1081,13 @@ grad_value_gather_kernel(const int64_t *__restrict__ shapes, const int64_t *__re
     // works through one stretch of the list, and of the records, at a time.
     // (Cutting the list into one contiguous stretch per XCD, by head or by
     // tile range, was measured slower.)
-    for (uint32_t w = blockIdx.x; w < total; w += gridDim.x) {
+    for (uint32_t w = blockIdx.x; w < total + nz; w += gridDim.x) {
+        if (w >= total) {
+            // an empty bin: no item writes its tile
+            zero_tile<kT>(grad_value, bin_tile<VOL>(zero[w - total], s_lv, M, dm.nb_max, dm.L),
+                          (size_t)dm.Nv * M * D, M, D, tid);
+            continue;
+        }
         const uint4 it = items[total - 1u - w];  // (bin, first record, records, whole bin)
         const int n = (int)min(it.z, (uint32_t)kChunk);
         // 1. the records, and each one's rank within its cell
@@ -1297,7 +1307,8 @@ hipError_t launch_grad_value(const WorkLayout &wl, int64_t Nq, int64_t M, const 
         if (uses_gather<D>(Nq, M)) {
             hipLaunchKernelGGL((grad_value_gather_kernel<D, VOL, kGatherCPL>),
                                dim3((unsigned)grid), dim3(gather_threads<kGatherCPL>()), 0, s,
-                               shapes, starts, gout, items, work_total, w.recs, gval, dm);
+                               shapes, starts, gout, items, work_total, w.recs,
+                               dm.zero_list ? w.zero : nullptr, gval, dm);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
             // split bins: more than kChunk records each, and at most one per bin
@@ -1409,13 +1420,15 @@ msda_status per_batch(int64_t B, int64_t per_b, F &&launch) {
 }
 
 // The grad_value pipeline on the caller's stream: clear the bin counters,
-// count, scan (work list, zero list), scatter the records (zeroing the
-// listed tiles first), and the grad_value kernel.  In overwrite mode the
-// tiles no single work item writes -- empty and split bins -- must start at
-// zero: with at least two points per pixel and head most bins are full and
-// the scan lists the few others; sparser problems (the decoder's 300
-// queries) leave most bins empty, and grad_value is then zero-filled whole
-// first, by many workgroups at streaming speed.
+// count, scan (work list, zero list, split list), scatter the records, and
+// the grad_value kernel(s).  In overwrite mode the tiles no work item writes
+// outright must be zeroed: the scan lists them (empty bins; with the tile
+// kernel also split bins, whose items add atomically).  The gather kernel
+// zeroes the listed tiles itself, after its work items, with workgroups the
+// items leave free; for the tile kernel the scatter kernel zeroes them first
+// when the problem has at least two points per pixel and head, and sparser
+// problems are zero-filled whole, by many workgroups at streaming speed (the
+// scatter kernel's few workgroups would be slow to zero most of the tiles).
 template <int D, bool VOL>
 msda_status run_bins(const int64_t *shapes, const int64_t *starts, const float *loc,
                      const float *attn, const float *gout, float *gval, int64_t B, int64_t Nv,
@@ -1423,7 +1436,8 @@ msda_status run_bins(const int64_t *shapes, const int64_t *starts, const float *
                      unsigned char *ws, bool accumulate, bool align, const Exec &ex) {
     const hipStream_t s = ex.s;
     const Work w = work_at(wl, ws);
-    const bool zero_list = !accumulate && Nq * L * K >= 2 * Nv;
+    const bool gather = uses_gather<D>(Nq, M);
+    const bool zero_list = !accumulate && (gather || Nq * L * K >= 2 * Nv);
     // the counts region is padded to 256 bytes, so whole float4s can be cleared
     ex.stamp(kStageClear, false, s);
     msda_status st = fill_zero(w.counts, (wl.off_start - wl.off_counts) / 16, s);
@@ -1438,7 +1452,7 @@ msda_status run_bins(const int64_t *shapes, const int64_t *starts, const float *
             accumulate ? 1 : 0, make_fastdiv((uint32_t)(L * K)), make_fastdiv((uint32_t)K)};
     dm.align = align ? 1 : 0;
     dm.zero_list = zero_list ? 1 : 0;
-    dm.combine = uses_gather<D>(Nq, M) ? 1 : 0;
+    dm.combine = gather ? 1 : 0;
     ex.stamp(kStageCount, false, s);
     st = per_batch(B, gb * M, [&](int64_t b0, unsigned grid) {
         Dims d2 = dm;
@@ -1462,8 +1476,8 @@ msda_status run_bins(const int64_t *shapes, const int64_t *starts, const float *
         Dims d2 = dm;
         d2.b0 = (int)b0;
         // the first launch zeroes every listed tile of the whole problem
-        const ZeroList zl{(zero_list && b0 == 0) ? w.zero : nullptr, w.work_total, gval,
-                          (int)D};
+        const ZeroList zl{(zero_list && !gather && b0 == 0) ? w.zero : nullptr, w.work_total,
+                          gval, (int)D};
         hipLaunchKernelGGL(bin_scatter_kernel<VOL>, dim3(grid), dim3(kThreads),
                            8 * (size_t)hist_cap, s, shapes, starts, loc, attn, w.cursor, w.recs,
                            hist_cap, zl, d2);
