@@ -360,8 +360,9 @@ msda_status msda_backward_fused(const void *value, int value_dtype,
  * eight neighbours (grad_loc.z carries the factor Z_l, or Z_l - 1 with
  * MSDA_ALIGN_CORNERS).  grad_value is overwritten unless flags has
  * MSDA_BWD_ACCUMULATE; it is summed per 8x8 tile of each plane as in the 2-D
- * backward (atomic adds only where a tile is split), so its last bits may
- * differ between calls; grad_sampling_loc and grad_attn_weight are
+ * backward (the records of a tile arrive in no fixed order; with heads of 64
+ * channels or more a tile split over several work items is also added to
+ * atomically), so its last bits may differ between calls; grad_sampling_loc and grad_attn_weight are
  * overwritten and deterministic.  workspace: at least
  * msda3d_backward_workspace_size(...) bytes (128 bytes per point -- up to
  * eight 16-byte records, two planes of four tiles -- plus about 16 bytes
