@@ -54,9 +54,12 @@
  * The backward entry points can also use a second, caller-owned stream
  * (side_stream, with two caller-created hipEvent_t in side_events[0..1]):
  * the grad_attn_weight / grad_sampling_loc kernel then runs there,
- * concurrently with the grad_value kernels on `stream`.  The call forks
- * side_stream from `stream` (side_events[0]) and joins it back into `stream`
- * (side_events[1]) before returning -- on its error paths too -- so work
+ * concurrently with the grad_value kernels on `stream`, on problems of at
+ * least 2^18 sampling points (B * Nq * M * L * K); smaller ones run on
+ * `stream` alone, as the fork and join would cost more than they save.
+ * When it uses side_stream the call forks it from `stream` (side_events[0])
+ * and joins it back into `stream` (side_events[1]) before returning -- on
+ * its error paths too -- so work
  * enqueued on `stream` afterwards sees every output complete (this also
  * holds under stream capture).  side_stream NULL (or equal to `stream`):
  * everything runs on `stream`, side_events is ignored.  A side stream and its
@@ -203,7 +206,8 @@ msda_status msda_backward_noalloc(const void *value, int value_dtype,
  * work on the same streams, which in addition records caller-owned HIP events
  * around each of its MSDA_BWD_STAGES stages: events[2i] just before the
  * stage's kernel and events[2i + 1] just after it, on the stream that runs it
- * (stage 0 runs on side_stream when one is given, the others on `stream`).
+ * (stage 0 runs on side_stream when the call uses one, the others on
+ * `stream`).
  * Nothing is synchronized; once the caller has waited for `stream`,
  * hipEventElapsedTime(events[2i], events[2i + 1]) is the duration of stage i.
  * Stages:

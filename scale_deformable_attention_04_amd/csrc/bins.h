@@ -330,16 +330,21 @@ __device__ __forceinline__ void zero_tile(float *__restrict__ grad_value, const 
 }
 // ---------------------------------------------------------------------------
 // backward: points per bin
-// Workgroup = (batch b, head m, kBinPoints consecutive points of the
-// (b, m) list in (query, level, point) order), kBinPPT points per thread,
+// Workgroup = (batch b, head m, PPT * kThreads consecutive points of the
+// (b, m) list in (query, level, point) order), PPT points per thread,
 // all of whose coordinates are loaded before any is used.
 // ---------------------------------------------------------------------------
+// Points per thread: kBinPPT, or kBinPPTSmall where that would leave fewer
+// than kBinMinGrid workgroups (small problems such as the decoder's 300
+// queries, 32 workgroups: more workgroups, each with fewer points in flight;
+// the voxel workload's 384 measured slower with more).
 constexpr int kBinPPT = 16;
-constexpr int kBinPoints = kBinPPT * kThreads;
+constexpr int kBinPPTSmall = 1;
+constexpr int kBinMinGrid = 128;
 
 // VOL: volume levels; a location is (u, v, w) and a point feeds the tiles of
 // its two planes.
-template <bool VOL>
+template <bool VOL, int PPT>
 __global__ void __launch_bounds__(kThreads)
 bin_count_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ starts,
                  const float *__restrict__ loc, uint32_t *__restrict__ counts, int hist_cap,
@@ -352,14 +357,14 @@ bin_count_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__
     const int wg = xcd_contiguous(blockIdx.x, gridDim.x);
     const int bm = wg / dm.nblk + dm.b0 * M;
     const int m = bm % M, b = bm / M;
-    const int f0 = (wg % dm.nblk) * kBinPoints;
+    const int f0 = (wg % dm.nblk) * (PPT * kThreads);
     const int nf = Nq * LK;
     const size_t row0 = (size_t)b * Nq * M + m;  // item row of query 0
 
-    float2 uv[kBinPPT];
-    float wz[kBinPPT];  // VOL: the z coordinate
+    float2 uv[PPT];
+    float wz[PPT];  // VOL: the z coordinate
 #pragma unroll
-    for (int r = 0; r < kBinPPT; ++r) {
+    for (int r = 0; r < PPT; ++r) {
         const int f = f0 + threadIdx.x + r * kThreads;
         uv[r] = make_float2(0.f, 0.f);
         wz[r] = 0.f;
@@ -383,7 +388,7 @@ bin_count_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__
         __syncthreads();
     }
 #pragma unroll
-    for (int r = 0; r < kBinPPT; ++r) {
+    for (int r = 0; r < PPT; ++r) {
         const int f = f0 + threadIdx.x + r * kThreads;
         if (f < nf) {
             const int q = (int)fdiv((uint32_t)f, dm.div_lk), j = f - q * LK;
@@ -615,7 +620,7 @@ struct ZeroList {
     int D;
 };
 
-template <bool VOL>
+template <bool VOL, int PPT>
 __global__ void __launch_bounds__(kThreads)
 bin_scatter_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ starts,
                    const float *__restrict__ loc, const float *__restrict__ attn,
@@ -630,16 +635,16 @@ bin_scatter_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict
     const int wg = xcd_contiguous(blockIdx.x, gridDim.x);
     const int bm = wg / dm.nblk + dm.b0 * M;
     const int m = bm % M, b = bm / M;
-    const int f0 = (wg % dm.nblk) * kBinPoints;
+    const int f0 = (wg % dm.nblk) * (PPT * kThreads);
     const int nf = Nq * LK;
     const size_t row0 = (size_t)b * Nq * M + m;  // item row of query 0
 
     // the thread's points: coordinates and weights, kept for both passes
-    float2 uv[kBinPPT];
-    float aw[kBinPPT];
-    float wz[kBinPPT];  // VOL: the z coordinate
+    float2 uv[PPT];
+    float aw[PPT];
+    float wz[PPT];  // VOL: the z coordinate
 #pragma unroll
-    for (int r = 0; r < kBinPPT; ++r) {
+    for (int r = 0; r < PPT; ++r) {
         const int f = f0 + threadIdx.x + r * kThreads;
         uv[r] = make_float2(0.f, 0.f);
         aw[r] = 0.f;
@@ -671,7 +676,7 @@ bin_scatter_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict
         for (int i = threadIdx.x; i < nbins; i += kThreads) s_cnt[i] = 0u;
         __syncthreads();
 #pragma unroll
-        for (int r = 0; r < kBinPPT; ++r) {
+        for (int r = 0; r < PPT; ++r) {
             const int f = f0 + threadIdx.x + r * kThreads;
             if (f < nf) {
                 const int q = (int)fdiv((uint32_t)f, dm.div_lk), j = f - q * LK;
@@ -705,7 +710,7 @@ bin_scatter_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict
         __syncthreads();
     }
 #pragma unroll
-    for (int r = 0; r < kBinPPT; ++r) {
+    for (int r = 0; r < PPT; ++r) {
         const int f = f0 + threadIdx.x + r * kThreads;
         if (f < nf) {
             const int q = (int)fdiv((uint32_t)f, dm.div_lk), j = f - q * LK;
@@ -1387,8 +1392,18 @@ inline msda_status exec_side(Exec &ex, void *side_stream, void *const *side_even
     return MSDA_OK;
 }
 
-// The side stream waits for everything enqueued on s so far.
-inline msda_status exec_fork(const Exec &ex) {
+// Below this many sampling points (B * Nq * M * L * K) the backward runs on
+// s alone: the fork and join cost more host time (two cross-stream waits,
+// about 8 us each to enqueue) than running the grad_attn / grad_loc kernel
+// beside the grad_value kernels saves.  Measured with the encoder's levels,
+// B = 2, M = 8, L = K = 4: one stream 5 us faster at 300 queries (77k
+// points), even at 1000, the side stream 5 us faster from 2000 on.
+constexpr int64_t kSideMinPoints = (int64_t)1 << 18;
+
+// The side stream, if the problem is large enough to use it, waits for
+// everything enqueued on s so far; otherwise the side stream is dropped.
+inline msda_status exec_fork(Exec &ex, int64_t points) {
+    if (points < kSideMinPoints) ex.side = nullptr;
     if (!ex.side) return MSDA_OK;
     msda_status st = hip_status(hipEventRecord(ex.fork, ex.s));
     if (st == MSDA_OK) st = hip_status(hipStreamWaitEvent(ex.side, ex.fork, 0));
@@ -1447,7 +1462,10 @@ msda_status run_bins(const int64_t *shapes, const int64_t *starts, const float *
     ex.stamp(kStageClear, true, s);
 
     const int hist_cap = (int)(wl.nb_max < kHistLds ? wl.nb_max : kHistLds);
-    const int64_t gb = (Nq * L * K + kBinPoints - 1) / kBinPoints;  // per (batch, head)
+    const int64_t pts_bm = Nq * L * K;  // points per (batch, head)
+    const int64_t big = kBinPPT * kThreads, small = kBinPPTSmall * kThreads;
+    const bool few = B * M * ((pts_bm + big - 1) / big) < kBinMinGrid;
+    const int64_t gb = (pts_bm + (few ? small : big) - 1) / (few ? small : big);  // per (b, m)
     Dims dm{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, 0, 0, 0, (int)gb, (int)wl.nb_max,
             accumulate ? 1 : 0, make_fastdiv((uint32_t)(L * K)), make_fastdiv((uint32_t)K)};
     dm.align = align ? 1 : 0;
@@ -1457,8 +1475,14 @@ msda_status run_bins(const int64_t *shapes, const int64_t *starts, const float *
     st = per_batch(B, gb * M, [&](int64_t b0, unsigned grid) {
         Dims d2 = dm;
         d2.b0 = (int)b0;
-        hipLaunchKernelGGL(bin_count_kernel<VOL>, dim3(grid), dim3(kThreads),
-                           4 * (size_t)hist_cap, s, shapes, starts, loc, w.counts, hist_cap, d2);
+        if (few)
+            hipLaunchKernelGGL((bin_count_kernel<VOL, kBinPPTSmall>), dim3(grid), dim3(kThreads),
+                               4 * (size_t)hist_cap, s, shapes, starts, loc, w.counts, hist_cap,
+                               d2);
+        else
+            hipLaunchKernelGGL((bin_count_kernel<VOL, kBinPPT>), dim3(grid), dim3(kThreads),
+                               4 * (size_t)hist_cap, s, shapes, starts, loc, w.counts, hist_cap,
+                               d2);
     });
     if (st != MSDA_OK) return st;
     ex.stamp(kStageCount, true, s);
@@ -1478,9 +1502,14 @@ msda_status run_bins(const int64_t *shapes, const int64_t *starts, const float *
         // the first launch zeroes every listed tile of the whole problem
         const ZeroList zl{(zero_list && !gather && b0 == 0) ? w.zero : nullptr, w.work_total,
                           gval, (int)D};
-        hipLaunchKernelGGL(bin_scatter_kernel<VOL>, dim3(grid), dim3(kThreads),
-                           8 * (size_t)hist_cap, s, shapes, starts, loc, attn, w.cursor, w.recs,
-                           hist_cap, zl, d2);
+        if (few)
+            hipLaunchKernelGGL((bin_scatter_kernel<VOL, kBinPPTSmall>), dim3(grid),
+                               dim3(kThreads), 8 * (size_t)hist_cap, s, shapes, starts, loc, attn,
+                               w.cursor, w.recs, hist_cap, zl, d2);
+        else
+            hipLaunchKernelGGL((bin_scatter_kernel<VOL, kBinPPT>), dim3(grid), dim3(kThreads),
+                               8 * (size_t)hist_cap, s, shapes, starts, loc, attn, w.cursor,
+                               w.recs, hist_cap, zl, d2);
     });
     if (st != MSDA_OK) return st;
     ex.stamp(kStageScatter, true, s);

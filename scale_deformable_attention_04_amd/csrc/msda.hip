@@ -1178,7 +1178,7 @@ msda_status backward_impl(const void *value, int value_dtype, const int64_t *spa
         }
         return st;
     }
-    st = exec_fork(ex);
+    st = exec_fork(ex, B * Nq * M * L * K);
     if (st != MSDA_OK) return st;
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     if (value_dtype == MSDA_F32)

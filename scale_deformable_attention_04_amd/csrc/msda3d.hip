@@ -496,7 +496,7 @@ msda_status msda3d_backward(const void *value, int value_dtype, const int64_t *v
     if (st != MSDA_OK) return st;
     const bool acc = (flags & MSDA_BWD_ACCUMULATE) != 0;
     if (!work) return acc ? MSDA_OK : fill_zero(grad_value, (size_t)nval / 4, s);  // D % 4 == 0
-    st = exec_fork(ex);
+    st = exec_fork(ex, B * Nq * M * L * K);
     if (st != MSDA_OK) return st;
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     const bool align = (flags & MSDA_ALIGN_CORNERS) != 0;

@@ -558,8 +558,9 @@ def test_overwrite_replaces_every_element(msda, side):
     """Overwrite mode writes every element of grad_value: a NaN-filled buffer
     comes back equal to the oracle.  The points crowd into a corner of each
     map, so most 8x8 tiles receive nothing (zeroed from the zero list), and
-    the small coarse level's one tile is split over several work items."""
-    w = workloads.random_case(1300, 2, ((48, 64), (24, 32), (5, 6)), 1500, 2, 32, 4,
+    the small coarse level's one tile is split over several work items.
+    288,000 points: enough for the backward to use the side stream."""
+    w = workloads.random_case(1300, 2, ((48, 64), (24, 32), (5, 6)), 1500, 8, 32, 4,
                               0.0, 0.3)
     x = dev_inputs(w)
     g = torch.from_numpy(w.grad_out).cuda()
