@@ -128,10 +128,28 @@ msda_status msda_forward(const void *value, int value_dtype,
  * nothing is launched or the sizes are invalid).  It depends on the sizes
  * only, not on the level table: 64 bytes per sampling point (room for one
  * 16-byte record per 8x8 value tile the point's neighbours touch, at most
- * four) plus about 32 bytes per tile bound and head.
+ * four) plus about 32 bytes per tile bound and head.  This is the size for
+ * the fastest call, which sorts every point's records at once.
  */
 size_t msda_backward_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
                                     int64_t L, int64_t K);
+
+/*
+ * The smallest workspace msda_backward accepts for these sizes (0 as for
+ * msda_backward_workspace_size): the layout of one pass over one head of one
+ * batch and min(Nq, 1024) queries.  Given less than
+ * msda_backward_workspace_size, the backward computes grad_value in passes,
+ * one after another on `stream`, each over a box of batches x heads x
+ * queries whose layout fits the workspace, as few as the workspace allows:
+ * groups of whole batches; else ranges of queries of one batch with every
+ * head (the passes after a range's first adding to grad_value); else, below
+ * room for 1024 queries of every head, groups of heads and ranges of
+ * queries.  The gradients are the same up to summation order; each pass
+ * costs its own launches (at the encoder shape about 60 us: 345 us in one
+ * pass, 716 us in the 6 passes of 64 MiB).
+ */
+size_t msda_backward_workspace_min(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
+                                   int64_t L, int64_t K);
 
 /*
  * Backward of msda_forward for the upstream gradient grad_out.  The pages give
@@ -146,9 +164,10 @@ size_t msda_backward_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int64_t M
  * At an integer pixel coordinate the derivative is the one of the cell
  * [x0, x0+1) chosen by the floor.
  *
- * workspace: a DEVICE buffer of at least msda_backward_workspace_size(...)
- * bytes, 256-byte aligned, owned by the caller; its contents on entry do not
- * matter and are clobbered.  Calls that overlap in time (other streams) need
+ * workspace: a DEVICE buffer of at least msda_backward_workspace_min(...)
+ * bytes (msda_backward_workspace_size(...) for a single pass), 256-byte
+ * aligned, owned by the caller; its contents on entry do not matter and are
+ * clobbered; workspace_bytes is its size.  Calls that overlap in time (other streams) need
  * separate workspaces.
  *
  * flags: MSDA_BWD_ACCUMULATE and/or MSDA_ALIGN_CORNERS (the latter as given to
@@ -186,8 +205,9 @@ msda_status msda_backward(const void *value, int value_dtype,
  * each GPU it runs on until the process ends.  The call allocates nothing
  * (the array's address is looked up once per device, on the first call with
  * that device current).  Problems whose msda_backward_workspace_size exceeds
- * MSDA_NOALLOC_SCRATCH_BYTES are rejected with MSDA_ERR_SCRATCH before any
- * work is enqueued.  Every call on one GPU uses the same array, and each call
+ * MSDA_NOALLOC_SCRATCH_BYTES run in passes (see msda_backward_workspace_min);
+ * those whose msda_backward_workspace_min exceeds it are rejected with
+ * MSDA_ERR_SCRATCH before any work is enqueued.  Every call on one GPU uses the same array, and each call
  * clears what it needs: calls that overlap in time on one GPU (other streams,
  * other threads) race on it and must not be made.
  */
@@ -216,7 +236,9 @@ msda_status msda_backward_noalloc(const void *value, int value_dtype,
  *   list of tiles to zero)   4 zeroing of the listed tiles, then the record
  *   scatter into tiles   5 grad_value tiles
  * A small problem (see msda_backward) runs as one kernel, recorded as stage 0;
- * its other stages are empty.
+ * its other stages are empty.  With grad_value in several passes (a
+ * workspace below msda_backward_workspace_size), stages 1-5 are recorded
+ * from their start in the first pass to their end in the last.
  * events: 2 * MSDA_BWD_STAGES hipEvent_t created by the caller (with timing);
  * a null entry is skipped (an event record costs the stream a few
  * microseconds, so a caller timing one stage passes only its two events).
@@ -288,10 +310,15 @@ msda_status msda_forward_fused(const void *value, int value_dtype,
 
 /*
  * Workspace bytes of msda_backward_fused: msda_backward_workspace_size plus
- * 12 bytes per sampling point (the locations and weights, recomputed).
+ * 12 bytes per sampling point (the locations and weights, recomputed) and
+ * 8 bytes per (batch, query, head, level).  _min: the same with
+ * msda_backward_workspace_min in place of msda_backward_workspace_size (the
+ * grad_value pipeline then runs in passes, as for msda_backward).
  */
 size_t msda_backward_fused_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int64_t M,
                                           int64_t D, int64_t L, int64_t K);
+size_t msda_backward_fused_workspace_min(int64_t B, int64_t Nv, int64_t Nq, int64_t M,
+                                         int64_t D, int64_t L, int64_t K);
 
 /*
  * Backward of msda_forward_fused: the chain rule through the prologue on top
@@ -312,8 +339,9 @@ size_t msda_backward_fused_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int
  * msda_forward_fused stored for these same inputs and flags (then they are
  * read instead; anything else gives the gradients at those locations and
  * weights, not at the raw inputs').
- * workspace: at least msda_backward_fused_workspace_size(...) bytes, 256-byte
- * aligned, as for msda_backward.
+ * workspace: at least msda_backward_fused_workspace_min(...) bytes
+ * (msda_backward_fused_workspace_size(...) for one pass), 256-byte aligned,
+ * as for msda_backward.
  * events: NULL, or 2 * MSDA_BWD_FUSED_STAGES caller-owned HIP events recorded
  * around the stages as msda_backward_events does (null entries skipped):
  * stages 0-5 as there, 6 the prologue (locations and weights into the
@@ -368,14 +396,17 @@ msda_status msda_backward_fused(const void *value, int value_dtype,
  * channels or more a tile split over several work items is also added to
  * atomically), so its last bits may differ between calls; grad_sampling_loc and grad_attn_weight are
  * overwritten and deterministic.  workspace: at least
- * msda3d_backward_workspace_size(...) bytes (128 bytes per point -- up to
- * eight 16-byte records, two planes of four tiles -- plus about 16 bytes
- * per voxel and head), 256-byte aligned, caller-owned, contents irrelevant.
- * stream, side_stream, side_events as for msda_backward; also needs
- * Nq <= 2^25.
+ * msda3d_backward_workspace_min(...) bytes, msda3d_backward_workspace_size(...)
+ * for one pass (128 bytes per point -- up to eight 16-byte records, two
+ * planes of four tiles -- plus about 16 bytes per voxel and head); with less
+ * than the latter grad_value is computed in passes as for msda_backward;
+ * 256-byte aligned, caller-owned, contents irrelevant.  stream, side_stream,
+ * side_events as for msda_backward; also needs Nq <= 2^25.
  */
 size_t msda3d_backward_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
                                       int64_t L, int64_t K);
+size_t msda3d_backward_workspace_min(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
+                                     int64_t L, int64_t K);
 
 msda_status msda3d_forward(const void *value, int value_dtype,
                            const int64_t *volume_shapes, const int64_t *level_start_index,

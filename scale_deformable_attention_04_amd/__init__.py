@@ -15,14 +15,16 @@ from ._binding import (BWD_FUSED_STAGES, BWD_STAGES, EXPORTED, LIB_PATH, MSDA_AL
                        MSDA_SOFTMAX_PER_LEVEL, MSDAError, NOALLOC_SCRATCH_BYTES,
                        backward, backward3d, backward_fused, backward_noalloc, dat_attention,
                        dat_attention_backward, dat_sample, dat_sample_backward, forward,
-                       forward3d, forward_fused, fused_workspace_size, load, make_events,
-                       stage_times, status_string, validate_host, validate_host3d,
-                       workspace_size)
+                       forward3d, forward_fused, fused_workspace_min, fused_workspace_size,
+                       load, make_events, stage_times, status_string, validate_host,
+                       validate_host3d, workspace_min, workspace_min3d, workspace_size,
+                       workspace_size3d)
 
 __all__ = ["forward", "backward", "backward_noalloc", "NOALLOC_SCRATCH_BYTES",
            "forward_fused", "backward_fused", "BWD_STAGES",
            "BWD_FUSED_STAGES", "make_events", "stage_times", "workspace_size",
-           "fused_workspace_size", "validate_host", "status_string", "load",
+           "workspace_min", "fused_workspace_size", "fused_workspace_min", "workspace_size3d",
+           "workspace_min3d", "validate_host", "status_string", "load",
            "MSDAError",
            "ms_deform_attn", "MSDeformAttnFunction", "ms_deform_attn_fused",
            "MSDeformAttnFusedFunction", "forward3d", "backward3d", "validate_host3d",

@@ -32,9 +32,11 @@ MSDA_ALIGN_CORNERS = 2
 MSDA_SOFTMAX_PER_LEVEL = 4
 MSDA_BWD_BINNED = 8
 
-EXPORTED = ("msda_forward", "msda_backward_workspace_size", "msda_backward",
-            "msda_backward_noalloc", "msda_backward_events", "msda_forward_fused", "msda_backward_fused_workspace_size",
-            "msda_backward_fused", "msda3d_forward", "msda3d_backward_workspace_size",
+EXPORTED = ("msda_forward", "msda_backward_workspace_size", "msda_backward_workspace_min",
+            "msda_backward", "msda_backward_noalloc", "msda_backward_events",
+            "msda_forward_fused", "msda_backward_fused_workspace_size",
+            "msda_backward_fused_workspace_min", "msda_backward_fused", "msda3d_forward",
+            "msda3d_backward_workspace_size", "msda3d_backward_workspace_min",
             "msda3d_backward", "msda3d_validate_host",
             "msda_dat_attention_forward", "msda_dat_attention_workspace_size",
             "msda_dat_attention_backward",
@@ -77,10 +79,14 @@ def load():
     lib.msda_backward_events.restype = ci
     lib.msda_backward_workspace_size.argtypes = [i64] * 7
     lib.msda_backward_workspace_size.restype = ctypes.c_size_t
+    lib.msda_backward_workspace_min.argtypes = [i64] * 7
+    lib.msda_backward_workspace_min.restype = ctypes.c_size_t
     lib.msda_forward_fused.argtypes = [p, ci, p, p, p, p, p, p, p, p, p] + [i64] * 7 + [u32, p]
     lib.msda_forward_fused.restype = ci
     lib.msda_backward_fused_workspace_size.argtypes = [i64] * 7
     lib.msda_backward_fused_workspace_size.restype = ctypes.c_size_t
+    lib.msda_backward_fused_workspace_min.argtypes = [i64] * 7
+    lib.msda_backward_fused_workspace_min.restype = ctypes.c_size_t
     lib.msda_backward_fused.argtypes = ([p, ci, p, p, p, p, p, p, p, p, p, p, p, p, p, p] +
                                         [i64] * 7 +
                                         [p, ctypes.c_size_t, u32, p, p, p, p])
@@ -91,6 +97,8 @@ def load():
                                     [p, ctypes.c_size_t, u32, p, p, p])
     lib.msda3d_backward_workspace_size.argtypes = [i64] * 7
     lib.msda3d_backward_workspace_size.restype = ctypes.c_size_t
+    lib.msda3d_backward_workspace_min.argtypes = [i64] * 7
+    lib.msda3d_backward_workspace_min.restype = ctypes.c_size_t
     lib.msda3d_backward.restype = ci
     lib.msda3d_validate_host.argtypes = [p, p] + [i64] * 7
     lib.msda3d_validate_host.restype = ci
@@ -166,8 +174,25 @@ _sides = {}
 
 
 def workspace_size(B, Nv, Nq, M, D, L, K) -> int:
-    """msda_backward_workspace_size: bytes of scratch the backward needs."""
+    """msda_backward_workspace_size: bytes of scratch the backward needs to
+    compute grad_value in one pass."""
     return int(load().msda_backward_workspace_size(B, Nv, Nq, M, D, L, K))
+
+
+def workspace_min(B, Nv, Nq, M, D, L, K) -> int:
+    """msda_backward_workspace_min: the least scratch the backward accepts
+    (grad_value then computed in passes)."""
+    return int(load().msda_backward_workspace_min(B, Nv, Nq, M, D, L, K))
+
+
+def _given_workspace(workspace, dev, size: int, least: int):
+    """The caller's workspace (checked: >= least bytes), else the cached
+    one of `size` bytes."""
+    if workspace is None:
+        return _workspace(dev, size)
+    if workspace.device != dev or workspace.dtype != torch.uint8 or workspace.numel() < least:
+        raise ValueError(f"workspace must be a uint8 tensor on {dev} of >= {least} bytes")
+    return workspace
 
 
 def _workspace(dev: torch.device, nbytes: int) -> Optional[torch.Tensor]:
@@ -299,8 +324,10 @@ def backward(value: torch.Tensor, spatial_shapes: torch.Tensor, level_start_inde
     align_corners must be the value given to the forward.
     binned=True runs the binned grad_value pipeline even where the library
     would take its one-kernel path for small problems.
-    workspace: a uint8 device tensor of at least workspace_size(...) bytes; by
-    default a buffer this module caches per (device, current stream).
+    workspace: a uint8 device tensor of at least workspace_min(...) bytes
+    (workspace_size(...) for grad_value in one pass, the fastest); by default
+    a buffer of workspace_size(...) bytes this module caches per (device,
+    current stream).
     events: 2 * len(BWD_STAGES) torch.cuda.Event(enable_timing=True) objects
     or None; if given, msda_backward_events is called instead, which records
     events 2i and 2i + 1 around stage i (see stage_times), skipping None.
@@ -326,11 +353,8 @@ def backward(value: torch.Tensor, spatial_shapes: torch.Tensor, level_start_inde
         _need(grad_attn_weight, "grad_attn_weight", torch.float32, dev, attn_weight.shape)
     flags = ((MSDA_BWD_ACCUMULATE if accumulate else 0) |
              (MSDA_ALIGN_CORNERS if align_corners else 0) | (MSDA_BWD_BINNED if binned else 0))
-    need = workspace_size(B, Nv, Nq, M, D, L, K)
-    if workspace is None:
-        workspace = _workspace(dev, need)
-    elif workspace.device != dev or workspace.dtype != torch.uint8 or workspace.numel() < need:
-        raise ValueError(f"workspace must be a uint8 tensor on {dev} of >= {need} bytes")
+    workspace = _given_workspace(workspace, dev, workspace_size(B, Nv, Nq, M, D, L, K),
+                                 workspace_min(B, Nv, Nq, M, D, L, K))
     ws_bytes = workspace.numel() if workspace is not None else 0
     args = [_ptr(value), _dtype_code(value), _ptr(spatial_shapes), _ptr(level_start_index),
             _ptr(sampling_loc), _ptr(attn_weight), _ptr(grad_out), _ptr(grad_value),
@@ -359,8 +383,9 @@ def backward_noalloc(value: torch.Tensor, spatial_shapes: torch.Tensor,
                      align_corners: bool = False, binned: bool = False, side_stream=None
                      ) -> None:
     """msda_backward_noalloc into caller-allocated outputs: the backward with its
-    workspace in the library's static per-GPU scratch (problems needing more
-    than NOALLOC_SCRATCH_BYTES raise MSDAError with MSDA_ERR_SCRATCH).  The
+    workspace in the library's static per-GPU scratch: problems whose
+    workspace_size exceeds NOALLOC_SCRATCH_BYTES run in passes, those whose
+    workspace_min exceeds it raise MSDAError with MSDA_ERR_SCRATCH.  The
     call itself allocates nothing; calls overlapping in time on one GPU must
     not be made.  side_stream defaults to None here (everything on the
     current stream); a torch.cuda.Stream or "auto" work as for backward()."""
@@ -456,6 +481,11 @@ def fused_workspace_size(B, Nv, Nq, M, D, L, K) -> int:
     return int(load().msda_backward_fused_workspace_size(B, Nv, Nq, M, D, L, K))
 
 
+def fused_workspace_min(B, Nv, Nq, M, D, L, K) -> int:
+    """msda_backward_fused_workspace_min."""
+    return int(load().msda_backward_fused_workspace_min(B, Nv, Nq, M, D, L, K))
+
+
 def backward_fused(value: torch.Tensor, spatial_shapes: torch.Tensor,
                    level_start_index: torch.Tensor, reference_points: torch.Tensor,
                    sampling_offsets: torch.Tensor, attn_logits: torch.Tensor,
@@ -468,7 +498,8 @@ def backward_fused(value: torch.Tensor, spatial_shapes: torch.Tensor,
     """msda_backward_fused: (grad_value, grad_sampling_offsets, grad_attn_logits,
     grad_reference_points or None when need_grad_ref is False), and
     grad_scale as a fifth element when scale (the forward's) is given.
-    side_stream as for backward().
+    side_stream as for backward(); workspace too, with fused_workspace_min /
+    fused_workspace_size.
     saved: the (sampling_loc, attn_weight) forward_fused(save=True) returned
     for these inputs, or None to recompute them.
     events: 2 * len(BWD_FUSED_STAGES) timing events or None (see stage_times)."""
@@ -493,11 +524,8 @@ def backward_fused(value: torch.Tensor, spatial_shapes: torch.Tensor,
     g_ref = torch.empty_like(reference_points) if need_grad_ref else None
     g_scale = torch.empty_like(scale) if scale is not None else None
     flags = _fused_flags(per_level, align_corners) | (MSDA_BWD_ACCUMULATE if accumulate else 0)
-    need = fused_workspace_size(B, Nv, Nq, M, D, L, K)
-    if workspace is None:
-        workspace = _workspace(dev, need)
-    elif workspace.device != dev or workspace.dtype != torch.uint8 or workspace.numel() < need:
-        raise ValueError(f"workspace must be a uint8 tensor on {dev} of >= {need} bytes")
+    workspace = _given_workspace(workspace, dev, fused_workspace_size(B, Nv, Nq, M, D, L, K),
+                                 fused_workspace_min(B, Nv, Nq, M, D, L, K))
     ws_bytes = workspace.numel() if workspace is not None else 0
     with torch.cuda.device(dev):
         stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
@@ -582,13 +610,19 @@ def workspace_size3d(B, Nv, Nq, M, D, L, K) -> int:
     return int(load().msda3d_backward_workspace_size(B, Nv, Nq, M, D, L, K))
 
 
+def workspace_min3d(B, Nv, Nq, M, D, L, K) -> int:
+    """msda3d_backward_workspace_min."""
+    return int(load().msda3d_backward_workspace_min(B, Nv, Nq, M, D, L, K))
+
+
 def backward3d(value: torch.Tensor, volume_shapes: torch.Tensor, level_start_index: torch.Tensor,
                sampling_loc: torch.Tensor, attn_weight: torch.Tensor, grad_out: torch.Tensor,
                grad_value: Optional[torch.Tensor] = None, accumulate: bool = False,
                validate: bool = True, align_corners: bool = False,
                workspace: Optional[torch.Tensor] = None, side_stream="auto"):
     """msda3d_backward: (grad_value fp32 [B,Nv,M,D], grad_sampling_loc, grad_attn_weight).
-    side_stream as for backward()."""
+    side_stream as for backward(); workspace too, with workspace_min3d /
+    workspace_size3d."""
     lib = load()
     dev, (B, Nv, Nq, M, D, L, K) = _check_inputs3d(value, volume_shapes, level_start_index,
                                                   sampling_loc, attn_weight, validate)
@@ -602,11 +636,8 @@ def backward3d(value: torch.Tensor, volume_shapes: torch.Tensor, level_start_ind
     g_loc = torch.empty_like(sampling_loc)
     g_attn = torch.empty_like(attn_weight)
     flags = (MSDA_BWD_ACCUMULATE if accumulate else 0) | (MSDA_ALIGN_CORNERS if align_corners else 0)
-    need = workspace_size3d(B, Nv, Nq, M, D, L, K)
-    if workspace is None:
-        workspace = _workspace(dev, need)
-    elif workspace.device != dev or workspace.dtype != torch.uint8 or workspace.numel() < need:
-        raise ValueError(f"workspace must be a uint8 tensor on {dev} of >= {need} bytes")
+    workspace = _given_workspace(workspace, dev, workspace_size3d(B, Nv, Nq, M, D, L, K),
+                                 workspace_min3d(B, Nv, Nq, M, D, L, K))
     ws_bytes = workspace.numel() if workspace is not None else 0
     with torch.cuda.device(dev):
         stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)

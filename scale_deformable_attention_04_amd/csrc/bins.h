@@ -258,6 +258,10 @@ struct Dims {
     int softmax_run; // dots kernel: softmax backward over runs of this many points (0: none)
     int zero_list;   // scan: list the bins to zero (overwrite mode, grad_value not filled)
     int combine;     // split bins: partial tiles added up by the combine kernel
+    // bin pipeline: the tensors' head count and queries per batch (strides
+    // of loc, attn, grad_out and grad_value) when M and Nq are those of a
+    // pass over some of them
+    int Ms, Nqs;
 };
 
 // Workspace of the backward pipeline (all 32-bit words).
@@ -314,7 +318,8 @@ __device__ __forceinline__ BinTile bin_tile(uint32_t bin, const LevelLds &lv, in
 }
 
 // Zero the channels of head t.m of the tile's pixels inside the map, with
-// NT threads (thread index tid); D channels per head, M heads per row.
+// NT threads (thread index tid); D channels per head, M heads per row
+// (the tensor's head stride).
 template <int NT>
 __device__ __forceinline__ void zero_tile(float *__restrict__ grad_value, const BinTile &t,
                                           size_t slice_v, int M, int D, int tid) {
@@ -359,7 +364,7 @@ bin_count_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__
     const int m = bm % M, b = bm / M;
     const int f0 = (wg % dm.nblk) * (PPT * kThreads);
     const int nf = Nq * LK;
-    const size_t row0 = (size_t)b * Nq * M + m;  // item row of query 0
+    const size_t row0 = (size_t)b * dm.Nqs * dm.Ms + m;  // item row of query 0
 
     float2 uv[PPT];
     float wz[PPT];  // VOL: the z coordinate
@@ -370,7 +375,7 @@ bin_count_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__
         wz[r] = 0.f;
         if (f < nf) {
             const int q = (int)fdiv((uint32_t)f, dm.div_lk), j = f - q * LK;
-            const size_t p = (row0 + (size_t)q * M) * LK + j;
+            const size_t p = (row0 + (size_t)q * dm.Ms) * LK + j;
             if constexpr (VOL) {
                 uv[r] = make_float2(loc[3 * p], loc[3 * p + 1]);
                 wz[r] = loc[3 * p + 2];
@@ -637,7 +642,7 @@ bin_scatter_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict
     const int m = bm % M, b = bm / M;
     const int f0 = (wg % dm.nblk) * (PPT * kThreads);
     const int nf = Nq * LK;
-    const size_t row0 = (size_t)b * Nq * M + m;  // item row of query 0
+    const size_t row0 = (size_t)b * dm.Nqs * dm.Ms + m;  // item row of query 0
 
     // the thread's points: coordinates and weights, kept for both passes
     float2 uv[PPT];
@@ -651,7 +656,7 @@ bin_scatter_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict
         wz[r] = 0.f;
         if (f < nf) {
             const int q = (int)fdiv((uint32_t)f, dm.div_lk), j = f - q * LK;
-            const size_t p = (row0 + (size_t)q * M) * LK + j;
+            const size_t p = (row0 + (size_t)q * dm.Ms) * LK + j;
             if constexpr (VOL) {
                 uv[r] = make_float2(loc[3 * p], loc[3 * p + 1]);
                 wz[r] = loc[3 * p + 2];
@@ -664,10 +669,10 @@ bin_scatter_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict
     stage_bin_levels<VOL>(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
     if (zl.zero) {
         const uint32_t nz = zl.work_total[1];
-        const size_t slice_v = (size_t)dm.Nv * M * zl.D;
+        const size_t slice_v = (size_t)dm.Nv * dm.Ms * zl.D;
         for (uint32_t zi = blockIdx.x; zi < nz; zi += gridDim.x)
             zero_tile<kThreads>(zl.grad_value, bin_tile<VOL>(zl.zero[zi], s_lv, M, dm.nb_max, dm.L),
-                                slice_v, M, zl.D, threadIdx.x);
+                                slice_v, dm.Ms, zl.D, threadIdx.x);
     }
     const int nbins = s_lv.nbins;
     const bool lds = nbins <= hist_cap;
@@ -920,11 +925,11 @@ grad_value_tile_kernel(const int64_t *__restrict__ shapes, const int64_t *__rest
             const uint32_t bm = Bn.it.x;  // (b * nb_max + tile) * M + m
             const int m = (int)(bm % (uint32_t)M);
             const int b = (int)(bm / (uint32_t)M / (uint32_t)dm.nb_max);
-            const float *gob = grad_out + ((size_t)b * Nq * M + m) * D;
+            const float *gob = grad_out + ((size_t)b * dm.Nqs * dm.Ms + m) * D;
             for (int i = tid; i < nb * kQuads; i += kTileThreads) {
                 const int slot = i / kQuads, qd = i - slot * kQuads;
                 const uint32_t qy = min(s_q[slot], (uint32_t)Nq - 1u);  // a query of this batch
-                const float *src = gob + (size_t)qy * M * D + 4 * qd;
+                const float *src = gob + (size_t)qy * dm.Ms * D + 4 * qd;
                 // each wave fills 64 consecutive float4 slots: lane l writes slot base + l
                 __builtin_amdgcn_global_load_lds((global_void_t *)src,
                                                  (lds_void_t *)(gF + (i & ~63)), 16, 0, 0);
@@ -951,7 +956,7 @@ grad_value_tile_kernel(const int64_t *__restrict__ shapes, const int64_t *__rest
             // 6. the item ends with A: write its tile
             if (A.off + kSub >= A.it.z) {
                 const BinTile t = bin_tile<VOL>(A.it.x, s_lv, M, dm.nb_max, dm.L);
-                const size_t slice = (size_t)dm.Nv * M * D;
+                const size_t slice = (size_t)dm.Nv * dm.Ms * D;
                 float *gv = grad_value + (size_t)t.b * slice + (size_t)t.m * D;
 #pragma unroll
                 for (int o = 0; o < kOwn; ++o) {
@@ -963,7 +968,7 @@ grad_value_tile_kernel(const int64_t *__restrict__ shapes, const int64_t *__rest
                     float4 a = acc[o];
                     acc[o] = make_float4(0.f, 0.f, 0.f, 0.f);
                     if (gy >= t.H || gx >= t.W) continue;
-                    float *dst = gv + (size_t)(t.row0 + gy * t.W + gx) * M * D + 4 * q;
+                    float *dst = gv + (size_t)(t.row0 + gy * t.W + gx) * dm.Ms * D + 4 * q;
                     if (A.it.w) {
                         // this work item alone owns the pixel: plain read-add-write
                         float4 *d4 = reinterpret_cast<float4 *>(dst);
@@ -1075,10 +1080,10 @@ grad_value_gather_kernel(const int64_t *__restrict__ shapes, const int64_t *__re
     const bool owner = tid < kPairs;
     const int cell = tid / kGroups, grp = tid - cell * kGroups;
     const int cx = cell % kCellsW, cy = cell / kCellsW;
-    const uint32_t row_stride = (uint32_t)M * D * 4u;
-    // one batch of grad_out; the host keeps it below 2^32 bytes, and an
-    // offset of `slice` reads zeros (outside the descriptor's range)
-    const uint32_t slice = (uint32_t)((size_t)Nq * M * D * 4);
+    const uint32_t row_stride = (uint32_t)dm.Ms * D * 4u;
+    // the rows of one batch's queries; the host keeps them below 2^32 bytes,
+    // and an offset of `slice` reads zeros (outside the descriptor's range)
+    const uint32_t slice = (uint32_t)((size_t)Nq * dm.Ms * D * 4);
     __syncthreads();
 
     // Workgroup g takes items g, g + grid, ... counted from the end of the
@@ -1090,7 +1095,7 @@ grad_value_gather_kernel(const int64_t *__restrict__ shapes, const int64_t *__re
         if (w >= total) {
             // an empty bin: no item writes its tile
             zero_tile<kT>(grad_value, bin_tile<VOL>(zero[w - total], s_lv, M, dm.nb_max, dm.L),
-                          (size_t)dm.Nv * M * D, M, D, tid);
+                          (size_t)dm.Nv * dm.Ms * D, dm.Ms, D, tid);
             continue;
         }
         const uint4 it = items[total - 1u - w];  // (bin, first record, records, whole bin)
@@ -1145,7 +1150,7 @@ grad_value_gather_kernel(const int64_t *__restrict__ shapes, const int64_t *__re
 #pragma unroll
             for (int k = 0; k < kQPL; ++k) acc[r][k] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (owner) {
-            const rsrc_t go = make_rsrc(grad_out + (size_t)b * Nq * M * D, slice);
+            const rsrc_t go = make_rsrc(grad_out + (size_t)b * dm.Nqs * dm.Ms * D, slice);
             const uint32_t lane_off = (uint32_t)m * D * 4u + 16u * (uint32_t)(grp * kQPL);
             const int e0 = (int)s_st[cell], e1 = (int)s_st[cell + 1];
             for (int e = e0; e < e1; e += kGatherBatch) {
@@ -1196,7 +1201,7 @@ grad_value_gather_kernel(const int64_t *__restrict__ shapes, const int64_t *__re
         __syncthreads();
         // 5. the tile: pixel = the four roles' sums
         const BinTile tile = bin_tile<VOL>(bin, s_lv, M, dm.nb_max, dm.L);
-        const size_t slice_v = (size_t)dm.Nv * M * D;
+        const size_t slice_v = (size_t)dm.Nv * dm.Ms * D;
         float *gv = grad_value + (size_t)b * slice_v + (size_t)m * D;
         auto tile_sum = [&](int i) {  // i = pixel * kQuads + quad
             const int j = red_slot(i);
@@ -1211,7 +1216,7 @@ grad_value_gather_kernel(const int64_t *__restrict__ shapes, const int64_t *__re
             const int gy = tile.y0 + (px >> kTileShift);
             if (gy >= tile.H || gx >= tile.W) return;
             float4 *d4 = reinterpret_cast<float4 *>(
-                gv + (size_t)(tile.row0 + gy * tile.W + gx) * M * D + 4 * q);
+                gv + (size_t)(tile.row0 + gy * tile.W + gx) * dm.Ms * D + 4 * q);
             if (dm.accumulate) add4(a, *d4);
             *d4 = a;
         };
@@ -1229,6 +1234,9 @@ grad_value_gather_kernel(const int64_t *__restrict__ shapes, const int64_t *__re
     }
 }
 
+using msda_host::min_workspace;
+using msda_host::pass_plan;
+using msda_host::PassPlan;
 using msda_host::WorkLayout;
 using msda_host::work_layout;
 
@@ -1276,7 +1284,7 @@ split_combine_kernel(const int64_t *__restrict__ shapes, const int64_t *__restri
                 for (int u = 0; u < kPerT; ++u) add4(a[u], v[c][u]);
         }
         const BinTile tile = bin_tile<VOL>(bin, s_lv, M, dm.nb_max, dm.L);
-        float *gv = grad_value + (size_t)tile.b * dm.Nv * M * D + (size_t)tile.m * D;
+        float *gv = grad_value + (size_t)tile.b * dm.Nv * dm.Ms * D + (size_t)tile.m * D;
 #pragma unroll
         for (int u = 0; u < kPerT; ++u) {
             const int i = threadIdx.x + u * kThreads;
@@ -1285,7 +1293,7 @@ split_combine_kernel(const int64_t *__restrict__ shapes, const int64_t *__restri
             const int gy = tile.y0 + (px >> kTileShift);
             if (i >= kTilePx * kQuads || gy >= tile.H || gx >= tile.W) continue;
             float4 *d4 = reinterpret_cast<float4 *>(
-                gv + (size_t)(tile.row0 + gy * tile.W + gx) * M * D + 4 * q);
+                gv + (size_t)(tile.row0 + gy * tile.W + gx) * dm.Ms * D + 4 * q);
             if (dm.accumulate) add4(a[u], *d4);
             *d4 = a[u];
         }
@@ -1296,20 +1304,21 @@ split_combine_kernel(const int64_t *__restrict__ shapes, const int64_t *__restri
 // channels whose grad_out batch is 32-bit addressable (then the combine
 // kernel writes the tiles of split bins), else the tile kernel (whose
 // split-bin items add into zeroed tiles atomically).
+// Nq queries of rows of Ms heads.
 template <int D>
-bool uses_gather(int64_t Nq, int64_t M) {
-    return D <= kGatherMaxD && Nq * M * D * 4 < ((int64_t)1 << 32) - 64;
+bool uses_gather(int64_t Nq, int64_t Ms) {
+    return D <= kGatherMaxD && Nq * Ms * D * 4 < ((int64_t)1 << 32) - 64;
 }
 
 template <int D, bool VOL>
-hipError_t launch_grad_value(const WorkLayout &wl, int64_t Nq, int64_t M, const int64_t *shapes,
+hipError_t launch_grad_value(const WorkLayout &wl, int64_t Nq, int64_t Ms, const int64_t *shapes,
                              const int64_t *starts, const float *gout, const Work &w,
                              float *gval, const Dims &dm, hipStream_t s) {
     const int64_t grid = wl.work_max < kTileGrid ? wl.work_max : kTileGrid;
     const uint4 *items = w.items, *recs = w.recs;
     const uint32_t *work_total = w.work_total;
     if constexpr (D <= kGatherMaxD) {
-        if (uses_gather<D>(Nq, M)) {
+        if (uses_gather<D>(Nq, Ms)) {
             hipLaunchKernelGGL((grad_value_gather_kernel<D, VOL, kGatherCPL>),
                                dim3((unsigned)grid), dim3(gather_threads<kGatherCPL>()), 0, s,
                                shapes, starts, gout, items, work_total, w.recs,
@@ -1371,8 +1380,12 @@ struct Exec {
     hipStream_t side;         // nullptr: everything on s
     hipEvent_t fork, join;
     hipEvent_t *ev;           // optional: 2 * stages caller events (start, end)
+    // in a pipeline of several passes: whether this is the first / last one
+    // (a stage's start is recorded in the first pass, its end in the last)
+    bool first = true, last = true;
     // record the start (end = false) or end event of stage i on stream `on`
     void stamp(int i, bool end, hipStream_t on) const {
+        if (end ? !last : !first) return;
         if (ev && ev[2 * i + (end ? 1 : 0)]) (void)hipEventRecord(ev[2 * i + (end ? 1 : 0)], on);
     }
     hipStream_t dots_stream() const { return side ? side : s; }
@@ -1444,15 +1457,21 @@ msda_status per_batch(int64_t B, int64_t per_b, F &&launch) {
 // when the problem has at least two points per pixel and head, and sparser
 // problems are zero-filled whole, by many workgroups at streaming speed (the
 // scatter kernel's few workgroups would be slow to zero most of the tiles).
+// The tensors hold Ms heads and Nqs queries per batch; this call covers
+// heads [0, M) and queries [0, Nq) from the pointers given (a pass of
+// run_bins_passes), and grad_value's slice of those heads.
 template <int D, bool VOL>
 msda_status run_bins(const int64_t *shapes, const int64_t *starts, const float *loc,
                      const float *attn, const float *gout, float *gval, int64_t B, int64_t Nv,
-                     int64_t Nq, int64_t M, int64_t L, int64_t K, const WorkLayout &wl,
-                     unsigned char *ws, bool accumulate, bool align, const Exec &ex) {
+                     int64_t Nq, int64_t M, int64_t L, int64_t K, int64_t Ms, int64_t Nqs,
+                     const WorkLayout &wl, unsigned char *ws, bool accumulate, bool align,
+                     const Exec &ex) {
     const hipStream_t s = ex.s;
     const Work w = work_at(wl, ws);
-    const bool gather = uses_gather<D>(Nq, M);
-    const bool zero_list = !accumulate && (gather || Nq * L * K >= 2 * Nv);
+    const bool gather = uses_gather<D>(Nq, Ms);
+    // a pass over some of the heads cannot fill grad_value whole: its
+    // untouched tiles are zeroed from the list
+    const bool zero_list = !accumulate && (gather || Nq * L * K >= 2 * Nv || M != Ms);
     // the counts region is padded to 256 bytes, so whole float4s can be cleared
     ex.stamp(kStageClear, false, s);
     msda_status st = fill_zero(w.counts, (wl.off_start - wl.off_counts) / 16, s);
@@ -1471,6 +1490,8 @@ msda_status run_bins(const int64_t *shapes, const int64_t *starts, const float *
     dm.align = align ? 1 : 0;
     dm.zero_list = zero_list ? 1 : 0;
     dm.combine = gather ? 1 : 0;
+    dm.Ms = (int)Ms;
+    dm.Nqs = (int)Nqs;
     ex.stamp(kStageCount, false, s);
     st = per_batch(B, gb * M, [&](int64_t b0, unsigned grid) {
         Dims d2 = dm;
@@ -1515,9 +1536,50 @@ msda_status run_bins(const int64_t *shapes, const int64_t *starts, const float *
     ex.stamp(kStageScatter, true, s);
 
     ex.stamp(kStageGather, false, s);
-    st = hip_status(launch_grad_value<D, VOL>(wl, Nq, M, shapes, starts, gout, w, gval, dm, s));
+    st = hip_status(launch_grad_value<D, VOL>(wl, Nq, Ms, shapes, starts, gout, w, gval, dm, s));
     ex.stamp(kStageGather, true, s);
     return st;
+}
+
+// The grad_value pipeline over the whole problem in the passes of `pp`
+// (pass_plan): boxes of pp.nb batches x pp.nm heads x pp.nq queries.  A pass
+// is the problem restricted to its box -- the kernels address the tensors
+// with the whole problem's strides (M heads, Nq queries per batch) from
+// pointers to the box's first element, and the pass's bins are those of its
+// (batch, head) pairs -- so it runs as a call of its own, reusing the
+// workspace.  Boxes of different batches or heads write disjoint parts of
+// grad_value; the boxes after the first of a query range add to it.  Passes
+// are enqueued in order on s, which orders their use of the workspace.
+template <int D, bool VOL>
+msda_status run_bins_passes(const int64_t *shapes, const int64_t *starts, const float *loc,
+                            const float *attn, const float *gout, float *gval, int64_t B,
+                            int64_t Nv, int64_t Nq, int64_t M, int64_t L, int64_t K,
+                            const PassPlan &pp, unsigned char *ws, bool accumulate, bool align,
+                            const Exec &ex) {
+    const int64_t coords = VOL ? 3 : 2, LK = L * K;
+    auto part = [](int64_t from, int64_t step, int64_t n) { return n - from < step ? n - from : step; };
+    for (int64_t b0 = 0; b0 < B; b0 += pp.nb) {
+        const int64_t nb = part(b0, pp.nb, B);
+        for (int64_t m0 = 0; m0 < M; m0 += pp.nm) {
+            const int64_t nm = part(m0, pp.nm, M);
+            for (int64_t q0 = 0; q0 < Nq; q0 += pp.nq) {
+                const int64_t nq = part(q0, pp.nq, Nq);
+                const int64_t row = (b0 * Nq + q0) * M + m0;  // the box's first (query, head) row
+                Exec ep = ex;
+                ep.first = b0 == 0 && m0 == 0 && q0 == 0;
+                ep.last = b0 + nb == B && m0 + nm == M && q0 + nq == Nq;
+                const WorkLayout wl = nb == pp.nb && nm == pp.nm && nq == pp.nq
+                                          ? pp.wl
+                                          : work_layout(nb, Nv, nq, nm, L, K, VOL);
+                const msda_status st = run_bins<D, VOL>(
+                    shapes, starts, loc + coords * row * LK, attn + row * LK, gout + row * D,
+                    gval + (b0 * Nv * M + m0) * D, nb, Nv, nq, nm, L, K, M, Nq, wl, ws,
+                    accumulate || q0 > 0, align, ep);
+                if (st != MSDA_OK) return st;
+            }
+        }
+    }
+    return MSDA_OK;
 }
 
 }  // namespace

@@ -32,6 +32,13 @@ size_t msda_backward_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int64_t M
     return work_layout(B, Nv, Nq, M, L, K).bytes;
 }
 
+size_t msda_backward_workspace_min(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
+                                   int64_t L, int64_t K) {
+    if (check_sizes(MSDA_F32, B, Nv, Nq, M, D, L, K) != MSDA_OK) return 0;
+    if (B == 0 || Nq == 0) return 0;
+    return min_workspace(Nv, Nq, L, K, false);
+}
+
 size_t msda_backward_fused_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int64_t M,
                                           int64_t D, int64_t L, int64_t K) {
     if (check_sizes(MSDA_F32, B, Nv, Nq, M, D, L, K) != MSDA_OK) return 0;
@@ -39,11 +46,26 @@ size_t msda_backward_fused_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int
     return fused_layout(B, Nv, Nq, M, L, K).bytes;
 }
 
+size_t msda_backward_fused_workspace_min(int64_t B, int64_t Nv, int64_t Nq, int64_t M,
+                                         int64_t D, int64_t L, int64_t K) {
+    if (check_sizes(MSDA_F32, B, Nv, Nq, M, D, L, K) != MSDA_OK) return 0;
+    if (B == 0 || Nq == 0) return 0;
+    const FusedLayout f = fused_layout(B, Nv, Nq, M, L, K);
+    return f.off_core + f.core_min;
+}
+
 size_t msda3d_backward_workspace_size(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
                                       int64_t L, int64_t K) {
     if (check_sizes3(MSDA_F32, B, Nv, Nq, M, D, L, K) != MSDA_OK) return 0;
     if (B == 0 || Nq == 0) return 0;
     return work_layout(B, Nv, Nq, M, L, K, true).bytes;
+}
+
+size_t msda3d_backward_workspace_min(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t D,
+                                     int64_t L, int64_t K) {
+    if (check_sizes3(MSDA_F32, B, Nv, Nq, M, D, L, K) != MSDA_OK) return 0;
+    if (B == 0 || Nq == 0) return 0;
+    return min_workspace(Nv, Nq, L, K, true);
 }
 
 const char *msda_status_string(int status) { return status_string(status); }

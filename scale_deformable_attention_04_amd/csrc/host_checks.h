@@ -135,22 +135,89 @@ inline WorkLayout work_layout(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int6
     return w;
 }
 
-// Workspace of the fused backward: the core's, then the locations [pts][2]
-// and weights [pts] the prologue writes, then the per-(item, level)
-// location-gradient sums.
+// Fewest queries in a pass of the grad_value pipeline (see pass_plan): below
+// this the passes' launches would cost more than their work.
+constexpr int64_t kMinPassQueries = 1024;
+
+// The passes of the grad_value pipeline in a workspace of `bytes`: boxes of
+// nb batches x nm heads x nq queries, each run as a problem of its own in a
+// layout `wl` for that box.  A pass costs its launches and their latency
+// (about 60 us at the encoder shape), so the plan takes the fewest passes:
+// the whole problem; else groups of whole batches; else one batch and
+// ranges of nq queries with every head (the tensors' rows stay contiguous);
+// only when not even min(Nq, kMinPassQueries) queries of every head fit,
+// groups of nm heads and ranges of queries.  nb = 0: not even the smallest
+// pass (one head, min(Nq, kMinPassQueries) queries) fits.  Layout sizes grow
+// with the batches, heads and queries, so each largest fit is found by
+// bisection.
+struct PassPlan {
+    int64_t nb, nm, nq;
+    WorkLayout wl;
+};
+
+inline int64_t min_pass_queries(int64_t Nq) { return Nq < kMinPassQueries ? Nq : kMinPassQueries; }
+
+// The smallest workspace any pass plan accepts (one batch, one head,
+// min_pass_queries).
+inline size_t min_workspace(int64_t Nv, int64_t Nq, int64_t L, int64_t K, bool vol) {
+    return work_layout(1, Nv, min_pass_queries(Nq), 1, L, K, vol).bytes;
+}
+
+inline PassPlan pass_plan(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t L, int64_t K,
+                          bool vol, size_t bytes) {
+    auto fits = [&](int64_t nb, int64_t nm, int64_t nq) {
+        return work_layout(nb, Nv, nq, nm, L, K, vol).bytes <= bytes;
+    };
+    // the largest n in [lo, hi] with fit(n), given fit(lo)
+    auto largest = [](int64_t lo, int64_t hi, auto fit) {
+        while (lo < hi) {
+            const int64_t mid = lo + (hi - lo + 1) / 2;
+            if (fit(mid))
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        return lo;
+    };
+    const int64_t q_min = min_pass_queries(Nq);
+    PassPlan p{B, M, Nq, WorkLayout{}};
+    if (!fits(B, M, Nq)) {
+        if (fits(1, M, Nq)) {
+            p.nb = largest(1, B - 1, [&](int64_t nb) { return fits(nb, M, Nq); });
+        } else if (fits(1, M, q_min)) {
+            p.nb = 1;
+            p.nq = largest(q_min, Nq - 1, [&](int64_t nq) { return fits(1, M, nq); });
+        } else if (fits(1, 1, q_min)) {
+            p.nb = 1;
+            p.nm = largest(1, M - 1, [&](int64_t nm) { return fits(1, nm, q_min); });
+            p.nq = largest(q_min, Nq, [&](int64_t nq) { return fits(1, p.nm, nq); });
+        } else {
+            return PassPlan{0, 0, 0, WorkLayout{}};
+        }
+    }
+    p.wl = work_layout(p.nb, Nv, p.nq, p.nm, L, K, vol);
+    return p;
+}
+
+// Workspace of the fused backward: the locations [pts][2] and weights [pts]
+// the prologue writes, the per-(item, level) location-gradient sums, then
+// the core's (`core` bytes at off_core for the whole problem in one pass,
+// at least core_min).
 struct FusedLayout {
-    size_t core, off_loc, off_attn, off_part, bytes;
+    size_t off_loc, off_attn, off_part, off_core, core, core_min, bytes;
 };
 
 inline FusedLayout fused_layout(int64_t B, int64_t Nv, int64_t Nq, int64_t M, int64_t L,
                                 int64_t K) {
     const size_t pts = (size_t)(B * Nq * M * L * K);
     FusedLayout f;
-    f.core = work_layout(B, Nv, Nq, M, L, K).bytes;
-    f.off_loc = f.core;
+    f.off_loc = 0;
     f.off_attn = align256(f.off_loc + 8 * pts);
     f.off_part = align256(f.off_attn + 4 * pts);
-    f.bytes = align256(f.off_part + 8 * (size_t)(B * Nq * M * L));
+    f.off_core = align256(f.off_part + 8 * (size_t)(B * Nq * M * L));
+    f.core = work_layout(B, Nv, Nq, M, L, K).bytes;
+    f.core_min = min_workspace(Nv, Nq, L, K, false);
+    f.bytes = f.off_core + f.core;
     return f;
 }
 

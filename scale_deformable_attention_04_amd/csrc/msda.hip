@@ -932,7 +932,7 @@ template <int D, typename VT>
 msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *starts,
                        const float *loc, const float *attn, const float *gout, float *gval,
                        float *gloc, float *gattn, int64_t B, int64_t Nv, int64_t Nq, int64_t M,
-                       int64_t L, int64_t K, const WorkLayout &wl, unsigned char *ws,
+                       int64_t L, int64_t K, const PassPlan &pp, unsigned char *ws,
                        bool accumulate, bool align, FusedBwd *fz, const Exec &ex) {
     // grad_attn_weight and grad_sampling_loc do not depend on the bin
     // pipeline: with a side stream they are computed there, concurrently
@@ -960,8 +960,8 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
     });
     if (st != MSDA_OK) return st;
     ex.stamp(kStageDots, true, ds);
-    return run_bins<D, false>(shapes, starts, loc, attn, gout, gval, B, Nv, Nq, M, L, K, wl, ws,
-                              accumulate, align, ex);
+    return run_bins_passes<D, false>(shapes, starts, loc, attn, gout, gval, B, Nv, Nq, M, L, K,
+                                     pp, ws, accumulate, align, ex);
 }
 
 template <typename VT>
@@ -1036,12 +1036,12 @@ msda_status dispatch_bwd(int64_t D, const void *value, const int64_t *shapes,
                          const int64_t *starts, const float *loc, const float *attn,
                          const float *gout, float *gval, float *gloc, float *gattn, int64_t B,
                          int64_t Nv, int64_t Nq, int64_t M, int64_t L, int64_t K,
-                         const WorkLayout &wl, unsigned char *ws, bool acc, bool align,
+                         const PassPlan &pp, unsigned char *ws, bool acc, bool align,
                          FusedBwd *fz, const Exec &ex) {
 #define MSDA_BWD_CASE(DD)                                                                      \
     case DD:                                                                                   \
         return launch_bwd<DD, VT>(value, shapes, starts, loc, attn, gout, gval, gloc, gattn, B, \
-                                  Nv, Nq, M, L, K, wl, ws, acc, align, fz, ex);
+                                  Nv, Nq, M, L, K, pp, ws, acc, align, fz, ex);
     switch (D) {
         MSDA_BWD_CASE(4)
         MSDA_BWD_CASE(8)
@@ -1134,18 +1134,19 @@ msda_status backward_impl(const void *value, int value_dtype, const int64_t *spa
     Exec ex{s, nullptr, nullptr, nullptr, ev};
     st = exec_side(ex, side_stream, side_events);
     if (st != MSDA_OK) return st;
-    WorkLayout wl{};
+    PassPlan pp{};
     if (work) {
         if (Nv < 1) return MSDA_ERR_SHAPE;
         if (!value || !spatial_shapes || !level_start_index || !sampling_loc || !attn_weight ||
             !grad_out || !grad_sampling_loc || !grad_attn_weight)
             return MSDA_ERR_NULL;
-        wl = work_layout(B, Nv, Nq, M, L, K);
-        // bin counters and work items are indexed with 31-bit integers
-        if (wl.bm_bins >= ((int64_t)1 << 31) || wl.work_max >= ((int64_t)1 << 31))
-            return MSDA_ERR_UNSUPPORTED;
         if (!workspace) return MSDA_ERR_NULL;
-        if (workspace_bytes < wl.bytes) return MSDA_ERR_WORKSPACE;
+        // the grad_value pipeline in as few passes as the workspace allows
+        pp = pass_plan(B, Nv, Nq, M, L, K, false, workspace_bytes);
+        if (pp.nb == 0) return MSDA_ERR_WORKSPACE;
+        // bin counters and work items are indexed with 31-bit integers
+        if (pp.wl.bm_bins >= ((int64_t)1 << 31) || pp.wl.work_max >= ((int64_t)1 << 31))
+            return MSDA_ERR_UNSUPPORTED;
         if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return MSDA_ERR_WORKSPACE;
     }
     const bool acc = (flags & MSDA_BWD_ACCUMULATE) != 0;
@@ -1184,12 +1185,12 @@ msda_status backward_impl(const void *value, int value_dtype, const int64_t *spa
     if (value_dtype == MSDA_F32)
         st = dispatch_bwd<float>(D, value, spatial_shapes, level_start_index, sampling_loc,
                                  attn_weight, grad_out, grad_value, grad_sampling_loc,
-                                 grad_attn_weight, B, Nv, Nq, M, L, K, wl, ws, acc, align, fz,
+                                 grad_attn_weight, B, Nv, Nq, M, L, K, pp, ws, acc, align, fz,
                                  ex);
     else
         st = dispatch_bwd<uint16_t>(D, value, spatial_shapes, level_start_index, sampling_loc,
                                     attn_weight, grad_out, grad_value, grad_sampling_loc,
-                                    grad_attn_weight, B, Nv, Nq, M, L, K, wl, ws, acc, align, fz,
+                                    grad_attn_weight, B, Nv, Nq, M, L, K, pp, ws, acc, align, fz,
                                     ex);
     const msda_status js = exec_join(ex);
     return st != MSDA_OK ? st : js;
@@ -1234,7 +1235,7 @@ msda_status backward_fused_impl(const void *value, int value_dtype, const int64_
     if ((scale == nullptr) != (grad_scale == nullptr)) return MSDA_ERR_NULL;
     if (!workspace) return MSDA_ERR_NULL;
     const FusedLayout fl = fused_layout(B, Nv, Nq, M, L, K);
-    if (workspace_bytes < fl.bytes) return MSDA_ERR_WORKSPACE;
+    if (workspace_bytes < fl.off_core + fl.core_min) return MSDA_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return MSDA_ERR_WORKSPACE;
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     const bool saved = saved_loc != nullptr;
@@ -1262,7 +1263,8 @@ msda_status backward_fused_impl(const void *value, int value_dtype, const int64_
                 ScaleBwd{logits, scale, grad_scale}};
     const float *use_loc = saved ? saved_loc : loc, *use_attn = saved ? saved_attn : attn;
     st = backward_impl(value, value_dtype, shapes, starts, use_loc, use_attn, grad_out,
-                       grad_value, grad_off, grad_logits, B, Nv, Nq, M, D, L, K, ws, fl.core,
+                       grad_value, grad_off, grad_logits, B, Nv, Nq, M, D, L, K,
+                       ws + fl.off_core, workspace_bytes - fl.off_core,
                        core_flags, &fz, s, side_stream, side_events, ev);
     if (st != MSDA_OK) return st;
 
@@ -1402,7 +1404,7 @@ msda_status msda_backward_noalloc(const void *value, int value_dtype,
     msda_status st = check_sizes(value_dtype, B, Nv, Nq, M, D, L, K);
     if (st != MSDA_OK) return st;
     const bool work = B > 0 && Nq > 0;
-    const size_t need = work ? work_layout(B, Nv, Nq, M, L, K).bytes : 0;
+    const size_t need = work ? min_workspace(Nv, Nq, L, K, false) : 0;
     if (need > MSDA_NOALLOC_SCRATCH_BYTES) return MSDA_ERR_SCRATCH;
     // the pointer checks of msda_backward, before the one-time symbol lookup
     if (B * Nv * M * D > 0 && !grad_value) return MSDA_ERR_NULL;

@@ -382,7 +382,7 @@ template <int D, typename VT>
 msda_status launch3_bwd(const void *value, const int64_t *shapes, const int64_t *starts,
                         const float *loc, const float *attn, const float *gout, float *gval,
                         float *gloc, float *gattn, int64_t B, int64_t Nv, int64_t Nq, int64_t M,
-                        int64_t L, int64_t K, bool align, bool accumulate, const WorkLayout &wl,
+                        int64_t L, int64_t K, bool align, bool accumulate, const PassPlan &pp,
                         unsigned char *ws, const Exec &ex) {
     // grad_attn_weight and grad_sampling_loc on the side stream (when there is one)
     const hipStream_t ds = ex.dots_stream();
@@ -398,8 +398,8 @@ msda_status launch3_bwd(const void *value, const int64_t *shapes, const int64_t 
     });
     if (st != MSDA_OK) return st;
     // grad_value: the binned pipeline over volume levels
-    return run_bins<D, true>(shapes, starts, loc, attn, gout, gval, B, Nv, Nq, M, L, K, wl, ws,
-                             accumulate, align, ex);
+    return run_bins_passes<D, true>(shapes, starts, loc, attn, gout, gval, B, Nv, Nq, M, L, K,
+                                    pp, ws, accumulate, align, ex);
 }
 
 #define MSDA3D_DISPATCH(FN, VT, ...)                                                           \
@@ -428,9 +428,9 @@ msda_status dispatch3_bwd(int64_t D, const void *value, const int64_t *shapes,
                           const int64_t *starts, const float *loc, const float *attn,
                           const float *gout, float *gval, float *gloc, float *gattn, int64_t B,
                           int64_t Nv, int64_t Nq, int64_t M, int64_t L, int64_t K, bool align,
-                          bool acc, const WorkLayout &wl, unsigned char *ws, const Exec &ex) {
+                          bool acc, const PassPlan &pp, unsigned char *ws, const Exec &ex) {
     MSDA3D_DISPATCH(launch3_bwd, VT, value, shapes, starts, loc, attn, gout, gval, gloc, gattn,
-                    B, Nv, Nq, M, L, K, align, acc, wl, ws, ex)
+                    B, Nv, Nq, M, L, K, align, acc, pp, ws, ex)
 }
 
 #undef MSDA3D_DISPATCH
@@ -476,18 +476,19 @@ msda_status msda3d_backward(const void *value, int value_dtype, const int64_t *v
     const int64_t nval = B * Nv * M * D;
     if (nval > 0 && !grad_value) return MSDA_ERR_NULL;
     const bool work = B > 0 && Nq > 0;
-    WorkLayout wl{};
+    PassPlan pp{};
     if (work) {
         if (Nv < 1) return MSDA_ERR_SHAPE;
         if (!value || !volume_shapes || !level_start_index || !sampling_loc || !attn_weight ||
             !grad_out || !grad_sampling_loc || !grad_attn_weight)
             return MSDA_ERR_NULL;
-        wl = work_layout(B, Nv, Nq, M, L, K, true);
-        if (wl.bm_bins >= ((int64_t)1 << 31) || wl.work_max >= ((int64_t)1 << 31) ||
-            wl.sorted_max >= ((int64_t)1 << 32))
-            return MSDA_ERR_UNSUPPORTED;
         if (!workspace) return MSDA_ERR_NULL;
-        if (workspace_bytes < wl.bytes) return MSDA_ERR_WORKSPACE;
+        // the grad_value pipeline in as few passes as the workspace allows
+        pp = pass_plan(B, Nv, Nq, M, L, K, true, workspace_bytes);
+        if (pp.nb == 0) return MSDA_ERR_WORKSPACE;
+        if (pp.wl.bm_bins >= ((int64_t)1 << 31) || pp.wl.work_max >= ((int64_t)1 << 31) ||
+            pp.wl.sorted_max >= ((int64_t)1 << 32))
+            return MSDA_ERR_UNSUPPORTED;
         if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return MSDA_ERR_WORKSPACE;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -503,11 +504,11 @@ msda_status msda3d_backward(const void *value, int value_dtype, const int64_t *v
     if (value_dtype == MSDA_F32)
         st = dispatch3_bwd<float>(D, value, volume_shapes, level_start_index, sampling_loc,
                                   attn_weight, grad_out, grad_value, grad_sampling_loc,
-                                  grad_attn_weight, B, Nv, Nq, M, L, K, align, acc, wl, ws, ex);
+                                  grad_attn_weight, B, Nv, Nq, M, L, K, align, acc, pp, ws, ex);
     else
         st = dispatch3_bwd<uint16_t>(D, value, volume_shapes, level_start_index, sampling_loc,
                                      attn_weight, grad_out, grad_value, grad_sampling_loc,
-                                     grad_attn_weight, B, Nv, Nq, M, L, K, align, acc, wl, ws,
+                                     grad_attn_weight, B, Nv, Nq, M, L, K, align, acc, pp, ws,
                                      ex);
     const msda_status js = exec_join(ex);
     return st != MSDA_OK ? st : js;

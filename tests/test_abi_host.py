@@ -124,13 +124,45 @@ def test_backward_workspace_checks():
         fake, 0, fake, fake, fake, fake, fake, fake, fake, fake, 1, 80, 16, 2, 8, 2, 2, ws,
         nbytes, 0, z, side, sev)
     need = lib.msda_backward_workspace_size(1, 80, 16, 2, 8, 2, 2)
+    least = lib.msda_backward_workspace_min(1, 80, 16, 2, 8, 2, 2)
+    assert least < need
     assert bwd(z, need) == B_.MSDA_ERR_NULL
-    assert bwd(fake, need - 1) == B_.MSDA_ERR_WORKSPACE
+    assert bwd(fake, least - 1) == B_.MSDA_ERR_WORKSPACE
     assert bwd(ctypes.c_void_p((1 << 20) + 4), need) == B_.MSDA_ERR_WORKSPACE
     # a side stream needs its two events (checked before anything is enqueued)
     assert bwd(fake, need, side=fake) == B_.MSDA_ERR_NULL
     half = (ctypes.c_void_p * 2)(1 << 20, 0)
     assert bwd(fake, need, side=fake, sev=half) == B_.MSDA_ERR_NULL
+
+
+def test_backward_workspace_min():
+    """The smallest workspace: one pass over one head of one batch and 1024
+    queries (all of them when there are fewer); the call rejects anything
+    below it before any launch."""
+    lib = msda.load()
+    enc = (2, 22223, 22223, 8, 32, 4, 4)
+    size, least = lib.msda_backward_workspace_size(*enc), lib.msda_backward_workspace_min(*enc)
+    pass_pts = 1024 * 16
+    assert 64 * pass_pts <= least <= 64 * pass_pts + (1 << 20) < size
+    small = (2, 80, 16, 2, 8, 2, 2)
+    assert (lib.msda_backward_workspace_min(*small) ==
+            lib.msda_backward_workspace_size(1, 80, 16, 1, 8, 2, 2))
+    assert lib.msda_backward_workspace_min(0, 80, 16, 2, 8, 2, 2) == 0
+    assert lib.msda_backward_workspace_min(1, 80, 16, 2, 12, 2, 2) == 0   # invalid D
+    # the fused backward's extra regions come on top of either
+    fs, fm = lib.msda_backward_fused_workspace_size(*enc), lib.msda_backward_fused_workspace_min(*enc)
+    assert fs - fm == size - least
+    v_size, v_min = lib.msda3d_backward_workspace_size(*enc), lib.msda3d_backward_workspace_min(*enc)
+    assert 128 * pass_pts <= v_min < v_size
+    z = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(1 << 20)   # never dereferenced: the checks fail first
+    bwd = lambda nbytes: lib.msda_backward(fake, 0, fake, fake, fake, fake, fake, fake, fake,
+                                           fake, *enc, fake, nbytes, 0, z, z, None)
+    assert bwd(least - 1) == B_.MSDA_ERR_WORKSPACE
+    assert bwd(0) == B_.MSDA_ERR_WORKSPACE
+    b3 = lambda nbytes: lib.msda3d_backward(fake, 0, fake, fake, fake, fake, fake, fake, fake,
+                                            fake, *enc, fake, nbytes, 0, z, z, None)
+    assert b3(v_min - 1) == B_.MSDA_ERR_WORKSPACE
 
 
 def test_forward_fused_rejects_before_launch():
@@ -175,7 +207,8 @@ def test_backward_fused_rejects_before_launch():
     # the scale attention and its gradient come as a pair
     assert bwd(0, 0, *dims, ws=fake, nbytes=need, sc=fake) == B_.MSDA_ERR_NULL
     assert bwd(0, 0, *dims, ws=fake, nbytes=need, gsc=fake) == B_.MSDA_ERR_NULL
-    assert bwd(0, 0, *dims, ws=fake, nbytes=need - 1) == B_.MSDA_ERR_WORKSPACE
+    least = lib.msda_backward_fused_workspace_min(*dims)
+    assert bwd(0, 0, *dims, ws=fake, nbytes=least - 1) == B_.MSDA_ERR_WORKSPACE
     assert bwd(0, 0, *dims, ws=ctypes.c_void_p((1 << 20) + 8), nbytes=need) == B_.MSDA_ERR_WORKSPACE
     # B = 0: nothing to do at all
     assert bwd(0, B_.MSDA_SOFTMAX_PER_LEVEL, 0, 80, 16, 2, 8, 2, 2) == B_.MSDA_OK
@@ -204,7 +237,8 @@ def test_volume_entry_points_reject_before_launch():
     b2 = lambda ws, nb: lib.msda3d_backward(fake, 0, fake, fake, fake, fake, fake, fake, fake,
                                             fake, 1, 80, 16, 2, 8, 2, 2, ws, nb, 0, z, z, None)
     assert b2(z, need) == B_.MSDA_ERR_NULL
-    assert b2(fake, need - 1) == B_.MSDA_ERR_WORKSPACE
+    assert b2(fake, lib.msda3d_backward_workspace_min(1, 80, 16, 2, 8, 2, 2) - 1) == \
+        B_.MSDA_ERR_WORKSPACE
     # the level table: rows (Z, H, W)
     ss = _i64([[2, 4, 8], [1, 2, 4]])
     st = _i64([0, 64])
@@ -260,15 +294,20 @@ def test_binding_refuses_cpu_tensors():
 
 
 def test_backward_noalloc_rejects_before_launch():
-    """The no-allocation backward rejects a problem whose workspace exceeds its
-    static scratch, and missing pointers, before touching the GPU."""
+    """The no-allocation backward rejects a problem whose smallest workspace
+    exceeds its static scratch, and missing pointers, before touching the
+    GPU; one whose full workspace exceeds it runs in passes."""
     lib = msda.load()
     z = ctypes.c_void_p(0)
     fake = ctypes.c_void_p(1 << 20)
     bwd = lambda *dims, ptr=fake: lib.msda_backward_noalloc(
         ptr, 0, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, *dims, 0, z, z, None)
-    big = (2, 22223, 22223, 8, 32, 4, 4)   # the encoder shape: ~365 MB of workspace
-    assert lib.msda_backward_workspace_size(*big) > msda.NOALLOC_SCRATCH_BYTES
+    enc = (2, 22223, 22223, 8, 32, 4, 4)   # the encoder shape: ~367 MB in one pass
+    assert (lib.msda_backward_workspace_min(*enc) <= msda.NOALLOC_SCRATCH_BYTES
+            < lib.msda_backward_workspace_size(*enc))
+    assert bwd(*enc, ptr=z) == B_.MSDA_ERR_NULL   # accepted as far as the pointers
+    big = (1, 22223, 22223, 8, 32, 16, 128)  # 2048 points per head: 134 MB in the smallest pass
+    assert lib.msda_backward_workspace_min(*big) > msda.NOALLOC_SCRATCH_BYTES
     assert bwd(*big) == B_.MSDA_ERR_SCRATCH
     small = (2, 22223, 300, 8, 32, 4, 4)   # the decoder shape fits
     assert 0 < lib.msda_backward_workspace_size(*small) <= msda.NOALLOC_SCRATCH_BYTES

@@ -188,6 +188,33 @@ def test_fused_accumulate(msda):
     assert e <= BWD_TOL
 
 
+@pytest.mark.parametrize("acc", [False, True])
+def test_fused_in_passes(msda, acc):
+    """The smallest fused workspace: grad_value in passes of 1024 queries of
+    one head of one batch (1500 = 1024 + 476; 2 batches x 2 heads), the
+    other gradients as ever."""
+    w = workloads.fused_case(611, 2, SHAPES, 1500, 2, 16, 4)
+    B, Nv, Nq, M, D, L, K = (w.dims[k] for k in ("B", "Nv", "Nq", "M", "D", "L", "K"))
+    least = msda.fused_workspace_min(B, Nv, Nq, M, D, L, K)
+    assert least < msda.fused_workspace_size(B, Nv, Nq, M, D, L, K)
+    _say(f"fused in passes acc={acc}, workspace {least} bytes")
+    x = dev_inputs(w)
+    g = torch.from_numpy(w.grad_out).cuda()
+    base = torch.randn(tuple(w.value.shape), generator=torch.Generator().manual_seed(4)).cuda()
+    gv0 = base.clone() if acc else torch.full(tuple(w.value.shape), float("nan"), device="cuda")
+    res = msda.backward_fused(**x, grad_out=g, grad_value=gv0, accumulate=acc,
+                              workspace=torch.empty(least, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    ref = ofused.backward(*_oracle_args(w), w.grad_out)
+    got_v = res[0].cpu().numpy() - (base.cpu().numpy() if acc else 0.0)
+    for name, a, r in (("grad_value", got_v, ref[0]),
+                       ("grad_sampling_offsets", res[1].cpu().numpy(), ref[1]),
+                       ("grad_attn_logits", res[2].cpu().numpy(), ref[2]),
+                       ("grad_reference_points", res[3].cpu().numpy(), ref[3])):
+        e = max_rel(a, r)
+        assert e <= BWD_TOL, f"{name} max rel {e:.3e}"
+
+
 def test_fused_empty(msda):
     _say("fused empty")
     w = workloads.fused_case(701, 1, SHAPES, 0, 2, 8, 3)

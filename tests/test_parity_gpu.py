@@ -553,6 +553,75 @@ def test_two_streams_backward_concurrently(msda):
             close(x.cpu().numpy(), r, BWD_TOL, f"{w.name} {n}")
 
 
+@pytest.mark.parametrize("acc", [False, True])
+@pytest.mark.parametrize("budget", ["min", "heads", "batches", "queries"])
+def test_backward_in_passes(msda, budget, acc):
+    """A workspace below workspace_size: grad_value in passes, each a box of
+    batches x heads x queries run as a problem of its own, the passes after
+    a query range's first adding to grad_value.  Budgets (3 batches, 4 heads,
+    2500 queries): "batches" holds 2 whole batches (passes of 2 and 1);
+    "queries" 1500 queries of every head of one batch (6 passes: 1500 +
+    1000 a batch); "heads" 1024 queries of two heads (18 passes); "min"
+    (workspace_min) 1024 queries of one head (36 passes: 1024 + 1024 + 452).
+    Overwrite mode starts from NaN."""
+    w = workloads.random_case(1500, 3, ((40, 56), (20, 28), (10, 14), (5, 7)), 2500, 4, 32, 4)
+    B, Nv, Nq, M, D, L, K = (w.dims[k] for k in ("B", "Nv", "Nq", "M", "D", "L", "K"))
+    full = msda.workspace_size(B, Nv, Nq, M, D, L, K)
+    nbytes = {"min": msda.workspace_min(B, Nv, Nq, M, D, L, K),
+              "heads": msda.workspace_size(1, Nv, 1024, 2, D, L, K),
+              "batches": msda.workspace_size(2, Nv, Nq, M, D, L, K),
+              "queries": msda.workspace_size(1, Nv, 1500, M, D, L, K)}[budget]
+    assert nbytes < full
+    _say(f"backward in passes: budget {budget} ({nbytes} of {full} bytes), acc={acc}")
+    x = dev_inputs(w)
+    g = torch.from_numpy(w.grad_out).cuda()
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    base = torch.randn(w.value.shape, device="cuda") if acc else None
+    gv0 = base.clone() if acc else torch.full(tuple(w.value.shape), float("nan"), device="cuda")
+    gv, gl, ga = msda.backward(**x, grad_out=g, grad_value=gv0, accumulate=acc, workspace=ws)
+    torch.cuda.synchronize()
+    rv, rl, ra = oracle_bwd(w)
+    got_v = gv.cpu().numpy() - (base.cpu().numpy() if acc else 0.0)
+    close(got_v, rv, BWD_TOL, "grad_value")
+    close(gl.cpu().numpy(), rl, BWD_TOL, "grad_sampling_loc")
+    close(ga.cpu().numpy(), ra, BWD_TOL, "grad_attn_weight")
+
+
+@pytest.mark.parametrize("D", [16, 128])
+def test_backward_head_passes_tile_kernel_and_sparse(msda, D):
+    """Head passes through both grad_value kernels: D = 128 takes the tile
+    kernel (the 5x6 level's one tile, 2400 records a head, split and added
+    atomically into its zeroed tile); the sparse maps (few points per pixel,
+    otherwise zero-filled whole) have most tiles empty, zeroed from the list."""
+    w = workloads.random_case(1510 + D, 2, ((64, 96), (32, 48), (5, 6)), 600, 3, D, 4)
+    B, Nv, Nq, M, _, L, K = (w.dims[k] for k in ("B", "Nv", "Nq", "M", "D", "L", "K"))
+    # room for two of the three heads of 600 queries: passes of heads {0, 1}
+    # and {2} of each batch
+    nbytes = msda.workspace_size(1, Nv, Nq, 2, D, L, K)
+    _say(f"head passes D={D} ({nbytes} bytes)")
+    x = dev_inputs(w)
+    g = torch.from_numpy(w.grad_out).cuda()
+    gv0 = torch.full(tuple(w.value.shape), float("nan"), device="cuda")
+    gv, gl, ga = msda.backward(**x, grad_out=g, grad_value=gv0,
+                               workspace=torch.empty(nbytes, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    rv, rl, ra = oracle_bwd(w)
+    close(gv.cpu().numpy(), rv, BWD_TOL, "grad_value")
+    close(gl.cpu().numpy(), rl, BWD_TOL, "grad_sampling_loc")
+    close(ga.cpu().numpy(), ra, BWD_TOL, "grad_attn_weight")
+
+
+def test_backward_below_min_workspace_raises(msda):
+    w = workloads.random_case(1501, 1, ((40, 56), (20, 28)), 2000, 2, 16, 4)
+    B, Nv, Nq, M, D, L, K = (w.dims[k] for k in ("B", "Nv", "Nq", "M", "D", "L", "K"))
+    least = msda.workspace_min(B, Nv, Nq, M, D, L, K)
+    x = dev_inputs(w)
+    g = torch.from_numpy(w.grad_out).cuda()
+    with pytest.raises(ValueError):
+        msda.backward(**x, grad_out=g, workspace=torch.empty(least - 256, dtype=torch.uint8,
+                                                              device="cuda"))
+
+
 @pytest.mark.parametrize("side", ["auto", None])
 def test_overwrite_replaces_every_element(msda, side):
     """Overwrite mode writes every element of grad_value: a NaN-filled buffer

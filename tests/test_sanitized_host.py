@@ -25,8 +25,10 @@ lib = ctypes.CDLL({host!r})
 p, i64 = ctypes.c_void_p, ctypes.c_int64
 lib.msda_validate_host.argtypes = [p, p] + [i64] * 7
 lib.msda3d_validate_host.argtypes = [p, p] + [i64] * 7
-for f in ("msda_backward_workspace_size", "msda_backward_fused_workspace_size",
-          "msda3d_backward_workspace_size"):
+SIZES = ("msda_backward_workspace_size", "msda_backward_fused_workspace_size",
+         "msda3d_backward_workspace_size", "msda_backward_workspace_min",
+         "msda_backward_fused_workspace_min", "msda3d_backward_workspace_min")
+for f in SIZES:
     getattr(lib, f).argtypes = [i64] * 7
     getattr(lib, f).restype = ctypes.c_size_t
 lib.msda_status_string.argtypes = [ctypes.c_int]
@@ -53,17 +55,15 @@ for trial in range(4000):
                       for v in (2, 300, 8, 32, 4))
     fn = lib.msda3d_validate_host if dims3 else lib.msda_validate_host
     fn(ptr(ext), ptr(starts), B, Nv, Nq, M, D, L, K)
-    for f in ("msda_backward_workspace_size", "msda_backward_fused_workspace_size",
-              "msda3d_backward_workspace_size"):
+    for f in SIZES:
         getattr(lib, f)(B, Nv, Nq, M, D, L, K)
     n += 1
 for dims in [(2, 22223, 22223, 8, 32, 4, 4), (4, 22223, 22223, 8, 32, 4, 8),
              ((1 << 40), 80, 16, 2, 8, 2, 2), (1, (1 << 40), 16, 2, 8, 2, 2),
              (1, 80, (1 << 40), 2, 8, 2, 2), (1, 80, 16, (1 << 30), 8, 2, 2),
              (1, 80, 16, 2, 8, 2, (1 << 40)), (1 << 30, 1, 1, 1, 4, 1, 1)]:
-    lib.msda_backward_workspace_size(*dims)
-    lib.msda_backward_fused_workspace_size(*dims)
-    lib.msda3d_backward_workspace_size(*dims)
+    for f in SIZES:
+        getattr(lib, f)(*dims)
 print("host checks:", n, "fuzzed calls", flush=True)
 
 # the oracles, against their pins

@@ -184,6 +184,30 @@ def test_volume_split_bins(msda, D):
         assert e <= BWD_TOL, f"{w.name}: {name} max rel {e:.3e}"
 
 
+@pytest.mark.parametrize("D", [32, 64])
+def test_volume_in_passes(msda, D):
+    # the smallest workspace (msda3d_backward_workspace_min): grad_value in
+    # passes of 1024 queries of one head of one batch (1500 = 1024 + 476;
+    # 2 batches x 2 heads); overwrite mode from NaN
+    w = workloads.volume_case(2800 + D, 2, ((1, 5, 6), (2, 8, 9)), 1500, 2, D, 4)
+    B, Nv, Nq, M, _, L, K = (w.dims[k] for k in ("B", "Nv", "Nq", "M", "D", "L", "K"))
+    least = msda.workspace_min3d(B, Nv, Nq, M, D, L, K)
+    assert least < msda.workspace_size3d(B, Nv, Nq, M, D, L, K)
+    x = dev_inputs(w)
+    g = torch.from_numpy(w.grad_out).cuda()
+    _say(f"volume in passes D={D}, workspace {least} bytes")
+    gv0 = torch.full(tuple(w.value.shape), float("nan"), device="cuda")
+    gv, gl, ga = msda.backward3d(**x, grad_out=g, grad_value=gv0,
+                                 workspace=torch.empty(least, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    rv, rl, ra = ov.backward(*_args(w), w.grad_out, mode=oracle.SPEC)
+    for name, a, r in (("grad_value", gv.cpu().numpy(), rv),
+                       ("grad_sampling_loc", gl.cpu().numpy(), rl),
+                       ("grad_attn_weight", ga.cpu().numpy(), ra)):
+        e = max_rel(a, r)
+        assert e <= BWD_TOL, f"{w.name}: {name} max rel {e:.3e}"
+
+
 def test_volume_workload(msda):
     # the voxel workload: pyramid 4x128x128, 2x64x64, 1x32x32, 16,384 bird's-eye
     # queries, M=8, D=32, K=4, forward and backward in full
