@@ -28,9 +28,11 @@ measured here by the probe kernel of libmsda_probe.so ("gather_ceiling").
 "stream_copy" is a streaming 16-byte copy, the achievable HBM bandwidth.
 "decoder" and "train_bf16" are the other two configurations (forward and
 backward each).  "cpu_baseline" times the CPU oracle on this host's cores
-and on one core.  --extra adds the fused prologue at the encoder shape, the
-3-D trilinear variant on a voxel workload, and DAT's sampled-key attention
-(sampling and MFMA attention) at its two configurations.
+and on one core.  --extra adds the encoder backward in workspaces below its
+one-pass size (grad_value in passes, and the no-allocation entry point), the
+fused prologue at the encoder shape, the 3-D trilinear variant on a voxel
+workload, and DAT's sampled-key attention (sampling and MFMA attention) at its
+two configurations.
 """
 from __future__ import annotations
 
@@ -192,6 +194,32 @@ def measure_config(torch, msda, w, bf16, reps, flush, label):
                            "algorithmic_bytes": bm["backward"]}
     log(f"{label}: {json.dumps(res)}")
     return res, x, g, bm
+
+
+def measure_bounded(torch, msda, x, g, dims, reps):
+    """The encoder backward with workspaces below the one-pass size (grad_value
+    in passes, see msda_backward_workspace_min), and through the no-allocation
+    entry point (its 64 MiB static scratch), back to back."""
+    B, Nv, Nq, M, D, L, K = (dims[k] for k in ("B", "Nv", "Nq", "M", "D", "L", "K"))
+    full = msda.workspace_size(B, Nv, Nq, M, D, L, K)
+    bufs = dict(grad_value=torch.empty(x["value"].shape, dtype=torch.float32, device="cuda"),
+                grad_sampling_loc=torch.empty_like(x["sampling_loc"]),
+                grad_attn_weight=torch.empty_like(x["attn_weight"]))
+    res = {"one_pass_bytes": full,
+           "least_bytes": msda.workspace_min(B, Nv, Nq, M, D, L, K)}
+    for label, nbytes in (("full", full), ("64MiB", 64 << 20), ("32MiB", 32 << 20)):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        fn = lambda: msda.backward(**x, grad_out=g, **bufs, validate=False, workspace=ws)
+        for _ in range(3):
+            fn()
+        res[label] = {"bytes": nbytes, "us_warm": time_warm(torch, fn, reps)}
+        del ws
+    fn = lambda: msda.backward_noalloc(**x, grad_out=g, side_stream="auto", **bufs)
+    for _ in range(3):
+        fn()
+    res["noalloc"] = {"bytes": msda.NOALLOC_SCRATCH_BYTES, "us_warm": time_warm(torch, fn, reps)}
+    log(f"bounded workspace: {json.dumps(res)}")
+    return res
 
 
 def measure_fused(torch, msda, reps, flush):
@@ -648,6 +676,8 @@ def main():
 
     extra = {}
     if args.extra:
+        extra["encoder_bounded_workspace"] = measure_bounded(torch, msda, x, g, dims,
+                                                             max(5, args.reps // 3))
         extra["fused_encoder"] = measure_fused(torch, msda, args.reps, flush)
         extra["volume"] = measure_volume(torch, msda, args.reps, flush)
         extra["dat"] = measure_dat(torch, msda, args.reps, flush)

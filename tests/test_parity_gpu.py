@@ -587,6 +587,26 @@ def test_backward_in_passes(msda, budget, acc):
     close(ga.cpu().numpy(), ra, BWD_TOL, "grad_attn_weight")
 
 
+def test_backward_in_passes_bf16_align_corners(msda):
+    """Query-range passes (room for 1100 queries of every head: 2 passes a
+    batch) with a bf16 value and the align_corners convention, against the
+    oracle on the bf16-rounded value in that convention."""
+    w = workloads.random_case(1520, 2, ((40, 56), (20, 28), (10, 14)), 2200, 4, 32, 4,
+                              -0.1, 1.1, bf16=True)
+    B, Nv, Nq, M, D, L, K = (w.dims[k] for k in ("B", "Nv", "Nq", "M", "D", "L", "K"))
+    nbytes = msda.workspace_size(1, Nv, 1100, M, D, L, K)
+    _say(f"backward in passes, bf16 value, align_corners ({nbytes} bytes)")
+    x = dev_inputs(w, bf16=True)
+    g = torch.from_numpy(w.grad_out).cuda()
+    gv, gl, ga = msda.backward(**x, grad_out=g, align_corners=True,
+                               workspace=torch.empty(nbytes, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    rv, rl, ra = oracle_bwd(w, mode=oracle.SPEC | oracle.ALIGN)
+    close(gv.cpu().numpy(), rv, BWD_TOL, "grad_value")
+    close(gl.cpu().numpy(), rl, BWD_TOL, "grad_sampling_loc")
+    close(ga.cpu().numpy(), ra, BWD_TOL, "grad_attn_weight")
+
+
 @pytest.mark.parametrize("D", [16, 128])
 def test_backward_head_passes_tile_kernel_and_sparse(msda, D):
     """Head passes through both grad_value kernels: D = 128 takes the tile
