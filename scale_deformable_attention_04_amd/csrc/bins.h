@@ -18,6 +18,7 @@ constexpr int kTilePx = kTile * kTile;
 using msda_host::kChunk;                   // records per grad_value work item, at most
 constexpr int kHistLds = 4096;             // bins of one (batch, head) kept in an LDS histogram
 constexpr int kScanThreads = 512;           // placed sooner beside the dots kernel than 1024
+constexpr int kScanBlock = 8 * kScanThreads;  // bins scanned by one workgroup
 constexpr int kTileGrid = 16384;           // workgroups of the tile kernel, at most
 
 template <int CTRL, int ROWS>
@@ -436,9 +437,12 @@ bin_count_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__
 
 // ---------------------------------------------------------------------------
 // backward: scan of the bin counts, work list, zero list
-// One workgroup of kScanThreads.  Bins are visited in (batch, tile, head)
-// order, which is also their order in memory: bin (b * nb_max + tile) * M + m;
-// all batches form one flat scan.
+// One workgroup of kScanThreads per block of kScanBlock bins.  Bins are
+// visited in (batch, tile, head) order, which is also their order in memory:
+// bin (b * nb_max + tile) * M + m; all batches form one flat scan.  Each
+// workgroup first sums the counts of every bin before its block (a
+// redundant reduction, coalesced: the blocks are few -- two at the encoder
+// shape -- and no workgroup waits for another), then scans its block.
 // Each bin of n > 0 points becomes ceil(n / kChunk) work items (bin, first
 // record, records, whole bin).  In overwrite mode the bins whose pixels no
 // single work item writes outright -- empty bins, and bins split over several
@@ -475,6 +479,29 @@ __device__ __forceinline__ void block_exclusive_scan3(uint32_t &a, uint32_t &b, 
     __syncthreads();  // s_wave is reused by the next call
 }
 
+// Sum of (a, b, c, d) over the kScanThreads threads of the block, returned
+// to every thread.
+__device__ __forceinline__ uint4 block_sum4(uint4 v, uint4 *s_wave) {
+    constexpr int kWaves = kScanThreads / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v.x = wave_inclusive_scan(v.x);
+    v.y = wave_inclusive_scan(v.y);
+    v.z = wave_inclusive_scan(v.z);
+    v.w = wave_inclusive_scan(v.w);
+    if (lane == 63) s_wave[wave] = v;  // the wave's totals
+    __syncthreads();
+    uint4 t = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+        t.x += s_wave[i].x;
+        t.y += s_wave[i].y;
+        t.z += s_wave[i].z;
+        t.w += s_wave[i].w;
+    }
+    __syncthreads();  // s_wave is reused
+    return t;
+}
+
 // The items of a bin of cnt > kChunk records: nch = ceil(cnt / kChunk) of
 // them, item k taking records [floor(k cnt / nch), floor((k+1) cnt / nch)),
 // so that each holds between kChunk / 2 and kChunk records.  The bounds are
@@ -502,25 +529,34 @@ bin_scan_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ 
                 uint32_t *__restrict__ cursor, uint4 *__restrict__ items,
                 uint32_t *__restrict__ work_total, uint32_t *__restrict__ zero,
                 uint32_t *__restrict__ split, int B, Dims dm) {
-    constexpr int kPer = 8;
-    constexpr uint32_t kPass = kScanThreads * kPer;  // bins per pass
-    static_assert(kPass < (1 << 16), "list counts of one pass fit 16 bits");
+    constexpr int kPer = kScanBlock / kScanThreads;
+    constexpr uint32_t kPass = kScanBlock;  // bins of the workgroup
+    static_assert(kPass < (1 << 16), "list counts of one block fit 16 bits");
     __shared__ LevelLds s_lv;
     __shared__ uint4 s_wave[kScanThreads / 64 + 1];
-    // one pass of bins in flat order: their counts; for each thread's kPer
+    // the block's bins in flat order: their counts; for each thread's kPer
     // bins, the first record, first item, and zero- and split-list positions
     // (16 bits each) of the first.  Little LDS, so that the workgroup finds a
     // place beside the kernel on the other stream.
     __shared__ uint32_t s_cnt[kPass], s_e[kScanThreads], s_ch[kScanThreads], s_zs[kScanThreads];
     stage_bin_levels<VOL>(&s_lv, shapes, starts, dm.L, dm.Nv, dm.nb_max);
-    // The used bins of every batch as one flat sequence f = (b * nbins + tile) * M + m,
-    // scanned in passes of kPass.  Bin f is at f + b * gap in memory (the
-    // bins of batch b start at b * nb_max * M).  Counts are loaded and the
-    // results stored with consecutive lanes on consecutive bins; in between,
+    // The used bins of every batch as one flat sequence f = (b * nbins + tile) * M + m;
+    // this workgroup scans f in [base, base + kPass).  Bin f is at f + b * gap in
+    // memory (the bins of batch b start at b * nb_max * M).  Counts are loaded and
+    // the results stored with consecutive lanes on consecutive bins; in between,
     // each thread sums kPer consecutive bins, through LDS.
     const uint32_t nbins = (uint32_t)s_lv.nbins, Mu = (uint32_t)dm.M;
     const uint32_t per_b = nbins * Mu, gap = ((uint32_t)dm.nb_max - nbins) * Mu;
     const uint32_t nf = per_b * (uint32_t)B;
+    const uint32_t base = blockIdx.x * kPass;
+    if (base >= nf) {  // past the used bins (the grid is sized for the bound)
+        if (blockIdx.x == 0 && threadIdx.x == 0) {  // no bins at all
+            work_total[0] = 0u;
+            work_total[1] = 0u;
+            work_total[2] = 0u;
+        }
+        return;
+    }
     const bool zeroing = dm.zero_list != 0, combine = dm.combine != 0;
     // split bins need zeroed tiles only when their items add atomically
     const uint32_t zero_above = combine ? 0xffffffffu : (uint32_t)kChunk;
@@ -528,17 +564,34 @@ bin_scan_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ 
         return ((zeroing && (c == 0u || c > zero_above)) ? 1u : 0u) |
                ((combine && c > (uint32_t)kChunk) ? 1u << 16 : 0u);
     };
-    // records, items, zero-list and split-list entries of the passes before
-    uint32_t carry_e = 0, carry_c = 0, carry_z = 0, carry_s = 0;
-    for (uint32_t base = 0; base < nf; base += kPass) {
-        // 1. the pass's counts, coalesced, into LDS (zero past the end)
+    // 0. records, items, zero-list and split-list entries of the bins before
+    // the block (the list counts summed apart: they may pass 16 bits)
+    uint32_t carry_e, carry_c, carry_z, carry_s;
+    {
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        for (uint32_t f = threadIdx.x; f < base; f += kScanThreads) {
+            const uint32_t c = counts[f + f / per_b * gap];
+            const uint32_t l = listed(c);
+            v.x += c;
+            v.y += (c + kChunk - 1) / kChunk;
+            v.z += l & 0xffffu;
+            v.w += l >> 16;
+        }
+        v = block_sum4(v, s_wave);
+        carry_e = v.x;
+        carry_c = v.y;
+        carry_z = v.z;
+        carry_s = v.w;
+    }
+    {
+        // 1. the block's counts, coalesced, into LDS (zero past the end)
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const uint32_t f = base + threadIdx.x + i * kScanThreads;
             s_cnt[f - base] = f < nf ? counts[f + f / per_b * gap] : 0u;
         }
         __syncthreads();
-        // 2. thread t: bins t * kPer ... of the pass
+        // 2. thread t: bins t * kPer ... of the block
         const uint32_t j0 = threadIdx.x * kPer;
         uint32_t cnt[kPer], e = 0, ch = 0, zs = 0;
 #pragma unroll
@@ -554,9 +607,7 @@ bin_scan_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ 
         s_ch[threadIdx.x] = ch;
         s_zs[threadIdx.x] = zs;
         __syncthreads();
-        // 3. bin starts, cursors, work items and list entries, coalesced;
-        // a rolled loop, since this one workgroup's instruction fetches are
-        // not hidden by other waves
+        // 3. bin starts, cursors, work items and list entries, coalesced
         {
 #pragma unroll 1
             for (uint32_t f = base + threadIdx.x; f < nf && f < base + kPass; f += kScanThreads) {
@@ -595,9 +646,9 @@ bin_scan_kernel(const int64_t *__restrict__ shapes, const int64_t *__restrict__ 
         carry_c += tot.y;
         carry_z += tot.z & 0xffffu;
         carry_s += tot.z >> 16;
-        __syncthreads();  // the LDS arrays are refilled by the next pass
     }
-    if (threadIdx.x == 0) {
+    // the block holding the last bin writes the totals
+    if (base + kPass >= nf && threadIdx.x == 0) {
         work_total[0] = carry_c;
         work_total[1] = carry_z;
         work_total[2] = carry_s;
@@ -1509,7 +1560,9 @@ msda_status run_bins(const int64_t *shapes, const int64_t *starts, const float *
     ex.stamp(kStageCount, true, s);
 
     ex.stamp(kStageScan, false, s);
-    hipLaunchKernelGGL(bin_scan_kernel<VOL>, dim3(1), dim3(kScanThreads), 0, s, shapes, starts,
+    // a workgroup per block of bins the bound allows; those past the used bins exit
+    const unsigned scan_grid = (unsigned)((wl.bm_bins + kScanBlock - 1) / kScanBlock);
+    hipLaunchKernelGGL(bin_scan_kernel<VOL>, dim3(scan_grid), dim3(kScanThreads), 0, s, shapes, starts,
                        w.counts, w.start, w.cursor, w.items, w.work_total, w.zero, w.split,
                        (int)B, dm);
     st = hip_status(hipGetLastError());
