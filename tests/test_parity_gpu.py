@@ -587,6 +587,38 @@ def test_backward_in_passes(msda, budget, acc):
     close(ga.cpu().numpy(), ra, BWD_TOL, "grad_attn_weight")
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_backward_in_passes_random_budgets(msda, seed):
+    """Random shapes and workspaces anywhere between workspace_min and
+    workspace_size (every plan shape, ragged boxes, both grad_value kernels),
+    overwrite from NaN or accumulate, against the oracle."""
+    r = np.random.default_rng(1600 + seed)
+    B, M = int(r.integers(1, 4)), int(r.integers(1, 5))
+    Nq, K = int(r.integers(300, 2600)), int(r.integers(1, 5))
+    D = int(r.choice([8, 16, 32, 64, 128]))
+    L = int(r.integers(1, 4))
+    shapes = tuple((int(r.integers(3, 40)), int(r.integers(3, 60))) for _ in range(L))
+    acc = bool(r.integers(0, 2))
+    w = workloads.random_case(1610 + seed, B, shapes, Nq, M, D, K)
+    Nv = w.dims["Nv"]
+    lo, hi = msda.workspace_min(B, Nv, Nq, M, D, L, K), msda.workspace_size(B, Nv, Nq, M, D, L, K)
+    nbytes = int(r.integers(lo, hi)) if hi > lo else lo
+    _say(f"passes, random budget: B={B} M={M} Nq={Nq} D={D} L={L} K={K} shapes={shapes} "
+         f"acc={acc} workspace {nbytes} of [{lo}, {hi}]")
+    x = dev_inputs(w)
+    g = torch.from_numpy(w.grad_out).cuda()
+    base = torch.randn(w.value.shape, device="cuda") if acc else None
+    gv0 = base.clone() if acc else torch.full(tuple(w.value.shape), float("nan"), device="cuda")
+    gv, gl, ga = msda.backward(**x, grad_out=g, grad_value=gv0, accumulate=acc,
+                               workspace=torch.empty(nbytes, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    rv, rl, ra = oracle_bwd(w)
+    got_v = gv.cpu().numpy() - (base.cpu().numpy() if acc else 0.0)
+    close(got_v, rv, BWD_TOL, "grad_value")
+    close(gl.cpu().numpy(), rl, BWD_TOL, "grad_sampling_loc")
+    close(ga.cpu().numpy(), ra, BWD_TOL, "grad_attn_weight")
+
+
 def test_backward_in_passes_bf16_align_corners(msda):
     """Query-range passes (room for 1100 queries of every head: 2 passes a
     batch) with a bf16 value and the align_corners convention, against the
