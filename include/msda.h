@@ -97,8 +97,8 @@ typedef enum msda_status {
     MSDA_ERR_UNSUPPORTED = -4, /* valid but outside the limits above (D, L, size)     */
     MSDA_ERR_HIP = -5,         /* the HIP runtime refused a launch (see msda_last_hip_error) */
     MSDA_ERR_WORKSPACE = -6,   /* workspace too small or not 256-byte aligned             */
-    MSDA_ERR_SCRATCH = -7      /* msda_backward_noalloc: the problem needs more scratch
-                                  than MSDA_NOALLOC_SCRATCH_BYTES                      */
+    MSDA_ERR_SCRATCH = -7      /* msda_backward_noalloc: even the smallest pass needs
+                                  more than MSDA_NOALLOC_SCRATCH_BYTES                 */
 } msda_status;
 
 typedef enum msda_dtype {
@@ -207,9 +207,10 @@ msda_status msda_backward(const void *value, int value_dtype,
  * that device current).  Problems whose msda_backward_workspace_size exceeds
  * MSDA_NOALLOC_SCRATCH_BYTES run in passes (see msda_backward_workspace_min);
  * those whose msda_backward_workspace_min exceeds it are rejected with
- * MSDA_ERR_SCRATCH before any work is enqueued.  Every call on one GPU uses the same array, and each call
- * clears what it needs: calls that overlap in time on one GPU (other streams,
- * other threads) race on it and must not be made.
+ * MSDA_ERR_SCRATCH before any work is enqueued.  Every call on one GPU uses
+ * the same array, and each call clears what it needs: calls that overlap in
+ * time on one GPU (other streams, other threads) race on it and must not be
+ * made.
  */
 #define MSDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 msda_status msda_backward_noalloc(const void *value, int value_dtype,

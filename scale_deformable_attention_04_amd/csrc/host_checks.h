@@ -231,10 +231,10 @@ inline const char *status_string(int status) {
         return "outside the supported limits (D in {4,8,...,256}, 1 <= L <= 16, 31-bit slices)";
     case MSDA_ERR_HIP: return "the HIP runtime refused a launch";
     case MSDA_ERR_WORKSPACE:
-        return "workspace smaller than msda_backward_workspace_size or not 256-byte aligned";
+        return "workspace smaller than the *_workspace_min size or not 256-byte aligned";
     case MSDA_ERR_SCRATCH:
-        return "the problem needs more scratch than msda_backward_noalloc's static buffer "
-               "(MSDA_NOALLOC_SCRATCH_BYTES)";
+        return "even the smallest pass needs more scratch than msda_backward_noalloc's "
+               "static buffer (MSDA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown msda status";
     }
 }
