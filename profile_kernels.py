@@ -216,7 +216,9 @@ def _trace_stats(dirpath):
     """Per (kernel, workgroups) launch statistics from a kernel trace."""
     per = collections.defaultdict(list)
     for r in _rows(os.path.join(dirpath, "**", "*kernel_trace.csv")):
-        wgs = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+        wgs = 1
+        for ax in "XYZ":  # workgroups over all three grid dimensions
+            wgs *= int(r.get(f"Grid_Size_{ax}") or 1) // max(1, int(r.get(f"Workgroup_Size_{ax}") or 1))
         dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
         per[(short_name(r["Kernel_Name"]), wgs)].append(dur)
     total = sum(sum(v) for v in per.values()) or 1.0
