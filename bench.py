@@ -714,7 +714,12 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
-        result["cpu_baseline"] = cpu_baseline(w)
+        cpu = cpu_baseline(w)
+        # the GPU step rate over the oracle's, on all cores and on one
+        cpu["gpu_over_oracle"] = result["value"] / cpu["value"]
+        if "single_core" in cpu:
+            cpu["single_core"]["gpu_over_oracle"] = result["value"] / cpu["single_core"]["value"]
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 
