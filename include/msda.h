@@ -237,7 +237,9 @@ msda_status msda_backward_noalloc(const void *value, int value_dtype,
  *   list of tiles to zero)   4 zeroing of the listed tiles, then the record
  *   scatter into tiles   5 grad_value tiles
  * A small problem (see msda_backward) runs as one kernel, recorded as stage 0;
- * its other stages are empty.  With grad_value in several passes (a
+ * its other stages are empty.  Without a side stream, the stage-0 kernel
+ * also clears the bin counters, so stage 1 then holds only grad_value's
+ * zero-fill (when there is one).  With grad_value in several passes (a
  * workspace below msda_backward_workspace_size), stages 1-5 are recorded
  * from their start in the first pass to their end in the last.
  * events: 2 * MSDA_BWD_STAGES hipEvent_t created by the caller (with timing);

@@ -1516,7 +1516,7 @@ msda_status run_bins(const int64_t *shapes, const int64_t *starts, const float *
                      const float *attn, const float *gout, float *gval, int64_t B, int64_t Nv,
                      int64_t Nq, int64_t M, int64_t L, int64_t K, int64_t Ms, int64_t Nqs,
                      const WorkLayout &wl, unsigned char *ws, bool accumulate, bool align,
-                     const Exec &ex) {
+                     const Exec &ex, bool counts_clear) {
     const hipStream_t s = ex.s;
     const Work w = work_at(wl, ws);
     const bool gather = uses_gather<D>(Nq, Ms);
@@ -1524,8 +1524,10 @@ msda_status run_bins(const int64_t *shapes, const int64_t *starts, const float *
     // untouched tiles are zeroed from the list
     const bool zero_list = !accumulate && (gather || Nq * L * K >= 2 * Nv || M != Ms);
     // the counts region is padded to 256 bytes, so whole float4s can be cleared
+    // (unless the caller has: counts_clear)
     ex.stamp(kStageClear, false, s);
-    msda_status st = fill_zero(w.counts, (wl.off_start - wl.off_counts) / 16, s);
+    msda_status st =
+        counts_clear ? MSDA_OK : fill_zero(w.counts, (wl.off_start - wl.off_counts) / 16, s);
     if (st == MSDA_OK && !accumulate && !zero_list)
         st = fill_zero(gval, (size_t)(B * Nv * M * D) / 4, s);
     if (st != MSDA_OK) return st;
@@ -1603,12 +1605,14 @@ msda_status run_bins(const int64_t *shapes, const int64_t *starts, const float *
 // workspace.  Boxes of different batches or heads write disjoint parts of
 // grad_value; the boxes after the first of a query range add to it.  Passes
 // are enqueued in order on s, which orders their use of the workspace.
+// counts_clear: the first pass's bin counters are zero already (cleared by
+// the kernel enqueued before it on s).
 template <int D, bool VOL>
 msda_status run_bins_passes(const int64_t *shapes, const int64_t *starts, const float *loc,
                             const float *attn, const float *gout, float *gval, int64_t B,
                             int64_t Nv, int64_t Nq, int64_t M, int64_t L, int64_t K,
                             const PassPlan &pp, unsigned char *ws, bool accumulate, bool align,
-                            const Exec &ex) {
+                            const Exec &ex, bool counts_clear = false) {
     const int64_t coords = VOL ? 3 : 2, LK = L * K;
     auto part = [](int64_t from, int64_t step, int64_t n) { return n - from < step ? n - from : step; };
     for (int64_t b0 = 0; b0 < B; b0 += pp.nb) {
@@ -1627,7 +1631,7 @@ msda_status run_bins_passes(const int64_t *shapes, const int64_t *starts, const 
                 const msda_status st = run_bins<D, VOL>(
                     shapes, starts, loc + coords * row * LK, attn + row * LK, gout + row * D,
                     gval + (b0 * Nv * M + m0) * D, nb, Nv, nq, nm, L, K, M, Nq, wl, ws,
-                    accumulate || q0 > 0, align, ep);
+                    accumulate || q0 > 0, align, ep, counts_clear && ep.first);
                 if (st != MSDA_OK) return st;
             }
         }

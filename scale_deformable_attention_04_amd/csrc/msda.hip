@@ -310,13 +310,19 @@ bwd_dots_kernel(const VT *__restrict__ value, const int64_t *__restrict__ shapes
                 const int64_t *__restrict__ starts, const float *__restrict__ loc,
                 const float *__restrict__ attn, const float *__restrict__ grad_out,
                 float *__restrict__ grad_loc, float *__restrict__ grad_attn,
-                float *__restrict__ ref_part, ScaleBwd sb, Dims dm) {
+                float *__restrict__ ref_part, ScaleBwd sb, float4 *__restrict__ clear,
+                uint32_t clear_n4, Dims dm) {
     constexpr int G = D / 4;
     constexpr int IPB = kThreads / G;
     __shared__ LevelLds s_lv;
     extern __shared__ __align__(16) unsigned char smem[];
     uint4 *s_off = reinterpret_cast<uint4 *>(smem);  // row offsets, then the dots
     float4 *s_aux = reinterpret_cast<float4 *>(s_off + IPB * dm.PS);
+
+    // on one stream, the bin counters of the grad_value pipeline that follows
+    // (clear_n4 float4s, none otherwise)
+    for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < clear_n4; i += gridDim.x * kThreads)
+        clear[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 
     const int M = dm.M, K = dm.K, LK = dm.L * dm.K, Nq = dm.Nq;
     // per level, d pixel / d (location or offset): (W, H) or (W-1, H-1), over
@@ -944,6 +950,12 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
     if (fz) fz->in_dots = fz->softmax_run > 0 && p.pc == L * K;
     float *ref_part = fz && fz->in_dots ? fz->ref_part : nullptr;
     const ScaleBwd sb = fz && fz->in_dots ? fz->scale : ScaleBwd{nullptr, nullptr, nullptr};
+    // on one stream this kernel runs just before the grad_value pipeline and
+    // also clears the bin counters of its first pass, which saves that pass a
+    // launch (latency-bound small problems such as the decoder's gain ~5 us)
+    const bool clear_here = ds == ex.s;
+    float4 *clear = reinterpret_cast<float4 *>(ws + pp.wl.off_counts);
+    const uint32_t clear_n4 = (uint32_t)((pp.wl.off_start - pp.wl.off_counts) / 16);
     ex.stamp(kStageDots, false, ds);
     msda_status st = per_batch(B, gq * M, [&](int64_t b0, unsigned grid) {
         Dims d2{(int)Nv, (int)Nq, (int)M, (int)L, (int)K, p.pc, p.ps, (int)b0, (int)gq, 0, 0};
@@ -954,14 +966,15 @@ msda_status launch_bwd(const void *value, const int64_t *shapes, const int64_t *
         // one workgroup per block of queries: beside the grad_value kernels the
         // backward takes the same time with a capped persistent grid (measured:
         // 512 workgroups), and this kernel finishes sooner uncapped
+        const bool c = clear_here && b0 == 0;
         hipLaunchKernelGGL((bwd_dots_kernel<D, VT>), dim3(grid), dim3(kThreads), p.lds, ds,
                            static_cast<const VT *>(value), shapes, starts, loc, attn, gout, gloc,
-                           gattn, ref_part, sb, d2);
+                           gattn, ref_part, sb, c ? clear : nullptr, c ? clear_n4 : 0u, d2);
     });
     if (st != MSDA_OK) return st;
     ex.stamp(kStageDots, true, ds);
     return run_bins_passes<D, false>(shapes, starts, loc, attn, gout, gval, B, Nv, Nq, M, L, K,
-                                     pp, ws, accumulate, align, ex);
+                                     pp, ws, accumulate, align, ex, clear_here);
 }
 
 template <typename VT>
