@@ -22,7 +22,8 @@ its average duration there give "achieved", against the 8 TB/s HBM peak.
 "traffic" is the HBM byte count rocprofv3 measured for that kernel
 (profiles/traffic.json) and "counters" its L2 hit rate and atomic requests
 (profiles/counters.json), each when taken on the current 2-D kernel sources.
-"roofline.forward" places the forward against both of its ceilings: the HBM
+"roofline.alone" is the same kernel timed with the backward on one stream,
+nothing beside it.  "roofline.forward" places the forward against both of its ceilings: the HBM
 roofline (cold and warm) and the row-gather rate of the vector memory path,
 measured here by the probe kernel of libmsda_probe.so ("gather_ceiling").
 "stream_copy" is a streaming 16-byte copy, the achievable HBM bandwidth.
@@ -664,6 +665,21 @@ def main():
                 "achievable_copy_GBps": round(copy["GBps"], 1),
                 "forward": forward_roofline(enc["forward"], bm["points"], ceiling)}
     roofline["forward"]["counters"] = counters_for(KERNELS["forward"])
+    # the same kernel with nothing beside it: the backward on one stream (in
+    # the step the grad_attn/grad_loc kernel shares the chip with the grad_value
+    # kernels, and its duration there depends on how the two share it)
+    if dom == "forward":
+        us_alone = us
+    else:
+        sets = [msda.make_events(dom) for _ in range(20)]
+        for ev in sets:
+            msda.backward(**x, grad_out=g, grad_value=gv, grad_sampling_loc=gl,
+                          grad_attn_weight=ga, validate=False, events=ev, side_stream=None)
+        torch.cuda.synchronize()
+        us_alone = statistics.mean(msda.stage_times(ev)[k] for ev in sets)
+    roofline["alone"] = {"avg_launch_us": round(us_alone, 2),
+                         "achieved": round(bm[dom] / us_alone / 1e3, 1),
+                         "frac": round(bm[dom] / us_alone / 1e3 / HBM_PEAK_GBS, 4)}
 
     # the other two configurations: the decoder and the bf16 training shape
     dec_w = workloads.make(2)
