@@ -553,9 +553,10 @@ def test_two_streams_backward_concurrently(msda):
             close(x.cpu().numpy(), r, BWD_TOL, f"{w.name} {n}")
 
 
+@pytest.mark.parametrize("side", ["auto", None])
 @pytest.mark.parametrize("acc", [False, True])
 @pytest.mark.parametrize("budget", ["min", "heads", "batches", "queries"])
-def test_backward_in_passes(msda, budget, acc):
+def test_backward_in_passes(msda, budget, acc, side):
     """A workspace below workspace_size: grad_value in passes, each a box of
     batches x heads x queries run as a problem of its own, the passes after
     a query range's first adding to grad_value.  Budgets (3 batches, 4 heads,
@@ -563,7 +564,8 @@ def test_backward_in_passes(msda, budget, acc):
     "queries" 1500 queries of every head of one batch (6 passes: 1500 +
     1000 a batch); "heads" 1024 queries of two heads (18 passes); "min"
     (workspace_min) 1024 queries of one head (36 passes: 1024 + 1024 + 452).
-    Overwrite mode starts from NaN."""
+    Overwrite mode starts from NaN.  On one stream (side None) the dots kernel
+    clears the first pass's bin counters and the later passes clear their own."""
     w = workloads.random_case(1500, 3, ((40, 56), (20, 28), (10, 14), (5, 7)), 2500, 4, 32, 4)
     B, Nv, Nq, M, D, L, K = (w.dims[k] for k in ("B", "Nv", "Nq", "M", "D", "L", "K"))
     full = msda.workspace_size(B, Nv, Nq, M, D, L, K)
@@ -572,13 +574,15 @@ def test_backward_in_passes(msda, budget, acc):
               "batches": msda.workspace_size(2, Nv, Nq, M, D, L, K),
               "queries": msda.workspace_size(1, Nv, 1500, M, D, L, K)}[budget]
     assert nbytes < full
-    _say(f"backward in passes: budget {budget} ({nbytes} of {full} bytes), acc={acc}")
+    _say(f"backward in passes: budget {budget} ({nbytes} of {full} bytes), acc={acc}, "
+         f"side_stream={side}")
     x = dev_inputs(w)
     g = torch.from_numpy(w.grad_out).cuda()
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     base = torch.randn(w.value.shape, device="cuda") if acc else None
     gv0 = base.clone() if acc else torch.full(tuple(w.value.shape), float("nan"), device="cuda")
-    gv, gl, ga = msda.backward(**x, grad_out=g, grad_value=gv0, accumulate=acc, workspace=ws)
+    gv, gl, ga = msda.backward(**x, grad_out=g, grad_value=gv0, accumulate=acc, workspace=ws,
+                               side_stream=side)
     torch.cuda.synchronize()
     rv, rl, ra = oracle_bwd(w)
     got_v = gv.cpu().numpy() - (base.cpu().numpy() if acc else 0.0)
@@ -661,6 +665,21 @@ def test_backward_head_passes_tile_kernel_and_sparse(msda, D):
     close(gv.cpu().numpy(), rv, BWD_TOL, "grad_value")
     close(gl.cpu().numpy(), rl, BWD_TOL, "grad_sampling_loc")
     close(ga.cpu().numpy(), ra, BWD_TOL, "grad_attn_weight")
+
+
+def test_one_stream_matches_side_stream_at_encoder_shape(msda):
+    """The encoder shape on one stream (the dots kernel then also clears the
+    bin counters) against the side-stream run: the point gradients are
+    deterministic and equal bit for bit, grad_value equal to summation order."""
+    w = workloads.make(3)
+    x = dev_inputs(w)
+    g = torch.from_numpy(w.grad_out).cuda()
+    _say("encoder backward, one stream against side stream")
+    a = msda.backward(**x, grad_out=g, validate=False, side_stream="auto")
+    b = msda.backward(**x, grad_out=g, validate=False, side_stream=None)
+    torch.cuda.synchronize()
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+    close(b[0].cpu().numpy(), a[0].cpu().numpy(), 1e-5, "grad_value")
 
 
 def test_backward_below_min_workspace_raises(msda):
