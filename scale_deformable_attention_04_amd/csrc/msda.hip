@@ -15,10 +15,11 @@
 // consecutive queries of one (batch, head).
 //
 // Backward (msda_backward):
-//   bwd_dots_kernel (on a side stream, concurrently with the rest): per
-//      point the four <grad_out row, neighbour row> dot products, reduced
-//      across the lane group with DPP, give grad_attn_weight and
-//      grad_sampling_loc.
+//   bwd_dots_kernel (on a side stream, concurrently with the rest, for
+//      problems of at least 2^18 points; otherwise first on the caller's
+//      stream, where it also clears the bin counters): per point the four
+//      <grad_out row, neighbour row> dot products, reduced across the lane
+//      group with DPP, give grad_attn_weight and grad_sampling_loc.
 //   grad_value is a scatter (every point adds A * w * grad_out into four
 //   pixels).  fp32 atomics run at a few hundred G lane-ops/s on this chip,
 //   in LDS as in memory, so it is computed in gather form instead, per 8x8
@@ -26,7 +27,8 @@
 //   bin_count_kernel: points per bin (LDS histogram, one global add per bin
 //      and workgroup).
 //   bin_scan_kernel: exclusive scan of the counts -> bin offsets, and a work
-//      list of (bin, chunk of at most kChunk records).
+//      list of (bin, chunk of at most kChunk records); a workgroup per block
+//      of bins.
 //   bin_scatter_kernel: one 16-byte record per (point, bin) it touches,
 //      written into its bin (LDS ranks, one global reservation per bin and
 //      workgroup).
