@@ -452,6 +452,30 @@ def test_scan_two_passes(msda, D, acc):
     close(ga.cpu().numpy(), ra, BWD_TOL, "grad_attn_weight")
 
 
+@pytest.mark.parametrize("D,acc", [(8, False), (8, True), (64, False)])
+def test_scan_many_blocks(msda, D, acc):
+    """8 batches x 8 heads x (320 + 80 + 20) tiles = 26,880 bins: seven scan
+    workgroups, each summing the counts of the blocks before its own; few
+    points (200 queries), so most bins are empty and, with the gather kernel
+    (D = 8), the zero list runs through every block (D = 64 takes the tile
+    kernel, and such a sparse problem has grad_value zero-filled whole).
+    Overwrite mode starts from NaN."""
+    w = workloads.random_case(1980 + D, 8, ((128, 160), (64, 80), (32, 40)), 200, 8, D, 2)
+    x = dev_inputs(w)
+    g = torch.from_numpy(w.grad_out).cuda()
+    base = torch.randn(w.value.shape, device="cuda") if acc else None
+    _say(f"many-block scan D={D} acc={acc}")
+    gv0 = base.clone() if acc else torch.full(tuple(w.value.shape), float("nan"), device="cuda")
+    gv, gl, ga = msda.backward(**x, grad_out=g, grad_value=gv0, accumulate=acc, binned=True)
+    torch.cuda.synchronize()
+    rv, rl, ra = oracle_bwd(w)
+    got_v = gv.cpu().numpy() - (base.cpu().numpy() if acc else 0.0)
+    assert np.all(np.isfinite(got_v))
+    close(got_v, rv, BWD_TOL, "grad_value")
+    close(gl.cpu().numpy(), rl, BWD_TOL, "grad_sampling_loc")
+    close(ga.cpu().numpy(), ra, BWD_TOL, "grad_attn_weight")
+
+
 def test_runs_on_the_callers_stream(msda):
     w = workloads.random_case(700, 2, ((9, 9), (4, 4)), 90, 4, 32, 4)
     x = dev_inputs(w)
