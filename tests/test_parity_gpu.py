@@ -554,6 +554,31 @@ def test_backward_with_stage_events(msda, accumulate):
     close(ga.cpu().numpy(), ra, BWD_TOL, "grad_attn_weight")
 
 
+@pytest.mark.parametrize("side", ["auto", None])
+def test_stage_events_span_passes(msda, side):
+    """With grad_value in passes (the smallest workspace: 1024-query ranges of
+    one head), each stage's events run from its start in the first pass to
+    its end in the last: every stage is timed, and the gradients match the
+    oracle."""
+    w = workloads.random_case(910, 2, ((40, 56), (20, 28)), 2300, 2, 32, 4)
+    B, Nv, Nq, M, D, L, K = (w.dims[k] for k in ("B", "Nv", "Nq", "M", "D", "L", "K"))
+    least = msda.workspace_min(B, Nv, Nq, M, D, L, K)
+    x = dev_inputs(w)
+    g = torch.from_numpy(w.grad_out).cuda()
+    _say(f"stage events over passes, side_stream={side}")
+    ev = msda.make_events()
+    gv, gl, ga = msda.backward(**x, grad_out=g, events=ev, side_stream=side,
+                               workspace=torch.empty(least, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    st = msda.stage_times(ev)
+    assert len(st) == len(msda.BWD_STAGES) and all(t >= 0.0 for t in st)
+    assert st[msda.BWD_STAGES.index("tiles")] > 0.0 and st[msda.BWD_STAGES.index("count")] > 0.0
+    rv, rl, ra = oracle_bwd(w)
+    close(gv.cpu().numpy(), rv, BWD_TOL, "grad_value")
+    close(gl.cpu().numpy(), rl, BWD_TOL, "grad_sampling_loc")
+    close(ga.cpu().numpy(), ra, BWD_TOL, "grad_attn_weight")
+
+
 def test_two_streams_backward_concurrently(msda):
     """Two backwards issued on two torch streams without a host wait between
     them, each with its own workspace (and, by default, its own side stream
